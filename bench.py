@@ -1,0 +1,278 @@
+#!/usr/bin/env python3
+"""Throughput of one mixture-of-experts layer forward on one MI355X.
+
+A step is one moe_layer_forward call (router, permutation, grouped gate/up and
+down GEMMs over the routed experts plus the shared expert, combine) over one
+batch of synthetic tokens already resident in HBM. The default workload is
+the 30B-shaped decode step (T=64, d=4096, E=128, top-6, F=1024, one shared
+expert, FP8 E4M3 weights, bf16 activations); the 3584-token prefill is timed
+as a second, reported workload.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
+FP8_PEAK_TFLOPS = 5000.0    # MI355X dense FP8 MFMA, published
+METRIC = "MoE-layer tokens/s at T=64 decode & T=3584 prefill; % of HBM / FP8 MFMA peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Hip:
+    """HIP events through the runtime that torch already loaded."""
+
+    def __init__(self):
+        self.L = C.CDLL("libamdhip64.so")
+        self.L.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.L.hipEventSynchronize.argtypes = [C.c_void_p]
+        self.L.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.L.hipEventDestroy.argtypes = [C.c_void_p]
+
+    def event(self) -> int:
+        e = C.c_void_p()
+        if self.L.hipEventCreate(C.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e.value
+
+    def ms(self, a: int, b: int) -> float:
+        self.L.hipEventSynchronize(C.c_void_p(b))
+        t = C.c_float()
+        if self.L.hipEventElapsedTime(C.byref(t), C.c_void_p(a), C.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return t.value
+
+    def destroy(self, e: int):
+        self.L.hipEventDestroy(C.c_void_p(e))
+
+
+def accounting(cfg, counts):
+    """Algorithmic bytes and FLOPs of the layer and of the gate/up GEMM launch,
+    given the rows per routed expert (`counts`, from the run's own routing)."""
+    T, d, E, k, F, Fs = cfg.T, cfg.d, cfg.E, cfg.k, cfg.F, cfg.F_shared
+    touched = int((counts > 0).sum())
+    groups = touched + (1 if Fs else 0)
+    rows = T * k + (T if Fs else 0)
+    # gate/up launch: each touched group's W13 codes + scales once; per row the
+    # x codes + scale in and the h codes + block scales out
+    up_bytes = touched * (2 * F * d + 8 * F) + (2 * Fs * d + 8 * Fs if Fs else 0) \
+        + rows * (d + 4) + T * k * (F + F // 32) + (T * (Fs + Fs // 32) if Fs else 0)
+    up_flops = 2.0 * d * (T * k * 2 * F + (T * 2 * Fs if Fs else 0))
+    # whole layer: every touched expert's weights and scales once, router
+    # weight, x in, y out; FP8 GEMM FLOPs 6 d F per (token, expert) pair
+    layer_bytes = touched * (3 * d * F + (2 * F + d) * 4) \
+        + ((3 * d * Fs + (2 * Fs + d) * 4) if Fs else 0) + E * d * 2 + 2 * T * d * 2
+    layer_flops = 6.0 * d * (T * k * F + (T * Fs if Fs else 0))
+    return dict(touched=touched, groups=groups, rows=rows, up_bytes=up_bytes, up_flops=up_flops,
+                layer_bytes=layer_bytes, layer_flops=layer_flops)
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in ("ffn.hip", "common.h"):
+        h.update(open(os.path.join(ROOT, "mixture_experts_softmax_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per gate/up launch from committed counter runs, or None when
+    missing or taken on another version of the kernel source."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(workload)
+    if not ent or ent.get("kernel_digest") != kernel_source_digest():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def time_layer(cfg, steps, warmup, hip):
+    import torch
+
+    import mixture_experts_softmax_amd as M
+    from mixture_experts_softmax_amd import _lib
+    from synthetic import make_layer
+
+    t = time.time()
+    lt = make_layer(cfg, device="cuda")
+    torch.cuda.synchronize()
+    log(f"[bench] {cfg.name}: inputs generated in {time.time() - t:.1f}s")
+    L = M.MoELayer(d=cfg.d, E=cfg.E, k=cfg.k, F=cfg.F, F_shared=cfg.F_shared,
+                   precision=cfg.precision, w_router=lt.w_router, router_bias=lt.router_bias,
+                   w13=lt.w13, w13_scale=lt.w13_scale, w2=lt.w2, w2_scale=lt.w2_scale, ws13=lt.ws13,
+                   ws13_scale=lt.ws13_scale, ws2=lt.ws2, ws2_scale=lt.ws2_scale)
+    T = cfg.T
+    s = L.shape(T)
+    ws = L.workspace(T, "cuda")
+    W = _lib.make_weights(s, **L.tensors)
+    x = lt.x
+    y = torch.empty_like(x)
+    ids = torch.empty((T, cfg.k), dtype=torch.int32, device="cuda")
+    gw = torch.empty((T, cfg.k), dtype=torch.float32, device="cuda")
+    nsteps = len(_lib.MOE_STEPS)
+    UP = _lib.MOE_STEPS.index("gate_up")
+
+    for _ in range(warmup):
+        _lib.moe_layer_forward(s, W, x, y, ids, gw, ws)
+    torch.cuda.synchronize()
+
+    ev_a = [hip.event() for _ in range(steps)]
+    ev_b = [hip.event() for _ in range(steps)]
+    none = [None] * nsteps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        st, sp = list(none), list(none)
+        st[UP], sp[UP] = ev_a[i], ev_b[i]
+        _lib.moe_layer_forward_events(s, W, x, y, ids, gw, ws, st, sp)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / steps
+    up_ms = sum(hip.ms(a, b) for a, b in zip(ev_a, ev_b)) / steps
+    for e in ev_a + ev_b:
+        hip.destroy(e)
+
+    # per-step breakdown (separate short loop, all steps bracketed)
+    reps = min(steps, 10)
+    starts = [[hip.event() for _ in range(nsteps)] for _ in range(reps)]
+    stops = [[hip.event() for _ in range(nsteps)] for _ in range(reps)]
+    for i in range(reps):
+        _lib.moe_layer_forward_events(s, W, x, y, ids, gw, ws, starts[i], stops[i])
+    torch.cuda.synchronize()
+    breakdown = {}
+    for j, name in enumerate(_lib.MOE_STEPS):
+        breakdown[name] = round(1e3 * sum(hip.ms(starts[i][j], stops[i][j]) for i in range(reps)) / reps, 2)
+    for row in starts + stops:
+        for e in row:
+            hip.destroy(e)
+
+    import numpy as np
+    counts = np.bincount(ids.cpu().numpy().reshape(-1), minlength=cfg.E)
+    acc = accounting(cfg, counts)
+    del L, ws, W, x, y
+    return dict(ms_step=ms_step, up_ms=up_ms, breakdown_us=breakdown, acc=acc, counts=counts, lt=lt)
+
+
+def cpu_baseline(cfg, lt, n_tokens):
+    """The oracle, untouched, on the first n_tokens tokens of the same inputs
+    the GPU just ran (host copies of the touched experts made beforehand)."""
+    import numpy as np
+
+    from oracle import inputs as oinputs
+    from oracle import moe as omoe
+
+    inp = oinputs.layer_inputs(lt, cache_all=True)
+    tok = np.arange(n_tokens)
+    # host copies of the touched experts are made before the clock starts
+    x64 = omoe.activations(inp)[:n_tokens]
+    ids = omoe.topk_ids(omoe.router_logits(x64, omoe.router_weight(inp), inp.router_bias), cfg.k)
+    for e in np.unique(ids):
+        inp.expert(int(e))
+    t = time.perf_counter()
+    omoe.layer_forward_tokens(inp, tok)
+    dt = time.perf_counter() - t
+    try:
+        import threadpoolctl
+        cores = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    return dict(value=round(n_tokens / dt, 3), unit="tokens/s", cores=int(cores), kind="oracle",
+                sample=f"first {n_tokens} tokens of the {cfg.name} workload (T={cfg.T}), "
+                       f"{len(np.unique(ids))} touched experts, {dt:.1f}s of float64 numpy")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "b100", "skew"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=8)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer would shard by expert across GPUs, which is not implemented)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    from synthetic import CONFIGS
+    hip = Hip()
+    cfg = CONFIGS[args.workload]
+    r = time_layer(cfg, args.steps, args.warmup, hip)
+    lt = r.pop("lt")
+    acc = r["acc"]
+    value = cfg.T / (r["ms_step"] / 1e3)
+    achieved = acc["up_bytes"] / (r["up_ms"] / 1e3) / 1e9
+    traffic = measured_traffic(args.workload)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: T={cfg.T} d={cfg.d} E={cfg.E} top-{cfg.k} "
+                               f"F={cfg.F} shared F={cfg.F_shared}, FP8 E4M3 weights, bf16 x",
+                   "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k, "F": cfg.F,
+                   "F_shared": cfg.F_shared, "parallelism": "none (1 GPU)"},
+        "roofline": {"kernel": "gate_up_fp8_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "alg_bytes_per_launch": acc["up_bytes"], "avg_launch_us": round(r["up_ms"] * 1e3, 2)},
+        "layer": {"alg_bytes": acc["layer_bytes"], "fp8_flops": acc["layer_flops"],
+                  "hbm_frac": round(acc["layer_bytes"] / (r["ms_step"] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                  "fp8_mfma_frac": round(acc["layer_flops"] / (r["ms_step"] / 1e3) / 1e12 / FP8_PEAK_TFLOPS, 4),
+                  "touched_experts": acc["touched"], "step_breakdown_us": r["breakdown_us"]},
+    }
+    if not args.no_secondary and args.workload != "prefill":
+        p = CONFIGS["prefill"]
+        rp = time_layer(p, max(5, args.steps // 2), max(2, args.warmup // 2), hip)
+        del rp["lt"]
+        torch.cuda.empty_cache()
+        ap_ = rp["acc"]
+        t = rp["ms_step"] / 1e3
+        out["prefill"] = {
+            "workload": f"prefill: T={p.T}", "value": round(p.T / t, 1), "unit": "tokens/s",
+            "ms_per_step": round(rp["ms_step"], 4),
+            "hbm_frac": round(ap_["layer_bytes"] / t / 1e9 / HBM_PEAK_GBS, 4),
+            "fp8_mfma_frac": round(ap_["layer_flops"] / t / 1e12 / FP8_PEAK_TFLOPS, 4),
+            "gate_up_us": round(rp["up_ms"] * 1e3, 2),
+            "gate_up_GBs": round(ap_["up_bytes"] / (rp["up_ms"] / 1e3) / 1e9, 1),
+            "gate_up_TFLOPs": round(ap_["up_flops"] / (rp["up_ms"] / 1e3) / 1e12, 1),
+            "step_breakdown_us": rp["breakdown_us"]}
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        out["cpu_baseline"] = cpu_baseline(cfg, lt, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,244 @@
+/*
+ * moe.h -- C ABI of libmoe, the forward pass of one mixture-of-experts layer
+ * with softmax top-k gating, SwiGLU experts stored in FP8 and one always-on
+ * shared expert, as hand-written HIP kernels for AMD Instinct MI355X (gfx950).
+ *
+ * The layer follows the model described on the NVIDIA blog "How NVIDIA extreme
+ * hardware-software co-design delivered a large inference boost for Sarvam
+ * AI's sovereign models" (section "Scaling multilingual sovereign AI with
+ * MoE": 128 routed experts, top-6 or top-8 routing, a shared expert beside the
+ * routed ones; Table 1: router logits and top-k as one fused step, routed
+ * experts as grouped GEMMs, the shared expert as a separate computation).
+ *
+ * Conventions for every entry point:
+ *  - Pointers named as device pointers must point to device memory (or memory
+ *    the device can access) owned by the caller; the library never allocates,
+ *    frees or synchronises inside these calls and keeps no global state, so
+ *    calls on different streams do not interfere unless their buffers alias.
+ *  - `stream` is a hipStream_t (NULL = the null stream). Calls only enqueue
+ *    work and return; results are ready when the stream reaches them.
+ *  - Arguments are checked on the host before anything is enqueued; a
+ *    rejected call returns a negative status and enqueues nothing. A failed
+ *    launch returns MOE_ERR_HIP.
+ *  - All arrays are dense and row-major; weight matrices are [out][in].
+ *    Activation, weight and output arrays must start on a 16-byte boundary
+ *    and workspaces on a 256-byte boundary (MOE_ERR_INVALID_ARG /
+ *    MOE_ERR_WORKSPACE otherwise).
+ *  - Inputs are assumed finite; results for NaN or Inf inputs are unspecified.
+ *  - T == 0 is valid and enqueues nothing.
+ *
+ * Supported precisions (moe_shape_t.act_dtype, .w_dtype):
+ *  - (MOE_DTYPE_BF16, MOE_DTYPE_FP8_E4M3): bf16 activations and router weight,
+ *    OCP FP8 E4M3 expert weights with one float32 scale per output channel,
+ *    bf16 output. Activations entering the expert GEMMs are quantised to FP8
+ *    E4M3: x per token, the SwiGLU output h per (row, 128-column block), each
+ *    with a float32 scale amax/448 (1.0 for an all-zero block), codes rounded
+ *    to nearest even with saturation at +-448.
+ *  - (MOE_DTYPE_F32, MOE_DTYPE_F32): float32 throughout, no quantisation.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+/* Limits checked by every entry point. */
+#define MOE_MAX_E 256      /* routed experts */
+#define MOE_MAX_K 16       /* experts per token */
+#define MOE_MAX_D 16384    /* hidden size */
+#define MOE_MAX_F 16384    /* expert FFN width */
+#define MOE_MAX_T (1 << 22)
+#define MOE_DIM_ALIGN 128  /* d, F and F_shared must be multiples of this */
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null pointer, bad size or shape */
+  MOE_ERR_UNSUPPORTED = -2, /* unsupported (act_dtype, w_dtype) pair */
+  MOE_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+  MOE_ERR_HIP = -4          /* the HIP runtime reported an error */
+} moe_status_t;
+
+typedef enum moe_dtype {
+  MOE_DTYPE_F32 = 0,
+  MOE_DTYPE_BF16 = 1,
+  MOE_DTYPE_FP8_E4M3 = 2
+} moe_dtype_t;
+
+/* Shape of one layer call. */
+typedef struct moe_shape {
+  int32_t T;         /* tokens in this call, 0 <= T <= MOE_MAX_T */
+  int32_t d;         /* hidden size */
+  int32_t E;         /* routed experts, 1..MOE_MAX_E */
+  int32_t k;         /* experts chosen per token, 1..min(E, MOE_MAX_K) */
+  int32_t F;         /* routed expert FFN width */
+  int32_t F_shared;  /* shared expert FFN width; 0 = no shared expert */
+  int32_t act_dtype; /* moe_dtype_t of x, the router weight and y */
+  int32_t w_dtype;   /* moe_dtype_t of the expert weights */
+} moe_shape_t;
+
+/* The layer's weights (device pointers). */
+typedef struct moe_weights {
+  const void* w_router;     /* [E][d], act_dtype */
+  const float* router_bias; /* [E] added to the logits before softmax, or NULL */
+  const void* w13;          /* [E][2F][d], w_dtype; rows 0..F-1 gate, F..2F-1 up */
+  const float* w13_scale;   /* [E][2F] per-output-row scales (FP8 only, else NULL) */
+  const void* w2;           /* [E][d][F], w_dtype */
+  const float* w2_scale;    /* [E][d] (FP8 only) */
+  const void* ws13;         /* shared expert [2F_shared][d] (NULL if F_shared == 0) */
+  const float* ws13_scale;  /* [2F_shared] (FP8 only) */
+  const void* ws2;          /* shared expert [d][F_shared] */
+  const float* ws2_scale;   /* [d] (FP8 only) */
+} moe_weights_t;
+
+/* One grouped SwiGLU FFN call: G groups of rows, each group g multiplying its
+ * rows by its own expert's weights. */
+typedef struct moe_ffn {
+  int32_t d;                    /* hidden size (multiple of 128) */
+  int32_t F;                    /* FFN width of every group (multiple of 128) */
+  int32_t num_groups;           /* G >= 1 */
+  int32_t max_rows;             /* rows of `out`; group_offsets[G] must not exceed it */
+  int32_t w_dtype;              /* MOE_DTYPE_FP8_E4M3 or MOE_DTYPE_F32 */
+  const int32_t* group_offsets; /* device [G+1], non-decreasing, [0] == 0: group g owns
+                                   grouped rows group_offsets[g] .. group_offsets[g+1]-1 */
+  const int32_t* row_src;       /* device [max_rows] or NULL: grouped row r reads activation
+                                   row row_src[r] / src_div (NULL: activation row r) */
+  int32_t src_div;              /* >= 1 */
+  int32_t a_rows;               /* rows of `a`; every source row must be below it */
+  const void* a;                /* [a_rows][d]: FP8 codes (FP8 path) or float32 */
+  const float* a_scale;         /* [a_rows] per-row scales (FP8 path), else NULL */
+  const void* w13;              /* [G][2F][d] */
+  const float* w13_scale;       /* [G][2F] (FP8 path) */
+  const void* w2;               /* [G][d][F] */
+  const float* w2_scale;        /* [G][d] (FP8 path) */
+  void* out;                    /* [max_rows][d]: bf16 (FP8 path) or float32 */
+} moe_ffn_t;
+
+/* ABI version (MOE_ABI_VERSION) and a static text for a status code. */
+int32_t moe_abi_version(void);
+const char* moe_status_string(int32_t status);
+
+/* Checks a layer shape against the limits above. */
+moe_status_t moe_check_shape(const moe_shape_t* shape);
+
+/* Workspace sizes in bytes (host-only queries, nothing is enqueued). */
+moe_status_t moe_layer_workspace_size(const moe_shape_t* shape, size_t* bytes);
+moe_status_t moe_permute_workspace_size(const moe_shape_t* shape, size_t* bytes);
+moe_status_t moe_grouped_ffn_workspace_size(const moe_ffn_t* ffn, size_t* bytes);
+
+/*
+ * Router: logits, softmax, top-k selection and renormalised gate weights in
+ * one kernel (NVIDIA blog, Table 1 row "Router logits and TopK" and the
+ * paragraph on MoE routing; peacm.com repost section 3.1: the fused router
+ * writes integer expert indices and float scores; ijyty.com "InferX" page
+ * section 2.4: softmax over the expert logits, then top-k).
+ *
+ *   l[t, e]  = sum_i x[t, i] * w_router[e, i] + router_bias[e]   (float32 accumulation)
+ *   ids[t]   = the k experts with the largest l[t, .], largest first, equal
+ *              logits ordered by lower expert index
+ *   w[t, j]  = softmax(l[t, .])[ids[t, j]] / sum_j' softmax(l[t, .])[ids[t, j']]
+ *
+ * x [T][d] and w_router [E][d] in act_dtype; router_bias [E] float32 or NULL.
+ * Outputs topk_ids [T][k] int32 and topk_w [T][k] float32. On the FP8 path the
+ * same kernel also writes xq [T][d] (FP8 E4M3 codes of x / x_scale[t]) and
+ * x_scale [T] (amax of row t over 448, 1.0 for a zero row); both are required
+ * there and ignored on the float32 path.
+ */
+moe_status_t moe_route_topk(const moe_shape_t* shape, const void* x, const void* w_router,
+                            const float* router_bias, int32_t* topk_ids, float* topk_w,
+                            uint8_t* xq, float* x_scale, void* stream);
+
+/*
+ * Permutation of the T*k (token, slot) pairs into expert-contiguous order (the
+ * scatter that the InferX page, section 3.3, fuses after its top-k router).
+ * Pair p = t*k + j. Rows of expert e are offsets[e] .. offsets[e+1]-1, pairs
+ * of one expert in ascending token order:
+ *   offsets     [E+1]  offsets[0] = 0, offsets[E] = T*k
+ *   sorted_pair [T*k]  row -> pair
+ *   pair_to_row [T*k]  pair -> row
+ * topk_ids must hold values in [0, E), distinct within a token; a pair with an
+ * id outside [0, E) gets no row and pair_to_row = -1. Needs a workspace of
+ * moe_permute_workspace_size() bytes.
+ */
+moe_status_t moe_permute(const moe_shape_t* shape, const int32_t* topk_ids, int32_t* offsets,
+                         int32_t* sorted_pair, int32_t* pair_to_row, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
+ * Grouped SwiGLU expert FFN (NVIDIA blog, section "Performance challenges":
+ * routed experts run as grouped GEMM kernels with the expert weights resident
+ * in HBM; Table 1 rows "Routed expert compute" and "Shared expert compute").
+ * For grouped row r of group g with activation row s:
+ *   FP8 path:  gu[n] = a_scale[s] * w13_scale[g][n] * sum_i a[s][i] * w13[g][n][i]
+ *              h[n]  = silu(gu[n]) * gu[F + n],  silu(z) = z / (1 + exp(-z))
+ *              h is quantised per 128-column block (scale amax/448, E4M3 codes)
+ *              out[r][m] = w2_scale[g][m] * sum_b s_h[b] * sum_{n in b} hq[n] * w2[g][m][n]
+ *              out is rounded to bf16 (nearest even)
+ *   F32 path:  the same without any quantisation, float32 out.
+ * Rows beyond group_offsets[G] are not written. Needs a workspace of
+ * moe_grouped_ffn_workspace_size() bytes. The shared expert is one group over
+ * all tokens (row_src = NULL).
+ */
+moe_status_t moe_grouped_ffn(const moe_ffn_t* ffn, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/*
+ * Gate-weighted combine, in this order with float32 accumulation and no
+ * atomics:  y[t] = sum_{j=0}^{k-1} topk_w[t, j] * expert_out[pair_to_row[t*k + j]]
+ *                  + shared_out[t]
+ * expert_out [T*k][d] and shared_out [T][d] (NULL: no shared term) are bf16 on
+ * the FP8 path and float32 on the float32 path, as is y [T][d]. Pairs whose
+ * pair_to_row is outside [0, T*k) contribute nothing.
+ */
+moe_status_t moe_combine(const moe_shape_t* shape, const void* expert_out,
+                         const int32_t* pair_to_row, const float* topk_w,
+                         const void* shared_out, void* y, void* stream);
+
+/*
+ * The whole layer: router, permutation, grouped FFN over the routed experts
+ * and the shared expert, combine. x [T][d] and y [T][d] in act_dtype.
+ * topk_ids [T][k] and topk_w [T][k] receive the routing when non-NULL. Needs a
+ * workspace of moe_layer_workspace_size() bytes, aligned to 256 bytes.
+ */
+moe_status_t moe_layer_forward(const moe_shape_t* shape, const moe_weights_t* weights,
+                               const void* x, void* y, int32_t* topk_ids, float* topk_w,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Steps of moe_layer_forward, in launch order (for moe_layer_forward_events). */
+typedef enum moe_step {
+  MOE_STEP_ROUTE = 0,    /* router kernel */
+  MOE_STEP_PERMUTE = 1,  /* the three permutation kernels */
+  MOE_STEP_TILES = 2,    /* grouped-FFN tile list */
+  MOE_STEP_GATE_UP = 3,  /* gate/up GEMM + SwiGLU + h quantisation */
+  MOE_STEP_DOWN = 4,     /* down GEMM */
+  MOE_STEP_COMBINE = 5,  /* combine */
+  MOE_NUM_STEPS = 6
+} moe_step_t;
+
+/*
+ * moe_layer_forward that also records caller-created HIP events (hipEvent_t)
+ * on `stream`: start_events[i] just before the first kernel of step i and
+ * stop_events[i] just after its last kernel. Either array, or any entry, may
+ * be NULL to skip it. Results are identical to moe_layer_forward.
+ */
+moe_status_t moe_layer_forward_events(const moe_shape_t* shape, const moe_weights_t* weights,
+                                      const void* x, void* y, int32_t* topk_ids, float* topk_w,
+                                      void* workspace, size_t workspace_bytes, void* stream,
+                                      void* const* start_events, void* const* stop_events);
+
+/*
+ * Host-side copy of the E4M3 encoder the kernels use (float32 -> code, round
+ * to nearest even, saturating at +-448), for testing it without a GPU.
+ */
+void moe_host_e4m3_encode(const float* in, uint8_t* out, int64_t n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

@@ -1,0 +1,299 @@
+"""ctypes binding of libmoe.so: the C ABI declared in include/moe.h, with the
+same function names. Argument marshalling only: tensors are checked for
+device, dtype, contiguity and size (a host pointer or a short buffer handed to
+a kernel would fault the GPU), then their device pointers are passed on. All
+computation happens in the library's HIP kernels.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_DTYPE_F32, MOE_DTYPE_BF16, MOE_DTYPE_FP8_E4M3 = 0, 1, 2
+
+# Names declared in include/moe.h, in order.
+EXPORTS = [
+    "moe_abi_version", "moe_status_string", "moe_check_shape",
+    "moe_layer_workspace_size", "moe_permute_workspace_size", "moe_grouped_ffn_workspace_size",
+    "moe_route_topk", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_forward",
+    "moe_layer_forward_events", "moe_host_e4m3_encode",
+]
+
+
+class MoeShape(C.Structure):
+    _fields_ = [("T", C.c_int32), ("d", C.c_int32), ("E", C.c_int32), ("k", C.c_int32),
+                ("F", C.c_int32), ("F_shared", C.c_int32), ("act_dtype", C.c_int32),
+                ("w_dtype", C.c_int32)]
+
+
+class MoeWeights(C.Structure):
+    _fields_ = [("w_router", C.c_void_p), ("router_bias", C.c_void_p),
+                ("w13", C.c_void_p), ("w13_scale", C.c_void_p),
+                ("w2", C.c_void_p), ("w2_scale", C.c_void_p),
+                ("ws13", C.c_void_p), ("ws13_scale", C.c_void_p),
+                ("ws2", C.c_void_p), ("ws2_scale", C.c_void_p)]
+
+
+class MoeFfn(C.Structure):
+    _fields_ = [("d", C.c_int32), ("F", C.c_int32), ("num_groups", C.c_int32),
+                ("max_rows", C.c_int32), ("w_dtype", C.c_int32),
+                ("group_offsets", C.c_void_p), ("row_src", C.c_void_p), ("src_div", C.c_int32),
+                ("a_rows", C.c_int32), ("a", C.c_void_p), ("a_scale", C.c_void_p),
+                ("w13", C.c_void_p), ("w13_scale", C.c_void_p),
+                ("w2", C.c_void_p), ("w2_scale", C.c_void_p), ("out", C.c_void_p)]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+        self.status = status
+
+
+_lib: Optional[C.CDLL] = None
+
+
+def lib() -> C.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m mixture_experts_softmax_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        P, I32, SZ = C.c_void_p, C.c_int32, C.c_size_t
+        L.moe_abi_version.restype = I32
+        L.moe_status_string.restype = C.c_char_p
+        L.moe_status_string.argtypes = [I32]
+        L.moe_check_shape.restype = I32
+        L.moe_check_shape.argtypes = [P]
+        for n in ("moe_layer_workspace_size", "moe_permute_workspace_size",
+                  "moe_grouped_ffn_workspace_size"):
+            getattr(L, n).restype = I32
+            getattr(L, n).argtypes = [P, C.POINTER(SZ)]
+        L.moe_route_topk.restype = I32
+        L.moe_route_topk.argtypes = [P] * 9
+        L.moe_permute.restype = I32
+        L.moe_permute.argtypes = [P, P, P, P, P, P, SZ, P]
+        L.moe_grouped_ffn.restype = I32
+        L.moe_grouped_ffn.argtypes = [P, P, SZ, P]
+        L.moe_combine.restype = I32
+        L.moe_combine.argtypes = [P] * 7
+        L.moe_layer_forward.restype = I32
+        L.moe_layer_forward.argtypes = [P, P, P, P, P, P, P, SZ, P]
+        L.moe_layer_forward_events.restype = I32
+        L.moe_layer_forward_events.argtypes = [P, P, P, P, P, P, P, SZ, P, P, P]
+        L.moe_host_e4m3_encode.restype = None
+        L.moe_host_e4m3_encode.argtypes = [P, P, C.c_int64]
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().moe_status_string(status).decode()
+
+
+def _check(status: int, what: str):
+    if status != MOE_OK:
+        raise MoeError(status, what)
+
+
+# ------------------------------------------------------------ marshalling --
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtype=None, numel: Optional[int] = None,
+         device: bool = True):
+    """Device pointer of a contiguous tensor (None -> NULL) after checks."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name}: must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name}: {t.numel()} elements, need {numel}")
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> Optional[C.c_void_p]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def shape(T, d, E, k, F, F_shared, precision: str) -> MoeShape:
+    if precision == "fp8":
+        return MoeShape(T, d, E, k, F, F_shared, MOE_DTYPE_BF16, MOE_DTYPE_FP8_E4M3)
+    if precision == "f32":
+        return MoeShape(T, d, E, k, F, F_shared, MOE_DTYPE_F32, MOE_DTYPE_F32)
+    raise ValueError(precision)
+
+
+def _is_fp8(s: MoeShape) -> bool:
+    return s.w_dtype == MOE_DTYPE_FP8_E4M3
+
+
+def _act_dtype(s: MoeShape):
+    return torch.bfloat16 if _is_fp8(s) else torch.float32
+
+
+def _w_dtype(s: MoeShape):
+    return torch.uint8 if _is_fp8(s) else torch.float32
+
+
+# ------------------------------------------------------------ the C calls --
+
+def moe_abi_version() -> int:
+    return lib().moe_abi_version()
+
+
+def moe_check_shape(s: MoeShape) -> int:
+    return lib().moe_check_shape(C.byref(s))
+
+
+def moe_layer_workspace_size(s: MoeShape) -> int:
+    n = C.c_size_t(0)
+    _check(lib().moe_layer_workspace_size(C.byref(s), C.byref(n)), "moe_layer_workspace_size")
+    return n.value
+
+
+def moe_permute_workspace_size(s: MoeShape) -> int:
+    n = C.c_size_t(0)
+    _check(lib().moe_permute_workspace_size(C.byref(s), C.byref(n)), "moe_permute_workspace_size")
+    return n.value
+
+
+def moe_grouped_ffn_workspace_size(f: MoeFfn) -> int:
+    n = C.c_size_t(0)
+    _check(lib().moe_grouped_ffn_workspace_size(C.byref(f), C.byref(n)),
+           "moe_grouped_ffn_workspace_size")
+    return n.value
+
+
+def moe_route_topk(s: MoeShape, x, w_router, router_bias, topk_ids, topk_w, xq=None,
+                   x_scale=None, stream=None):
+    T, d, E, k = s.T, s.d, s.E, s.k
+    fp8 = _is_fp8(s)
+    args = (C.byref(s), _ptr(x, "x", _act_dtype(s), T * d), _ptr(w_router, "w_router", _act_dtype(s), E * d),
+            _ptr(router_bias, "router_bias", torch.float32, E),
+            _ptr(topk_ids, "topk_ids", torch.int32, T * k), _ptr(topk_w, "topk_w", torch.float32, T * k),
+            _ptr(xq, "xq", torch.uint8, T * d) if fp8 else None,
+            _ptr(x_scale, "x_scale", torch.float32, T) if fp8 else None, _stream(stream))
+    _check(lib().moe_route_topk(*args), "moe_route_topk")
+
+
+def moe_permute(s: MoeShape, topk_ids, offsets, sorted_pair, pair_to_row, workspace, stream=None):
+    n = s.T * s.k
+    _check(lib().moe_permute(C.byref(s), _ptr(topk_ids, "topk_ids", torch.int32, n),
+                             _ptr(offsets, "offsets", torch.int32, s.E + 1),
+                             _ptr(sorted_pair, "sorted_pair", torch.int32, n),
+                             _ptr(pair_to_row, "pair_to_row", torch.int32, n),
+                             _ptr(workspace, "workspace", torch.uint8),
+                             workspace.numel() if workspace is not None else 0, _stream(stream)),
+           "moe_permute")
+
+
+def make_ffn(d, F, num_groups, max_rows, fp8: bool, group_offsets, row_src, src_div, a, a_scale,
+             w13, w13_scale, w2, w2_scale, out) -> MoeFfn:
+    G = num_groups
+    wd = torch.uint8 if fp8 else torch.float32
+    a_rows = a.shape[0] if a is not None else 0
+    return MoeFfn(
+        d, F, G, max_rows, MOE_DTYPE_FP8_E4M3 if fp8 else MOE_DTYPE_F32,
+        _ptr(group_offsets, "group_offsets", torch.int32, G + 1),
+        _ptr(row_src, "row_src", torch.int32, max_rows), src_div, a_rows,
+        _ptr(a, "a", wd, a_rows * d),
+        _ptr(a_scale, "a_scale", torch.float32, a_rows) if fp8 else None,
+        _ptr(w13, "w13", wd, G * 2 * F * d),
+        _ptr(w13_scale, "w13_scale", torch.float32, G * 2 * F) if fp8 else None,
+        _ptr(w2, "w2", wd, G * d * F),
+        _ptr(w2_scale, "w2_scale", torch.float32, G * d) if fp8 else None,
+        _ptr(out, "out", torch.bfloat16 if fp8 else torch.float32, max_rows * d))
+
+
+def moe_grouped_ffn(f: MoeFfn, workspace, stream=None):
+    _check(lib().moe_grouped_ffn(C.byref(f), _ptr(workspace, "workspace", torch.uint8),
+                                 workspace.numel() if workspace is not None else 0,
+                                 _stream(stream)), "moe_grouped_ffn")
+
+
+def moe_combine(s: MoeShape, expert_out, pair_to_row, topk_w, shared_out, y, stream=None):
+    T, d, k = s.T, s.d, s.k
+    ad = _act_dtype(s)
+    _check(lib().moe_combine(C.byref(s), _ptr(expert_out, "expert_out", ad, T * k * d),
+                             _ptr(pair_to_row, "pair_to_row", torch.int32, T * k),
+                             _ptr(topk_w, "topk_w", torch.float32, T * k),
+                             _ptr(shared_out, "shared_out", ad, T * d),
+                             _ptr(y, "y", ad, T * d), _stream(stream)), "moe_combine")
+
+
+def make_weights(s: MoeShape, w_router, router_bias, w13, w13_scale, w2, w2_scale,
+                 ws13=None, ws13_scale=None, ws2=None, ws2_scale=None) -> MoeWeights:
+    E, d, F, Fs = s.E, s.d, s.F, s.F_shared
+    fp8 = _is_fp8(s)
+    wd, ad = _w_dtype(s), _act_dtype(s)
+    f32 = torch.float32
+    return MoeWeights(
+        _ptr(w_router, "w_router", ad, E * d), _ptr(router_bias, "router_bias", f32, E),
+        _ptr(w13, "w13", wd, E * 2 * F * d), _ptr(w13_scale, "w13_scale", f32, E * 2 * F) if fp8 else None,
+        _ptr(w2, "w2", wd, E * d * F), _ptr(w2_scale, "w2_scale", f32, E * d) if fp8 else None,
+        _ptr(ws13, "ws13", wd, 2 * Fs * d) if Fs else None,
+        _ptr(ws13_scale, "ws13_scale", f32, 2 * Fs) if (Fs and fp8) else None,
+        _ptr(ws2, "ws2", wd, d * Fs) if Fs else None,
+        _ptr(ws2_scale, "ws2_scale", f32, d) if (Fs and fp8) else None)
+
+
+def moe_layer_forward(s: MoeShape, weights: MoeWeights, x, y, topk_ids, topk_w, workspace,
+                      stream=None):
+    T, d, k = s.T, s.d, s.k
+    ad = _act_dtype(s)
+    _check(lib().moe_layer_forward(C.byref(s), C.byref(weights), _ptr(x, "x", ad, T * d),
+                                   _ptr(y, "y", ad, T * d),
+                                   _ptr(topk_ids, "topk_ids", torch.int32, T * k),
+                                   _ptr(topk_w, "topk_w", torch.float32, T * k),
+                                   _ptr(workspace, "workspace", torch.uint8),
+                                   workspace.numel() if workspace is not None else 0,
+                                   _stream(stream)), "moe_layer_forward")
+
+
+MOE_STEPS = ["route", "permute", "tiles", "gate_up", "down", "combine"]
+
+
+def moe_layer_forward_events(s: MoeShape, weights: MoeWeights, x, y, topk_ids, topk_w, workspace,
+                             start_events, stop_events, stream=None):
+    """start_events / stop_events: sequences of len(MOE_STEPS) raw hipEvent_t
+    handles (int) or None."""
+    T, d, k = s.T, s.d, s.k
+    ad = _act_dtype(s)
+    n = len(MOE_STEPS)
+    arr_t = C.c_void_p * n
+
+    def arr(evs):
+        if evs is None:
+            return None
+        return arr_t(*[C.c_void_p(e) if e else None for e in evs])
+    _check(lib().moe_layer_forward_events(C.byref(s), C.byref(weights), _ptr(x, "x", ad, T * d),
+                                          _ptr(y, "y", ad, T * d),
+                                          _ptr(topk_ids, "topk_ids", torch.int32, T * k),
+                                          _ptr(topk_w, "topk_w", torch.float32, T * k),
+                                          _ptr(workspace, "workspace", torch.uint8),
+                                          workspace.numel() if workspace is not None else 0,
+                                          _stream(stream), arr(start_events), arr(stop_events)),
+           "moe_layer_forward_events")
+
+
+def moe_host_e4m3_encode(values) -> "numpy.ndarray":
+    import numpy as np
+    v = np.ascontiguousarray(values, dtype=np.float32)
+    out = np.empty(v.shape, dtype=np.uint8)
+    lib().moe_host_e4m3_encode(v.ctypes.data, out.ctypes.data, v.size)
+    return out

@@ -1,0 +1,363 @@
+// C ABI of libmoe: argument checks, workspace layout and kernel launches.
+// Nothing here allocates, frees or synchronises.
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+#include "internal.h"
+#include "moe.h"
+
+using namespace moe;
+
+namespace {
+
+bool is_dim(int v, int max) { return v >= MOE_DIM_ALIGN && v <= max && v % MOE_DIM_ALIGN == 0; }
+
+moe_status_t check_shape(const moe_shape_t* s) {
+  if (s == nullptr) return MOE_ERR_INVALID_ARG;
+  if (s->T < 0 || s->T > MOE_MAX_T) return MOE_ERR_INVALID_ARG;
+  if (!is_dim(s->d, MOE_MAX_D) || !is_dim(s->F, MOE_MAX_F)) return MOE_ERR_INVALID_ARG;
+  if (s->F_shared != 0 && !is_dim(s->F_shared, MOE_MAX_F)) return MOE_ERR_INVALID_ARG;
+  if (s->E < 1 || s->E > MOE_MAX_E) return MOE_ERR_INVALID_ARG;
+  if (s->k < 1 || s->k > s->E || s->k > MOE_MAX_K) return MOE_ERR_INVALID_ARG;
+  const bool fp8 = s->act_dtype == MOE_DTYPE_BF16 && s->w_dtype == MOE_DTYPE_FP8_E4M3;
+  const bool f32 = s->act_dtype == MOE_DTYPE_F32 && s->w_dtype == MOE_DTYPE_F32;
+  if (!fp8 && !f32) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+bool is_fp8(const moe_shape_t* s) { return s->w_dtype == MOE_DTYPE_FP8_E4M3; }
+
+bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+bool al256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255) == 0; }
+
+moe_status_t from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Bump allocator over a caller-provided workspace (256-byte aligned regions).
+struct Carve {
+  uint8_t* base;
+  size_t off = 0;
+  explicit Carve(void* b) : base(static_cast<uint8_t*>(b)) {}
+  template <typename T>
+  T* take(size_t bytes) {
+    T* p = reinterpret_cast<T*>(base == nullptr ? nullptr : base + off);
+    off += align_up(bytes, 256);
+    return p;
+  }
+};
+
+moe_status_t check_ffn(const moe_ffn_t* f) {
+  if (f == nullptr) return MOE_ERR_INVALID_ARG;
+  if (!is_dim(f->d, MOE_MAX_D) || !is_dim(f->F, MOE_MAX_F)) return MOE_ERR_INVALID_ARG;
+  if (f->num_groups < 1 || f->num_groups > 1023) return MOE_ERR_INVALID_ARG;
+  if (f->max_rows < 0 || f->max_rows > MOE_MAX_T * MOE_MAX_K) return MOE_ERR_INVALID_ARG;
+  if (f->src_div < 1 || f->a_rows < 0) return MOE_ERR_INVALID_ARG;
+  if (f->w_dtype != MOE_DTYPE_FP8_E4M3 && f->w_dtype != MOE_DTYPE_F32) return MOE_ERR_UNSUPPORTED;
+  if (f->max_rows == 0) return MOE_OK;
+  if (f->a_rows < 1) return MOE_ERR_INVALID_ARG;
+  if (!f->group_offsets || !f->a || !f->w13 || !f->w2 || !f->out) return MOE_ERR_INVALID_ARG;
+  if (!al16(f->a) || !al16(f->w13) || !al16(f->w2) || !al16(f->out)) return MOE_ERR_INVALID_ARG;
+  if (f->w_dtype == MOE_DTYPE_FP8_E4M3 && (!f->a_scale || !f->w13_scale || !f->w2_scale))
+    return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+FfnSet make_set(const void* w13, const float* s13, const void* w2, const float* s2,
+                const int32_t* offsets, const int32_t* row_src, int src_div, int G, int F,
+                int rows_fixed, int max_rows, void* out) {
+  FfnSet S{};
+  S.w13 = static_cast<const uint8_t*>(w13);
+  S.s13 = s13;
+  S.w2 = static_cast<const uint8_t*>(w2);
+  S.s2 = s2;
+  S.offsets = offsets;
+  S.row_src = row_src;
+  S.src_div = src_div;
+  S.G = G;
+  S.F = F;
+  S.rows_fixed = rows_fixed;
+  S.max_rows = max_rows;
+  S.out = out;
+  return S;
+}
+
+// Lays out (and, with a real base, assigns) the per-set h buffers and the tile
+// lists of one grouped-FFN call; returns the bytes used.
+size_t carve_ffn(FfnCall& c, bool fp8, Carve& cv, void** tiles) {
+  for (int i = 0; i < c.nsets; ++i) {
+    FfnSet& S = c.set[i];
+    S.h = cv.take<uint8_t>(ffn_h_bytes(S.max_rows, S.F, fp8));
+    S.h_scale = fp8 ? cv.take<float>(ffn_hs_bytes(S.max_rows, S.F)) : nullptr;
+  }
+  *tiles = fp8 ? cv.take<uint8_t>(ffn_tiles_ws_bytes(c)) : nullptr;
+  return cv.off;
+}
+
+// The layer's workspace; with base == nullptr only the size is computed.
+struct LayerWs {
+  int32_t* ids;
+  float* w;
+  uint8_t* xq;
+  float* xs;
+  int32_t* perm;
+  int32_t* offsets;
+  int32_t* sorted_pair;
+  int32_t* pair_to_row;
+  void* expert_out;
+  void* shared_out;
+  void* tiles;
+  size_t bytes;
+};
+
+LayerWs layer_ws(const moe_shape_t* s, void* base, FfnCall* call) {
+  const bool fp8 = is_fp8(s);
+  const size_t T = s->T, k = s->k, d = s->d, E = s->E;
+  const size_t ob = fp8 ? 2 : 4;
+  Carve cv(base);
+  LayerWs L{};
+  L.ids = cv.take<int32_t>(T * k * 4);
+  L.w = cv.take<float>(T * k * 4);
+  L.xq = fp8 ? cv.take<uint8_t>(T * d) : nullptr;
+  L.xs = fp8 ? cv.take<float>(T * 4) : nullptr;
+  L.perm = cv.take<int32_t>(permute_ws_bytes(s->T, s->E));
+  L.offsets = cv.take<int32_t>((E + 1) * 4);
+  L.sorted_pair = cv.take<int32_t>(T * k * 4);
+  L.pair_to_row = cv.take<int32_t>(T * k * 4);
+  L.expert_out = cv.take<uint8_t>(T * k * d * ob);
+  L.shared_out = s->F_shared > 0 ? cv.take<uint8_t>(T * d * ob) : nullptr;
+  FfnCall c{};
+  c.d = s->d;
+  c.nsets = s->F_shared > 0 ? 2 : 1;
+  c.set[0] = make_set(nullptr, nullptr, nullptr, nullptr, L.offsets, L.sorted_pair, s->k, s->E,
+                      s->F, 0, s->T * s->k, L.expert_out);
+  if (c.nsets > 1)
+    c.set[1] = make_set(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 1, 1, s->F_shared,
+                        s->T, s->T, L.shared_out);
+  carve_ffn(c, fp8, cv, &L.tiles);
+  L.bytes = cv.off;
+  if (call) *call = c;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_string(int32_t status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported dtype combination";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+moe_status_t moe_check_shape(const moe_shape_t* shape) { return check_shape(shape); }
+
+moe_status_t moe_layer_workspace_size(const moe_shape_t* shape, size_t* bytes) {
+  const moe_status_t st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
+  *bytes = layer_ws(shape, nullptr, nullptr).bytes;
+  return MOE_OK;
+}
+
+moe_status_t moe_permute_workspace_size(const moe_shape_t* shape, size_t* bytes) {
+  const moe_status_t st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
+  *bytes = permute_ws_bytes(shape->T, shape->E);
+  return MOE_OK;
+}
+
+static FfnCall ffn_call(const moe_ffn_t* f) {
+  FfnCall c{};
+  c.d = f->d;
+  c.a_rows = f->a_rows;
+  c.a = f->a;
+  c.a_scale = f->a_scale;
+  c.nsets = 1;
+  c.set[0] = make_set(f->w13, f->w13_scale, f->w2, f->w2_scale, f->group_offsets, f->row_src,
+                      f->src_div, f->num_groups, f->F, 0, f->max_rows, f->out);
+  return c;
+}
+
+moe_status_t moe_grouped_ffn_workspace_size(const moe_ffn_t* ffn, size_t* bytes) {
+  const moe_status_t st = check_ffn(ffn);
+  if (st != MOE_OK) return st;
+  if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
+  FfnCall c = ffn_call(ffn);
+  Carve cv(nullptr);
+  void* tiles;
+  *bytes = carve_ffn(c, ffn->w_dtype == MOE_DTYPE_FP8_E4M3, cv, &tiles);
+  return MOE_OK;
+}
+
+moe_status_t moe_route_topk(const moe_shape_t* s, const void* x, const void* w_router,
+                            const float* router_bias, int32_t* topk_ids, float* topk_w,
+                            uint8_t* xq, float* x_scale, void* stream) {
+  moe_status_t st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (s->T == 0) return MOE_OK;
+  if (!x || !w_router || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+  if (!al16(x) || !al16(w_router)) return MOE_ERR_INVALID_ARG;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (is_fp8(s)) {
+    if (!xq || !x_scale || !al16(xq)) return MOE_ERR_INVALID_ARG;
+    return from_hip(launch_route_bf16(static_cast<const uint16_t*>(x),
+                                      static_cast<const uint16_t*>(w_router), router_bias, s->T,
+                                      s->d, s->E, s->k, topk_ids, topk_w, xq, x_scale, hs));
+  }
+  return from_hip(launch_route_f32(static_cast<const float*>(x),
+                                   static_cast<const float*>(w_router), router_bias, s->T, s->d,
+                                   s->E, s->k, topk_ids, topk_w, hs));
+}
+
+moe_status_t moe_permute(const moe_shape_t* s, const int32_t* topk_ids, int32_t* offsets,
+                         int32_t* sorted_pair, int32_t* pair_to_row, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  moe_status_t st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (s->T == 0) return MOE_OK;
+  if (!topk_ids || !offsets || !sorted_pair || !pair_to_row) return MOE_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < permute_ws_bytes(s->T, s->E) || !al256(workspace))
+    return MOE_ERR_WORKSPACE;
+  return from_hip(launch_permute(topk_ids, s->T, s->E, s->k, offsets, sorted_pair, pair_to_row,
+                                 workspace, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_grouped_ffn(const moe_ffn_t* f, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  moe_status_t st = check_ffn(f);
+  if (st != MOE_OK) return st;
+  if (f->max_rows == 0) return MOE_OK;
+  const bool fp8 = f->w_dtype == MOE_DTYPE_FP8_E4M3;
+  FfnCall c = ffn_call(f);
+  {
+    Carve probe(nullptr);
+    void* t;
+    const size_t need = carve_ffn(c, fp8, probe, &t);
+    if (!workspace || workspace_bytes < need || !al256(workspace)) return MOE_ERR_WORKSPACE;
+  }
+  Carve cv(workspace);
+  void* tiles = nullptr;
+  carve_ffn(c, fp8, cv, &tiles);
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (fp8) {
+    const int hint = ceil_div(f->max_rows, f->num_groups);
+    return from_hip(launch_grouped_ffn_fp8(c, tiles, hint, hs));
+  }
+  return from_hip(launch_grouped_ffn_f32(c, hs));
+}
+
+moe_status_t moe_combine(const moe_shape_t* s, const void* expert_out,
+                         const int32_t* pair_to_row, const float* topk_w,
+                         const void* shared_out, void* y, void* stream) {
+  moe_status_t st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (s->T == 0) return MOE_OK;
+  if (!expert_out || !pair_to_row || !topk_w || !y) return MOE_ERR_INVALID_ARG;
+  if (!al16(expert_out) || !al16(y) || (shared_out && !al16(shared_out))) return MOE_ERR_INVALID_ARG;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (is_fp8(s))
+    return from_hip(launch_combine_bf16(static_cast<const uint16_t*>(expert_out), pair_to_row,
+                                        topk_w, static_cast<const uint16_t*>(shared_out),
+                                        static_cast<uint16_t*>(y), s->T, s->d, s->k, hs));
+  return from_hip(launch_combine_f32(static_cast<const float*>(expert_out), pair_to_row, topk_w,
+                                     static_cast<const float*>(shared_out),
+                                     static_cast<float*>(y), s->T, s->d, s->k, hs));
+}
+
+moe_status_t moe_layer_forward(const moe_shape_t* s, const moe_weights_t* wt, const void* x,
+                               void* y, int32_t* topk_ids, float* topk_w, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return moe_layer_forward_events(s, wt, x, y, topk_ids, topk_w, workspace, workspace_bytes,
+                                  stream, nullptr, nullptr);
+}
+
+moe_status_t moe_layer_forward_events(const moe_shape_t* s, const moe_weights_t* wt,
+                                      const void* x, void* y, int32_t* topk_ids, float* topk_w,
+                                      void* workspace, size_t workspace_bytes, void* stream,
+                                      void* const* start_events, void* const* stop_events) {
+  StepEvents ev;
+  ev.start = start_events;
+  ev.stop = stop_events;
+  moe_status_t st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (s->T == 0) return MOE_OK;
+  if (!wt || !x || !y || !wt->w_router || !wt->w13 || !wt->w2) return MOE_ERR_INVALID_ARG;
+  if (!al16(x) || !al16(y) || !al16(wt->w_router) || !al16(wt->w13) || !al16(wt->w2))
+    return MOE_ERR_INVALID_ARG;
+  if (s->F_shared > 0 && (!al16(wt->ws13) || !al16(wt->ws2))) return MOE_ERR_INVALID_ARG;
+  const bool fp8 = is_fp8(s);
+  if (fp8 && (!wt->w13_scale || !wt->w2_scale)) return MOE_ERR_INVALID_ARG;
+  if (s->F_shared > 0 && (!wt->ws13 || !wt->ws2 || (fp8 && (!wt->ws13_scale || !wt->ws2_scale))))
+    return MOE_ERR_INVALID_ARG;
+  const size_t need = layer_ws(s, nullptr, nullptr).bytes;
+  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255))
+    return MOE_ERR_WORKSPACE;
+
+  FfnCall c;
+  LayerWs L = layer_ws(s, workspace, &c);
+  int32_t* ids = topk_ids ? topk_ids : L.ids;
+  float* w = topk_w ? topk_w : L.w;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+
+  hipError_t e;
+  ev.mark(true, MOE_STEP_ROUTE, hs);
+  if (fp8)
+    e = launch_route_bf16(static_cast<const uint16_t*>(x),
+                          static_cast<const uint16_t*>(wt->w_router), wt->router_bias, s->T, s->d,
+                          s->E, s->k, ids, w, L.xq, L.xs, hs);
+  else
+    e = launch_route_f32(static_cast<const float*>(x), static_cast<const float*>(wt->w_router),
+                         wt->router_bias, s->T, s->d, s->E, s->k, ids, w, hs);
+  ev.mark(false, MOE_STEP_ROUTE, hs);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  ev.mark(true, MOE_STEP_PERMUTE, hs);
+  e = launch_permute(ids, s->T, s->E, s->k, L.offsets, L.sorted_pair, L.pair_to_row, L.perm, hs);
+  ev.mark(false, MOE_STEP_PERMUTE, hs);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+
+  c.a_rows = s->T;
+  c.a = fp8 ? static_cast<const void*>(L.xq) : x;
+  c.a_scale = L.xs;
+  FfnSet& R = c.set[0];
+  R.w13 = static_cast<const uint8_t*>(wt->w13);
+  R.s13 = wt->w13_scale;
+  R.w2 = static_cast<const uint8_t*>(wt->w2);
+  R.s2 = wt->w2_scale;
+  if (c.nsets > 1) {
+    FfnSet& Sh = c.set[1];
+    Sh.w13 = static_cast<const uint8_t*>(wt->ws13);
+    Sh.s13 = wt->ws13_scale;
+    Sh.w2 = static_cast<const uint8_t*>(wt->ws2);
+    Sh.s2 = wt->ws2_scale;
+  }
+  if (fp8)
+    e = launch_grouped_ffn_fp8(c, L.tiles, ceil_div(s->T * s->k, s->E), hs, ev);
+  else
+    e = launch_grouped_ffn_f32(c, hs, ev);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+
+  ev.mark(true, MOE_STEP_COMBINE, hs);
+  if (fp8)
+    e = launch_combine_bf16(static_cast<const uint16_t*>(L.expert_out), L.pair_to_row, w,
+                            static_cast<const uint16_t*>(L.shared_out), static_cast<uint16_t*>(y),
+                            s->T, s->d, s->k, hs);
+  else
+    e = launch_combine_f32(static_cast<const float*>(L.expert_out), L.pair_to_row, w,
+                           static_cast<const float*>(L.shared_out), static_cast<float*>(y), s->T,
+                           s->d, s->k, hs);
+  ev.mark(false, MOE_STEP_COMBINE, hs);
+  return from_hip(e);
+}
+
+void moe_host_e4m3_encode(const float* in, uint8_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = moe::e4m3_encode(in[i]);
+}
+
+}  // extern "C"

@@ -1,0 +1,591 @@
+// Grouped SwiGLU expert FFN: the routed experts' grouped GEMMs and the shared
+// expert as one more group, as the NVIDIA Sarvam blog runs routed experts as
+// grouped GEMM kernels with resident expert weights (section "Performance
+// challenges") and the shared expert as a separate computation (Table 1).
+//
+// FP8 path, per group g, grouped row r with activation row s:
+//   gate/up:  gu = (a[s] . w13[g][n]) * a_scale[s] * w13_scale[g][n]   (E4M3 x E4M3 MFMA)
+//             h  = silu(gu[n]) * gu[F + n], quantised per (row, 128 columns)
+//   down:     out[r][m] = w2_scale[g][m] * sum_b s_h[r][b] * (hq[r][b] . w2[g][m][b])
+//
+// Work is a device-built list of tiles (group, up to BM rows, one N tile), so
+// empty groups cost nothing and the host never reads routing results. Block i
+// of a launch takes list entry (i % 8) * ceil(n / 8) + i / 8: consecutive
+// entries -- the M tiles of one (group, N tile), then the next N tile of the
+// same group -- run on the same XCD (blocks are dealt to the 8 XCDs in turn),
+// so a weight tile read by several M tiles, and a group's activation rows, are
+// served from that XCD's L2.
+#include "common.h"
+#include "internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kBK = 128;      // K bytes per MFMA step (FP8 16x16x128)
+constexpr int kHN = 128;      // h columns per gate/up tile = one h quantisation block
+constexpr int kDownBN = 256;  // output channels per down tile
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * kWave;
+constexpr int kMaxGroups = 1024;
+constexpr int kXcds = 8;
+constexpr int kBuildThreads = 256;
+
+struct TileEntry {
+  int row0;   // first row of the tile, in the set's grouped row space
+  int nrows;  // rows in this tile, 1..BM
+  int gid;    // (set << 16) | group
+  int ntile;  // N tile index
+};
+
+struct TileHeader {
+  int n_up;
+  int n_down;
+  int pad[62];
+};
+
+__host__ __device__ inline int up_ntiles(int F) { return F / kHN; }
+__host__ __device__ inline int down_ntiles(int d) { return ceil_div(d, kDownBN); }
+
+size_t tiles_cap(const FfnCall& c, int bm, bool up) {
+  size_t n = 0;
+  for (int s = 0; s < c.nsets; ++s) {
+    const FfnSet& S = c.set[s];
+    const size_t mt = (size_t)ceil_div(S.max_rows, bm) + (size_t)S.G;
+    n += mt * (size_t)(up ? up_ntiles(S.F) : down_ntiles(c.d));
+  }
+  return n;
+}
+
+// ---------------------------------------------------------------------------
+// Tile-list builder: one workgroup.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kBuildThreads) void build_tiles_kernel(FfnCall c, int bm,
+                                                                    TileHeader* hdr,
+                                                                    TileEntry* up,
+                                                                    TileEntry* down, int cap_up,
+                                                                    int cap_dn) {
+  __shared__ int g_row0[kMaxGroups], g_rows[kMaxGroups], g_set[kMaxGroups];
+  __shared__ int pre_up[kMaxGroups + 1], pre_dn[kMaxGroups + 1];
+  __shared__ int part_up[kBuildThreads], part_dn[kBuildThreads];
+  const int tid = threadIdx.x;
+  const int G0 = c.set[0].G;
+  const int NG = G0 + (c.nsets > 1 ? c.set[1].G : 0);
+  const int dnt = down_ntiles(c.d);
+
+  // per group: rows and tile counts
+  for (int i = tid; i < NG; i += kBuildThreads) {
+    const int s = (i < G0) ? 0 : 1;
+    const int g = (s == 0) ? i : i - G0;
+    const FfnSet S = (s == 0) ? c.set[0] : c.set[1];
+    // clamp to [0, max_rows] so malformed offsets cannot send a tile outside
+    // the buffers (rows of such groups are then simply not computed)
+    int r0 = 0, r1 = min(S.rows_fixed, S.max_rows);
+    if (S.offsets != nullptr) {
+      r0 = min(max(S.offsets[g], 0), S.max_rows);
+      r1 = min(max(S.offsets[g + 1], r0), S.max_rows);
+    }
+    const int rows = r1 - r0;
+    g_row0[i] = r0;
+    g_rows[i] = rows;
+    g_set[i] = s;
+  }
+  __syncthreads();
+  // exclusive scans of the per-group tile counts (each thread owns a run of groups)
+  const int per = ceil_div(NG, kBuildThreads);
+  const int lo = min(NG, tid * per), hi = min(NG, lo + per);
+  int su = 0, sd = 0;
+  for (int i = lo; i < hi; ++i) {
+    const int mt = ceil_div(g_rows[i], bm);
+    su += mt * up_ntiles(g_set[i] == 0 ? c.set[0].F : c.set[1].F);
+    sd += mt * dnt;
+  }
+  part_up[tid] = su;
+  part_dn[tid] = sd;
+  __syncthreads();
+  for (int o = 1; o < kBuildThreads; o <<= 1) {
+    const int vu = (tid >= o) ? part_up[tid - o] : 0;
+    const int vd = (tid >= o) ? part_dn[tid - o] : 0;
+    __syncthreads();
+    part_up[tid] += vu;
+    part_dn[tid] += vd;
+    __syncthreads();
+  }
+  su = part_up[tid] - su;
+  sd = part_dn[tid] - sd;
+  for (int i = lo; i < hi; ++i) {
+    pre_up[i] = su;
+    pre_dn[i] = sd;
+    const int mt = ceil_div(g_rows[i], bm);
+    su += mt * up_ntiles(g_set[i] == 0 ? c.set[0].F : c.set[1].F);
+    sd += mt * dnt;
+  }
+  if (tid == kBuildThreads - 1) {
+    pre_up[NG] = part_up[kBuildThreads - 1];
+    pre_dn[NG] = part_dn[kBuildThreads - 1];
+  }
+  __syncthreads();
+  // overlapping (malformed) offsets could need more entries than the list
+  // holds: keep only what fits
+  const int n_up = min(pre_up[NG], cap_up), n_dn = min(pre_dn[NG], cap_dn);
+
+  // entries, spread over all threads: M tiles of one (group, N tile) adjacent
+  for (int w = tid; w < n_up + n_dn; w += kBuildThreads) {
+    const bool is_up = w < n_up;
+    const int idx = is_up ? w : w - n_up;
+    const int* pre = is_up ? pre_up : pre_dn;
+    int a = 0, b = NG;  // largest group i with pre[i] <= idx
+    while (b - a > 1) {
+      const int m = (a + b) >> 1;
+      if (pre[m] <= idx) a = m; else b = m;
+    }
+    // skip empty groups sharing the same prefix
+    while (a + 1 < NG && pre[a + 1] <= idx) ++a;
+    const int mt = ceil_div(g_rows[a], bm);
+    const int loc = idx - pre[a];
+    const int m = loc % mt, nt = loc / mt;
+    const int s = g_set[a];
+    const int g = (s == 0) ? a : a - G0;
+    TileEntry e;
+    e.row0 = g_row0[a] + m * bm;
+    e.nrows = min(bm, g_rows[a] - m * bm);
+    e.gid = (s << 16) | g;
+    e.ntile = nt;
+    if (is_up) up[idx] = e; else down[idx] = e;
+  }
+  if (tid == 0) {
+    hdr->n_up = n_up;
+    hdr->n_down = n_dn;
+  }
+}
+
+// Block -> list entry, XCD-contiguous. Returns false for blocks with no work.
+__device__ inline bool pick_tile(const int total, int& w) {
+  const int per = ceil_div(total, kXcds);
+  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+  w = xcd * per + slot;
+  return slot < per && w < total;
+}
+
+__device__ inline v8i pack8(const uint4& lo, const uint4& hi) {
+  return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+// Swizzled offset of 16-byte chunk c of row r in a [rows][128 B] LDS tile.
+__device__ inline int swz(int r, int c) { return r * kBK + ((c ^ (r & 7)) << 4); }
+
+// A fragment of M subtile i from an LDS tile: row (i*16 + lane%16), bytes
+// [(lane/16)*16, +16) and [64 + (lane/16)*16, +16) of the 128-byte K step.
+__device__ inline v8i lds_afrag(const uint8_t* tile, int i, int lane) {
+  const int r = i * 16 + (lane & 15);
+  const uint4 lo = *reinterpret_cast<const uint4*>(tile + swz(r, lane >> 4));
+  const uint4 hi = *reinterpret_cast<const uint4*>(tile + swz(r, 4 + (lane >> 4)));
+  return pack8(lo, hi);
+}
+
+// B fragment: 16 weight rows, lane reads row (lane%16) at the same byte slices.
+__device__ inline v8i glb_bfrag(const uint8_t* p) {
+  const uint4 lo = *reinterpret_cast<const uint4*>(p);
+  const uint4 hi = *reinterpret_cast<const uint4*>(p + 64);
+  return pack8(lo, hi);
+}
+
+// ---------------------------------------------------------------------------
+// Gate/up GEMM + SwiGLU + h quantisation. Tile: BM rows x 128 h columns
+// (128 gate + 128 up weight rows); wave w owns h columns [32w, 32w + 32).
+// A (activation rows, gathered) is staged through LDS, double buffered;
+// each wave streams its own weight rows straight into registers.
+// ---------------------------------------------------------------------------
+template <int BM>
+__global__ __launch_bounds__(kThreads) void gateup_fp8_kernel(FfnCall c,
+                                                              const TileHeader* __restrict__ hdr,
+                                                              const TileEntry* __restrict__ list) {
+  constexpr int MS = BM / 16;
+  constexpr int WN = kHN / kWaves;  // 32 h columns per wave
+  constexpr int NS = WN / 16;       // 2 h subtiles per wave
+  constexpr int NB = 2 * NS;        // weight subtiles per wave (gate, up)
+  constexpr int CH = BM * (kBK / 16);
+  constexpr int CPT = (CH + kThreads - 1) / kThreads;
+
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * kBK];
+  __shared__ float sxl[BM];
+  __shared__ float red[kWaves][BM];
+
+  int w;
+  if (!pick_tile(hdr->n_up, w)) return;
+  const TileEntry te = list[w];
+  const int sid = te.gid >> 16, g = te.gid & 0xffff;
+  const FfnSet S = (sid == 0) ? c.set[0] : c.set[1];
+  const int d = c.d, F = S.F;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const uint8_t* a = static_cast<const uint8_t*>(c.a);
+
+  // activation rows of this tile (gathered), their scales into LDS
+  const uint8_t* a_src[CPT];
+  int a_dst[CPT];
+  bool a_ok[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int ch = tid + i * kThreads;
+    a_ok[i] = ch < CH;
+    const int r = min(ch >> 3, BM - 1), c16 = ch & 7;
+    const int grow = te.row0 + min(r, te.nrows - 1);
+    const int src = min(max(S.row_src ? S.row_src[grow] / S.src_div : grow, 0), c.a_rows - 1);
+    a_src[i] = a + (size_t)src * d + c16 * 16;
+    a_dst[i] = swz(r, c16);
+    if (a_ok[i] && c16 == 0) sxl[r] = c.a_scale[src];
+  }
+  // weight rows of this wave
+  const uint8_t* w13 = S.w13 + (size_t)g * 2 * F * d;
+  const uint8_t* b_src[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int hc = te.ntile * kHN + wave * WN + (j % NS) * 16 + (lane & 15);
+    const int wrow = (j < NS) ? hc : F + hc;
+    b_src[j] = w13 + (size_t)wrow * d + (lane >> 4) * 16;
+  }
+
+  v4f acc[MS][NB];
+#pragma unroll
+  for (int i = 0; i < MS; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  uint4 a_stage[CPT];
+  v8i bcur[NB], bnext[NB];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i)
+    if (a_ok[i]) a_stage[i] = *reinterpret_cast<const uint4*>(a_src[i]);
+#pragma unroll
+  for (int j = 0; j < NB; ++j) bcur[j] = glb_bfrag(b_src[j]);
+#pragma unroll
+  for (int i = 0; i < CPT; ++i)
+    if (a_ok[i]) *reinterpret_cast<uint4*>(&lds_a[0][a_dst[i]]) = a_stage[i];
+  __syncthreads();
+
+  const int KT = d / kBK;
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
+    const bool more = kt + 1 < KT;
+    if (more) {
+      const int k0 = (kt + 1) * kBK;
+#pragma unroll
+      for (int i = 0; i < CPT; ++i)
+        if (a_ok[i]) a_stage[i] = *reinterpret_cast<const uint4*>(a_src[i] + k0);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) bnext[j] = glb_bfrag(b_src[j] + k0);
+    }
+#pragma unroll
+    for (int i = 0; i < MS; ++i) {
+      const v8i af = lds_afrag(lds_a[cur], i, lane);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) acc[i][j] = mfma_fp8_16x16x128(af, bcur[j], acc[i][j]);
+    }
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < CPT; ++i)
+        if (a_ok[i]) *reinterpret_cast<uint4*>(&lds_a[cur ^ 1][a_dst[i]]) = a_stage[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NB; ++j) bcur[j] = bnext[j];
+  }
+
+  // ---- epilogue: scales, SwiGLU, per-(row, 128-col) amax ----
+  const float* s13 = S.s13 + (size_t)g * 2 * F;
+  float sg[NS], su[NS];
+#pragma unroll
+  for (int jj = 0; jj < NS; ++jj) {
+    const int hc = te.ntile * kHN + wave * WN + jj * 16 + (lane & 15);
+    sg[jj] = s13[hc];
+    su[jj] = s13[F + hc];
+  }
+#pragma unroll
+  for (int i = 0; i < MS; ++i) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = i * 16 + 4 * (lane >> 4) + q;
+      const float sx = sxl[r];
+      float m = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < NS; ++jj) {
+        const float gv = acc[i][jj][q] * sx * sg[jj];
+        const float uv = acc[i][NS + jj][q] * sx * su[jj];
+        const float h = gv / (1.0f + __expf(-gv)) * uv;
+        acc[i][jj][q] = h;
+        m = fmaxf(m, fabsf(h));
+      }
+      m = max16(m);
+      if ((lane & 15) == 0) red[wave][r] = m;
+    }
+  }
+  __syncthreads();
+  const int hblocks = F / kHN;
+#pragma unroll
+  for (int i = 0; i < MS; ++i) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = i * 16 + 4 * (lane >> 4) + q;
+      if (r >= te.nrows) continue;
+      float am = red[0][r];
+#pragma unroll
+      for (int ww = 1; ww < kWaves; ++ww) am = fmaxf(am, red[ww][r]);
+      const float s = (am > 0.f) ? __fdiv_rn(am, kE4M3Max) : 1.0f;
+      const size_t grow = (size_t)(te.row0 + r);
+      uint8_t* hrow = S.h + grow * F;
+#pragma unroll
+      for (int jj = 0; jj < NS; ++jj) {
+        const int hc = te.ntile * kHN + wave * WN + jj * 16 + (lane & 15);
+        hrow[hc] = e4m3_encode(__fdiv_rn(acc[i][jj][q], s));
+      }
+      if (wave == 0 && (lane & 15) == 0) S.h_scale[grow * hblocks + te.ntile] = s;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Down GEMM with per-(row, 128-K block) h scales. Tile: BM rows x 256 output
+// channels; wave w owns channels [64w, 64w + 64). Each 128-wide K step is one
+// h block: its MFMA partial is scaled by s_h[row][block] and accumulated.
+// ---------------------------------------------------------------------------
+template <int BM>
+__global__ __launch_bounds__(kThreads) void down_fp8_kernel(FfnCall c,
+                                                            const TileHeader* __restrict__ hdr,
+                                                            const TileEntry* __restrict__ list) {
+  constexpr int MS = BM / 16;
+  constexpr int NB = 4;  // 16-channel subtiles per wave
+  constexpr int CH = BM * (kBK / 16);
+  constexpr int CPT = (CH + kThreads - 1) / kThreads;
+
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * kBK];
+  __shared__ float hsl[2][BM];
+
+  int w;
+  if (!pick_tile(hdr->n_down, w)) return;
+  const TileEntry te = list[w];
+  const int sid = te.gid >> 16, g = te.gid & 0xffff;
+  const FfnSet S = (sid == 0) ? c.set[0] : c.set[1];
+  const int d = c.d, F = S.F, hblocks = F / kHN;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+
+  const uint8_t* a_src[CPT];
+  int a_dst[CPT];
+  bool a_ok[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int ch = tid + i * kThreads;
+    a_ok[i] = ch < CH;
+    const int r = min(ch >> 3, BM - 1), c16 = ch & 7;
+    const int grow = te.row0 + min(r, te.nrows - 1);
+    a_src[i] = S.h + (size_t)grow * F + c16 * 16;
+    a_dst[i] = swz(r, c16);
+  }
+  // per-row h scales: thread r < BM fetches s_h[row r][kt]
+  const float* hs_src = S.h_scale + (size_t)(te.row0 + min(tid, te.nrows - 1)) * hblocks;
+
+  const uint8_t* w2 = S.w2 + (size_t)g * d * F;
+  const uint8_t* b_src[NB];
+  int mcol[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    mcol[j] = te.ntile * kDownBN + wave * (NB * 16) + j * 16 + (lane & 15);
+    b_src[j] = w2 + (size_t)min(mcol[j], d - 1) * F + (lane >> 4) * 16;
+  }
+
+  v4f acc[MS][NB];
+#pragma unroll
+  for (int i = 0; i < MS; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  uint4 a_stage[CPT];
+  float hs_stage = 0.f;
+  v8i bcur[NB], bnext[NB];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i)
+    if (a_ok[i]) a_stage[i] = *reinterpret_cast<const uint4*>(a_src[i]);
+  if (tid < BM) hs_stage = hs_src[0];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) bcur[j] = glb_bfrag(b_src[j]);
+#pragma unroll
+  for (int i = 0; i < CPT; ++i)
+    if (a_ok[i]) *reinterpret_cast<uint4*>(&lds_a[0][a_dst[i]]) = a_stage[i];
+  if (tid < BM) hsl[0][tid] = hs_stage;
+  __syncthreads();
+
+  const int KT = F / kBK;
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
+    const bool more = kt + 1 < KT;
+    if (more) {
+      const int k0 = (kt + 1) * kBK;
+#pragma unroll
+      for (int i = 0; i < CPT; ++i)
+        if (a_ok[i]) a_stage[i] = *reinterpret_cast<const uint4*>(a_src[i] + k0);
+      if (tid < BM) hs_stage = hs_src[kt + 1];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) bnext[j] = glb_bfrag(b_src[j] + k0);
+    }
+#pragma unroll
+    for (int i = 0; i < MS; ++i) {
+      const v8i af = lds_afrag(lds_a[cur], i, lane);
+      v4f part[NB];
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        part[j] = mfma_fp8_16x16x128(af, bcur[j], v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float hs = hsl[cur][i * 16 + 4 * (lane >> 4) + q];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j][q] = fmaf(part[j][q], hs, acc[i][j][q]);
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < CPT; ++i)
+        if (a_ok[i]) *reinterpret_cast<uint4*>(&lds_a[cur ^ 1][a_dst[i]]) = a_stage[i];
+      if (tid < BM) hsl[cur ^ 1][tid] = hs_stage;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NB; ++j) bcur[j] = bnext[j];
+  }
+
+  // ---- epilogue: channel scale, bf16 ----
+  const float* s2 = S.s2 + (size_t)g * d;
+  uint16_t* out = static_cast<uint16_t*>(S.out);
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    if (mcol[j] >= d) continue;
+    const float sc = s2[mcol[j]];
+#pragma unroll
+    for (int i = 0; i < MS; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = i * 16 + 4 * (lane >> 4) + q;
+        if (r < te.nrows)
+          out[(size_t)(te.row0 + r) * d + mcol[j]] = f32_to_bf16(acc[i][j][q] * sc);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// float32 path: one thread per output element, plain sequential dot products.
+// ---------------------------------------------------------------------------
+__device__ inline int find_group(const FfnSet& S, int r) {
+  if (S.offsets == nullptr) return (r < min(S.rows_fixed, S.max_rows)) ? 0 : -1;
+  if (r >= S.offsets[S.G]) return -1;
+  int a = 0, b = S.G;  // offsets[a] <= r < offsets[b]
+  while (b - a > 1) {
+    const int m = (a + b) >> 1;
+    if (S.offsets[m] <= r) a = m; else b = m;
+  }
+  return a;
+}
+
+__global__ __launch_bounds__(256) void gateup_f32_kernel(FfnCall c, int sid) {
+  const FfnSet S = (sid == 0) ? c.set[0] : c.set[1];
+  const int F = S.F, d = c.d;
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (size_t)S.max_rows * F) return;
+  const int r = (int)(idx / F), n = (int)(idx % F);
+  const int g = find_group(S, r);
+  if (g < 0) return;
+  const int src = min(max(S.row_src ? S.row_src[r] / S.src_div : r, 0), c.a_rows - 1);
+  const float* x = static_cast<const float*>(c.a) + (size_t)src * d;
+  const float* w = reinterpret_cast<const float*>(S.w13) + (size_t)g * 2 * F * d;
+  const float* wg = w + (size_t)n * d;
+  const float* wu = w + (size_t)(F + n) * d;
+  float gv = 0.f, uv = 0.f;
+  for (int i = 0; i < d; ++i) {
+    gv = fmaf(x[i], wg[i], gv);
+    uv = fmaf(x[i], wu[i], uv);
+  }
+  reinterpret_cast<float*>(S.h)[(size_t)r * F + n] = gv / (1.0f + expf(-gv)) * uv;
+}
+
+__global__ __launch_bounds__(256) void down_f32_kernel(FfnCall c, int sid) {
+  const FfnSet S = (sid == 0) ? c.set[0] : c.set[1];
+  const int F = S.F, d = c.d;
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (size_t)S.max_rows * d) return;
+  const int r = (int)(idx / d), m = (int)(idx % d);
+  const int g = find_group(S, r);
+  if (g < 0) return;
+  const float* h = reinterpret_cast<const float*>(S.h) + (size_t)r * F;
+  const float* w = reinterpret_cast<const float*>(S.w2) + (size_t)g * d * F + (size_t)m * F;
+  float acc = 0.f;
+  for (int n = 0; n < F; ++n) acc = fmaf(h[n], w[n], acc);
+  static_cast<float*>(S.out)[(size_t)r * d + m] = acc;
+}
+
+template <int BM>
+hipError_t launch_fp8_bm(const FfnCall& c, TileHeader* hdr, TileEntry* up, TileEntry* dn,
+                         hipStream_t s, const StepEvents& ev) {
+  const size_t cap_u = tiles_cap(c, BM, true), cap_d = tiles_cap(c, BM, false);
+  ev.mark(true, MOE_STEP_TILES, s);
+  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(kBuildThreads), 0, s, c, BM, hdr, up, dn,
+                     (int)cap_u, (int)cap_d);
+  ev.mark(false, MOE_STEP_TILES, s);
+  const size_t cu = align_up(cap_u, kXcds);
+  const size_t cd = align_up(cap_d, kXcds);
+  ev.mark(true, MOE_STEP_GATE_UP, s);
+  if (cu > 0) hipLaunchKernelGGL(gateup_fp8_kernel<BM>, dim3((unsigned)cu), dim3(kThreads), 0, s, c, hdr, up);
+  ev.mark(false, MOE_STEP_GATE_UP, s);
+  ev.mark(true, MOE_STEP_DOWN, s);
+  if (cd > 0) hipLaunchKernelGGL(down_fp8_kernel<BM>, dim3((unsigned)cd), dim3(kThreads), 0, s, c, hdr, dn);
+  ev.mark(false, MOE_STEP_DOWN, s);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t ffn_tiles_ws_bytes(const FfnCall& c) {
+  // capacity for the smallest tile height (the largest list)
+  return align_up(sizeof(TileHeader) + (tiles_cap(c, 16, true) + tiles_cap(c, 16, false)) *
+                                            sizeof(TileEntry),
+                  256);
+}
+
+size_t ffn_h_bytes(int max_rows, int F, bool fp8) {
+  return align_up((size_t)max_rows * F * (fp8 ? 1 : sizeof(float)), 256);
+}
+
+size_t ffn_hs_bytes(int max_rows, int F) {
+  return align_up((size_t)max_rows * (F / kHN) * sizeof(float), 256);
+}
+
+hipError_t launch_grouped_ffn_fp8(const FfnCall& c, void* tiles_ws, int rows_hint, hipStream_t s,
+                                  const StepEvents& ev) {
+  TileHeader* hdr = static_cast<TileHeader*>(tiles_ws);
+  TileEntry* up = reinterpret_cast<TileEntry*>(hdr + 1);
+  const size_t cap_up16 = tiles_cap(c, 16, true);
+  TileEntry* dn = up + cap_up16;
+  if (rows_hint <= 24) return launch_fp8_bm<16>(c, hdr, up, dn, s, ev);
+  if (rows_hint <= 48) return launch_fp8_bm<32>(c, hdr, up, dn, s, ev);
+  if (rows_hint <= 96) return launch_fp8_bm<64>(c, hdr, up, dn, s, ev);
+  return launch_fp8_bm<128>(c, hdr, up, dn, s, ev);
+}
+
+hipError_t launch_grouped_ffn_f32(const FfnCall& c, hipStream_t s, const StepEvents& ev) {
+  ev.mark(true, MOE_STEP_GATE_UP, s);
+  for (int sid = 0; sid < c.nsets; ++sid) {
+    const FfnSet& S = c.set[sid];
+    const size_t nu = (size_t)S.max_rows * S.F;
+    if (nu > 0)
+      hipLaunchKernelGGL(gateup_f32_kernel, dim3((unsigned)((nu + 255) / 256)), dim3(256), 0, s, c, sid);
+  }
+  ev.mark(false, MOE_STEP_GATE_UP, s);
+  ev.mark(true, MOE_STEP_DOWN, s);
+  for (int sid = 0; sid < c.nsets; ++sid) {
+    const FfnSet& S = c.set[sid];
+    const size_t nd = (size_t)S.max_rows * c.d;
+    if (nd > 0)
+      hipLaunchKernelGGL(down_f32_kernel, dim3((unsigned)((nd + 255) / 256)), dim3(256), 0, s, c, sid);
+  }
+  ev.mark(false, MOE_STEP_DOWN, s);
+  return hipGetLastError();
+}
+
+}  // namespace moe

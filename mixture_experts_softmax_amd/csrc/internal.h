@@ -1,0 +1,88 @@
+// Internal launch interface between the C ABI layer (api.hip) and the kernel
+// files. Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Tokens per router workgroup and per permutation tile.
+constexpr int kRouteTokens = 16;
+constexpr int kPermTile = 64;
+
+// ----- router ---------------------------------------------------------------
+hipError_t launch_route_bf16(const uint16_t* x, const uint16_t* w_router, const float* bias,
+                             int T, int d, int E, int k, int32_t* ids, float* w,
+                             uint8_t* xq, float* x_scale, hipStream_t s);
+hipError_t launch_route_f32(const float* x, const float* w_router, const float* bias, int T,
+                            int d, int E, int k, int32_t* ids, float* w, hipStream_t s);
+
+// ----- permutation ----------------------------------------------------------
+size_t permute_ws_bytes(int T, int E);
+hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* offsets,
+                          int32_t* sorted_pair, int32_t* pair_to_row, void* ws, hipStream_t s);
+
+// ----- grouped FFN ----------------------------------------------------------
+// A "set" is a family of groups sharing one weight layout: the routed experts
+// (G groups, row ranges from a device offsets array, activation rows gathered
+// through row_src) or the shared expert (one group over `rows_fixed` rows).
+struct FfnSet {
+  const uint8_t* w13;    // [G][2F][d] (bytes: FP8 codes, or float32 when f32)
+  const float* s13;      // [G][2F]
+  const uint8_t* w2;     // [G][d][F]
+  const float* s2;       // [G][d]
+  const int32_t* offsets;  // device [G+1], or nullptr: one group of rows_fixed rows
+  const int32_t* row_src;  // gather, nullptr = identity
+  int src_div;
+  int G;
+  int F;
+  int rows_fixed;
+  int max_rows;          // upper bound of this set's rows
+  uint8_t* h;            // [max_rows][F] FP8 codes (float32 on the f32 path)
+  float* h_scale;        // [max_rows][F/128]
+  void* out;             // [max_rows][d] bf16 (float32 on the f32 path)
+};
+
+struct FfnCall {
+  int d;
+  int a_rows;
+  const void* a;         // [a_rows][d] FP8 codes or float32
+  const float* a_scale;  // [a_rows]
+  int nsets;             // 1 or 2
+  FfnSet set[2];
+};
+
+// Optional per-step HIP events (start/stop per MOE_STEP_*), recorded around
+// the kernels of each step.
+struct StepEvents {
+  void* const* start = nullptr;
+  void* const* stop = nullptr;
+  void mark(bool begin, int step, hipStream_t s) const {
+    void* const* a = begin ? start : stop;
+    if (a != nullptr && a[step] != nullptr) (void)hipEventRecord(static_cast<hipEvent_t>(a[step]), s);
+  }
+};
+
+// Workspace for the tile lists of one call (both GEMMs), given the sets'
+// row bounds; plus per-set h buffers sized by ffn_h_bytes.
+size_t ffn_tiles_ws_bytes(const FfnCall& c);
+size_t ffn_h_bytes(int max_rows, int F, bool fp8);
+size_t ffn_hs_bytes(int max_rows, int F);
+hipError_t launch_grouped_ffn_fp8(const FfnCall& c, void* tiles_ws, int rows_hint, hipStream_t s,
+                                  const StepEvents& ev = StepEvents());
+hipError_t launch_grouped_ffn_f32(const FfnCall& c, hipStream_t s,
+                                  const StepEvents& ev = StepEvents());
+
+// ----- combine --------------------------------------------------------------
+hipError_t launch_combine_bf16(const uint16_t* expert_out, const int32_t* pair_to_row,
+                               const float* w, const uint16_t* shared_out, uint16_t* y, int T,
+                               int d, int k, hipStream_t s);
+hipError_t launch_combine_f32(const float* expert_out, const int32_t* pair_to_row,
+                              const float* w, const float* shared_out, float* y, int T, int d,
+                              int k, hipStream_t s);
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+}  // namespace moe

@@ -25,14 +25,15 @@ def _np(t):
     return t.numpy().copy()
 
 
-def layer_inputs(lt) -> moe.LayerInputs:
+def layer_inputs(lt, cache_all: bool = False) -> moe.LayerInputs:
+    """cache_all keeps every expert copied so far (else at most 8 are held)."""
     cfg = lt.cfg
     fp8 = cfg.precision == "fp8"
     cache = {}
 
     def expert(e: int) -> moe.ExpertWeights:
         if e not in cache:
-            if len(cache) > 8:
+            if len(cache) > 8 and not cache_all:
                 cache.clear()
             cache[e] = moe.ExpertWeights(
                 _np(lt.w13[e]), _np(lt.w13_scale[e]) if fp8 else None,
