@@ -117,6 +117,9 @@ typedef struct moe_ffn {
   const void* w2;               /* [G][d][F] */
   const float* w2_scale;        /* [G][d] (FP8 path) */
   void* out;                    /* [max_rows][d]: bf16 (FP8 path) or float32 */
+  void* h_out;                  /* optional: receives h, [max_rows][F] FP8 codes (FP8 path)
+                                   or float32; NULL keeps h in the workspace */
+  float* h_scale_out;           /* optional: [max_rows][F/128] block scales of h (FP8 path) */
 } moe_ffn_t;
 
 /* ABI version (MOE_ABI_VERSION) and a static text for a status code. */

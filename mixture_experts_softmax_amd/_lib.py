@@ -47,7 +47,8 @@ class MoeFfn(C.Structure):
                 ("group_offsets", C.c_void_p), ("row_src", C.c_void_p), ("src_div", C.c_int32),
                 ("a_rows", C.c_int32), ("a", C.c_void_p), ("a_scale", C.c_void_p),
                 ("w13", C.c_void_p), ("w13_scale", C.c_void_p),
-                ("w2", C.c_void_p), ("w2_scale", C.c_void_p), ("out", C.c_void_p)]
+                ("w2", C.c_void_p), ("w2_scale", C.c_void_p), ("out", C.c_void_p),
+                ("h_out", C.c_void_p), ("h_scale_out", C.c_void_p)]
 
 
 class MoeError(RuntimeError):
@@ -203,7 +204,7 @@ def moe_permute(s: MoeShape, topk_ids, offsets, sorted_pair, pair_to_row, worksp
 
 
 def make_ffn(d, F, num_groups, max_rows, fp8: bool, group_offsets, row_src, src_div, a, a_scale,
-             w13, w13_scale, w2, w2_scale, out) -> MoeFfn:
+             w13, w13_scale, w2, w2_scale, out, h_out=None, h_scale_out=None) -> MoeFfn:
     G = num_groups
     wd = torch.uint8 if fp8 else torch.float32
     a_rows = a.shape[0] if a is not None else 0
@@ -217,7 +218,9 @@ def make_ffn(d, F, num_groups, max_rows, fp8: bool, group_offsets, row_src, src_
         _ptr(w13_scale, "w13_scale", torch.float32, G * 2 * F) if fp8 else None,
         _ptr(w2, "w2", wd, G * d * F),
         _ptr(w2_scale, "w2_scale", torch.float32, G * d) if fp8 else None,
-        _ptr(out, "out", torch.bfloat16 if fp8 else torch.float32, max_rows * d))
+        _ptr(out, "out", torch.bfloat16 if fp8 else torch.float32, max_rows * d),
+        _ptr(h_out, "h_out", wd, max_rows * F),
+        _ptr(h_scale_out, "h_scale_out", torch.float32, max_rows * (F // 128)) if fp8 else None)
 
 
 def moe_grouped_ffn(f: MoeFfn, workspace, stream=None):

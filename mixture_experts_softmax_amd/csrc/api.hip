@@ -55,7 +55,8 @@ moe_status_t check_ffn(const moe_ffn_t* f) {
   if (f->max_rows == 0) return MOE_OK;
   if (f->a_rows < 1) return MOE_ERR_INVALID_ARG;
   if (!f->group_offsets || !f->a || !f->w13 || !f->w2 || !f->out) return MOE_ERR_INVALID_ARG;
-  if (!al16(f->a) || !al16(f->w13) || !al16(f->w2) || !al16(f->out)) return MOE_ERR_INVALID_ARG;
+  if (!al16(f->a) || !al16(f->w13) || !al16(f->w2) || !al16(f->out) || !al16(f->h_out))
+    return MOE_ERR_INVALID_ARG;
   if (f->w_dtype == MOE_DTYPE_FP8_E4M3 && (!f->a_scale || !f->w13_scale || !f->w2_scale))
     return MOE_ERR_INVALID_ARG;
   return MOE_OK;
@@ -245,6 +246,8 @@ moe_status_t moe_grouped_ffn(const moe_ffn_t* f, void* workspace, size_t workspa
   Carve cv(workspace);
   void* tiles = nullptr;
   carve_ffn(c, fp8, cv, &tiles);
+  if (f->h_out != nullptr) c.set[0].h = static_cast<uint8_t*>(f->h_out);
+  if (fp8 && f->h_scale_out != nullptr) c.set[0].h_scale = f->h_scale_out;
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   if (fp8) {
     const int hint = ceil_div(f->max_rows, f->num_groups);

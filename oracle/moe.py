@@ -192,27 +192,37 @@ def ffn_fp32(x: np.ndarray, ew: ExpertWeights) -> np.ndarray:
     return h @ np.asarray(ew.w2, np.float64).T
 
 
-def ffn_fp8(xq: np.ndarray, s_x: np.ndarray, ew: ExpertWeights) -> np.ndarray:
-    """FP8 path for rows whose activations are already quantised (codes xq,
-    per-row scales s_x):
+def swiglu_h_fp8(xq: np.ndarray, s_x: np.ndarray, ew: ExpertWeights) -> np.ndarray:
+    """The SwiGLU activation of rows whose x is already quantised (codes xq,
+    per-row scales s_x), before h is quantised:
         g, u = s_x * s_w13[n] * sum_i xq_i q13[n, i]   (gate rows n < F, up rows n >= F)
         h    = silu(g) * u
-        hq, s_h = per-(row, 128-block) quantisation of h
-        o[m] = s_w2[m] * sum_b s_h[b] * sum_{n in b} hq[n] q2[m, n]
-    """
+    The dot products of E4M3 values are exact in float64."""
     F = ew.w13.shape[0] // 2
     xv = codecs.e4m3_decode(xq)                                # [R][d]
     gu = xv @ codecs.e4m3_decode(ew.w13).T                      # [R][2F]
     gu = gu * np.asarray(s_x, np.float64)[:, None] * np.asarray(ew.w13_scale, np.float64)[None, :]
-    h = silu(gu[:, :F]) * gu[:, F:]
-    hq, s_h = quantize_blocks_e4m3(h)
+    return silu(gu[:, :F]) * gu[:, F:]
+
+
+def down_fp8(hq: np.ndarray, s_h: np.ndarray, ew: ExpertWeights) -> np.ndarray:
+    """o[m] = s_w2[m] * sum_b s_h[b] * sum_{n in b} hq[n] q2[m, n]."""
+    F = hq.shape[1]
     hv = codecs.e4m3_decode(hq)                                 # [R][F]
     q2 = codecs.e4m3_decode(ew.w2)                              # [d][F]
-    o = np.zeros((xq.shape[0], q2.shape[0]), dtype=np.float64)
+    o = np.zeros((hq.shape[0], q2.shape[0]), dtype=np.float64)
     for b in range(F // H_BLOCK):
         cols = slice(b * H_BLOCK, (b + 1) * H_BLOCK)
         o += np.asarray(s_h[:, b], np.float64)[:, None] * (hv[:, cols] @ q2[:, cols].T)
     return o * np.asarray(ew.w2_scale, np.float64)[None, :]
+
+
+def ffn_fp8(xq: np.ndarray, s_x: np.ndarray, ew: ExpertWeights) -> np.ndarray:
+    """FP8 path of one expert on rows with quantised x: SwiGLU h, its
+    per-(row, 128-column block) quantisation, then the down projection."""
+    h = swiglu_h_fp8(xq, s_x, ew)
+    hq, s_h = quantize_blocks_e4m3(h)
+    return down_fp8(hq, s_h, ew)
 
 
 # ---------------------------------------------------------------------------

@@ -55,16 +55,116 @@ def shape_of(c, T=None):
     return _lib.shape(c.T if T is None else T, c.d, c.E, c.k, c.F, c.F_shared, c.precision)
 
 
-def compare_y(y_gpu: np.ndarray, y_ref: np.ndarray, precision: str, what: str = "y"):
+def run_stepwise(lt: LayerTensors, x=None):
+    """The layer through the separate entry points (route, permute, grouped FFN
+    over the routed experts, grouped FFN over the shared expert, combine),
+    keeping every intermediate; returns host numpy arrays."""
+    c = lt.cfg
+    x = lt.x if x is None else x
+    T, d, E, k, F, Fs = x.shape[0], c.d, c.E, c.k, c.F, c.F_shared
+    fp8 = c.precision == "fp8"
+    s = shape_of(c, T)
+    i32, f32 = torch.int32, torch.float32
+    ids = torch.empty((T, k), dtype=i32, device=DEV)
+    w = torch.empty((T, k), dtype=f32, device=DEV)
+    xq = torch.empty((T, d), dtype=torch.uint8, device=DEV) if fp8 else None
+    xs = torch.empty((T,), dtype=f32, device=DEV) if fp8 else None
+    _lib.moe_route_topk(s, x, lt.w_router, lt.router_bias, ids, w, xq, xs)
+    off = torch.empty(E + 1, dtype=i32, device=DEV)
+    sp = torch.empty(T * k, dtype=i32, device=DEV)
+    p2r = torch.empty(T * k, dtype=i32, device=DEV)
+    _lib.moe_permute(s, ids, off, sp, p2r, moe_lib.alloc_workspace(_lib.moe_permute_workspace_size(s), DEV))
+    odt = torch.bfloat16 if fp8 else f32
+    hdt = torch.uint8 if fp8 else f32
+    a, a_s = (xq, xs) if fp8 else (x, None)
+
+    def ffn(G, offsets, row_src, div, rows, FF, w13, s13, w2, s2):
+        out = torch.empty((rows, d), dtype=odt, device=DEV)
+        h = torch.empty((rows, FF), dtype=hdt, device=DEV)
+        hs = torch.empty((rows, FF // 128), dtype=f32, device=DEV) if fp8 else None
+        f = _lib.make_ffn(d, FF, G, rows, fp8, offsets, row_src, div, a, a_s, w13, s13, w2, s2, out, h, hs)
+        _lib.moe_grouped_ffn(f, moe_lib.alloc_workspace(_lib.moe_grouped_ffn_workspace_size(f), DEV))
+        return out, h, hs
+    eo, h, hs = ffn(E, off, sp, k, T * k, F, lt.w13, lt.w13_scale, lt.w2, lt.w2_scale)
+    so = hsh = hssh = None
+    if Fs:
+        so, hsh, hssh = ffn(1, torch.tensor([0, T], dtype=i32, device=DEV), None, 1, T, Fs,
+                            lt.ws13, lt.ws13_scale, lt.ws2, lt.ws2_scale)
+    y = torch.empty((T, d), dtype=odt, device=DEV)
+    _lib.moe_combine(s, eo, p2r, w, so, y)
+    torch.cuda.synchronize()
+
+    return dict(ids=ids.cpu().numpy(), w=w.cpu().numpy(), xq=None if xq is None else xq.cpu().numpy(),
+                xs=None if xs is None else xs.cpu().numpy(), offsets=off.cpu().numpy(),
+                sorted_pair=sp.cpu().numpy(), pair_to_row=p2r.cpu().numpy(),
+                eo=eo.to(torch.float64).cpu().numpy(), h=h.cpu().numpy(),
+                hs=None if hs is None else hs.cpu().numpy(),
+                so=None if so is None else so.to(torch.float64).cpu().numpy(),
+                h_sh=None if hsh is None else hsh.cpu().numpy(),
+                hs_sh=None if hssh is None else hssh.cpu().numpy(),
+                y=y.to(torch.float64).cpu().numpy())
+
+
+def compare_y(y_gpu: np.ndarray, y_ref: np.ndarray, precision: str, what: str = "y",
+              extra_abs=0.0):
+    """y_ref is the oracle's float64 value before any output rounding.
+    extra_abs (scalar or elementwise) widens the max-abs bound where validated
+    quantisation decisions of the kernel differ from the oracle's."""
     diff = np.abs(y_gpu - y_ref)
     max_abs = float(diff.max()) if diff.size else 0.0
     den = float(np.sqrt((y_ref ** 2).sum()))
     rel = float(np.sqrt((diff ** 2).sum()) / den) if den > 0 else max_abs
     lim_abs, lim_rel = (FP8_MAX_ABS, FP8_REL_L2) if precision == "fp8" else (F32_MAX_ABS, F32_REL_L2)
-    say(f"  {what}: max_abs={max_abs:.3e} rel_l2={rel:.3e} (limits {lim_abs:g}, {lim_rel:g})")
-    assert max_abs <= lim_abs, f"{what}: max abs err {max_abs} > {lim_abs}"
+    lim = lim_abs + np.asarray(extra_abs, np.float64)
+    widened = int((diff > lim_abs).sum())
+    say(f"  {what}: max_abs={max_abs:.3e} rel_l2={rel:.3e} (limits {lim_abs:g}, {lim_rel:g}); "
+        f"{widened} of {diff.size} outputs beyond {lim_abs:g}, each within its validated-decision bound")
+    bad = diff > lim
+    assert not bad.any(), f"{what}: {int(bad.sum())} outputs exceed their bound (max abs err {max_abs})"
     assert rel <= lim_rel, f"{what}: rel-L2 err {rel} > {lim_rel}"
     return max_abs, rel
+
+
+def fp8_bounds(inp, st, tokens=None):
+    """Validate the kernel's h decisions (routed groups and shared expert) for
+    the given tokens (default: all) against the oracle's exact h; return the
+    elementwise extra bound for y [len(tokens)][d], the extra bound for
+    expert_out rows {row: [d]} and for shared_out [len(tokens)][d], and the
+    number of neighbouring-code decisions."""
+    from tests import fp8_checks as FC
+    k = inp.k
+    T = st["ids"].shape[0]
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens)
+    d = st["y"].shape[1]
+    x64 = omoe.activations(inp)[tokens]
+    xq, sx = omoe.quantize_rows_e4m3(x64)
+    ids = st["ids"][tokens]
+    p2r = st["pair_to_row"]
+    row_bound = {}
+    flips = 0
+    for e in np.unique(ids):
+        sel = np.argwhere(ids == e)           # (token index, slot)
+        ew = inp.expert(int(e))
+        h64 = omoe.swiglu_h_fp8(xq[sel[:, 0]], sx[sel[:, 0]], ew)
+        rows = p2r[tokens[sel[:, 0]] * k + sel[:, 1]]
+        n, dhq = FC.validate_h(h64, st["h"][rows], st["hs"][rows])
+        flips += n
+        eff = FC.down_effect(dhq, ew)
+        for i, r in enumerate(rows):
+            row_bound[int(r)] = eff[i]
+    extra = np.zeros((len(tokens), d))
+    w = st["w"][tokens]
+    for i, t in enumerate(tokens):
+        for j in range(k):
+            extra[i] += w[i, j] * row_bound[int(p2r[t * k + j])]
+    shared_extra = None
+    if inp.shared is not None:
+        h64 = omoe.swiglu_h_fp8(xq, sx, inp.shared)
+        n, dhq = FC.validate_h(h64, st["h_sh"][tokens], st["hs_sh"][tokens])
+        flips += n
+        shared_extra = FC.down_effect(dhq, inp.shared)
+        extra += shared_extra
+    return extra, row_bound, shared_extra, flips
 
 
 def check_routing_invariants(ids: np.ndarray, w: np.ndarray, E: int):

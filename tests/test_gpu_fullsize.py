@@ -49,12 +49,17 @@ def test_fullsize_sampled(name):
         # tokens landing in the hottest and in the emptiest non-empty group
         hot_e = int(np.argmax(counts))
         extra = tuple(np.nonzero((ids == hot_e).any(1))[0][:3].tolist())
+    st = H.run_stepwise(lt)
+    assert np.array_equal(st["y"], y), "moe_layer_forward differs from the separate entry points"
     tok = _sample(cfg.T, SAMPLES[name], cfg.seed, extra)
     inp = oinputs.layer_inputs(lt)
-    r_ids, r_w, _, _, _, r_y = omoe.layer_forward_tokens(inp, tok)
+    r_ids, r_w, r_xq, r_sx, r_y64, _ = omoe.layer_forward_tokens(inp, tok)
     assert np.array_equal(ids[tok], r_ids)
     assert np.abs(w[tok] - r_w).max() <= H.W_MAX_ABS
-    H.compare_y(y[tok], r_y, "fp8", f"y[{len(tok)} sampled tokens]")
+    assert np.array_equal(st["xq"][tok], r_xq) and np.array_equal(st["xs"][tok], r_sx)
+    bound, _, _, flips = H.fp8_bounds(inp, st, tokens=tok)
+    H.say(f"  h: {flips} validated neighbouring-code decisions on the sampled tokens")
+    H.compare_y(y[tok], r_y64, "fp8", f"y[{len(tok)} sampled tokens]", bound)
     assert np.all(np.isfinite(y))
 
 

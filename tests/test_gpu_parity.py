@@ -92,7 +92,10 @@ def test_permute_out_of_range_ids_get_no_row():
 @pytest.mark.parametrize("name", ["fp8_small", "fp8_ragged", "fp8_wide", "fp8_skew_small", "tiny",
                                   "f32_ragged"])
 def test_grouped_ffn(name):
-    """moe_grouped_ffn on the routed groups (oracle routing and x codes as input)."""
+    """moe_grouped_ffn on the routed groups and on the shared expert, with the
+    oracle's routing and x codes as input; h decisions validated, outputs
+    within the y bound plus the effect of validated h decisions."""
+    from tests import fp8_checks as FC
     cfg = get(name)
     lt = H.gen(cfg)
     H.say(f"  cfg={cfg}")
@@ -103,32 +106,49 @@ def test_grouped_ffn(name):
     rows = T * k
     off = torch.from_numpy(ref.perm.offsets).to(H.DEV)
     sp = torch.from_numpy(ref.perm.sorted_pair).to(H.DEV)
+    odt = torch.bfloat16 if fp8 else torch.float32
+    hdt = torch.uint8 if fp8 else torch.float32
     if fp8:
         a = torch.from_numpy(ref.xq).to(H.DEV)
         a_s = torch.from_numpy(ref.s_x).to(H.DEV)
-        out = torch.empty((rows, d), dtype=torch.bfloat16, device=H.DEV)
     else:
-        a = lt.x
-        a_s = None
-        out = torch.empty((rows, d), dtype=torch.float32, device=H.DEV)
-    f = _lib.make_ffn(d, F, E, rows, fp8, off, sp, k, a, a_s, lt.w13, lt.w13_scale, lt.w2,
-                      lt.w2_scale, out)
-    ws = alloc_workspace(_lib.moe_grouped_ffn_workspace_size(f), H.DEV)
-    _lib.moe_grouped_ffn(f, ws)
-    torch.cuda.synchronize()
-    got = out.to(torch.float64).cpu().numpy()
-    H.compare_y(got, ref.expert_out, cfg.precision, "expert_out")
-    # the shared expert as one group over all tokens, identity rows
+        a, a_s = lt.x, None
+
+    def run(G, offsets, row_src, div, nrows, FF, w13, s13, w2, s2):
+        out = torch.empty((nrows, d), dtype=odt, device=H.DEV)
+        h = torch.empty((nrows, FF), dtype=hdt, device=H.DEV)
+        hs = torch.empty((nrows, FF // 128), dtype=torch.float32, device=H.DEV) if fp8 else None
+        f = _lib.make_ffn(d, FF, G, nrows, fp8, offsets, row_src, div, a, a_s, w13, s13, w2, s2, out, h, hs)
+        _lib.moe_grouped_ffn(f, alloc_workspace(_lib.moe_grouped_ffn_workspace_size(f), H.DEV))
+        torch.cuda.synchronize()
+        return (out.to(torch.float64).cpu().numpy(), h.cpu().numpy(),
+                None if hs is None else hs.cpu().numpy())
+
+    eo, h, hs = run(E, off, sp, k, rows, F, lt.w13, lt.w13_scale, lt.w2, lt.w2_scale)
+    extra = np.zeros_like(eo)
+    if fp8:
+        flips = 0
+        for e in range(E):
+            r0, r1 = int(ref.perm.offsets[e]), int(ref.perm.offsets[e + 1])
+            if r1 == r0:
+                continue
+            tok = ref.perm.sorted_pair[r0:r1] // k
+            ew = inp.expert(e)
+            n, dhq = FC.validate_h(omoe.swiglu_h_fp8(ref.xq[tok], ref.s_x[tok], ew), h[r0:r1], hs[r0:r1])
+            flips += n
+            extra[r0:r1] = FC.down_effect(dhq, ew)
+        H.say(f"  routed h: {flips} validated neighbouring-code decisions of {h.size}")
+    H.compare_y(eo, ref.expert_out, cfg.precision, "expert_out", extra)
     if cfg.F_shared:
         Fs = cfg.F_shared
-        out_s = torch.empty((T, d), dtype=out.dtype, device=H.DEV)
         off_s = torch.tensor([0, T], dtype=torch.int32, device=H.DEV)
-        fs = _lib.make_ffn(d, Fs, 1, T, fp8, off_s, None, 1, a, a_s, lt.ws13, lt.ws13_scale, lt.ws2,
-                           lt.ws2_scale, out_s)
-        ws2 = alloc_workspace(_lib.moe_grouped_ffn_workspace_size(fs), H.DEV)
-        _lib.moe_grouped_ffn(fs, ws2)
-        torch.cuda.synchronize()
-        H.compare_y(out_s.to(torch.float64).cpu().numpy(), ref.shared_out, cfg.precision, "shared_out")
+        so, hsh, hssh = run(1, off_s, None, 1, T, Fs, lt.ws13, lt.ws13_scale, lt.ws2, lt.ws2_scale)
+        extra_s = 0.0
+        if fp8:
+            n, dhq = FC.validate_h(omoe.swiglu_h_fp8(ref.xq, ref.s_x, inp.shared), hsh, hssh)
+            H.say(f"  shared h: {n} validated neighbouring-code decisions of {hsh.size}")
+            extra_s = FC.down_effect(dhq, inp.shared)
+        H.compare_y(so, ref.shared_out, cfg.precision, "shared_out", extra_s)
 
 
 @pytest.mark.parametrize("precision", ["fp8", "f32"])
@@ -147,25 +167,38 @@ def test_combine(precision):
                      so.to(H.DEV), y)
     torch.cuda.synchronize()
     eo64 = eo.to(torch.float64).numpy()
-    ref = omoe.combine(w.astype(np.float64), eo64[p2r].reshape(T, k, d), so.to(torch.float64).numpy())
-    ref = omoe.round_output(ref, precision)
+    pairs = eo64[p2r].reshape(T, k, d)
+    so64 = so.to(torch.float64).numpy()
+    exact = omoe.combine(w.astype(np.float64), pairs, so64)
     got = y.to(torch.float64).cpu().numpy()
-    if precision == "fp8":  # within one bf16 rounding of the exact sum
-        assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-6)
+    # float32 accumulation of k+1 terms: <= (k+1) * 2^-24 * sum |terms|
+    acc_err = (k + 1) * 2.0 ** -24 * (np.einsum("tj,tjd->td", np.abs(w), np.abs(pairs)) + np.abs(so64))
+    if precision == "fp8":  # plus half a bf16 ulp (<= 2^-8 relative) for the output rounding
+        assert np.all(np.abs(got - exact) <= np.abs(exact) * 2.0 ** -8 + acc_err * 1.01)
     else:
-        assert np.abs(got - ref).max() <= 1e-5
+        assert np.all(np.abs(got - exact) <= np.abs(exact) * 2.0 ** -24 + acc_err * 1.01)
 
 
 @pytest.mark.parametrize("name", SMALL)
 def test_layer_forward(name):
+    """moe_layer_forward against the oracle; the separate entry points give
+    bit-identical results, and their h decisions are validated."""
     cfg = get(name)
     lt = H.gen(cfg)
     H.say(f"  cfg={cfg} redraws={lt.redraws}")
     ids, w, y = H.run_layer(lt)
-    ref = omoe.layer_forward(oinputs.layer_inputs(lt))
+    st = H.run_stepwise(lt)
+    assert np.array_equal(st["ids"], ids) and np.array_equal(st["w"], w)
+    assert np.array_equal(st["y"], y), "moe_layer_forward differs from the separate entry points"
+    inp = oinputs.layer_inputs(lt)
+    ref = omoe.layer_forward(inp)
     assert np.array_equal(ids, ref.ids)
     assert np.abs(w - ref.w).max() <= H.W_MAX_ABS
-    H.compare_y(y, ref.y, cfg.precision)
+    extra = 0.0
+    if cfg.precision == "fp8":
+        extra, _, _, flips = H.fp8_bounds(inp, st)
+        H.say(f"  h: {flips} validated neighbouring-code decisions")
+    H.compare_y(y, ref.y64, cfg.precision, "y", extra)
 
 
 def test_layer_zero_input_gives_zero():
@@ -179,11 +212,15 @@ def test_layer_zero_input_gives_zero():
 def test_layer_t1_and_empty():
     cfg = get("fp8_ragged")
     lt = H.gen(cfg)
-    ids, w, y = H.run_layer(lt, x=lt.x[:1].contiguous())
+    x1 = lt.x[:1].contiguous()
+    ids, w, y = H.run_layer(lt, x=x1)
+    st = H.run_stepwise(lt, x=x1)
+    assert np.array_equal(st["y"], y)
     inp = oinputs.layer_inputs(lt)
-    r_ids, r_w, _, _, _, r_y = omoe.layer_forward_tokens(inp, np.array([0]))
+    r_ids, r_w, _, _, r_y64, _ = omoe.layer_forward_tokens(inp, np.array([0]))
     assert np.array_equal(ids, r_ids)
-    H.compare_y(y, r_y, "fp8", "y[T=1]")
+    extra, _, _, _ = H.fp8_bounds(inp, st, tokens=np.array([0]))
+    H.compare_y(y, r_y64, "fp8", "y[T=1]", extra)
     # T == 0: nothing enqueued, output untouched
     y0 = torch.empty((0, cfg.d), dtype=torch.bfloat16, device=H.DEV)
     H.layer(lt).forward(lt.x[:0], y=y0)
