@@ -42,6 +42,7 @@ class Hip:
         self.L.hipEventSynchronize.argtypes = [C.c_void_p]
         self.L.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
         self.L.hipEventDestroy.argtypes = [C.c_void_p]
+        self.L.hipGetLastError.restype = C.c_int
 
     def event(self) -> int:
         e = C.c_void_p()
@@ -49,10 +50,13 @@ class Hip:
             raise RuntimeError("hipEventCreate failed")
         return e.value
 
-    def ms(self, a: int, b: int) -> float:
+    def ms(self, a: int, b: int, missing_ok: bool = False):
         self.L.hipEventSynchronize(C.c_void_p(b))
         t = C.c_float()
         if self.L.hipEventElapsedTime(C.byref(t), C.c_void_p(a), C.c_void_p(b)) != 0:
+            self.L.hipGetLastError()  # clear the runtime's error state
+            if missing_ok:
+                return None
             raise RuntimeError("hipEventElapsedTime failed")
         return t.value
 
@@ -147,19 +151,24 @@ def time_layer(cfg, steps, warmup, hip):
     for e in ev_a + ev_b:
         hip.destroy(e)
 
-    # per-step breakdown (separate short loop, all steps bracketed)
+    # per-step breakdown (separate short loop, every step of the layer path
+    # bracketed; its tile lists come from the permutation scan, so it has no
+    # separate "tiles" step)
     reps = min(steps, 10)
-    starts = [[hip.event() for _ in range(nsteps)] for _ in range(reps)]
-    stops = [[hip.event() for _ in range(nsteps)] for _ in range(reps)]
+    steps_here = [j for j, n in enumerate(_lib.MOE_STEPS) if n != "tiles"]
+    starts = [[hip.event() if j in steps_here else None for j in range(nsteps)] for _ in range(reps)]
+    stops = [[hip.event() if j in steps_here else None for j in range(nsteps)] for _ in range(reps)]
     for i in range(reps):
         _lib.moe_layer_forward_events(s, W, x, y, ids, gw, ws, starts[i], stops[i])
     torch.cuda.synchronize()
     breakdown = {}
-    for j, name in enumerate(_lib.MOE_STEPS):
-        breakdown[name] = round(1e3 * sum(hip.ms(starts[i][j], stops[i][j]) for i in range(reps)) / reps, 2)
+    for j in steps_here:
+        t = [hip.ms(starts[i][j], stops[i][j]) for i in range(reps)]
+        breakdown[_lib.MOE_STEPS[j]] = round(1e3 * sum(t) / reps, 2)
     for row in starts + stops:
         for e in row:
-            hip.destroy(e)
+            if e is not None:
+                hip.destroy(e)
 
     import numpy as np
     counts = np.bincount(ids.cpu().numpy().reshape(-1), minlength=cfg.E)
@@ -204,7 +213,10 @@ def main():
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "b100", "skew"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=8)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a 1 GiB device-to-device copy (counter calibration) and exit")
+    ap.add_argument("--cpu-tokens", type=int, default=0,
+                    help="tokens of the workload the CPU oracle runs (0: the whole batch, capped at 64)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -217,6 +229,17 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_probe:
+        # a plain copy of known size: HBM counters read on its dispatches give
+        # the scale between counter units and bytes moved
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "copies": 3}), flush=True)
+        return
     from synthetic import CONFIGS
     hip = Hip()
     cfg = CONFIGS[args.workload]
@@ -270,7 +293,8 @@ def main():
             "step_breakdown_us": rp["breakdown_us"]}
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
-        out["cpu_baseline"] = cpu_baseline(cfg, lt, args.cpu_tokens)
+        n = args.cpu_tokens if args.cpu_tokens > 0 else min(cfg.T, 64)
+        out["cpu_baseline"] = cpu_baseline(cfg, lt, n)
     print(json.dumps(out), flush=True)
 
 

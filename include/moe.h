@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 /* Limits checked by every entry point. */
 #define MOE_MAX_E 256      /* routed experts */
@@ -131,6 +131,7 @@ moe_status_t moe_check_shape(const moe_shape_t* shape);
 
 /* Workspace sizes in bytes (host-only queries, nothing is enqueued). */
 moe_status_t moe_layer_workspace_size(const moe_shape_t* shape, size_t* bytes);
+moe_status_t moe_route_workspace_size(const moe_shape_t* shape, size_t* bytes);
 moe_status_t moe_permute_workspace_size(const moe_shape_t* shape, size_t* bytes);
 moe_status_t moe_grouped_ffn_workspace_size(const moe_ffn_t* ffn, size_t* bytes);
 
@@ -150,11 +151,13 @@ moe_status_t moe_grouped_ffn_workspace_size(const moe_ffn_t* ffn, size_t* bytes)
  * Outputs topk_ids [T][k] int32 and topk_w [T][k] float32. On the FP8 path the
  * same kernel also writes xq [T][d] (FP8 E4M3 codes of x / x_scale[t]) and
  * x_scale [T] (amax of row t over 448, 1.0 for a zero row); both are required
- * there and ignored on the float32 path.
+ * there and ignored on the float32 path. Needs a workspace of
+ * moe_route_workspace_size() bytes (the float32 logits).
  */
 moe_status_t moe_route_topk(const moe_shape_t* shape, const void* x, const void* w_router,
                             const float* router_bias, int32_t* topk_ids, float* topk_w,
-                            uint8_t* xq, float* x_scale, void* stream);
+                            uint8_t* xq, float* x_scale, void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 /*
  * Permutation of the T*k (token, slot) pairs into expert-contiguous order (the
@@ -214,9 +217,9 @@ moe_status_t moe_layer_forward(const moe_shape_t* shape, const moe_weights_t* we
 
 /* Steps of moe_layer_forward, in launch order (for moe_layer_forward_events). */
 typedef enum moe_step {
-  MOE_STEP_ROUTE = 0,    /* router kernel */
-  MOE_STEP_PERMUTE = 1,  /* the three permutation kernels */
-  MOE_STEP_TILES = 2,    /* grouped-FFN tile list */
+  MOE_STEP_ROUTE = 0,    /* router: logits and top-k kernels */
+  MOE_STEP_PERMUTE = 1,  /* permutation: scan (which also writes the FFN tile lists) and scatter */
+  MOE_STEP_TILES = 2,    /* separate FFN tile-list kernel (moe_grouped_ffn only; none in the layer) */
   MOE_STEP_GATE_UP = 3,  /* gate/up GEMM + SwiGLU + h quantisation */
   MOE_STEP_DOWN = 4,     /* down GEMM */
   MOE_STEP_COMBINE = 5,  /* combine */

@@ -21,7 +21,8 @@ MOE_DTYPE_F32, MOE_DTYPE_BF16, MOE_DTYPE_FP8_E4M3 = 0, 1, 2
 # Names declared in include/moe.h, in order.
 EXPORTS = [
     "moe_abi_version", "moe_status_string", "moe_check_shape",
-    "moe_layer_workspace_size", "moe_permute_workspace_size", "moe_grouped_ffn_workspace_size",
+    "moe_layer_workspace_size", "moe_route_workspace_size", "moe_permute_workspace_size",
+    "moe_grouped_ffn_workspace_size",
     "moe_route_topk", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_forward",
     "moe_layer_forward_events", "moe_host_e4m3_encode",
 ]
@@ -74,12 +75,12 @@ def lib() -> C.CDLL:
         L.moe_status_string.argtypes = [I32]
         L.moe_check_shape.restype = I32
         L.moe_check_shape.argtypes = [P]
-        for n in ("moe_layer_workspace_size", "moe_permute_workspace_size",
-                  "moe_grouped_ffn_workspace_size"):
+        for n in ("moe_layer_workspace_size", "moe_route_workspace_size",
+                  "moe_permute_workspace_size", "moe_grouped_ffn_workspace_size"):
             getattr(L, n).restype = I32
             getattr(L, n).argtypes = [P, C.POINTER(SZ)]
         L.moe_route_topk.restype = I32
-        L.moe_route_topk.argtypes = [P] * 9
+        L.moe_route_topk.argtypes = [P] * 9 + [SZ, P]
         L.moe_permute.restype = I32
         L.moe_permute.argtypes = [P, P, P, P, P, P, SZ, P]
         L.moe_grouped_ffn.restype = I32
@@ -167,6 +168,12 @@ def moe_layer_workspace_size(s: MoeShape) -> int:
     return n.value
 
 
+def moe_route_workspace_size(s: MoeShape) -> int:
+    n = C.c_size_t(0)
+    _check(lib().moe_route_workspace_size(C.byref(s), C.byref(n)), "moe_route_workspace_size")
+    return n.value
+
+
 def moe_permute_workspace_size(s: MoeShape) -> int:
     n = C.c_size_t(0)
     _check(lib().moe_permute_workspace_size(C.byref(s), C.byref(n)), "moe_permute_workspace_size")
@@ -180,15 +187,17 @@ def moe_grouped_ffn_workspace_size(f: MoeFfn) -> int:
     return n.value
 
 
-def moe_route_topk(s: MoeShape, x, w_router, router_bias, topk_ids, topk_w, xq=None,
-                   x_scale=None, stream=None):
+def moe_route_topk(s: MoeShape, x, w_router, router_bias, topk_ids, topk_w, xq, x_scale,
+                   workspace, stream=None):
     T, d, E, k = s.T, s.d, s.E, s.k
     fp8 = _is_fp8(s)
     args = (C.byref(s), _ptr(x, "x", _act_dtype(s), T * d), _ptr(w_router, "w_router", _act_dtype(s), E * d),
             _ptr(router_bias, "router_bias", torch.float32, E),
             _ptr(topk_ids, "topk_ids", torch.int32, T * k), _ptr(topk_w, "topk_w", torch.float32, T * k),
             _ptr(xq, "xq", torch.uint8, T * d) if fp8 else None,
-            _ptr(x_scale, "x_scale", torch.float32, T) if fp8 else None, _stream(stream))
+            _ptr(x_scale, "x_scale", torch.float32, T) if fp8 else None,
+            _ptr(workspace, "workspace", torch.uint8),
+            workspace.numel() if workspace is not None else 0, _stream(stream))
     _check(lib().moe_route_topk(*args), "moe_route_topk")
 
 

@@ -99,7 +99,9 @@ struct LayerWs {
   float* w;
   uint8_t* xq;
   float* xs;
-  int32_t* perm;
+  float* logits;
+  uint64_t* masks;
+  int32_t* counts;
   int32_t* offsets;
   int32_t* sorted_pair;
   int32_t* pair_to_row;
@@ -119,7 +121,9 @@ LayerWs layer_ws(const moe_shape_t* s, void* base, FfnCall* call) {
   L.w = cv.take<float>(T * k * 4);
   L.xq = fp8 ? cv.take<uint8_t>(T * d) : nullptr;
   L.xs = fp8 ? cv.take<float>(T * 4) : nullptr;
-  L.perm = cv.take<int32_t>(permute_ws_bytes(s->T, s->E));
+  L.logits = cv.take<float>(route_ws_bytes(s->T, s->E));
+  L.masks = cv.take<uint64_t>(perm_masks_bytes(s->T, s->E));
+  L.counts = cv.take<int32_t>(perm_counts_bytes(s->T, s->E));
   L.offsets = cv.take<int32_t>((E + 1) * 4);
   L.sorted_pair = cv.take<int32_t>(T * k * 4);
   L.pair_to_row = cv.take<int32_t>(T * k * 4);
@@ -166,6 +170,14 @@ moe_status_t moe_layer_workspace_size(const moe_shape_t* shape, size_t* bytes) {
   return MOE_OK;
 }
 
+moe_status_t moe_route_workspace_size(const moe_shape_t* shape, size_t* bytes) {
+  const moe_status_t st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
+  *bytes = route_ws_bytes(shape->T, shape->E);
+  return MOE_OK;
+}
+
 moe_status_t moe_permute_workspace_size(const moe_shape_t* shape, size_t* bytes) {
   const moe_status_t st = check_shape(shape);
   if (st != MOE_OK) return st;
@@ -199,22 +211,21 @@ moe_status_t moe_grouped_ffn_workspace_size(const moe_ffn_t* ffn, size_t* bytes)
 
 moe_status_t moe_route_topk(const moe_shape_t* s, const void* x, const void* w_router,
                             const float* router_bias, int32_t* topk_ids, float* topk_w,
-                            uint8_t* xq, float* x_scale, void* stream) {
+                            uint8_t* xq, float* x_scale, void* workspace, size_t workspace_bytes,
+                            void* stream) {
   moe_status_t st = check_shape(s);
   if (st != MOE_OK) return st;
   if (s->T == 0) return MOE_OK;
   if (!x || !w_router || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
   if (!al16(x) || !al16(w_router)) return MOE_ERR_INVALID_ARG;
-  const hipStream_t hs = static_cast<hipStream_t>(stream);
-  if (is_fp8(s)) {
-    if (!xq || !x_scale || !al16(xq)) return MOE_ERR_INVALID_ARG;
-    return from_hip(launch_route_bf16(static_cast<const uint16_t*>(x),
-                                      static_cast<const uint16_t*>(w_router), router_bias, s->T,
-                                      s->d, s->E, s->k, topk_ids, topk_w, xq, x_scale, hs));
-  }
-  return from_hip(launch_route_f32(static_cast<const float*>(x),
-                                   static_cast<const float*>(w_router), router_bias, s->T, s->d,
-                                   s->E, s->k, topk_ids, topk_w, hs));
+  const bool fp8 = is_fp8(s);
+  if (fp8 && (!xq || !x_scale || !al16(xq))) return MOE_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < route_ws_bytes(s->T, s->E) || !al256(workspace))
+    return MOE_ERR_WORKSPACE;
+  return from_hip(launch_route(fp8, x, w_router, router_bias, s->T, s->d, s->E, s->k, topk_ids,
+                               topk_w, fp8 ? xq : nullptr, fp8 ? x_scale : nullptr,
+                               static_cast<float*>(workspace), nullptr, nullptr,
+                               static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_permute(const moe_shape_t* s, const int32_t* topk_ids, int32_t* offsets,
@@ -309,22 +320,6 @@ moe_status_t moe_layer_forward_events(const moe_shape_t* s, const moe_weights_t*
   float* w = topk_w ? topk_w : L.w;
   const hipStream_t hs = static_cast<hipStream_t>(stream);
 
-  hipError_t e;
-  ev.mark(true, MOE_STEP_ROUTE, hs);
-  if (fp8)
-    e = launch_route_bf16(static_cast<const uint16_t*>(x),
-                          static_cast<const uint16_t*>(wt->w_router), wt->router_bias, s->T, s->d,
-                          s->E, s->k, ids, w, L.xq, L.xs, hs);
-  else
-    e = launch_route_f32(static_cast<const float*>(x), static_cast<const float*>(wt->w_router),
-                         wt->router_bias, s->T, s->d, s->E, s->k, ids, w, hs);
-  ev.mark(false, MOE_STEP_ROUTE, hs);
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  ev.mark(true, MOE_STEP_PERMUTE, hs);
-  e = launch_permute(ids, s->T, s->E, s->k, L.offsets, L.sorted_pair, L.pair_to_row, L.perm, hs);
-  ev.mark(false, MOE_STEP_PERMUTE, hs);
-  if (e != hipSuccess) return MOE_ERR_HIP;
-
   c.a_rows = s->T;
   c.a = fp8 ? static_cast<const void*>(L.xq) : x;
   c.a_scale = L.xs;
@@ -340,8 +335,23 @@ moe_status_t moe_layer_forward_events(const moe_shape_t* s, const moe_weights_t*
     Sh.w2 = static_cast<const uint8_t*>(wt->ws2);
     Sh.s2 = wt->ws2_scale;
   }
+  const int bm = choose_bm(ceil_div(s->T * s->k, s->E));
+
+  hipError_t e;
+  ev.mark(true, MOE_STEP_ROUTE, hs);
+  e = launch_route(fp8, x, wt->w_router, wt->router_bias, s->T, s->d, s->E, s->k, ids, w, L.xq,
+                   L.xs, L.logits, L.masks, L.counts, hs);
+  ev.mark(false, MOE_STEP_ROUTE, hs);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  // scan + scatter; on the FP8 path the scan also writes the FFN tile lists
+  ev.mark(true, MOE_STEP_PERMUTE, hs);
+  e = launch_perm_scan_scatter(ids, s->T, s->E, s->k, L.masks, L.counts, L.offsets, L.sorted_pair,
+                               L.pair_to_row, fp8 ? &c : nullptr, bm, fp8 ? L.tiles : nullptr, hs);
+  ev.mark(false, MOE_STEP_PERMUTE, hs);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+
   if (fp8)
-    e = launch_grouped_ffn_fp8(c, L.tiles, ceil_div(s->T * s->k, s->E), hs, ev);
+    e = launch_ffn_gemms(c, bm, L.tiles, hs, ev);
   else
     e = launch_grouped_ffn_f32(c, hs, ev);
   if (e != hipSuccess) return MOE_ERR_HIP;

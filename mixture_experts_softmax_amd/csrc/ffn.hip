@@ -17,35 +17,17 @@
 // served from that XCD's L2.
 #include "common.h"
 #include "internal.h"
+#include "tiles.h"
 
 namespace moe {
 
 namespace {
 
 constexpr int kBK = 128;      // K bytes per MFMA step (FP8 16x16x128)
-constexpr int kHN = 128;      // h columns per gate/up tile = one h quantisation block
-constexpr int kDownBN = 256;  // output channels per down tile
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
-constexpr int kMaxGroups = 1024;
 constexpr int kXcds = 8;
-constexpr int kBuildThreads = 256;
-
-struct TileEntry {
-  int row0;   // first row of the tile, in the set's grouped row space
-  int nrows;  // rows in this tile, 1..BM
-  int gid;    // (set << 16) | group
-  int ntile;  // N tile index
-};
-
-struct TileHeader {
-  int n_up;
-  int n_down;
-  int pad[62];
-};
-
-__host__ __device__ inline int up_ntiles(int F) { return F / kHN; }
-__host__ __device__ inline int down_ntiles(int d) { return ceil_div(d, kDownBN); }
+constexpr int kTileThreads = 256;
 
 size_t tiles_cap(const FfnCall& c, int bm, bool up) {
   size_t n = 0;
@@ -58,23 +40,16 @@ size_t tiles_cap(const FfnCall& c, int bm, bool up) {
 }
 
 // ---------------------------------------------------------------------------
-// Tile-list builder: one workgroup.
+// Tile lists from group offsets held in device memory (moe_grouped_ffn).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kBuildThreads) void build_tiles_kernel(FfnCall c, int bm,
-                                                                    TileHeader* hdr,
-                                                                    TileEntry* up,
-                                                                    TileEntry* down, int cap_up,
-                                                                    int cap_dn) {
-  __shared__ int g_row0[kMaxGroups], g_rows[kMaxGroups], g_set[kMaxGroups];
-  __shared__ int pre_up[kMaxGroups + 1], pre_dn[kMaxGroups + 1];
-  __shared__ int part_up[kBuildThreads], part_dn[kBuildThreads];
-  const int tid = threadIdx.x;
+__global__ __launch_bounds__(kTileThreads) void ffn_tiles_kernel(FfnCall c, int bm,
+                                                                 TileHeader* hdr, TileEntry* up,
+                                                                 TileEntry* down, int cap_up,
+                                                                 int cap_dn) {
+  __shared__ TileLds L;
   const int G0 = c.set[0].G;
   const int NG = G0 + (c.nsets > 1 ? c.set[1].G : 0);
-  const int dnt = down_ntiles(c.d);
-
-  // per group: rows and tile counts
-  for (int i = tid; i < NG; i += kBuildThreads) {
+  for (int i = threadIdx.x; i < NG; i += kTileThreads) {
     const int s = (i < G0) ? 0 : 1;
     const int g = (s == 0) ? i : i - G0;
     const FfnSet S = (s == 0) ? c.set[0] : c.set[1];
@@ -85,78 +60,12 @@ __global__ __launch_bounds__(kBuildThreads) void build_tiles_kernel(FfnCall c, i
       r0 = min(max(S.offsets[g], 0), S.max_rows);
       r1 = min(max(S.offsets[g + 1], r0), S.max_rows);
     }
-    const int rows = r1 - r0;
-    g_row0[i] = r0;
-    g_rows[i] = rows;
-    g_set[i] = s;
+    L.g_row0[i] = r0;
+    L.g_rows[i] = r1 - r0;
+    L.g_set[i] = s;
   }
   __syncthreads();
-  // exclusive scans of the per-group tile counts (each thread owns a run of groups)
-  const int per = ceil_div(NG, kBuildThreads);
-  const int lo = min(NG, tid * per), hi = min(NG, lo + per);
-  int su = 0, sd = 0;
-  for (int i = lo; i < hi; ++i) {
-    const int mt = ceil_div(g_rows[i], bm);
-    su += mt * up_ntiles(g_set[i] == 0 ? c.set[0].F : c.set[1].F);
-    sd += mt * dnt;
-  }
-  part_up[tid] = su;
-  part_dn[tid] = sd;
-  __syncthreads();
-  for (int o = 1; o < kBuildThreads; o <<= 1) {
-    const int vu = (tid >= o) ? part_up[tid - o] : 0;
-    const int vd = (tid >= o) ? part_dn[tid - o] : 0;
-    __syncthreads();
-    part_up[tid] += vu;
-    part_dn[tid] += vd;
-    __syncthreads();
-  }
-  su = part_up[tid] - su;
-  sd = part_dn[tid] - sd;
-  for (int i = lo; i < hi; ++i) {
-    pre_up[i] = su;
-    pre_dn[i] = sd;
-    const int mt = ceil_div(g_rows[i], bm);
-    su += mt * up_ntiles(g_set[i] == 0 ? c.set[0].F : c.set[1].F);
-    sd += mt * dnt;
-  }
-  if (tid == kBuildThreads - 1) {
-    pre_up[NG] = part_up[kBuildThreads - 1];
-    pre_dn[NG] = part_dn[kBuildThreads - 1];
-  }
-  __syncthreads();
-  // overlapping (malformed) offsets could need more entries than the list
-  // holds: keep only what fits
-  const int n_up = min(pre_up[NG], cap_up), n_dn = min(pre_dn[NG], cap_dn);
-
-  // entries, spread over all threads: M tiles of one (group, N tile) adjacent
-  for (int w = tid; w < n_up + n_dn; w += kBuildThreads) {
-    const bool is_up = w < n_up;
-    const int idx = is_up ? w : w - n_up;
-    const int* pre = is_up ? pre_up : pre_dn;
-    int a = 0, b = NG;  // largest group i with pre[i] <= idx
-    while (b - a > 1) {
-      const int m = (a + b) >> 1;
-      if (pre[m] <= idx) a = m; else b = m;
-    }
-    // skip empty groups sharing the same prefix
-    while (a + 1 < NG && pre[a + 1] <= idx) ++a;
-    const int mt = ceil_div(g_rows[a], bm);
-    const int loc = idx - pre[a];
-    const int m = loc % mt, nt = loc / mt;
-    const int s = g_set[a];
-    const int g = (s == 0) ? a : a - G0;
-    TileEntry e;
-    e.row0 = g_row0[a] + m * bm;
-    e.nrows = min(bm, g_rows[a] - m * bm);
-    e.gid = (s << 16) | g;
-    e.ntile = nt;
-    if (is_up) up[idx] = e; else down[idx] = e;
-  }
-  if (tid == 0) {
-    hdr->n_up = n_up;
-    hdr->n_down = n_dn;
-  }
+  emit_tiles(c, bm, NG, G0, L, hdr, up, down, cap_up, cap_dn);
 }
 
 // Block -> list entry, XCD-contiguous. Returns false for blocks with no work.
@@ -167,8 +76,8 @@ __device__ inline bool pick_tile(const int total, int& w) {
   return slot < per && w < total;
 }
 
-__device__ inline v8i pack8(const uint4& lo, const uint4& hi) {
-  return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+__device__ inline v8i pack8(const v4i& lo, const v4i& hi) {
+  return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
 // Swizzled offset of 16-byte chunk c of row r in a [rows][128 B] LDS tile.
@@ -178,23 +87,58 @@ __device__ inline int swz(int r, int c) { return r * kBK + ((c ^ (r & 7)) << 4);
 // [(lane/16)*16, +16) and [64 + (lane/16)*16, +16) of the 128-byte K step.
 __device__ inline v8i lds_afrag(const uint8_t* tile, int i, int lane) {
   const int r = i * 16 + (lane & 15);
-  const uint4 lo = *reinterpret_cast<const uint4*>(tile + swz(r, lane >> 4));
-  const uint4 hi = *reinterpret_cast<const uint4*>(tile + swz(r, 4 + (lane >> 4)));
+  const v4i lo = *reinterpret_cast<const v4i*>(tile + swz(r, lane >> 4));
+  const v4i hi = *reinterpret_cast<const v4i*>(tile + swz(r, 4 + (lane >> 4)));
   return pack8(lo, hi);
 }
 
 // B fragment: 16 weight rows, lane reads row (lane%16) at the same byte slices.
 __device__ inline v8i glb_bfrag(const uint8_t* p) {
-  const uint4 lo = *reinterpret_cast<const uint4*>(p);
-  const uint4 hi = *reinterpret_cast<const uint4*>(p + 64);
+  const v4i lo = *reinterpret_cast<const v4i*>(p);
+  const v4i hi = *reinterpret_cast<const v4i*>(p + 64);
   return pack8(lo, hi);
 }
 
+// The fields of set `sid` (0 or 1), read field by field from the kernel
+// arguments so the compiler keeps them in scalar registers.
+struct SetView {
+  const uint8_t* w13;
+  const float* s13;
+  const uint8_t* w2;
+  const float* s2;
+  const int32_t* row_src;
+  int src_div, F;
+  uint8_t* h;
+  float* h_scale;
+  void* out;
+};
+
+__device__ inline SetView set_view(const FfnCall& c, int sid) {
+  SetView v;
+  v.w13 = sid ? c.set[1].w13 : c.set[0].w13;
+  v.s13 = sid ? c.set[1].s13 : c.set[0].s13;
+  v.w2 = sid ? c.set[1].w2 : c.set[0].w2;
+  v.s2 = sid ? c.set[1].s2 : c.set[0].s2;
+  v.row_src = sid ? c.set[1].row_src : c.set[0].row_src;
+  v.src_div = sid ? c.set[1].src_div : c.set[0].src_div;
+  v.F = sid ? c.set[1].F : c.set[0].F;
+  v.h = sid ? c.set[1].h : c.set[0].h;
+  v.h_scale = sid ? c.set[1].h_scale : c.set[0].h_scale;
+  v.out = sid ? c.set[1].out : c.set[0].out;
+  return v;
+}
+
+// B operand prefetch depth (K steps of weights in flight per wave).
+template <int BM>
+constexpr int prefetch_depth() { return BM <= 32 ? 3 : 2; }
+
 // ---------------------------------------------------------------------------
 // Gate/up GEMM + SwiGLU + h quantisation. Tile: BM rows x 128 h columns
-// (128 gate + 128 up weight rows); wave w owns h columns [32w, 32w + 32).
-// A (activation rows, gathered) is staged through LDS, double buffered;
-// each wave streams its own weight rows straight into registers.
+// (128 gate + 128 up weight rows); wave w owns h columns [32w, 32w + 32) for
+// all BM rows. A (activation rows, gathered through the permutation) is
+// staged through LDS, double buffered and XOR-swizzled; each wave streams its
+// own weight rows straight into a register ring PD K-steps deep (no LDS: no
+// other wave reads them).
 // ---------------------------------------------------------------------------
 template <int BM>
 __global__ __launch_bounds__(kThreads) void gateup_fp8_kernel(FfnCall c,
@@ -206,6 +150,7 @@ __global__ __launch_bounds__(kThreads) void gateup_fp8_kernel(FfnCall c,
   constexpr int NB = 2 * NS;        // weight subtiles per wave (gate, up)
   constexpr int CH = BM * (kBK / 16);
   constexpr int CPT = (CH + kThreads - 1) / kThreads;
+  constexpr int PD = prefetch_depth<BM>();
 
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * kBK];
   __shared__ float sxl[BM];
@@ -215,7 +160,7 @@ __global__ __launch_bounds__(kThreads) void gateup_fp8_kernel(FfnCall c,
   if (!pick_tile(hdr->n_up, w)) return;
   const TileEntry te = list[w];
   const int sid = te.gid >> 16, g = te.gid & 0xffff;
-  const FfnSet S = (sid == 0) ? c.set[0] : c.set[1];
+  const SetView S = set_view(c, sid);
   const int d = c.d, F = S.F;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const uint8_t* a = static_cast<const uint8_t*>(c.a);
@@ -223,17 +168,15 @@ __global__ __launch_bounds__(kThreads) void gateup_fp8_kernel(FfnCall c,
   // activation rows of this tile (gathered), their scales into LDS
   const uint8_t* a_src[CPT];
   int a_dst[CPT];
-  bool a_ok[CPT];
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
     const int ch = tid + i * kThreads;
-    a_ok[i] = ch < CH;
     const int r = min(ch >> 3, BM - 1), c16 = ch & 7;
     const int grow = te.row0 + min(r, te.nrows - 1);
     const int src = min(max(S.row_src ? S.row_src[grow] / S.src_div : grow, 0), c.a_rows - 1);
     a_src[i] = a + (size_t)src * d + c16 * 16;
     a_dst[i] = swz(r, c16);
-    if (a_ok[i] && c16 == 0) sxl[r] = c.a_scale[src];
+    if (ch < CH && c16 == 0) sxl[r] = c.a_scale[src];
   }
   // weight rows of this wave
   const uint8_t* w13 = S.w13 + (size_t)g * 2 * F * d;
@@ -251,44 +194,53 @@ __global__ __launch_bounds__(kThreads) void gateup_fp8_kernel(FfnCall c,
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  uint4 a_stage[CPT];
-  v8i bcur[NB], bnext[NB];
+  const int KT = d / kBK;
+  v4i a_stage[CPT];
+  v8i bq[PD][NB];
+#pragma unroll
+  for (int s = 0; s < PD; ++s)
+    if (s < KT)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) bq[s][j] = glb_bfrag(b_src[j] + s * kBK);
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) a_stage[i] = *reinterpret_cast<const v4i*>(a_src[i]);
 #pragma unroll
   for (int i = 0; i < CPT; ++i)
-    if (a_ok[i]) a_stage[i] = *reinterpret_cast<const uint4*>(a_src[i]);
-#pragma unroll
-  for (int j = 0; j < NB; ++j) bcur[j] = glb_bfrag(b_src[j]);
-#pragma unroll
-  for (int i = 0; i < CPT; ++i)
-    if (a_ok[i]) *reinterpret_cast<uint4*>(&lds_a[0][a_dst[i]]) = a_stage[i];
+    if (CH % kThreads == 0 || tid + i * kThreads < CH)
+      *reinterpret_cast<v4i*>(&lds_a[0][a_dst[i]]) = a_stage[i];
   __syncthreads();
 
-  const int KT = d / kBK;
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < KT;
-    if (more) {
-      const int k0 = (kt + 1) * kBK;
+  for (int kt0 = 0; kt0 < KT; kt0 += PD) {
 #pragma unroll
-      for (int i = 0; i < CPT; ++i)
-        if (a_ok[i]) a_stage[i] = *reinterpret_cast<const uint4*>(a_src[i] + k0);
+    for (int s = 0; s < PD; ++s) {
+      const int kt = kt0 + s;
+      if (kt < KT) {
+        const int cur = kt & 1;
+        const bool more = kt + 1 < KT;
+        if (more) {
 #pragma unroll
-      for (int j = 0; j < NB; ++j) bnext[j] = glb_bfrag(b_src[j] + k0);
+          for (int i = 0; i < CPT; ++i)
+            a_stage[i] = *reinterpret_cast<const v4i*>(a_src[i] + (kt + 1) * kBK);
+        }
+#pragma unroll
+        for (int i = 0; i < MS; ++i) {
+          const v8i af = lds_afrag(lds_a[cur], i, lane);
+#pragma unroll
+          for (int j = 0; j < NB; ++j) acc[i][j] = mfma_fp8_16x16x128(af, bq[s][j], acc[i][j]);
+        }
+        if (kt + PD < KT) {
+#pragma unroll
+          for (int j = 0; j < NB; ++j) bq[s][j] = glb_bfrag(b_src[j] + (kt + PD) * kBK);
+        }
+        if (more) {
+#pragma unroll
+          for (int i = 0; i < CPT; ++i)
+            if (CH % kThreads == 0 || tid + i * kThreads < CH)
+              *reinterpret_cast<v4i*>(&lds_a[cur ^ 1][a_dst[i]]) = a_stage[i];
+        }
+        __syncthreads();
+      }
     }
-#pragma unroll
-    for (int i = 0; i < MS; ++i) {
-      const v8i af = lds_afrag(lds_a[cur], i, lane);
-#pragma unroll
-      for (int j = 0; j < NB; ++j) acc[i][j] = mfma_fp8_16x16x128(af, bcur[j], acc[i][j]);
-    }
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < CPT; ++i)
-        if (a_ok[i]) *reinterpret_cast<uint4*>(&lds_a[cur ^ 1][a_dst[i]]) = a_stage[i];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < NB; ++j) bcur[j] = bnext[j];
   }
 
   // ---- epilogue: scales, SwiGLU, per-(row, 128-col) amax ----
@@ -356,6 +308,7 @@ __global__ __launch_bounds__(kThreads) void down_fp8_kernel(FfnCall c,
   constexpr int NB = 4;  // 16-channel subtiles per wave
   constexpr int CH = BM * (kBK / 16);
   constexpr int CPT = (CH + kThreads - 1) / kThreads;
+  constexpr int PD = prefetch_depth<BM>();
 
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * kBK];
   __shared__ float hsl[2][BM];
@@ -364,17 +317,15 @@ __global__ __launch_bounds__(kThreads) void down_fp8_kernel(FfnCall c,
   if (!pick_tile(hdr->n_down, w)) return;
   const TileEntry te = list[w];
   const int sid = te.gid >> 16, g = te.gid & 0xffff;
-  const FfnSet S = (sid == 0) ? c.set[0] : c.set[1];
+  const SetView S = set_view(c, sid);
   const int d = c.d, F = S.F, hblocks = F / kHN;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
 
   const uint8_t* a_src[CPT];
   int a_dst[CPT];
-  bool a_ok[CPT];
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
     const int ch = tid + i * kThreads;
-    a_ok[i] = ch < CH;
     const int r = min(ch >> 3, BM - 1), c16 = ch & 7;
     const int grow = te.row0 + min(r, te.nrows - 1);
     a_src[i] = S.h + (size_t)grow * F + c16 * 16;
@@ -398,57 +349,66 @@ __global__ __launch_bounds__(kThreads) void down_fp8_kernel(FfnCall c,
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  uint4 a_stage[CPT];
+  const int KT = F / kBK;
+  v4i a_stage[CPT];
   float hs_stage = 0.f;
-  v8i bcur[NB], bnext[NB];
+  v8i bq[PD][NB];
+#pragma unroll
+  for (int s = 0; s < PD; ++s)
+    if (s < KT)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) bq[s][j] = glb_bfrag(b_src[j] + s * kBK);
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) a_stage[i] = *reinterpret_cast<const v4i*>(a_src[i]);
+  hs_stage = hs_src[0];
 #pragma unroll
   for (int i = 0; i < CPT; ++i)
-    if (a_ok[i]) a_stage[i] = *reinterpret_cast<const uint4*>(a_src[i]);
-  if (tid < BM) hs_stage = hs_src[0];
-#pragma unroll
-  for (int j = 0; j < NB; ++j) bcur[j] = glb_bfrag(b_src[j]);
-#pragma unroll
-  for (int i = 0; i < CPT; ++i)
-    if (a_ok[i]) *reinterpret_cast<uint4*>(&lds_a[0][a_dst[i]]) = a_stage[i];
+    if (CH % kThreads == 0 || tid + i * kThreads < CH)
+      *reinterpret_cast<v4i*>(&lds_a[0][a_dst[i]]) = a_stage[i];
   if (tid < BM) hsl[0][tid] = hs_stage;
   __syncthreads();
 
-  const int KT = F / kBK;
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < KT;
-    if (more) {
-      const int k0 = (kt + 1) * kBK;
+  for (int kt0 = 0; kt0 < KT; kt0 += PD) {
 #pragma unroll
-      for (int i = 0; i < CPT; ++i)
-        if (a_ok[i]) a_stage[i] = *reinterpret_cast<const uint4*>(a_src[i] + k0);
-      if (tid < BM) hs_stage = hs_src[kt + 1];
+    for (int s = 0; s < PD; ++s) {
+      const int kt = kt0 + s;
+      if (kt < KT) {
+        const int cur = kt & 1;
+        const bool more = kt + 1 < KT;
+        if (more) {
 #pragma unroll
-      for (int j = 0; j < NB; ++j) bnext[j] = glb_bfrag(b_src[j] + k0);
-    }
+          for (int i = 0; i < CPT; ++i)
+            a_stage[i] = *reinterpret_cast<const v4i*>(a_src[i] + (kt + 1) * kBK);
+          hs_stage = hs_src[kt + 1];
+        }
 #pragma unroll
-    for (int i = 0; i < MS; ++i) {
-      const v8i af = lds_afrag(lds_a[cur], i, lane);
-      v4f part[NB];
+        for (int i = 0; i < MS; ++i) {
+          const v8i af = lds_afrag(lds_a[cur], i, lane);
+          v4f part[NB];
 #pragma unroll
-      for (int j = 0; j < NB; ++j)
-        part[j] = mfma_fp8_16x16x128(af, bcur[j], v4f{0.f, 0.f, 0.f, 0.f});
+          for (int j = 0; j < NB; ++j)
+            part[j] = mfma_fp8_16x16x128(af, bq[s][j], v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float hs = hsl[cur][i * 16 + 4 * (lane >> 4) + q];
+          for (int q = 0; q < 4; ++q) {
+            const float hs = hsl[cur][i * 16 + 4 * (lane >> 4) + q];
 #pragma unroll
-        for (int j = 0; j < NB; ++j) acc[i][j][q] = fmaf(part[j][q], hs, acc[i][j][q]);
+            for (int j = 0; j < NB; ++j) acc[i][j][q] = fmaf(part[j][q], hs, acc[i][j][q]);
+          }
+        }
+        if (kt + PD < KT) {
+#pragma unroll
+          for (int j = 0; j < NB; ++j) bq[s][j] = glb_bfrag(b_src[j] + (kt + PD) * kBK);
+        }
+        if (more) {
+#pragma unroll
+          for (int i = 0; i < CPT; ++i)
+            if (CH % kThreads == 0 || tid + i * kThreads < CH)
+              *reinterpret_cast<v4i*>(&lds_a[cur ^ 1][a_dst[i]]) = a_stage[i];
+          if (tid < BM) hsl[cur ^ 1][tid] = hs_stage;
+        }
+        __syncthreads();
       }
     }
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < CPT; ++i)
-        if (a_ok[i]) *reinterpret_cast<uint4*>(&lds_a[cur ^ 1][a_dst[i]]) = a_stage[i];
-      if (tid < BM) hsl[cur ^ 1][tid] = hs_stage;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < NB; ++j) bcur[j] = bnext[j];
   }
 
   // ---- epilogue: channel scale, bf16 ----
@@ -520,21 +480,16 @@ __global__ __launch_bounds__(256) void down_f32_kernel(FfnCall c, int sid) {
   static_cast<float*>(S.out)[(size_t)r * d + m] = acc;
 }
 
-template <int BM>
-hipError_t launch_fp8_bm(const FfnCall& c, TileHeader* hdr, TileEntry* up, TileEntry* dn,
-                         hipStream_t s, const StepEvents& ev) {
-  const size_t cap_u = tiles_cap(c, BM, true), cap_d = tiles_cap(c, BM, false);
-  ev.mark(true, MOE_STEP_TILES, s);
-  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(kBuildThreads), 0, s, c, BM, hdr, up, dn,
-                     (int)cap_u, (int)cap_d);
-  ev.mark(false, MOE_STEP_TILES, s);
+template <int BM, int BMD>
+hipError_t launch_gemms_bm(const FfnCall& c, TileHeader* hdr, TileEntry* up, TileEntry* dn,
+                           size_t cap_u, size_t cap_d, hipStream_t s, const StepEvents& ev) {
   const size_t cu = align_up(cap_u, kXcds);
   const size_t cd = align_up(cap_d, kXcds);
   ev.mark(true, MOE_STEP_GATE_UP, s);
   if (cu > 0) hipLaunchKernelGGL(gateup_fp8_kernel<BM>, dim3((unsigned)cu), dim3(kThreads), 0, s, c, hdr, up);
   ev.mark(false, MOE_STEP_GATE_UP, s);
   ev.mark(true, MOE_STEP_DOWN, s);
-  if (cd > 0) hipLaunchKernelGGL(down_fp8_kernel<BM>, dim3((unsigned)cd), dim3(kThreads), 0, s, c, hdr, dn);
+  if (cd > 0) hipLaunchKernelGGL(down_fp8_kernel<BMD>, dim3((unsigned)cd), dim3(kThreads), 0, s, c, hdr, dn);
   ev.mark(false, MOE_STEP_DOWN, s);
   return hipGetLastError();
 }
@@ -556,16 +511,63 @@ size_t ffn_hs_bytes(int max_rows, int F) {
   return align_up((size_t)max_rows * (F / kHN) * sizeof(float), 256);
 }
 
+int choose_bm(int rows_hint) {
+  // fewest (M tiles x (BM + 64)): 64 rows' worth of cost per tile for
+  // streaming its weights, BM rows of MFMA work (padding included)
+  static const int cand[] = {16, 32, 64, 128, 192};
+  int best = 16;
+  long best_cost = -1;
+  for (int bm : cand) {
+    const long cost = (long)ceil_div(max(rows_hint, 1), bm) * (bm + 64);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = bm;
+    }
+  }
+  return best;
+}
+
+void tile_lists(const FfnCall& c, int bm_up, int bm_dn, void* ws, TileHeader** hdr,
+                TileEntry** up, TileEntry** dn, int* cap_up, int* cap_dn) {
+  *hdr = static_cast<TileHeader*>(ws);
+  *up = reinterpret_cast<TileEntry*>(*hdr + 1);
+  *dn = *up + tiles_cap(c, 16, true);
+  *cap_up = (int)tiles_cap(c, bm_up, true);
+  *cap_dn = (int)tiles_cap(c, bm_dn, false);
+}
+
+hipError_t launch_ffn_tiles(const FfnCall& c, int bm, void* ws, hipStream_t s) {
+  TileHeader* hdr;
+  TileEntry *up, *dn;
+  int cu, cd;
+  tile_lists(c, bm, down_bm(bm), ws, &hdr, &up, &dn, &cu, &cd);
+  hipLaunchKernelGGL(ffn_tiles_kernel, dim3(1), dim3(kTileThreads), 0, s, c, bm, hdr, up, dn, cu, cd);
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn_gemms(const FfnCall& c, int bm, void* ws, hipStream_t s,
+                            const StepEvents& ev) {
+  TileHeader* hdr;
+  TileEntry *up, *dn;
+  int cu, cd;
+  tile_lists(c, bm, down_bm(bm), ws, &hdr, &up, &dn, &cu, &cd);
+  switch (bm) {
+    case 16: return launch_gemms_bm<16, 16>(c, hdr, up, dn, cu, cd, s, ev);
+    case 32: return launch_gemms_bm<32, 32>(c, hdr, up, dn, cu, cd, s, ev);
+    case 64: return launch_gemms_bm<64, 64>(c, hdr, up, dn, cu, cd, s, ev);
+    case 128: return launch_gemms_bm<128, 128>(c, hdr, up, dn, cu, cd, s, ev);
+    default: return launch_gemms_bm<192, 128>(c, hdr, up, dn, cu, cd, s, ev);
+  }
+}
+
 hipError_t launch_grouped_ffn_fp8(const FfnCall& c, void* tiles_ws, int rows_hint, hipStream_t s,
                                   const StepEvents& ev) {
-  TileHeader* hdr = static_cast<TileHeader*>(tiles_ws);
-  TileEntry* up = reinterpret_cast<TileEntry*>(hdr + 1);
-  const size_t cap_up16 = tiles_cap(c, 16, true);
-  TileEntry* dn = up + cap_up16;
-  if (rows_hint <= 24) return launch_fp8_bm<16>(c, hdr, up, dn, s, ev);
-  if (rows_hint <= 48) return launch_fp8_bm<32>(c, hdr, up, dn, s, ev);
-  if (rows_hint <= 96) return launch_fp8_bm<64>(c, hdr, up, dn, s, ev);
-  return launch_fp8_bm<128>(c, hdr, up, dn, s, ev);
+  const int bm = choose_bm(rows_hint);
+  ev.mark(true, MOE_STEP_TILES, s);
+  hipError_t e = launch_ffn_tiles(c, bm, tiles_ws, s);
+  ev.mark(false, MOE_STEP_TILES, s);
+  if (e != hipSuccess) return e;
+  return launch_ffn_gemms(c, bm, tiles_ws, s, ev);
 }
 
 hipError_t launch_grouped_ffn_f32(const FfnCall& c, hipStream_t s, const StepEvents& ev) {

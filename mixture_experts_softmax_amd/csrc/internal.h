@@ -13,16 +13,26 @@ constexpr int kRouteTokens = 16;
 constexpr int kPermTile = 64;
 
 // ----- router ---------------------------------------------------------------
-hipError_t launch_route_bf16(const uint16_t* x, const uint16_t* w_router, const float* bias,
-                             int T, int d, int E, int k, int32_t* ids, float* w,
-                             uint8_t* xq, float* x_scale, hipStream_t s);
-hipError_t launch_route_f32(const float* x, const float* w_router, const float* bias, int T,
-                            int d, int E, int k, int32_t* ids, float* w, hipStream_t s);
+// logits [T][E] float32 scratch; masks/counts (optional, [ceil(T/64)][E]) get
+// the permutation's per-tile expert masks and counts.
+size_t route_ws_bytes(int T, int E);
+hipError_t launch_route(bool bf16, const void* x, const void* w_router, const float* bias, int T,
+                        int d, int E, int k, int32_t* ids, float* w, uint8_t* xq, float* x_scale,
+                        float* logits, uint64_t* masks, int32_t* counts, hipStream_t s);
 
 // ----- permutation ----------------------------------------------------------
+size_t perm_masks_bytes(int T, int E);
+size_t perm_counts_bytes(int T, int E);
 size_t permute_ws_bytes(int T, int E);
 hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* offsets,
                           int32_t* sorted_pair, int32_t* pair_to_row, void* ws, hipStream_t s);
+struct FfnCall;
+// scan + scatter from masks/counts already computed (counts become the tile
+// bases); with c != nullptr also writes the grouped-FFN tile lists of c.
+hipError_t launch_perm_scan_scatter(const int32_t* ids, int T, int E, int k, uint64_t* masks,
+                                    int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
+                                    int32_t* pair_to_row, const FfnCall* c, int bm, void* tiles_ws,
+                                    hipStream_t s);
 
 // ----- grouped FFN ----------------------------------------------------------
 // A "set" is a family of groups sharing one weight layout: the routed experts
@@ -70,6 +80,10 @@ struct StepEvents {
 size_t ffn_tiles_ws_bytes(const FfnCall& c);
 size_t ffn_h_bytes(int max_rows, int F, bool fp8);
 size_t ffn_hs_bytes(int max_rows, int F);
+int choose_bm(int rows_hint);
+hipError_t launch_ffn_tiles(const FfnCall& c, int bm, void* tiles_ws, hipStream_t s);
+hipError_t launch_ffn_gemms(const FfnCall& c, int bm, void* tiles_ws, hipStream_t s,
+                            const StepEvents& ev = StepEvents());
 hipError_t launch_grouped_ffn_fp8(const FfnCall& c, void* tiles_ws, int rows_hint, hipStream_t s,
                                   const StepEvents& ev = StepEvents());
 hipError_t launch_grouped_ffn_f32(const FfnCall& c, hipStream_t s,

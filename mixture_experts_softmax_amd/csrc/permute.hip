@@ -1,25 +1,32 @@
 // Permutation of (token, slot) pairs into expert-contiguous rows, ascending
 // token order inside each expert's group (the scatter the InferX page, section
-// 3.3, places after its top-k router). Deterministic and atomic-free in global
-// memory:
-//   1. count:   per 64-token tile, a 64-bit token mask per expert in LDS
-//               (ds_or), its popcount is the tile's count for that expert;
-//   2. scan:    per expert, exclusive prefix over tiles; exclusive prefix over
-//               experts of the totals gives offsets[E+1];
-//   3. scatter: row = offsets[e] + tile prefix[e] + popcount(mask[e] below the
+// 3.3, places after its top-k router). Deterministic, no global atomics:
+//   1. count:   per 64-token tile, a 64-bit token mask per expert (ds_or in
+//               LDS) and its popcount. The layer path gets both from the
+//               top-k kernel instead.
+//   2. scan:    one workgroup; per expert an exclusive prefix over tiles (tile
+//               counts staged through LDS in chunks), then an exclusive prefix
+//               over experts gives offsets[E+1]. In the layer path the same
+//               workgroup also writes the grouped-FFN tile lists, since it is
+//               the first to know every group's size.
+//   3. scatter: row = offsets[e] + tile base[e] + popcount(mask[e] below the
 //               token's lane).
 #include "common.h"
 #include "internal.h"
+#include "tiles.h"
 
 namespace moe {
 
 namespace {
 
-constexpr int kScanThreads = 256;  // >= MOE_MAX_E
+constexpr int kScanThreads = 1024;
+constexpr int kScanStage = 8192;  // tile counts staged per chunk (32 KiB of LDS)
 
-// Builds the per-expert token masks of one 64-token tile in LDS.
-__device__ void tile_masks(const int32_t* __restrict__ ids, int T, int E, int k,
-                           unsigned long long* mask) {
+__global__ __launch_bounds__(kPermTile) void perm_count_kernel(const int32_t* __restrict__ ids,
+                                                               int T, int E, int k,
+                                                               uint64_t* __restrict__ masks,
+                                                               int32_t* __restrict__ counts) {
+  __shared__ unsigned long long mask[MOE_MAX_E];
   const int lane = threadIdx.x;
   for (int e = lane; e < E; e += kPermTile) mask[e] = 0ull;
   __syncthreads();
@@ -31,55 +38,78 @@ __device__ void tile_masks(const int32_t* __restrict__ ids, int T, int E, int k,
     }
   }
   __syncthreads();
-}
-
-__global__ __launch_bounds__(kPermTile) void perm_count_kernel(const int32_t* __restrict__ ids,
-                                                               int T, int E, int k,
-                                                               int32_t* __restrict__ counts) {
-  __shared__ unsigned long long mask[256];
-  tile_masks(ids, T, E, k, mask);
-  for (int e = threadIdx.x; e < E; e += kPermTile)
+  for (int e = lane; e < E; e += kPermTile) {
+    masks[(size_t)blockIdx.x * E + e] = mask[e];
     counts[(size_t)blockIdx.x * E + e] = __popcll(mask[e]);
+  }
 }
 
-// One workgroup: per-expert scan over tiles (counts -> tile bases in place)
-// and the exclusive scan over experts.
-__global__ __launch_bounds__(kScanThreads) void perm_scan_kernel(int32_t* __restrict__ counts,
-                                                                 int ntiles, int E,
-                                                                 int32_t* __restrict__ offsets) {
-  __shared__ int32_t tot[kScanThreads];
-  const int e = threadIdx.x;
+// One workgroup. counts [ntiles][E] is replaced by the per-tile bases. With
+// hdr != nullptr also emits the tile lists of `c` (set 0 = the E routed
+// groups with these offsets, set 1 = the shared expert if present).
+__global__ __launch_bounds__(kScanThreads) void perm_scan_kernel(
+    int32_t* __restrict__ counts, int ntiles, int E, int32_t* __restrict__ offsets, FfnCall c,
+    int bm, TileHeader* hdr, TileEntry* up, TileEntry* down, int cap_up, int cap_dn) {
+  __shared__ int stage[kScanStage];
+  __shared__ int tot[MOE_MAX_E];
+  __shared__ TileLds L;
+  const int tid = threadIdx.x;
   int run = 0;
-  if (e < E) {
-    for (int t = 0; t < ntiles; ++t) {
-      const int c = counts[(size_t)t * E + e];
-      counts[(size_t)t * E + e] = run;
-      run += c;
+  const int ct = kScanStage / E;  // tiles per chunk
+  for (int t0 = 0; t0 < ntiles; t0 += ct) {
+    const int nt = min(ct, ntiles - t0);
+    for (int i = tid; i < nt * E; i += kScanThreads) stage[i] = counts[(size_t)t0 * E + i];
+    __syncthreads();
+    if (tid < E) {
+      for (int t = 0; t < nt; ++t) {
+        const int v = stage[t * E + tid];
+        stage[t * E + tid] = run;
+        run += v;
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < nt * E; i += kScanThreads) counts[(size_t)t0 * E + i] = stage[i];
+    __syncthreads();
+  }
+  // inclusive scan of the per-expert totals (Hillis-Steele over MOE_MAX_E entries)
+  if (tid < MOE_MAX_E) tot[tid] = (tid < E) ? run : 0;
+  __syncthreads();
+  for (int o = 1; o < MOE_MAX_E; o <<= 1) {
+    const int v = (tid < MOE_MAX_E && tid >= o) ? tot[tid - o] : 0;
+    __syncthreads();
+    if (tid < MOE_MAX_E) tot[tid] += v;
+    __syncthreads();
+  }
+  if (tid < E) offsets[tid + 1] = tot[tid];
+  if (tid == 0) offsets[0] = 0;
+  if (hdr == nullptr) return;
+
+  // groups: routed experts (set 0), then the shared expert (set 1)
+  const int NG = E + (c.nsets > 1 ? 1 : 0);
+  for (int i = tid; i < NG; i += kScanThreads) {
+    if (i < E) {
+      L.g_row0[i] = (i == 0) ? 0 : tot[i - 1];
+      L.g_rows[i] = tot[i] - L.g_row0[i];
+      L.g_set[i] = 0;
+    } else {
+      L.g_row0[i] = 0;
+      L.g_rows[i] = min(c.set[1].rows_fixed, c.set[1].max_rows);
+      L.g_set[i] = 1;
     }
   }
-  tot[e] = (e < E) ? run : 0;
   __syncthreads();
-  // Hillis-Steele inclusive scan over kScanThreads entries
-  for (int o = 1; o < kScanThreads; o <<= 1) {
-    const int v = (e >= o) ? tot[e - o] : 0;
-    __syncthreads();
-    tot[e] += v;
-    __syncthreads();
-  }
-  if (e < E) offsets[e + 1] = tot[e];
-  if (e == 0) offsets[0] = 0;
+  emit_tiles(c, bm, NG, E, L, hdr, up, down, cap_up, cap_dn);
 }
 
 __global__ __launch_bounds__(kPermTile) void perm_scatter_kernel(
-    const int32_t* __restrict__ ids, int T, int E, int k, const int32_t* __restrict__ base,
-    const int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pair,
-    int32_t* __restrict__ pair_to_row) {
-  __shared__ unsigned long long mask[256];
-  tile_masks(ids, T, E, k, mask);
+    const int32_t* __restrict__ ids, int T, int E, int k, const uint64_t* __restrict__ masks,
+    const int32_t* __restrict__ bases, const int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_to_row) {
   const int lane = threadIdx.x;
   const int t = blockIdx.x * kPermTile + lane;
   if (t >= T) return;
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const size_t tb = (size_t)blockIdx.x * E;
   for (int j = 0; j < k; ++j) {
     const int p = t * k + j;
     const int e = ids[p];
@@ -87,7 +117,7 @@ __global__ __launch_bounds__(kPermTile) void perm_scatter_kernel(
       pair_to_row[p] = -1;
       continue;
     }
-    const int row = offsets[e] + base[(size_t)blockIdx.x * E + e] + __popcll(mask[e] & below);
+    const int row = offsets[e] + bases[tb + e] + __popcll(masks[tb + e] & below);
     sorted_pair[row] = p;
     pair_to_row[p] = row;
   }
@@ -95,21 +125,43 @@ __global__ __launch_bounds__(kPermTile) void perm_scatter_kernel(
 
 }  // namespace
 
-size_t permute_ws_bytes(int T, int E) {
+size_t perm_masks_bytes(int T, int E) {
+  return align_up((size_t)ceil_div(T, kPermTile) * E * sizeof(uint64_t), 256);
+}
+size_t perm_counts_bytes(int T, int E) {
   return align_up((size_t)ceil_div(T, kPermTile) * E * sizeof(int32_t), 256);
+}
+size_t permute_ws_bytes(int T, int E) { return perm_masks_bytes(T, E) + perm_counts_bytes(T, E); }
+
+hipError_t launch_perm_scan_scatter(const int32_t* ids, int T, int E, int k, uint64_t* masks,
+                                    int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
+                                    int32_t* pair_to_row, const FfnCall* c, int bm, void* tiles_ws,
+                                    hipStream_t s) {
+  const int ntiles = ceil_div(T, kPermTile);
+  TileHeader* hdr = nullptr;
+  TileEntry *up = nullptr, *dn = nullptr;
+  int cap_up = 0, cap_dn = 0;
+  FfnCall cc{};
+  if (c != nullptr && tiles_ws != nullptr) {
+    cc = *c;
+    tile_lists(cc, bm, down_bm(bm), tiles_ws, &hdr, &up, &dn, &cap_up, &cap_dn);
+  }
+  hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, counts, ntiles, E,
+                     offsets, cc, bm, hdr, up, dn, cap_up, cap_dn);
+  hipLaunchKernelGGL(perm_scatter_kernel, dim3(ntiles), dim3(kPermTile), 0, s, ids, T, E, k, masks,
+                     counts, offsets, sorted_pair, pair_to_row);
+  return hipGetLastError();
 }
 
 hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* offsets,
                           int32_t* sorted_pair, int32_t* pair_to_row, void* ws, hipStream_t s) {
-  const int ntiles = ceil_div(T, kPermTile);
-  int32_t* counts = static_cast<int32_t*>(ws);
-  hipLaunchKernelGGL(perm_count_kernel, dim3(ntiles), dim3(kPermTile), 0, s, ids, T, E, k,
-                     counts);
-  hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, counts, ntiles, E,
-                     offsets);
-  hipLaunchKernelGGL(perm_scatter_kernel, dim3(ntiles), dim3(kPermTile), 0, s, ids, T, E, k,
-                     counts, offsets, sorted_pair, pair_to_row);
-  return hipGetLastError();
+  uint64_t* masks = static_cast<uint64_t*>(ws);
+  int32_t* counts =
+      reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + perm_masks_bytes(T, E));
+  hipLaunchKernelGGL(perm_count_kernel, dim3(ceil_div(T, kPermTile)), dim3(kPermTile), 0, s, ids,
+                     T, E, k, masks, counts);
+  return launch_perm_scan_scatter(ids, T, E, k, masks, counts, offsets, sorted_pair, pair_to_row,
+                                  nullptr, 0, nullptr, s);
 }
 
 }  // namespace moe

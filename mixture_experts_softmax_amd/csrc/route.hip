@@ -1,7 +1,11 @@
-// Router kernels: logits GEMM, softmax + top-k selection with renormalised
-// gate weights, and (bf16/FP8 path) per-token FP8 quantisation of x -- one
-// kernel per path, as the NVIDIA Sarvam blog's Table 1 row "Router logits and
-// TopK" fuses logit computation and selection (its paragraph on MoE routing).
+// Router: logits GEMM, then softmax + top-k selection with renormalised gate
+// weights, and (bf16/FP8 path) per-token FP8 quantisation of x. The NVIDIA
+// Sarvam blog (Table 1 row "Router logits and TopK", MoE-routing paragraph)
+// fuses logit computation and selection into one kernel to cut launches and
+// memory round trips; here the logits of a token tile never leave the L2
+// between the two kernels, and the split buys parallelism: a T=64 decode
+// step spreads its 4096-deep dot products over 16 workgroups x 4 waves
+// instead of 4 workgroups.
 //
 // Selection rule: the k largest logits, largest first, equal logits ordered
 // by lower expert index. Gate weights are the softmax over all E logits
@@ -17,123 +21,64 @@ namespace moe {
 
 namespace {
 
-constexpr int kRouteWaves = 4;
-constexpr int kMaxPerLane = 4;  // E <= 256 = 64 lanes * 4
-constexpr int kLgStride = 257;  // logits row stride in LDS (E <= 256, +1 pad)
+constexpr int kLogitWaves = 4;     // K split across the waves of a logits tile
+constexpr int kLogitExperts = 32;  // experts per logits tile (2 MFMA column tiles)
+constexpr int kMaxPerLane = 4;     // E <= 256 = 64 lanes * 4
+constexpr int kTopkWaves = 16;     // one 64-token tile per top-k workgroup
+constexpr int kTokPerWave = kPermTile / kTopkWaves;
 
-// Wave-cooperative top-k over E <= 256 values held 4 per lane (expert
-// lane + 64 * c in slot c; -inf for padding). Writes ids/weights for one token.
-__device__ void wave_topk_store(const float (&v)[kMaxPerLane], int E, int k, int lane,
-                                int32_t* ids_out, float* w_out) {
-  bool taken[kMaxPerLane] = {false, false, false, false};
-  int my_e = 0;
-  float my_v = -FLT_MAX;
-  float top = 0.f;
-  for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int c = 0; c < kMaxPerLane; ++c) {
-      const int e = lane + kWave * c;
-      if (e < E && !taken[c] && (v[c] > bv || (v[c] == bv && e < bi))) {
-        bv = v[c];
-        bi = e;
-      }
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, kWave);
-      const int oi = __shfl_xor(bi, o, kWave);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if ((bi & (kWave - 1)) == lane) {
-#pragma unroll
-      for (int c = 0; c < kMaxPerLane; ++c)
-        if (bi == lane + kWave * c) taken[c] = true;
-    }
-    if (j == 0) top = bv;
-    if (lane == j) {
-      my_e = bi;
-      my_v = bv;
-    }
-  }
-  const float ex = (lane < k) ? expf(my_v - top) : 0.f;
-  float den = ex;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o, kWave);
-  if (lane < k) {
-    ids_out[lane] = my_e;
-    w_out[lane] = ex / den;
-  }
-}
-
-// bf16 router: one workgroup per 16 tokens, 4 waves splitting the experts in
-// 16-wide MFMA column tiles (bf16 16x16x32, float32 accumulation).
-__global__ __launch_bounds__(kRouteWaves * kWave) void route_bf16_kernel(
+// ---------------------------------------------------------------------------
+// Logits, bf16: tile = 16 tokens x 32 experts; wave w accumulates K range
+// [w*d/4, (w+1)*d/4) with bf16 16x16x32 MFMAs; the partial tiles are summed
+// in LDS (fixed order: wave 0..3). Blocks with blockIdx.y == 0 also quantise
+// their tokens' x rows to FP8.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kLogitWaves * kWave) void route_logits_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
-    const float* __restrict__ bias, int T, int d, int E, int k, int32_t* __restrict__ ids,
-    float* __restrict__ wts, uint8_t* __restrict__ xq, float* __restrict__ xs) {
-  __shared__ float lg[kRouteTokens][kLgStride];
+    const float* __restrict__ bias, int T, int d, int E, float* __restrict__ logits,
+    uint8_t* __restrict__ xq, float* __restrict__ xs) {
+  __shared__ float part[kLogitWaves][kRouteTokens][kLogitExperts + 1];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int tok0 = blockIdx.x * kRouteTokens;
-  const int nsub = ceil_div(E, 16);
+  const int e0 = blockIdx.y * kLogitExperts;
 
-  // ---- logits: lane holds token row (lane % 16), K slice (lane / 16) * 8 ----
-  v4f acc[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
   const int tok = min(tok0 + (lane & 15), T - 1);
-  const uint16_t* xrow = x + (size_t)tok * d + (lane >> 4) * 8;
-  const uint16_t* wrow[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = min((wave + kRouteWaves * i) * 16 + (lane & 15), E - 1);
-    wrow[i] = wr + (size_t)e * d + (lane >> 4) * 8;
-  }
-#pragma unroll 4
-  for (int k0 = 0; k0 < d; k0 += 32) {
-    const v8bf a = *reinterpret_cast<const v8bf*>(xrow + k0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (wave + kRouteWaves * i < nsub) {
-        const v8bf b = *reinterpret_cast<const v8bf*>(wrow[i] + k0);
-        acc[i] = mfma_bf16_16x16x32(a, b, acc[i]);
-      }
-    }
+  const int kslice = d / kLogitWaves;
+  const int kbeg = wave * kslice + (lane >> 4) * 8;
+  const uint16_t* xrow = x + (size_t)tok * d + kbeg;
+  const uint16_t* w0 = wr + (size_t)min(e0 + (lane & 15), E - 1) * d + kbeg;
+  const uint16_t* w1 = wr + (size_t)min(e0 + 16 + (lane & 15), E - 1) * d + kbeg;
+  v4f a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+  for (int k0 = 0; k0 < kslice; k0 += 32) {
+    const v8bf xa = *reinterpret_cast<const v8bf*>(xrow + k0);
+    const v8bf b0 = *reinterpret_cast<const v8bf*>(w0 + k0);
+    const v8bf b1 = *reinterpret_cast<const v8bf*>(w1 + k0);
+    a0 = mfma_bf16_16x16x32(xa, b0, a0);
+    a1 = mfma_bf16_16x16x32(xa, b1, a1);
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int s = wave + kRouteWaves * i;
-    if (s < nsub) {
-      const int e = s * 16 + (lane & 15);
-      const float b = (bias != nullptr && e < E) ? bias[e] : 0.f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) lg[4 * (lane >> 4) + q][e] = acc[i][q] + b;
-    }
+  for (int q = 0; q < 4; ++q) {
+    part[wave][4 * (lane >> 4) + q][lane & 15] = a0[q];
+    part[wave][4 * (lane >> 4) + q][16 + (lane & 15)] = a1[q];
   }
   __syncthreads();
-
-  // ---- top-k + gates: wave w handles token rows 4w .. 4w+3 ----
-  for (int r = 0; r < 4; ++r) {
-    const int row = wave * 4 + r;
-    const int t = tok0 + row;
-    if (t >= T) break;
-    float v[kMaxPerLane];
+  for (int i = threadIdx.x; i < kRouteTokens * kLogitExperts; i += kLogitWaves * kWave) {
+    const int r = i / kLogitExperts, c = i % kLogitExperts;
+    const int t = tok0 + r, e = e0 + c;
+    if (t < T && e < E) {
+      float v = part[0][r][c];
 #pragma unroll
-    for (int c = 0; c < kMaxPerLane; ++c) {
-      const int e = lane + kWave * c;
-      v[c] = (e < E) ? lg[row][e] : -INFINITY;
+      for (int w = 1; w < kLogitWaves; ++w) v += part[w][r][c];
+      logits[(size_t)t * E + e] = v + (bias != nullptr ? bias[e] : 0.f);
     }
-    wave_topk_store(v, E, k, lane, ids + (size_t)t * k, wts + (size_t)t * k);
   }
 
   // ---- FP8 quantisation of x, per token: s = amax / 448, codes E4M3(x / s) ----
-  for (int r = 0; r < 4; ++r) {
-    const int t = tok0 + wave * 4 + r;
+  if (blockIdx.y != 0 || xq == nullptr) return;
+  for (int r = 0; r < kRouteTokens / kLogitWaves; ++r) {
+    const int t = tok0 + wave * (kRouteTokens / kLogitWaves) + r;
     if (t >= T) break;
     const uint16_t* xr = x + (size_t)t * d;
     float amax = 0.f;
@@ -169,46 +114,122 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void route_bf16_kernel(
   }
 }
 
-// float32 router: one wave per token; lane computes the logits of experts
-// lane + 64c with a sequential float32 dot product.
-__global__ __launch_bounds__(kRouteWaves * kWave) void route_f32_kernel(
+// Logits, float32: one wave per token, lane computes experts lane + 64c with a
+// sequential float32 dot product.
+__global__ __launch_bounds__(kLogitWaves * kWave) void route_logits_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias,
-    int T, int d, int E, int k, int32_t* __restrict__ ids, float* __restrict__ wts) {
+    int T, int d, int E, float* __restrict__ logits) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int t = blockIdx.x * kRouteWaves + threadIdx.x / kWave;
+  const int t = blockIdx.x * kLogitWaves + threadIdx.x / kWave;
   if (t >= T) return;
   const float* xr = x + (size_t)t * d;
-  float v[kMaxPerLane];
+  for (int e = lane; e < E; e += kWave) {
+    const float* w = wr + (size_t)e * d;
+    float acc = 0.f;
+    for (int i = 0; i < d; ++i) acc = fmaf(xr[i], w[i], acc);
+    logits[(size_t)t * E + e] = acc + (bias != nullptr ? bias[e] : 0.f);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Top-k over the logits of one 64-token tile: wave w takes tokens 4w..4w+3;
+// k rounds of a 64-lane (value desc, index asc) argmax butterfly. Optionally
+// records, per expert, the 64-bit mask of the tile's tokens routed to it and
+// its popcount (the permutation's per-tile histogram).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kTopkWaves * kWave) void route_topk_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ ids,
+    float* __restrict__ wts, uint64_t* __restrict__ masks, int32_t* __restrict__ counts) {
+  __shared__ unsigned long long mask[MOE_MAX_E];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int tile = blockIdx.x;
+  if (masks != nullptr) {
+    for (int e = threadIdx.x; e < E; e += kTopkWaves * kWave) mask[e] = 0ull;
+    __syncthreads();
+  }
+  for (int r = 0; r < kTokPerWave; ++r) {
+    const int tl = wave * kTokPerWave + r;  // token within the tile
+    const int t = tile * kPermTile + tl;
+    if (t >= T) break;
+    const float* lr = logits + (size_t)t * E;
+    float v[kMaxPerLane];
+    bool taken[kMaxPerLane];
 #pragma unroll
-  for (int c = 0; c < kMaxPerLane; ++c) {
-    const int e = lane + kWave * c;
-    if (e < E) {
-      const float* w = wr + (size_t)e * d;
-      float acc = 0.f;
-      for (int i = 0; i < d; ++i) acc = fmaf(xr[i], w[i], acc);
-      v[c] = acc + (bias != nullptr ? bias[e] : 0.f);
-    } else {
-      v[c] = -INFINITY;
+    for (int c = 0; c < kMaxPerLane; ++c) {
+      const int e = lane + kWave * c;
+      v[c] = (e < E) ? lr[e] : -INFINITY;
+      taken[c] = false;
+    }
+    int my_e = 0;
+    float my_v = -FLT_MAX, top = 0.f;
+    for (int j = 0; j < k; ++j) {
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int c = 0; c < kMaxPerLane; ++c) {
+        const int e = lane + kWave * c;
+        if (e < E && !taken[c] && (v[c] > bv || (v[c] == bv && e < bi))) {
+          bv = v[c];
+          bi = e;
+        }
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, kWave);
+        const int oi = __shfl_xor(bi, o, kWave);
+        if (ov > bv || (ov == bv && oi < bi)) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < kMaxPerLane; ++c)
+        if (bi == lane + kWave * c) taken[c] = true;
+      if (j == 0) top = bv;
+      if (lane == j) {
+        my_e = bi;
+        my_v = bv;
+      }
+    }
+    const float ex = (lane < k) ? expf(my_v - top) : 0.f;
+    float den = ex;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o, kWave);
+    if (lane < k) {
+      ids[(size_t)t * k + lane] = my_e;
+      wts[(size_t)t * k + lane] = ex / den;
+      if (masks != nullptr) atomicOr(&mask[my_e], 1ull << tl);
     }
   }
-  wave_topk_store(v, E, k, lane, ids + (size_t)t * k, wts + (size_t)t * k);
+  if (masks != nullptr) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += kTopkWaves * kWave) {
+      masks[(size_t)tile * E + e] = mask[e];
+      counts[(size_t)tile * E + e] = __popcll(mask[e]);
+    }
+  }
 }
 
 }  // namespace
 
-hipError_t launch_route_bf16(const uint16_t* x, const uint16_t* w_router, const float* bias,
-                             int T, int d, int E, int k, int32_t* ids, float* w, uint8_t* xq,
-                             float* x_scale, hipStream_t s) {
-  const dim3 grid(ceil_div(T, kRouteTokens)), block(kRouteWaves * kWave);
-  hipLaunchKernelGGL(route_bf16_kernel, grid, block, 0, s, x, w_router, bias, T, d, E, k, ids,
-                     w, xq, x_scale);
-  return hipGetLastError();
-}
+size_t route_ws_bytes(int T, int E) { return align_up((size_t)T * E * sizeof(float), 256); }
 
-hipError_t launch_route_f32(const float* x, const float* w_router, const float* bias, int T,
-                            int d, int E, int k, int32_t* ids, float* w, hipStream_t s) {
-  const dim3 grid(ceil_div(T, kRouteWaves)), block(kRouteWaves * kWave);
-  hipLaunchKernelGGL(route_f32_kernel, grid, block, 0, s, x, w_router, bias, T, d, E, k, ids, w);
+hipError_t launch_route(bool bf16, const void* x, const void* w_router, const float* bias, int T,
+                        int d, int E, int k, int32_t* ids, float* w, uint8_t* xq, float* x_scale,
+                        float* logits, uint64_t* masks, int32_t* counts, hipStream_t s) {
+  if (bf16) {
+    const dim3 grid(ceil_div(T, kRouteTokens), ceil_div(E, kLogitExperts));
+    hipLaunchKernelGGL(route_logits_bf16_kernel, grid, dim3(kLogitWaves * kWave), 0, s,
+                       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router),
+                       bias, T, d, E, logits, xq, x_scale);
+  } else {
+    hipLaunchKernelGGL(route_logits_f32_kernel, dim3(ceil_div(T, kLogitWaves)),
+                       dim3(kLogitWaves * kWave), 0, s, static_cast<const float*>(x),
+                       static_cast<const float*>(w_router), bias, T, d, E, logits);
+  }
+  hipLaunchKernelGGL(route_topk_kernel, dim3(ceil_div(T, kPermTile)), dim3(kTopkWaves * kWave), 0,
+                     s, logits, T, E, k, ids, w, masks, counts);
   return hipGetLastError();
 }
 

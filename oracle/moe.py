@@ -192,16 +192,20 @@ def ffn_fp32(x: np.ndarray, ew: ExpertWeights) -> np.ndarray:
     return h @ np.asarray(ew.w2, np.float64).T
 
 
-def swiglu_h_fp8(xq: np.ndarray, s_x: np.ndarray, ew: ExpertWeights) -> np.ndarray:
-    """The SwiGLU activation of rows whose x is already quantised (codes xq,
-    per-row scales s_x), before h is quantised:
-        g, u = s_x * s_w13[n] * sum_i xq_i q13[n, i]   (gate rows n < F, up rows n >= F)
-        h    = silu(g) * u
-    The dot products of E4M3 values are exact in float64."""
-    F = ew.w13.shape[0] // 2
+def gate_up_fp8(xq: np.ndarray, s_x: np.ndarray, ew: ExpertWeights) -> np.ndarray:
+    """gu[r, n] = s_x[r] * s_w13[n] * sum_i xq[r, i] q13[n, i] for rows whose x
+    is already quantised (codes xq, per-row scales s_x); columns n < F are the
+    gate, n >= F the up projection. The dot products of E4M3 values are exact
+    in float64 (every partial sum is a multiple of 2^-18 below 2^31)."""
     xv = codecs.e4m3_decode(xq)                                # [R][d]
     gu = xv @ codecs.e4m3_decode(ew.w13).T                      # [R][2F]
-    gu = gu * np.asarray(s_x, np.float64)[:, None] * np.asarray(ew.w13_scale, np.float64)[None, :]
+    return gu * np.asarray(s_x, np.float64)[:, None] * np.asarray(ew.w13_scale, np.float64)[None, :]
+
+
+def swiglu_h_fp8(xq: np.ndarray, s_x: np.ndarray, ew: ExpertWeights) -> np.ndarray:
+    """h = silu(gate) * up, before h is quantised."""
+    F = ew.w13.shape[0] // 2
+    gu = gate_up_fp8(xq, s_x, ew)
     return silu(gu[:, :F]) * gu[:, F:]
 
 

@@ -162,7 +162,7 @@ def make_layer(cfg: LayerConfig, device="cpu", hooks: Optional[RoutingHooks] = N
         bias = bias_for(beta)
 
     redraws = 0
-    if hooks is not None and T > 0:
+    if hooks is not None and T > 0 and not zero_x:  # an all-zero x ties every logit on purpose
         rd = np.random.Generator(np.random.PCG64(kids[_REDRAW]))
         for _ in range(1000):
             bad = hooks.near_tie(act_values(x_t), wr64, bias, k, min_gap)

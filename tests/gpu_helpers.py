@@ -69,7 +69,8 @@ def run_stepwise(lt: LayerTensors, x=None):
     w = torch.empty((T, k), dtype=f32, device=DEV)
     xq = torch.empty((T, d), dtype=torch.uint8, device=DEV) if fp8 else None
     xs = torch.empty((T,), dtype=f32, device=DEV) if fp8 else None
-    _lib.moe_route_topk(s, x, lt.w_router, lt.router_bias, ids, w, xq, xs)
+    _lib.moe_route_topk(s, x, lt.w_router, lt.router_bias, ids, w, xq, xs,
+                        moe_lib.alloc_workspace(_lib.moe_route_workspace_size(s), DEV))
     off = torch.empty(E + 1, dtype=i32, device=DEV)
     sp = torch.empty(T * k, dtype=i32, device=DEV)
     p2r = torch.empty(T * k, dtype=i32, device=DEV)
@@ -145,9 +146,8 @@ def fp8_bounds(inp, st, tokens=None):
     for e in np.unique(ids):
         sel = np.argwhere(ids == e)           # (token index, slot)
         ew = inp.expert(int(e))
-        h64 = omoe.swiglu_h_fp8(xq[sel[:, 0]], sx[sel[:, 0]], ew)
         rows = p2r[tokens[sel[:, 0]] * k + sel[:, 1]]
-        n, dhq = FC.validate_h(h64, st["h"][rows], st["hs"][rows])
+        n, dhq = FC.validate_h(xq[sel[:, 0]], sx[sel[:, 0]], ew, st["h"][rows], st["hs"][rows])
         flips += n
         eff = FC.down_effect(dhq, ew)
         for i, r in enumerate(rows):
@@ -159,8 +159,7 @@ def fp8_bounds(inp, st, tokens=None):
             extra[i] += w[i, j] * row_bound[int(p2r[t * k + j])]
     shared_extra = None
     if inp.shared is not None:
-        h64 = omoe.swiglu_h_fp8(xq, sx, inp.shared)
-        n, dhq = FC.validate_h(h64, st["h_sh"][tokens], st["hs_sh"][tokens])
+        n, dhq = FC.validate_h(xq, sx, inp.shared, st["h_sh"][tokens], st["hs_sh"][tokens])
         flips += n
         shared_extra = FC.down_effect(dhq, inp.shared)
         extra += shared_extra

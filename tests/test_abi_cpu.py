@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
     L = _lib.lib()
     for n in header_functions():
         assert hasattr(L, n), n
-    assert _lib.moe_abi_version() == 1
+    assert _lib.moe_abi_version() == 2
 
 
 def fp8_shape(**kw):
@@ -70,14 +70,14 @@ def test_unsupported_dtype_pairs():
 def test_null_pointers_rejected_before_launch():
     L = _lib.lib()
     s = fp8_shape()
-    assert L.moe_route_topk(C.byref(s), None, None, None, None, None, None, None, None) == _lib.MOE_ERR_INVALID_ARG
+    assert L.moe_route_topk(C.byref(s), None, None, None, None, None, None, None, None, 0, None) == _lib.MOE_ERR_INVALID_ARG
     assert L.moe_combine(C.byref(s), None, None, None, None, None, None) == _lib.MOE_ERR_INVALID_ARG
     assert L.moe_permute(C.byref(s), None, None, None, None, None, 0, None) == _lib.MOE_ERR_INVALID_ARG
     assert L.moe_layer_forward(C.byref(s), None, None, None, None, None, None, 0, None) == _lib.MOE_ERR_INVALID_ARG
     assert L.moe_layer_forward(None, None, None, None, None, None, None, 0, None) == _lib.MOE_ERR_INVALID_ARG
     # T == 0 is a valid no-op even with null pointers
     s0 = fp8_shape(T=0)
-    assert L.moe_route_topk(C.byref(s0), None, None, None, None, None, None, None, None) == _lib.MOE_OK
+    assert L.moe_route_topk(C.byref(s0), None, None, None, None, None, None, None, None, 0, None) == _lib.MOE_OK
     assert L.moe_layer_forward(C.byref(s0), None, None, None, None, None, None, 0, None) == _lib.MOE_OK
 
 
@@ -93,6 +93,9 @@ def test_workspace_checks():
     assert L.moe_layer_forward(C.byref(s), C.byref(w), fake, fake, None, None, None, need, None) == _lib.MOE_ERR_WORKSPACE
     assert L.moe_layer_forward(C.byref(s), C.byref(w), fake, fake, None, None, fake, need - 1, None) == _lib.MOE_ERR_WORKSPACE
     assert L.moe_layer_forward(C.byref(s), C.byref(w), fake, fake, None, None, C.c_void_p((1 << 40) + 16), need, None) == _lib.MOE_ERR_WORKSPACE
+    rw = _lib.moe_route_workspace_size(s)
+    assert rw >= 64 * 128 * 4
+    assert L.moe_route_topk(C.byref(s), fake, fake, None, fake, fake, fake, fake, fake, rw - 1, None) == _lib.MOE_ERR_WORKSPACE
     pw = _lib.moe_permute_workspace_size(s)
     assert L.moe_permute(C.byref(s), fake, fake, fake, fake, fake, pw - 1, None) == _lib.MOE_ERR_WORKSPACE
     # shared expert requested but its weights missing

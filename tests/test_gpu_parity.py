@@ -36,7 +36,8 @@ def test_route_topk(name):
     fp8 = cfg.precision == "fp8"
     xq = torch.empty((T, d), dtype=torch.uint8, device=H.DEV) if fp8 else None
     xs = torch.empty((T,), dtype=torch.float32, device=H.DEV) if fp8 else None
-    _lib.moe_route_topk(s, lt.x, lt.w_router, lt.router_bias, ids, w, xq, xs)
+    _lib.moe_route_topk(s, lt.x, lt.w_router, lt.router_bias, ids, w, xq, xs,
+                        alloc_workspace(_lib.moe_route_workspace_size(s), H.DEV))
     torch.cuda.synchronize()
     inp = oinputs.layer_inputs(lt)
     x64 = omoe.activations(inp)
@@ -134,7 +135,7 @@ def test_grouped_ffn(name):
                 continue
             tok = ref.perm.sorted_pair[r0:r1] // k
             ew = inp.expert(e)
-            n, dhq = FC.validate_h(omoe.swiglu_h_fp8(ref.xq[tok], ref.s_x[tok], ew), h[r0:r1], hs[r0:r1])
+            n, dhq = FC.validate_h(ref.xq[tok], ref.s_x[tok], ew, h[r0:r1], hs[r0:r1])
             flips += n
             extra[r0:r1] = FC.down_effect(dhq, ew)
         H.say(f"  routed h: {flips} validated neighbouring-code decisions of {h.size}")
@@ -145,7 +146,7 @@ def test_grouped_ffn(name):
         so, hsh, hssh = run(1, off_s, None, 1, T, Fs, lt.ws13, lt.ws13_scale, lt.ws2, lt.ws2_scale)
         extra_s = 0.0
         if fp8:
-            n, dhq = FC.validate_h(omoe.swiglu_h_fp8(ref.xq, ref.s_x, inp.shared), hsh, hssh)
+            n, dhq = FC.validate_h(ref.xq, ref.s_x, inp.shared, hsh, hssh)
             H.say(f"  shared h: {n} validated neighbouring-code decisions of {hsh.size}")
             extra_s = FC.down_effect(dhq, inp.shared)
         H.compare_y(so, ref.shared_out, cfg.precision, "shared_out", extra_s)
