@@ -61,6 +61,16 @@ __device__ inline float wave_max(float v) {
   return v;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ inline int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int u = __shfl_up(v, o, kWave);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
 // max over the 16 lanes that share (lane / 16)
 __device__ inline float max16(float v) {
 #pragma unroll

@@ -140,7 +140,7 @@ constexpr int prefetch_depth() { return BM <= 32 ? 3 : 2; }
 // own weight rows straight into a register ring PD K-steps deep (no LDS: no
 // other wave reads them).
 // ---------------------------------------------------------------------------
-template <int BM>
+template <int BM, int KTC>
 __global__ __launch_bounds__(kThreads) void gateup_fp8_kernel(FfnCall c,
                                                               const TileHeader* __restrict__ hdr,
                                                               const TileEntry* __restrict__ list) {
@@ -194,51 +194,63 @@ __global__ __launch_bounds__(kThreads) void gateup_fp8_kernel(FfnCall c,
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  const int KT = d / kBK;
+  // Software pipeline, one K step (128 bytes of K) per stage:
+  //   B (weights): register ring of PD steps; step kt's fragments are loaded
+  //                right after step kt - PD has used the slot;
+  //   A (rows):    LDS double buffer; step kt+1 is stored from registers loaded
+  //                one full step earlier, then step kt+2 is loaded.
+  // Every load is unconditional (the step index is clamped; tail re-loads hit
+  // the cache), so the number of loads in flight is the same on every path and
+  // the compiler's wait counts stay exact.
+  const int KT = KTC > 0 ? KTC : d / kBK;  // KTC: K steps known at compile time
   v4i a_stage[CPT];
   v8i bq[PD][NB];
 #pragma unroll
   for (int s = 0; s < PD; ++s)
-    if (s < KT)
 #pragma unroll
-      for (int j = 0; j < NB; ++j) bq[s][j] = glb_bfrag(b_src[j] + s * kBK);
+    for (int j = 0; j < NB; ++j) bq[s][j] = glb_bfrag(b_src[j] + min(s, KT - 1) * kBK);
 #pragma unroll
   for (int i = 0; i < CPT; ++i) a_stage[i] = *reinterpret_cast<const v4i*>(a_src[i]);
 #pragma unroll
   for (int i = 0; i < CPT; ++i)
     if (CH % kThreads == 0 || tid + i * kThreads < CH)
       *reinterpret_cast<v4i*>(&lds_a[0][a_dst[i]]) = a_stage[i];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i)
+    a_stage[i] = *reinterpret_cast<const v4i*>(a_src[i] + min(1, KT - 1) * kBK);
   __syncthreads();
 
+  // With KTC > 0 the loop is fully unrolled: no back edge, so the compiler's
+  // wait counts are exact at every step.
+#pragma unroll (KTC > 0 ? KTC : 1)
   for (int kt0 = 0; kt0 < KT; kt0 += PD) {
 #pragma unroll
     for (int s = 0; s < PD; ++s) {
       const int kt = kt0 + s;
       if (kt < KT) {
         const int cur = kt & 1;
-        const bool more = kt + 1 < KT;
-        if (more) {
-#pragma unroll
-          for (int i = 0; i < CPT; ++i)
-            a_stage[i] = *reinterpret_cast<const v4i*>(a_src[i] + (kt + 1) * kBK);
-        }
 #pragma unroll
         for (int i = 0; i < MS; ++i) {
           const v8i af = lds_afrag(lds_a[cur], i, lane);
 #pragma unroll
           for (int j = 0; j < NB; ++j) acc[i][j] = mfma_fp8_16x16x128(af, bq[s][j], acc[i][j]);
         }
-        if (kt + PD < KT) {
+        // A for step kt+1 into the other buffer (its readers finished at the
+        // barrier ending step kt-1), then fetch A for step kt+2
 #pragma unroll
-          for (int j = 0; j < NB; ++j) bq[s][j] = glb_bfrag(b_src[j] + (kt + PD) * kBK);
-        }
-        if (more) {
+        for (int i = 0; i < CPT; ++i)
+          if (CH % kThreads == 0 || tid + i * kThreads < CH)
+            *reinterpret_cast<v4i*>(&lds_a[cur ^ 1][a_dst[i]]) = a_stage[i];
+        const int ka = min(kt + 2, KT - 1), kb = min(kt + PD, KT - 1);
 #pragma unroll
-          for (int i = 0; i < CPT; ++i)
-            if (CH % kThreads == 0 || tid + i * kThreads < CH)
-              *reinterpret_cast<v4i*>(&lds_a[cur ^ 1][a_dst[i]]) = a_stage[i];
-        }
+        for (int i = 0; i < CPT; ++i)
+          a_stage[i] = *reinterpret_cast<const v4i*>(a_src[i] + ka * kBK);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) bq[s][j] = glb_bfrag(b_src[j] + kb * kBK);
         __syncthreads();
+        // keep each step's instructions in its step (bounds register pressure
+        // of the unrolled loop)
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
@@ -300,7 +312,7 @@ __global__ __launch_bounds__(kThreads) void gateup_fp8_kernel(FfnCall c,
 // channels; wave w owns channels [64w, 64w + 64). Each 128-wide K step is one
 // h block: its MFMA partial is scaled by s_h[row][block] and accumulated.
 // ---------------------------------------------------------------------------
-template <int BM>
+template <int BM, int KTC>
 __global__ __launch_bounds__(kThreads) void down_fp8_kernel(FfnCall c,
                                                             const TileHeader* __restrict__ hdr,
                                                             const TileEntry* __restrict__ list) {
@@ -349,15 +361,16 @@ __global__ __launch_bounds__(kThreads) void down_fp8_kernel(FfnCall c,
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  const int KT = F / kBK;
+  // Same pipeline as the gate/up GEMM; the per-row h scale of step kt+1 rides
+  // with its A tile.
+  const int KT = KTC > 0 ? KTC : F / kBK;  // KTC: K steps known at compile time
   v4i a_stage[CPT];
-  float hs_stage = 0.f;
+  float hs_stage;
   v8i bq[PD][NB];
 #pragma unroll
   for (int s = 0; s < PD; ++s)
-    if (s < KT)
 #pragma unroll
-      for (int j = 0; j < NB; ++j) bq[s][j] = glb_bfrag(b_src[j] + s * kBK);
+    for (int j = 0; j < NB; ++j) bq[s][j] = glb_bfrag(b_src[j] + min(s, KT - 1) * kBK);
 #pragma unroll
   for (int i = 0; i < CPT; ++i) a_stage[i] = *reinterpret_cast<const v4i*>(a_src[i]);
   hs_stage = hs_src[0];
@@ -366,21 +379,19 @@ __global__ __launch_bounds__(kThreads) void down_fp8_kernel(FfnCall c,
     if (CH % kThreads == 0 || tid + i * kThreads < CH)
       *reinterpret_cast<v4i*>(&lds_a[0][a_dst[i]]) = a_stage[i];
   if (tid < BM) hsl[0][tid] = hs_stage;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i)
+    a_stage[i] = *reinterpret_cast<const v4i*>(a_src[i] + min(1, KT - 1) * kBK);
+  hs_stage = hs_src[min(1, KT - 1)];
   __syncthreads();
 
+#pragma unroll (KTC > 0 ? KTC : 1)
   for (int kt0 = 0; kt0 < KT; kt0 += PD) {
 #pragma unroll
     for (int s = 0; s < PD; ++s) {
       const int kt = kt0 + s;
       if (kt < KT) {
         const int cur = kt & 1;
-        const bool more = kt + 1 < KT;
-        if (more) {
-#pragma unroll
-          for (int i = 0; i < CPT; ++i)
-            a_stage[i] = *reinterpret_cast<const v4i*>(a_src[i] + (kt + 1) * kBK);
-          hs_stage = hs_src[kt + 1];
-        }
 #pragma unroll
         for (int i = 0; i < MS; ++i) {
           const v8i af = lds_afrag(lds_a[cur], i, lane);
@@ -395,18 +406,22 @@ __global__ __launch_bounds__(kThreads) void down_fp8_kernel(FfnCall c,
             for (int j = 0; j < NB; ++j) acc[i][j][q] = fmaf(part[j][q], hs, acc[i][j][q]);
           }
         }
-        if (kt + PD < KT) {
 #pragma unroll
-          for (int j = 0; j < NB; ++j) bq[s][j] = glb_bfrag(b_src[j] + (kt + PD) * kBK);
-        }
-        if (more) {
+        for (int i = 0; i < CPT; ++i)
+          if (CH % kThreads == 0 || tid + i * kThreads < CH)
+            *reinterpret_cast<v4i*>(&lds_a[cur ^ 1][a_dst[i]]) = a_stage[i];
+        if (tid < BM) hsl[cur ^ 1][tid] = hs_stage;
+        const int ka = min(kt + 2, KT - 1), kb = min(kt + PD, KT - 1);
 #pragma unroll
-          for (int i = 0; i < CPT; ++i)
-            if (CH % kThreads == 0 || tid + i * kThreads < CH)
-              *reinterpret_cast<v4i*>(&lds_a[cur ^ 1][a_dst[i]]) = a_stage[i];
-          if (tid < BM) hsl[cur ^ 1][tid] = hs_stage;
-        }
+        for (int i = 0; i < CPT; ++i)
+          a_stage[i] = *reinterpret_cast<const v4i*>(a_src[i] + ka * kBK);
+        hs_stage = hs_src[ka];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) bq[s][j] = glb_bfrag(b_src[j] + kb * kBK);
         __syncthreads();
+        // keep each step's instructions in its step (bounds register pressure
+        // of the unrolled loop)
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
@@ -480,18 +495,32 @@ __global__ __launch_bounds__(256) void down_f32_kernel(FfnCall c, int sid) {
   static_cast<float*>(S.out)[(size_t)r * d + m] = acc;
 }
 
-template <int BM, int BMD>
+template <int BM, int KTU, int BMD, int KTD>
 hipError_t launch_gemms_bm(const FfnCall& c, TileHeader* hdr, TileEntry* up, TileEntry* dn,
                            size_t cap_u, size_t cap_d, hipStream_t s, const StepEvents& ev) {
   const size_t cu = align_up(cap_u, kXcds);
   const size_t cd = align_up(cap_d, kXcds);
   ev.mark(true, MOE_STEP_GATE_UP, s);
-  if (cu > 0) hipLaunchKernelGGL(gateup_fp8_kernel<BM>, dim3((unsigned)cu), dim3(kThreads), 0, s, c, hdr, up);
+  if (cu > 0)
+    hipLaunchKernelGGL((gateup_fp8_kernel<BM, KTU>), dim3((unsigned)cu), dim3(kThreads), 0, s, c,
+                       hdr, up);
   ev.mark(false, MOE_STEP_GATE_UP, s);
   ev.mark(true, MOE_STEP_DOWN, s);
-  if (cd > 0) hipLaunchKernelGGL(down_fp8_kernel<BMD>, dim3((unsigned)cd), dim3(kThreads), 0, s, c, hdr, dn);
+  if (cd > 0)
+    hipLaunchKernelGGL((down_fp8_kernel<BMD, KTD>), dim3((unsigned)cd), dim3(kThreads), 0, s, c,
+                       hdr, dn);
   ev.mark(false, MOE_STEP_DOWN, s);
   return hipGetLastError();
+}
+
+// The gate/up GEMM is fully unrolled for d = 4096 (32 K steps, the model
+// shape); other hidden sizes, and the down GEMM (whose unrolled form runs out
+// of registers), use the looped kernels.
+template <int BM, int BMD>
+hipError_t launch_gemms_k(const FfnCall& c, TileHeader* hdr, TileEntry* up, TileEntry* dn,
+                          size_t cap_u, size_t cap_d, hipStream_t s, const StepEvents& ev) {
+  if (c.d / kBK == 32) return launch_gemms_bm<BM, 32, BMD, 0>(c, hdr, up, dn, cap_u, cap_d, s, ev);
+  return launch_gemms_bm<BM, 0, BMD, 0>(c, hdr, up, dn, cap_u, cap_d, s, ev);
 }
 
 }  // namespace
@@ -552,11 +581,11 @@ hipError_t launch_ffn_gemms(const FfnCall& c, int bm, void* ws, hipStream_t s,
   int cu, cd;
   tile_lists(c, bm, down_bm(bm), ws, &hdr, &up, &dn, &cu, &cd);
   switch (bm) {
-    case 16: return launch_gemms_bm<16, 16>(c, hdr, up, dn, cu, cd, s, ev);
-    case 32: return launch_gemms_bm<32, 32>(c, hdr, up, dn, cu, cd, s, ev);
-    case 64: return launch_gemms_bm<64, 64>(c, hdr, up, dn, cu, cd, s, ev);
-    case 128: return launch_gemms_bm<128, 128>(c, hdr, up, dn, cu, cd, s, ev);
-    default: return launch_gemms_bm<192, 128>(c, hdr, up, dn, cu, cd, s, ev);
+    case 16: return launch_gemms_k<16, 16>(c, hdr, up, dn, cu, cd, s, ev);
+    case 32: return launch_gemms_k<32, 32>(c, hdr, up, dn, cu, cd, s, ev);
+    case 64: return launch_gemms_k<64, 64>(c, hdr, up, dn, cu, cd, s, ev);
+    case 128: return launch_gemms_k<128, 128>(c, hdr, up, dn, cu, cd, s, ev);
+    default: return launch_gemms_k<192, 128>(c, hdr, up, dn, cu, cd, s, ev);
   }
 }
 

@@ -71,17 +71,31 @@ __global__ __launch_bounds__(kScanThreads) void perm_scan_kernel(
     for (int i = tid; i < nt * E; i += kScanThreads) counts[(size_t)t0 * E + i] = stage[i];
     __syncthreads();
   }
-  // inclusive scan of the per-expert totals (Hillis-Steele over MOE_MAX_E entries)
-  if (tid < MOE_MAX_E) tot[tid] = (tid < E) ? run : 0;
+  // inclusive scan of the per-expert totals, by wave 0 (4 experts per lane)
+  if (tid < E) tot[tid] = run;
   __syncthreads();
-  for (int o = 1; o < MOE_MAX_E; o <<= 1) {
-    const int v = (tid < MOE_MAX_E && tid >= o) ? tot[tid - o] : 0;
-    __syncthreads();
-    if (tid < MOE_MAX_E) tot[tid] += v;
-    __syncthreads();
+  if (tid < kWave) {
+    constexpr int per = MOE_MAX_E / kWave;
+    int v[per], sum = 0;
+#pragma unroll
+    for (int i = 0; i < per; ++i) {
+      const int e = tid * per + i;
+      v[i] = (e < E) ? tot[e] : 0;
+      sum += v[i];
+    }
+    int acc = wave_incl_scan(sum, tid) - sum;
+#pragma unroll
+    for (int i = 0; i < per; ++i) {
+      const int e = tid * per + i;
+      acc += v[i];
+      if (e < E) {
+        tot[e] = acc;
+        offsets[e + 1] = acc;
+      }
+    }
+    if (tid == 0) offsets[0] = 0;
   }
-  if (tid < E) offsets[tid + 1] = tot[tid];
-  if (tid == 0) offsets[0] = 0;
+  __syncthreads();
   if (hdr == nullptr) return;
 
   // groups: routed experts (set 0), then the shared expert (set 1)

@@ -23,15 +23,75 @@ namespace {
 
 constexpr int kLogitWaves = 4;     // K split across the waves of a logits tile
 constexpr int kLogitExperts = 32;  // experts per logits tile (2 MFMA column tiles)
-constexpr int kMaxPerLane = 4;     // E <= 256 = 64 lanes * 4
 constexpr int kTopkWaves = 16;     // one 64-token tile per top-k workgroup
 constexpr int kTokPerWave = kPermTile / kTopkWaves;
+
+constexpr int kQuantGroup = 8;  // 16-byte loads per lane in flight per group
+
+__device__ inline float absmax8(const v4i& c, float m) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    m = fmaxf(m, fabsf(bf16_to_f32((uint16_t)((uint32_t)c[q] & 0xffff))));
+    m = fmaxf(m, fabsf(bf16_to_f32((uint16_t)((uint32_t)c[q] >> 16))));
+  }
+  return m;
+}
+
+__device__ inline uint2 encode8(const v4i& c, float s) {
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t c0 = e4m3_encode(__fdiv_rn(bf16_to_f32((uint16_t)((uint32_t)c[q] & 0xffff)), s));
+    const uint32_t c1 = e4m3_encode(__fdiv_rn(bf16_to_f32((uint16_t)((uint32_t)c[q] >> 16)), s));
+    const uint32_t pair = c0 | (c1 << 8);
+    if (q < 2)
+      lo |= pair << (16 * q);
+    else
+      hi |= pair << (16 * (q - 2));
+  }
+  return make_uint2(lo, hi);
+}
+
+// One wave quantises one bf16 row of length d (a multiple of 8) to FP8 E4M3
+// with scale amax/448: an amax pass and an encode pass, each issuing its
+// 16-byte loads in groups of 8 per lane.
+__device__ inline void quantize_row(const uint16_t* __restrict__ xr, int d, int lane,
+                                    uint8_t* __restrict__ qr, float* __restrict__ s_out) {
+  const int nch = d / 8;  // 8-element chunks in the row
+  float amax = 0.f;
+  for (int c0 = 0; c0 < nch; c0 += kWave * kQuantGroup) {
+    v4i v[kQuantGroup];
+#pragma unroll
+    for (int i = 0; i < kQuantGroup; ++i) {
+      const int c = c0 + i * kWave + lane;
+      v[i] = (c < nch) ? *reinterpret_cast<const v4i*>(xr + (size_t)c * 8) : v4i{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < kQuantGroup; ++i) amax = absmax8(v[i], amax);
+  }
+  amax = wave_max(amax);
+  const float s = (amax > 0.f) ? __fdiv_rn(amax, kE4M3Max) : 1.0f;
+  for (int c0 = 0; c0 < nch; c0 += kWave * kQuantGroup) {
+    v4i v[kQuantGroup];
+#pragma unroll
+    for (int i = 0; i < kQuantGroup; ++i) {
+      const int c = c0 + i * kWave + lane;
+      v[i] = (c < nch) ? *reinterpret_cast<const v4i*>(xr + (size_t)c * 8) : v4i{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < kQuantGroup; ++i) {
+      const int c = c0 + i * kWave + lane;
+      if (c < nch) *reinterpret_cast<uint2*>(qr + (size_t)c * 8) = encode8(v[i], s);
+    }
+  }
+  if (lane == 0) *s_out = s;
+}
 
 // ---------------------------------------------------------------------------
 // Logits, bf16: tile = 16 tokens x 32 experts; wave w accumulates K range
 // [w*d/4, (w+1)*d/4) with bf16 16x16x32 MFMAs; the partial tiles are summed
-// in LDS (fixed order: wave 0..3). Blocks with blockIdx.y == 0 also quantise
-// their tokens' x rows to FP8.
+// in LDS (fixed order: wave 0..3). The workgroups of a token tile also
+// quantise its tokens' x rows to FP8.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kLogitWaves * kWave) void route_logits_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
@@ -76,41 +136,14 @@ __global__ __launch_bounds__(kLogitWaves * kWave) void route_logits_bf16_kernel(
   }
 
   // ---- FP8 quantisation of x, per token: s = amax / 448, codes E4M3(x / s) ----
-  if (blockIdx.y != 0 || xq == nullptr) return;
-  for (int r = 0; r < kRouteTokens / kLogitWaves; ++r) {
-    const int t = tok0 + wave * (kRouteTokens / kLogitWaves) + r;
+  // The tile's 16 tokens are shared out over the gridDim.y workgroups of this
+  // token tile and their waves.
+  if (xq == nullptr) return;
+  const int nq = kLogitWaves * (int)gridDim.y;  // quantising waves per token tile
+  for (int r = blockIdx.y * kLogitWaves + wave; r < kRouteTokens; r += nq) {
+    const int t = tok0 + r;
     if (t >= T) break;
-    const uint16_t* xr = x + (size_t)t * d;
-    float amax = 0.f;
-    for (int c = lane * 8; c < d; c += kWave * 8) {
-      const uint4 p = *reinterpret_cast<const uint4*>(xr + c);
-      const uint32_t w4[4] = {p.x, p.y, p.z, p.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        amax = fmaxf(amax, fabsf(bf16_to_f32((uint16_t)(w4[q] & 0xffff))));
-        amax = fmaxf(amax, fabsf(bf16_to_f32((uint16_t)(w4[q] >> 16))));
-      }
-    }
-    amax = wave_max(amax);
-    const float s = (amax > 0.f) ? __fdiv_rn(amax, kE4M3Max) : 1.0f;
-    uint8_t* qr = xq + (size_t)t * d;
-    for (int c = lane * 8; c < d; c += kWave * 8) {
-      const uint4 p = *reinterpret_cast<const uint4*>(xr + c);
-      const uint32_t w4[4] = {p.x, p.y, p.z, p.w};
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t c0 = e4m3_encode(__fdiv_rn(bf16_to_f32((uint16_t)(w4[q] & 0xffff)), s));
-        const uint32_t c1 = e4m3_encode(__fdiv_rn(bf16_to_f32((uint16_t)(w4[q] >> 16)), s));
-        const uint32_t pair = c0 | (c1 << 8);
-        if (q < 2)
-          lo |= pair << (16 * q);
-        else
-          hi |= pair << (16 * (q - 2));
-      }
-      *reinterpret_cast<uint2*>(qr + c) = make_uint2(lo, hi);
-    }
-    if (lane == 0) xs[t] = s;
+    quantize_row(x + (size_t)t * d, d, lane, xq + (size_t)t * d, xs + t);
   }
 }
 
@@ -132,81 +165,79 @@ __global__ __launch_bounds__(kLogitWaves * kWave) void route_logits_f32_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Top-k over the logits of one 64-token tile: wave w takes tokens 4w..4w+3;
-// k rounds of a 64-lane (value desc, index asc) argmax butterfly. Optionally
-// records, per expert, the 64-bit mask of the tile's tokens routed to it and
-// its popcount (the permutation's per-tile histogram).
+// Top-k over the logits of one 64-token tile. Each wave serves 4 tokens at
+// once: the 16 lanes [16q, 16q + 16) take token 4w + q, lane holding experts
+// (lane % 16) + 16c. k rounds of a 16-lane (value desc, index asc) argmax
+// butterfly. Optionally records, per expert, the 64-bit mask of the tile's
+// tokens routed to it and its popcount (the permutation's per-tile histogram).
 // ---------------------------------------------------------------------------
+constexpr int kPerLane16 = MOE_MAX_E / 16;  // logits held per lane
+
 __global__ __launch_bounds__(kTopkWaves * kWave) void route_topk_kernel(
     const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ ids,
     float* __restrict__ wts, uint64_t* __restrict__ masks, int32_t* __restrict__ counts) {
   __shared__ unsigned long long mask[MOE_MAX_E];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int tile = blockIdx.x;
+  const int sub = lane & 15;
+  const int tl = wave * kTokPerWave + (lane >> 4);  // token within the tile
+  const int t = blockIdx.x * kPermTile + tl;
   if (masks != nullptr) {
     for (int e = threadIdx.x; e < E; e += kTopkWaves * kWave) mask[e] = 0ull;
     __syncthreads();
   }
-  for (int r = 0; r < kTokPerWave; ++r) {
-    const int tl = wave * kTokPerWave + r;  // token within the tile
-    const int t = tile * kPermTile + tl;
-    if (t >= T) break;
-    const float* lr = logits + (size_t)t * E;
-    float v[kMaxPerLane];
-    bool taken[kMaxPerLane];
+  const bool live = t < T;
+  const float* lr = logits + (size_t)min(t, T - 1) * E;
+  float v[kPerLane16];
 #pragma unroll
-    for (int c = 0; c < kMaxPerLane; ++c) {
-      const int e = lane + kWave * c;
-      v[c] = (e < E) ? lr[e] : -INFINITY;
-      taken[c] = false;
-    }
-    int my_e = 0;
-    float my_v = -FLT_MAX, top = 0.f;
-    for (int j = 0; j < k; ++j) {
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
+  for (int c = 0; c < kPerLane16; ++c) {
+    const int e = sub + 16 * c;
+    v[c] = (e < E) ? lr[e] : -INFINITY;
+  }
+  uint32_t taken = 0;
+  int my_e = 0;
+  float my_v = -FLT_MAX, top = 0.f;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
 #pragma unroll
-      for (int c = 0; c < kMaxPerLane; ++c) {
-        const int e = lane + kWave * c;
-        if (e < E && !taken[c] && (v[c] > bv || (v[c] == bv && e < bi))) {
-          bv = v[c];
-          bi = e;
-        }
-      }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, kWave);
-        const int oi = __shfl_xor(bi, o, kWave);
-        if (ov > bv || (ov == bv && oi < bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < kMaxPerLane; ++c)
-        if (bi == lane + kWave * c) taken[c] = true;
-      if (j == 0) top = bv;
-      if (lane == j) {
-        my_e = bi;
-        my_v = bv;
+    for (int c = 0; c < kPerLane16; ++c) {
+      const int e = sub + 16 * c;
+      if (e < E && !((taken >> c) & 1u) && (v[c] > bv || (v[c] == bv && e < bi))) {
+        bv = v[c];
+        bi = e;
       }
     }
-    const float ex = (lane < k) ? expf(my_v - top) : 0.f;
-    float den = ex;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o, kWave);
-    if (lane < k) {
-      ids[(size_t)t * k + lane] = my_e;
-      wts[(size_t)t * k + lane] = ex / den;
-      if (masks != nullptr) atomicOr(&mask[my_e], 1ull << tl);
+    for (int o = 8; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, kWave);
+      const int oi = __shfl_xor(bi, o, kWave);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
     }
+    if ((bi & 15) == sub) taken |= 1u << (bi >> 4);
+    if (j == 0) top = bv;
+    if (sub == j) {
+      my_e = bi;
+      my_v = bv;
+    }
+  }
+  const float ex = (sub < k) ? expf(my_v - top) : 0.f;
+  float den = ex;
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) den += __shfl_xor(den, o, kWave);
+  if (live && sub < k) {
+    ids[(size_t)t * k + sub] = my_e;
+    wts[(size_t)t * k + sub] = ex / den;
+    if (masks != nullptr) atomicOr(&mask[my_e], 1ull << tl);
   }
   if (masks != nullptr) {
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += kTopkWaves * kWave) {
-      masks[(size_t)tile * E + e] = mask[e];
-      counts[(size_t)tile * E + e] = __popcll(mask[e]);
+      masks[(size_t)blockIdx.x * E + e] = mask[e];
+      counts[(size_t)blockIdx.x * E + e] = __popcll(mask[e]);
     }
   }
 }

@@ -37,8 +37,6 @@ struct TileLds {
   int g_set[kMaxGroups];
   int pre_up[kMaxGroups + 1];
   int pre_dn[kMaxGroups + 1];
-  int part_up[1024];
-  int part_dn[1024];
 };
 
 // Host: where the lists of call c live in its tile workspace, and their
@@ -60,40 +58,33 @@ __device__ inline void emit_tiles(const FfnCall& c, int bm, int NG, int G0, Tile
   const int tid = threadIdx.x, nth = blockDim.x;
   const int dnt = down_ntiles(c.d);
   const int F0 = c.set[0].F, F1 = c.set[1].F;
-  // exclusive scans of per-group entry counts; thread tid owns a run of groups
-  const int per = ceil_div(NG, nth);
-  const int lo = min(NG, tid * per), hi = min(NG, lo + per);
-  int su = 0, sd = 0;
-  for (int i = lo; i < hi; ++i) {
-    su += ceil_div(L.g_rows[i], bm) * up_ntiles(L.g_set[i] == 0 ? F0 : F1);
-    sd += ceil_div(L.g_rows[i], bmd) * dnt;
-  }
-  L.part_up[tid] = su;
-  L.part_dn[tid] = sd;
-  __syncthreads();
-  for (int o = 1; o < nth; o <<= 1) {
-    const int vu = (tid >= o) ? L.part_up[tid - o] : 0;
-    const int vd = (tid >= o) ? L.part_dn[tid - o] : 0;
-    __syncthreads();
-    L.part_up[tid] += vu;
-    L.part_dn[tid] += vd;
-    __syncthreads();
-  }
-  su = L.part_up[tid] - su;
-  sd = L.part_dn[tid] - sd;
-  for (int i = lo; i < hi; ++i) {
-    L.pre_up[i] = su;
-    L.pre_dn[i] = sd;
-    su += ceil_div(L.g_rows[i], bm) * up_ntiles(L.g_set[i] == 0 ? F0 : F1);
-    sd += ceil_div(L.g_rows[i], bmd) * dnt;
-  }
-  if (tid == nth - 1) {
-    L.pre_up[NG] = L.part_up[nth - 1];
-    L.pre_dn[NG] = L.part_dn[nth - 1];
+  // exclusive scans of the per-group entry counts, by wave 0 (lane owns a run
+  // of groups; a shuffle scan over the lanes)
+  const int lane = tid & (kWave - 1), wave = tid / kWave, nwaves = nth / kWave;
+  if (wave == 0) {
+    const int per = ceil_div(NG, kWave);
+    const int lo = min(NG, lane * per), hi = min(NG, lo + per);
+    int su = 0, sd = 0;
+    for (int i = lo; i < hi; ++i) {
+      su += ceil_div(L.g_rows[i], bm) * up_ntiles(L.g_set[i] == 0 ? F0 : F1);
+      sd += ceil_div(L.g_rows[i], bmd) * dnt;
+    }
+    const int iu = wave_incl_scan(su, lane), id = wave_incl_scan(sd, lane);
+    su = iu - su;
+    sd = id - sd;
+    for (int i = lo; i < hi; ++i) {
+      L.pre_up[i] = su;
+      L.pre_dn[i] = sd;
+      su += ceil_div(L.g_rows[i], bm) * up_ntiles(L.g_set[i] == 0 ? F0 : F1);
+      sd += ceil_div(L.g_rows[i], bmd) * dnt;
+    }
+    if (lane == kWave - 1) {
+      L.pre_up[NG] = iu;
+      L.pre_dn[NG] = id;
+    }
   }
   __syncthreads();
   // one wave per group writes its entries
-  const int lane = tid & (kWave - 1), wave = tid / kWave, nwaves = nth / kWave;
   for (int i = wave; i < NG; i += nwaves) {
     const int rows = L.g_rows[i];
     if (rows == 0) continue;
