@@ -24,8 +24,6 @@ namespace moe {
 namespace {
 
 constexpr int kBK = 128;      // K bytes per MFMA step (FP8 16x16x128)
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * kWave;
 constexpr int kXcds = 8;
 constexpr int kTileThreads = 256;
 
@@ -128,33 +126,42 @@ __device__ inline SetView set_view(const FfnCall& c, int sid) {
   return v;
 }
 
-// B operand prefetch depth (K steps of weights in flight per wave).
-template <int BM>
-constexpr int prefetch_depth() { return BM <= 32 ? 3 : 2; }
+// B operand prefetch depth (K steps of weights in flight per wave), by the
+// rows a wave holds (more rows: a bigger accumulator, fewer registers left).
+template <int ROWS, int LIMIT>
+constexpr int prefetch_depth() { return ROWS <= LIMIT ? 3 : 2; }
+
+// Waves of a GEMM workgroup: 4 along N (each owns a quarter of the tile's
+// columns) times WM along M (each owns BM / WM rows). WM = 2 halves every
+// wave's accumulator, which buys registers for a deeper weight ring and two
+// waves per SIMD; the two M halves read the same weight fragments, the
+// second time from the L2.
+constexpr int kNWaves = 4;
 
 // ---------------------------------------------------------------------------
 // Gate/up GEMM + SwiGLU + h quantisation. Tile: BM rows x 128 h columns
-// (128 gate + 128 up weight rows); wave w owns h columns [32w, 32w + 32) for
-// all BM rows. A (activation rows, gathered through the permutation) is
-// staged through LDS, double buffered and XOR-swizzled; each wave streams its
-// own weight rows straight into a register ring PD K-steps deep (no LDS: no
-// other wave reads them).
+// (128 gate + 128 up weight rows); wave (wm, wn) owns h columns
+// [32 wn, 32 wn + 32) of rows [wm BM/WM, (wm + 1) BM/WM). A (activation rows,
+// gathered through the permutation) is staged through LDS, double buffered
+// and XOR-swizzled; each wave streams its own weight rows straight into a
+// register ring PD K-steps deep.
 // ---------------------------------------------------------------------------
-template <int BM, int KTC>
-__global__ __launch_bounds__(kThreads) void gateup_fp8_kernel(FfnCall c,
-                                                              const TileHeader* __restrict__ hdr,
-                                                              const TileEntry* __restrict__ list) {
-  constexpr int MS = BM / 16;
-  constexpr int WN = kHN / kWaves;  // 32 h columns per wave
+template <int BM, int WM, int KTC>
+__global__ __launch_bounds__(kNWaves * WM * kWave) void gateup_fp8_kernel(
+    FfnCall c, const TileHeader* __restrict__ hdr, const TileEntry* __restrict__ list) {
+  constexpr int NTH = kNWaves * WM * kWave;
+  constexpr int BMW = BM / WM;      // rows per wave
+  constexpr int MS = BMW / 16;
+  constexpr int WN = kHN / kNWaves; // 32 h columns per wave
   constexpr int NS = WN / 16;       // 2 h subtiles per wave
   constexpr int NB = 2 * NS;        // weight subtiles per wave (gate, up)
   constexpr int CH = BM * (kBK / 16);
-  constexpr int CPT = (CH + kThreads - 1) / kThreads;
-  constexpr int PD = prefetch_depth<BM>();
+  constexpr int CPT = (CH + NTH - 1) / NTH;
+  constexpr int PD = prefetch_depth<BMW, 64>();
 
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * kBK];
   __shared__ float sxl[BM];
-  __shared__ float red[kWaves][BM];
+  __shared__ float red[kNWaves][BM];
 
   int w;
   if (!pick_tile(hdr->n_up, w)) return;
@@ -163,6 +170,8 @@ __global__ __launch_bounds__(kThreads) void gateup_fp8_kernel(FfnCall c,
   const SetView S = set_view(c, sid);
   const int d = c.d, F = S.F;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int wm = wave / kNWaves, wn = wave % kNWaves;
+  const int rbase = wm * BMW;
   const uint8_t* a = static_cast<const uint8_t*>(c.a);
 
   // activation rows of this tile (gathered), their scales into LDS
@@ -170,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void gateup_fp8_kernel(FfnCall c,
   int a_dst[CPT];
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
-    const int ch = tid + i * kThreads;
+    const int ch = tid + i * NTH;
     const int r = min(ch >> 3, BM - 1), c16 = ch & 7;
     const int grow = te.row0 + min(r, te.nrows - 1);
     const int src = min(max(S.row_src ? S.row_src[grow] / S.src_div : grow, 0), c.a_rows - 1);
@@ -183,7 +192,7 @@ __global__ __launch_bounds__(kThreads) void gateup_fp8_kernel(FfnCall c,
   const uint8_t* b_src[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
-    const int hc = te.ntile * kHN + wave * WN + (j % NS) * 16 + (lane & 15);
+    const int hc = te.ntile * kHN + wn * WN + (j % NS) * 16 + (lane & 15);
     const int wrow = (j < NS) ? hc : F + hc;
     b_src[j] = w13 + (size_t)wrow * d + (lane >> 4) * 16;
   }
@@ -213,7 +222,7 @@ __global__ __launch_bounds__(kThreads) void gateup_fp8_kernel(FfnCall c,
   for (int i = 0; i < CPT; ++i) a_stage[i] = *reinterpret_cast<const v4i*>(a_src[i]);
 #pragma unroll
   for (int i = 0; i < CPT; ++i)
-    if (CH % kThreads == 0 || tid + i * kThreads < CH)
+    if (CH % NTH == 0 || tid + i * NTH < CH)
       *reinterpret_cast<v4i*>(&lds_a[0][a_dst[i]]) = a_stage[i];
 #pragma unroll
   for (int i = 0; i < CPT; ++i)
@@ -231,7 +240,7 @@ __global__ __launch_bounds__(kThreads) void gateup_fp8_kernel(FfnCall c,
         const int cur = kt & 1;
 #pragma unroll
         for (int i = 0; i < MS; ++i) {
-          const v8i af = lds_afrag(lds_a[cur], i, lane);
+          const v8i af = lds_afrag(lds_a[cur] + rbase * kBK, i, lane);
 #pragma unroll
           for (int j = 0; j < NB; ++j) acc[i][j] = mfma_fp8_16x16x128(af, bq[s][j], acc[i][j]);
         }
@@ -239,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void gateup_fp8_kernel(FfnCall c,
         // barrier ending step kt-1), then fetch A for step kt+2
 #pragma unroll
         for (int i = 0; i < CPT; ++i)
-          if (CH % kThreads == 0 || tid + i * kThreads < CH)
+          if (CH % NTH == 0 || tid + i * NTH < CH)
             *reinterpret_cast<v4i*>(&lds_a[cur ^ 1][a_dst[i]]) = a_stage[i];
         const int ka = min(kt + 2, KT - 1), kb = min(kt + PD, KT - 1);
 #pragma unroll
@@ -260,7 +269,7 @@ __global__ __launch_bounds__(kThreads) void gateup_fp8_kernel(FfnCall c,
   float sg[NS], su[NS];
 #pragma unroll
   for (int jj = 0; jj < NS; ++jj) {
-    const int hc = te.ntile * kHN + wave * WN + jj * 16 + (lane & 15);
+    const int hc = te.ntile * kHN + wn * WN + jj * 16 + (lane & 15);
     sg[jj] = s13[hc];
     su[jj] = s13[F + hc];
   }
@@ -268,7 +277,7 @@ __global__ __launch_bounds__(kThreads) void gateup_fp8_kernel(FfnCall c,
   for (int i = 0; i < MS; ++i) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int r = i * 16 + 4 * (lane >> 4) + q;
+      const int r = rbase + i * 16 + 4 * (lane >> 4) + q;
       const float sx = sxl[r];
       float m = 0.f;
 #pragma unroll
@@ -280,7 +289,7 @@ __global__ __launch_bounds__(kThreads) void gateup_fp8_kernel(FfnCall c,
         m = fmaxf(m, fabsf(h));
       }
       m = max16(m);
-      if ((lane & 15) == 0) red[wave][r] = m;
+      if ((lane & 15) == 0) red[wn][r] = m;
     }
   }
   __syncthreads();
@@ -289,38 +298,40 @@ __global__ __launch_bounds__(kThreads) void gateup_fp8_kernel(FfnCall c,
   for (int i = 0; i < MS; ++i) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int r = i * 16 + 4 * (lane >> 4) + q;
+      const int r = rbase + i * 16 + 4 * (lane >> 4) + q;
       if (r >= te.nrows) continue;
       float am = red[0][r];
 #pragma unroll
-      for (int ww = 1; ww < kWaves; ++ww) am = fmaxf(am, red[ww][r]);
+      for (int ww = 1; ww < kNWaves; ++ww) am = fmaxf(am, red[ww][r]);
       const float s = (am > 0.f) ? __fdiv_rn(am, kE4M3Max) : 1.0f;
       const size_t grow = (size_t)(te.row0 + r);
       uint8_t* hrow = S.h + grow * F;
 #pragma unroll
       for (int jj = 0; jj < NS; ++jj) {
-        const int hc = te.ntile * kHN + wave * WN + jj * 16 + (lane & 15);
+        const int hc = te.ntile * kHN + wn * WN + jj * 16 + (lane & 15);
         hrow[hc] = e4m3_encode(__fdiv_rn(acc[i][jj][q], s));
       }
-      if (wave == 0 && (lane & 15) == 0) S.h_scale[grow * hblocks + te.ntile] = s;
+      if (wn == 0 && (lane & 15) == 0) S.h_scale[grow * hblocks + te.ntile] = s;
     }
   }
 }
 
 // ---------------------------------------------------------------------------
 // Down GEMM with per-(row, 128-K block) h scales. Tile: BM rows x 256 output
-// channels; wave w owns channels [64w, 64w + 64). Each 128-wide K step is one
-// h block: its MFMA partial is scaled by s_h[row][block] and accumulated.
+// channels; wave (wm, wn) owns channels [64 wn, 64 wn + 64) of rows
+// [wm BM/WM, (wm + 1) BM/WM). Each 128-wide K step is one h block: its MFMA
+// partial is scaled by s_h[row][block] and accumulated.
 // ---------------------------------------------------------------------------
-template <int BM, int KTC>
-__global__ __launch_bounds__(kThreads) void down_fp8_kernel(FfnCall c,
-                                                            const TileHeader* __restrict__ hdr,
-                                                            const TileEntry* __restrict__ list) {
-  constexpr int MS = BM / 16;
+template <int BM, int WM, int KTC>
+__global__ __launch_bounds__(kNWaves * WM * kWave) void down_fp8_kernel(
+    FfnCall c, const TileHeader* __restrict__ hdr, const TileEntry* __restrict__ list) {
+  constexpr int NTH = kNWaves * WM * kWave;
+  constexpr int BMW = BM / WM;
+  constexpr int MS = BMW / 16;
   constexpr int NB = 4;  // 16-channel subtiles per wave
   constexpr int CH = BM * (kBK / 16);
-  constexpr int CPT = (CH + kThreads - 1) / kThreads;
-  constexpr int PD = prefetch_depth<BM>();
+  constexpr int CPT = (CH + NTH - 1) / NTH;
+  constexpr int PD = prefetch_depth<BMW, 32>();
 
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * kBK];
   __shared__ float hsl[2][BM];
@@ -332,12 +343,14 @@ __global__ __launch_bounds__(kThreads) void down_fp8_kernel(FfnCall c,
   const SetView S = set_view(c, sid);
   const int d = c.d, F = S.F, hblocks = F / kHN;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int wm = wave / kNWaves, wn = wave % kNWaves;
+  const int rbase = wm * BMW;
 
   const uint8_t* a_src[CPT];
   int a_dst[CPT];
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
-    const int ch = tid + i * kThreads;
+    const int ch = tid + i * NTH;
     const int r = min(ch >> 3, BM - 1), c16 = ch & 7;
     const int grow = te.row0 + min(r, te.nrows - 1);
     a_src[i] = S.h + (size_t)grow * F + c16 * 16;
@@ -351,7 +364,7 @@ __global__ __launch_bounds__(kThreads) void down_fp8_kernel(FfnCall c,
   int mcol[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
-    mcol[j] = te.ntile * kDownBN + wave * (NB * 16) + j * 16 + (lane & 15);
+    mcol[j] = te.ntile * kDownBN + wn * (NB * 16) + j * 16 + (lane & 15);
     b_src[j] = w2 + (size_t)min(mcol[j], d - 1) * F + (lane >> 4) * 16;
   }
 
@@ -376,7 +389,7 @@ __global__ __launch_bounds__(kThreads) void down_fp8_kernel(FfnCall c,
   hs_stage = hs_src[0];
 #pragma unroll
   for (int i = 0; i < CPT; ++i)
-    if (CH % kThreads == 0 || tid + i * kThreads < CH)
+    if (CH % NTH == 0 || tid + i * NTH < CH)
       *reinterpret_cast<v4i*>(&lds_a[0][a_dst[i]]) = a_stage[i];
   if (tid < BM) hsl[0][tid] = hs_stage;
 #pragma unroll
@@ -394,21 +407,21 @@ __global__ __launch_bounds__(kThreads) void down_fp8_kernel(FfnCall c,
         const int cur = kt & 1;
 #pragma unroll
         for (int i = 0; i < MS; ++i) {
-          const v8i af = lds_afrag(lds_a[cur], i, lane);
+          const v8i af = lds_afrag(lds_a[cur] + rbase * kBK, i, lane);
           v4f part[NB];
 #pragma unroll
           for (int j = 0; j < NB; ++j)
             part[j] = mfma_fp8_16x16x128(af, bq[s][j], v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const float hs = hsl[cur][i * 16 + 4 * (lane >> 4) + q];
+            const float hs = hsl[cur][rbase + i * 16 + 4 * (lane >> 4) + q];
 #pragma unroll
             for (int j = 0; j < NB; ++j) acc[i][j][q] = fmaf(part[j][q], hs, acc[i][j][q]);
           }
         }
 #pragma unroll
         for (int i = 0; i < CPT; ++i)
-          if (CH % kThreads == 0 || tid + i * kThreads < CH)
+          if (CH % NTH == 0 || tid + i * NTH < CH)
             *reinterpret_cast<v4i*>(&lds_a[cur ^ 1][a_dst[i]]) = a_stage[i];
         if (tid < BM) hsl[cur ^ 1][tid] = hs_stage;
         const int ka = min(kt + 2, KT - 1), kb = min(kt + PD, KT - 1);
@@ -419,8 +432,6 @@ __global__ __launch_bounds__(kThreads) void down_fp8_kernel(FfnCall c,
 #pragma unroll
         for (int j = 0; j < NB; ++j) bq[s][j] = glb_bfrag(b_src[j] + kb * kBK);
         __syncthreads();
-        // keep each step's instructions in its step (bounds register pressure
-        // of the unrolled loop)
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -437,7 +448,7 @@ __global__ __launch_bounds__(kThreads) void down_fp8_kernel(FfnCall c,
     for (int i = 0; i < MS; ++i) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int r = i * 16 + 4 * (lane >> 4) + q;
+        const int r = rbase + i * 16 + 4 * (lane >> 4) + q;
         if (r < te.nrows)
           out[(size_t)(te.row0 + r) * d + mcol[j]] = f32_to_bf16(acc[i][j][q] * sc);
       }
@@ -495,27 +506,31 @@ __global__ __launch_bounds__(256) void down_f32_kernel(FfnCall c, int sid) {
   static_cast<float*>(S.out)[(size_t)r * d + m] = acc;
 }
 
+// Waves along M for a tile height: one for decode-sized tiles, two from 64 rows.
+template <int BM>
+constexpr int waves_m() { return BM >= 64 ? 2 : 1; }
+
 template <int BM, int KTU, int BMD, int KTD>
 hipError_t launch_gemms_bm(const FfnCall& c, TileHeader* hdr, TileEntry* up, TileEntry* dn,
                            size_t cap_u, size_t cap_d, hipStream_t s, const StepEvents& ev) {
   const size_t cu = align_up(cap_u, kXcds);
   const size_t cd = align_up(cap_d, kXcds);
+  constexpr int WU = waves_m<BM>(), WD = waves_m<BMD>();
   ev.mark(true, MOE_STEP_GATE_UP, s);
   if (cu > 0)
-    hipLaunchKernelGGL((gateup_fp8_kernel<BM, KTU>), dim3((unsigned)cu), dim3(kThreads), 0, s, c,
-                       hdr, up);
+    hipLaunchKernelGGL((gateup_fp8_kernel<BM, WU, KTU>), dim3((unsigned)cu),
+                       dim3(kNWaves * WU * kWave), 0, s, c, hdr, up);
   ev.mark(false, MOE_STEP_GATE_UP, s);
   ev.mark(true, MOE_STEP_DOWN, s);
   if (cd > 0)
-    hipLaunchKernelGGL((down_fp8_kernel<BMD, KTD>), dim3((unsigned)cd), dim3(kThreads), 0, s, c,
-                       hdr, dn);
+    hipLaunchKernelGGL((down_fp8_kernel<BMD, WD, KTD>), dim3((unsigned)cd),
+                       dim3(kNWaves * WD * kWave), 0, s, c, hdr, dn);
   ev.mark(false, MOE_STEP_DOWN, s);
   return hipGetLastError();
 }
 
 // The gate/up GEMM is fully unrolled for d = 4096 (32 K steps, the model
-// shape); other hidden sizes, and the down GEMM (whose unrolled form runs out
-// of registers), use the looped kernels.
+// shape); other hidden sizes, and the down GEMM, use the looped kernels.
 template <int BM, int BMD>
 hipError_t launch_gemms_k(const FfnCall& c, TileHeader* hdr, TileEntry* up, TileEntry* dn,
                           size_t cap_u, size_t cap_d, hipStream_t s, const StepEvents& ev) {
