@@ -196,6 +196,17 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void gateup_fp8_kernel(
     const int wrow = (j < NS) ? hc : F + hc;
     b_src[j] = w13 + (size_t)wrow * d + (lane >> 4) * 16;
   }
+  // weight scales of this wave's columns, loaded now so that the epilogue
+  // waits on no load (its stores sit under row guards, where a pending load
+  // would make every store wait for all earlier ones)
+  const float* s13 = S.s13 + (size_t)g * 2 * F;
+  float sg[NS], su[NS];
+#pragma unroll
+  for (int jj = 0; jj < NS; ++jj) {
+    const int hc = te.ntile * kHN + wn * WN + jj * 16 + (lane & 15);
+    sg[jj] = s13[hc];
+    su[jj] = s13[F + hc];
+  }
 
   v4f acc[MS][NB];
 #pragma unroll
@@ -265,14 +276,6 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void gateup_fp8_kernel(
   }
 
   // ---- epilogue: scales, SwiGLU, per-(row, 128-col) amax ----
-  const float* s13 = S.s13 + (size_t)g * 2 * F;
-  float sg[NS], su[NS];
-#pragma unroll
-  for (int jj = 0; jj < NS; ++jj) {
-    const int hc = te.ntile * kHN + wn * WN + jj * 16 + (lane & 15);
-    sg[jj] = s13[hc];
-    su[jj] = s13[F + hc];
-  }
 #pragma unroll
   for (int i = 0; i < MS; ++i) {
 #pragma unroll
@@ -367,6 +370,10 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void down_fp8_kernel(
     mcol[j] = te.ntile * kDownBN + wn * (NB * 16) + j * 16 + (lane & 15);
     b_src[j] = w2 + (size_t)min(mcol[j], d - 1) * F + (lane >> 4) * 16;
   }
+  // channel scales, loaded now so that the epilogue waits on no load
+  float s2v[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) s2v[j] = S.s2[(size_t)g * d + min(mcol[j], d - 1)];
 
   v4f acc[MS][NB];
 #pragma unroll
@@ -438,17 +445,151 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void down_fp8_kernel(
   }
 
   // ---- epilogue: channel scale, bf16 ----
-  const float* s2 = S.s2 + (size_t)g * d;
   uint16_t* out = static_cast<uint16_t*>(S.out);
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
     if (mcol[j] >= d) continue;
-    const float sc = s2[mcol[j]];
+    const float sc = s2v[j];
 #pragma unroll
     for (int i = 0; i < MS; ++i) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int r = rbase + i * 16 + 4 * (lane >> 4) + q;
+        if (r < te.nrows)
+          out[(size_t)(te.row0 + r) * d + mcol[j]] = f32_to_bf16(acc[i][j][q] * sc);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Down GEMM for short tiles (BM x KT x 128 bytes of h fit in 32 KiB of LDS:
+// the decode shapes). The tile's whole h slab and its block scales are
+// loaded into LDS once, so the K loop has no barrier and no activation
+// traffic: each wave only streams its weight rows through a PD-deep register
+// ring, with exact wait counts (K fully unrolled). Same tile and wave layout
+// as down_fp8_kernel with WM = 1.
+// ---------------------------------------------------------------------------
+template <int BM, int KTC>
+__global__ __launch_bounds__(kNWaves * kWave) void down_fp8_resident_kernel(
+    FfnCall c, const TileHeader* __restrict__ hdr, const TileEntry* __restrict__ list) {
+  constexpr int NTH = kNWaves * kWave;
+  constexpr int MS = BM / 16;
+  constexpr int NB = 4;
+  constexpr int CHK = BM * (kBK / 16);  // 16-byte chunks per K step
+  constexpr int CPT = (CHK * KTC + NTH - 1) / NTH;
+  constexpr int PD = KTC < 4 ? KTC : 4;
+  static_assert(BM * KTC * kBK <= 32768, "h slab exceeds the LDS budget");
+
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a[KTC][BM * kBK];
+  __shared__ float hsl[KTC][BM];
+
+  int w;
+  if (!pick_tile(hdr->n_down, w)) return;
+  const TileEntry te = list[w];
+  const int sid = te.gid >> 16, g = te.gid & 0xffff;
+  const SetView S = set_view(c, sid);
+  const int d = c.d, F = S.F;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wn = tid / kWave;
+
+  const uint8_t* w2 = S.w2 + (size_t)g * d * F;
+  const uint8_t* b_src[NB];
+  int mcol[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    mcol[j] = te.ntile * kDownBN + wn * (NB * 16) + j * 16 + (lane & 15);
+    b_src[j] = w2 + (size_t)min(mcol[j], d - 1) * F + (lane >> 4) * 16;
+  }
+  // channel scales, loaded now so that the epilogue waits on no load
+  float s2v[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) s2v[j] = S.s2[(size_t)g * d + min(mcol[j], d - 1)];
+  // the h slab: chunk ch = (step, row, 16-byte column); rows past the tile's
+  // end repeat its last row (never stored)
+  v4i st[CPT];
+  int dst[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int ch = min(tid + i * NTH, CHK * KTC - 1);
+    const int kt = ch / CHK, cc = ch % CHK;
+    const int r = cc >> 3, c16 = cc & 7;
+    const size_t grow = (size_t)(te.row0 + min(r, te.nrows - 1));
+    st[i] = *reinterpret_cast<const v4i*>(S.h + grow * F + kt * kBK + c16 * 16);
+    dst[i] = kt * (BM * kBK) + swz(r, c16);
+  }
+  float hv[(BM * KTC + NTH - 1) / NTH];
+#pragma unroll
+  for (int i = 0; i < (BM * KTC + NTH - 1) / NTH; ++i) {
+    const int e = min(tid + i * NTH, BM * KTC - 1);
+    const int r = e / KTC, kt = e % KTC;
+    hv[i] = S.h_scale[(size_t)(te.row0 + min(r, te.nrows - 1)) * KTC + kt];
+  }
+  // weight ring, issued after the slab so that storing the slab to LDS waits
+  // for the slab alone
+  v8i bq[PD][NB];
+#pragma unroll
+  for (int s = 0; s < PD; ++s)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) bq[s][j] = glb_bfrag(b_src[j] + s * kBK);
+
+#pragma unroll
+  for (int i = 0; i < CPT; ++i)
+    if ((CHK * KTC) % NTH == 0 || tid + i * NTH < CHK * KTC)
+      *reinterpret_cast<v4i*>(&lds_a[0][0] + dst[i]) = st[i];
+#pragma unroll
+  for (int i = 0; i < (BM * KTC + NTH - 1) / NTH; ++i) {
+    const int e = tid + i * NTH;
+    if ((BM * KTC) % NTH == 0 || e < BM * KTC) hsl[e % KTC][e / KTC] = hv[i];
+  }
+  __syncthreads();
+
+  v4f acc[MS][NB];
+#pragma unroll
+  for (int i = 0; i < MS; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int kt = 0; kt < KTC; ++kt) {
+    const int s = kt % PD;
+#pragma unroll
+    for (int i = 0; i < MS; ++i) {
+      const v8i af = lds_afrag(lds_a[kt], i, lane);
+      v4f part[NB];
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        part[j] = mfma_fp8_16x16x128(af, bq[s][j], v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float hs = hsl[kt][i * 16 + 4 * (lane >> 4) + q];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j][q] = fmaf(part[j][q], hs, acc[i][j][q]);
+      }
+    }
+    if (kt + PD < KTC) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j) bq[s][j] = glb_bfrag(b_src[j] + (kt + PD) * kBK);
+    }
+    // keep each step's loads and scaled accumulation in the step (the
+    // scheduler would otherwise sink the loads towards their use, shortening
+    // the ring, and hold every partial product live to the end)
+#pragma unroll
+    for (int i = 0; i < MS; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) asm volatile("" : "+v"(acc[i][j]));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  uint16_t* out = static_cast<uint16_t*>(S.out);
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    if (mcol[j] >= d) continue;
+    const float sc = s2v[j];
+#pragma unroll
+    for (int i = 0; i < MS; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = i * 16 + 4 * (lane >> 4) + q;
         if (r < te.nrows)
           out[(size_t)(te.row0 + r) * d + mcol[j]] = f32_to_bf16(acc[i][j][q] * sc);
       }
@@ -522,19 +663,30 @@ hipError_t launch_gemms_bm(const FfnCall& c, TileHeader* hdr, TileEntry* up, Til
                        dim3(kNWaves * WU * kWave), 0, s, c, hdr, up);
   ev.mark(false, MOE_STEP_GATE_UP, s);
   ev.mark(true, MOE_STEP_DOWN, s);
-  if (cd > 0)
-    hipLaunchKernelGGL((down_fp8_kernel<BMD, WD, KTD>), dim3((unsigned)cd),
-                       dim3(kNWaves * WD * kWave), 0, s, c, hdr, dn);
+  if (cd > 0) {
+    if constexpr (KTD > 0 && BMD * KTD * kBK <= 32768)
+      hipLaunchKernelGGL((down_fp8_resident_kernel<BMD, KTD>), dim3((unsigned)cd),
+                         dim3(kNWaves * kWave), 0, s, c, hdr, dn);
+    else
+      hipLaunchKernelGGL((down_fp8_kernel<BMD, WD, KTD>), dim3((unsigned)cd),
+                         dim3(kNWaves * WD * kWave), 0, s, c, hdr, dn);
+  }
   ev.mark(false, MOE_STEP_DOWN, s);
   return hipGetLastError();
 }
 
-// The gate/up GEMM is fully unrolled for d = 4096 (32 K steps, the model
-// shape); other hidden sizes, and the down GEMM, use the looped kernels.
+// The K loops are fully unrolled for the model shape (d = 4096: 32 gate/up K
+// steps; F = 1024: 8 down K steps, routed and shared alike); other sizes use
+// the looped kernels.
 template <int BM, int BMD>
 hipError_t launch_gemms_k(const FfnCall& c, TileHeader* hdr, TileEntry* up, TileEntry* dn,
                           size_t cap_u, size_t cap_d, hipStream_t s, const StepEvents& ev) {
-  if (c.d / kBK == 32) return launch_gemms_bm<BM, 32, BMD, 0>(c, hdr, up, dn, cap_u, cap_d, s, ev);
+  const bool ku = c.d / kBK == 32;
+  const bool kd = c.set[0].F / kBK == 8 && (c.nsets < 2 || c.set[1].F / kBK == 8);
+  constexpr int KD = BMD <= 32 ? 8 : 0;  // larger tiles: the looped kernel
+  if (ku && kd) return launch_gemms_bm<BM, 32, BMD, KD>(c, hdr, up, dn, cap_u, cap_d, s, ev);
+  if (ku) return launch_gemms_bm<BM, 32, BMD, 0>(c, hdr, up, dn, cap_u, cap_d, s, ev);
+  if (kd) return launch_gemms_bm<BM, 0, BMD, KD>(c, hdr, up, dn, cap_u, cap_d, s, ev);
   return launch_gemms_bm<BM, 0, BMD, 0>(c, hdr, up, dn, cap_u, cap_d, s, ev);
 }
 

@@ -63,6 +63,13 @@ PARITY = {
     "fp8_wide": LayerConfig("fp8_wide", 600, 2048, 64, 6, 512, 512, "fp8", seed=18),
     "fp8_skew_small": LayerConfig("fp8_skew_small", 512, 1024, 128, 6, 256, 256, "fp8",
                                   seed=19, skew=True),
+    # the model's d = 4096 and F = 1024 (the shapes with fully unrolled K
+    # loops) at few tokens, one per GEMM tile height: ~12, 24, 100 and 190
+    # rows per expert select 16-, 32-, 128- and 192-row tiles
+    "fp8_model_m16": LayerConfig("fp8_model_m16", 48, 4096, 16, 4, 1024, 1024, "fp8", seed=20),
+    "fp8_model_m32": LayerConfig("fp8_model_m32", 96, 4096, 16, 4, 1024, 1024, "fp8", seed=21),
+    "fp8_model_m128": LayerConfig("fp8_model_m128", 400, 4096, 8, 2, 1024, 1024, "fp8", seed=22),
+    "fp8_model_m192": LayerConfig("fp8_model_m192", 380, 4096, 8, 4, 1024, 1024, "fp8", seed=23),
 }
 
 

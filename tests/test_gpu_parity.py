@@ -15,6 +15,7 @@ pytestmark = pytest.mark.gpu
 
 SMALL = ["tiny", "f32_ragged", "f32_noshared", "fp8_small", "fp8_ragged", "fp8_noshared",
          "fp8_k1", "fp8_kE", "fp8_wide", "fp8_skew_small"]
+MODEL = ["fp8_model_m16", "fp8_model_m32", "fp8_model_m128", "fp8_model_m192"]
 
 
 @pytest.fixture(autouse=True)
@@ -91,7 +92,7 @@ def test_permute_out_of_range_ids_get_no_row():
 
 
 @pytest.mark.parametrize("name", ["fp8_small", "fp8_ragged", "fp8_wide", "fp8_skew_small", "tiny",
-                                  "f32_ragged"])
+                                  "f32_ragged", "fp8_model_m16", "fp8_model_m128"])
 def test_grouped_ffn(name):
     """moe_grouped_ffn on the routed groups and on the shared expert, with the
     oracle's routing and x codes as input; h decisions validated, outputs
@@ -180,7 +181,7 @@ def test_combine(precision):
         assert np.all(np.abs(got - exact) <= np.abs(exact) * 2.0 ** -24 + acc_err * 1.01)
 
 
-@pytest.mark.parametrize("name", SMALL)
+@pytest.mark.parametrize("name", SMALL + MODEL)
 def test_layer_forward(name):
     """moe_layer_forward against the oracle; the separate entry points give
     bit-identical results, and their h decisions are validated."""
