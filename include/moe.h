@@ -136,23 +136,25 @@ moe_status_t moe_permute_workspace_size(const moe_shape_t* shape, size_t* bytes)
 moe_status_t moe_grouped_ffn_workspace_size(const moe_ffn_t* ffn, size_t* bytes);
 
 /*
- * Router: logits, softmax, top-k selection and renormalised gate weights in
- * one kernel (NVIDIA blog, Table 1 row "Router logits and TopK" and the
+ * Router: logits, softmax, top-k selection and renormalised gate weights
+ * (NVIDIA blog, Table 1 row "Router logits and TopK" and the
  * paragraph on MoE routing; peacm.com repost section 3.1: the fused router
  * writes integer expert indices and float scores; ijyty.com "InferX" page
  * section 2.4: softmax over the expert logits, then top-k).
  *
- *   l[t, e]  = sum_i x[t, i] * w_router[e, i] + router_bias[e]   (float32 accumulation)
+ *   l[t, e]  = sum_i x[t, i] * w_router[e, i] + router_bias[e]   (float32 accumulation;
+ *              on the bf16 path split over K, the slices summed in slice order)
  *   ids[t]   = the k experts with the largest l[t, .], largest first, equal
  *              logits ordered by lower expert index
  *   w[t, j]  = softmax(l[t, .])[ids[t, j]] / sum_j' softmax(l[t, .])[ids[t, j']]
  *
  * x [T][d] and w_router [E][d] in act_dtype; router_bias [E] float32 or NULL.
  * Outputs topk_ids [T][k] int32 and topk_w [T][k] float32. On the FP8 path the
- * same kernel also writes xq [T][d] (FP8 E4M3 codes of x / x_scale[t]) and
+ * logits launch also writes xq [T][d] (FP8 E4M3 codes of x / x_scale[t]) and
  * x_scale [T] (amax of row t over 448, 1.0 for a zero row); both are required
- * there and ignored on the float32 path. Needs a workspace of
- * moe_route_workspace_size() bytes (the float32 logits).
+ * there and ignored on the float32 path. Two launches (logits, selection).
+ * Needs a workspace of moe_route_workspace_size() bytes (the float32 partial
+ * logits of the K slices).
  */
 moe_status_t moe_route_topk(const moe_shape_t* shape, const void* x, const void* w_router,
                             const float* router_bias, int32_t* topk_ids, float* topk_w,
@@ -217,8 +219,10 @@ moe_status_t moe_layer_forward(const moe_shape_t* shape, const moe_weights_t* we
 
 /* Steps of moe_layer_forward, in launch order (for moe_layer_forward_events). */
 typedef enum moe_step {
-  MOE_STEP_ROUTE = 0,    /* router: logits and top-k kernels */
-  MOE_STEP_PERMUTE = 1,  /* permutation: scan (which also writes the FFN tile lists) and scatter */
+  MOE_STEP_ROUTE = 0,    /* router: logits and top-k kernels (T <= 64: the top-k kernel also
+                            does the permutation and writes the FFN tile lists) */
+  MOE_STEP_PERMUTE = 1,  /* permutation: scan (which also writes the FFN tile lists) and
+                            scatter; no kernels when T <= 64 */
   MOE_STEP_TILES = 2,    /* separate FFN tile-list kernel (moe_grouped_ffn only; none in the layer) */
   MOE_STEP_GATE_UP = 3,  /* gate/up GEMM + SwiGLU + h quantisation */
   MOE_STEP_DOWN = 4,     /* down GEMM */

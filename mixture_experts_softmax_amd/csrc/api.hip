@@ -121,7 +121,7 @@ LayerWs layer_ws(const moe_shape_t* s, void* base, FfnCall* call) {
   L.w = cv.take<float>(T * k * 4);
   L.xq = fp8 ? cv.take<uint8_t>(T * d) : nullptr;
   L.xs = fp8 ? cv.take<float>(T * 4) : nullptr;
-  L.logits = cv.take<float>(route_ws_bytes(s->T, s->E));
+  L.logits = cv.take<float>(route_ws_bytes(s->T, s->d, s->E));
   L.masks = cv.take<uint64_t>(perm_masks_bytes(s->T, s->E));
   L.counts = cv.take<int32_t>(perm_counts_bytes(s->T, s->E));
   L.offsets = cv.take<int32_t>((E + 1) * 4);
@@ -174,7 +174,7 @@ moe_status_t moe_route_workspace_size(const moe_shape_t* shape, size_t* bytes) {
   const moe_status_t st = check_shape(shape);
   if (st != MOE_OK) return st;
   if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
-  *bytes = route_ws_bytes(shape->T, shape->E);
+  *bytes = route_ws_bytes(shape->T, shape->d, shape->E);
   return MOE_OK;
 }
 
@@ -220,11 +220,11 @@ moe_status_t moe_route_topk(const moe_shape_t* s, const void* x, const void* w_r
   if (!al16(x) || !al16(w_router)) return MOE_ERR_INVALID_ARG;
   const bool fp8 = is_fp8(s);
   if (fp8 && (!xq || !x_scale || !al16(xq))) return MOE_ERR_INVALID_ARG;
-  if (!workspace || workspace_bytes < route_ws_bytes(s->T, s->E) || !al256(workspace))
+  if (!workspace || workspace_bytes < route_ws_bytes(s->T, s->d, s->E) || !al256(workspace))
     return MOE_ERR_WORKSPACE;
   return from_hip(launch_route(fp8, x, w_router, router_bias, s->T, s->d, s->E, s->k, topk_ids,
                                topk_w, fp8 ? xq : nullptr, fp8 ? x_scale : nullptr,
-                               static_cast<float*>(workspace), nullptr, nullptr,
+                               workspace, nullptr, nullptr, nullptr,
                                static_cast<hipStream_t>(stream)));
 }
 
@@ -337,16 +337,24 @@ moe_status_t moe_layer_forward_events(const moe_shape_t* s, const moe_weights_t*
   }
   const int bm = choose_bm(ceil_div(s->T * s->k, s->E));
 
+  // Up to one permutation tile of tokens, the top-k workgroup also does the
+  // permutation (and, FP8 path, writes the FFN tile lists); the permute step
+  // then has no kernels of its own.
+  const bool fused = s->T <= kPermTile;
+  RoutePermute rp{L.offsets, L.sorted_pair, L.pair_to_row, fp8 ? &c : nullptr, bm,
+                  fp8 ? L.tiles : nullptr};
   hipError_t e;
   ev.mark(true, MOE_STEP_ROUTE, hs);
   e = launch_route(fp8, x, wt->w_router, wt->router_bias, s->T, s->d, s->E, s->k, ids, w, L.xq,
-                   L.xs, L.logits, L.masks, L.counts, hs);
+                   L.xs, L.logits, L.masks, L.counts, fused ? &rp : nullptr, hs);
   ev.mark(false, MOE_STEP_ROUTE, hs);
   if (e != hipSuccess) return MOE_ERR_HIP;
   // scan + scatter; on the FP8 path the scan also writes the FFN tile lists
   ev.mark(true, MOE_STEP_PERMUTE, hs);
-  e = launch_perm_scan_scatter(ids, s->T, s->E, s->k, L.masks, L.counts, L.offsets, L.sorted_pair,
-                               L.pair_to_row, fp8 ? &c : nullptr, bm, fp8 ? L.tiles : nullptr, hs);
+  if (!fused)
+    e = launch_perm_scan_scatter(ids, s->T, s->E, s->k, L.masks, L.counts, L.offsets,
+                                 L.sorted_pair, L.pair_to_row, fp8 ? &c : nullptr, bm,
+                                 fp8 ? L.tiles : nullptr, hs);
   ev.mark(false, MOE_STEP_PERMUTE, hs);
   if (e != hipSuccess) return MOE_ERR_HIP;
 

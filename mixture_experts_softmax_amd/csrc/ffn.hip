@@ -27,12 +27,13 @@ constexpr int kBK = 128;      // K bytes per MFMA step (FP8 16x16x128)
 constexpr int kXcds = 8;
 constexpr int kTileThreads = 256;
 
-size_t tiles_cap(const FfnCall& c, int bm, bool up) {
+// Bound on the M-tile entries of one list: per set, its rows in tiles of bm
+// plus one partial tile per group.
+size_t tiles_cap(const FfnCall& c, int bm) {
   size_t n = 0;
   for (int s = 0; s < c.nsets; ++s) {
     const FfnSet& S = c.set[s];
-    const size_t mt = (size_t)ceil_div(S.max_rows, bm) + (size_t)S.G;
-    n += mt * (size_t)(up ? up_ntiles(S.F) : down_ntiles(c.d));
+    n += (size_t)ceil_div(S.max_rows, bm) + (size_t)S.G;
   }
   return n;
 }
@@ -66,12 +67,36 @@ __global__ __launch_bounds__(kTileThreads) void ffn_tiles_kernel(FfnCall c, int 
   emit_tiles(c, bm, NG, G0, L, hdr, up, down, cap_up, cap_dn);
 }
 
-// Block -> list entry, XCD-contiguous. Returns false for blocks with no work.
-__device__ inline bool pick_tile(const int total, int& w) {
+// Block -> work tile. The launch covers n_entries x NT items, dealt to the
+// XCDs in contiguous runs; item w belongs to list entry w / NT, whose group
+// owns items [first NT, (first + mt) NT) in N-tile-major, M-tile-minor order.
+// So the blocks of one XCD run the M tiles of one (group, N tile) one after
+// the other, sharing that weight tile in the XCD's L2, and a group's tiles
+// stay on one XCD. Returns false for blocks with no work.
+struct Tile {
+  int row0;   // first row, in the set's grouped row space
+  int nrows;  // 1..BM
+  int gid;    // (set << 16) | group
+  int ntile;
+};
+
+template <int BM>
+__device__ inline bool pick_tile(const TileEntry* __restrict__ list, int n_entries, int NT,
+                                 Tile& t) {
+  const int total = n_entries * NT;
   const int per = ceil_div(total, kXcds);
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
-  w = xcd * per + slot;
-  return slot < per && w < total;
+  const int w = xcd * per + slot;
+  if (slot >= per || w >= total) return false;
+  const TileEntry te = list[w / NT];
+  const int mt = ceil_div(te.rows, BM);
+  const int local = w - te.first * NT;
+  t.ntile = local / mt;
+  const int m = local - t.ntile * mt;
+  t.row0 = te.row0 + m * BM;
+  t.nrows = min(BM, te.rows - m * BM);
+  t.gid = te.gid;
+  return true;
 }
 
 __device__ inline v8i pack8(const v4i& lo, const v4i& hi) {
@@ -163,12 +188,13 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void gateup_fp8_kernel(
   __shared__ float sxl[BM];
   __shared__ float red[kNWaves][BM];
 
-  int w;
-  if (!pick_tile(hdr->n_up, w)) return;
-  const TileEntry te = list[w];
+  Tile te;
+  if (!pick_tile<BM>(list, hdr->n_up, up_ntiles_max(c), te)) return;
+  const int ntile = te.ntile;
   const int sid = te.gid >> 16, g = te.gid & 0xffff;
   const SetView S = set_view(c, sid);
   const int d = c.d, F = S.F;
+  if (ntile >= F / kHN) return;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int wm = wave / kNWaves, wn = wave % kNWaves;
   const int rbase = wm * BMW;
@@ -192,7 +218,7 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void gateup_fp8_kernel(
   const uint8_t* b_src[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
-    const int hc = te.ntile * kHN + wn * WN + (j % NS) * 16 + (lane & 15);
+    const int hc = ntile * kHN + wn * WN + (j % NS) * 16 + (lane & 15);
     const int wrow = (j < NS) ? hc : F + hc;
     b_src[j] = w13 + (size_t)wrow * d + (lane >> 4) * 16;
   }
@@ -203,7 +229,7 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void gateup_fp8_kernel(
   float sg[NS], su[NS];
 #pragma unroll
   for (int jj = 0; jj < NS; ++jj) {
-    const int hc = te.ntile * kHN + wn * WN + jj * 16 + (lane & 15);
+    const int hc = ntile * kHN + wn * WN + jj * 16 + (lane & 15);
     sg[jj] = s13[hc];
     su[jj] = s13[F + hc];
   }
@@ -311,10 +337,10 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void gateup_fp8_kernel(
       uint8_t* hrow = S.h + grow * F;
 #pragma unroll
       for (int jj = 0; jj < NS; ++jj) {
-        const int hc = te.ntile * kHN + wn * WN + jj * 16 + (lane & 15);
+        const int hc = ntile * kHN + wn * WN + jj * 16 + (lane & 15);
         hrow[hc] = e4m3_encode(__fdiv_rn(acc[i][jj][q], s));
       }
-      if (wn == 0 && (lane & 15) == 0) S.h_scale[grow * hblocks + te.ntile] = s;
+      if (wn == 0 && (lane & 15) == 0) S.h_scale[grow * hblocks + ntile] = s;
     }
   }
 }
@@ -339,9 +365,9 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void down_fp8_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * kBK];
   __shared__ float hsl[2][BM];
 
-  int w;
-  if (!pick_tile(hdr->n_down, w)) return;
-  const TileEntry te = list[w];
+  Tile te;
+  if (!pick_tile<BM>(list, hdr->n_down, down_ntiles(c.d), te)) return;
+  const int ntile = te.ntile;
   const int sid = te.gid >> 16, g = te.gid & 0xffff;
   const SetView S = set_view(c, sid);
   const int d = c.d, F = S.F, hblocks = F / kHN;
@@ -367,7 +393,7 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void down_fp8_kernel(
   int mcol[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
-    mcol[j] = te.ntile * kDownBN + wn * (NB * 16) + j * 16 + (lane & 15);
+    mcol[j] = ntile * kDownBN + wn * (NB * 16) + j * 16 + (lane & 15);
     b_src[j] = w2 + (size_t)min(mcol[j], d - 1) * F + (lane >> 4) * 16;
   }
   // channel scales, loaded now so that the epilogue waits on no load
@@ -484,9 +510,9 @@ __global__ __launch_bounds__(kNWaves * kWave) void down_fp8_resident_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[KTC][BM * kBK];
   __shared__ float hsl[KTC][BM];
 
-  int w;
-  if (!pick_tile(hdr->n_down, w)) return;
-  const TileEntry te = list[w];
+  Tile te;
+  if (!pick_tile<BM>(list, hdr->n_down, down_ntiles(c.d), te)) return;
+  const int ntile = te.ntile;
   const int sid = te.gid >> 16, g = te.gid & 0xffff;
   const SetView S = set_view(c, sid);
   const int d = c.d, F = S.F;
@@ -497,7 +523,7 @@ __global__ __launch_bounds__(kNWaves * kWave) void down_fp8_resident_kernel(
   int mcol[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
-    mcol[j] = te.ntile * kDownBN + wn * (NB * 16) + j * 16 + (lane & 15);
+    mcol[j] = ntile * kDownBN + wn * (NB * 16) + j * 16 + (lane & 15);
     b_src[j] = w2 + (size_t)min(mcol[j], d - 1) * F + (lane >> 4) * 16;
   }
   // channel scales, loaded now so that the epilogue waits on no load
@@ -654,8 +680,8 @@ constexpr int waves_m() { return BM >= 64 ? 2 : 1; }
 template <int BM, int KTU, int BMD, int KTD>
 hipError_t launch_gemms_bm(const FfnCall& c, TileHeader* hdr, TileEntry* up, TileEntry* dn,
                            size_t cap_u, size_t cap_d, hipStream_t s, const StepEvents& ev) {
-  const size_t cu = align_up(cap_u, kXcds);
-  const size_t cd = align_up(cap_d, kXcds);
+  const size_t cu = align_up(cap_u * up_ntiles_max(c), kXcds);
+  const size_t cd = align_up(cap_d * down_ntiles(c.d), kXcds);
   constexpr int WU = waves_m<BM>(), WD = waves_m<BMD>();
   ev.mark(true, MOE_STEP_GATE_UP, s);
   if (cu > 0)
@@ -694,9 +720,7 @@ hipError_t launch_gemms_k(const FfnCall& c, TileHeader* hdr, TileEntry* up, Tile
 
 size_t ffn_tiles_ws_bytes(const FfnCall& c) {
   // capacity for the smallest tile height (the largest list)
-  return align_up(sizeof(TileHeader) + (tiles_cap(c, 16, true) + tiles_cap(c, 16, false)) *
-                                            sizeof(TileEntry),
-                  256);
+  return align_up(sizeof(TileHeader) + 2 * tiles_cap(c, 16) * sizeof(TileEntry), 256);
 }
 
 size_t ffn_h_bytes(int max_rows, int F, bool fp8) {
@@ -727,9 +751,9 @@ void tile_lists(const FfnCall& c, int bm_up, int bm_dn, void* ws, TileHeader** h
                 TileEntry** up, TileEntry** dn, int* cap_up, int* cap_dn) {
   *hdr = static_cast<TileHeader*>(ws);
   *up = reinterpret_cast<TileEntry*>(*hdr + 1);
-  *dn = *up + tiles_cap(c, 16, true);
-  *cap_up = (int)tiles_cap(c, bm_up, true);
-  *cap_dn = (int)tiles_cap(c, bm_dn, false);
+  *dn = *up + tiles_cap(c, 16);
+  *cap_up = (int)tiles_cap(c, bm_up);
+  *cap_dn = (int)tiles_cap(c, bm_dn);
 }
 
 hipError_t launch_ffn_tiles(const FfnCall& c, int bm, void* ws, hipStream_t s) {

@@ -13,12 +13,26 @@ constexpr int kRouteTokens = 16;
 constexpr int kPermTile = 64;
 
 // ----- router ---------------------------------------------------------------
-// logits [T][E] float32 scratch; masks/counts (optional, [ceil(T/64)][E]) get
-// the permutation's per-tile expert masks and counts.
-size_t route_ws_bytes(int T, int E);
+struct FfnCall;
+// Optional fused permutation for a batch of at most kPermTile tokens: the
+// top-k workgroup writes offsets, sorted_pair and pair_to_row, and with c and
+// tiles_ws also the grouped-FFN tile lists of c for tile height bm.
+struct RoutePermute {
+  int32_t* offsets;
+  int32_t* sorted_pair;
+  int32_t* pair_to_row;
+  const FfnCall* c;
+  int bm;
+  void* tiles_ws;
+};
+// ws: the K-split partial logits (route_ws_bytes). masks/counts (optional,
+// [ceil(T/64)][E]) get the permutation's per-tile expert masks and counts;
+// ignored when the permutation is fused (T <= kPermTile and fuse != nullptr).
+size_t route_ws_bytes(int T, int d, int E);
 hipError_t launch_route(bool bf16, const void* x, const void* w_router, const float* bias, int T,
                         int d, int E, int k, int32_t* ids, float* w, uint8_t* xq, float* x_scale,
-                        float* logits, uint64_t* masks, int32_t* counts, hipStream_t s);
+                        void* ws, uint64_t* masks, int32_t* counts, const RoutePermute* fuse,
+                        hipStream_t s);
 
 // ----- permutation ----------------------------------------------------------
 size_t perm_masks_bytes(int T, int E);
@@ -26,7 +40,6 @@ size_t perm_counts_bytes(int T, int E);
 size_t permute_ws_bytes(int T, int E);
 hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* offsets,
                           int32_t* sorted_pair, int32_t* pair_to_row, void* ws, hipStream_t s);
-struct FfnCall;
 // scan + scatter from masks/counts already computed (counts become the tile
 // bases); with c != nullptr also writes the grouped-FFN tile lists of c.
 hipError_t launch_perm_scan_scatter(const int32_t* ids, int T, int E, int k, uint64_t* masks,

@@ -2,10 +2,13 @@
 // weights, and (bf16/FP8 path) per-token FP8 quantisation of x. The NVIDIA
 // Sarvam blog (Table 1 row "Router logits and TopK", MoE-routing paragraph)
 // fuses logit computation and selection into one kernel to cut launches and
-// memory round trips; here the logits of a token tile never leave the L2
-// between the two kernels, and the split buys parallelism: a T=64 decode
-// step spreads its 4096-deep dot products over 16 workgroups x 4 waves
-// instead of 4 workgroups.
+// memory round trips. Here the logits GEMM is split over K so that a decode
+// step's few tokens still spread their 4096-deep dot products over enough
+// workgroups to have the router weights in flight at once; the selection
+// kernel sums the K slices in a fixed order. For a batch of at most 64
+// tokens the selection workgroup also performs the whole permutation
+// (offsets, rows, FFN work lists), so routing and permutation take two
+// launches in all.
 //
 // Selection rule: the k largest logits, largest first, equal logits ordered
 // by lower expert index. Gate weights are the softmax over all E logits
@@ -16,15 +19,20 @@
 
 #include "common.h"
 #include "internal.h"
+#include "tiles.h"
 
 namespace moe {
 
 namespace {
 
-constexpr int kLogitWaves = 4;     // K split across the waves of a logits tile
-constexpr int kLogitExperts = 32;  // experts per logits tile (2 MFMA column tiles)
-constexpr int kTopkWaves = 16;     // one 64-token tile per top-k workgroup
+constexpr int kLogitWaves = 4;
+constexpr int kLogitExperts = kLogitWaves * 32;  // experts per logits tile (32 per wave)
+constexpr int kLogitChunk = 128;                  // K per pipeline stage (4 MFMA steps)
+constexpr int kLogitMinSlice = 256;               // smallest K slice
+constexpr int kLogitTargetWgs = 256;              // aim: at least one workgroup per CU
+constexpr int kTopkWaves = 16;  // one 64-token tile per top-k workgroup
 constexpr int kTokPerWave = kPermTile / kTopkWaves;
+constexpr int kXcds = 8;
 
 constexpr int kQuantGroup = 8;  // 16-byte loads per lane in flight per group
 
@@ -54,7 +62,9 @@ __device__ inline uint2 encode8(const v4i& c, float s) {
 
 // One wave quantises one bf16 row of length d (a multiple of 8) to FP8 E4M3
 // with scale amax/448: an amax pass and an encode pass, each issuing its
-// 16-byte loads in groups of 8 per lane.
+// 16-byte loads in groups of 8 per lane. Loads are unconditional (chunk index
+// clamped: a repeated chunk changes no maximum and is never stored) and the
+// codes are computed before the guarded stores, so no store waits on a load.
 __device__ inline void quantize_row(const uint16_t* __restrict__ xr, int d, int lane,
                                     uint8_t* __restrict__ qr, float* __restrict__ s_out) {
   const int nch = d / 8;  // 8-element chunks in the row
@@ -63,8 +73,8 @@ __device__ inline void quantize_row(const uint16_t* __restrict__ xr, int d, int 
     v4i v[kQuantGroup];
 #pragma unroll
     for (int i = 0; i < kQuantGroup; ++i) {
-      const int c = c0 + i * kWave + lane;
-      v[i] = (c < nch) ? *reinterpret_cast<const v4i*>(xr + (size_t)c * 8) : v4i{0, 0, 0, 0};
+      const int c = min(c0 + i * kWave + lane, nch - 1);
+      v[i] = *reinterpret_cast<const v4i*>(xr + (size_t)c * 8);
     }
 #pragma unroll
     for (int i = 0; i < kQuantGroup; ++i) amax = absmax8(v[i], amax);
@@ -75,83 +85,130 @@ __device__ inline void quantize_row(const uint16_t* __restrict__ xr, int d, int 
     v4i v[kQuantGroup];
 #pragma unroll
     for (int i = 0; i < kQuantGroup; ++i) {
-      const int c = c0 + i * kWave + lane;
-      v[i] = (c < nch) ? *reinterpret_cast<const v4i*>(xr + (size_t)c * 8) : v4i{0, 0, 0, 0};
+      const int c = min(c0 + i * kWave + lane, nch - 1);
+      v[i] = *reinterpret_cast<const v4i*>(xr + (size_t)c * 8);
     }
+    uint2 q[kQuantGroup];
+#pragma unroll
+    for (int i = 0; i < kQuantGroup; ++i) q[i] = encode8(v[i], s);
 #pragma unroll
     for (int i = 0; i < kQuantGroup; ++i) {
       const int c = c0 + i * kWave + lane;
-      if (c < nch) *reinterpret_cast<uint2*>(qr + (size_t)c * 8) = encode8(v[i], s);
+      if (c < nch) *reinterpret_cast<uint2*>(qr + (size_t)c * 8) = q[i];
     }
   }
   if (lane == 0) *s_out = s;
 }
 
 // ---------------------------------------------------------------------------
-// Logits, bf16: tile = 16 tokens x 32 experts; wave w accumulates K range
-// [w*d/4, (w+1)*d/4) with bf16 16x16x32 MFMAs; the partial tiles are summed
-// in LDS (fixed order: wave 0..3). The workgroups of a token tile also
-// quantise its tokens' x rows to FP8.
+// Logits, bf16, split over K: workgroup (token tile, expert tile, K slice)
+// computes 16 tokens x 128 experts over its slice, wave w the experts
+// [32 w, 32 w + 32) with bf16 16x16x32 MFMAs, two 128-deep K chunks in flight
+// per wave; it writes the raw partial sums (no bias) to part[slice][T][E].
+// Blocks past the logits grid quantise x: one token row per wave.
 // ---------------------------------------------------------------------------
+struct LogitGrid {
+  int n_tt, n_et, ks, cps;  // token tiles, expert tiles, K slices, chunks per slice
+  int n_logit;              // logits work items
+  int n_lblocks;            // logits blocks: n_logit rounded up to a multiple of the XCDs
+  int n_quant;              // quantisation workgroups
+};
+
+LogitGrid logit_grid(int T, int d, int E, bool quant) {
+  LogitGrid g;
+  g.n_tt = ceil_div(T, kRouteTokens);
+  g.n_et = ceil_div(E, kLogitExperts);
+  const int nch = d / kLogitChunk;
+  const int tiles = max(1, g.n_tt * g.n_et);  // T = 0 still sizes one tile
+  int ks = max(1, min(ceil_div(kLogitTargetWgs, tiles), d / kLogitMinSlice));
+  g.cps = ceil_div(nch, ks);
+  g.ks = ceil_div(nch, g.cps);  // no empty slice
+  g.n_logit = tiles * g.ks;
+  g.n_lblocks = (int)align_up(g.n_logit, kXcds);
+  g.n_quant = quant ? ceil_div(T, kLogitWaves) : 0;
+  return g;
+}
+
+__device__ inline void load_chunk(const uint16_t* xr, const uint16_t* w0, const uint16_t* w1,
+                                  int k0, v8bf* xa, v8bf* b0, v8bf* b1) {
+#pragma unroll
+  for (int s = 0; s < kLogitChunk / 32; ++s) {
+    xa[s] = *reinterpret_cast<const v8bf*>(xr + k0 + 32 * s);
+    b0[s] = *reinterpret_cast<const v8bf*>(w0 + k0 + 32 * s);
+    b1[s] = *reinterpret_cast<const v8bf*>(w1 + k0 + 32 * s);
+  }
+}
+
 __global__ __launch_bounds__(kLogitWaves * kWave) void route_logits_bf16_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
-    const float* __restrict__ bias, int T, int d, int E, float* __restrict__ logits,
-    uint8_t* __restrict__ xq, float* __restrict__ xs) {
-  __shared__ float part[kLogitWaves][kRouteTokens][kLogitExperts + 1];
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int d, int E,
+    LogitGrid g, float* __restrict__ part, uint8_t* __restrict__ xq, float* __restrict__ xs) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int tok0 = blockIdx.x * kRouteTokens;
-  const int e0 = blockIdx.y * kLogitExperts;
-
-  const int tok = min(tok0 + (lane & 15), T - 1);
-  const int kslice = d / kLogitWaves;
-  const int kbeg = wave * kslice + (lane >> 4) * 8;
-  const uint16_t* xrow = x + (size_t)tok * d + kbeg;
-  const uint16_t* w0 = wr + (size_t)min(e0 + (lane & 15), E - 1) * d + kbeg;
-  const uint16_t* w1 = wr + (size_t)min(e0 + 16 + (lane & 15), E - 1) * d + kbeg;
-  v4f a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-  for (int k0 = 0; k0 < kslice; k0 += 32) {
-    const v8bf xa = *reinterpret_cast<const v8bf*>(xrow + k0);
-    const v8bf b0 = *reinterpret_cast<const v8bf*>(w0 + k0);
-    const v8bf b1 = *reinterpret_cast<const v8bf*>(w1 + k0);
-    a0 = mfma_bf16_16x16x32(xa, b0, a0);
-    a1 = mfma_bf16_16x16x32(xa, b1, a1);
+  const int b = blockIdx.x;
+  if (b >= g.n_lblocks) {  // ---- FP8 quantisation of x: s = amax / 448, codes E4M3(x / s) ----
+    const int t = (b - g.n_lblocks) * kLogitWaves + wave;
+    if (t < T) quantize_row(x + (size_t)t * d, d, lane, xq + (size_t)t * d, xs + t);
+    return;
   }
+  // blocks are dealt to the XCDs in turn: remap so that one XCD takes a run
+  // of consecutive items, which share a K slice of the router weights (a
+  // bijection of [0, n_lblocks); items past n_logit have no work)
+  const int per_xcd = g.n_lblocks / kXcds;
+  const int wi = (b % kXcds) * per_xcd + b / kXcds;
+  if (wi >= g.n_logit) return;
+  const int tt = wi % g.n_tt;
+  const int et = (wi / g.n_tt) % g.n_et;
+  const int kz = wi / (g.n_tt * g.n_et);
+
+  const int tok = min(tt * kRouteTokens + (lane & 15), T - 1);
+  const int kq = (lane >> 4) * 8;  // the lane's 8 K elements of each 32-deep MFMA step
+  const int eb = et * kLogitExperts + wave * 32;
+  const uint16_t* xr = x + (size_t)tok * d + kq;
+  const uint16_t* w0 = wr + (size_t)min(eb + (lane & 15), E - 1) * d + kq;
+  const uint16_t* w1 = wr + (size_t)min(eb + 16 + (lane & 15), E - 1) * d + kq;
+  const int c0 = kz * g.cps;
+  const int c1 = min(c0 + g.cps, d / kLogitChunk);
+
+  constexpr int NS = kLogitChunk / 32;
+  v8bf xa[2][NS], b0[2][NS], b1[2][NS];
+  v4f a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+  // two chunks in flight; every load is issued (tail chunks re-load the last
+  // one) so the wait counts stay exact
+  load_chunk(xr, w0, w1, c0 * kLogitChunk, xa[0], b0[0], b1[0]);
+  load_chunk(xr, w0, w1, min(c0 + 1, c1 - 1) * kLogitChunk, xa[1], b0[1], b1[1]);
+  for (int c = c0; c < c1; c += 2) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      a0 = mfma_bf16_16x16x32(xa[0][s], b0[0][s], a0);
+      a1 = mfma_bf16_16x16x32(xa[0][s], b1[0][s], a1);
+    }
+    load_chunk(xr, w0, w1, min(c + 2, c1 - 1) * kLogitChunk, xa[0], b0[0], b1[0]);
+    if (c + 1 < c1) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        a0 = mfma_bf16_16x16x32(xa[1][s], b0[1][s], a0);
+        a1 = mfma_bf16_16x16x32(xa[1][s], b1[1][s], a1);
+      }
+    }
+    load_chunk(xr, w0, w1, min(c + 3, c1 - 1) * kLogitChunk, xa[1], b0[1], b1[1]);
+  }
+  float* out = part + (size_t)kz * T * E;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    part[wave][4 * (lane >> 4) + q][lane & 15] = a0[q];
-    part[wave][4 * (lane >> 4) + q][16 + (lane & 15)] = a1[q];
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < kRouteTokens * kLogitExperts; i += kLogitWaves * kWave) {
-    const int r = i / kLogitExperts, c = i % kLogitExperts;
-    const int t = tok0 + r, e = e0 + c;
-    if (t < T && e < E) {
-      float v = part[0][r][c];
-#pragma unroll
-      for (int w = 1; w < kLogitWaves; ++w) v += part[w][r][c];
-      logits[(size_t)t * E + e] = v + (bias != nullptr ? bias[e] : 0.f);
+    const int t = tt * kRouteTokens + 4 * (lane >> 4) + q;
+    const int e = eb + (lane & 15);
+    if (t < T) {
+      if (e < E) out[(size_t)t * E + e] = a0[q];
+      if (e + 16 < E) out[(size_t)t * E + e + 16] = a1[q];
     }
-  }
-
-  // ---- FP8 quantisation of x, per token: s = amax / 448, codes E4M3(x / s) ----
-  // The tile's 16 tokens are shared out over the gridDim.y workgroups of this
-  // token tile and their waves.
-  if (xq == nullptr) return;
-  const int nq = kLogitWaves * (int)gridDim.y;  // quantising waves per token tile
-  for (int r = blockIdx.y * kLogitWaves + wave; r < kRouteTokens; r += nq) {
-    const int t = tok0 + r;
-    if (t >= T) break;
-    quantize_row(x + (size_t)t * d, d, lane, xq + (size_t)t * d, xs + t);
   }
 }
 
 // Logits, float32: one wave per token, lane computes experts lane + 64c with a
-// sequential float32 dot product.
+// sequential float32 dot product (no bias; one K slice).
 __global__ __launch_bounds__(kLogitWaves * kWave) void route_logits_f32_kernel(
-    const float* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias,
-    int T, int d, int E, float* __restrict__ logits) {
+    const float* __restrict__ x, const float* __restrict__ wr, int T, int d, int E,
+    float* __restrict__ logits) {
   const int lane = threadIdx.x & (kWave - 1);
   const int t = blockIdx.x * kLogitWaves + threadIdx.x / kWave;
   if (t >= T) return;
@@ -160,39 +217,153 @@ __global__ __launch_bounds__(kLogitWaves * kWave) void route_logits_f32_kernel(
     const float* w = wr + (size_t)e * d;
     float acc = 0.f;
     for (int i = 0; i < d; ++i) acc = fmaf(xr[i], w[i], acc);
-    logits[(size_t)t * E + e] = acc + (bias != nullptr ? bias[e] : 0.f);
+    logits[(size_t)t * E + e] = acc;
   }
 }
 
 // ---------------------------------------------------------------------------
 // Top-k over the logits of one 64-token tile. Each wave serves 4 tokens at
-// once: the 16 lanes [16q, 16q + 16) take token 4w + q, lane holding experts
-// (lane % 16) + 16c. k rounds of a 16-lane (value desc, index asc) argmax
-// butterfly. Optionally records, per expert, the 64-bit mask of the tile's
-// tokens routed to it and its popcount (the permutation's per-tile histogram).
+// once: the 16 lanes [16q, 16q + 16) take token 4w + q, lane s holding the
+// PL = ceil(E/16) experts [s PL, s PL + PL). A logit is the sum of its K
+// slices in slice order, plus the bias. k rounds of a 16-lane (value desc,
+// index asc) argmax butterfly. Records, per expert, the 64-bit mask of the
+// tile's tokens routed to it; then either writes masks and popcounts (the
+// permutation's per-tile histogram) or, with FUSED (the batch is this one
+// tile), performs the permutation itself.
 // ---------------------------------------------------------------------------
-constexpr int kPerLane16 = MOE_MAX_E / 16;  // logits held per lane
+constexpr int kPerLane16 = MOE_MAX_E / 16;  // logits held per lane, at most
 
+struct TopkPermute {  // FUSED outputs
+  int32_t* offsets;
+  int32_t* sorted_pair;
+  int32_t* pair_to_row;
+  TileHeader* hdr;  // nullptr: no tile lists
+  TileEntry* up;
+  TileEntry* dn;
+  int cap_up, cap_dn, bm;
+};
+
+// 16-lane butterfly by DPP (within each row of 16 lanes): lane l exchanges
+// with l^1, l^2, then the mirror in its half row and in its row. Every lane
+// of a row ends with the same result for any commutative operation.
+template <int CTRL>
+__device__ inline int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ inline float dpp_f(float v) {
+  return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, v)));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror
+constexpr int kDppMirror = 0x140;      // row_mirror
+
+template <int CTRL>
+__device__ inline void argmax_step(float& bv, int& bi) {
+  const float ov = dpp_f<CTRL>(bv);
+  const int oi = dpp_i<CTRL>(bi);
+  if (ov > bv || (ov == bv && oi < bi)) {
+    bv = ov;
+    bi = oi;
+  }
+}
+// (largest value, lowest index among equal values) over the 16 lanes of a row
+__device__ inline void argmax16(float& bv, int& bi) {
+  argmax_step<kDppXor1>(bv, bi);
+  argmax_step<kDppXor2>(bv, bi);
+  argmax_step<kDppHalfMirror>(bv, bi);
+  argmax_step<kDppMirror>(bv, bi);
+}
+__device__ inline float sum16(float v) {
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  v += dpp_f<kDppMirror>(v);
+  return v;
+}
+
+// PL4 > 0: E = 64 PL4, lane logits read as PL4 16-byte vectors per K slice;
+// PL4 = 0: any E, scalar reads. Either way every read of a batch of K slices
+// is issued before the first is used, and the slices are added in order.
+template <bool FUSED, int PL4>
 __global__ __launch_bounds__(kTopkWaves * kWave) void route_topk_kernel(
-    const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ ids,
-    float* __restrict__ wts, uint64_t* __restrict__ masks, int32_t* __restrict__ counts) {
+    const float* __restrict__ part, int ks, const float* __restrict__ bias, int T, int E, int k,
+    int32_t* __restrict__ ids, float* __restrict__ wts, uint64_t* __restrict__ masks,
+    int32_t* __restrict__ counts, TopkPermute po, FfnCall c) {
   __shared__ unsigned long long mask[MOE_MAX_E];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int sub = lane & 15;
   const int tl = wave * kTokPerWave + (lane >> 4);  // token within the tile
   const int t = blockIdx.x * kPermTile + tl;
-  if (masks != nullptr) {
+  const bool track = FUSED || masks != nullptr;
+  if (track) {
     for (int e = threadIdx.x; e < E; e += kTopkWaves * kWave) mask[e] = 0ull;
     __syncthreads();
   }
   const bool live = t < T;
-  const float* lr = logits + (size_t)min(t, T - 1) * E;
-  float v[kPerLane16];
+  const int tc = min(t, T - 1);
+  const int PL = PL4 > 0 ? 4 * PL4 : ceil_div(E, 16);
+  const int ebase = sub * PL;
+  // bias first (all reads issued together, clamped index; unused past E)
+  float bsv[kPerLane16];
 #pragma unroll
-  for (int c = 0; c < kPerLane16; ++c) {
-    const int e = sub + 16 * c;
-    v[c] = (e < E) ? lr[e] : -INFINITY;
+  for (int cc = 0; cc < kPerLane16; ++cc)
+    bsv[cc] = (bias != nullptr && cc < PL) ? bias[min(ebase + cc, E - 1)] : 0.f;
+  float v[kPerLane16];
+  if constexpr (PL4 > 0) {
+    constexpr int ZB = 16 / PL4;  // K slices per batch (16 vectors in flight)
+    v4f acc[PL4];
+#pragma unroll
+    for (int c4 = 0; c4 < PL4; ++c4) acc[c4] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int z0 = 0; z0 < ks; z0 += ZB) {
+      v4f p[ZB][PL4];
+#pragma unroll
+      for (int zz = 0; zz < ZB; ++zz) {
+        const int z = min(z0 + zz, ks - 1);
+#pragma unroll
+        for (int c4 = 0; c4 < PL4; ++c4)
+          p[zz][c4] = *reinterpret_cast<const v4f*>(part + ((size_t)z * T + tc) * E + ebase + 4 * c4);
+      }
+#pragma unroll
+      for (int zz = 0; zz < ZB; ++zz)
+        if (z0 + zz < ks) {
+#pragma unroll
+          for (int c4 = 0; c4 < PL4; ++c4)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[c4][q] += p[zz][c4][q];
+        }
+    }
+#pragma unroll
+    for (int c4 = 0; c4 < PL4; ++c4)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[4 * c4 + q] = acc[c4][q];
+  } else {
+    constexpr int ZB = 2;
+#pragma unroll
+    for (int cc = 0; cc < kPerLane16; ++cc) v[cc] = 0.f;
+    for (int z0 = 0; z0 < ks; z0 += ZB) {
+      float p[ZB][kPerLane16];
+#pragma unroll
+      for (int zz = 0; zz < ZB; ++zz) {
+        const int z = min(z0 + zz, ks - 1);
+#pragma unroll
+        for (int cc = 0; cc < kPerLane16; ++cc)
+          p[zz][cc] = part[((size_t)z * T + tc) * E + min(ebase + cc, E - 1)];
+      }
+#pragma unroll
+      for (int zz = 0; zz < ZB; ++zz)
+        if (z0 + zz < ks) {
+#pragma unroll
+          for (int cc = 0; cc < kPerLane16; ++cc) v[cc] += p[zz][cc];
+        }
+    }
+  }
+#pragma unroll
+  for (int cc = 0; cc < kPerLane16; ++cc) {
+    const int e = ebase + cc;
+    if (cc < PL) v[cc] = (e < E) ? v[cc] + bsv[cc] : -INFINITY;
   }
   uint32_t taken = 0;
   int my_e = 0;
@@ -201,23 +372,16 @@ __global__ __launch_bounds__(kTopkWaves * kWave) void route_topk_kernel(
     float bv = -INFINITY;
     int bi = 0x7fffffff;
 #pragma unroll
-    for (int c = 0; c < kPerLane16; ++c) {
-      const int e = sub + 16 * c;
-      if (e < E && !((taken >> c) & 1u) && (v[c] > bv || (v[c] == bv && e < bi))) {
-        bv = v[c];
+    for (int cc = 0; cc < kPerLane16; ++cc) {
+      const int e = ebase + cc;
+      if (cc < PL && e < E && !((taken >> cc) & 1u) && (v[cc] > bv || (v[cc] == bv && e < bi))) {
+        bv = v[cc];
         bi = e;
       }
     }
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, kWave);
-      const int oi = __shfl_xor(bi, o, kWave);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if ((bi & 15) == sub) taken |= 1u << (bi >> 4);
+    argmax16(bv, bi);
+    const int own = bi - ebase;
+    if (own >= 0 && own < PL) taken |= 1u << own;
     if (j == 0) top = bv;
     if (sub == j) {
       my_e = bi;
@@ -225,42 +389,143 @@ __global__ __launch_bounds__(kTopkWaves * kWave) void route_topk_kernel(
     }
   }
   const float ex = (sub < k) ? expf(my_v - top) : 0.f;
-  float den = ex;
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) den += __shfl_xor(den, o, kWave);
-  if (live && sub < k) {
+  const float den = sum16(ex);
+  const bool mine = live && sub < k;
+  if (mine) {
     ids[(size_t)t * k + sub] = my_e;
     wts[(size_t)t * k + sub] = ex / den;
-    if (masks != nullptr) atomicOr(&mask[my_e], 1ull << tl);
+    if (track) atomicOr(&mask[my_e], 1ull << tl);
   }
-  if (masks != nullptr) {
-    __syncthreads();
+  if (!track) return;
+  __syncthreads();
+  if constexpr (!FUSED) {
     for (int e = threadIdx.x; e < E; e += kTopkWaves * kWave) {
       masks[(size_t)blockIdx.x * E + e] = mask[e];
       counts[(size_t)blockIdx.x * E + e] = __popcll(mask[e]);
     }
+  } else {
+    // the permutation of this one tile: group sizes are the mask popcounts,
+    // offsets their exclusive scan (wave 0, 4 experts per lane), a pair's row
+    // its group offset plus the number of earlier tokens in the group
+    __shared__ int offs[MOE_MAX_E + 1];
+    __shared__ TileLds L;
+    if (wave == 0) {
+      constexpr int per = MOE_MAX_E / kWave;
+      int cnt[per], sum = 0;
+#pragma unroll
+      for (int i = 0; i < per; ++i) {
+        const int e = lane * per + i;
+        cnt[i] = (e < E) ? __popcll(mask[e]) : 0;
+        sum += cnt[i];
+      }
+      int acc = wave_incl_scan(sum, lane) - sum;
+#pragma unroll
+      for (int i = 0; i < per; ++i) {
+        const int e = lane * per + i;
+        if (e < E) {
+          offs[e] = acc;
+          po.offsets[e] = acc;
+          if (po.hdr != nullptr) {
+            L.g_row0[e] = acc;
+            L.g_rows[e] = cnt[i];
+            L.g_set[e] = 0;
+          }
+        }
+        acc += cnt[i];
+      }
+      if (lane == kWave - 1) {
+        offs[E] = acc;
+        po.offsets[E] = acc;
+      }
+      if (lane == 0 && po.hdr != nullptr && c.nsets > 1) {
+        L.g_row0[E] = 0;
+        L.g_rows[E] = min(c.set[1].rows_fixed, c.set[1].max_rows);
+        L.g_set[E] = 1;
+      }
+    }
+    __syncthreads();
+    if (mine) {
+      const unsigned long long below = (tl == 0) ? 0ull : (~0ull >> (64 - tl));
+      const int p = t * k + sub;
+      const int row = offs[my_e] + __popcll(mask[my_e] & below);
+      po.sorted_pair[row] = p;
+      po.pair_to_row[p] = row;
+    }
+    if (po.hdr != nullptr)
+      emit_tiles(c, po.bm, E + (c.nsets > 1 ? 1 : 0), E, L, po.hdr, po.up, po.dn, po.cap_up,
+                 po.cap_dn);
   }
 }
 
 }  // namespace
 
-size_t route_ws_bytes(int T, int E) { return align_up((size_t)T * E * sizeof(float), 256); }
+// Rows of partial logits (K slices x tokens) the workspace holds: a bound on
+// ks * T that grows with T, so a workspace sized for a batch serves every
+// smaller one. ks <= d/256 gives T * max(1, d/256); ks <= ceil(256 / tiles)
+// with T <= 16 * token tiles gives T + 4096 / expert tiles.
+size_t route_partial_rows(int T, int d, int E) {
+  const size_t n_et = ceil_div(E, kLogitExperts);
+  const size_t a = (size_t)T * max(1, d / kLogitMinSlice);
+  const size_t b = (size_t)T + ceil_div(kLogitTargetWgs * kRouteTokens, (int)n_et);
+  return a < b ? a : b;
+}
+
+size_t route_ws_bytes(int T, int d, int E) {
+  return align_up(route_partial_rows(T, d, E) * E * sizeof(float), 256);
+}
 
 hipError_t launch_route(bool bf16, const void* x, const void* w_router, const float* bias, int T,
                         int d, int E, int k, int32_t* ids, float* w, uint8_t* xq, float* x_scale,
-                        float* logits, uint64_t* masks, int32_t* counts, hipStream_t s) {
+                        void* ws, uint64_t* masks, int32_t* counts, const RoutePermute* fuse,
+                        hipStream_t s) {
+  float* part = static_cast<float*>(ws);
+  int ks = 1;
   if (bf16) {
-    const dim3 grid(ceil_div(T, kRouteTokens), ceil_div(E, kLogitExperts));
-    hipLaunchKernelGGL(route_logits_bf16_kernel, grid, dim3(kLogitWaves * kWave), 0, s,
-                       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router),
-                       bias, T, d, E, logits, xq, x_scale);
+    const LogitGrid g = logit_grid(T, d, E, xq != nullptr);
+    ks = g.ks;
+    if ((size_t)ks * T > route_partial_rows(T, d, E)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(route_logits_bf16_kernel, dim3(g.n_lblocks + g.n_quant),
+                       dim3(kLogitWaves * kWave), 0, s, static_cast<const uint16_t*>(x),
+                       static_cast<const uint16_t*>(w_router), T, d, E, g, part, xq, x_scale);
   } else {
     hipLaunchKernelGGL(route_logits_f32_kernel, dim3(ceil_div(T, kLogitWaves)),
                        dim3(kLogitWaves * kWave), 0, s, static_cast<const float*>(x),
-                       static_cast<const float*>(w_router), bias, T, d, E, logits);
+                       static_cast<const float*>(w_router), T, d, E, part);
   }
-  hipLaunchKernelGGL(route_topk_kernel, dim3(ceil_div(T, kPermTile)), dim3(kTopkWaves * kWave), 0,
-                     s, logits, T, E, k, ids, w, masks, counts);
+  const dim3 grid(ceil_div(T, kPermTile)), block(kTopkWaves * kWave);
+  TopkPermute po{};
+  FfnCall c{};
+  if (fuse != nullptr && T <= kPermTile) {
+    po.offsets = fuse->offsets;
+    po.sorted_pair = fuse->sorted_pair;
+    po.pair_to_row = fuse->pair_to_row;
+    if (fuse->c != nullptr && fuse->tiles_ws != nullptr) {
+      c = *fuse->c;
+      po.bm = fuse->bm;
+      tile_lists(c, po.bm, down_bm(po.bm), fuse->tiles_ws, &po.hdr, &po.up, &po.dn, &po.cap_up,
+                 &po.cap_dn);
+    }
+  }
+  const bool fused = po.offsets != nullptr;
+  const int pl4 = (E % 64 == 0) ? E / 64 : 0;
+#define MOE_TOPK(F, P)                                                                          \
+  hipLaunchKernelGGL((route_topk_kernel<F, P>), grid, block, 0, s, part, ks, bias, T, E, k, ids, \
+                     w, masks, counts, po, c)
+#define MOE_TOPK_F(F)        \
+  switch (pl4) {             \
+    case 1: MOE_TOPK(F, 1); break; \
+    case 2: MOE_TOPK(F, 2); break; \
+    case 3: MOE_TOPK(F, 3); break; \
+    case 4: MOE_TOPK(F, 4); break; \
+    default: MOE_TOPK(F, 0); break; \
+  }
+  if (fused) {
+    MOE_TOPK_F(true)
+  } else {
+    MOE_TOPK_F(false)
+  }
+#undef MOE_TOPK_F
+#undef MOE_TOPK
   return hipGetLastError();
 }
 

@@ -1,8 +1,9 @@
-// Grouped-FFN work lists: for every non-empty group, its M tiles (up to BM
-// rows) times its N tiles, the M tiles of one (group, N tile) adjacent so
-// that consecutive list entries share weights. Emitted by one workgroup;
-// used by the tile-list kernel of moe_grouped_ffn and by the permutation scan
-// of moe_layer_forward (which knows the group sizes first).
+// Grouped-FFN work lists: for every non-empty group, one entry per M tile (up
+// to BM rows each), one list for the gate/up GEMM (tile height bm) and one
+// for the down GEMM (down_bm(bm)). A GEMM launch covers (list entry, N tile)
+// pairs; the block index selects the pair. Emitted by one workgroup; used by
+// the tile-list kernel of moe_grouped_ffn and by the permutation of
+// moe_layer_forward (which knows the group sizes first).
 #pragma once
 
 #include "common.h"
@@ -14,29 +15,39 @@ constexpr int kHN = 128;      // h columns per gate/up tile = one h quantisation
 constexpr int kDownBN = 256;  // output channels per down tile
 constexpr int kMaxGroups = 1024;
 
+// One entry per M tile of a group; every entry of a group holds the group's
+// data (a block finds its M tile from the entry's position).
 struct TileEntry {
-  int row0;   // first row of the tile, in the set's grouped row space
-  int nrows;  // rows in this tile, 1..BM
+  int row0;   // first row of the group, in the set's grouped row space
+  int rows;   // rows of the group (> 0)
   int gid;    // (set << 16) | group
-  int ntile;  // N tile index
+  int first;  // index of the group's first entry in this list
 };
 
 struct TileHeader {
-  int n_up;
-  int n_down;
+  int n_up;    // entries in the gate/up list
+  int n_down;  // entries in the down list
   int pad[62];
 };
 
 __host__ __device__ inline int up_ntiles(int F) { return F / kHN; }
 __host__ __device__ inline int down_ntiles(int d) { return ceil_div(d, kDownBN); }
+// N tiles of a gate/up launch: the widest set's h blocks (blocks past a
+// narrower set's width exit at once).
+__host__ __device__ inline int up_ntiles_max(const FfnCall& c) {
+  const int f = (c.nsets > 1 && c.set[1].F > c.set[0].F) ? c.set[1].F : c.set[0].F;
+  return up_ntiles(f);
+}
 
 // LDS state of the emitter; the caller fills g_row0/g_rows/g_set for NG groups.
 struct TileLds {
   int g_row0[kMaxGroups];
   int g_rows[kMaxGroups];
   int g_set[kMaxGroups];
-  int pre_up[kMaxGroups + 1];
+  int pre_up[kMaxGroups + 1];  // exclusive prefix of the groups' list entries
   int pre_dn[kMaxGroups + 1];
+  int wtot_up[16];             // per-wave totals of one scan chunk
+  int wtot_dn[16];
 };
 
 // Host: where the lists of call c live in its tile workspace, and their
@@ -48,67 +59,81 @@ void tile_lists(const FfnCall& c, int bm_up, int bm_dn, void* ws, TileHeader** h
 // holds no more than 128 rows).
 __host__ __device__ inline int down_bm(int bm_up) { return bm_up < 128 ? bm_up : 128; }
 
-// All threads of the block call this after the group arrays are filled and
-// synchronised. cap_up / cap_dn bound the lists (entries beyond are dropped,
-// which only happens for malformed group offsets).
+// All threads of the block (at most 1024) call this after the group arrays are
+// filled and synchronised. cap_up / cap_dn bound the lists (entries beyond are
+// dropped, which only happens for malformed group offsets).
+//   1. M tiles per group, exclusive block-wide scan (chunks of the block
+//      size: wave scans, then the wave totals);
+//   2. one thread per list entry: its group is the last one whose prefix is
+//      not above the entry's index (binary search; empty groups never match).
 __device__ inline void emit_tiles(const FfnCall& c, int bm, int NG, int G0, TileLds& L,
                                   TileHeader* hdr, TileEntry* up, TileEntry* down, int cap_up,
                                   int cap_dn) {
   const int bmd = down_bm(bm);
   const int tid = threadIdx.x, nth = blockDim.x;
-  const int dnt = down_ntiles(c.d);
-  const int F0 = c.set[0].F, F1 = c.set[1].F;
-  // exclusive scans of the per-group entry counts, by wave 0 (lane owns a run
-  // of groups; a shuffle scan over the lanes)
   const int lane = tid & (kWave - 1), wave = tid / kWave, nwaves = nth / kWave;
-  if (wave == 0) {
-    const int per = ceil_div(NG, kWave);
-    const int lo = min(NG, lane * per), hi = min(NG, lo + per);
-    int su = 0, sd = 0;
-    for (int i = lo; i < hi; ++i) {
-      su += ceil_div(L.g_rows[i], bm) * up_ntiles(L.g_set[i] == 0 ? F0 : F1);
-      sd += ceil_div(L.g_rows[i], bmd) * dnt;
+  int carry_u = 0, carry_d = 0;  // identical in every thread
+  for (int base = 0; base < NG; base += nth) {
+    const int i = base + tid;
+    int cu = 0, cd = 0;
+    if (i < NG) {
+      const int rows = L.g_rows[i];
+      cu = ceil_div(rows, bm);
+      cd = ceil_div(rows, bmd);
     }
-    const int iu = wave_incl_scan(su, lane), id = wave_incl_scan(sd, lane);
-    su = iu - su;
-    sd = id - sd;
-    for (int i = lo; i < hi; ++i) {
-      L.pre_up[i] = su;
-      L.pre_dn[i] = sd;
-      su += ceil_div(L.g_rows[i], bm) * up_ntiles(L.g_set[i] == 0 ? F0 : F1);
-      sd += ceil_div(L.g_rows[i], bmd) * dnt;
-    }
+    const int iu = wave_incl_scan(cu, lane), id = wave_incl_scan(cd, lane);
     if (lane == kWave - 1) {
-      L.pre_up[NG] = iu;
-      L.pre_dn[NG] = id;
+      L.wtot_up[wave] = iu;
+      L.wtot_dn[wave] = id;
     }
-  }
-  __syncthreads();
-  // one wave per group writes its entries
-  for (int i = wave; i < NG; i += nwaves) {
-    const int rows = L.g_rows[i];
-    if (rows == 0) continue;
-    const int mt = ceil_div(rows, bm), mtd = ceil_div(rows, bmd);
-    const int s = L.g_set[i];
-    const int gid = (s << 16) | (s == 0 ? i : i - G0);
-    const int nu = mt * up_ntiles(s == 0 ? F0 : F1), nd = mtd * dnt;
-    for (int j = lane; j < nu + nd; j += kWave) {
-      const bool is_up = j < nu;
-      const int loc = is_up ? j : j - nu;
-      const int idx = (is_up ? L.pre_up[i] : L.pre_dn[i]) + loc;
-      if (idx >= (is_up ? cap_up : cap_dn)) continue;
-      const int h = is_up ? bm : bmd, m = loc % (is_up ? mt : mtd);
-      TileEntry e;
-      e.row0 = L.g_row0[i] + m * h;
-      e.nrows = min(h, rows - m * h);
-      e.gid = gid;
-      e.ntile = loc / (is_up ? mt : mtd);
-      (is_up ? up : down)[idx] = e;
+    __syncthreads();
+    int pu = carry_u, pd = carry_d, tu = 0, td = 0;
+    for (int w = 0; w < nwaves; ++w) {
+      const int a = L.wtot_up[w], b = L.wtot_dn[w];
+      if (w < wave) {
+        pu += a;
+        pd += b;
+      }
+      tu += a;
+      td += b;
     }
+    if (i < NG) {
+      L.pre_up[i] = pu + iu - cu;
+      L.pre_dn[i] = pd + id - cd;
+    }
+    carry_u += tu;
+    carry_d += td;
+    __syncthreads();  // wave totals are rewritten by the next chunk
   }
   if (tid == 0) {
-    hdr->n_up = min(L.pre_up[NG], cap_up);
-    hdr->n_down = min(L.pre_dn[NG], cap_dn);
+    L.pre_up[NG] = carry_u;
+    L.pre_dn[NG] = carry_d;
+  }
+  const int n_up = min(carry_u, cap_up), n_dn = min(carry_d, cap_dn);
+  __syncthreads();
+  for (int idx = tid; idx < n_up + n_dn; idx += nth) {
+    const bool is_up = idx < n_up;
+    const int j = is_up ? idx : idx - n_up;
+    const int* pre = is_up ? L.pre_up : L.pre_dn;
+    int lo = 0, hi = NG - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pre[mid] <= j)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    const int s = L.g_set[lo];
+    TileEntry e;
+    e.row0 = L.g_row0[lo];
+    e.rows = L.g_rows[lo];
+    e.gid = (s << 16) | (s == 0 ? lo : lo - G0);
+    e.first = pre[lo];
+    (is_up ? up : down)[j] = e;
+  }
+  if (tid == 0) {
+    hdr->n_up = n_up;
+    hdr->n_down = n_dn;
   }
 }
 

@@ -60,6 +60,22 @@ def test_check_shape(kw, status):
     assert _lib.moe_check_shape(fp8_shape(**kw)) == status
 
 
+@pytest.mark.parametrize("T", [0, 1, 63, 64, 65, 3584, 1 << 22])
+@pytest.mark.parametrize("d,E", [(128, 1), (256, 8), (4096, 128), (16384, 256)])
+def test_workspace_sizes_for_any_batch(T, d, E):
+    """Host-only size queries are defined for every valid shape, the empty
+    batch included, and grow with the batch."""
+    for prec in ("fp8", "f32"):
+        s = _lib.shape(T, d, E, min(2, E), 128, 128, prec)
+        assert _lib.moe_check_shape(s) == _lib.MOE_OK
+        lw, rw, pw = (_lib.moe_layer_workspace_size(s), _lib.moe_route_workspace_size(s),
+                      _lib.moe_permute_workspace_size(s))
+        assert lw >= 0 and rw >= T * E * 4 and pw >= 0
+        if T:
+            s0 = _lib.shape(T - 1, d, E, min(2, E), 128, 128, prec)
+            assert _lib.moe_layer_workspace_size(s0) <= lw
+
+
 def test_unsupported_dtype_pairs():
     for act, w in [(_lib.MOE_DTYPE_BF16, _lib.MOE_DTYPE_F32), (_lib.MOE_DTYPE_F32, _lib.MOE_DTYPE_FP8_E4M3),
                    (_lib.MOE_DTYPE_FP8_E4M3, _lib.MOE_DTYPE_FP8_E4M3), (7, 2)]:
