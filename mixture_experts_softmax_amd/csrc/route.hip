@@ -259,28 +259,43 @@ constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
 constexpr int kDppHalfMirror = 0x141;  // row_half_mirror
 constexpr int kDppMirror = 0x140;      // row_mirror
 
-template <int CTRL>
-__device__ inline void argmax_step(float& bv, int& bi) {
-  const float ov = dpp_f<CTRL>(bv);
-  const int oi = dpp_i<CTRL>(bi);
-  if (ov > bv || (ov == bv && oi < bi)) {
-    bv = ov;
-    bi = oi;
-  }
-}
-// (largest value, lowest index among equal values) over the 16 lanes of a row
-__device__ inline void argmax16(float& bv, int& bi) {
-  argmax_step<kDppXor1>(bv, bi);
-  argmax_step<kDppXor2>(bv, bi);
-  argmax_step<kDppHalfMirror>(bv, bi);
-  argmax_step<kDppMirror>(bv, bi);
-}
 __device__ inline float sum16(float v) {
   v += dpp_f<kDppXor1>(v);
   v += dpp_f<kDppXor2>(v);
   v += dpp_f<kDppHalfMirror>(v);
   v += dpp_f<kDppMirror>(v);
   return v;
+}
+
+// 64-bit selection key of (logit v, expert e): float bits mapped so that
+// unsigned order is float order, above the complemented index. -0 is taken
+// as +0 (equal logits tie on the index). Key 0 is below every real key.
+__device__ inline uint64_t logit_key(float v, int e) {
+  const uint32_t u = __float_as_uint(v + 0.0f);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)o << 32) | (uint32_t)~(uint32_t)e;
+}
+__device__ inline int key_expert(uint64_t key) { return (int)~(uint32_t)key; }
+__device__ inline float key_logit(uint64_t key) {
+  const uint32_t o = (uint32_t)(key >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+template <int CTRL>
+__device__ inline uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)dpp_i<CTRL>((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)dpp_i<CTRL>((int)(uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+template <int CTRL>
+__device__ inline uint64_t max_step_u64(uint64_t v) {
+  const uint64_t o = dpp_u64<CTRL>(v);
+  return o > v ? o : v;
+}
+__device__ inline uint64_t max16_u64(uint64_t v) {
+  v = max_step_u64<kDppXor1>(v);
+  v = max_step_u64<kDppXor2>(v);
+  v = max_step_u64<kDppHalfMirror>(v);
+  return max_step_u64<kDppMirror>(v);
 }
 
 // PL4 > 0: E = 64 PL4, lane logits read as PL4 16-byte vectors per K slice;
@@ -365,23 +380,28 @@ __global__ __launch_bounds__(kTopkWaves * kWave) void route_topk_kernel(
     const int e = ebase + cc;
     if (cc < PL) v[cc] = (e < E) ? v[cc] + bsv[cc] : -INFINITY;
   }
-  uint32_t taken = 0;
+  // Selection on 64-bit keys (order-preserving bits of the logit, then the
+  // complement of the expert index): the largest key is the largest logit,
+  // lowest index first among equal logits. Branch-free: per round the lane's
+  // largest remaining key, the row's largest by DPP butterfly, and the owner
+  // clears it.
+  uint64_t key[kPerLane16];
+#pragma unroll
+  for (int cc = 0; cc < kPerLane16; ++cc) {
+    const int e = ebase + cc;
+    key[cc] = (cc < PL && e < E) ? logit_key(v[cc], e) : 0ull;
+  }
   int my_e = 0;
   float my_v = -FLT_MAX, top = 0.f;
   for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
+    uint64_t best = key[0];
 #pragma unroll
-    for (int cc = 0; cc < kPerLane16; ++cc) {
-      const int e = ebase + cc;
-      if (cc < PL && e < E && !((taken >> cc) & 1u) && (v[cc] > bv || (v[cc] == bv && e < bi))) {
-        bv = v[cc];
-        bi = e;
-      }
-    }
-    argmax16(bv, bi);
-    const int own = bi - ebase;
-    if (own >= 0 && own < PL) taken |= 1u << own;
+    for (int cc = 1; cc < kPerLane16; ++cc) best = key[cc] > best ? key[cc] : best;
+    best = max16_u64(best);
+#pragma unroll
+    for (int cc = 0; cc < kPerLane16; ++cc) key[cc] = key[cc] == best ? 0ull : key[cc];
+    const int bi = key_expert(best);
+    const float bv = key_logit(best);
     if (j == 0) top = bv;
     if (sub == j) {
       my_e = bi;
