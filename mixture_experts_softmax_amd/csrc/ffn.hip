@@ -489,95 +489,114 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void down_fp8_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Down GEMM for short tiles (BM x KT x 128 bytes of h fit in 32 KiB of LDS:
-// the decode shapes). The tile's whole h slab and its block scales are
-// loaded into LDS once, so the K loop has no barrier and no activation
-// traffic: each wave only streams its weight rows through a PD-deep register
-// ring, with exact wait counts (K fully unrolled). Same tile and wave layout
-// as down_fp8_kernel with WM = 1.
+// Down GEMM with the tile's h slab resident in LDS (BM x KT x 128 bytes, at
+// most 64 KiB: BM <= 64 at F = 1024). The slab and its block scales are
+// loaded once; then the workgroup streams the weights of NTW consecutive N
+// tiles (256 output channels each) through one continuous K loop of NTW x KT
+// steps: each wave keeps PD steps of its weight rows in flight in registers,
+// across N-tile boundaries, so the pipeline fills once per workgroup, and
+// the K loop has no barrier. With NW waves, wave w owns channels
+// [w 256/NW, (w + 1) 256/NW) of every N tile, over all BM rows.
 // ---------------------------------------------------------------------------
-template <int BM, int KTC>
-__global__ __launch_bounds__(kNWaves * kWave) void down_fp8_resident_kernel(
+template <int BM, int KTC, int NTW, int NW>
+__global__ __launch_bounds__(NW * kWave) void down_fp8_resident_kernel(
     FfnCall c, const TileHeader* __restrict__ hdr, const TileEntry* __restrict__ list) {
-  constexpr int NTH = kNWaves * kWave;
+  constexpr int NTH = NW * kWave;
   constexpr int MS = BM / 16;
-  constexpr int NB = 4;
+  constexpr int NB = kDownBN / 16 / NW;  // 16-channel subtiles per wave
   constexpr int CHK = BM * (kBK / 16);  // 16-byte chunks per K step
   constexpr int CPT = (CHK * KTC + NTH - 1) / NTH;
-  constexpr int PD = KTC < 4 ? KTC : 4;
-  static_assert(BM * KTC * kBK <= 32768, "h slab exceeds the LDS budget");
+  constexpr int GRP = 8;                 // slab chunks per thread per load group
+  constexpr int NSTEP = NTW * KTC;
+  constexpr int PD = NSTEP < 4 ? NSTEP : 4;
+  constexpr int HPT = (BM * KTC + NTH - 1) / NTH;
+  static_assert(BM * KTC * kBK <= 65536, "h slab exceeds the LDS budget");
 
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[KTC][BM * kBK];
   __shared__ float hsl[KTC][BM];
 
+  const int d = c.d, dnt = down_ntiles(d);
   Tile te;
-  if (!pick_tile<BM>(list, hdr->n_down, down_ntiles(c.d), te)) return;
-  const int ntile = te.ntile;
+  if (!pick_tile<BM>(list, hdr->n_down, ceil_div(dnt, NTW), te)) return;
+  const int nt0 = te.ntile * NTW;
   const int sid = te.gid >> 16, g = te.gid & 0xffff;
   const SetView S = set_view(c, sid);
-  const int d = c.d, F = S.F;
+  const int F = S.F;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wn = tid / kWave;
 
-  const uint8_t* w2 = S.w2 + (size_t)g * d * F;
-  const uint8_t* b_src[NB];
-  int mcol[NB];
+  const uint8_t* w2 = S.w2 + (size_t)g * d * F + (lane >> 4) * 16;
+  // output channel of (N tile n of this workgroup, subtile j) for this lane
+  auto mcol = [&](int n, int j) {
+    return (nt0 + n) * kDownBN + wn * (NB * 16) + j * 16 + (lane & 15);
+  };
+  // weight fragment address of step s (N tile s / KT, K step s % KT); steps
+  // past the last N tile re-read its rows (never used)
+  auto bsrc = [&](int st, int j) {
+    const int n = min(st / KTC, dnt - 1 - nt0);
+    return w2 + (size_t)min(mcol(n, j), d - 1) * F + (st % KTC) * kBK;
+  };
+  // channel scales of every N tile, loaded now so the epilogues wait on no load
+  float s2v[NTW][NB];
 #pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    mcol[j] = ntile * kDownBN + wn * (NB * 16) + j * 16 + (lane & 15);
-    b_src[j] = w2 + (size_t)min(mcol[j], d - 1) * F + (lane >> 4) * 16;
-  }
-  // channel scales, loaded now so that the epilogue waits on no load
-  float s2v[NB];
+  for (int n = 0; n < NTW; ++n)
 #pragma unroll
-  for (int j = 0; j < NB; ++j) s2v[j] = S.s2[(size_t)g * d + min(mcol[j], d - 1)];
-  // the h slab: chunk ch = (step, row, 16-byte column); rows past the tile's
-  // end repeat its last row (never stored)
-  v4i st[CPT];
-  int dst[CPT];
+    for (int j = 0; j < NB; ++j) s2v[n][j] = S.s2[(size_t)g * d + min(mcol(n, j), d - 1)];
+  float hv[HPT];
 #pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const int ch = min(tid + i * NTH, CHK * KTC - 1);
-    const int kt = ch / CHK, cc = ch % CHK;
-    const int r = cc >> 3, c16 = cc & 7;
-    const size_t grow = (size_t)(te.row0 + min(r, te.nrows - 1));
-    st[i] = *reinterpret_cast<const v4i*>(S.h + grow * F + kt * kBK + c16 * 16);
-    dst[i] = kt * (BM * kBK) + swz(r, c16);
-  }
-  float hv[(BM * KTC + NTH - 1) / NTH];
-#pragma unroll
-  for (int i = 0; i < (BM * KTC + NTH - 1) / NTH; ++i) {
+  for (int i = 0; i < HPT; ++i) {
     const int e = min(tid + i * NTH, BM * KTC - 1);
     const int r = e / KTC, kt = e % KTC;
     hv[i] = S.h_scale[(size_t)(te.row0 + min(r, te.nrows - 1)) * KTC + kt];
   }
-  // weight ring, issued after the slab so that storing the slab to LDS waits
-  // for the slab alone
+  // The h slab in groups of GRP chunks per thread (chunk ch = (step, row,
+  // 16-byte column); rows past the tile's end repeat its last row and are
+  // never stored). The weight ring is issued after the first group, so the
+  // first group's stores wait for that group alone.
   v8i bq[PD][NB];
 #pragma unroll
-  for (int s = 0; s < PD; ++s)
+  for (int g0 = 0; g0 < CPT; g0 += GRP) {
+    v4i st[GRP];
+    int dst[GRP];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) bq[s][j] = glb_bfrag(b_src[j] + s * kBK);
-
+    for (int i = 0; i < GRP; ++i) {
+      if (g0 + i < CPT) {
+        const int ch = min(tid + (g0 + i) * NTH, CHK * KTC - 1);
+        const int kt = ch / CHK, cc = ch % CHK;
+        const int r = cc >> 3, c16 = cc & 7;
+        const size_t grow = (size_t)(te.row0 + min(r, te.nrows - 1));
+        st[i] = *reinterpret_cast<const v4i*>(S.h + grow * F + kt * kBK + c16 * 16);
+        dst[i] = kt * (BM * kBK) + swz(r, c16);
+      }
+    }
+    if (g0 == 0) {
 #pragma unroll
-  for (int i = 0; i < CPT; ++i)
-    if ((CHK * KTC) % NTH == 0 || tid + i * NTH < CHK * KTC)
-      *reinterpret_cast<v4i*>(&lds_a[0][0] + dst[i]) = st[i];
+      for (int s = 0; s < PD; ++s)
 #pragma unroll
-  for (int i = 0; i < (BM * KTC + NTH - 1) / NTH; ++i) {
+        for (int j = 0; j < NB; ++j) bq[s][j] = glb_bfrag(bsrc(s, j));
+    }
+#pragma unroll
+    for (int i = 0; i < GRP; ++i)
+      if (g0 + i < CPT && ((CHK * KTC) % NTH == 0 || tid + (g0 + i) * NTH < CHK * KTC))
+        *reinterpret_cast<v4i*>(&lds_a[0][0] + dst[i]) = st[i];
+  }
+#pragma unroll
+  for (int i = 0; i < HPT; ++i) {
     const int e = tid + i * NTH;
     if ((BM * KTC) % NTH == 0 || e < BM * KTC) hsl[e % KTC][e / KTC] = hv[i];
   }
   __syncthreads();
 
+  uint16_t* out = static_cast<uint16_t*>(S.out);
   v4f acc[MS][NB];
+#pragma unroll (NSTEP)
+  for (int st = 0; st < NSTEP; ++st) {
+    const int s = st % PD, kt = st % KTC, n = st / KTC;
+    if (kt == 0) {
 #pragma unroll
-  for (int i = 0; i < MS; ++i)
+      for (int i = 0; i < MS; ++i)
 #pragma unroll
-    for (int j = 0; j < NB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-#pragma unroll
-  for (int kt = 0; kt < KTC; ++kt) {
-    const int s = kt % PD;
+        for (int j = 0; j < NB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
     for (int i = 0; i < MS; ++i) {
       const v8i af = lds_afrag(lds_a[kt], i, lane);
@@ -592,9 +611,9 @@ __global__ __launch_bounds__(kNWaves * kWave) void down_fp8_resident_kernel(
         for (int j = 0; j < NB; ++j) acc[i][j][q] = fmaf(part[j][q], hs, acc[i][j][q]);
       }
     }
-    if (kt + PD < KTC) {
+    if (st + PD < NSTEP) {
 #pragma unroll
-      for (int j = 0; j < NB; ++j) bq[s][j] = glb_bfrag(b_src[j] + (kt + PD) * kBK);
+      for (int j = 0; j < NB; ++j) bq[s][j] = glb_bfrag(bsrc(st + PD, j));
     }
     // keep each step's loads and scaled accumulation in the step (the
     // scheduler would otherwise sink the loads towards their use, shortening
@@ -603,23 +622,23 @@ __global__ __launch_bounds__(kNWaves * kWave) void down_fp8_resident_kernel(
     for (int i = 0; i < MS; ++i)
 #pragma unroll
       for (int j = 0; j < NB; ++j) asm volatile("" : "+v"(acc[i][j]));
-    __builtin_amdgcn_sched_barrier(0);
-  }
-
-  uint16_t* out = static_cast<uint16_t*>(S.out);
+    if (kt == KTC - 1 && nt0 + n < dnt) {  // this N tile is done: channel scale, bf16
 #pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    if (mcol[j] >= d) continue;
-    const float sc = s2v[j];
+      for (int j = 0; j < NB; ++j) {
+        const int m = mcol(n, j);
+        if (m >= d) continue;
 #pragma unroll
-    for (int i = 0; i < MS; ++i) {
+        for (int i = 0; i < MS; ++i) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = i * 16 + 4 * (lane >> 4) + q;
-        if (r < te.nrows)
-          out[(size_t)(te.row0 + r) * d + mcol[j]] = f32_to_bf16(acc[i][j][q] * sc);
+          for (int q = 0; q < 4; ++q) {
+            const int r = i * 16 + 4 * (lane >> 4) + q;
+            if (r < te.nrows)
+              out[(size_t)(te.row0 + r) * d + m] = f32_to_bf16(acc[i][j][q] * s2v[n][j]);
+          }
+        }
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -689,13 +708,17 @@ hipError_t launch_gemms_bm(const FfnCall& c, TileHeader* hdr, TileEntry* up, Til
                        dim3(kNWaves * WU * kWave), 0, s, c, hdr, up);
   ev.mark(false, MOE_STEP_GATE_UP, s);
   ev.mark(true, MOE_STEP_DOWN, s);
-  if (cd > 0) {
-    if constexpr (KTD > 0 && BMD * KTD * kBK <= 32768)
-      hipLaunchKernelGGL((down_fp8_resident_kernel<BMD, KTD>), dim3((unsigned)cd),
-                         dim3(kNWaves * kWave), 0, s, c, hdr, dn);
-    else
+  if (cap_d > 0) {
+    if constexpr (KTD > 0 && BMD * KTD * kBK <= 65536) {
+      // resident h slab; 64-row tiles: 8 waves, 4 N tiles per workgroup
+      constexpr int NTW = BMD >= 64 ? 4 : 1, NWD = BMD >= 64 ? 8 : 4;
+      const size_t cdr = align_up(cap_d * ceil_div(down_ntiles(c.d), NTW), kXcds);
+      hipLaunchKernelGGL((down_fp8_resident_kernel<BMD, KTD, NTW, NWD>), dim3((unsigned)cdr),
+                         dim3(NWD * kWave), 0, s, c, hdr, dn);
+    } else {
       hipLaunchKernelGGL((down_fp8_kernel<BMD, WD, KTD>), dim3((unsigned)cd),
                          dim3(kNWaves * WD * kWave), 0, s, c, hdr, dn);
+    }
   }
   ev.mark(false, MOE_STEP_DOWN, s);
   return hipGetLastError();
@@ -709,7 +732,7 @@ hipError_t launch_gemms_k(const FfnCall& c, TileHeader* hdr, TileEntry* up, Tile
                           size_t cap_u, size_t cap_d, hipStream_t s, const StepEvents& ev) {
   const bool ku = c.d / kBK == 32;
   const bool kd = c.set[0].F / kBK == 8 && (c.nsets < 2 || c.set[1].F / kBK == 8);
-  constexpr int KD = BMD <= 32 ? 8 : 0;  // larger tiles: the looped kernel
+  constexpr int KD = BMD <= 64 ? 8 : 0;  // larger tiles: the looped kernel
   if (ku && kd) return launch_gemms_bm<BM, 32, BMD, KD>(c, hdr, up, dn, cap_u, cap_d, s, ev);
   if (ku) return launch_gemms_bm<BM, 32, BMD, 0>(c, hdr, up, dn, cap_u, cap_d, s, ev);
   if (kd) return launch_gemms_bm<BM, 0, BMD, KD>(c, hdr, up, dn, cap_u, cap_d, s, ev);
@@ -747,20 +770,20 @@ int choose_bm(int rows_hint) {
   return best;
 }
 
-void tile_lists(const FfnCall& c, int bm_up, int bm_dn, void* ws, TileHeader** hdr,
-                TileEntry** up, TileEntry** dn, int* cap_up, int* cap_dn) {
+void tile_lists(const FfnCall& c, int bm, void* ws, TileHeader** hdr, TileEntry** up,
+                TileEntry** dn, int* cap_up, int* cap_dn) {
   *hdr = static_cast<TileHeader*>(ws);
   *up = reinterpret_cast<TileEntry*>(*hdr + 1);
   *dn = *up + tiles_cap(c, 16);
-  *cap_up = (int)tiles_cap(c, bm_up);
-  *cap_dn = (int)tiles_cap(c, bm_dn);
+  *cap_up = (int)tiles_cap(c, bm);
+  *cap_dn = (int)tiles_cap(c, down_bm(c, bm));
 }
 
 hipError_t launch_ffn_tiles(const FfnCall& c, int bm, void* ws, hipStream_t s) {
   TileHeader* hdr;
   TileEntry *up, *dn;
   int cu, cd;
-  tile_lists(c, bm, down_bm(bm), ws, &hdr, &up, &dn, &cu, &cd);
+  tile_lists(c, bm, ws, &hdr, &up, &dn, &cu, &cd);
   hipLaunchKernelGGL(ffn_tiles_kernel, dim3(1), dim3(kTileThreads), 0, s, c, bm, hdr, up, dn, cu, cd);
   return hipGetLastError();
 }
@@ -770,13 +793,18 @@ hipError_t launch_ffn_gemms(const FfnCall& c, int bm, void* ws, hipStream_t s,
   TileHeader* hdr;
   TileEntry *up, *dn;
   int cu, cd;
-  tile_lists(c, bm, down_bm(bm), ws, &hdr, &up, &dn, &cu, &cd);
+  tile_lists(c, bm, ws, &hdr, &up, &dn, &cu, &cd);
+  const bool d64 = down_bm(c, bm) == 64;
   switch (bm) {
     case 16: return launch_gemms_k<16, 16>(c, hdr, up, dn, cu, cd, s, ev);
     case 32: return launch_gemms_k<32, 32>(c, hdr, up, dn, cu, cd, s, ev);
     case 64: return launch_gemms_k<64, 64>(c, hdr, up, dn, cu, cd, s, ev);
-    case 128: return launch_gemms_k<128, 128>(c, hdr, up, dn, cu, cd, s, ev);
-    default: return launch_gemms_k<192, 128>(c, hdr, up, dn, cu, cd, s, ev);
+    case 128:
+      return d64 ? launch_gemms_k<128, 64>(c, hdr, up, dn, cu, cd, s, ev)
+                 : launch_gemms_k<128, 128>(c, hdr, up, dn, cu, cd, s, ev);
+    default:
+      return d64 ? launch_gemms_k<192, 64>(c, hdr, up, dn, cu, cd, s, ev)
+                 : launch_gemms_k<192, 128>(c, hdr, up, dn, cu, cd, s, ev);
   }
 }
 

@@ -158,7 +158,7 @@ hipError_t launch_perm_scan_scatter(const int32_t* ids, int T, int E, int k, uin
   FfnCall cc{};
   if (c != nullptr && tiles_ws != nullptr) {
     cc = *c;
-    tile_lists(cc, bm, down_bm(bm), tiles_ws, &hdr, &up, &dn, &cap_up, &cap_dn);
+    tile_lists(cc, bm, tiles_ws, &hdr, &up, &dn, &cap_up, &cap_dn);
   }
   hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, counts, ntiles, E,
                      offsets, cc, bm, hdr, up, dn, cap_up, cap_dn);

@@ -522,8 +522,7 @@ hipError_t launch_route(bool bf16, const void* x, const void* w_router, const fl
     if (fuse->c != nullptr && fuse->tiles_ws != nullptr) {
       c = *fuse->c;
       po.bm = fuse->bm;
-      tile_lists(c, po.bm, down_bm(po.bm), fuse->tiles_ws, &po.hdr, &po.up, &po.dn, &po.cap_up,
-                 &po.cap_dn);
+      tile_lists(c, po.bm, fuse->tiles_ws, &po.hdr, &po.up, &po.dn, &po.cap_up, &po.cap_dn);
     }
   }
   const bool fused = po.offsets != nullptr;

@@ -1,6 +1,6 @@
 // Grouped-FFN work lists: for every non-empty group, one entry per M tile (up
 // to BM rows each), one list for the gate/up GEMM (tile height bm) and one
-// for the down GEMM (down_bm(bm)). A GEMM launch covers (list entry, N tile)
+// for the down GEMM (down_bm(c, bm)). A GEMM launch covers (list entry, N tile)
 // pairs; the block index selects the pair. Emitted by one workgroup; used by
 // the tile-list kernel of moe_grouped_ffn and by the permutation of
 // moe_layer_forward (which knows the group sizes first).
@@ -51,13 +51,20 @@ struct TileLds {
 };
 
 // Host: where the lists of call c live in its tile workspace, and their
-// capacities for tile height bm.
-void tile_lists(const FfnCall& c, int bm_up, int bm_dn, void* ws, TileHeader** hdr,
-                TileEntry** up, TileEntry** dn, int* cap_up, int* cap_dn);
+// capacities for gate/up tile height bm (down: down_bm(c, bm)).
+void tile_lists(const FfnCall& c, int bm, void* ws, TileHeader** hdr, TileEntry** up,
+                TileEntry** dn, int* cap_up, int* cap_dn);
 
-// Tile height of the down GEMM for a gate/up tile height (its register tile
-// holds no more than 128 rows).
-__host__ __device__ inline int down_bm(int bm_up) { return bm_up < 128 ? bm_up : 128; }
+// Tile height of the down GEMM for a gate/up tile height: the same up to 32
+// rows; above, 64 rows when every set has F = 1024 (the h slab of a 64-row
+// tile then fits 64 KiB of LDS and stays resident), else at most 128 (the
+// looped kernel's register tile).
+__host__ __device__ inline int down_bm(const FfnCall& c, int bm_up) {
+  if (bm_up <= 32) return bm_up;
+  const bool f1024 = c.set[0].F == 1024 && (c.nsets < 2 || c.set[1].F == 1024);
+  if (f1024) return 64;
+  return bm_up < 128 ? bm_up : 128;
+}
 
 // All threads of the block (at most 1024) call this after the group arrays are
 // filled and synchronised. cap_up / cap_dn bound the lists (entries beyond are
@@ -69,7 +76,7 @@ __host__ __device__ inline int down_bm(int bm_up) { return bm_up < 128 ? bm_up :
 __device__ inline void emit_tiles(const FfnCall& c, int bm, int NG, int G0, TileLds& L,
                                   TileHeader* hdr, TileEntry* up, TileEntry* down, int cap_up,
                                   int cap_dn) {
-  const int bmd = down_bm(bm);
+  const int bmd = down_bm(c, bm);
   const int tid = threadIdx.x, nth = blockDim.x;
   const int lane = tid & (kWave - 1), wave = tid / kWave, nwaves = nth / kWave;
   int carry_u = 0, carry_d = 0;  // identical in every thread
