@@ -163,6 +163,61 @@ constexpr int prefetch_depth() { return ROWS <= LIMIT ? 3 : 2; }
 // second time from the L2.
 constexpr int kNWaves = 4;
 
+// Gate/up epilogue, shared by the gate/up kernels: x and weight scales,
+// SwiGLU, per-(row, 128-column) amax across the kNWaves N waves (through LDS
+// `red`), then FP8 h codes and their block scale. acc[i][jj] holds gate
+// columns, acc[i][NS + jj] the matching up columns; the wave owns rows
+// [rbase, rbase + 16 MS) and h columns [32 wn, 32 wn + 32) of the tile.
+template <int BM, int MS, int NS>
+__device__ inline void gateup_epilogue(v4f (&acc)[MS][2 * NS], const float* sxl,
+                                       float (&red)[kNWaves][BM], const float* sg,
+                                       const float* su, int rbase, int wn, int lane,
+                                       const Tile& te, const SetView& S, int ntile) {
+  constexpr int WN = NS * 16;
+  const int F = S.F;
+#pragma unroll
+  for (int i = 0; i < MS; ++i) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = rbase + i * 16 + 4 * (lane >> 4) + q;
+      const float sx = sxl[r];
+      float m = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < NS; ++jj) {
+        const float gv = acc[i][jj][q] * sx * sg[jj];
+        const float uv = acc[i][NS + jj][q] * sx * su[jj];
+        const float h = gv / (1.0f + __expf(-gv)) * uv;
+        acc[i][jj][q] = h;
+        m = fmaxf(m, fabsf(h));
+      }
+      m = max16(m);
+      if ((lane & 15) == 0) red[wn][r] = m;
+    }
+  }
+  __syncthreads();
+  const int hblocks = F / kHN;
+#pragma unroll
+  for (int i = 0; i < MS; ++i) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = rbase + i * 16 + 4 * (lane >> 4) + q;
+      if (r >= te.nrows) continue;
+      float am = red[0][r];
+#pragma unroll
+      for (int ww = 1; ww < kNWaves; ++ww) am = fmaxf(am, red[ww][r]);
+      const float s = (am > 0.f) ? __fdiv_rn(am, kE4M3Max) : 1.0f;
+      const size_t grow = (size_t)(te.row0 + r);
+      uint8_t* hrow = S.h + grow * F;
+#pragma unroll
+      for (int jj = 0; jj < NS; ++jj) {
+        const int hc = ntile * kHN + wn * WN + jj * 16 + (lane & 15);
+        hrow[hc] = e4m3_encode(__fdiv_rn(acc[i][jj][q], s));
+      }
+      if (wn == 0 && (lane & 15) == 0) S.h_scale[grow * hblocks + ntile] = s;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Gate/up GEMM + SwiGLU + h quantisation. Tile: BM rows x 128 h columns
 // (128 gate + 128 up weight rows); wave (wm, wn) owns h columns
@@ -301,48 +356,152 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void gateup_fp8_kernel(
     }
   }
 
-  // ---- epilogue: scales, SwiGLU, per-(row, 128-col) amax ----
+  gateup_epilogue<BM, MS, NS>(acc, sxl, red, sg, su, rbase, wn, lane, te, S, ntile);
+}
+
+// ---------------------------------------------------------------------------
+// Gate/up GEMM for tall tiles (prefill): both operands staged through LDS by
+// direct global->LDS loads, so each weight byte is fetched once per
+// workgroup (the two M halves share it) and no register is spent staging.
+// Tile BM x 128 h columns (256 weight rows), 8 waves, wave (wm, wn) owns rows
+// [wm BM/2, (wm + 1) BM/2) and h columns [32 wn, 32 wn + 32). Weights go
+// through a 3-stage LDS ring (loads for step kt+2 are issued at step kt),
+// activation rows through 2 stages. Every stage is its own LDS array and the
+// K loop is fully unrolled, so each wait names the exact number of loads
+// that may stay in flight.
+//
+// A direct load writes lane l's 16 bytes at the instruction's LDS base + 16 l
+// (one wave: 1 KiB, 8 rows of 128 bytes); the swizzle is applied by choosing
+// which global chunk each lane fetches.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ inline void dma16(const uint8_t* src, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (lds_void_t*)lds_base, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) alone (expcnt and lgkmcnt left at their "no wait"
+// maxima; gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt out of range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <int BM, int KTC>
+__global__ __launch_bounds__(8 * kWave) void gateup_fp8_lds_kernel(
+    FfnCall c, const TileHeader* __restrict__ hdr, const TileEntry* __restrict__ list) {
+  constexpr int NW = 8, NTH = NW * kWave;
+  constexpr int BMW = BM / 2, MS = BMW / 16;
+  constexpr int NS = 2, NB = 2 * NS;
+  constexpr int BROWS = 2 * kHN;                     // weight rows per tile
+  constexpr int NAD = BM * kBK / 1024 / NW;          // A loads per thread per step
+  constexpr int NBD = BROWS * kBK / 1024 / NW;       // B loads per thread per step
+  static_assert(BM * kBK % (1024 * NW) == 0, "A tile must split into whole wave loads");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t a0[BM * kBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t a1[BM * kBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t b0[BROWS * kBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t b1[BROWS * kBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t b2[BROWS * kBK];
+  __shared__ float sxl[BM];
+  __shared__ float red[kNWaves][BM];
+
+  Tile te;
+  if (!pick_tile<BM>(list, hdr->n_up, up_ntiles_max(c), te)) return;
+  const int ntile = te.ntile;
+  const int sid = te.gid >> 16, g = te.gid & 0xffff;
+  const SetView S = set_view(c, sid);
+  const int d = c.d, F = S.F;
+  if (ntile >= F / kHN) return;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int wm = wave / kNWaves, wn = wave % kNWaves;
+  const int rbase = wm * BMW;
+  const uint8_t* a = static_cast<const uint8_t*>(c.a);
+
+  // this thread's direct-load sources: A load i covers tile rows
+  // 8 (NAD wave + i) + lane / 8, B load i weight-tile rows 8 (NBD wave + i) + lane / 8
+  const uint8_t* asrc[NAD];
 #pragma unroll
-  for (int i = 0; i < MS; ++i) {
+  for (int i = 0; i < NAD; ++i) {
+    const int r = 8 * (NAD * wave + i) + (lane >> 3);
+    const int cch = (lane & 7) ^ (r & 7);
+    const int grow = te.row0 + min(r, te.nrows - 1);
+    const int src = min(max(S.row_src ? S.row_src[grow] / S.src_div : grow, 0), c.a_rows - 1);
+    asrc[i] = a + (size_t)src * d + cch * 16;
+  }
+  const uint8_t* w13 = S.w13 + (size_t)g * 2 * F * d;
+  const uint8_t* bsrc[NBD];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = rbase + i * 16 + 4 * (lane >> 4) + q;
-      const float sx = sxl[r];
-      float m = 0.f;
+  for (int i = 0; i < NBD; ++i) {
+    const int rr = 8 * (NBD * wave + i) + (lane >> 3);
+    const int cch = (lane & 7) ^ (rr & 7);
+    const int wrow = (rr < kHN) ? ntile * kHN + rr : F + ntile * kHN + (rr - kHN);
+    bsrc[i] = w13 + (size_t)wrow * d + cch * 16;
+  }
+  if (tid < BM) {
+    const int grow = te.row0 + min(tid, te.nrows - 1);
+    const int src = min(max(S.row_src ? S.row_src[grow] / S.src_div : grow, 0), c.a_rows - 1);
+    sxl[tid] = c.a_scale[src];
+  }
+  const float* s13 = S.s13 + (size_t)g * 2 * F;
+  float sg[NS], su[NS];
 #pragma unroll
-      for (int jj = 0; jj < NS; ++jj) {
-        const float gv = acc[i][jj][q] * sx * sg[jj];
-        const float uv = acc[i][NS + jj][q] * sx * su[jj];
-        const float h = gv / (1.0f + __expf(-gv)) * uv;
-        acc[i][jj][q] = h;
-        m = fmaxf(m, fabsf(h));
-      }
-      m = max16(m);
-      if ((lane & 15) == 0) red[wn][r] = m;
+  for (int jj = 0; jj < NS; ++jj) {
+    const int hc = ntile * kHN + wn * 32 + jj * 16 + (lane & 15);
+    sg[jj] = s13[hc];
+    su[jj] = s13[F + hc];
+  }
+
+  auto load_a = [&](int kt, uint8_t* dst) {
+#pragma unroll
+    for (int i = 0; i < NAD; ++i) dma16(asrc[i] + kt * kBK, dst + (NAD * wave + i) * 1024);
+  };
+  auto load_b = [&](int kt, uint8_t* dst) {
+#pragma unroll
+    for (int i = 0; i < NBD; ++i) dma16(bsrc[i] + kt * kBK, dst + (NBD * wave + i) * 1024);
+  };
+
+  v4f acc[MS][NB];
+#pragma unroll
+  for (int i = 0; i < MS; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // prologue: B(0), A(0), B(1)
+  load_b(0, b0);
+  load_a(0, a0);
+  if (KTC > 1) load_b(1, b1);
+
+#pragma unroll
+  for (int kt = 0; kt < KTC; ++kt) {
+    // A(kt) and B(kt) landed: only B(kt+1) (issued after A(kt)) may still fly
+    if (kt + 1 < KTC)
+      wait_vmcnt<NBD>();
+    else
+      wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    uint8_t* as = (kt % 2 == 0) ? a0 : a1;
+    uint8_t* bs = (kt % 3 == 0) ? b0 : (kt % 3 == 1) ? b1 : b2;
+    // refill the stages read at step kt-1 (every wave is past it)
+    if (kt + 1 < KTC) load_a(kt + 1, (kt % 2 == 0) ? a1 : a0);
+    if (kt + 2 < KTC) load_b(kt + 2, (kt % 3 == 0) ? b2 : (kt % 3 == 1) ? b0 : b1);
+    v8i bf[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int row0 = (j < NS) ? wn * 32 + j * 16 : kHN + wn * 32 + (j - NS) * 16;
+      bf[j] = lds_afrag(bs + row0 * kBK, 0, lane);
     }
+#pragma unroll
+    for (int i = 0; i < MS; ++i) {
+      const v8i af = lds_afrag(as + rbase * kBK, i, lane);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) acc[i][j] = mfma_fp8_16x16x128(af, bf[j], acc[i][j]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
   __syncthreads();
-  const int hblocks = F / kHN;
-#pragma unroll
-  for (int i = 0; i < MS; ++i) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = rbase + i * 16 + 4 * (lane >> 4) + q;
-      if (r >= te.nrows) continue;
-      float am = red[0][r];
-#pragma unroll
-      for (int ww = 1; ww < kNWaves; ++ww) am = fmaxf(am, red[ww][r]);
-      const float s = (am > 0.f) ? __fdiv_rn(am, kE4M3Max) : 1.0f;
-      const size_t grow = (size_t)(te.row0 + r);
-      uint8_t* hrow = S.h + grow * F;
-#pragma unroll
-      for (int jj = 0; jj < NS; ++jj) {
-        const int hc = ntile * kHN + wn * WN + jj * 16 + (lane & 15);
-        hrow[hc] = e4m3_encode(__fdiv_rn(acc[i][jj][q], s));
-      }
-      if (wn == 0 && (lane & 15) == 0) S.h_scale[grow * hblocks + ntile] = s;
-    }
-  }
+  gateup_epilogue<BM, MS, NS>(acc, sxl, red, sg, su, rbase, wn, lane, te, S, ntile);
 }
 
 // ---------------------------------------------------------------------------
@@ -703,9 +862,14 @@ hipError_t launch_gemms_bm(const FfnCall& c, TileHeader* hdr, TileEntry* up, Til
   const size_t cd = align_up(cap_d * down_ntiles(c.d), kXcds);
   constexpr int WU = waves_m<BM>(), WD = waves_m<BMD>();
   ev.mark(true, MOE_STEP_GATE_UP, s);
-  if (cu > 0)
-    hipLaunchKernelGGL((gateup_fp8_kernel<BM, WU, KTU>), dim3((unsigned)cu),
-                       dim3(kNWaves * WU * kWave), 0, s, c, hdr, up);
+  if (cu > 0) {
+    if constexpr (KTU > 0 && BM >= 128)  // tall tiles: both operands through LDS
+      hipLaunchKernelGGL((gateup_fp8_lds_kernel<BM, KTU>), dim3((unsigned)cu), dim3(8 * kWave),
+                         0, s, c, hdr, up);
+    else
+      hipLaunchKernelGGL((gateup_fp8_kernel<BM, WU, KTU>), dim3((unsigned)cu),
+                         dim3(kNWaves * WU * kWave), 0, s, c, hdr, up);
+  }
   ev.mark(false, MOE_STEP_GATE_UP, s);
   ev.mark(true, MOE_STEP_DOWN, s);
   if (cap_d > 0) {
