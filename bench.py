@@ -170,11 +170,116 @@ def time_layer(cfg, steps, warmup, hip):
             if e is not None:
                 hip.destroy(e)
 
+    # per-call distribution: one event pair around each whole call
+    reps = max(20, min(steps, 50))
+    ca = [hip.event() for _ in range(reps)]
+    cb = [hip.event() for _ in range(reps)]
+    for i in range(reps):
+        st, sp = list(none), list(none)
+        st[0], sp[nsteps - 1] = ca[i], cb[i]
+        _lib.moe_layer_forward_events(s, W, x, y, ids, gw, ws, st, sp)
+    torch.cuda.synchronize()
     import numpy as np
+    per_call = np.array([hip.ms(a, b) * 1e3 for a, b in zip(ca, cb)])
+    for e in ca + cb:
+        hip.destroy(e)
+    pct = {"p10": round(float(np.percentile(per_call, 10)), 2),
+           "p50": round(float(np.percentile(per_call, 50)), 2),
+           "p90": round(float(np.percentile(per_call, 90)), 2), "calls": reps}
+
     counts = np.bincount(ids.cpu().numpy().reshape(-1), minlength=cfg.E)
     acc = accounting(cfg, counts)
     del L, ws, W, x, y
-    return dict(ms_step=ms_step, up_ms=up_ms, breakdown_us=breakdown, acc=acc, counts=counts, lt=lt)
+    return dict(ms_step=ms_step, up_ms=up_ms, breakdown_us=breakdown, acc=acc, counts=counts, lt=lt,
+                call_us=pct)
+
+
+def time_chunked(cfg, chunk, steps, warmup, hip):
+    """The workload's tokens as consecutive calls of `chunk` tokens (one step =
+    all chunks, in order); returns ms per step and per-chunk accounting."""
+    import numpy as np
+    import torch
+
+    import mixture_experts_softmax_amd as M
+    from mixture_experts_softmax_amd import _lib
+    from synthetic import make_layer
+
+    lt = make_layer(cfg, device="cuda")
+    L = M.MoELayer(d=cfg.d, E=cfg.E, k=cfg.k, F=cfg.F, F_shared=cfg.F_shared,
+                   precision=cfg.precision, w_router=lt.w_router, router_bias=lt.router_bias,
+                   w13=lt.w13, w13_scale=lt.w13_scale, w2=lt.w2, w2_scale=lt.w2_scale, ws13=lt.ws13,
+                   ws13_scale=lt.ws13_scale, ws2=lt.ws2, ws2_scale=lt.ws2_scale)
+    n = cfg.T // chunk
+    s = L.shape(chunk)
+    ws = L.workspace(chunk, "cuda")
+    W = _lib.make_weights(s, **L.tensors)
+    x = lt.x
+    y = torch.empty_like(x)
+    ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
+    gw = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device="cuda")
+
+    def step():
+        for c in range(n):
+            sl = slice(c * chunk, (c + 1) * chunk)
+            _lib.moe_layer_forward(s, W, x[sl], y[sl], ids[sl], gw[sl], ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    a, b = hip.event(), hip.event()
+    hip.L.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
+    stream = torch.cuda.current_stream().cuda_stream
+    hip.L.hipEventRecord(C.c_void_p(a), C.c_void_p(stream))
+    for _ in range(steps):
+        step()
+    hip.L.hipEventRecord(C.c_void_p(b), C.c_void_p(stream))
+    ms = hip.ms(a, b) / steps
+    hip.destroy(a)
+    hip.destroy(b)
+    idn = ids.cpu().numpy()
+    bytes_sum = flops_sum = 0.0
+    for c in range(n):
+        counts = np.bincount(idn[c * chunk:(c + 1) * chunk].reshape(-1), minlength=cfg.E)
+        ac = accounting(cfg.with_(T=chunk), counts)
+        bytes_sum += ac["layer_bytes"]
+        flops_sum += ac["layer_flops"]
+    del L, ws, W, x, y, lt
+    return dict(ms=ms, chunks=n, bytes=bytes_sum, flops=flops_sum)
+
+
+def hbm_copy_probe():
+    """Device-to-device copy of 1 GiB (torch's copy kernel), read + write bytes
+    per second: a streaming figure measured on this GPU beside the kernels'."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(5):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    gbs = 5 * 2 * n / (a.elapsed_time(b) / 1e3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return round(gbs, 1)
+
+
+def summarize(cfg, r):
+    a = r["acc"]
+    t = r["ms_step"] / 1e3
+    return {"workload": f"{cfg.name}: T={cfg.T} k={cfg.k} F={cfg.F}", "value": round(cfg.T / t, 1),
+            "unit": "tokens/s", "ms_per_step": round(r["ms_step"], 4),
+            "hbm_frac": round(a["layer_bytes"] / t / 1e9 / HBM_PEAK_GBS, 4),
+            "fp8_mfma_frac": round(a["layer_flops"] / t / 1e12 / FP8_PEAK_TFLOPS, 4),
+            "touched_experts": a["touched"], "call_us": r["call_us"],
+            "gate_up_us": round(r["up_ms"] * 1e3, 2),
+            "gate_up_GBs": round(a["up_bytes"] / (r["up_ms"] / 1e3) / 1e9, 1),
+            "gate_up_TFLOPs": round(a["up_flops"] / (r["up_ms"] / 1e3) / 1e12, 1),
+            "step_breakdown_us": r["breakdown_us"]}
 
 
 def cpu_baseline(cfg, lt, n_tokens):
@@ -212,7 +317,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "b100", "skew"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the other workloads (prefill, 100B-shaped, skewed, chunked prefill) "
+                         "and the copy probe")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 1 GiB device-to-device copy (counter calibration) and exit")
     ap.add_argument("--cpu-tokens", type=int, default=0,
@@ -240,6 +347,8 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n, "copies": 3}), flush=True)
         return
+    import numpy as np
+
     from synthetic import CONFIGS
     hip = Hip()
     cfg = CONFIGS[args.workload]
@@ -275,22 +384,36 @@ def main():
                   "fp8_mfma_frac": round(acc["layer_flops"] / (r["ms_step"] / 1e3) / 1e12 / FP8_PEAK_TFLOPS, 4),
                   "touched_experts": acc["touched"], "step_breakdown_us": r["breakdown_us"]},
     }
-    if not args.no_secondary and args.workload != "prefill":
+    out["layer"]["call_us"] = r["call_us"]
+    if not args.no_secondary:
+        # the other workloads, reported beside the headline (not part of `value`)
+        sec_steps, sec_warm = max(5, args.steps // 2), max(2, args.warmup // 2)
+        for name in ("prefill", "b100", "skew"):
+            if name == args.workload:
+                continue
+            c2 = CONFIGS[name]
+            log(f"[bench] secondary workload {name}")
+            r2 = time_layer(c2, sec_steps, sec_warm, hip)
+            del r2["lt"]
+            out[name] = summarize(c2, r2)
+            if name == "skew":
+                nz = r2["counts"][r2["counts"] > 0]
+                out[name]["group_rows"] = {"empty": int((r2["counts"] == 0).sum()),
+                                           "min": int(nz.min()), "median": int(np.median(nz)),
+                                           "max": int(nz.max())}
+            torch.cuda.empty_cache()
         p = CONFIGS["prefill"]
-        rp = time_layer(p, max(5, args.steps // 2), max(2, args.warmup // 2), hip)
-        del rp["lt"]
+        log("[bench] secondary workload prefill in 256-token chunks")
+        rc = time_chunked(p, 256, sec_steps, sec_warm, hip)
+        t = rc["ms"] / 1e3
+        out["prefill_chunked"] = {
+            "workload": f"prefill: T={p.T} as {rc['chunks']} calls of 256 tokens",
+            "value": round(p.T / t, 1), "unit": "tokens/s", "ms_per_step": round(rc["ms"], 4),
+            "us_per_chunk": round(rc["ms"] * 1e3 / rc["chunks"], 2),
+            "hbm_frac": round(rc["bytes"] / t / 1e9 / HBM_PEAK_GBS, 4),
+            "fp8_mfma_frac": round(rc["flops"] / t / 1e12 / FP8_PEAK_TFLOPS, 4)}
         torch.cuda.empty_cache()
-        ap_ = rp["acc"]
-        t = rp["ms_step"] / 1e3
-        out["prefill"] = {
-            "workload": f"prefill: T={p.T}", "value": round(p.T / t, 1), "unit": "tokens/s",
-            "ms_per_step": round(rp["ms_step"], 4),
-            "hbm_frac": round(ap_["layer_bytes"] / t / 1e9 / HBM_PEAK_GBS, 4),
-            "fp8_mfma_frac": round(ap_["layer_flops"] / t / 1e12 / FP8_PEAK_TFLOPS, 4),
-            "gate_up_us": round(rp["up_ms"] * 1e3, 2),
-            "gate_up_GBs": round(ap_["up_bytes"] / (rp["up_ms"] / 1e3) / 1e9, 1),
-            "gate_up_TFLOPs": round(ap_["up_flops"] / (rp["up_ms"] / 1e3) / 1e12, 1),
-            "step_breakdown_us": rp["breakdown_us"]}
+        out["hbm_copy_probe_GBs"] = hbm_copy_probe()
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
         n = args.cpu_tokens if args.cpu_tokens > 0 else min(cfg.T, 64)
