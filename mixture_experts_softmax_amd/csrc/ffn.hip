@@ -648,6 +648,164 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void down_fp8_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Down GEMM for tall tiles (prefill): the LDS-staged structure of the gate/up
+// kernel above. Tile BM rows x 256 output channels, 8 waves, wave (wm, wn)
+// owns rows [wm BM/2, (wm + 1) BM/2) and channels [64 wn, 64 wn + 64). h rows
+// (2 stages) and W2 rows (3 stages) arrive by direct loads; a workgroup runs
+// NTW consecutive N tiles as one continuous sequence of NTW x KT steps, so
+// each group's weights are fetched once and the ring fills once. The per-row
+// h block scale of each K step multiplies that step's MFMA partial.
+// ---------------------------------------------------------------------------
+template <int BM, int KTC, int NTW>
+__global__ __launch_bounds__(8 * kWave) void down_fp8_lds_kernel(
+    FfnCall c, const TileHeader* __restrict__ hdr, const TileEntry* __restrict__ list) {
+  constexpr int NW = 8, NTH = NW * kWave;
+  constexpr int BMW = BM / 2, MS = BMW / 16;
+  constexpr int NB = 4;
+  constexpr int NAD = BM * kBK / 1024 / NW;           // A loads per thread per step
+  constexpr int NBD = kDownBN * kBK / 1024 / NW;      // B loads per thread per step
+  constexpr int NSTEP = NTW * KTC;
+  constexpr int HPT = (BM * KTC + NTH - 1) / NTH;
+  static_assert(BM * kBK % (1024 * NW) == 0, "A tile must split into whole wave loads");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t a0[BM * kBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t a1[BM * kBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t b0[kDownBN * kBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t b1[kDownBN * kBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t b2[kDownBN * kBK];
+  __shared__ float hsl[KTC][BM];
+
+  const int d = c.d, dnt = down_ntiles(d);
+  Tile te;
+  if (!pick_tile<BM>(list, hdr->n_down, ceil_div(dnt, NTW), te)) return;
+  const int nt0 = te.ntile * NTW;
+  const int sid = te.gid >> 16, g = te.gid & 0xffff;
+  const SetView S = set_view(c, sid);
+  const int F = S.F;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int wm = wave / kNWaves, wn = wave % kNWaves;
+  const int rbase = wm * BMW;
+
+  // direct-load sources: A load i covers tile rows 8 (NAD wave + i) + lane / 8
+  const uint8_t* asrc[NAD];
+#pragma unroll
+  for (int i = 0; i < NAD; ++i) {
+    const int r = 8 * (NAD * wave + i) + (lane >> 3);
+    const int cch = (lane & 7) ^ (r & 7);
+    asrc[i] = S.h + (size_t)(te.row0 + min(r, te.nrows - 1)) * F + cch * 16;
+  }
+  // B load i covers channel rows 8 (NBD wave + i) + lane / 8 of an N tile;
+  // steps past the last N tile re-read its rows (never used)
+  const uint8_t* w2 = S.w2 + (size_t)g * d * F;
+  int brow[NBD], bcc[NBD];
+#pragma unroll
+  for (int i = 0; i < NBD; ++i) {
+    const int rr = 8 * (NBD * wave + i) + (lane >> 3);
+    brow[i] = rr;
+    bcc[i] = ((lane & 7) ^ (rr & 7)) * 16;
+  }
+  auto load_a = [&](int st, uint8_t* dst) {
+    const int kt = st % KTC;
+#pragma unroll
+    for (int i = 0; i < NAD; ++i) dma16(asrc[i] + kt * kBK, dst + (NAD * wave + i) * 1024);
+  };
+  auto load_b = [&](int st, uint8_t* dst) {
+    const int n = min(st / KTC, dnt - 1 - nt0), kt = st % KTC;
+#pragma unroll
+    for (int i = 0; i < NBD; ++i) {
+      const int ch = min((nt0 + n) * kDownBN + brow[i], d - 1);
+      dma16(w2 + (size_t)ch * F + kt * kBK + bcc[i], dst + (NBD * wave + i) * 1024);
+    }
+  };
+  // h block scales of the tile's rows, and every N tile's channel scales
+  float hv[HPT];
+#pragma unroll
+  for (int i = 0; i < HPT; ++i) {
+    const int e = min(tid + i * NTH, BM * KTC - 1);
+    const int r = e / KTC, kt = e % KTC;
+    hv[i] = S.h_scale[(size_t)(te.row0 + min(r, te.nrows - 1)) * KTC + kt];
+  }
+  auto mcol = [&](int n, int j) {
+    return (nt0 + n) * kDownBN + wn * (NB * 16) + j * 16 + (lane & 15);
+  };
+  float s2v[NTW][NB];
+#pragma unroll
+  for (int n = 0; n < NTW; ++n)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) s2v[n][j] = S.s2[(size_t)g * d + min(mcol(n, j), d - 1)];
+#pragma unroll
+  for (int i = 0; i < HPT; ++i) {
+    const int e = tid + i * NTH;
+    if ((BM * KTC) % NTH == 0 || e < BM * KTC) hsl[e % KTC][e / KTC] = hv[i];
+  }
+
+  // prologue: B(0), A(0), B(1)
+  load_b(0, b0);
+  load_a(0, a0);
+  if (NSTEP > 1) load_b(1, b1);
+
+  uint16_t* out = static_cast<uint16_t*>(S.out);
+  v4f acc[MS][NB];
+#pragma unroll (NSTEP)
+  for (int st = 0; st < NSTEP; ++st) {
+    const int kt = st % KTC, n = st / KTC;
+    if (kt == 0) {
+#pragma unroll
+      for (int i = 0; i < MS; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
+    if (st + 1 < NSTEP)
+      wait_vmcnt<NBD>();
+    else
+      wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();  // also publishes hsl on the first step
+    uint8_t* as = (st % 2 == 0) ? a0 : a1;
+    uint8_t* bs = (st % 3 == 0) ? b0 : (st % 3 == 1) ? b1 : b2;
+    if (st + 1 < NSTEP) load_a(st + 1, (st % 2 == 0) ? a1 : a0);
+    if (st + 2 < NSTEP) load_b(st + 2, (st % 3 == 0) ? b2 : (st % 3 == 1) ? b0 : b1);
+    v8i bf[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) bf[j] = lds_afrag(bs + (wn * 64 + j * 16) * kBK, 0, lane);
+#pragma unroll
+    for (int i = 0; i < MS; ++i) {
+      const v8i af = lds_afrag(as + rbase * kBK, i, lane);
+      v4f part[NB];
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        part[j] = mfma_fp8_16x16x128(af, bf[j], v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float hs = hsl[kt][rbase + i * 16 + 4 * (lane >> 4) + q];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j][q] = fmaf(part[j][q], hs, acc[i][j][q]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < MS; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) asm volatile("" : "+v"(acc[i][j]));
+    if (kt == KTC - 1 && nt0 + n < dnt) {  // this N tile is done: channel scale, bf16
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int m = mcol(n, j);
+        if (m >= d) continue;
+#pragma unroll
+        for (int i = 0; i < MS; ++i) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = rbase + i * 16 + 4 * (lane >> 4) + q;
+            if (r < te.nrows)
+              out[(size_t)(te.row0 + r) * d + m] = f32_to_bf16(acc[i][j][q] * s2v[n][j]);
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Down GEMM with the tile's h slab resident in LDS (BM x KT x 128 bytes, at
 // most 64 KiB: BM <= 64 at F = 1024). The slab and its block scales are
 // loaded once; then the workgroup streams the weights of NTW consecutive N
@@ -873,7 +1031,13 @@ hipError_t launch_gemms_bm(const FfnCall& c, TileHeader* hdr, TileEntry* up, Til
   ev.mark(false, MOE_STEP_GATE_UP, s);
   ev.mark(true, MOE_STEP_DOWN, s);
   if (cap_d > 0) {
-    if constexpr (KTD > 0 && BMD * KTD * kBK <= 65536) {
+    if constexpr (KTD > 0 && BMD >= 128) {
+      // tall tiles: both operands through LDS, 16 steps per workgroup
+      constexpr int NTW = KTD >= 16 ? 1 : 16 / KTD;
+      const size_t cdl = align_up(cap_d * ceil_div(down_ntiles(c.d), NTW), kXcds);
+      hipLaunchKernelGGL((down_fp8_lds_kernel<BMD, KTD, NTW>), dim3((unsigned)cdl),
+                         dim3(8 * kWave), 0, s, c, hdr, dn);
+    } else if constexpr (KTD > 0 && BMD * KTD * kBK <= 65536) {
       // resident h slab; 64-row tiles: 8 waves, 4 N tiles per workgroup
       constexpr int NTW = BMD >= 64 ? 4 : 1, NWD = BMD >= 64 ? 8 : 4;
       const size_t cdr = align_up(cap_d * ceil_div(down_ntiles(c.d), NTW), kXcds);
@@ -888,19 +1052,30 @@ hipError_t launch_gemms_bm(const FfnCall& c, TileHeader* hdr, TileEntry* up, Til
   return hipGetLastError();
 }
 
-// The K loops are fully unrolled for the model shape (d = 4096: 32 gate/up K
-// steps; F = 1024: 8 down K steps, routed and shared alike); other sizes use
-// the looped kernels.
+// The K loops are fully unrolled where the compile-time step counts match
+// the call: 32 gate/up steps (d = 4096); 8 down steps (F = 1024, every set)
+// for the resident and the tall-tile down kernels, or 16 (F = 2048) for the
+// tall-tile one. Other sizes use the looped kernels.
+template <int BM, int BMD, int KTU>
+hipError_t launch_gemms_kd(const FfnCall& c, TileHeader* hdr, TileEntry* up, TileEntry* dn,
+                           size_t cap_u, size_t cap_d, hipStream_t s, const StepEvents& ev) {
+  const int kdn = down_ksteps(c);
+  if constexpr (BMD <= 64 || BMD >= 128) {
+    if (kdn == 8) return launch_gemms_bm<BM, KTU, BMD, 8>(c, hdr, up, dn, cap_u, cap_d, s, ev);
+  }
+  if constexpr (BMD >= 128) {
+    if (kdn == 16) return launch_gemms_bm<BM, KTU, BMD, 16>(c, hdr, up, dn, cap_u, cap_d, s, ev);
+  }
+  if constexpr (BMD <= 128)  // taller down tiles exist only where K is fixed (above)
+    return launch_gemms_bm<BM, KTU, BMD, 0>(c, hdr, up, dn, cap_u, cap_d, s, ev);
+  return hipErrorInvalidValue;
+}
+
 template <int BM, int BMD>
 hipError_t launch_gemms_k(const FfnCall& c, TileHeader* hdr, TileEntry* up, TileEntry* dn,
                           size_t cap_u, size_t cap_d, hipStream_t s, const StepEvents& ev) {
-  const bool ku = c.d / kBK == 32;
-  const bool kd = c.set[0].F / kBK == 8 && (c.nsets < 2 || c.set[1].F / kBK == 8);
-  constexpr int KD = BMD <= 64 ? 8 : 0;  // larger tiles: the looped kernel
-  if (ku && kd) return launch_gemms_bm<BM, 32, BMD, KD>(c, hdr, up, dn, cap_u, cap_d, s, ev);
-  if (ku) return launch_gemms_bm<BM, 32, BMD, 0>(c, hdr, up, dn, cap_u, cap_d, s, ev);
-  if (kd) return launch_gemms_bm<BM, 0, BMD, KD>(c, hdr, up, dn, cap_u, cap_d, s, ev);
-  return launch_gemms_bm<BM, 0, BMD, 0>(c, hdr, up, dn, cap_u, cap_d, s, ev);
+  if (c.d / kBK == 32) return launch_gemms_kd<BM, BMD, 32>(c, hdr, up, dn, cap_u, cap_d, s, ev);
+  return launch_gemms_kd<BM, BMD, 0>(c, hdr, up, dn, cap_u, cap_d, s, ev);
 }
 
 }  // namespace
@@ -958,17 +1133,14 @@ hipError_t launch_ffn_gemms(const FfnCall& c, int bm, void* ws, hipStream_t s,
   TileEntry *up, *dn;
   int cu, cd;
   tile_lists(c, bm, ws, &hdr, &up, &dn, &cu, &cd);
-  const bool d64 = down_bm(c, bm) == 64;
   switch (bm) {
     case 16: return launch_gemms_k<16, 16>(c, hdr, up, dn, cu, cd, s, ev);
     case 32: return launch_gemms_k<32, 32>(c, hdr, up, dn, cu, cd, s, ev);
     case 64: return launch_gemms_k<64, 64>(c, hdr, up, dn, cu, cd, s, ev);
-    case 128:
-      return d64 ? launch_gemms_k<128, 64>(c, hdr, up, dn, cu, cd, s, ev)
-                 : launch_gemms_k<128, 128>(c, hdr, up, dn, cu, cd, s, ev);
+    case 128: return launch_gemms_k<128, 128>(c, hdr, up, dn, cu, cd, s, ev);
     default:
-      return d64 ? launch_gemms_k<192, 64>(c, hdr, up, dn, cu, cd, s, ev)
-                 : launch_gemms_k<192, 128>(c, hdr, up, dn, cu, cd, s, ev);
+      return down_bm(c, bm) == 192 ? launch_gemms_k<192, 192>(c, hdr, up, dn, cu, cd, s, ev)
+                                   : launch_gemms_k<192, 128>(c, hdr, up, dn, cu, cd, s, ev);
   }
 }
 

@@ -55,14 +55,21 @@ struct TileLds {
 void tile_lists(const FfnCall& c, int bm, void* ws, TileHeader** hdr, TileEntry** up,
                 TileEntry** dn, int* cap_up, int* cap_dn);
 
+// K steps of the down GEMM when every set has the same F of 1024 or 2048
+// (the shapes with fully unrolled down kernels), else 0.
+__host__ __device__ inline int down_ksteps(const FfnCall& c) {
+  const int f = c.set[0].F;
+  if (c.nsets > 1 && c.set[1].F != f) return 0;
+  return (f == 1024 || f == 2048) ? f / kHN : 0;
+}
+
 // Tile height of the down GEMM for a gate/up tile height: the same up to 32
-// rows; above, 64 rows when every set has F = 1024 (the h slab of a 64-row
-// tile then fits 64 KiB of LDS and stays resident), else at most 128 (the
-// looped kernel's register tile).
+// rows; 64 rows stay 64 (h slab resident in LDS when F = 1024); taller tiles
+// keep their height where the tall-tile kernel's K is fixed (F = 1024 or
+// 2048), else at most 128 (the looped kernel's register tile).
 __host__ __device__ inline int down_bm(const FfnCall& c, int bm_up) {
-  if (bm_up <= 32) return bm_up;
-  const bool f1024 = c.set[0].F == 1024 && (c.nsets < 2 || c.set[1].F == 1024);
-  if (f1024) return 64;
+  if (bm_up <= 64) return bm_up;
+  if (down_ksteps(c) > 0) return bm_up;
   return bm_up < 128 ? bm_up : 128;
 }
 

@@ -70,6 +70,8 @@ PARITY = {
     "fp8_model_m32": LayerConfig("fp8_model_m32", 96, 4096, 16, 4, 1024, 1024, "fp8", seed=21),
     "fp8_model_m128": LayerConfig("fp8_model_m128", 400, 4096, 8, 2, 1024, 1024, "fp8", seed=22),
     "fp8_model_m192": LayerConfig("fp8_model_m192", 380, 4096, 8, 4, 1024, 1024, "fp8", seed=23),
+    # the 100B-shaped expert width F = 2048 (16 down K steps) with 128-row tiles
+    "fp8_model_f2048": LayerConfig("fp8_model_f2048", 400, 4096, 8, 2, 2048, 2048, "fp8", seed=24),
 }
 
 

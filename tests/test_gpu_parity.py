@@ -15,7 +15,7 @@ pytestmark = pytest.mark.gpu
 
 SMALL = ["tiny", "f32_ragged", "f32_noshared", "fp8_small", "fp8_ragged", "fp8_noshared",
          "fp8_k1", "fp8_kE", "fp8_wide", "fp8_skew_small"]
-MODEL = ["fp8_model_m16", "fp8_model_m32", "fp8_model_m128", "fp8_model_m192"]
+MODEL = ["fp8_model_m16", "fp8_model_m32", "fp8_model_m128", "fp8_model_m192", "fp8_model_f2048"]
 
 
 @pytest.fixture(autouse=True)
