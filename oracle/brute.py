@@ -5,8 +5,10 @@ scalars, so it shares no structure with `oracle.moe`.
 
 TEST INFRASTRUCTURE (used only by the CPU test suite to pin the oracle).
 
-It uses the FP8 codec from `oracle.codecs`, which is pinned on its own against
-the format's definition and against an independent library cast.
+It uses the FP8 and E2M1 value tables from `oracle.codecs`, which are pinned
+on their own against the formats' definitions (OCP spec fixtures) and, for
+FP8, against an independent library cast. MXFP4 weights are unpacked here
+nibble by nibble and scaled block by block, without the codec's array code.
 """
 from __future__ import annotations
 
@@ -34,11 +36,28 @@ def _quant_vec(v):
     return vals, s
 
 
-def _expert_out(xrow, w13, w13_scale, w2, w2_scale, fp8: bool):
-    """One expert on one token, scalar by scalar."""
-    twoF, d = len(w13), len(w13[0])
+def _mx_row(packed_row, scale_row):
+    """One MXFP4 weight row: element i is the E2M1 value of nibble i (low
+    nibble first) times 2^(scale of block i // 32 - 127)."""
+    vals = []
+    for i in range(2 * len(packed_row)):
+        byte = int(packed_row[i // 2])
+        nib = (byte >> 4) if i % 2 else (byte & 0xF)
+        vals.append(float(codecs.E2M1_TABLE[nib]) * 2.0 ** (int(scale_row[i // 32]) - 127))
+    return vals
+
+
+def _expert_out(xrow, w13, w13_scale, w2, w2_scale, fp8: bool, mx: bool = False):
+    """One expert on one token, scalar by scalar. fp8: quantised activations
+    and E4M3 weights with channel scales; mx: quantised activations and MXFP4
+    weights (block scales, no channel scale)."""
+    twoF = len(w13)
     F = twoF // 2
-    if fp8:
+    if mx:
+        xv, sx = _quant_vec(xrow)
+        gu = [_dot(xv, _mx_row(w13[n], w13_scale[n])) * sx for n in range(twoF)]
+        fp8 = True
+    elif fp8:
         xv, sx = _quant_vec(xrow)
         gu = [_dot(xv, [codecs.E4M3_TABLE[c] for c in w13[n]]) * sx * float(w13_scale[n])
               for n in range(twoF)]
@@ -55,20 +74,22 @@ def _expert_out(xrow, w13, w13_scale, w2, w2_scale, fp8: bool):
             vals, s = _quant_vec(h[b0:b0 + 128])
             blocks.append((b0, vals, s))
         for m in range(len(w2)):
+            wrow = (_mx_row(w2[m], w2_scale[m]) if mx
+                    else [codecs.E4M3_TABLE[c] for c in w2[m]])
             acc = 0.0
             for b0, vals, s in blocks:
                 part = 0.0
                 for i, hv in enumerate(vals):
-                    part += hv * codecs.E4M3_TABLE[w2[m][b0 + i]]
+                    part += hv * wrow[b0 + i]
                 acc += s * part
-            out.append(acc * float(w2_scale[m]))
+            out.append(acc if mx else acc * float(w2_scale[m]))
     else:
         for m in range(len(w2)):
             out.append(_dot(h, w2[m]))
     return out
 
 
-def brute_layer(x, w_router, bias, k, experts, shared, fp8: bool):
+def brute_layer(x, w_router, bias, k, experts, shared, fp8: bool, mxfp4: bool = False):
     """x: [T][d] float64 values; w_router: [E][d] float64 values; experts: list
     of (w13, w13_scale, w2, w2_scale) per routed expert (codes or floats);
     shared: the same tuple or None. Returns (ids [T][k], w [T][k], y [T][d]) with
@@ -97,12 +118,12 @@ def brute_layer(x, w_router, bias, k, experts, shared, fp8: bool):
         gate = {e: p[e] / psum for e in chosen}
         y = [0.0] * len(x[t])
         for e in range(E):  # every expert runs; the mask zeroes the unchosen ones
-            o = _expert_out(x[t], *experts[e], fp8=fp8)
+            o = _expert_out(x[t], *experts[e], fp8=fp8, mx=mxfp4)
             m = gate.get(e, 0.0)
             for i in range(len(y)):
                 y[i] += m * o[i]
         if shared is not None:
-            o = _expert_out(x[t], *shared, fp8=fp8)
+            o = _expert_out(x[t], *shared, fp8=fp8, mx=mxfp4)
             for i in range(len(y)):
                 y[i] += o[i]
         ids_all.append(chosen)

@@ -1,4 +1,5 @@
-"""Number formats used by the oracle: OCP FP8 E4M3 and bfloat16.
+"""Number formats used by the oracle: OCP FP8 E4M3, bfloat16, and the OCP
+Microscaling MXFP4 weight format (E2M1 elements with one E8M0 scale per 32).
 
 TEST INFRASTRUCTURE. Part of the CPU oracle; only the test suite, the smoke
 check and the benchmark's CPU-baseline leg may import it. Nothing here is
@@ -109,3 +110,57 @@ def bf16_encode(values: np.ndarray) -> np.ndarray:
     """float64 -> uint16 bfloat16 bit patterns (round to nearest even)."""
     r = bf16_round(values).astype(np.float32)  # exact: r has 8 significant bits
     return (r.view(np.uint32) >> 16).astype(np.uint16)
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 (OCP Microscaling Formats, version 1.0): blocks of 32 FP4 E2M1
+# elements sharing one E8M0 scale. Used for expert weights only.
+#   E2M1: 1 sign bit, 2 exponent bits (bias 1), 1 mantissa bit, subnormals,
+#         no infinities or NaN; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+#   E8M0: an unsigned exponent byte e, value 2^(e - 127); 0xFF is NaN.
+# Storage convention of this layer (not fixed by the spec): two elements per
+# byte along the reduction dimension, element 2i in the low nibble of byte i;
+# scales one byte per (row, 32-element block) in block order.
+# ---------------------------------------------------------------------------
+
+def _e2m1_decode_code(code: int) -> float:
+    """Value of one E2M1 nibble, from the format's field definition."""
+    sign = -1.0 if (code >> 3) & 1 else 1.0
+    exp_field = (code >> 1) & 0x3
+    man_field = code & 0x1
+    if exp_field == 0:  # subnormal: 2^(1-bias) * 0.m
+        return sign * (man_field / 2.0)
+    return sign * (2.0 ** (exp_field - 1)) * (1.0 + man_field / 2.0)
+
+
+E2M1_TABLE = np.array([_e2m1_decode_code(c) for c in range(16)], dtype=np.float64)
+MX_BLOCK = 32
+
+
+def e2m1_decode(codes: np.ndarray) -> np.ndarray:
+    """4-bit codes (0..15, any integer dtype) -> float64 values."""
+    return E2M1_TABLE[np.asarray(codes, dtype=np.uint8) & 0xF]
+
+
+def e8m0_decode(e: np.ndarray) -> np.ndarray:
+    """E8M0 scale bytes -> float64 2^(e - 127); 0xFF gives NaN."""
+    e = np.asarray(e, dtype=np.int64)
+    v = np.ldexp(1.0, e - 127)
+    return np.where(e == 0xFF, np.nan, v)
+
+
+def unpack_fp4(packed: np.ndarray) -> np.ndarray:
+    """[..., K/2] bytes -> [..., K] 4-bit codes, element 2i from the low nibble."""
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), dtype=np.uint8)
+    out[..., 0::2] = p & 0xF
+    out[..., 1::2] = p >> 4
+    return out
+
+
+def mxfp4_decode(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """MXFP4 matrix -> float64: element value times its block's E8M0 scale.
+    packed [R][K/2] bytes, scales [R][K/32] bytes."""
+    v = e2m1_decode(unpack_fp4(packed))                          # [R][K]
+    s = e8m0_decode(scales)                                      # [R][K/32]
+    return v * np.repeat(s, MX_BLOCK, axis=-1)

@@ -28,7 +28,8 @@ def _np(t):
 def layer_inputs(lt, cache_all: bool = False) -> moe.LayerInputs:
     """cache_all keeps every expert copied so far (else at most 8 are held)."""
     cfg = lt.cfg
-    fp8 = cfg.precision == "fp8"
+    quant = cfg.precision != "f32"
+    fmt = "mxfp4" if cfg.precision == "mxfp4" else "fp8"
     cache = {}
 
     def expert(e: int) -> moe.ExpertWeights:
@@ -36,13 +37,14 @@ def layer_inputs(lt, cache_all: bool = False) -> moe.LayerInputs:
             if len(cache) > 8 and not cache_all:
                 cache.clear()
             cache[e] = moe.ExpertWeights(
-                _np(lt.w13[e]), _np(lt.w13_scale[e]) if fp8 else None,
-                _np(lt.w2[e]), _np(lt.w2_scale[e]) if fp8 else None)
+                _np(lt.w13[e]), _np(lt.w13_scale[e]) if quant else None,
+                _np(lt.w2[e]), _np(lt.w2_scale[e]) if quant else None, fmt)
         return cache[e]
 
     shared = None
     if lt.ws13 is not None:
-        shared = moe.ExpertWeights(_np(lt.ws13), _np(lt.ws13_scale), _np(lt.ws2), _np(lt.ws2_scale))
+        shared = moe.ExpertWeights(_np(lt.ws13), _np(lt.ws13_scale) if quant else None,
+                                   _np(lt.ws2), _np(lt.ws2_scale) if quant else None, fmt)
     return moe.LayerInputs(
         precision=cfg.precision, x=_np(lt.x), w_router=_np(lt.w_router),
         router_bias=_np(lt.router_bias), k=cfg.k, E=cfg.E, expert=expert, shared=shared)

@@ -42,6 +42,11 @@ design notes):
      amax is 0), codes by round-to-nearest-even with saturation.
   R8 output: bfloat16 (round to nearest even) on the FP8 path, float32 on the
      float32 path.
+  R13 MXFP4 expert weights (a later format, the analogue of the NVFP4 weights
+     the NVIDIA blog runs on Blackwell, section "Running on Blackwell"): OCP
+     Microscaling MXFP4, E2M1 elements with one E8M0 power-of-two scale per 32
+     along the reduction dimension and no channel scale; activations stay as
+     in R7. A weight's value is its E2M1 value times its block's 2^(e - 127).
 """
 from __future__ import annotations
 
@@ -175,12 +180,15 @@ def silu(z: np.ndarray) -> np.ndarray:
 
 @dataclass
 class ExpertWeights:
-    """One expert, as stored. FP8 path: w13/w2 are uint8 codes with float32
-    per-output-channel scales. Float32 path: float arrays, scales None."""
+    """One expert, as stored. fmt "fp8": w13/w2 are uint8 E4M3 codes with
+    float32 per-output-channel scales. fmt "mxfp4": w13 [2F][d/2] / w2
+    [d][F/2] packed E2M1 codes with E8M0 block scales [2F][d/32] / [d][F/32]
+    (OCP MXFP4, no channel scale). Float32 path: float arrays, scales None."""
     w13: np.ndarray                  # [2F][d]
     w13_scale: Optional[np.ndarray]  # [2F]
     w2: np.ndarray                   # [d][F]
     w2_scale: Optional[np.ndarray]   # [d]
+    fmt: str = "fp8"
 
 
 def ffn_fp32(x: np.ndarray, ew: ExpertWeights) -> np.ndarray:
@@ -198,6 +206,9 @@ def gate_up_fp8(xq: np.ndarray, s_x: np.ndarray, ew: ExpertWeights) -> np.ndarra
     gate, n >= F the up projection. The dot products of E4M3 values are exact
     in float64 (every partial sum is a multiple of 2^-18 below 2^31)."""
     xv = codecs.e4m3_decode(xq)                                # [R][d]
+    if ew.fmt == "mxfp4":  # each weight is its E2M1 value times its block's 2^e
+        gu = xv @ codecs.mxfp4_decode(ew.w13, ew.w13_scale).T   # [R][2F]
+        return gu * np.asarray(s_x, np.float64)[:, None]
     gu = xv @ codecs.e4m3_decode(ew.w13).T                      # [R][2F]
     return gu * np.asarray(s_x, np.float64)[:, None] * np.asarray(ew.w13_scale, np.float64)[None, :]
 
@@ -210,15 +221,18 @@ def swiglu_h_fp8(xq: np.ndarray, s_x: np.ndarray, ew: ExpertWeights) -> np.ndarr
 
 
 def down_fp8(hq: np.ndarray, s_h: np.ndarray, ew: ExpertWeights) -> np.ndarray:
-    """o[m] = s_w2[m] * sum_b s_h[b] * sum_{n in b} hq[n] q2[m, n]."""
+    """o[m] = s_w2[m] * sum_b s_h[b] * sum_{n in b} hq[n] q2[m, n] (FP8
+    weights); with MXFP4 weights q2 is the decoded weight (element times its
+    block's 2^e) and there is no s_w2."""
     F = hq.shape[1]
     hv = codecs.e4m3_decode(hq)                                 # [R][F]
-    q2 = codecs.e4m3_decode(ew.w2)                              # [d][F]
+    mx = ew.fmt == "mxfp4"
+    q2 = codecs.mxfp4_decode(ew.w2, ew.w2_scale) if mx else codecs.e4m3_decode(ew.w2)  # [d][F]
     o = np.zeros((hq.shape[0], q2.shape[0]), dtype=np.float64)
     for b in range(F // H_BLOCK):
         cols = slice(b * H_BLOCK, (b + 1) * H_BLOCK)
         o += np.asarray(s_h[:, b], np.float64)[:, None] * (hv[:, cols] @ q2[:, cols].T)
-    return o * np.asarray(ew.w2_scale, np.float64)[None, :]
+    return o if mx else o * np.asarray(ew.w2_scale, np.float64)[None, :]
 
 
 def ffn_fp8(xq: np.ndarray, s_x: np.ndarray, ew: ExpertWeights) -> np.ndarray:
@@ -237,7 +251,8 @@ def ffn_fp8(xq: np.ndarray, s_x: np.ndarray, ew: ExpertWeights) -> np.ndarray:
 class LayerInputs:
     """Host copies of every input, as stored (bf16 as uint16 bits, FP8 as uint8
     codes). `expert(e)` returns routed expert e; `shared` is the shared expert
-    or None. precision: "fp8" (bf16 activations, FP8 weights) or "f32"."""
+    or None. precision: "fp8" (bf16 activations, FP8 weights), "mxfp4" (bf16
+    activations, MXFP4 weights) or "f32"."""
     precision: str
     x: np.ndarray             # [T][d] uint16 bf16 bits, or float32
     w_router: np.ndarray      # [E][d] uint16 bf16 bits, or float32
@@ -250,13 +265,13 @@ class LayerInputs:
 
 def activations(inp: LayerInputs) -> np.ndarray:
     """x as float64 (bf16 bit patterns decoded exactly)."""
-    if inp.precision == "fp8":
+    if inp.precision != "f32":
         return codecs.bf16_decode(inp.x)
     return np.asarray(inp.x, np.float64)
 
 
 def router_weight(inp: LayerInputs) -> np.ndarray:
-    if inp.precision == "fp8":
+    if inp.precision != "f32":
         return codecs.bf16_decode(inp.w_router)
     return np.asarray(inp.w_router, np.float64)
 
@@ -283,7 +298,7 @@ def combine(w: np.ndarray, o_pairs: np.ndarray, o_shared: Optional[np.ndarray]) 
 
 
 def round_output(y64: np.ndarray, precision: str) -> np.ndarray:
-    if precision == "fp8":
+    if precision != "f32":
         return codecs.bf16_round(y64)
     return y64.astype(np.float32).astype(np.float64)
 
@@ -297,7 +312,7 @@ def layer_forward(inp: LayerInputs, keep_intermediates: bool = True) -> LayerRes
     _, _, ids, w = route(x, router_weight(inp), inp.router_bias, k)
     perm = permute(ids, E)
     xq = s_x = None
-    if inp.precision == "fp8":
+    if inp.precision != "f32":
         xq, s_x = quantize_rows_e4m3(x)
     expert_out = np.zeros((T * k, d), dtype=np.float64)
     for e in range(E):
@@ -306,13 +321,13 @@ def layer_forward(inp: LayerInputs, keep_intermediates: bool = True) -> LayerRes
             continue  # empty group: no rows, no work
         tok = perm.sorted_pair[r0:r1] // k
         ew = inp.expert(e)
-        if inp.precision == "fp8":
+        if inp.precision != "f32":
             expert_out[r0:r1] = ffn_fp8(xq[tok], s_x[tok], ew)
         else:
             expert_out[r0:r1] = ffn_fp32(x[tok], ew)
     shared_out = None
     if inp.shared is not None:
-        shared_out = (ffn_fp8(xq, s_x, inp.shared) if inp.precision == "fp8"
+        shared_out = (ffn_fp8(xq, s_x, inp.shared) if inp.precision != "f32"
                       else ffn_fp32(x, inp.shared))
     o_pairs = expert_out[perm.pair_to_row].reshape(T, k, d)
     y64 = combine(w, o_pairs, shared_out)
@@ -330,20 +345,20 @@ def layer_forward_tokens(inp: LayerInputs, tokens: np.ndarray):
     k = inp.k
     _, _, ids, w = route(x, router_weight(inp), inp.router_bias, k)
     xq = s_x = None
-    if inp.precision == "fp8":
+    if inp.precision != "f32":
         xq, s_x = quantize_rows_e4m3(x)
     T, d = x.shape
     o_pairs = np.zeros((T, k, d), dtype=np.float64)
     for e in np.unique(ids):
         ew = inp.expert(int(e))
         rows, slots = np.nonzero(ids == e)
-        if inp.precision == "fp8":
+        if inp.precision != "f32":
             o_pairs[rows, slots] = ffn_fp8(xq[rows], s_x[rows], ew)
         else:
             o_pairs[rows, slots] = ffn_fp32(x[rows], ew)
     shared_out = None
     if inp.shared is not None:
-        shared_out = (ffn_fp8(xq, s_x, inp.shared) if inp.precision == "fp8"
+        shared_out = (ffn_fp8(xq, s_x, inp.shared) if inp.precision != "f32"
                       else ffn_fp32(x, inp.shared))
     y64 = combine(w, o_pairs, shared_out)
     return ids, w, xq, s_x, y64, round_output(y64, inp.precision)

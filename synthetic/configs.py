@@ -26,7 +26,8 @@ class LayerConfig:
     k: int          # experts per token
     F: int          # routed expert FFN width
     F_shared: int   # shared expert FFN width (0: no shared expert)
-    precision: str  # "fp8": bf16 activations + FP8 E4M3 weights; "f32": float32 throughout
+    precision: str  # "fp8": bf16 activations + FP8 E4M3 weights; "mxfp4": bf16
+                    # activations + OCP MXFP4 weights; "f32": float32 throughout
     seed: int
     skew: bool = False   # seeded per-expert router bias: 8 hot experts, 40 starved
 
@@ -49,6 +50,8 @@ CONFIGS = {
     "b100": LayerConfig("b100", 4096, 4096, 128, 8, 2048, 2048, "fp8", seed=4),
     # skewed routing: 8 hot experts take ~half the assignments, 40 get none
     "skew": LayerConfig("skew", 2048, 4096, 128, 6, 1024, 1024, "fp8", seed=5, skew=True),
+    # the decode step with MXFP4 expert weights
+    "decode_mxfp4": LayerConfig("decode_mxfp4", 64, 4096, 128, 6, 1024, 1024, "mxfp4", seed=2),
 }
 
 # Small parity shapes (several tiles, ragged tails).
@@ -72,6 +75,12 @@ PARITY = {
     "fp8_model_m192": LayerConfig("fp8_model_m192", 380, 4096, 8, 4, 1024, 1024, "fp8", seed=23),
     # the 100B-shaped expert width F = 2048 (16 down K steps) with 128-row tiles
     "fp8_model_f2048": LayerConfig("fp8_model_f2048", 400, 4096, 8, 2, 2048, 2048, "fp8", seed=24),
+    # MXFP4 expert weights (FP8 activations): small and model-shaped
+    "mx_small": LayerConfig("mx_small", 45, 512, 16, 4, 256, 256, "mxfp4", seed=31),
+    "mx_ragged": LayerConfig("mx_ragged", 203, 1024, 32, 6, 384, 256, "mxfp4", seed=32),
+    "mx_model_m16": LayerConfig("mx_model_m16", 48, 4096, 16, 4, 1024, 1024, "mxfp4", seed=33),
+    "mx_model_m64": LayerConfig("mx_model_m64", 200, 4096, 8, 2, 1024, 1024, "mxfp4", seed=34),
+    "mx_model_m192": LayerConfig("mx_model_m192", 380, 4096, 8, 4, 1024, 1024, "mxfp4", seed=35),
 }
 
 

@@ -84,7 +84,7 @@ def _torch_seed(ss: np.random.SeedSequence) -> int:
 
 def _to_act(a: np.ndarray, precision: str, device) -> torch.Tensor:
     t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
-    if precision == "fp8":
+    if precision != "f32":
         t = t.to(torch.bfloat16)
     return t.to(device)
 
@@ -103,6 +103,35 @@ def quantize_master_fp8(master: torch.Tensor):
     return q.view(torch.uint8), scale
 
 
+# E2M1 magnitudes in code order, and the midpoints between neighbours.
+_E2M1_MAG = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+_E2M1_MID = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)
+
+
+def quantize_master_mxfp4(master: torch.Tensor):
+    """OCP MXFP4 storage of a float32 master [rows][cols] (cols a multiple of
+    32): per 32-column block the shared exponent is floor(log2(amax)) - 2
+    (E2M1's largest exponent), the block is divided by 2^exponent and each
+    value rounded to the nearest E2M1 value (ties to the even code),
+    saturating at 6. Returns (packed codes [rows][cols/2] uint8, element 2i in
+    the low nibble; E8M0 scales [rows][cols/32] uint8)."""
+    rows, cols = master.shape
+    b = master.reshape(rows, cols // 32, 32)
+    amax = b.abs().amax(dim=-1)
+    _, ex = torch.frexp(amax)                       # amax = m 2^ex, 0.5 <= m < 1
+    e = torch.where(amax > 0, ex - 1 - 2, torch.full_like(ex, -127)).clamp(-127, 127)
+    scaled = b / torch.exp2(e.to(torch.float32))[..., None]
+    mag = scaled.abs().clamp(max=6.0)
+    mid = torch.tensor(_E2M1_MID, dtype=torch.float32, device=master.device)
+    lo = torch.searchsorted(mid, mag.contiguous(), right=False)
+    hi = torch.searchsorted(mid, mag.contiguous(), right=True)
+    code = torch.where(lo == hi, lo, torch.where(lo % 2 == 0, lo, hi))  # exact midpoint: even code
+    code = code.to(torch.uint8) | (torch.signbit(scaled).to(torch.uint8) << 3)
+    code = code.reshape(rows, cols)
+    packed = code[:, 0::2] | (code[:, 1::2] << 4)
+    return packed.contiguous(), (e + 127).to(torch.uint8).contiguous()
+
+
 def _expert(seed_ss, rows13: int, d: int, F: int, precision: str, device):
     g = torch.Generator(device=device)
     g.manual_seed(_torch_seed(seed_ss))
@@ -111,6 +140,10 @@ def _expert(seed_ss, rows13: int, d: int, F: int, precision: str, device):
     if precision == "fp8":
         q13, s13 = quantize_master_fp8(m13)
         q2, s2 = quantize_master_fp8(m2)
+        return q13, s13, q2, s2
+    if precision == "mxfp4":
+        q13, s13 = quantize_master_mxfp4(m13)
+        q2, s2 = quantize_master_mxfp4(m2)
         return q13, s13, q2, s2
     return m13, None, m2, None
 
@@ -175,13 +208,19 @@ def make_layer(cfg: LayerConfig, device="cpu", hooks: Optional[RoutingHooks] = N
         else:
             raise RuntimeError("make_layer: near-tie redraw did not converge")
 
-    wdt = torch.uint8 if cfg.precision == "fp8" else torch.float32
-    w13 = torch.empty((E, 2 * F, d), dtype=wdt, device=device)
-    w2 = torch.empty((E, d, F), dtype=wdt, device=device)
     w13_scale = w2_scale = None
-    if cfg.precision == "fp8":
-        w13_scale = torch.empty((E, 2 * F), dtype=torch.float32, device=device)
-        w2_scale = torch.empty((E, d), dtype=torch.float32, device=device)
+    if cfg.precision == "mxfp4":
+        w13 = torch.empty((E, 2 * F, d // 2), dtype=torch.uint8, device=device)
+        w2 = torch.empty((E, d, F // 2), dtype=torch.uint8, device=device)
+        w13_scale = torch.empty((E, 2 * F, d // 32), dtype=torch.uint8, device=device)
+        w2_scale = torch.empty((E, d, F // 32), dtype=torch.uint8, device=device)
+    else:
+        wdt = torch.uint8 if cfg.precision == "fp8" else torch.float32
+        w13 = torch.empty((E, 2 * F, d), dtype=wdt, device=device)
+        w2 = torch.empty((E, d, F), dtype=wdt, device=device)
+        if cfg.precision == "fp8":
+            w13_scale = torch.empty((E, 2 * F), dtype=torch.float32, device=device)
+            w2_scale = torch.empty((E, d), dtype=torch.float32, device=device)
     for e in range(E):
         q13, s13, q2, s2 = _expert(kids[_EXPERT0 + e], 2 * F, d, F, cfg.precision, device)
         w13[e].copy_(q13)

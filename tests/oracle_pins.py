@@ -267,6 +267,68 @@ def pin_f32_layer_vs_brute():
     assert np.allclose(r.y64, y, atol=1e-12, rtol=0)
 
 
+def _random_mx_layer(seed, T, d, E, k, F, Fs):
+    rng = _rng(seed)
+    x = codecs.bf16_encode(rng.standard_normal((T, d)))
+    wr = codecs.bf16_encode(rng.standard_normal((E, d)) / math.sqrt(d))
+
+    def mk(F_):
+        # random nibbles, block exponents around 2^-7 (weights of order 0.01-0.05)
+        return moe.ExpertWeights(
+            rng.integers(0, 256, (2 * F_, d // 2), dtype=np.uint8),
+            rng.integers(118, 123, (2 * F_, d // 32), dtype=np.uint8),
+            rng.integers(0, 256, (d, F_ // 2), dtype=np.uint8),
+            rng.integers(118, 123, (d, F_ // 32), dtype=np.uint8), "mxfp4")
+    experts = [mk(F) for _ in range(E)]
+    shared = mk(Fs) if Fs else None
+    return moe.LayerInputs("mxfp4", x, wr, None, k, E, lambda e: experts[e], shared), experts, shared
+
+
+def pin_mxfp4_layer_vs_brute():
+    """MXFP4 expert weights: the layer equals the scalar loop that unpacks
+    each nibble and applies its block's power of two itself."""
+    inp, experts, shared = _random_mx_layer(112, T=3, d=128, E=4, k=2, F=256, Fs=128)
+    r = moe.layer_forward(inp)
+    ex = [(e.w13, e.w13_scale, e.w2, e.w2_scale) for e in experts]
+    sh = (shared.w13, shared.w13_scale, shared.w2, shared.w2_scale)
+    ids, w, y = brute.brute_layer(codecs.bf16_decode(inp.x), codecs.bf16_decode(inp.w_router),
+                                  None, inp.k, ex, sh, fp8=True, mxfp4=True)
+    assert np.array_equal(r.ids, ids)
+    assert np.allclose(r.y64, y, atol=1e-9, rtol=0)
+
+
+def pin_mxfp4_decode_worked_example():
+    """One row, two blocks: byte 0x21 holds element 0 = 0.5 (code 1, low
+    nibble) and element 1 = 1.0 (code 2); block 0 scale 2^3, block 1 scale
+    2^-1; byte 0xF7 holds 6.0 (code 7) then -6.0 (code 0xF)."""
+    packed = np.zeros((1, 32), np.uint8)
+    packed[0, 0] = 0x21
+    packed[0, 16] = 0xF7            # element 32: 6.0, element 33: -6.0
+    scales = np.array([[127 + 3, 127 - 1]], np.uint8)
+    v = codecs.mxfp4_decode(packed, scales)
+    assert v.shape == (1, 64)
+    assert v[0, 0] == 4.0 and v[0, 1] == 8.0 and np.all(v[0, 2:32] == 0)
+    assert v[0, 32] == 3.0 and v[0, 33] == -3.0 and np.all(v[0, 34:] == 0)
+
+
+def pin_mxfp4_dense_is_textbook():
+    """E = k = 1 with MXFP4 weights: the layer is torch's SwiGLU on the
+    decoded weights and the quantised activations, with h quantised per
+    128-column block."""
+    inp, experts, _ = _random_mx_layer(113, T=4, d=128, E=1, k=1, F=128, Fs=0)
+    r = moe.layer_forward(inp)
+    ew = experts[0]
+    w13 = codecs.mxfp4_decode(ew.w13, ew.w13_scale)
+    w2 = codecs.mxfp4_decode(ew.w2, ew.w2_scale)
+    xq = codecs.e4m3_decode(r.xq) * r.s_x.astype(np.float64)[:, None]
+    gu = tF.linear(torch.from_numpy(xq), torch.from_numpy(w13))
+    h = (tF.silu(gu[:, :128]) * gu[:, 128:]).numpy()
+    hq, s_h = moe.quantize_blocks_e4m3(h)
+    want = tF.linear(torch.from_numpy(codecs.e4m3_decode(hq) * s_h.astype(np.float64)),
+                     torch.from_numpy(w2)).numpy()
+    assert np.allclose(r.y64, want, atol=1e-10, rtol=0)
+
+
 def pin_worked_example_closed_form():
     """Hand-derived layer: d=2, E=3, top-2, F=1, one shared expert.
     logits [ln4, 0, ln2] -> p = [4, 1, 2]/7 -> ids [0, 2], w = [2/3, 1/3];

@@ -108,3 +108,36 @@ def test_bf16_round_direct_from_float64():
     assert codecs.bf16_round(np.array([1.0 + 2.0 ** -8]))[0] == 1.0
     assert codecs.bf16_round(np.array([1.0 + 2.0 ** -8 + 2.0 ** -40]))[0] == 1.0 + 2.0 ** -7
     assert codecs.bf16_round(np.array([1.0 + 3 * 2.0 ** -8]))[0] == 1.0 + 2.0 ** -6
+
+
+MX_GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "e2m1_e8m0_ocp_mx_spec.txt")
+
+
+def test_mx_spec_values():
+    """Every E2M1 code and the E8M0 boundary codes equal the OCP MX spec's."""
+    n = 0
+    for line in open(MX_GOLDEN):
+        if not line.strip() or line.startswith("#"):
+            continue
+        fmt, code, val = line.split()
+        got = codecs.E2M1_TABLE[int(code, 16)] if fmt == "E2M1" else codecs.e8m0_decode(int(code, 16))
+        if val == "nan":
+            assert np.isnan(got)
+        else:
+            assert got == float(val) and np.signbit(got) == val.startswith("-"), (fmt, code, got)
+        n += 1
+    assert n == 21
+
+
+def test_e2m1_structure():
+    """Magnitudes increase with the code, the sign bit mirrors them, and the
+    spacing doubles from one binade to the next (one mantissa bit)."""
+    pos = codecs.E2M1_TABLE[:8]
+    assert np.all(np.diff(pos) > 0)
+    assert np.array_equal(codecs.E2M1_TABLE[8:], -pos)
+    assert np.array_equal(np.diff(pos), [0.5, 0.5, 0.5, 0.5, 1.0, 1.0, 2.0])
+
+
+def test_unpack_fp4_low_nibble_first():
+    p = np.array([[0x21, 0xF0, 0x9A]], np.uint8)
+    assert codecs.unpack_fp4(p).tolist() == [[1, 2, 0, 15, 10, 9]]

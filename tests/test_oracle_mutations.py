@@ -70,6 +70,18 @@ def _shared_dropped(w, o_pairs, o_shared):
     return ORIG["combine"](w, o_pairs, None)
 
 
+def _fp4_high_nibble_first(packed):
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), dtype=np.uint8)
+    out[..., 0::2] = p >> 4
+    out[..., 1::2] = p & 0xF
+    return out
+
+
+def _e8m0_bias_126(e):
+    return np.ldexp(1.0, np.asarray(e, np.int64) - 126)
+
+
 ORIG = {n: getattr(moe, n) for n in
         ["ffn_fp32", "ffn_fp8", "router_logits", "permute", "combine"]}
 
@@ -83,11 +95,17 @@ MUTANTS = {
     "scale_amax_over_255": ("quantize_rows_e4m3", _quant_scale_255),
     "w13_scale_misindexed": ("ffn_fp8", _w13_scale_by_input),
     "shared_expert_dropped": ("combine", _shared_dropped),
+    "fp4_high_nibble_first": ("codecs.unpack_fp4", _fp4_high_nibble_first),
+    "e8m0_bias_126": ("codecs.e8m0_decode", _e8m0_bias_126),
 }
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(name, monkeypatch):
     attr, fn = MUTANTS[name]
-    monkeypatch.setattr(moe, attr, fn)
+    if attr.startswith("codecs."):
+        from oracle import codecs
+        monkeypatch.setattr(codecs, attr.split(".", 1)[1], fn)
+    else:
+        monkeypatch.setattr(moe, attr, fn)
     assert _any_pin_fails(), f"no pin catches mutant {name}"
