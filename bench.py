@@ -71,15 +71,21 @@ def accounting(cfg, counts):
     touched = int((counts > 0).sum())
     groups = touched + (1 if Fs else 0)
     rows = T * k + (T if Fs else 0)
+
+    def wb(r, c):
+        """bytes of an [r][c] weight matrix with its scales: E4M3 codes and a
+        float32 per row, or MXFP4 (half a byte per element, one E8M0 byte
+        per 32 elements)"""
+        return r * c // 2 + r * c // 32 if cfg.precision == "mxfp4" else r * c + 4 * r
     # gate/up launch: each touched group's W13 codes + scales once; per row the
     # x codes + scale in and the h codes + block scales out
-    up_bytes = touched * (2 * F * d + 8 * F) + (2 * Fs * d + 8 * Fs if Fs else 0) \
+    up_bytes = touched * wb(2 * F, d) + (wb(2 * Fs, d) if Fs else 0) \
         + rows * (d + 4) + T * k * (F + F // 32) + (T * (Fs + Fs // 32) if Fs else 0)
     up_flops = 2.0 * d * (T * k * 2 * F + (T * 2 * Fs if Fs else 0))
     # whole layer: every touched expert's weights and scales once, router
-    # weight, x in, y out; FP8 GEMM FLOPs 6 d F per (token, expert) pair
-    layer_bytes = touched * (3 * d * F + (2 * F + d) * 4) \
-        + ((3 * d * Fs + (2 * Fs + d) * 4) if Fs else 0) + E * d * 2 + 2 * T * d * 2
+    # weight, x in, y out; GEMM FLOPs 6 d F per (token, expert) pair
+    layer_bytes = touched * (wb(2 * F, d) + wb(d, F)) \
+        + ((wb(2 * Fs, d) + wb(d, Fs)) if Fs else 0) + E * d * 2 + 2 * T * d * 2
     layer_flops = 6.0 * d * (T * k * F + (T * Fs if Fs else 0))
     return dict(touched=touched, groups=groups, rows=rows, up_bytes=up_bytes, up_flops=up_flops,
                 layer_bytes=layer_bytes, layer_flops=layer_flops)
@@ -315,7 +321,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "b100", "skew"])
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "prefill", "b100", "skew", "decode_mxfp4"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the other workloads (prefill, 100B-shaped, skewed, chunked prefill) "
@@ -369,10 +376,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3",
+        "dtype": "fp8_e4m3" if cfg.precision == "fp8" else "fp8_e4m3 x mxfp4",
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: T={cfg.T} d={cfg.d} E={cfg.E} top-{cfg.k} "
-                               f"F={cfg.F} shared F={cfg.F_shared}, FP8 E4M3 weights, bf16 x",
+                               f"F={cfg.F} shared F={cfg.F_shared}, "
+                               f"{'MXFP4' if cfg.precision == 'mxfp4' else 'FP8 E4M3'} weights, bf16 x",
                    "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k, "F": cfg.F,
                    "F_shared": cfg.F_shared, "parallelism": "none (1 GPU)"},
         "roofline": {"kernel": "gate_up_fp8_kernel", "bound": "hbm", "achieved": round(achieved, 1),
@@ -388,7 +396,7 @@ def main():
     if not args.no_secondary:
         # the other workloads, reported beside the headline (not part of `value`)
         sec_steps, sec_warm = max(5, args.steps // 2), max(2, args.warmup // 2)
-        for name in ("prefill", "b100", "skew"):
+        for name in ("prefill", "b100", "skew", "decode_mxfp4"):
             if name == args.workload:
                 continue
             c2 = CONFIGS[name]

@@ -34,6 +34,16 @@
  *    E4M3: x per token, the SwiGLU output h per (row, 128-column block), each
  *    with a float32 scale amax/448 (1.0 for an all-zero block), codes rounded
  *    to nearest even with saturation at +-448.
+ *  - (MOE_DTYPE_BF16, MOE_DTYPE_MXFP4): as the FP8 path, with OCP
+ *    Microscaling MXFP4 expert weights (the analogue of the NVFP4 weights the
+ *    NVIDIA blog runs on Blackwell, section "Running on Blackwell"): E2M1
+ *    elements packed two per byte along the reduction dimension (element 2i in
+ *    the low nibble of byte i) with one E8M0 scale byte (value 2^(e - 127)) per
+ *    32 elements, and no channel scale:
+ *      w13 [E][2F][d/2] bytes, w13_scale [E][2F][d/32] bytes,
+ *      w2  [E][d][F/2],        w2_scale  [E][d][F/32],
+ *    the shared expert likewise without the E dimension. A weight's value is
+ *    its E2M1 value times its block's scale.
  *  - (MOE_DTYPE_F32, MOE_DTYPE_F32): float32 throughout, no quantisation.
  */
 #ifndef MOE_H_
@@ -46,7 +56,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 /* Limits checked by every entry point. */
 #define MOE_MAX_E 256      /* routed experts */
@@ -67,7 +77,8 @@ typedef enum moe_status {
 typedef enum moe_dtype {
   MOE_DTYPE_F32 = 0,
   MOE_DTYPE_BF16 = 1,
-  MOE_DTYPE_FP8_E4M3 = 2
+  MOE_DTYPE_FP8_E4M3 = 2,
+  MOE_DTYPE_MXFP4 = 3       /* expert weights only */
 } moe_dtype_t;
 
 /* Shape of one layer call. */
@@ -87,13 +98,14 @@ typedef struct moe_weights {
   const void* w_router;     /* [E][d], act_dtype */
   const float* router_bias; /* [E] added to the logits before softmax, or NULL */
   const void* w13;          /* [E][2F][d], w_dtype; rows 0..F-1 gate, F..2F-1 up */
-  const float* w13_scale;   /* [E][2F] per-output-row scales (FP8 only, else NULL) */
+  const void* w13_scale;    /* FP8: float32 [E][2F] per-output-row scales; MXFP4: E8M0
+                               bytes [E][2F][d/32]; F32: NULL */
   const void* w2;           /* [E][d][F], w_dtype */
-  const float* w2_scale;    /* [E][d] (FP8 only) */
+  const void* w2_scale;     /* FP8: float32 [E][d]; MXFP4: E8M0 bytes [E][d][F/32] */
   const void* ws13;         /* shared expert [2F_shared][d] (NULL if F_shared == 0) */
-  const float* ws13_scale;  /* [2F_shared] (FP8 only) */
+  const void* ws13_scale;   /* FP8: float32 [2F_shared]; MXFP4: bytes [2F_shared][d/32] */
   const void* ws2;          /* shared expert [d][F_shared] */
-  const float* ws2_scale;   /* [d] (FP8 only) */
+  const void* ws2_scale;    /* FP8: float32 [d]; MXFP4: bytes [d][F_shared/32] */
 } moe_weights_t;
 
 /* One grouped SwiGLU FFN call: G groups of rows, each group g multiplying its
@@ -103,23 +115,23 @@ typedef struct moe_ffn {
   int32_t F;                    /* FFN width of every group (multiple of 128) */
   int32_t num_groups;           /* G >= 1 */
   int32_t max_rows;             /* rows of `out`; group_offsets[G] must not exceed it */
-  int32_t w_dtype;              /* MOE_DTYPE_FP8_E4M3 or MOE_DTYPE_F32 */
+  int32_t w_dtype;              /* MOE_DTYPE_FP8_E4M3, MOE_DTYPE_MXFP4 or MOE_DTYPE_F32 */
   const int32_t* group_offsets; /* device [G+1], non-decreasing, [0] == 0: group g owns
                                    grouped rows group_offsets[g] .. group_offsets[g+1]-1 */
   const int32_t* row_src;       /* device [max_rows] or NULL: grouped row r reads activation
                                    row row_src[r] / src_div (NULL: activation row r) */
   int32_t src_div;              /* >= 1 */
   int32_t a_rows;               /* rows of `a`; every source row must be below it */
-  const void* a;                /* [a_rows][d]: FP8 codes (FP8 path) or float32 */
-  const float* a_scale;         /* [a_rows] per-row scales (FP8 path), else NULL */
-  const void* w13;              /* [G][2F][d] */
-  const float* w13_scale;       /* [G][2F] (FP8 path) */
-  const void* w2;               /* [G][d][F] */
-  const float* w2_scale;        /* [G][d] (FP8 path) */
-  void* out;                    /* [max_rows][d]: bf16 (FP8 path) or float32 */
-  void* h_out;                  /* optional: receives h, [max_rows][F] FP8 codes (FP8 path)
+  const void* a;                /* [a_rows][d]: FP8 codes (FP8, MXFP4 paths) or float32 */
+  const float* a_scale;         /* [a_rows] per-row scales (FP8/MXFP4 paths), else NULL */
+  const void* w13;              /* [G][2F][d] (MXFP4: [G][2F][d/2] packed) */
+  const void* w13_scale;        /* FP8: float32 [G][2F]; MXFP4: E8M0 bytes [G][2F][d/32] */
+  const void* w2;               /* [G][d][F] (MXFP4: [G][d][F/2] packed) */
+  const void* w2_scale;         /* FP8: float32 [G][d]; MXFP4: E8M0 bytes [G][d][F/32] */
+  void* out;                    /* [max_rows][d]: bf16 (FP8, MXFP4 paths) or float32 */
+  void* h_out;                  /* optional: receives h, [max_rows][F] FP8 codes (FP8, MXFP4)
                                    or float32; NULL keeps h in the workspace */
-  float* h_scale_out;           /* optional: [max_rows][F/128] block scales of h (FP8 path) */
+  float* h_scale_out;           /* optional: [max_rows][F/128] block scales of h (FP8, MXFP4) */
 } moe_ffn_t;
 
 /* ABI version (MOE_ABI_VERSION) and a static text for a status code. */
@@ -149,7 +161,8 @@ moe_status_t moe_grouped_ffn_workspace_size(const moe_ffn_t* ffn, size_t* bytes)
  *   w[t, j]  = softmax(l[t, .])[ids[t, j]] / sum_j' softmax(l[t, .])[ids[t, j']]
  *
  * x [T][d] and w_router [E][d] in act_dtype; router_bias [E] float32 or NULL.
- * Outputs topk_ids [T][k] int32 and topk_w [T][k] float32. On the FP8 path the
+ * Outputs topk_ids [T][k] int32 and topk_w [T][k] float32. On the FP8 and MXFP4
+ * paths (bf16 activations) the
  * logits launch also writes xq [T][d] (FP8 E4M3 codes of x / x_scale[t]) and
  * x_scale [T] (amax of row t over 448, 1.0 for a zero row); both are required
  * there and ignored on the float32 path. Two launches (logits, selection).
@@ -187,6 +200,9 @@ moe_status_t moe_permute(const moe_shape_t* shape, const int32_t* topk_ids, int3
  *              h is quantised per 128-column block (scale amax/448, E4M3 codes)
  *              out[r][m] = w2_scale[g][m] * sum_b s_h[b] * sum_{n in b} hq[n] * w2[g][m][n]
  *              out is rounded to bf16 (nearest even)
+ *   MXFP4:     as the FP8 path with w13[g][n][i] and w2[g][m][n] the decoded
+ *              MXFP4 values (E2M1 value times 2^(block scale - 127)) and no
+ *              w13_scale / w2_scale factor.
  *   F32 path:  the same without any quantisation, float32 out.
  * Rows beyond group_offsets[G] are not written. Needs a workspace of
  * moe_grouped_ffn_workspace_size() bytes. The shared expert is one group over
@@ -200,7 +216,7 @@ moe_status_t moe_grouped_ffn(const moe_ffn_t* ffn, void* workspace, size_t works
  * atomics:  y[t] = sum_{j=0}^{k-1} topk_w[t, j] * expert_out[pair_to_row[t*k + j]]
  *                  + shared_out[t]
  * expert_out [T*k][d] and shared_out [T][d] (NULL: no shared term) are bf16 on
- * the FP8 path and float32 on the float32 path, as is y [T][d]. Pairs whose
+ * the FP8 and MXFP4 paths and float32 on the float32 path, as is y [T][d]. Pairs whose
  * pair_to_row is outside [0, T*k) contribute nothing.
  */
 moe_status_t moe_combine(const moe_shape_t* shape, const void* expert_out,

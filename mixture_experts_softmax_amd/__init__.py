@@ -1,5 +1,5 @@
 """MI355X-native forward pass of one mixture-of-experts layer (softmax top-k
-gating, FP8 SwiGLU experts, one shared expert) as hand-written HIP kernels for
+gating, FP8 or MXFP4 SwiGLU experts, one shared expert) as hand-written HIP kernels for
 gfx950 behind a C ABI (include/moe.h, libmoe.so).
 
 This package is the thin Python side: `_lib` mirrors the C entry points one to
@@ -35,8 +35,11 @@ class MoELayer:
     """One layer: shape, device weights and a reusable workspace.
 
     precision "fp8": x/y bf16 [T][d], router bf16 [E][d], expert weights uint8
-    E4M3 codes with float32 per-output-row scales. precision "f32": float32
-    everywhere, scales None.
+    E4M3 codes with float32 per-output-row scales. precision "mxfp4": as
+    "fp8" with MXFP4 expert weights: uint8 w13 [E][2F][d/2] and w2 [E][d][F/2]
+    (two E2M1 codes a byte, low nibble first) and uint8 E8M0 scales
+    w13_scale [E][2F][d/32], w2_scale [E][d][F/32] (the shared expert alike).
+    precision "f32": float32 everywhere, scales None.
     """
 
     def __init__(self, *, d, E, k, F, F_shared, precision, w_router, router_bias, w13, w13_scale,

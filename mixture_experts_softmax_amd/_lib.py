@@ -16,7 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
-MOE_DTYPE_F32, MOE_DTYPE_BF16, MOE_DTYPE_FP8_E4M3 = 0, 1, 2
+MOE_DTYPE_F32, MOE_DTYPE_BF16, MOE_DTYPE_FP8_E4M3, MOE_DTYPE_MXFP4 = 0, 1, 2, 3
 
 # Names declared in include/moe.h, in order.
 EXPORTS = [
@@ -132,16 +132,30 @@ def _stream(stream) -> Optional[C.c_void_p]:
     return C.c_void_p(stream.cuda_stream)
 
 
+_W_DTYPE = {"fp8": MOE_DTYPE_FP8_E4M3, "mxfp4": MOE_DTYPE_MXFP4, "f32": MOE_DTYPE_F32}
+
+
 def shape(T, d, E, k, F, F_shared, precision: str) -> MoeShape:
-    if precision == "fp8":
-        return MoeShape(T, d, E, k, F, F_shared, MOE_DTYPE_BF16, MOE_DTYPE_FP8_E4M3)
-    if precision == "f32":
-        return MoeShape(T, d, E, k, F, F_shared, MOE_DTYPE_F32, MOE_DTYPE_F32)
-    raise ValueError(precision)
+    """precision: "fp8" (bf16 activations, E4M3 weights), "mxfp4" (bf16
+    activations, MXFP4 weights) or "f32"."""
+    if precision not in _W_DTYPE:
+        raise ValueError(precision)
+    act = MOE_DTYPE_F32 if precision == "f32" else MOE_DTYPE_BF16
+    return MoeShape(T, d, E, k, F, F_shared, act, _W_DTYPE[precision])
 
 
 def _is_fp8(s: MoeShape) -> bool:
-    return s.w_dtype == MOE_DTYPE_FP8_E4M3
+    """The quantised path (FP8 activation codes; FP8 or MXFP4 weights)."""
+    return s.w_dtype != MOE_DTYPE_F32
+
+
+def _w_sizes(w_dtype: int, rows: int, cols: int):
+    """(weight bytes or elements, scale dtype, scale elements) of a [rows][cols]
+    weight matrix: FP8 has one float32 scale per row, MXFP4 packs two codes a
+    byte with one E8M0 byte per 32 columns."""
+    if w_dtype == MOE_DTYPE_MXFP4:
+        return rows * cols // 2, torch.uint8, rows * cols // 32
+    return rows * cols, torch.float32, rows
 
 
 def _act_dtype(s: MoeShape):
@@ -212,21 +226,27 @@ def moe_permute(s: MoeShape, topk_ids, offsets, sorted_pair, pair_to_row, worksp
            "moe_permute")
 
 
-def make_ffn(d, F, num_groups, max_rows, fp8: bool, group_offsets, row_src, src_div, a, a_scale,
+def make_ffn(d, F, num_groups, max_rows, fp8, group_offsets, row_src, src_div, a, a_scale,
              w13, w13_scale, w2, w2_scale, out, h_out=None, h_scale_out=None) -> MoeFfn:
+    """fp8: True / "fp8" (E4M3 weights), "mxfp4", or False / "f32"."""
     G = num_groups
+    fmt = {True: "fp8", False: "f32"}.get(fp8, fp8)
+    wdt = _W_DTYPE[fmt]
+    fp8 = fmt != "f32"
     wd = torch.uint8 if fp8 else torch.float32
     a_rows = a.shape[0] if a is not None else 0
+    n13, sd, ns13 = _w_sizes(wdt, G * 2 * F, d)
+    n2, _, ns2 = _w_sizes(wdt, G * d, F)
     return MoeFfn(
-        d, F, G, max_rows, MOE_DTYPE_FP8_E4M3 if fp8 else MOE_DTYPE_F32,
+        d, F, G, max_rows, wdt,
         _ptr(group_offsets, "group_offsets", torch.int32, G + 1),
         _ptr(row_src, "row_src", torch.int32, max_rows), src_div, a_rows,
         _ptr(a, "a", wd, a_rows * d),
         _ptr(a_scale, "a_scale", torch.float32, a_rows) if fp8 else None,
-        _ptr(w13, "w13", wd, G * 2 * F * d),
-        _ptr(w13_scale, "w13_scale", torch.float32, G * 2 * F) if fp8 else None,
-        _ptr(w2, "w2", wd, G * d * F),
-        _ptr(w2_scale, "w2_scale", torch.float32, G * d) if fp8 else None,
+        _ptr(w13, "w13", wd, n13),
+        _ptr(w13_scale, "w13_scale", sd, ns13) if fp8 else None,
+        _ptr(w2, "w2", wd, n2),
+        _ptr(w2_scale, "w2_scale", sd, ns2) if fp8 else None,
         _ptr(out, "out", torch.bfloat16 if fp8 else torch.float32, max_rows * d),
         _ptr(h_out, "h_out", wd, max_rows * F),
         _ptr(h_scale_out, "h_scale_out", torch.float32, max_rows * (F // 128)) if fp8 else None)
@@ -254,14 +274,18 @@ def make_weights(s: MoeShape, w_router, router_bias, w13, w13_scale, w2, w2_scal
     fp8 = _is_fp8(s)
     wd, ad = _w_dtype(s), _act_dtype(s)
     f32 = torch.float32
+    n13, sd, ns13 = _w_sizes(s.w_dtype, E * 2 * F, d)
+    n2, _, ns2 = _w_sizes(s.w_dtype, E * d, F)
+    nh13, _, nhs13 = _w_sizes(s.w_dtype, 2 * Fs, d)
+    nh2, _, nhs2 = _w_sizes(s.w_dtype, d, Fs)
     return MoeWeights(
         _ptr(w_router, "w_router", ad, E * d), _ptr(router_bias, "router_bias", f32, E),
-        _ptr(w13, "w13", wd, E * 2 * F * d), _ptr(w13_scale, "w13_scale", f32, E * 2 * F) if fp8 else None,
-        _ptr(w2, "w2", wd, E * d * F), _ptr(w2_scale, "w2_scale", f32, E * d) if fp8 else None,
-        _ptr(ws13, "ws13", wd, 2 * Fs * d) if Fs else None,
-        _ptr(ws13_scale, "ws13_scale", f32, 2 * Fs) if (Fs and fp8) else None,
-        _ptr(ws2, "ws2", wd, d * Fs) if Fs else None,
-        _ptr(ws2_scale, "ws2_scale", f32, d) if (Fs and fp8) else None)
+        _ptr(w13, "w13", wd, n13), _ptr(w13_scale, "w13_scale", sd, ns13) if fp8 else None,
+        _ptr(w2, "w2", wd, n2), _ptr(w2_scale, "w2_scale", sd, ns2) if fp8 else None,
+        _ptr(ws13, "ws13", wd, nh13) if Fs else None,
+        _ptr(ws13_scale, "ws13_scale", sd, nhs13) if (Fs and fp8) else None,
+        _ptr(ws2, "ws2", wd, nh2) if Fs else None,
+        _ptr(ws2_scale, "ws2_scale", sd, nhs2) if (Fs and fp8) else None)
 
 
 def moe_layer_forward(s: MoeShape, weights: MoeWeights, x, y, topk_ids, topk_w, workspace,

@@ -19,13 +19,17 @@ moe_status_t check_shape(const moe_shape_t* s) {
   if (s->F_shared != 0 && !is_dim(s->F_shared, MOE_MAX_F)) return MOE_ERR_INVALID_ARG;
   if (s->E < 1 || s->E > MOE_MAX_E) return MOE_ERR_INVALID_ARG;
   if (s->k < 1 || s->k > s->E || s->k > MOE_MAX_K) return MOE_ERR_INVALID_ARG;
-  const bool fp8 = s->act_dtype == MOE_DTYPE_BF16 && s->w_dtype == MOE_DTYPE_FP8_E4M3;
+  const bool fp8 = s->act_dtype == MOE_DTYPE_BF16 &&
+                   (s->w_dtype == MOE_DTYPE_FP8_E4M3 || s->w_dtype == MOE_DTYPE_MXFP4);
   const bool f32 = s->act_dtype == MOE_DTYPE_F32 && s->w_dtype == MOE_DTYPE_F32;
   if (!fp8 && !f32) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
-bool is_fp8(const moe_shape_t* s) { return s->w_dtype == MOE_DTYPE_FP8_E4M3; }
+// The quantised path: bf16 activations, FP8 activation codes in the GEMMs,
+// FP8 or MXFP4 weights.
+bool is_fp8(const moe_shape_t* s) { return s->w_dtype != MOE_DTYPE_F32; }
+bool is_w4(int w_dtype) { return w_dtype == MOE_DTYPE_MXFP4; }
 
 bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 bool al256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255) == 0; }
@@ -51,25 +55,37 @@ moe_status_t check_ffn(const moe_ffn_t* f) {
   if (f->num_groups < 1 || f->num_groups > 1023) return MOE_ERR_INVALID_ARG;
   if (f->max_rows < 0 || f->max_rows > MOE_MAX_T * MOE_MAX_K) return MOE_ERR_INVALID_ARG;
   if (f->src_div < 1 || f->a_rows < 0) return MOE_ERR_INVALID_ARG;
-  if (f->w_dtype != MOE_DTYPE_FP8_E4M3 && f->w_dtype != MOE_DTYPE_F32) return MOE_ERR_UNSUPPORTED;
+  if (f->w_dtype != MOE_DTYPE_FP8_E4M3 && f->w_dtype != MOE_DTYPE_MXFP4 &&
+      f->w_dtype != MOE_DTYPE_F32)
+    return MOE_ERR_UNSUPPORTED;
   if (f->max_rows == 0) return MOE_OK;
   if (f->a_rows < 1) return MOE_ERR_INVALID_ARG;
   if (!f->group_offsets || !f->a || !f->w13 || !f->w2 || !f->out) return MOE_ERR_INVALID_ARG;
   if (!al16(f->a) || !al16(f->w13) || !al16(f->w2) || !al16(f->out) || !al16(f->h_out))
     return MOE_ERR_INVALID_ARG;
-  if (f->w_dtype == MOE_DTYPE_FP8_E4M3 && (!f->a_scale || !f->w13_scale || !f->w2_scale))
+  if (f->w_dtype != MOE_DTYPE_F32 && (!f->a_scale || !f->w13_scale || !f->w2_scale))
+    return MOE_ERR_INVALID_ARG;
+  if (is_w4(f->w_dtype) && (!al16(f->w13_scale) || !al16(f->w2_scale)))
     return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
 
-FfnSet make_set(const void* w13, const float* s13, const void* w2, const float* s2,
+// Weight pointers of one set; scales are float32 channel scales (FP8) or E8M0
+// block-scale bytes (MXFP4, w4).
+FfnSet make_set(const void* w13, const void* s13, const void* w2, const void* s2, bool w4,
                 const int32_t* offsets, const int32_t* row_src, int src_div, int G, int F,
                 int rows_fixed, int max_rows, void* out) {
   FfnSet S{};
   S.w13 = static_cast<const uint8_t*>(w13);
-  S.s13 = s13;
   S.w2 = static_cast<const uint8_t*>(w2);
-  S.s2 = s2;
+  S.w4 = w4 ? 1 : 0;
+  if (w4) {
+    S.e13 = static_cast<const uint8_t*>(s13);
+    S.e2 = static_cast<const uint8_t*>(s2);
+  } else {
+    S.s13 = static_cast<const float*>(s13);
+    S.s2 = static_cast<const float*>(s2);
+  }
   S.offsets = offsets;
   S.row_src = row_src;
   S.src_div = src_div;
@@ -132,11 +148,12 @@ LayerWs layer_ws(const moe_shape_t* s, void* base, FfnCall* call) {
   FfnCall c{};
   c.d = s->d;
   c.nsets = s->F_shared > 0 ? 2 : 1;
-  c.set[0] = make_set(nullptr, nullptr, nullptr, nullptr, L.offsets, L.sorted_pair, s->k, s->E,
-                      s->F, 0, s->T * s->k, L.expert_out);
+  const bool w4 = is_w4(s->w_dtype);
+  c.set[0] = make_set(nullptr, nullptr, nullptr, nullptr, w4, L.offsets, L.sorted_pair, s->k,
+                      s->E, s->F, 0, s->T * s->k, L.expert_out);
   if (c.nsets > 1)
-    c.set[1] = make_set(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 1, 1, s->F_shared,
-                        s->T, s->T, L.shared_out);
+    c.set[1] = make_set(nullptr, nullptr, nullptr, nullptr, w4, nullptr, nullptr, 1, 1,
+                        s->F_shared, s->T, s->T, L.shared_out);
   carve_ffn(c, fp8, cv, &L.tiles);
   L.bytes = cv.off;
   if (call) *call = c;
@@ -193,8 +210,9 @@ static FfnCall ffn_call(const moe_ffn_t* f) {
   c.a = f->a;
   c.a_scale = f->a_scale;
   c.nsets = 1;
-  c.set[0] = make_set(f->w13, f->w13_scale, f->w2, f->w2_scale, f->group_offsets, f->row_src,
-                      f->src_div, f->num_groups, f->F, 0, f->max_rows, f->out);
+  c.set[0] = make_set(f->w13, f->w13_scale, f->w2, f->w2_scale, is_w4(f->w_dtype),
+                      f->group_offsets, f->row_src, f->src_div, f->num_groups, f->F, 0,
+                      f->max_rows, f->out);
   return c;
 }
 
@@ -205,7 +223,7 @@ moe_status_t moe_grouped_ffn_workspace_size(const moe_ffn_t* ffn, size_t* bytes)
   FfnCall c = ffn_call(ffn);
   Carve cv(nullptr);
   void* tiles;
-  *bytes = carve_ffn(c, ffn->w_dtype == MOE_DTYPE_FP8_E4M3, cv, &tiles);
+  *bytes = carve_ffn(c, ffn->w_dtype != MOE_DTYPE_F32, cv, &tiles);
   return MOE_OK;
 }
 
@@ -246,7 +264,7 @@ moe_status_t moe_grouped_ffn(const moe_ffn_t* f, void* workspace, size_t workspa
   moe_status_t st = check_ffn(f);
   if (st != MOE_OK) return st;
   if (f->max_rows == 0) return MOE_OK;
-  const bool fp8 = f->w_dtype == MOE_DTYPE_FP8_E4M3;
+  const bool fp8 = f->w_dtype != MOE_DTYPE_F32;
   FfnCall c = ffn_call(f);
   {
     Carve probe(nullptr);
@@ -307,8 +325,12 @@ moe_status_t moe_layer_forward_events(const moe_shape_t* s, const moe_weights_t*
     return MOE_ERR_INVALID_ARG;
   if (s->F_shared > 0 && (!al16(wt->ws13) || !al16(wt->ws2))) return MOE_ERR_INVALID_ARG;
   const bool fp8 = is_fp8(s);
+  const bool w4 = is_w4(s->w_dtype);
   if (fp8 && (!wt->w13_scale || !wt->w2_scale)) return MOE_ERR_INVALID_ARG;
   if (s->F_shared > 0 && (!wt->ws13 || !wt->ws2 || (fp8 && (!wt->ws13_scale || !wt->ws2_scale))))
+    return MOE_ERR_INVALID_ARG;
+  if (w4 && (!al16(wt->w13_scale) || !al16(wt->w2_scale) ||
+             (s->F_shared > 0 && (!al16(wt->ws13_scale) || !al16(wt->ws2_scale)))))
     return MOE_ERR_INVALID_ARG;
   const size_t need = layer_ws(s, nullptr, nullptr).bytes;
   if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255))
@@ -323,17 +345,26 @@ moe_status_t moe_layer_forward_events(const moe_shape_t* s, const moe_weights_t*
   c.a_rows = s->T;
   c.a = fp8 ? static_cast<const void*>(L.xq) : x;
   c.a_scale = L.xs;
-  FfnSet& R = c.set[0];
-  R.w13 = static_cast<const uint8_t*>(wt->w13);
-  R.s13 = wt->w13_scale;
-  R.w2 = static_cast<const uint8_t*>(wt->w2);
-  R.s2 = wt->w2_scale;
+  auto set_weights = [&](FfnSet& S, const void* w13, const void* s13, const void* w2,
+                         const void* s2) {
+    S = make_set(w13, s13, w2, s2, w4, S.offsets, S.row_src, S.src_div, S.G, S.F, S.rows_fixed,
+                 S.max_rows, S.out);
+  };
+  {
+    FfnSet& R = c.set[0];
+    uint8_t* h = R.h;
+    float* hs = R.h_scale;
+    set_weights(R, wt->w13, wt->w13_scale, wt->w2, wt->w2_scale);
+    R.h = h;
+    R.h_scale = hs;
+  }
   if (c.nsets > 1) {
     FfnSet& Sh = c.set[1];
-    Sh.w13 = static_cast<const uint8_t*>(wt->ws13);
-    Sh.s13 = wt->ws13_scale;
-    Sh.w2 = static_cast<const uint8_t*>(wt->ws2);
-    Sh.s2 = wt->ws2_scale;
+    uint8_t* h = Sh.h;
+    float* hs = Sh.h_scale;
+    set_weights(Sh, wt->ws13, wt->ws13_scale, wt->ws2, wt->ws2_scale);
+    Sh.h = h;
+    Sh.h_scale = hs;
   }
   const int bm = choose_bm(ceil_div(s->T * s->k, s->E));
 

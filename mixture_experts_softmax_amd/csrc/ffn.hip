@@ -15,6 +15,8 @@
 // same group -- run on the same XCD (blocks are dealt to the 8 XCDs in turn),
 // so a weight tile read by several M tiles, and a group's activation rows, are
 // served from that XCD's L2.
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 #include "tiles.h"
@@ -122,6 +124,45 @@ __device__ inline v8i glb_bfrag(const uint8_t* p) {
   return pack8(lo, hi);
 }
 
+// MXFP4 weights (OCP Microscaling: E2M1 elements, one E8M0 scale per 32).
+// With the A fragment above, lane group j of the FP8 operand holds K
+// [16 j, +16) and [64 + 16 j, +16) of the step, which the MFMA pairs with
+// K [32 j, +32) of an FP4 operand: 16 packed bytes, low nibble first, one
+// contiguous run of one scale block. So a lane reads 16 bytes at packed offset
+// 16 j of its row's 64-byte step and the one scale byte of block 4 kt + j,
+// which the instruction applies to that lane's 32 elements.
+struct Fp4Frag {
+  v4i w;
+  int s;  // E8M0 scale in the low byte
+};
+
+template <bool W4>
+using BFrag = typename std::conditional<W4, Fp4Frag, v8i>::type;
+
+// Weight bytes per row and K step (128 K elements).
+template <bool W4>
+constexpr int kstep_bytes() { return W4 ? kBK / 2 : kBK; }
+
+// Fragment of K step kt. p: the lane's row at its lane-group offset
+// ((lane / 16) * 16 bytes); e (MXFP4): the row's scale bytes + lane / 16.
+template <bool W4>
+__device__ inline BFrag<W4> load_bfrag(const uint8_t* p, const uint8_t* e, int kt) {
+  if constexpr (W4)
+    return Fp4Frag{*reinterpret_cast<const v4i*>(p + kt * (kBK / 2)), (int)e[kt * 4]};
+  else
+    return glb_bfrag(p + kt * kBK);
+}
+
+// E4M3 activations x E4M3 weights, or x MXFP4 weights (A scale 2^0, B scale
+// per lane from the fragment; the FP4 operand occupies the low 4 registers).
+__device__ inline v4f mfma_w(const v8i& a, const v8i& b, const v4f& c) {
+  return mfma_fp8_16x16x128(a, b, c);
+}
+__device__ inline v4f mfma_w(const v8i& a, const Fp4Frag& b, const v4f& c) {
+  const v8i bw = v8i{b.w[0], b.w[1], b.w[2], b.w[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bw, c, 0, 4, 0, 127, 0, b.s);
+}
+
 // The fields of set `sid` (0 or 1), read field by field from the kernel
 // arguments so the compiler keeps them in scalar registers.
 struct SetView {
@@ -129,6 +170,8 @@ struct SetView {
   const float* s13;
   const uint8_t* w2;
   const float* s2;
+  const uint8_t* e13;
+  const uint8_t* e2;
   const int32_t* row_src;
   int src_div, F;
   uint8_t* h;
@@ -142,6 +185,8 @@ __device__ inline SetView set_view(const FfnCall& c, int sid) {
   v.s13 = sid ? c.set[1].s13 : c.set[0].s13;
   v.w2 = sid ? c.set[1].w2 : c.set[0].w2;
   v.s2 = sid ? c.set[1].s2 : c.set[0].s2;
+  v.e13 = sid ? c.set[1].e13 : c.set[0].e13;
+  v.e2 = sid ? c.set[1].e2 : c.set[0].e2;
   v.row_src = sid ? c.set[1].row_src : c.set[0].row_src;
   v.src_div = sid ? c.set[1].src_div : c.set[0].src_div;
   v.F = sid ? c.set[1].F : c.set[0].F;
@@ -224,9 +269,11 @@ __device__ inline void gateup_epilogue(v4f (&acc)[MS][2 * NS], const float* sxl,
 // [32 wn, 32 wn + 32) of rows [wm BM/WM, (wm + 1) BM/WM). A (activation rows,
 // gathered through the permutation) is staged through LDS, double buffered
 // and XOR-swizzled; each wave streams its own weight rows straight into a
-// register ring PD K-steps deep.
+// register ring PD K-steps deep. W4: MXFP4 weights (half the bytes per step,
+// so the ring is twice as deep for the same bytes in flight; no channel
+// scales).
 // ---------------------------------------------------------------------------
-template <int BM, int WM, int KTC>
+template <int BM, int WM, int KTC, bool W4>
 __global__ __launch_bounds__(kNWaves * WM * kWave) void gateup_fp8_kernel(
     FfnCall c, const TileHeader* __restrict__ hdr, const TileEntry* __restrict__ list) {
   constexpr int NTH = kNWaves * WM * kWave;
@@ -237,7 +284,7 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void gateup_fp8_kernel(
   constexpr int NB = 2 * NS;        // weight subtiles per wave (gate, up)
   constexpr int CH = BM * (kBK / 16);
   constexpr int CPT = (CH + NTH - 1) / NTH;
-  constexpr int PD = prefetch_depth<BMW, 64>();
+  constexpr int PD = prefetch_depth<BMW, 64>() * (W4 && BMW <= 32 ? 2 : 1);
 
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * kBK];
   __shared__ float sxl[BM];
@@ -268,25 +315,32 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void gateup_fp8_kernel(
     a_dst[i] = swz(r, c16);
     if (ch < CH && c16 == 0) sxl[r] = c.a_scale[src];
   }
-  // weight rows of this wave
-  const uint8_t* w13 = S.w13 + (size_t)g * 2 * F * d;
+  // weight rows of this wave (and, MXFP4, their block scales)
+  const size_t wrb = W4 ? d / 2 : d;  // weight bytes per row
+  const uint8_t* w13 = S.w13 + (size_t)g * 2 * F * wrb;
   const uint8_t* b_src[NB];
+  const uint8_t* e_src[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
     const int hc = ntile * kHN + wn * WN + (j % NS) * 16 + (lane & 15);
     const int wrow = (j < NS) ? hc : F + hc;
-    b_src[j] = w13 + (size_t)wrow * d + (lane >> 4) * 16;
+    b_src[j] = w13 + (size_t)wrow * wrb + (lane >> 4) * 16;
+    e_src[j] = W4 ? S.e13 + ((size_t)g * 2 * F + wrow) * (d / 32) + (lane >> 4) : nullptr;
   }
   // weight scales of this wave's columns, loaded now so that the epilogue
   // waits on no load (its stores sit under row guards, where a pending load
   // would make every store wait for all earlier ones)
-  const float* s13 = S.s13 + (size_t)g * 2 * F;
   float sg[NS], su[NS];
 #pragma unroll
   for (int jj = 0; jj < NS; ++jj) {
     const int hc = ntile * kHN + wn * WN + jj * 16 + (lane & 15);
-    sg[jj] = s13[hc];
-    su[jj] = s13[F + hc];
+    if constexpr (W4) {
+      sg[jj] = 1.f;
+      su[jj] = 1.f;
+    } else {
+      sg[jj] = S.s13[(size_t)g * 2 * F + hc];
+      su[jj] = S.s13[(size_t)g * 2 * F + F + hc];
+    }
   }
 
   v4f acc[MS][NB];
@@ -305,11 +359,11 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void gateup_fp8_kernel(
   // the compiler's wait counts stay exact.
   const int KT = KTC > 0 ? KTC : d / kBK;  // KTC: K steps known at compile time
   v4i a_stage[CPT];
-  v8i bq[PD][NB];
+  BFrag<W4> bq[PD][NB];
 #pragma unroll
   for (int s = 0; s < PD; ++s)
 #pragma unroll
-    for (int j = 0; j < NB; ++j) bq[s][j] = glb_bfrag(b_src[j] + min(s, KT - 1) * kBK);
+    for (int j = 0; j < NB; ++j) bq[s][j] = load_bfrag<W4>(b_src[j], e_src[j], min(s, KT - 1));
 #pragma unroll
   for (int i = 0; i < CPT; ++i) a_stage[i] = *reinterpret_cast<const v4i*>(a_src[i]);
 #pragma unroll
@@ -334,7 +388,7 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void gateup_fp8_kernel(
         for (int i = 0; i < MS; ++i) {
           const v8i af = lds_afrag(lds_a[cur] + rbase * kBK, i, lane);
 #pragma unroll
-          for (int j = 0; j < NB; ++j) acc[i][j] = mfma_fp8_16x16x128(af, bq[s][j], acc[i][j]);
+          for (int j = 0; j < NB; ++j) acc[i][j] = mfma_w(af, bq[s][j], acc[i][j]);
         }
         // A for step kt+1 into the other buffer (its readers finished at the
         // barrier ending step kt-1), then fetch A for step kt+2
@@ -347,7 +401,7 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void gateup_fp8_kernel(
         for (int i = 0; i < CPT; ++i)
           a_stage[i] = *reinterpret_cast<const v4i*>(a_src[i] + ka * kBK);
 #pragma unroll
-        for (int j = 0; j < NB; ++j) bq[s][j] = glb_bfrag(b_src[j] + kb * kBK);
+        for (int j = 0; j < NB; ++j) bq[s][j] = load_bfrag<W4>(b_src[j], e_src[j], kb);
         __syncthreads();
         // keep each step's instructions in its step (bounds register pressure
         // of the unrolled loop)
@@ -510,7 +564,7 @@ __global__ __launch_bounds__(8 * kWave) void gateup_fp8_lds_kernel(
 // [wm BM/WM, (wm + 1) BM/WM). Each 128-wide K step is one h block: its MFMA
 // partial is scaled by s_h[row][block] and accumulated.
 // ---------------------------------------------------------------------------
-template <int BM, int WM, int KTC>
+template <int BM, int WM, int KTC, bool W4>
 __global__ __launch_bounds__(kNWaves * WM * kWave) void down_fp8_kernel(
     FfnCall c, const TileHeader* __restrict__ hdr, const TileEntry* __restrict__ list) {
   constexpr int NTH = kNWaves * WM * kWave;
@@ -519,7 +573,7 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void down_fp8_kernel(
   constexpr int NB = 4;  // 16-channel subtiles per wave
   constexpr int CH = BM * (kBK / 16);
   constexpr int CPT = (CH + NTH - 1) / NTH;
-  constexpr int PD = prefetch_depth<BMW, 32>();
+  constexpr int PD = prefetch_depth<BMW, 32>() + (W4 ? 1 : 0);
 
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * kBK];
   __shared__ float hsl[2][BM];
@@ -547,18 +601,22 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void down_fp8_kernel(
   // per-row h scales: thread r < BM fetches s_h[row r][kt]
   const float* hs_src = S.h_scale + (size_t)(te.row0 + min(tid, te.nrows - 1)) * hblocks;
 
-  const uint8_t* w2 = S.w2 + (size_t)g * d * F;
+  const size_t wrb = W4 ? F / 2 : F;  // weight bytes per row
+  const uint8_t* w2 = S.w2 + (size_t)g * d * wrb;
   const uint8_t* b_src[NB];
+  const uint8_t* e_src[NB];
   int mcol[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
     mcol[j] = ntile * kDownBN + wn * (NB * 16) + j * 16 + (lane & 15);
-    b_src[j] = w2 + (size_t)min(mcol[j], d - 1) * F + (lane >> 4) * 16;
+    const size_t row = min(mcol[j], d - 1);
+    b_src[j] = w2 + row * wrb + (lane >> 4) * 16;
+    e_src[j] = W4 ? S.e2 + ((size_t)g * d + row) * (F / 32) + (lane >> 4) : nullptr;
   }
   // channel scales, loaded now so that the epilogue waits on no load
   float s2v[NB];
 #pragma unroll
-  for (int j = 0; j < NB; ++j) s2v[j] = S.s2[(size_t)g * d + min(mcol[j], d - 1)];
+  for (int j = 0; j < NB; ++j) s2v[j] = W4 ? 1.f : S.s2[(size_t)g * d + min(mcol[j], d - 1)];
 
   v4f acc[MS][NB];
 #pragma unroll
@@ -571,11 +629,11 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void down_fp8_kernel(
   const int KT = KTC > 0 ? KTC : F / kBK;  // KTC: K steps known at compile time
   v4i a_stage[CPT];
   float hs_stage;
-  v8i bq[PD][NB];
+  BFrag<W4> bq[PD][NB];
 #pragma unroll
   for (int s = 0; s < PD; ++s)
 #pragma unroll
-    for (int j = 0; j < NB; ++j) bq[s][j] = glb_bfrag(b_src[j] + min(s, KT - 1) * kBK);
+    for (int j = 0; j < NB; ++j) bq[s][j] = load_bfrag<W4>(b_src[j], e_src[j], min(s, KT - 1));
 #pragma unroll
   for (int i = 0; i < CPT; ++i) a_stage[i] = *reinterpret_cast<const v4i*>(a_src[i]);
   hs_stage = hs_src[0];
@@ -603,7 +661,7 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void down_fp8_kernel(
           v4f part[NB];
 #pragma unroll
           for (int j = 0; j < NB; ++j)
-            part[j] = mfma_fp8_16x16x128(af, bq[s][j], v4f{0.f, 0.f, 0.f, 0.f});
+            part[j] = mfma_w(af, bq[s][j], v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const float hs = hsl[cur][rbase + i * 16 + 4 * (lane >> 4) + q];
@@ -622,7 +680,7 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void down_fp8_kernel(
           a_stage[i] = *reinterpret_cast<const v4i*>(a_src[i] + ka * kBK);
         hs_stage = hs_src[ka];
 #pragma unroll
-        for (int j = 0; j < NB; ++j) bq[s][j] = glb_bfrag(b_src[j] + kb * kBK);
+        for (int j = 0; j < NB; ++j) bq[s][j] = load_bfrag<W4>(b_src[j], e_src[j], kb);
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -815,7 +873,7 @@ __global__ __launch_bounds__(8 * kWave) void down_fp8_lds_kernel(
 // the K loop has no barrier. With NW waves, wave w owns channels
 // [w 256/NW, (w + 1) 256/NW) of every N tile, over all BM rows.
 // ---------------------------------------------------------------------------
-template <int BM, int KTC, int NTW, int NW>
+template <int BM, int KTC, int NTW, int NW, bool W4>
 __global__ __launch_bounds__(NW * kWave) void down_fp8_resident_kernel(
     FfnCall c, const TileHeader* __restrict__ hdr, const TileEntry* __restrict__ list) {
   constexpr int NTH = NW * kWave;
@@ -825,7 +883,8 @@ __global__ __launch_bounds__(NW * kWave) void down_fp8_resident_kernel(
   constexpr int CPT = (CHK * KTC + NTH - 1) / NTH;
   constexpr int GRP = 8;                 // slab chunks per thread per load group
   constexpr int NSTEP = NTW * KTC;
-  constexpr int PD = NSTEP < 4 ? NSTEP : 4;
+  constexpr int PDM = W4 ? 6 : 4;  // MXFP4: half the bytes per step, deeper ring
+  constexpr int PD = NSTEP < PDM ? NSTEP : PDM;
   constexpr int HPT = (BM * KTC + NTH - 1) / NTH;
   static_assert(BM * KTC * kBK <= 65536, "h slab exceeds the LDS budget");
 
@@ -841,23 +900,27 @@ __global__ __launch_bounds__(NW * kWave) void down_fp8_resident_kernel(
   const int F = S.F;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wn = tid / kWave;
 
-  const uint8_t* w2 = S.w2 + (size_t)g * d * F + (lane >> 4) * 16;
+  const size_t wrb = W4 ? F / 2 : F;  // weight bytes per row
+  const uint8_t* w2 = S.w2 + (size_t)g * d * wrb + (lane >> 4) * 16;
+  const uint8_t* e2 = W4 ? S.e2 + (size_t)g * d * (F / 32) + (lane >> 4) : nullptr;
   // output channel of (N tile n of this workgroup, subtile j) for this lane
   auto mcol = [&](int n, int j) {
     return (nt0 + n) * kDownBN + wn * (NB * 16) + j * 16 + (lane & 15);
   };
-  // weight fragment address of step s (N tile s / KT, K step s % KT); steps
-  // past the last N tile re-read its rows (never used)
-  auto bsrc = [&](int st, int j) {
+  // weight fragment of step s (N tile s / KT, K step s % KT); steps past the
+  // last N tile re-read its rows (never used)
+  auto bfrag = [&](int st, int j) {
     const int n = min(st / KTC, dnt - 1 - nt0);
-    return w2 + (size_t)min(mcol(n, j), d - 1) * F + (st % KTC) * kBK;
+    const size_t row = min(mcol(n, j), d - 1);
+    return load_bfrag<W4>(w2 + row * wrb, W4 ? e2 + row * (F / 32) : nullptr, st % KTC);
   };
   // channel scales of every N tile, loaded now so the epilogues wait on no load
   float s2v[NTW][NB];
 #pragma unroll
   for (int n = 0; n < NTW; ++n)
 #pragma unroll
-    for (int j = 0; j < NB; ++j) s2v[n][j] = S.s2[(size_t)g * d + min(mcol(n, j), d - 1)];
+    for (int j = 0; j < NB; ++j)
+      s2v[n][j] = W4 ? 1.f : S.s2[(size_t)g * d + min(mcol(n, j), d - 1)];
   float hv[HPT];
 #pragma unroll
   for (int i = 0; i < HPT; ++i) {
@@ -869,7 +932,7 @@ __global__ __launch_bounds__(NW * kWave) void down_fp8_resident_kernel(
   // 16-byte column); rows past the tile's end repeat its last row and are
   // never stored). The weight ring is issued after the first group, so the
   // first group's stores wait for that group alone.
-  v8i bq[PD][NB];
+  BFrag<W4> bq[PD][NB];
 #pragma unroll
   for (int g0 = 0; g0 < CPT; g0 += GRP) {
     v4i st[GRP];
@@ -889,7 +952,7 @@ __global__ __launch_bounds__(NW * kWave) void down_fp8_resident_kernel(
 #pragma unroll
       for (int s = 0; s < PD; ++s)
 #pragma unroll
-        for (int j = 0; j < NB; ++j) bq[s][j] = glb_bfrag(bsrc(s, j));
+        for (int j = 0; j < NB; ++j) bq[s][j] = bfrag(s, j);
     }
 #pragma unroll
     for (int i = 0; i < GRP; ++i)
@@ -920,7 +983,7 @@ __global__ __launch_bounds__(NW * kWave) void down_fp8_resident_kernel(
       v4f part[NB];
 #pragma unroll
       for (int j = 0; j < NB; ++j)
-        part[j] = mfma_fp8_16x16x128(af, bq[s][j], v4f{0.f, 0.f, 0.f, 0.f});
+        part[j] = mfma_w(af, bq[s][j], v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float hs = hsl[kt][i * 16 + 4 * (lane >> 4) + q];
@@ -930,7 +993,7 @@ __global__ __launch_bounds__(NW * kWave) void down_fp8_resident_kernel(
     }
     if (st + PD < NSTEP) {
 #pragma unroll
-      for (int j = 0; j < NB; ++j) bq[s][j] = glb_bfrag(bsrc(st + PD, j));
+      for (int j = 0; j < NB; ++j) bq[s][j] = bfrag(st + PD, j);
     }
     // keep each step's loads and scaled accumulation in the step (the
     // scheduler would otherwise sink the loads towards their use, shortening
@@ -1013,25 +1076,28 @@ __global__ __launch_bounds__(256) void down_f32_kernel(FfnCall c, int sid) {
 template <int BM>
 constexpr int waves_m() { return BM >= 64 ? 2 : 1; }
 
-template <int BM, int KTU, int BMD, int KTD>
+// W4: MXFP4 weights, which take the register-streaming kernels only (the
+// tall-tile LDS kernels stage FP8 weight rows).
+template <int BM, int KTU, int BMD, int KTD, bool W4>
 hipError_t launch_gemms_bm(const FfnCall& c, TileHeader* hdr, TileEntry* up, TileEntry* dn,
                            size_t cap_u, size_t cap_d, hipStream_t s, const StepEvents& ev) {
   const size_t cu = align_up(cap_u * up_ntiles_max(c), kXcds);
   const size_t cd = align_up(cap_d * down_ntiles(c.d), kXcds);
   constexpr int WU = waves_m<BM>(), WD = waves_m<BMD>();
+  static_assert(!W4 || BMD <= 128, "MXFP4 down tiles are at most 128 rows");
   ev.mark(true, MOE_STEP_GATE_UP, s);
   if (cu > 0) {
-    if constexpr (KTU > 0 && BM >= 128)  // tall tiles: both operands through LDS
+    if constexpr (!W4 && KTU > 0 && BM >= 128)  // tall tiles: both operands through LDS
       hipLaunchKernelGGL((gateup_fp8_lds_kernel<BM, KTU>), dim3((unsigned)cu), dim3(8 * kWave),
                          0, s, c, hdr, up);
-    else
-      hipLaunchKernelGGL((gateup_fp8_kernel<BM, WU, KTU>), dim3((unsigned)cu),
-                         dim3(kNWaves * WU * kWave), 0, s, c, hdr, up);
+    else  // (a fully unrolled K loop of tall tiles would spill: looped there)
+      hipLaunchKernelGGL((gateup_fp8_kernel<BM, WU, (BM >= 128 ? 0 : KTU), W4>),
+                         dim3((unsigned)cu), dim3(kNWaves * WU * kWave), 0, s, c, hdr, up);
   }
   ev.mark(false, MOE_STEP_GATE_UP, s);
   ev.mark(true, MOE_STEP_DOWN, s);
   if (cap_d > 0) {
-    if constexpr (KTD > 0 && BMD >= 128) {
+    if constexpr (!W4 && KTD > 0 && BMD >= 128) {
       // tall tiles: both operands through LDS, 16 steps per workgroup
       constexpr int NTW = KTD >= 16 ? 1 : 16 / KTD;
       const size_t cdl = align_up(cap_d * ceil_div(down_ntiles(c.d), NTW), kXcds);
@@ -1041,10 +1107,10 @@ hipError_t launch_gemms_bm(const FfnCall& c, TileHeader* hdr, TileEntry* up, Til
       // resident h slab; 64-row tiles: 8 waves, 4 N tiles per workgroup
       constexpr int NTW = BMD >= 64 ? 4 : 1, NWD = BMD >= 64 ? 8 : 4;
       const size_t cdr = align_up(cap_d * ceil_div(down_ntiles(c.d), NTW), kXcds);
-      hipLaunchKernelGGL((down_fp8_resident_kernel<BMD, KTD, NTW, NWD>), dim3((unsigned)cdr),
+      hipLaunchKernelGGL((down_fp8_resident_kernel<BMD, KTD, NTW, NWD, W4>), dim3((unsigned)cdr),
                          dim3(NWD * kWave), 0, s, c, hdr, dn);
     } else {
-      hipLaunchKernelGGL((down_fp8_kernel<BMD, WD, KTD>), dim3((unsigned)cd),
+      hipLaunchKernelGGL((down_fp8_kernel<BMD, WD, KTD, W4>), dim3((unsigned)cd),
                          dim3(kNWaves * WD * kWave), 0, s, c, hdr, dn);
     }
   }
@@ -1056,26 +1122,46 @@ hipError_t launch_gemms_bm(const FfnCall& c, TileHeader* hdr, TileEntry* up, Til
 // the call: 32 gate/up steps (d = 4096); 8 down steps (F = 1024, every set)
 // for the resident and the tall-tile down kernels, or 16 (F = 2048) for the
 // tall-tile one. Other sizes use the looped kernels.
-template <int BM, int BMD, int KTU>
+template <int BM, int BMD, int KTU, bool W4>
 hipError_t launch_gemms_kd(const FfnCall& c, TileHeader* hdr, TileEntry* up, TileEntry* dn,
                            size_t cap_u, size_t cap_d, hipStream_t s, const StepEvents& ev) {
   const int kdn = down_ksteps(c);
-  if constexpr (BMD <= 64 || BMD >= 128) {
-    if (kdn == 8) return launch_gemms_bm<BM, KTU, BMD, 8>(c, hdr, up, dn, cap_u, cap_d, s, ev);
+  if constexpr (BMD <= 64 || (!W4 && BMD >= 128)) {
+    if (kdn == 8)
+      return launch_gemms_bm<BM, KTU, BMD, 8, W4>(c, hdr, up, dn, cap_u, cap_d, s, ev);
   }
-  if constexpr (BMD >= 128) {
-    if (kdn == 16) return launch_gemms_bm<BM, KTU, BMD, 16>(c, hdr, up, dn, cap_u, cap_d, s, ev);
+  if constexpr (!W4 && BMD >= 128) {
+    if (kdn == 16)
+      return launch_gemms_bm<BM, KTU, BMD, 16, W4>(c, hdr, up, dn, cap_u, cap_d, s, ev);
   }
   if constexpr (BMD <= 128)  // taller down tiles exist only where K is fixed (above)
-    return launch_gemms_bm<BM, KTU, BMD, 0>(c, hdr, up, dn, cap_u, cap_d, s, ev);
+    return launch_gemms_bm<BM, KTU, BMD, 0, W4>(c, hdr, up, dn, cap_u, cap_d, s, ev);
   return hipErrorInvalidValue;
 }
 
-template <int BM, int BMD>
+template <int BM, int BMD, bool W4>
 hipError_t launch_gemms_k(const FfnCall& c, TileHeader* hdr, TileEntry* up, TileEntry* dn,
                           size_t cap_u, size_t cap_d, hipStream_t s, const StepEvents& ev) {
-  if (c.d / kBK == 32) return launch_gemms_kd<BM, BMD, 32>(c, hdr, up, dn, cap_u, cap_d, s, ev);
-  return launch_gemms_kd<BM, BMD, 0>(c, hdr, up, dn, cap_u, cap_d, s, ev);
+  if (c.d / kBK == 32)
+    return launch_gemms_kd<BM, BMD, 32, W4>(c, hdr, up, dn, cap_u, cap_d, s, ev);
+  return launch_gemms_kd<BM, BMD, 0, W4>(c, hdr, up, dn, cap_u, cap_d, s, ev);
+}
+
+template <bool W4>
+hipError_t launch_gemms_w(const FfnCall& c, int bm, TileHeader* hdr, TileEntry* up,
+                          TileEntry* dn, int cu, int cd, hipStream_t s, const StepEvents& ev) {
+  switch (bm) {
+    case 16: return launch_gemms_k<16, 16, W4>(c, hdr, up, dn, cu, cd, s, ev);
+    case 32: return launch_gemms_k<32, 32, W4>(c, hdr, up, dn, cu, cd, s, ev);
+    case 64: return launch_gemms_k<64, 64, W4>(c, hdr, up, dn, cu, cd, s, ev);
+    case 128: return launch_gemms_k<128, 128, W4>(c, hdr, up, dn, cu, cd, s, ev);
+    default:
+      if constexpr (!W4) {
+        if (down_bm(c, bm) == 192)
+          return launch_gemms_k<192, 192, W4>(c, hdr, up, dn, cu, cd, s, ev);
+      }
+      return launch_gemms_k<192, 128, W4>(c, hdr, up, dn, cu, cd, s, ev);
+  }
 }
 
 }  // namespace
@@ -1133,15 +1219,8 @@ hipError_t launch_ffn_gemms(const FfnCall& c, int bm, void* ws, hipStream_t s,
   TileEntry *up, *dn;
   int cu, cd;
   tile_lists(c, bm, ws, &hdr, &up, &dn, &cu, &cd);
-  switch (bm) {
-    case 16: return launch_gemms_k<16, 16>(c, hdr, up, dn, cu, cd, s, ev);
-    case 32: return launch_gemms_k<32, 32>(c, hdr, up, dn, cu, cd, s, ev);
-    case 64: return launch_gemms_k<64, 64>(c, hdr, up, dn, cu, cd, s, ev);
-    case 128: return launch_gemms_k<128, 128>(c, hdr, up, dn, cu, cd, s, ev);
-    default:
-      return down_bm(c, bm) == 192 ? launch_gemms_k<192, 192>(c, hdr, up, dn, cu, cd, s, ev)
-                                   : launch_gemms_k<192, 128>(c, hdr, up, dn, cu, cd, s, ev);
-  }
+  if (c.set[0].w4) return launch_gemms_w<true>(c, bm, hdr, up, dn, cu, cd, s, ev);
+  return launch_gemms_w<false>(c, bm, hdr, up, dn, cu, cd, s, ev);
 }
 
 hipError_t launch_grouped_ffn_fp8(const FfnCall& c, void* tiles_ws, int rows_hint, hipStream_t s,

@@ -52,10 +52,14 @@ hipError_t launch_perm_scan_scatter(const int32_t* ids, int T, int E, int k, uin
 // (G groups, row ranges from a device offsets array, activation rows gathered
 // through row_src) or the shared expert (one group over `rows_fixed` rows).
 struct FfnSet {
-  const uint8_t* w13;    // [G][2F][d] (bytes: FP8 codes, or float32 when f32)
-  const float* s13;      // [G][2F]
-  const uint8_t* w2;     // [G][d][F]
-  const float* s2;       // [G][d]
+  const uint8_t* w13;    // [G][2F][d] (bytes: FP8 codes, or float32 when f32);
+                         // MXFP4: [G][2F][d/2] packed E2M1
+  const float* s13;      // [G][2F] FP8 channel scales (nullptr for MXFP4)
+  const uint8_t* w2;     // [G][d][F]; MXFP4: [G][d][F/2]
+  const float* s2;       // [G][d] (nullptr for MXFP4)
+  const uint8_t* e13;    // MXFP4 E8M0 block scales [G][2F][d/32], else nullptr
+  const uint8_t* e2;     // MXFP4 [G][d][F/32], else nullptr
+  int w4;                // 1: MXFP4 weights
   const int32_t* offsets;  // device [G+1], or nullptr: one group of rows_fixed rows
   const int32_t* row_src;  // gather, nullptr = identity
   int src_div;

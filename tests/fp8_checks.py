@@ -43,12 +43,20 @@ def _dsilu(g):
     return sg * (1.0 + g * (1.0 - sg))
 
 
+def _abs_weights(codes, scale, fmt):
+    """|dequantised weights| [rows][cols]: E4M3 codes times their row's channel
+    scale, or MXFP4 elements times their block's 2^e."""
+    if fmt == "mxfp4":
+        return np.abs(codecs.mxfp4_decode(codes, scale))
+    return np.abs(codecs.e4m3_decode(codes) * np.asarray(scale, np.float64)[:, None])
+
+
 def h_error_bound(xq, s_x, ew):
     """Exact h [R][F] and a bound on |h_kernel - h| from the MFMA model."""
     F = ew.w13.shape[0] // 2
     gu = omoe.gate_up_fp8(xq, s_x, ew)
-    absum = np.abs(codecs.e4m3_decode(xq)) @ np.abs(codecs.e4m3_decode(ew.w13)).T
-    absum *= np.asarray(s_x, np.float64)[:, None] * np.asarray(ew.w13_scale, np.float64)[None, :]
+    absum = np.abs(codecs.e4m3_decode(xq)) @ _abs_weights(ew.w13, ew.w13_scale, ew.fmt).T
+    absum *= np.asarray(s_x, np.float64)[:, None]
     dgu = MFMA_EPS * absum + ROUND_EPS * np.abs(gu)
     g, u = gu[:, :F], gu[:, F:]
     h = omoe.silu(g) * u
@@ -100,5 +108,4 @@ def validate_h(xq, s_x, ew, q_gpu: np.ndarray, s_gpu: np.ndarray):
 def down_effect(dhq: np.ndarray, ew: omoe.ExpertWeights) -> np.ndarray:
     """Largest change of each expert output the h differences can cause:
     |dhq| @ |W2 dequantised|^T, [R][d]."""
-    w2 = np.abs(codecs.e4m3_decode(ew.w2) * np.asarray(ew.w2_scale, np.float64)[:, None])
-    return np.abs(dhq) @ w2.T
+    return np.abs(dhq) @ _abs_weights(ew.w2, ew.w2_scale, ew.fmt).T

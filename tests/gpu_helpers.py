@@ -62,7 +62,7 @@ def run_stepwise(lt: LayerTensors, x=None):
     c = lt.cfg
     x = lt.x if x is None else x
     T, d, E, k, F, Fs = x.shape[0], c.d, c.E, c.k, c.F, c.F_shared
-    fp8 = c.precision == "fp8"
+    fp8 = c.precision != "f32"
     s = shape_of(c, T)
     i32, f32 = torch.int32, torch.float32
     ids = torch.empty((T, k), dtype=i32, device=DEV)
@@ -83,7 +83,8 @@ def run_stepwise(lt: LayerTensors, x=None):
         out = torch.empty((rows, d), dtype=odt, device=DEV)
         h = torch.empty((rows, FF), dtype=hdt, device=DEV)
         hs = torch.empty((rows, FF // 128), dtype=f32, device=DEV) if fp8 else None
-        f = _lib.make_ffn(d, FF, G, rows, fp8, offsets, row_src, div, a, a_s, w13, s13, w2, s2, out, h, hs)
+        f = _lib.make_ffn(d, FF, G, rows, c.precision, offsets, row_src, div, a, a_s, w13, s13, w2, s2,
+                          out, h, hs)
         _lib.moe_grouped_ffn(f, moe_lib.alloc_workspace(_lib.moe_grouped_ffn_workspace_size(f), DEV))
         return out, h, hs
     eo, h, hs = ffn(E, off, sp, k, T * k, F, lt.w13, lt.w13_scale, lt.w2, lt.w2_scale)
@@ -115,7 +116,7 @@ def compare_y(y_gpu: np.ndarray, y_ref: np.ndarray, precision: str, what: str = 
     max_abs = float(diff.max()) if diff.size else 0.0
     den = float(np.sqrt((y_ref ** 2).sum()))
     rel = float(np.sqrt((diff ** 2).sum()) / den) if den > 0 else max_abs
-    lim_abs, lim_rel = (FP8_MAX_ABS, FP8_REL_L2) if precision == "fp8" else (F32_MAX_ABS, F32_REL_L2)
+    lim_abs, lim_rel = (FP8_MAX_ABS, FP8_REL_L2) if precision != "f32" else (F32_MAX_ABS, F32_REL_L2)
     lim = lim_abs + np.asarray(extra_abs, np.float64)
     widened = int((diff > lim_abs).sum())
     say(f"  {what}: max_abs={max_abs:.3e} rel_l2={rel:.3e} (limits {lim_abs:g}, {lim_rel:g}); "

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
     L = _lib.lib()
     for n in header_functions():
         assert hasattr(L, n), n
-    assert _lib.moe_abi_version() == 2
+    assert _lib.moe_abi_version() == 3
 
 
 def fp8_shape(**kw):
@@ -65,7 +65,7 @@ def test_check_shape(kw, status):
 def test_workspace_sizes_for_any_batch(T, d, E):
     """Host-only size queries are defined for every valid shape, the empty
     batch included, and grow with the batch."""
-    for prec in ("fp8", "f32"):
+    for prec in ("fp8", "mxfp4", "f32"):
         s = _lib.shape(T, d, E, min(2, E), 128, 128, prec)
         assert _lib.moe_check_shape(s) == _lib.MOE_OK
         lw, rw, pw = (_lib.moe_layer_workspace_size(s), _lib.moe_route_workspace_size(s),
@@ -78,9 +78,33 @@ def test_workspace_sizes_for_any_batch(T, d, E):
 
 def test_unsupported_dtype_pairs():
     for act, w in [(_lib.MOE_DTYPE_BF16, _lib.MOE_DTYPE_F32), (_lib.MOE_DTYPE_F32, _lib.MOE_DTYPE_FP8_E4M3),
-                   (_lib.MOE_DTYPE_FP8_E4M3, _lib.MOE_DTYPE_FP8_E4M3), (7, 2)]:
+                   (_lib.MOE_DTYPE_FP8_E4M3, _lib.MOE_DTYPE_FP8_E4M3), (7, 2),
+                   (_lib.MOE_DTYPE_F32, _lib.MOE_DTYPE_MXFP4), (_lib.MOE_DTYPE_MXFP4, _lib.MOE_DTYPE_MXFP4)]:
         s = _lib.MoeShape(16, 256, 8, 2, 128, 128, act, w)
         assert _lib.moe_check_shape(s) == _lib.MOE_ERR_UNSUPPORTED
+
+
+def test_mxfp4_shapes_and_workspace():
+    """bf16 activations with MXFP4 expert weights form a supported pair whose
+    layer workspace equals the FP8 path's (same activation codes and h)."""
+    s4 = _lib.shape(64, 4096, 128, 6, 1024, 1024, "mxfp4")
+    assert s4.w_dtype == _lib.MOE_DTYPE_MXFP4 and s4.act_dtype == _lib.MOE_DTYPE_BF16
+    assert _lib.moe_check_shape(s4) == _lib.MOE_OK
+    assert _lib.moe_layer_workspace_size(s4) == _lib.moe_layer_workspace_size(fp8_shape())
+    L = _lib.lib()
+    A = 1 << 40  # a well-aligned stand-in address; never dereferenced
+    need = _lib.moe_layer_workspace_size(s4)
+    fake = C.c_void_p(A)
+    # scales are required, and (byte arrays) must be 16-byte aligned
+    w = _lib.MoeWeights(A, None, A, None, A, A, A, A, A, A)
+    assert L.moe_layer_forward(C.byref(s4), C.byref(w), fake, fake, None, None, fake, need, None) == _lib.MOE_ERR_INVALID_ARG
+    w = _lib.MoeWeights(A, None, A, A + 1, A, A, A, A, A, A)
+    assert L.moe_layer_forward(C.byref(s4), C.byref(w), fake, fake, None, None, fake, need, None) == _lib.MOE_ERR_INVALID_ARG
+    f = _lib.MoeFfn(4096, 1024, 128, 384, _lib.MOE_DTYPE_MXFP4, A, None, 6, 64, A, A, A, A, A, A, A)
+    f8 = _lib.MoeFfn(4096, 1024, 128, 384, _lib.MOE_DTYPE_FP8_E4M3, A, None, 6, 64, A, A, A, A, A, A, A)
+    assert _lib.moe_grouped_ffn_workspace_size(f) == _lib.moe_grouped_ffn_workspace_size(f8)
+    odd = _lib.MoeFfn(4096, 1024, 4, 384, _lib.MOE_DTYPE_MXFP4, A, None, 6, 64, A, A, A, A + 4, A, A, A)
+    assert L.moe_grouped_ffn(C.byref(odd), fake, 1 << 30, None) == _lib.MOE_ERR_INVALID_ARG
 
 
 def test_null_pointers_rejected_before_launch():

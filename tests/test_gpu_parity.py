@@ -16,6 +16,10 @@ pytestmark = pytest.mark.gpu
 SMALL = ["tiny", "f32_ragged", "f32_noshared", "fp8_small", "fp8_ragged", "fp8_noshared",
          "fp8_k1", "fp8_kE", "fp8_wide", "fp8_skew_small"]
 MODEL = ["fp8_model_m16", "fp8_model_m32", "fp8_model_m128", "fp8_model_m192", "fp8_model_f2048"]
+# MXFP4 expert weights: every kernel variant (tile heights 16 to 192, looped
+# and unrolled K loops, resident and looped down GEMMs)
+MX = ["mx_small", "mx_ragged", "mx_model_m16", "mx_model_m32", "mx_model_m64", "mx_model_m192",
+      "mx_model_f2048"]
 
 
 @pytest.fixture(autouse=True)
@@ -34,7 +38,7 @@ def test_route_topk(name):
     T, k, d = cfg.T, cfg.k, cfg.d
     ids = torch.empty((T, k), dtype=torch.int32, device=H.DEV)
     w = torch.empty((T, k), dtype=torch.float32, device=H.DEV)
-    fp8 = cfg.precision == "fp8"
+    fp8 = cfg.precision != "f32"
     xq = torch.empty((T, d), dtype=torch.uint8, device=H.DEV) if fp8 else None
     xs = torch.empty((T,), dtype=torch.float32, device=H.DEV) if fp8 else None
     _lib.moe_route_topk(s, lt.x, lt.w_router, lt.router_bias, ids, w, xq, xs,
@@ -92,7 +96,8 @@ def test_permute_out_of_range_ids_get_no_row():
 
 
 @pytest.mark.parametrize("name", ["fp8_small", "fp8_ragged", "fp8_wide", "fp8_skew_small", "tiny",
-                                  "f32_ragged", "fp8_model_m16", "fp8_model_m128"])
+                                  "f32_ragged", "fp8_model_m16", "fp8_model_m128", "mx_small",
+                                  "mx_ragged", "mx_model_m16", "mx_model_m192"])
 def test_grouped_ffn(name):
     """moe_grouped_ffn on the routed groups and on the shared expert, with the
     oracle's routing and x codes as input; h decisions validated, outputs
@@ -103,7 +108,7 @@ def test_grouped_ffn(name):
     H.say(f"  cfg={cfg}")
     inp = oinputs.layer_inputs(lt)
     ref = omoe.layer_forward(inp)
-    fp8 = cfg.precision == "fp8"
+    fp8 = cfg.precision != "f32"
     T, k, d, E, F = cfg.T, cfg.k, cfg.d, cfg.E, cfg.F
     rows = T * k
     off = torch.from_numpy(ref.perm.offsets).to(H.DEV)
@@ -120,7 +125,8 @@ def test_grouped_ffn(name):
         out = torch.empty((nrows, d), dtype=odt, device=H.DEV)
         h = torch.empty((nrows, FF), dtype=hdt, device=H.DEV)
         hs = torch.empty((nrows, FF // 128), dtype=torch.float32, device=H.DEV) if fp8 else None
-        f = _lib.make_ffn(d, FF, G, nrows, fp8, offsets, row_src, div, a, a_s, w13, s13, w2, s2, out, h, hs)
+        f = _lib.make_ffn(d, FF, G, nrows, cfg.precision, offsets, row_src, div, a, a_s, w13, s13, w2,
+                          s2, out, h, hs)
         _lib.moe_grouped_ffn(f, alloc_workspace(_lib.moe_grouped_ffn_workspace_size(f), H.DEV))
         torch.cuda.synchronize()
         return (out.to(torch.float64).cpu().numpy(), h.cpu().numpy(),
@@ -157,7 +163,7 @@ def test_grouped_ffn(name):
 def test_combine(precision):
     T, d, k, E = 77, 512, 4, 16
     rng = np.random.default_rng(5)
-    dt = torch.bfloat16 if precision == "fp8" else torch.float32
+    dt = torch.bfloat16 if precision != "f32" else torch.float32
     eo = torch.from_numpy(rng.standard_normal((T * k, d)).astype(np.float32)).to(dt)
     so = torch.from_numpy(rng.standard_normal((T, d)).astype(np.float32)).to(dt)
     w = rng.uniform(0, 1, (T, k)).astype(np.float32)
@@ -175,13 +181,13 @@ def test_combine(precision):
     got = y.to(torch.float64).cpu().numpy()
     # float32 accumulation of k+1 terms: <= (k+1) * 2^-24 * sum |terms|
     acc_err = (k + 1) * 2.0 ** -24 * (np.einsum("tj,tjd->td", np.abs(w), np.abs(pairs)) + np.abs(so64))
-    if precision == "fp8":  # plus half a bf16 ulp (<= 2^-8 relative) for the output rounding
+    if precision != "f32":  # plus half a bf16 ulp (<= 2^-8 relative) for the output rounding
         assert np.all(np.abs(got - exact) <= np.abs(exact) * 2.0 ** -8 + acc_err * 1.01)
     else:
         assert np.all(np.abs(got - exact) <= np.abs(exact) * 2.0 ** -24 + acc_err * 1.01)
 
 
-@pytest.mark.parametrize("name", SMALL + MODEL)
+@pytest.mark.parametrize("name", SMALL + MODEL + MX)
 def test_layer_forward(name):
     """moe_layer_forward against the oracle; the separate entry points give
     bit-identical results, and their h decisions are validated."""
@@ -197,7 +203,7 @@ def test_layer_forward(name):
     assert np.array_equal(ids, ref.ids)
     assert np.abs(w - ref.w).max() <= H.W_MAX_ABS
     extra = 0.0
-    if cfg.precision == "fp8":
+    if cfg.precision != "f32":
         extra, _, _, flips = H.fp8_bounds(inp, st)
         H.say(f"  h: {flips} validated neighbouring-code decisions")
     H.compare_y(y, ref.y64, cfg.precision, "y", extra)
