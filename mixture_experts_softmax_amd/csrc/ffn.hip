@@ -145,13 +145,41 @@ constexpr int kstep_bytes() { return W4 ? kBK / 2 : kBK; }
 
 // Fragment of K step kt. p: the lane's row at its lane-group offset
 // ((lane / 16) * 16 bytes); e (MXFP4): the row's scale bytes + lane / 16.
-template <bool W4>
+// WS = false (MXFP4): the codes only, the scale comes from ScaleQuads.
+template <bool W4, bool WS = true>
 __device__ inline BFrag<W4> load_bfrag(const uint8_t* p, const uint8_t* e, int kt) {
   if constexpr (W4)
-    return Fp4Frag{*reinterpret_cast<const v4i*>(p + kt * (kBK / 2)), (int)e[kt * 4]};
+    return Fp4Frag{*reinterpret_cast<const v4i*>(p + kt * (kBK / 2)), WS ? (int)e[kt * 4] : 0};
   else
     return glb_bfrag(p + kt * kBK);
 }
+
+// MXFP4 block scales of NB weight rows, fetched 16 bytes (four K steps, all
+// four lane groups) of a row at a time: a byte load per fragment and step
+// costs a cache-line access per row, as much as the fragment's codes, and
+// halves the streaming rate. q[r] holds the quad r quads after the current
+// one; the lane takes its byte of step t of the current quad by a shift.
+template <int NQ, int NB>
+struct ScaleQuads {
+  v4i q[NQ][NB];
+  // e[j]: start of row j's scale bytes; qa: absolute quad index
+  __device__ inline void load(int r, const uint8_t* const (&e)[NB], int qa) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) q[r][j] = *reinterpret_cast<const v4i*>(e[j] + 16 * qa);
+  }
+  __device__ inline void rotate() {
+#pragma unroll
+    for (int r = 0; r + 1 < NQ; ++r)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) q[r][j] = q[r + 1][j];
+  }
+  // sh = 8 * (lane / 16)
+  __device__ inline int scale(int j, int t, int sh) const { return q[0][j][t] >> sh; }
+};
+
+// Quads in flight for a ring PD steps deep: the load issued after step kt is
+// for step kt + PD, at most (3 + PD) / 4 quads past kt's.
+constexpr int scale_quads(int pd) { return (3 + pd) / 4 + 1; }
 
 // E4M3 activations x E4M3 weights, or x MXFP4 weights (A scale 2^0, B scale
 // per lane from the fragment; the FP4 operand occupies the low 4 registers).
@@ -284,7 +312,10 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void gateup_fp8_kernel(
   constexpr int NB = 2 * NS;        // weight subtiles per wave (gate, up)
   constexpr int CH = BM * (kBK / 16);
   constexpr int CPT = (CH + NTH - 1) / NTH;
-  constexpr int PD = prefetch_depth<BMW, 64>() * (W4 && BMW <= 32 ? 2 : 1);
+  constexpr int PD = !W4 ? prefetch_depth<BMW, 64>() : BMW <= 16 ? 6 : BMW <= 32 ? 4 : 3;
+  // MXFP4 scales by quads where the K loop is unrolled over whole quads
+  constexpr bool QS = W4 && KTC > 0 && KTC % 4 == 0;
+  constexpr int NQ = scale_quads(PD);
 
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * kBK];
   __shared__ float sxl[BM];
@@ -325,8 +356,9 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void gateup_fp8_kernel(
     const int hc = ntile * kHN + wn * WN + (j % NS) * 16 + (lane & 15);
     const int wrow = (j < NS) ? hc : F + hc;
     b_src[j] = w13 + (size_t)wrow * wrb + (lane >> 4) * 16;
-    e_src[j] = W4 ? S.e13 + ((size_t)g * 2 * F + wrow) * (d / 32) + (lane >> 4) : nullptr;
+    e_src[j] = W4 ? S.e13 + ((size_t)g * 2 * F + wrow) * (d / 32) + (QS ? 0 : lane >> 4) : nullptr;
   }
+  const int sh = 8 * (lane >> 4);
   // weight scales of this wave's columns, loaded now so that the epilogue
   // waits on no load (its stores sit under row guards, where a pending load
   // would make every store wait for all earlier ones)
@@ -360,10 +392,15 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void gateup_fp8_kernel(
   const int KT = KTC > 0 ? KTC : d / kBK;  // KTC: K steps known at compile time
   v4i a_stage[CPT];
   BFrag<W4> bq[PD][NB];
+  ScaleQuads<NQ, NB> sq;
 #pragma unroll
   for (int s = 0; s < PD; ++s)
 #pragma unroll
-    for (int j = 0; j < NB; ++j) bq[s][j] = load_bfrag<W4>(b_src[j], e_src[j], min(s, KT - 1));
+    for (int j = 0; j < NB; ++j) bq[s][j] = load_bfrag<W4, !QS>(b_src[j], e_src[j], min(s, KT - 1));
+  if constexpr (QS) {
+#pragma unroll
+    for (int r = 0; r <= (PD - 1) / 4; ++r) sq.load(r, e_src, min(r, KT / 4 - 1));
+  }
 #pragma unroll
   for (int i = 0; i < CPT; ++i) a_stage[i] = *reinterpret_cast<const v4i*>(a_src[i]);
 #pragma unroll
@@ -384,6 +421,11 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void gateup_fp8_kernel(
       const int kt = kt0 + s;
       if (kt < KT) {
         const int cur = kt & 1;
+        if constexpr (QS) {
+          if (kt % 4 == 0 && kt > 0) sq.rotate();
+#pragma unroll
+          for (int j = 0; j < NB; ++j) bq[s][j].s = sq.scale(j, kt % 4, sh);
+        }
 #pragma unroll
         for (int i = 0; i < MS; ++i) {
           const v8i af = lds_afrag(lds_a[cur] + rbase * kBK, i, lane);
@@ -401,7 +443,10 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void gateup_fp8_kernel(
         for (int i = 0; i < CPT; ++i)
           a_stage[i] = *reinterpret_cast<const v4i*>(a_src[i] + ka * kBK);
 #pragma unroll
-        for (int j = 0; j < NB; ++j) bq[s][j] = load_bfrag<W4>(b_src[j], e_src[j], kb);
+        for (int j = 0; j < NB; ++j) bq[s][j] = load_bfrag<W4, !QS>(b_src[j], e_src[j], kb);
+        if constexpr (QS) {
+          if ((kt + PD) % 4 == 0) sq.load((kt % 4 + PD) / 4, e_src, min((kt + PD) / 4, KT / 4 - 1));
+        }
         __syncthreads();
         // keep each step's instructions in its step (bounds register pressure
         // of the unrolled loop)
@@ -885,6 +930,8 @@ __global__ __launch_bounds__(NW * kWave) void down_fp8_resident_kernel(
   constexpr int NSTEP = NTW * KTC;
   constexpr int PDM = W4 ? 6 : 4;  // MXFP4: half the bytes per step, deeper ring
   constexpr int PD = NSTEP < PDM ? NSTEP : PDM;
+  constexpr bool QS = W4 && KTC % 4 == 0;  // MXFP4 scales by quads (never straddle N tiles)
+  constexpr int NQ = scale_quads(PD);
   constexpr int HPT = (BM * KTC + NTH - 1) / NTH;
   static_assert(BM * KTC * kBK <= 65536, "h slab exceeds the LDS budget");
 
@@ -912,7 +959,18 @@ __global__ __launch_bounds__(NW * kWave) void down_fp8_resident_kernel(
   auto bfrag = [&](int st, int j) {
     const int n = min(st / KTC, dnt - 1 - nt0);
     const size_t row = min(mcol(n, j), d - 1);
-    return load_bfrag<W4>(w2 + row * wrb, W4 ? e2 + row * (F / 32) : nullptr, st % KTC);
+    return load_bfrag<W4, !QS>(w2 + row * wrb, W4 ? e2 + row * (F / 32) : nullptr, st % KTC);
+  };
+  // scale quad of global step st (QS): row starts of the step's N tile
+  ScaleQuads<NQ, NB> sq;
+  const int sh = 8 * (lane >> 4);
+  auto load_quad = [&](int r, int st) {
+    const int n = min(st / KTC, dnt - 1 - nt0);
+    const uint8_t* e[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      e[j] = S.e2 + ((size_t)g * d + min(mcol(n, j), d - 1)) * (F / 32);
+    sq.load(r, e, (st % KTC) / 4);
   };
   // channel scales of every N tile, loaded now so the epilogues wait on no load
   float s2v[NTW][NB];
@@ -953,6 +1011,10 @@ __global__ __launch_bounds__(NW * kWave) void down_fp8_resident_kernel(
       for (int s = 0; s < PD; ++s)
 #pragma unroll
         for (int j = 0; j < NB; ++j) bq[s][j] = bfrag(s, j);
+      if constexpr (QS) {
+#pragma unroll
+        for (int r = 0; r <= (PD - 1) / 4; ++r) load_quad(r, 4 * r);
+      }
     }
 #pragma unroll
     for (int i = 0; i < GRP; ++i)
@@ -977,6 +1039,11 @@ __global__ __launch_bounds__(NW * kWave) void down_fp8_resident_kernel(
 #pragma unroll
         for (int j = 0; j < NB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
     }
+    if constexpr (QS) {
+      if (st % 4 == 0 && st > 0) sq.rotate();
+#pragma unroll
+      for (int j = 0; j < NB; ++j) bq[s][j].s = sq.scale(j, st % 4, sh);
+    }
 #pragma unroll
     for (int i = 0; i < MS; ++i) {
       const v8i af = lds_afrag(lds_a[kt], i, lane);
@@ -994,6 +1061,9 @@ __global__ __launch_bounds__(NW * kWave) void down_fp8_resident_kernel(
     if (st + PD < NSTEP) {
 #pragma unroll
       for (int j = 0; j < NB; ++j) bq[s][j] = bfrag(st + PD, j);
+      if constexpr (QS) {
+        if ((st + PD) % 4 == 0) load_quad((st % 4 + PD) / 4, st + PD);
+      }
     }
     // keep each step's loads and scaled accumulation in the step (the
     // scheduler would otherwise sink the loads towards their use, shortening
