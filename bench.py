@@ -200,9 +200,11 @@ def time_layer(cfg, steps, warmup, hip):
                 call_us=pct)
 
 
-def time_chunked(cfg, chunk, steps, warmup, hip):
-    """The workload's tokens as consecutive calls of `chunk` tokens (one step =
-    all chunks, in order); returns ms per step and per-chunk accounting."""
+def time_graph(cfg, steps, warmup, hip):
+    """moe_layer_forward captured once into a HIP graph (torch.cuda.CUDAGraph
+    on the capturing stream) and replayed: per-replay GPU time from events on
+    the replay stream, back-to-back ms per call, and the host time to issue
+    one call, eager and replayed."""
     import numpy as np
     import torch
 
@@ -215,10 +217,98 @@ def time_chunked(cfg, chunk, steps, warmup, hip):
                    precision=cfg.precision, w_router=lt.w_router, router_bias=lt.router_bias,
                    w13=lt.w13, w13_scale=lt.w13_scale, w2=lt.w2, w2_scale=lt.w2_scale, ws13=lt.ws13,
                    ws13_scale=lt.ws13_scale, ws2=lt.ws2, ws2_scale=lt.ws2_scale)
-    n = cfg.T // chunk
-    s = L.shape(chunk)
-    ws = L.workspace(chunk, "cuda")
+    T = cfg.T
+    s = L.shape(T)
+    ws = L.workspace(T, "cuda")
     W = _lib.make_weights(s, **L.tensors)
+    x = lt.x
+    y = torch.empty_like(x)
+    ids = torch.empty((T, cfg.k), dtype=torch.int32, device="cuda")
+    gw = torch.empty((T, cfg.k), dtype=torch.float32, device="cuda")
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        for _ in range(3):
+            _lib.moe_layer_forward(s, W, x, y, ids, gw, ws)
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        _lib.moe_layer_forward(s, W, x, y, ids, gw, ws)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
+    hip.L.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
+
+    def per_call(issue, reps):
+        ca = [hip.event() for _ in range(reps)]
+        cb = [hip.event() for _ in range(reps)]
+        for i in range(reps):
+            hip.L.hipEventRecord(C.c_void_p(ca[i]), C.c_void_p(stream))
+            issue()
+            hip.L.hipEventRecord(C.c_void_p(cb[i]), C.c_void_p(stream))
+        torch.cuda.synchronize()
+        us = np.array([hip.ms(a, b) * 1e3 for a, b in zip(ca, cb)])
+        for e in ca + cb:
+            hip.destroy(e)
+        return {"p10": round(float(np.percentile(us, 10)), 2),
+                "p50": round(float(np.percentile(us, 50)), 2),
+                "p90": round(float(np.percentile(us, 90)), 2), "calls": reps}
+
+    def back_to_back(issue, reps):
+        torch.cuda.synchronize()
+        a, b = hip.event(), hip.event()
+        hip.L.hipEventRecord(C.c_void_p(a), C.c_void_p(stream))
+        h0 = time.perf_counter()
+        for _ in range(reps):
+            issue()
+        h1 = time.perf_counter()
+        hip.L.hipEventRecord(C.c_void_p(b), C.c_void_p(stream))
+        torch.cuda.synchronize()
+        ms = hip.ms(a, b) / reps
+        hip.destroy(a)
+        hip.destroy(b)
+        return ms, (h1 - h0) * 1e6 / reps
+
+    def eager():
+        _lib.moe_layer_forward(s, W, x, y, ids, gw, ws)
+
+    for _ in range(warmup):
+        g.replay()
+        eager()
+    reps = max(20, min(steps, 50))
+    out = {}
+    for name, fn in (("eager", eager), ("graph", g.replay)):
+        ms, host_us = back_to_back(fn, steps)
+        out[name] = {"ms_per_call": round(ms, 4), "host_us_per_call": round(host_us, 2),
+                     "call_us": per_call(fn, reps)}
+    del g, L, ws, W, x, y, lt
+    torch.cuda.empty_cache()
+    return out
+
+
+def time_chunked(cfg, chunk, steps, warmup, hip):
+    """The workload's tokens as consecutive calls of `chunk` tokens (one step =
+    all chunks, in order); returns ms per step and per-chunk accounting.
+    chunk may also be a list of call sizes that sum to the batch."""
+    import numpy as np
+    import torch
+
+    import mixture_experts_softmax_amd as M
+    from mixture_experts_softmax_amd import _lib
+    from synthetic import make_layer
+
+    lt = make_layer(cfg, device="cuda")
+    L = M.MoELayer(d=cfg.d, E=cfg.E, k=cfg.k, F=cfg.F, F_shared=cfg.F_shared,
+                   precision=cfg.precision, w_router=lt.w_router, router_bias=lt.router_bias,
+                   w13=lt.w13, w13_scale=lt.w13_scale, w2=lt.w2, w2_scale=lt.w2_scale, ws13=lt.ws13,
+                   ws13_scale=lt.ws13_scale, ws2=lt.ws2, ws2_scale=lt.ws2_scale)
+    sizes = list(chunk) if isinstance(chunk, (list, tuple)) else [chunk] * (cfg.T // chunk)
+    bounds = np.cumsum([0] + sizes)
+    assert bounds[-1] <= cfg.T
+    n = len(sizes)
+    shapes = [L.shape(c) for c in sizes]
+    ws = L.workspace(max(sizes), "cuda")
+    W = _lib.make_weights(shapes[0], **L.tensors)
     x = lt.x
     y = torch.empty_like(x)
     ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
@@ -226,8 +316,8 @@ def time_chunked(cfg, chunk, steps, warmup, hip):
 
     def step():
         for c in range(n):
-            sl = slice(c * chunk, (c + 1) * chunk)
-            _lib.moe_layer_forward(s, W, x[sl], y[sl], ids[sl], gw[sl], ws)
+            sl = slice(int(bounds[c]), int(bounds[c + 1]))
+            _lib.moe_layer_forward(shapes[c], W, x[sl], y[sl], ids[sl], gw[sl], ws)
 
     for _ in range(warmup):
         step()
@@ -245,8 +335,8 @@ def time_chunked(cfg, chunk, steps, warmup, hip):
     idn = ids.cpu().numpy()
     bytes_sum = flops_sum = 0.0
     for c in range(n):
-        counts = np.bincount(idn[c * chunk:(c + 1) * chunk].reshape(-1), minlength=cfg.E)
-        ac = accounting(cfg.with_(T=chunk), counts)
+        counts = np.bincount(idn[bounds[c]:bounds[c + 1]].reshape(-1), minlength=cfg.E)
+        ac = accounting(cfg.with_(T=sizes[c]), counts)
         bytes_sum += ac["layer_bytes"]
         flops_sum += ac["layer_flops"]
     del L, ws, W, x, y, lt
@@ -421,6 +511,22 @@ def main():
             "hbm_frac": round(rc["bytes"] / t / 1e9 / HBM_PEAK_GBS, 4),
             "fp8_mfma_frac": round(rc["flops"] / t / 1e12 / FP8_PEAK_TFLOPS, 4)}
         torch.cuda.empty_cache()
+        # mixed batch: 256 prefill-chunk tokens and 32 decode tokens in one
+        # call, against the same tokens as two calls (256, then 32)
+        mx_cfg = CONFIGS["mixed"]
+        log("[bench] secondary workload mixed (one call vs 256 + 32)")
+        rm = time_layer(mx_cfg, sec_steps, sec_warm, hip)
+        del rm["lt"]
+        out["mixed"] = summarize(mx_cfg, rm)
+        torch.cuda.empty_cache()
+        rs = time_chunked(mx_cfg, [256, 32], sec_steps, sec_warm, hip)
+        out["mixed"]["split_256_32_ms"] = round(rs["ms"], 4)
+        out["mixed"]["speedup_vs_split"] = round(rs["ms"] / rm["ms_step"], 3)
+        torch.cuda.empty_cache()
+        # the decode step captured into a HIP graph and replayed
+        log("[bench] decode replayed from a HIP graph")
+        out["decode_graph"] = time_graph(cfg if cfg.T <= 64 else CONFIGS["decode"],
+                                         sec_steps * 2, sec_warm, hip)
         out["hbm_copy_probe_GBs"] = hbm_copy_probe()
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")

@@ -50,6 +50,8 @@ CONFIGS = {
     "b100": LayerConfig("b100", 4096, 4096, 128, 8, 2048, 2048, "fp8", seed=4),
     # skewed routing: 8 hot experts take ~half the assignments, 40 get none
     "skew": LayerConfig("skew", 2048, 4096, 128, 6, 1024, 1024, "fp8", seed=5, skew=True),
+    # a mixed batch: a 256-token prefill chunk and 32 decode tokens in one call
+    "mixed": LayerConfig("mixed", 288, 4096, 128, 6, 1024, 1024, "fp8", seed=6),
     # the decode step with MXFP4 expert weights
     "decode_mxfp4": LayerConfig("decode_mxfp4", 64, 4096, 128, 6, 1024, 1024, "mxfp4", seed=2),
 }

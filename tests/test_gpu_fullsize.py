@@ -14,7 +14,7 @@ from tests import gpu_helpers as H
 
 pytestmark = pytest.mark.gpu
 
-SAMPLES = {"decode": 64, "prefill": 16, "b100": 10, "skew": 16}
+SAMPLES = {"decode": 64, "prefill": 16, "b100": 10, "skew": 16, "mixed": 24, "decode_mxfp4": 64}
 
 
 @pytest.fixture(autouse=True)
@@ -31,7 +31,7 @@ def _sample(T, n, seed, extra=()):
     return np.array(sorted(base | set(rest.tolist())))[: max(n, len(base))]
 
 
-@pytest.mark.parametrize("name", ["decode", "prefill", "b100", "skew"])
+@pytest.mark.parametrize("name", ["decode", "prefill", "b100", "skew", "mixed", "decode_mxfp4"])
 def test_fullsize_sampled(name):
     cfg = CONFIGS[name]
     lt = H.gen(cfg)
@@ -59,13 +59,15 @@ def test_fullsize_sampled(name):
     assert np.array_equal(st["xq"][tok], r_xq) and np.array_equal(st["xs"][tok], r_sx)
     bound, _, _, flips = H.fp8_bounds(inp, st, tokens=tok)
     H.say(f"  h: {flips} validated neighbouring-code decisions on the sampled tokens")
-    H.compare_y(y[tok], r_y64, "fp8", f"y[{len(tok)} sampled tokens]", bound)
+    H.compare_y(y[tok], r_y64, cfg.precision, f"y[{len(tok)} sampled tokens]", bound)
     assert np.all(np.isfinite(y))
 
 
 def test_prefill_chunked_equals_whole():
     """The prefill as 14 calls of 256 consecutive tokens gives the same routing
-    and outputs as one call over all 3584 tokens."""
+    as one call over all 3584 tokens, and gate weights and outputs equal up to
+    the router's float32 summation order (its K split depends on the batch
+    size, so logits may differ in the last bits)."""
     cfg = CONFIGS["prefill"]
     lt = H.gen(cfg)
     ids, w, y = H.run_layer(lt)
@@ -78,7 +80,9 @@ def test_prefill_chunked_equals_whole():
         L.forward(lt.x[sl], y=yc[sl], topk_ids=idc[sl], topk_w=wc[sl])
     torch.cuda.synchronize()
     assert np.array_equal(idc.cpu().numpy(), ids)
-    assert np.array_equal(wc.cpu().numpy(), w)
+    dw = np.abs(wc.cpu().numpy() - w).max()
+    H.say(f"  chunked vs whole: max |dw| = {dw:.3e}")
+    assert dw <= H.W_MAX_ABS
     yc = yc.to(torch.float64).cpu().numpy()
     d = np.abs(yc - y).max()
     H.say(f"  chunked vs whole: max |dy| = {d:.3e} (bit-identical: {d == 0})")
