@@ -12,6 +12,8 @@ Contents:
              expert FFNs, shared expert, combine.
   brute.py   a scalar brute-force loop over all experts for tiny inputs, used to
              pin moe.py.
+  qk_rope.py the QK-Norm + RoPE step before attention (per-head RMSNorm, then
+             the rotary embedding), in float64.
 
 Parity status: every function is pinned by CPU tests against the formats'
 definitions, closed forms, special cases reducing to library routines, and the
@@ -19,4 +21,4 @@ brute-force loop. The whole-layer result at the full benchmark sizes has no
 published values to compare against; it is pinned only through those checks
 on small shapes.
 """
-from . import codecs, moe  # noqa: F401
+from . import codecs, moe, qk_rope  # noqa: F401
