@@ -343,6 +343,56 @@ def time_chunked(cfg, chunk, steps, warmup, hip):
     return dict(ms=ms, chunks=n, bytes=bytes_sum, flops=flops_sum)
 
 
+def time_qk(cfg, steps, warmup, hip, copies=8):
+    """moe_qk_norm_rope in place on `copies` separate QKV buffers in turn (their
+    total exceeds the 256 MB Infinity Cache at the prefill size, so every call
+    streams from HBM); returns us per call, per-call percentiles and the
+    algorithmic bytes (q and k heads read and written once, positions,
+    weights)."""
+    import numpy as np
+    import torch
+
+    from mixture_experts_softmax_amd import _lib
+    from synthetic.qk import make_qk
+
+    qt = make_qk(cfg, device="cuda")
+    bufs = [qt.qkv.clone() for _ in range(copies)]
+    s = _lib.qk_shape(cfg.T, cfg.n_q, cfg.n_kv, cfg.head_dim, cfg.row, cfg.q_offset, cfg.k_offset,
+                      cfg.eps, cfg.theta, cfg.style, qt.qkv.dtype)
+    L = _lib.lib()
+    args = [(C.byref(s), C.c_void_p(b.data_ptr()), C.c_void_p(qt.positions.data_ptr()),
+             C.c_void_p(qt.q_weight.data_ptr()), C.c_void_p(qt.k_weight.data_ptr())) for b in bufs]
+    stream = torch.cuda.current_stream().cuda_stream
+    sp = C.c_void_p(stream)
+    for i in range(warmup):
+        _lib._check(L.moe_qk_norm_rope(*args[i % copies], sp), "moe_qk_norm_rope")
+    torch.cuda.synchronize()
+    hip.L.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
+    ev = [hip.event() for _ in range(steps + 1)]
+    for i in range(steps):
+        hip.L.hipEventRecord(C.c_void_p(ev[i]), sp)
+        L.moe_qk_norm_rope(*args[i % copies], sp)
+    hip.L.hipEventRecord(C.c_void_p(ev[steps]), sp)
+    torch.cuda.synchronize()
+    us = np.array([hip.ms(ev[i], ev[i + 1]) * 1e3 for i in range(steps)])
+    for e in ev:
+        hip.destroy(e)
+    el = 2 if cfg.precision == "bf16" else 4
+    alg = 2 * cfg.T * (cfg.n_q + cfg.n_kv) * cfg.head_dim * el + 4 * cfg.T + 2 * cfg.head_dim * el
+    mean_us = float(us.mean())
+    del bufs, qt
+    torch.cuda.empty_cache()
+    return {"workload": f"{cfg.name}: T={cfg.T} heads {cfg.n_q}+{cfg.n_kv} x {cfg.head_dim} "
+                        f"{cfg.precision} {cfg.style}, in place",
+            "us_per_call": round(mean_us, 2),
+            "call_us": {"p10": round(float(np.percentile(us, 10)), 2),
+                        "p50": round(float(np.percentile(us, 50)), 2),
+                        "p90": round(float(np.percentile(us, 90)), 2), "calls": steps},
+            "alg_bytes": alg, "GBs": round(alg / (mean_us / 1e6) / 1e9, 1),
+            "hbm_frac": round(alg / (mean_us / 1e6) / 1e9 / HBM_PEAK_GBS, 4),
+            "tokens_per_s": round(cfg.T / (mean_us / 1e6), 1)}
+
+
 def hbm_copy_probe():
     """Device-to-device copy of 1 GiB (torch's copy kernel), read + write bytes
     per second: a streaming figure measured on this GPU beside the kernels'."""
@@ -417,6 +467,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the other workloads (prefill, 100B-shaped, skewed, chunked prefill) "
                          "and the copy probe")
+    ap.add_argument("--qk-only", choices=["qk_prefill", "qk_decode"],
+                    help="only time the QK-Norm + RoPE step on that workload and print its line")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 1 GiB device-to-device copy (counter calibration) and exit")
     ap.add_argument("--cpu-tokens", type=int, default=0,
@@ -448,6 +500,11 @@ def main():
 
     from synthetic import CONFIGS
     hip = Hip()
+    if args.qk_only:
+        from synthetic.qk import QK_CONFIGS
+        print(json.dumps({"qk_norm_rope": time_qk(QK_CONFIGS[args.qk_only], args.steps,
+                                                  args.warmup, hip)}), flush=True)
+        return
     cfg = CONFIGS[args.workload]
     r = time_layer(cfg, args.steps, args.warmup, hip)
     lt = r.pop("lt")
@@ -527,6 +584,11 @@ def main():
         log("[bench] decode replayed from a HIP graph")
         out["decode_graph"] = time_graph(cfg if cfg.T <= 64 else CONFIGS["decode"],
                                          sec_steps * 2, sec_warm, hip)
+        # the step before the layer's attention: QK-Norm + RoPE in place
+        from synthetic.qk import QK_CONFIGS
+        for qn in ("qk_prefill", "qk_decode"):
+            log(f"[bench] secondary workload {qn}")
+            out[qn] = time_qk(QK_CONFIGS[qn], 50, 5, hip)
         out["hbm_copy_probe_GBs"] = hbm_copy_probe()
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")

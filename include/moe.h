@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 /* Limits checked by every entry point. */
 #define MOE_MAX_E 256      /* routed experts */
@@ -262,6 +262,60 @@ moe_status_t moe_layer_forward_events(const moe_shape_t* shape, const moe_weight
  * to nearest even, saturating at +-448), for testing it without a GPU.
  */
 void moe_host_e4m3_encode(const float* in, uint8_t* out, int64_t n);
+
+/* ---- QK-Norm + RoPE ---------------------------------------------------------
+ * The step before attention in the same transformer layer, which the NVIDIA
+ * Sarvam blog runs as one fused in-place pass over the query and key heads
+ * (Table 1, row "QK Norm + RoPE", and the paragraph on fused positional
+ * embedding): instead of a norm pass and a rotary pass that each read and
+ * write the heads, every head is read once, normalised, rotated and written
+ * back in place.
+ *
+ * For every token t (position p = positions[t]) and every query head h (and
+ * likewise every key head, with k_weight):
+ *   n[i]  = x[i] / sqrt(mean_j x[j]^2 + eps) * q_weight[i]          (RMSNorm)
+ *   pair (a, b) of n with pair index i in [0, head_dim/2) becomes
+ *   (a cos f - b sin f, a sin f + b cos f),  f = p * theta^(-2i / head_dim)
+ * where the pairs are (2i, 2i+1) (MOE_ROPE_INTERLEAVED, the rotary-embedding
+ * paper's definition) or (i, i + head_dim/2) (MOE_ROPE_HALVES). Value heads
+ * and every other column of a row are not touched. Arithmetic in float32, the
+ * angles' sines and cosines in float64; bf16 results rounded to nearest even.
+ *
+ * Layout: qkv [T][row_stride] elements of `dtype`, query head h at columns
+ * [q_offset + h head_dim, +head_dim), key head h at k_offset + h head_dim;
+ * the query and key column ranges must lie within the row and not overlap.
+ * positions [T] int32 (any value). q_weight, k_weight [head_dim] of `dtype`.
+ * qkv, q_weight and k_weight must be 16-byte aligned, and row_stride,
+ * q_offset and k_offset multiples of 16 bytes' worth of elements (8 bf16,
+ * 4 float32). All pointers are device memory owned by the caller; the call
+ * enqueues one kernel on `stream` and returns. T == 0 is a no-op.
+ * Errors (before any launch): MOE_ERR_INVALID_ARG for a null or misaligned
+ * pointer, head_dim not 64, 128 or 256, no heads or more than 256, ranges
+ * outside the row or overlapping, negative or non-finite eps, non-positive or
+ * non-finite theta, an unknown style; MOE_ERR_UNSUPPORTED for a dtype other
+ * than bf16 or float32.
+ */
+typedef enum moe_rope_style {
+  MOE_ROPE_INTERLEAVED = 0, /* pairs (2i, 2i+1) */
+  MOE_ROPE_HALVES = 1       /* pairs (i, i + head_dim/2) */
+} moe_rope_style_t;
+
+typedef struct moe_qk_shape {
+  int32_t T;          /* tokens (rows of qkv), 0 <= T <= MOE_MAX_T */
+  int32_t n_q;        /* query heads */
+  int32_t n_kv;       /* key heads; 1 <= n_q + n_kv <= 256 */
+  int32_t head_dim;   /* 64, 128 or 256 */
+  int64_t row_stride; /* elements from one token's row to the next */
+  int64_t q_offset;   /* element offset of query head 0 within a row */
+  int64_t k_offset;   /* element offset of key head 0 within a row */
+  float eps;          /* RMSNorm epsilon, inside the square root */
+  float theta;        /* rotary base */
+  int32_t style;      /* moe_rope_style_t */
+  int32_t dtype;      /* MOE_DTYPE_BF16 or MOE_DTYPE_F32 (qkv and both weights) */
+} moe_qk_shape_t;
+
+moe_status_t moe_qk_norm_rope(const moe_qk_shape_t* shape, void* qkv, const int32_t* positions,
+                              const void* q_weight, const void* k_weight, void* stream);
 
 #ifdef __cplusplus
 }

@@ -18,10 +18,10 @@ from . import _lib
 from ._lib import (MoeError, moe_abi_version, moe_check_shape, moe_combine,  # noqa: F401
                    moe_grouped_ffn, moe_grouped_ffn_workspace_size, moe_layer_forward,
                    moe_layer_workspace_size, moe_permute, moe_permute_workspace_size,
-                   moe_route_topk, moe_host_e4m3_encode)
+                   moe_route_topk, moe_host_e4m3_encode, moe_qk_norm_rope, qk_shape)
 
 __all__ = ["MoELayer", "MoeError", "moe_route_topk", "moe_permute", "moe_grouped_ffn",
-           "moe_combine", "moe_layer_forward"]
+           "moe_combine", "moe_layer_forward", "moe_qk_norm_rope", "qk_shape"]
 
 
 def alloc_workspace(nbytes: int, device) -> torch.Tensor:

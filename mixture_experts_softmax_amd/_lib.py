@@ -24,8 +24,9 @@ EXPORTS = [
     "moe_layer_workspace_size", "moe_route_workspace_size", "moe_permute_workspace_size",
     "moe_grouped_ffn_workspace_size",
     "moe_route_topk", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_forward",
-    "moe_layer_forward_events", "moe_host_e4m3_encode",
+    "moe_layer_forward_events", "moe_host_e4m3_encode", "moe_qk_norm_rope",
 ]
+MOE_ROPE_INTERLEAVED, MOE_ROPE_HALVES = 0, 1
 
 
 class MoeShape(C.Structure):
@@ -50,6 +51,13 @@ class MoeFfn(C.Structure):
                 ("w13", C.c_void_p), ("w13_scale", C.c_void_p),
                 ("w2", C.c_void_p), ("w2_scale", C.c_void_p), ("out", C.c_void_p),
                 ("h_out", C.c_void_p), ("h_scale_out", C.c_void_p)]
+
+
+class MoeQkShape(C.Structure):
+    _fields_ = [("T", C.c_int32), ("n_q", C.c_int32), ("n_kv", C.c_int32),
+                ("head_dim", C.c_int32), ("row_stride", C.c_int64), ("q_offset", C.c_int64),
+                ("k_offset", C.c_int64), ("eps", C.c_float), ("theta", C.c_float),
+                ("style", C.c_int32), ("dtype", C.c_int32)]
 
 
 class MoeError(RuntimeError):
@@ -93,6 +101,8 @@ def lib() -> C.CDLL:
         L.moe_layer_forward_events.argtypes = [P, P, P, P, P, P, P, SZ, P, P, P]
         L.moe_host_e4m3_encode.restype = None
         L.moe_host_e4m3_encode.argtypes = [P, P, C.c_int64]
+        L.moe_qk_norm_rope.restype = I32
+        L.moe_qk_norm_rope.argtypes = [P] * 6
         _lib = L
     return _lib
 
@@ -333,3 +343,27 @@ def moe_host_e4m3_encode(values) -> "numpy.ndarray":
     out = np.empty(v.shape, dtype=np.uint8)
     lib().moe_host_e4m3_encode(v.ctypes.data, out.ctypes.data, v.size)
     return out
+
+
+# ------------------------------------------------------- QK-Norm + RoPE --
+
+def qk_shape(T, n_q, n_kv, head_dim, row_stride, q_offset, k_offset, eps, theta, style: str,
+             dtype) -> MoeQkShape:
+    """style "interleaved" or "halves"; dtype torch.bfloat16 or torch.float32."""
+    st = {"interleaved": MOE_ROPE_INTERLEAVED, "halves": MOE_ROPE_HALVES}[style]
+    dt = {torch.bfloat16: MOE_DTYPE_BF16, torch.float32: MOE_DTYPE_F32}.get(dtype, -1)
+    return MoeQkShape(T, n_q, n_kv, head_dim, row_stride, q_offset, k_offset, eps, theta, st, dt)
+
+
+def moe_qk_norm_rope(s: MoeQkShape, qkv, positions, q_weight, k_weight, stream=None):
+    """In place on qkv [T][row_stride] (contiguous rows of the shape's dtype)."""
+    dt = {MOE_DTYPE_BF16: torch.bfloat16, MOE_DTYPE_F32: torch.float32}.get(s.dtype)
+    if s.T > 0:
+        if qkv is None or qkv.dim() != 2 or qkv.shape[0] < s.T or qkv.shape[1] != s.row_stride:
+            raise ValueError("qkv: expected a [T][row_stride] tensor")
+    _check(lib().moe_qk_norm_rope(
+        C.byref(s), _ptr(qkv, "qkv", dt, s.T * s.row_stride),
+        _ptr(positions, "positions", torch.int32, s.T),
+        _ptr(q_weight, "q_weight", dt, s.head_dim if s.n_q else 0),
+        _ptr(k_weight, "k_weight", dt, s.head_dim if s.n_kv else 0), _stream(stream)),
+        "moe_qk_norm_rope")

@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "route.hip", "permute.hip", "ffn.hip", "combine.hip"]
+SOURCES = ["api.hip", "route.hip", "permute.hip", "ffn.hip", "combine.hip", "qk_rope.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

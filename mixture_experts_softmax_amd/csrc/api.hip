@@ -2,6 +2,8 @@
 // Nothing here allocates, frees or synchronises.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
+
 #include "common.h"
 #include "internal.h"
 #include "moe.h"
@@ -160,9 +162,41 @@ LayerWs layer_ws(const moe_shape_t* s, void* base, FfnCall* call) {
   return L;
 }
 
+moe_status_t check_qk(const moe_qk_shape_t* s) {
+  if (s == nullptr) return MOE_ERR_INVALID_ARG;
+  if (s->dtype != MOE_DTYPE_BF16 && s->dtype != MOE_DTYPE_F32) return MOE_ERR_UNSUPPORTED;
+  if (s->T < 0 || s->T > MOE_MAX_T) return MOE_ERR_INVALID_ARG;
+  if (s->n_q < 0 || s->n_kv < 0 || s->n_q + s->n_kv < 1 || s->n_q + s->n_kv > 256)
+    return MOE_ERR_INVALID_ARG;
+  if (s->head_dim != 64 && s->head_dim != 128 && s->head_dim != 256) return MOE_ERR_INVALID_ARG;
+  if (s->style != MOE_ROPE_INTERLEAVED && s->style != MOE_ROPE_HALVES) return MOE_ERR_INVALID_ARG;
+  if (!(s->eps >= 0.f) || !std::isfinite(s->eps)) return MOE_ERR_INVALID_ARG;
+  if (!(s->theta > 0.f) || !std::isfinite(s->theta)) return MOE_ERR_INVALID_ARG;
+  const int64_t vec = s->dtype == MOE_DTYPE_BF16 ? 8 : 4;  // elements per 16 bytes
+  if (s->row_stride < 1 || s->q_offset < 0 || s->k_offset < 0) return MOE_ERR_INVALID_ARG;
+  if (s->row_stride % vec || s->q_offset % vec || s->k_offset % vec) return MOE_ERR_INVALID_ARG;
+  const int64_t qe = s->q_offset + (int64_t)s->n_q * s->head_dim;
+  const int64_t ke = s->k_offset + (int64_t)s->n_kv * s->head_dim;
+  if (qe > s->row_stride || ke > s->row_stride) return MOE_ERR_INVALID_ARG;
+  if (s->n_q > 0 && s->n_kv > 0 && s->q_offset < ke && s->k_offset < qe) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+moe_status_t moe_qk_norm_rope(const moe_qk_shape_t* s, void* qkv, const int32_t* positions,
+                              const void* q_weight, const void* k_weight, void* stream) {
+  const moe_status_t st = check_qk(s);
+  if (st != MOE_OK) return st;
+  if (s->T == 0) return MOE_OK;
+  if (!qkv || !positions || (s->n_q > 0 && !q_weight) || (s->n_kv > 0 && !k_weight))
+    return MOE_ERR_INVALID_ARG;
+  if (!al16(qkv) || !al16(q_weight) || !al16(k_weight)) return MOE_ERR_INVALID_ARG;
+  return from_hip(launch_qk_norm_rope(*s, qkv, positions, q_weight, k_weight,
+                                      static_cast<hipStream_t>(stream)));
+}
 
 int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
 

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "moe.h"
+
 namespace moe {
 
 // Tokens per router workgroup and per permutation tile.
@@ -46,6 +48,10 @@ hipError_t launch_perm_scan_scatter(const int32_t* ids, int T, int E, int k, uin
                                     int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
                                     int32_t* pair_to_row, const FfnCall* c, int bm, void* tiles_ws,
                                     hipStream_t s);
+
+// ----- QK-Norm + RoPE (shape already validated) --------------------------------
+hipError_t launch_qk_norm_rope(const moe_qk_shape_t& s, void* qkv, const int32_t* positions,
+                               const void* q_weight, const void* k_weight, hipStream_t st);
 
 // ----- grouped FFN ----------------------------------------------------------
 // A "set" is a family of groups sharing one weight layout: the routed experts

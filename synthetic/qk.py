@@ -65,6 +65,20 @@ QK_PARITY = {
     "qk_hd256": QkConfig("qk_hd256", 9, 2, 1, 256, "bf16", "halves", "random", seed=46, pad=8),
     "qk_one": QkConfig("qk_one", 1, 1, 1, 128, "bf16", "interleaved", "decode", seed=47, eps=0.5),
     "qk_many_heads": QkConfig("qk_many_heads", 5, 96, 16, 128, "bf16", "halves", "random", seed=48),
+    # fewer 16-byte chunks per token than the sin/cos table has pairs
+    "qk_hd256_two_heads": QkConfig("qk_hd256_two_heads", 3, 1, 1, 256, "bf16", "interleaved",
+                                   "random", seed=49),
+    # a large odd token count
+    "qk_two_per_block_tail": QkConfig("qk_two_per_block_tail", 1025, 8, 2, 64, "bf16", "halves",
+                                      "prefill", seed=50),
+    # 3 heads of 16 lanes: the wave's last 16 lanes hold no chunk but hold the
+    # cos/sin of pairs 48..63
+    "qk_idle_lanes": QkConfig("qk_idle_lanes", 7, 2, 1, 128, "bf16", "halves", "random", seed=51),
+    "qk_idle_lanes_f32": QkConfig("qk_idle_lanes_f32", 7, 1, 0, 256, "f32", "interleaved",
+                                  "random", seed=52, pad=4),
+    # 2048 chunks per token: two passes of 1024 threads
+    "qk_two_passes": QkConfig("qk_two_passes", 3, 120, 8, 128, "bf16", "interleaved", "decode",
+                              seed=53),
 }
 
 

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
     L = _lib.lib()
     for n in header_functions():
         assert hasattr(L, n), n
-    assert _lib.moe_abi_version() == 3
+    assert _lib.moe_abi_version() == 4
 
 
 def fp8_shape(**kw):
@@ -184,3 +184,54 @@ def test_kernel_e4m3_encoder_matches_oracle():
     ours = _lib.moe_host_e4m3_encode(v)
     want = codecs.e4m3_encode(v)
     assert np.array_equal(ours, want)
+
+
+def _qk(**kw):
+    p = dict(T=64, n_q=32, n_kv=4, head_dim=128, row_stride=40 * 128, q_offset=0,
+             k_offset=32 * 128, eps=1e-6, theta=10000.0, style=_lib.MOE_ROPE_HALVES,
+             dtype=_lib.MOE_DTYPE_BF16)
+    p.update(kw)
+    return _lib.MoeQkShape(p["T"], p["n_q"], p["n_kv"], p["head_dim"], p["row_stride"],
+                           p["q_offset"], p["k_offset"], p["eps"], p["theta"], p["style"], p["dtype"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), _lib.MOE_ERR_INVALID_ARG),
+    (dict(head_dim=512), _lib.MOE_ERR_INVALID_ARG),
+    (dict(n_q=0, n_kv=0), _lib.MOE_ERR_INVALID_ARG),
+    (dict(n_q=250, n_kv=7, row_stride=300 * 128), _lib.MOE_ERR_INVALID_ARG),
+    (dict(n_q=-1), _lib.MOE_ERR_INVALID_ARG),
+    (dict(T=-1), _lib.MOE_ERR_INVALID_ARG),
+    (dict(style=2), _lib.MOE_ERR_INVALID_ARG),
+    (dict(eps=-1.0), _lib.MOE_ERR_INVALID_ARG),
+    (dict(eps=float("nan")), _lib.MOE_ERR_INVALID_ARG),
+    (dict(theta=0.0), _lib.MOE_ERR_INVALID_ARG),
+    (dict(theta=float("inf")), _lib.MOE_ERR_INVALID_ARG),
+    (dict(row_stride=40 * 128 + 4), _lib.MOE_ERR_INVALID_ARG),     # not 16-byte rows (bf16)
+    (dict(q_offset=4), _lib.MOE_ERR_INVALID_ARG),
+    (dict(k_offset=31 * 128), _lib.MOE_ERR_INVALID_ARG),           # overlaps the query heads
+    (dict(k_offset=37 * 128), _lib.MOE_ERR_INVALID_ARG),           # runs past the row
+    (dict(dtype=_lib.MOE_DTYPE_FP8_E4M3), _lib.MOE_ERR_UNSUPPORTED),
+])
+def test_qk_norm_rope_rejects_bad_shapes(kw, status):
+    """Shape errors are found on the host before anything is enqueued."""
+    A = C.c_void_p(1 << 40)  # a well-aligned stand-in address; never dereferenced
+    s = _qk(**kw)
+    assert _lib.lib().moe_qk_norm_rope(C.byref(s), A, A, A, A, None) == status
+
+
+def test_qk_norm_rope_pointer_checks():
+    L = _lib.lib()
+    A = C.c_void_p(1 << 40)
+    s = _qk()
+    assert L.moe_qk_norm_rope(None, A, A, A, A, None) == _lib.MOE_ERR_INVALID_ARG
+    assert L.moe_qk_norm_rope(C.byref(s), None, A, A, A, None) == _lib.MOE_ERR_INVALID_ARG
+    assert L.moe_qk_norm_rope(C.byref(s), A, None, A, A, None) == _lib.MOE_ERR_INVALID_ARG
+    assert L.moe_qk_norm_rope(C.byref(s), A, A, None, A, None) == _lib.MOE_ERR_INVALID_ARG
+    assert L.moe_qk_norm_rope(C.byref(s), A, A, A, C.c_void_p((1 << 40) + 8), None) == _lib.MOE_ERR_INVALID_ARG
+    # float32 rows need 4-element (16-byte) alignment only
+    s32 = _qk(dtype=_lib.MOE_DTYPE_F32, row_stride=40 * 128 + 4, T=0)
+    assert L.moe_qk_norm_rope(C.byref(s32), None, None, None, None, None) == _lib.MOE_OK
+    # no key heads: the key weight may be NULL; T == 0 is a no-op
+    s0 = _qk(T=0, n_kv=0)
+    assert L.moe_qk_norm_rope(C.byref(s0), None, None, None, None, None) == _lib.MOE_OK
