@@ -145,7 +145,7 @@ constexpr int kstep_bytes() { return W4 ? kBK / 2 : kBK; }
 
 // Fragment of K step kt. p: the lane's row at its lane-group offset
 // ((lane / 16) * 16 bytes); e (MXFP4): the row's scale bytes + lane / 16.
-// WS = false (MXFP4): the codes only, the scale comes from ScaleQuads.
+// WS = false (MXFP4): the codes only; the scale comes from the row-resident scales.
 template <bool W4, bool WS = true>
 __device__ inline BFrag<W4> load_bfrag(const uint8_t* p, const uint8_t* e, int kt) {
   if constexpr (W4)
@@ -154,32 +154,26 @@ __device__ inline BFrag<W4> load_bfrag(const uint8_t* p, const uint8_t* e, int k
     return glb_bfrag(p + kt * kBK);
 }
 
-// MXFP4 block scales of NB weight rows, fetched 16 bytes (four K steps, all
-// four lane groups) of a row at a time: a byte load per fragment and step
-// costs a cache-line access per row, as much as the fragment's codes, and
-// halves the streaming rate. q[r] holds the quad r quads after the current
-// one; the lane takes its byte of step t of the current quad by a shift.
-template <int NQ, int NB>
-struct ScaleQuads {
-  v4i q[NQ][NB];
-  // e[j]: start of row j's scale bytes; qa: absolute quad index
-  __device__ inline void load(int r, const uint8_t* const (&e)[NB], int qa) {
+// MXFP4 block scales of a fragment's 16 weight rows over a K loop of KT
+// steps, held in registers for the whole loop: a byte load per fragment and
+// step costs a cache-line access per row (as many as the codes), and even
+// 16-byte loads every four steps re-fetch each row's scale line several times
+// from HBM. Instead the 4 lanes of a row (lane groups g = 0..3) each load a
+// quarter of the row's 4 KT scale bytes once: lane group g holds the dwords
+// of steps [g KT/4, (g + 1) KT/4). Step kt's dword (one byte per lane group)
+// is then read from lane (lane % 16) + 16 (kt / (KT/4)) and shifted to the
+// lane's byte.
+template <int KT>
+__device__ inline void load_scale_row(int (&sr)[KT / 4], const uint8_t* row, int lane) {
+  const int* p = reinterpret_cast<const int*>(row) + (lane >> 4) * (KT / 4);
 #pragma unroll
-    for (int j = 0; j < NB; ++j) q[r][j] = *reinterpret_cast<const v4i*>(e[j] + 16 * qa);
-  }
-  __device__ inline void rotate() {
-#pragma unroll
-    for (int r = 0; r + 1 < NQ; ++r)
-#pragma unroll
-      for (int j = 0; j < NB; ++j) q[r][j] = q[r + 1][j];
-  }
-  // sh = 8 * (lane / 16)
-  __device__ inline int scale(int j, int t, int sh) const { return q[0][j][t] >> sh; }
-};
-
-// Quads in flight for a ring PD steps deep: the load issued after step kt is
-// for step kt + PD, at most (3 + PD) / 4 quads past kt's.
-constexpr int scale_quads(int pd) { return (3 + pd) / 4 + 1; }
+  for (int t = 0; t < KT / 4; ++t) sr[t] = p[t];
+}
+template <int KT>
+__device__ inline int scale_of_step(const int (&sr)[KT / 4], int kt, int lane) {
+  constexpr int DW = KT / 4;
+  return __shfl(sr[kt % DW], (lane & 15) + 16 * (kt / DW)) >> (8 * (lane >> 4));
+}
 
 // E4M3 activations x E4M3 weights, or x MXFP4 weights (A scale 2^0, B scale
 // per lane from the fragment; the FP4 operand occupies the low 4 registers).
@@ -314,8 +308,12 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void gateup_fp8_kernel(
   constexpr int CPT = (CH + NTH - 1) / NTH;
   constexpr int PD = !W4 ? prefetch_depth<BMW, 64>() : BMW <= 16 ? 6 : BMW <= 32 ? 4 : 3;
   // MXFP4 scales by quads where the K loop is unrolled over whole quads
-  constexpr bool QS = W4 && KTC > 0 && KTC % 4 == 0;
-  constexpr int NQ = scale_quads(PD);
+  constexpr bool QS = W4 && KTC > 0 && KTC % 4 == 0;  // scales held per row (KT known)
+  constexpr int KTS = QS ? KTC : 4;
+  // MXFP4: a row's K step is half a 128-byte line; its two halves are loaded
+  // together (after every second step, into the two slots just consumed), as
+  // the FP8 fragment loads both halves of its line in one step
+  constexpr bool PAIR = W4 && PD % 2 == 0;
 
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * kBK];
   __shared__ float sxl[BM];
@@ -358,7 +356,6 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void gateup_fp8_kernel(
     b_src[j] = w13 + (size_t)wrow * wrb + (lane >> 4) * 16;
     e_src[j] = W4 ? S.e13 + ((size_t)g * 2 * F + wrow) * (d / 32) + (QS ? 0 : lane >> 4) : nullptr;
   }
-  const int sh = 8 * (lane >> 4);
   // weight scales of this wave's columns, loaded now so that the epilogue
   // waits on no load (its stores sit under row guards, where a pending load
   // would make every store wait for all earlier ones)
@@ -392,15 +389,15 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void gateup_fp8_kernel(
   const int KT = KTC > 0 ? KTC : d / kBK;  // KTC: K steps known at compile time
   v4i a_stage[CPT];
   BFrag<W4> bq[PD][NB];
-  ScaleQuads<NQ, NB> sq;
+  int srow[NB][KTS / 4];
+  if constexpr (QS) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) load_scale_row<KTS>(srow[j], e_src[j], lane);
+  }
 #pragma unroll
   for (int s = 0; s < PD; ++s)
 #pragma unroll
     for (int j = 0; j < NB; ++j) bq[s][j] = load_bfrag<W4, !QS>(b_src[j], e_src[j], min(s, KT - 1));
-  if constexpr (QS) {
-#pragma unroll
-    for (int r = 0; r <= (PD - 1) / 4; ++r) sq.load(r, e_src, min(r, KT / 4 - 1));
-  }
 #pragma unroll
   for (int i = 0; i < CPT; ++i) a_stage[i] = *reinterpret_cast<const v4i*>(a_src[i]);
 #pragma unroll
@@ -422,9 +419,8 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void gateup_fp8_kernel(
       if (kt < KT) {
         const int cur = kt & 1;
         if constexpr (QS) {
-          if (kt % 4 == 0 && kt > 0) sq.rotate();
 #pragma unroll
-          for (int j = 0; j < NB; ++j) bq[s][j].s = sq.scale(j, kt % 4, sh);
+          for (int j = 0; j < NB; ++j) bq[s][j].s = scale_of_step<KTS>(srow[j], kt, lane);
         }
 #pragma unroll
         for (int i = 0; i < MS; ++i) {
@@ -442,10 +438,18 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void gateup_fp8_kernel(
 #pragma unroll
         for (int i = 0; i < CPT; ++i)
           a_stage[i] = *reinterpret_cast<const v4i*>(a_src[i] + ka * kBK);
+        if constexpr (PAIR) {
+          if (s % 2 == 1) {  // kt0 is a multiple of the even PD: s has kt's parity
+            const int kb0 = min(kt + PD - 1, KT - 1);
 #pragma unroll
-        for (int j = 0; j < NB; ++j) bq[s][j] = load_bfrag<W4, !QS>(b_src[j], e_src[j], kb);
-        if constexpr (QS) {
-          if ((kt + PD) % 4 == 0) sq.load((kt % 4 + PD) / 4, e_src, min((kt + PD) / 4, KT / 4 - 1));
+            for (int j = 0; j < NB; ++j) {
+              bq[s - 1][j] = load_bfrag<W4, !QS>(b_src[j], e_src[j], kb0);
+              bq[s][j] = load_bfrag<W4, !QS>(b_src[j], e_src[j], kb);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < NB; ++j) bq[s][j] = load_bfrag<W4, !QS>(b_src[j], e_src[j], kb);
         }
         __syncthreads();
         // keep each step's instructions in its step (bounds register pressure
@@ -618,7 +622,8 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void down_fp8_kernel(
   constexpr int NB = 4;  // 16-channel subtiles per wave
   constexpr int CH = BM * (kBK / 16);
   constexpr int CPT = (CH + NTH - 1) / NTH;
-  constexpr int PD = prefetch_depth<BMW, 32>() + (W4 ? 1 : 0);
+  constexpr int PD = W4 ? 4 : prefetch_depth<BMW, 32>();
+  constexpr bool PAIR = W4;  // both halves of a row's line together (gate/up kernel)
 
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * kBK];
   __shared__ float hsl[2][BM];
@@ -724,8 +729,19 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void down_fp8_kernel(
         for (int i = 0; i < CPT; ++i)
           a_stage[i] = *reinterpret_cast<const v4i*>(a_src[i] + ka * kBK);
         hs_stage = hs_src[ka];
+        if constexpr (PAIR) {
+          if (s % 2 == 1) {
+            const int kb0 = min(kt + PD - 1, KT - 1);
 #pragma unroll
-        for (int j = 0; j < NB; ++j) bq[s][j] = load_bfrag<W4>(b_src[j], e_src[j], kb);
+            for (int j = 0; j < NB; ++j) {
+              bq[s - 1][j] = load_bfrag<W4>(b_src[j], e_src[j], kb0);
+              bq[s][j] = load_bfrag<W4>(b_src[j], e_src[j], kb);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < NB; ++j) bq[s][j] = load_bfrag<W4>(b_src[j], e_src[j], kb);
+        }
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -930,8 +946,9 @@ __global__ __launch_bounds__(NW * kWave) void down_fp8_resident_kernel(
   constexpr int NSTEP = NTW * KTC;
   constexpr int PDM = W4 ? 6 : 4;  // MXFP4: half the bytes per step, deeper ring
   constexpr int PD = NSTEP < PDM ? NSTEP : PDM;
-  constexpr bool QS = W4 && KTC % 4 == 0;  // MXFP4 scales by quads (never straddle N tiles)
-  constexpr int NQ = scale_quads(PD);
+  constexpr bool QS = W4 && KTC % 4 == 0;  // MXFP4 scales held per row for every N tile
+  constexpr int KTS = QS ? KTC : 4;
+  constexpr bool PAIR = W4 && PD % 2 == 0;   // both halves of a row's line together
   constexpr int HPT = (BM * KTC + NTH - 1) / NTH;
   static_assert(BM * KTC * kBK <= 65536, "h slab exceeds the LDS budget");
 
@@ -961,17 +978,18 @@ __global__ __launch_bounds__(NW * kWave) void down_fp8_resident_kernel(
     const size_t row = min(mcol(n, j), d - 1);
     return load_bfrag<W4, !QS>(w2 + row * wrb, W4 ? e2 + row * (F / 32) : nullptr, st % KTC);
   };
-  // scale quad of global step st (QS): row starts of the step's N tile
-  ScaleQuads<NQ, NB> sq;
-  const int sh = 8 * (lane >> 4);
-  auto load_quad = [&](int r, int st) {
-    const int n = min(st / KTC, dnt - 1 - nt0);
-    const uint8_t* e[NB];
+  // MXFP4 scales of every N tile's rows (QS)
+  int srow[NTW][NB][KTS / 4];
+  if constexpr (QS) {
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
-      e[j] = S.e2 + ((size_t)g * d + min(mcol(n, j), d - 1)) * (F / 32);
-    sq.load(r, e, (st % KTC) / 4);
-  };
+    for (int n = 0; n < NTW; ++n)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int nn = min(n, dnt - 1 - nt0);
+        load_scale_row<KTS>(srow[n][j], S.e2 + ((size_t)g * d + min(mcol(nn, j), d - 1)) * (F / 32),
+                            lane);
+      }
+  }
   // channel scales of every N tile, loaded now so the epilogues wait on no load
   float s2v[NTW][NB];
 #pragma unroll
@@ -1011,10 +1029,6 @@ __global__ __launch_bounds__(NW * kWave) void down_fp8_resident_kernel(
       for (int s = 0; s < PD; ++s)
 #pragma unroll
         for (int j = 0; j < NB; ++j) bq[s][j] = bfrag(s, j);
-      if constexpr (QS) {
-#pragma unroll
-        for (int r = 0; r <= (PD - 1) / 4; ++r) load_quad(r, 4 * r);
-      }
     }
 #pragma unroll
     for (int i = 0; i < GRP; ++i)
@@ -1040,9 +1054,8 @@ __global__ __launch_bounds__(NW * kWave) void down_fp8_resident_kernel(
         for (int j = 0; j < NB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
     }
     if constexpr (QS) {
-      if (st % 4 == 0 && st > 0) sq.rotate();
 #pragma unroll
-      for (int j = 0; j < NB; ++j) bq[s][j].s = sq.scale(j, st % 4, sh);
+      for (int j = 0; j < NB; ++j) bq[s][j].s = scale_of_step<KTS>(srow[n][j], kt, lane);
     }
 #pragma unroll
     for (int i = 0; i < MS; ++i) {
@@ -1058,13 +1071,19 @@ __global__ __launch_bounds__(NW * kWave) void down_fp8_resident_kernel(
         for (int j = 0; j < NB; ++j) acc[i][j][q] = fmaf(part[j][q], hs, acc[i][j][q]);
       }
     }
-    if (st + PD < NSTEP) {
+    if constexpr (PAIR) {
+      if (st % 2 == 1) {  // PD even: slot s - 1 held step st - 1
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          if (st + PD - 1 < NSTEP) bq[s - 1][j] = bfrag(st + PD - 1, j);
+          if (st + PD < NSTEP) bq[s][j] = bfrag(st + PD, j);
+        }
+      }
+    } else if (st + PD < NSTEP) {
 #pragma unroll
       for (int j = 0; j < NB; ++j) bq[s][j] = bfrag(st + PD, j);
-      if constexpr (QS) {
-        if ((st + PD) % 4 == 0) load_quad((st % 4 + PD) / 4, st + PD);
-      }
     }
+
     // keep each step's loads and scaled accumulation in the step (the
     // scheduler would otherwise sink the loads towards their use, shortening
     // the ring, and hold every partial product live to the end)
