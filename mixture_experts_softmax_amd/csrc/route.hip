@@ -30,6 +30,8 @@ constexpr int kLogitExperts = kLogitWaves * 32;  // experts per logits tile (32 
 constexpr int kLogitChunk = 128;                  // K per pipeline stage (4 MFMA steps)
 constexpr int kLogitMinSlice = 256;               // smallest K slice
 constexpr int kLogitTargetWgs = 256;              // aim: at least one workgroup per CU
+constexpr int kTallTokens = 64;                   // tokens per tall-batch logits workgroup
+constexpr int kTallMin = 64;                      // batches above this use the tall kernel
 constexpr int kTopkWaves = 16;  // one 64-token tile per top-k workgroup
 constexpr int kTokPerWave = kPermTile / kTopkWaves;
 constexpr int kXcds = 8;
@@ -116,7 +118,7 @@ struct LogitGrid {
 
 LogitGrid logit_grid(int T, int d, int E, bool quant) {
   LogitGrid g;
-  g.n_tt = ceil_div(T, kRouteTokens);
+  g.n_tt = ceil_div(T, T > kTallMin ? kTallTokens : kRouteTokens);
   g.n_et = ceil_div(E, kLogitExperts);
   const int nch = d / kLogitChunk;
   const int tiles = max(1, g.n_tt * g.n_et);  // T = 0 still sizes one tile
@@ -200,6 +202,124 @@ __global__ __launch_bounds__(kLogitWaves * kWave) void route_logits_bf16_kernel(
     if (t < T) {
       if (e < E) out[(size_t)t * E + e] = a0[q];
       if (e + 16 < E) out[(size_t)t * E + e + 16] = a1[q];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Logits for tall batches (T > 64): workgroup (64-token tile, 128-expert tile,
+// K slice), wave w the tokens [16 w, 16 w + 16) of the tile over all 128
+// experts (8 MFMA column blocks, so each x fragment feeds 8 MFMAs). Each
+// 128-deep K chunk of the router weights (128 experts x 256 bytes) is staged
+// once per workgroup into a double-buffered LDS tile shared by the 4 waves
+// (16-byte chunks XOR-swizzled by row, so the 16 rows a fragment read touches
+// fall in distinct banks); x fragments come straight from global memory, two
+// chunks ahead. Versus the decode kernel's 16-token tiles this reads x once
+// instead of once per wave and the weights once per 64 tokens instead of
+// once per 16.
+// ---------------------------------------------------------------------------
+__device__ inline int tall_swz(int r, int q) {  // element offset of 16-byte chunk q of row r
+  return r * kLogitChunk + ((q ^ (r & 15)) << 3);
+}
+
+__global__ __launch_bounds__(kLogitWaves * kWave) void route_logits_tall_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int d, int E,
+    LogitGrid g, float* __restrict__ part, uint8_t* __restrict__ xq, float* __restrict__ xs) {
+  constexpr int NS = kLogitChunk / 32;                        // MFMA K steps per chunk
+  constexpr int NB = kLogitExperts / 16;                      // column blocks per wave
+  constexpr int WPT = kLogitExperts * kLogitChunk / 8 / (kLogitWaves * kWave);  // 16 B pieces/thread
+  __shared__ __attribute__((aligned(16))) uint16_t wl[2][kLogitExperts * kLogitChunk];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int b = blockIdx.x;
+  if (b >= g.n_lblocks) {  // ---- FP8 quantisation of x (as in the decode kernel) ----
+    const int t = (b - g.n_lblocks) * kLogitWaves + wave;
+    if (t < T) quantize_row(x + (size_t)t * d, d, lane, xq + (size_t)t * d, xs + t);
+    return;
+  }
+  const int per_xcd = g.n_lblocks / kXcds;
+  const int wi = (b % kXcds) * per_xcd + b / kXcds;
+  if (wi >= g.n_logit) return;
+  const int tt = wi % g.n_tt;
+  const int et = (wi / g.n_tt) % g.n_et;
+  const int kz = wi / (g.n_tt * g.n_et);
+  const int c0 = kz * g.cps;
+  const int c1 = min(c0 + g.cps, d / kLogitChunk);
+  const int eb = et * kLogitExperts;
+
+  const int tok = min(tt * kTallTokens + wave * 16 + (lane & 15), T - 1);
+  const uint16_t* xr = x + (size_t)tok * d + (lane >> 4) * 8;
+  // this thread's pieces of a weight chunk: piece p = tid + 256 i is expert
+  // row p / 16, 16-byte column p % 16
+  const uint16_t* wsrc[WPT];
+  int wdst[WPT];
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    const int p = tid + i * kLogitWaves * kWave;
+    const int r = p / 16, q = p % 16;
+    wsrc[i] = wr + (size_t)min(eb + r, E - 1) * d + q * 8;
+    wdst[i] = tall_swz(r, q);
+  }
+  auto load_x = [&](int c, v8bf (&xa)[NS]) {
+#pragma unroll
+    for (int s2 = 0; s2 < NS; ++s2)
+      xa[s2] = *reinterpret_cast<const v8bf*>(xr + (size_t)c * kLogitChunk + 32 * s2);
+  };
+  auto load_w = [&](int c, v4i (&ws)[WPT]) {
+#pragma unroll
+    for (int i = 0; i < WPT; ++i)
+      ws[i] = *reinterpret_cast<const v4i*>(wsrc[i] + (size_t)c * kLogitChunk);
+  };
+  auto store_w = [&](const v4i (&ws)[WPT], uint16_t* dst) {
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) *reinterpret_cast<v4i*>(dst + wdst[i]) = ws[i];
+  };
+
+  v8bf xa[2][NS];
+  v4i wst[WPT];
+  v4f acc[NB];
+#pragma unroll
+  for (int n = 0; n < NB; ++n) acc[n] = v4f{0.f, 0.f, 0.f, 0.f};
+  // every load is issued (tail chunks re-load the last one), so the wait
+  // counts stay exact
+  load_w(c0, wst);
+  load_x(c0, xa[0]);
+  load_x(min(c0 + 1, c1 - 1), xa[1]);
+  store_w(wst, wl[0]);
+  load_w(min(c0 + 1, c1 - 1), wst);
+  __syncthreads();
+  for (int c = c0; c < c1; c += 2) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int cc = c + h;
+      if (cc < c1) {
+        const uint16_t* wb = wl[h];
+#pragma unroll
+        for (int s2 = 0; s2 < NS; ++s2) {
+#pragma unroll
+          for (int n = 0; n < NB; ++n) {
+            const int r = n * 16 + (lane & 15);
+            const v8bf bf = *reinterpret_cast<const v8bf*>(wb + tall_swz(r, 4 * s2 + (lane >> 4)));
+            acc[n] = mfma_bf16_16x16x32(xa[h][s2], bf, acc[n]);
+          }
+        }
+        // the other buffer's readers finished at the barrier ending chunk cc-1
+        store_w(wst, wl[h ^ 1]);
+        load_w(min(cc + 2, c1 - 1), wst);
+        load_x(min(cc + 2, c1 - 1), xa[h]);
+        __syncthreads();
+      }
+    }
+  }
+  float* out = part + (size_t)kz * T * E;
+#pragma unroll
+  for (int n = 0; n < NB; ++n) {
+    const int e = eb + n * 16 + (lane & 15);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int t = tt * kTallTokens + wave * 16 + 4 * (lane >> 4) + q;
+      if (t < T && e < E) out[(size_t)t * E + e] = acc[n][q];
     }
   }
 }
@@ -484,9 +604,12 @@ __global__ __launch_bounds__(kTopkWaves * kWave) void route_topk_kernel(
 // smaller one. ks <= d/256 gives T * max(1, d/256); ks <= ceil(256 / tiles)
 // with T <= 16 * token tiles gives T + 4096 / expert tiles.
 size_t route_partial_rows(int T, int d, int E) {
+  // K slices x tokens: at most d / kLogitMinSlice slices, and (slices =
+  // ceil(target / tiles)) at most T + target x tile height / expert tiles
+  // rows; the tall kernel's 64-token tiles give the larger second bound
   const size_t n_et = ceil_div(E, kLogitExperts);
   const size_t a = (size_t)T * max(1, d / kLogitMinSlice);
-  const size_t b = (size_t)T + ceil_div(kLogitTargetWgs * kRouteTokens, (int)n_et);
+  const size_t b = (size_t)T + ceil_div(kLogitTargetWgs * kTallTokens, (int)n_et);
   return a < b ? a : b;
 }
 
@@ -504,9 +627,14 @@ hipError_t launch_route(bool bf16, const void* x, const void* w_router, const fl
     const LogitGrid g = logit_grid(T, d, E, xq != nullptr);
     ks = g.ks;
     if ((size_t)ks * T > route_partial_rows(T, d, E)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(route_logits_bf16_kernel, dim3(g.n_lblocks + g.n_quant),
-                       dim3(kLogitWaves * kWave), 0, s, static_cast<const uint16_t*>(x),
-                       static_cast<const uint16_t*>(w_router), T, d, E, g, part, xq, x_scale);
+    if (T > kTallMin)
+      hipLaunchKernelGGL(route_logits_tall_kernel, dim3(g.n_lblocks + g.n_quant),
+                         dim3(kLogitWaves * kWave), 0, s, static_cast<const uint16_t*>(x),
+                         static_cast<const uint16_t*>(w_router), T, d, E, g, part, xq, x_scale);
+    else
+      hipLaunchKernelGGL(route_logits_bf16_kernel, dim3(g.n_lblocks + g.n_quant),
+                         dim3(kLogitWaves * kWave), 0, s, static_cast<const uint16_t*>(x),
+                         static_cast<const uint16_t*>(w_router), T, d, E, g, part, xq, x_scale);
   } else {
     hipLaunchKernelGGL(route_logits_f32_kernel, dim3(ceil_div(T, kLogitWaves)),
                        dim3(kLogitWaves * kWave), 0, s, static_cast<const float*>(x),

@@ -68,6 +68,8 @@ PARITY = {
     "fp8_wide": LayerConfig("fp8_wide", 600, 2048, 64, 6, 512, 512, "fp8", seed=18),
     "fp8_skew_small": LayerConfig("fp8_skew_small", 512, 1024, 128, 6, 256, 256, "fp8",
                                   seed=19, skew=True),
+    # the largest expert count: two 128-expert router tiles, a ragged token tail
+    "fp8_e256": LayerConfig("fp8_e256", 130, 512, 256, 8, 128, 128, "fp8", seed=25),
     # the model's d = 4096 and F = 1024 (the shapes with fully unrolled K
     # loops) at few tokens, one per GEMM tile height: ~12, 24, 100 and 190
     # rows per expert select 16-, 32-, 128- and 192-row tiles

@@ -143,13 +143,14 @@ def fp8_bounds(inp, st, tokens=None):
     ids = st["ids"][tokens]
     p2r = st["pair_to_row"]
     row_bound = {}
-    flips = 0
+    flips = codes = 0
     for e in np.unique(ids):
         sel = np.argwhere(ids == e)           # (token index, slot)
         ew = inp.expert(int(e))
         rows = p2r[tokens[sel[:, 0]] * k + sel[:, 1]]
         n, dhq = FC.validate_h(xq[sel[:, 0]], sx[sel[:, 0]], ew, st["h"][rows], st["hs"][rows])
         flips += n
+        codes += st["h"][rows].size
         eff = FC.down_effect(dhq, ew)
         for i, r in enumerate(rows):
             row_bound[int(r)] = eff[i]
@@ -162,8 +163,10 @@ def fp8_bounds(inp, st, tokens=None):
     if inp.shared is not None:
         n, dhq = FC.validate_h(xq, sx, inp.shared, st["h_sh"][tokens], st["hs_sh"][tokens])
         flips += n
+        codes += st["h_sh"][tokens].size
         shared_extra = FC.down_effect(dhq, inp.shared)
         extra += shared_extra
+    FC.check_flip_rate(flips, codes)
     return extra, row_bound, shared_extra, flips
 
 

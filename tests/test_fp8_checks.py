@@ -73,3 +73,10 @@ def test_down_effect_bounds_the_output_change():
     _, dhq = FC.validate_h(xq, sx, ew, q2, s2)
     diff = np.abs(omoe.down_fp8(q2, s2, ew) - omoe.down_fp8(q, s, ew))
     assert np.all(diff <= FC.down_effect(dhq, ew) * (1 + 1e-9) + 1e-12)
+
+
+def test_flip_rate_cap_is_over_the_whole_call():
+    FC.check_flip_rate(11, 1000)      # 1% of 1000 codes (+1)
+    with pytest.raises(AssertionError):
+        FC.check_flip_rate(12, 1000)
+    FC.check_flip_rate(1, 50)         # one decision in a tiny call is allowed

@@ -14,7 +14,7 @@ from tests import gpu_helpers as H
 pytestmark = pytest.mark.gpu
 
 SMALL = ["tiny", "f32_ragged", "f32_noshared", "fp8_small", "fp8_ragged", "fp8_noshared",
-         "fp8_k1", "fp8_kE", "fp8_wide", "fp8_skew_small"]
+         "fp8_k1", "fp8_kE", "fp8_wide", "fp8_skew_small", "fp8_e256"]
 MODEL = ["fp8_model_m16", "fp8_model_m32", "fp8_model_m128", "fp8_model_m192", "fp8_model_f2048"]
 # MXFP4 expert weights: every kernel variant (tile heights 16 to 192, looped
 # and unrolled K loops, resident and looped down GEMMs)
@@ -146,6 +146,7 @@ def test_grouped_ffn(name):
             flips += n
             extra[r0:r1] = FC.down_effect(dhq, ew)
         H.say(f"  routed h: {flips} validated neighbouring-code decisions of {h.size}")
+        FC.check_flip_rate(flips, h.size)
     H.compare_y(eo, ref.expert_out, cfg.precision, "expert_out", extra)
     if cfg.F_shared:
         Fs = cfg.F_shared
@@ -155,6 +156,7 @@ def test_grouped_ffn(name):
         if fp8:
             n, dhq = FC.validate_h(ref.xq, ref.s_x, inp.shared, hsh, hssh)
             H.say(f"  shared h: {n} validated neighbouring-code decisions of {hsh.size}")
+            FC.check_flip_rate(n, hsh.size)
             extra_s = FC.down_effect(dhq, inp.shared)
         H.compare_y(so, ref.shared_out, cfg.precision, "shared_out", extra_s)
 
