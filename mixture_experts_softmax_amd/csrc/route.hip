@@ -47,19 +47,23 @@ __device__ inline float absmax8(const v4i& c, float m) {
   return m;
 }
 
+// Eight bf16 values (one 16-byte chunk) divided by s and encoded to E4M3.
+// The quotients have magnitude at most 448 (s = amax / 448), where gfx950's
+// packed float32 -> FP8 conversion rounds to nearest even and saturates at
+// 448 exactly as e4m3_encode does (the two agree bit for bit on every
+// float32 of that range, both signs, subnormal results included).
 __device__ inline uint2 encode8(const v4i& c, float s) {
-  uint32_t lo = 0, hi = 0;
+  float f[8];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const uint32_t c0 = e4m3_encode(__fdiv_rn(bf16_to_f32((uint16_t)((uint32_t)c[q] & 0xffff)), s));
-    const uint32_t c1 = e4m3_encode(__fdiv_rn(bf16_to_f32((uint16_t)((uint32_t)c[q] >> 16)), s));
-    const uint32_t pair = c0 | (c1 << 8);
-    if (q < 2)
-      lo |= pair << (16 * q);
-    else
-      hi |= pair << (16 * (q - 2));
+    f[2 * q] = __fdiv_rn(bf16_to_f32((uint16_t)((uint32_t)c[q] & 0xffff)), s);
+    f[2 * q + 1] = __fdiv_rn(bf16_to_f32((uint16_t)((uint32_t)c[q] >> 16)), s);
   }
-  return make_uint2(lo, hi);
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], hi, true);
+  return make_uint2((uint32_t)lo, (uint32_t)hi);
 }
 
 // One wave quantises one bf16 row of length d (a multiple of 8) to FP8 E4M3
