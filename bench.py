@@ -26,7 +26,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
 FP8_PEAK_TFLOPS = 5000.0    # MI355X dense FP8 MFMA, published
 METRIC = "MoE-layer tokens/s at T=64 decode & T=3584 prefill; % of HBM / FP8 MFMA peak"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
 def log(*a):
