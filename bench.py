@@ -462,7 +462,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "prefill", "b100", "skew", "decode_mxfp4"])
+                    choices=["decode", "prefill", "b100", "skew", "decode_mxfp4", "prefill_mxfp4"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the other workloads (prefill, 100B-shaped, skewed, chunked prefill) "
@@ -543,7 +543,7 @@ def main():
     if not args.no_secondary:
         # the other workloads, reported beside the headline (not part of `value`)
         sec_steps, sec_warm = max(5, args.steps // 2), max(2, args.warmup // 2)
-        for name in ("prefill", "b100", "skew", "decode_mxfp4"):
+        for name in ("prefill", "b100", "skew", "decode_mxfp4", "prefill_mxfp4"):
             if name == args.workload:
                 continue
             c2 = CONFIGS[name]

@@ -175,6 +175,31 @@ __device__ inline int scale_of_step(const int (&sr)[KT / 4], int kt, int lane) {
   return __shfl(sr[kt % DW], (lane & 15) + 16 * (kt / DW)) >> (8 * (lane >> 4));
 }
 
+// The tall-tile kernels keep their weight rows' scales in LDS instead (the
+// registers are taken by the staging): row r's 4 KT scale bytes at dwords
+// [r (KT + 1), +KT) -- one dword of padding per row, so the 16 rows of a
+// fragment read fall in 16 different banks. Filled once per workgroup by all
+// NTH threads, 16 global bytes (4 K steps) per piece; rowp(r) is row r's
+// scale bytes in global memory.
+template <int KT, int ROWS, int NTH, typename RowPtr>
+__device__ inline void fill_scale_tile(int* tile, RowPtr rowp, int tid) {
+  constexpr int PPR = KT / 4;  // 16-byte pieces per row
+#pragma unroll
+  for (int i = 0; i < (ROWS * PPR + NTH - 1) / NTH; ++i) {
+    const int p = tid + i * NTH;
+    if (ROWS * PPR % NTH == 0 || p < ROWS * PPR) {
+      const int r = p / PPR, q = p % PPR;
+      const v4i v = *reinterpret_cast<const v4i*>(rowp(r) + 16 * q);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) tile[r * (KT + 1) + 4 * q + t] = v[t];
+    }
+  }
+}
+template <int KT>
+__device__ inline int scale_from_tile(const int* tile, int r, int kt, int lane) {
+  return reinterpret_cast<const uint8_t*>(tile)[4 * (r * (KT + 1) + kt) + (lane >> 4)];
+}
+
 // E4M3 activations x E4M3 weights, or x MXFP4 weights (A scale 2^0, B scale
 // per lane from the fragment; the FP4 operand occupies the low 4 registers).
 __device__ inline v4f mfma_w(const v8i& a, const v8i& b, const v4f& c) {
@@ -490,21 +515,24 @@ __device__ inline void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-template <int BM, int KTC>
+template <int BM, int KTC, bool W4>
 __global__ __launch_bounds__(8 * kWave) void gateup_fp8_lds_kernel(
     FfnCall c, const TileHeader* __restrict__ hdr, const TileEntry* __restrict__ list) {
   constexpr int NW = 8, NTH = NW * kWave;
   constexpr int BMW = BM / 2, MS = BMW / 16;
   constexpr int NS = 2, NB = 2 * NS;
   constexpr int BROWS = 2 * kHN;                     // weight rows per tile
+  constexpr int KB = kstep_bytes<W4>();              // weight bytes per row and K step
   constexpr int NAD = BM * kBK / 1024 / NW;          // A loads per thread per step
-  constexpr int NBD = BROWS * kBK / 1024 / NW;       // B loads per thread per step
+  constexpr int NBD = BROWS * KB / 1024 / NW;        // B loads per thread per step
   static_assert(BM * kBK % (1024 * NW) == 0, "A tile must split into whole wave loads");
+  static_assert(!W4 || KTC % 4 == 0, "MXFP4 scales are held per row in K-step quads");
 
   __shared__ __attribute__((aligned(1024))) uint8_t a0[BM * kBK];
   __shared__ __attribute__((aligned(1024))) uint8_t a1[BM * kBK];
-  __shared__ __attribute__((aligned(1024))) uint8_t b0[BROWS * kBK];
-  __shared__ __attribute__((aligned(1024))) uint8_t b1[BROWS * kBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t b0[BROWS * KB];
+  __shared__ __attribute__((aligned(1024))) uint8_t b1[BROWS * KB];
+  __shared__ int ssc[W4 ? BROWS * (KTC + 1) : 1];  // MXFP4 scale tile
   __shared__ float sxl[BM];
   __shared__ float red[kNWaves][BM];
 
@@ -533,27 +561,46 @@ __global__ __launch_bounds__(8 * kWave) void gateup_fp8_lds_kernel(
     const int src = min(max(S.row_src ? S.row_src[grow] / S.src_div : grow, 0), c.a_rows - 1);
     asrc[i] = a + (size_t)src * d + cch * 16;
   }
-  const uint8_t* w13 = S.w13 + (size_t)g * 2 * F * d;
+  // weight rows: FP8 as the A tile (8 rows of 128 bytes per 1 KiB block);
+  // MXFP4 16 rows of 64 bytes per block, 16-byte chunk q of row r stored at
+  // chunk q ^ ((r / 4) % 4), so the 16 rows a fragment read touches cover all
+  // 16 chunk slots of 256 bytes
+  const size_t wrb = W4 ? d / 2 : d;
+  const uint8_t* w13 = S.w13 + (size_t)g * 2 * F * wrb;
+  auto wrow_of = [&](int rr) { return (rr < kHN) ? ntile * kHN + rr : F + ntile * kHN + (rr - kHN); };
   const uint8_t* bsrc[NBD];
 #pragma unroll
   for (int i = 0; i < NBD; ++i) {
-    const int rr = 8 * (NBD * wave + i) + (lane >> 3);
-    const int cch = (lane & 7) ^ (rr & 7);
-    const int wrow = (rr < kHN) ? ntile * kHN + rr : F + ntile * kHN + (rr - kHN);
-    bsrc[i] = w13 + (size_t)wrow * d + cch * 16;
+    if constexpr (W4) {
+      const int rr = 16 * (NBD * wave + i) + (lane >> 2);
+      const int cch = (lane & 3) ^ ((rr >> 2) & 3);
+      bsrc[i] = w13 + (size_t)wrow_of(rr) * wrb + cch * 16;
+    } else {
+      const int rr = 8 * (NBD * wave + i) + (lane >> 3);
+      const int cch = (lane & 7) ^ (rr & 7);
+      bsrc[i] = w13 + (size_t)wrow_of(rr) * wrb + cch * 16;
+    }
   }
+  // MXFP4: the tile's E8M0 scales into LDS (published by the first barrier)
+  if constexpr (W4)
+    fill_scale_tile<KTC, BROWS, NTH>(
+        ssc, [&](int r) { return S.e13 + ((size_t)g * 2 * F + wrow_of(r)) * (d / 32); }, tid);
   if (tid < BM) {
     const int grow = te.row0 + min(tid, te.nrows - 1);
     const int src = min(max(S.row_src ? S.row_src[grow] / S.src_div : grow, 0), c.a_rows - 1);
     sxl[tid] = c.a_scale[src];
   }
-  const float* s13 = S.s13 + (size_t)g * 2 * F;
   float sg[NS], su[NS];
 #pragma unroll
   for (int jj = 0; jj < NS; ++jj) {
     const int hc = ntile * kHN + wn * 32 + jj * 16 + (lane & 15);
-    sg[jj] = s13[hc];
-    su[jj] = s13[F + hc];
+    if constexpr (W4) {
+      sg[jj] = 1.f;
+      su[jj] = 1.f;
+    } else {
+      sg[jj] = S.s13[(size_t)g * 2 * F + hc];
+      su[jj] = S.s13[(size_t)g * 2 * F + F + hc];
+    }
   }
 
   v4i ra[2][NAD], rb[2][NBD];  // K steps in flight, two deep
@@ -561,7 +608,7 @@ __global__ __launch_bounds__(8 * kWave) void gateup_fp8_lds_kernel(
 #pragma unroll
     for (int i = 0; i < NAD; ++i) ra[slot][i] = *reinterpret_cast<const v4i*>(asrc[i] + kt * kBK);
 #pragma unroll
-    for (int i = 0; i < NBD; ++i) rb[slot][i] = *reinterpret_cast<const v4i*>(bsrc[i] + kt * kBK);
+    for (int i = 0; i < NBD; ++i) rb[slot][i] = *reinterpret_cast<const v4i*>(bsrc[i] + kt * KB);
   };
   auto st = [&](int slot, uint8_t* ad, uint8_t* bd) {
 #pragma unroll
@@ -590,17 +637,31 @@ __global__ __launch_bounds__(8 * kWave) void gateup_fp8_lds_kernel(
   for (int kt = 0; kt < KTC; ++kt) {
     uint8_t* as = (kt % 2 == 0) ? a0 : a1;
     uint8_t* bs = (kt % 2 == 0) ? b0 : b1;
-    v8i bf[NB];
+    BFrag<W4> bf[NB];
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       const int row0 = (j < NS) ? wn * 32 + j * 16 : kHN + wn * 32 + (j - NS) * 16;
-      bf[j] = lds_afrag(bs + row0 * kBK, 0, lane);
+      if constexpr (W4) {
+        const int r = row0 + (lane & 15);
+        bf[j].w = *reinterpret_cast<const v4i*>(bs + r * KB + (((lane >> 4) ^ ((r >> 2) & 3)) << 4));
+        bf[j].s = scale_from_tile<KTC>(ssc, r, kt, lane);
+      } else {
+        bf[j] = lds_afrag(bs + row0 * kBK, 0, lane);
+      }
     }
 #pragma unroll
     for (int i = 0; i < MS; ++i) {
       const v8i af = lds_afrag(as + rbase * kBK, i, lane);
 #pragma unroll
-      for (int j = 0; j < NB; ++j) acc[i][j] = mfma_fp8_16x16x128(af, bf[j], acc[i][j]);
+      for (int j = 0; j < NB; ++j) acc[i][j] = mfma_w(af, bf[j], acc[i][j]);
+    }
+    if constexpr (W4) {
+      // keep the step's block-scaled MFMAs in the step (left free, the
+      // scheduler defers them and runs out of registers)
+#pragma unroll
+      for (int i = 0; i < MS; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) asm volatile("" : "+v"(acc[i][j]));
     }
     if (kt + 1 < KTC) {
       st((kt + 1) % 2, (kt % 2 == 0) ? a1 : a0, (kt % 2 == 0) ? b1 : b0);
@@ -781,23 +842,26 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void down_fp8_kernel(
 // each group's weights are fetched once and the ring fills once. The per-row
 // h block scale of each K step multiplies that step's MFMA partial.
 // ---------------------------------------------------------------------------
-template <int BM, int KTC, int NTW>
+template <int BM, int KTC, int NTW, bool W4>
 __global__ __launch_bounds__(8 * kWave) void down_fp8_lds_kernel(
     FfnCall c, const TileHeader* __restrict__ hdr, const TileEntry* __restrict__ list) {
   constexpr int NW = 8, NTH = NW * kWave;
   constexpr int BMW = BM / 2, MS = BMW / 16;
   constexpr int NB = 4;
+  constexpr int KB = kstep_bytes<W4>();               // weight bytes per row and K step
   constexpr int NAD = BM * kBK / 1024 / NW;           // A loads per thread per step
-  constexpr int NBD = kDownBN * kBK / 1024 / NW;      // B loads per thread per step
+  constexpr int NBD = kDownBN * KB / 1024 / NW;       // B loads per thread per step
   constexpr int NSTEP = NTW * KTC;
   constexpr int HPT = (BM * KTC + NTH - 1) / NTH;
   static_assert(BM * kBK % (1024 * NW) == 0, "A tile must split into whole wave loads");
+  static_assert(!W4 || KTC % 4 == 0, "MXFP4 scales are held per row in K-step quads");
 
   __shared__ __attribute__((aligned(1024))) uint8_t a0[BM * kBK];
   __shared__ __attribute__((aligned(1024))) uint8_t a1[BM * kBK];
-  __shared__ __attribute__((aligned(1024))) uint8_t b0[kDownBN * kBK];
-  __shared__ __attribute__((aligned(1024))) uint8_t b1[kDownBN * kBK];
-  __shared__ __attribute__((aligned(1024))) uint8_t b2[kDownBN * kBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t b0[kDownBN * KB];
+  __shared__ __attribute__((aligned(1024))) uint8_t b1[kDownBN * KB];
+  __shared__ __attribute__((aligned(1024))) uint8_t b2[kDownBN * KB];
+  __shared__ int ssc[W4 ? NTW * kDownBN * (KTC + 1) : 1];  // MXFP4 scale tile
   __shared__ float hsl[KTC][BM];
 
   const int d = c.d, dnt = down_ntiles(d);
@@ -819,15 +883,24 @@ __global__ __launch_bounds__(8 * kWave) void down_fp8_lds_kernel(
     const int cch = (lane & 7) ^ (r & 7);
     asrc[i] = S.h + (size_t)(te.row0 + min(r, te.nrows - 1)) * F + cch * 16;
   }
-  // B load i covers channel rows 8 (NBD wave + i) + lane / 8 of an N tile;
-  // steps past the last N tile re-read its rows (never used)
-  const uint8_t* w2 = S.w2 + (size_t)g * d * F;
+  // B load i covers channel rows 8 (NBD wave + i) + lane / 8 of an N tile
+  // (MXFP4: 16 rows of 64 bytes, chunk q of row r stored at q ^ ((r / 4) % 4),
+  // as in the gate/up kernel); steps past the last N tile re-read its rows
+  // (never used)
+  const size_t wrb = W4 ? F / 2 : F;
+  const uint8_t* w2 = S.w2 + (size_t)g * d * wrb;
   int brow[NBD], bcc[NBD];
 #pragma unroll
   for (int i = 0; i < NBD; ++i) {
-    const int rr = 8 * (NBD * wave + i) + (lane >> 3);
-    brow[i] = rr;
-    bcc[i] = ((lane & 7) ^ (rr & 7)) * 16;
+    if constexpr (W4) {
+      const int rr = 16 * (NBD * wave + i) + (lane >> 2);
+      brow[i] = rr;
+      bcc[i] = ((lane & 3) ^ ((rr >> 2) & 3)) * 16;
+    } else {
+      const int rr = 8 * (NBD * wave + i) + (lane >> 3);
+      brow[i] = rr;
+      bcc[i] = ((lane & 7) ^ (rr & 7)) * 16;
+    }
   }
   auto load_a = [&](int st, uint8_t* dst) {
     const int kt = st % KTC;
@@ -839,7 +912,7 @@ __global__ __launch_bounds__(8 * kWave) void down_fp8_lds_kernel(
 #pragma unroll
     for (int i = 0; i < NBD; ++i) {
       const int ch = min((nt0 + n) * kDownBN + brow[i], d - 1);
-      dma16(w2 + (size_t)ch * F + kt * kBK + bcc[i], dst + (NBD * wave + i) * 1024);
+      dma16(w2 + (size_t)ch * wrb + kt * KB + bcc[i], dst + (NBD * wave + i) * 1024);
     }
   };
   // h block scales of the tile's rows, and every N tile's channel scales
@@ -857,7 +930,19 @@ __global__ __launch_bounds__(8 * kWave) void down_fp8_lds_kernel(
 #pragma unroll
   for (int n = 0; n < NTW; ++n)
 #pragma unroll
-    for (int j = 0; j < NB; ++j) s2v[n][j] = S.s2[(size_t)g * d + min(mcol(n, j), d - 1)];
+    for (int j = 0; j < NB; ++j)
+      s2v[n][j] = W4 ? 1.f : S.s2[(size_t)g * d + min(mcol(n, j), d - 1)];
+  // MXFP4: every N tile's channel rows' E8M0 scales into LDS (published by
+  // the first barrier); tile row n 256 + r is channel (nt0 + n) 256 + r
+  if constexpr (W4)
+    fill_scale_tile<KTC, NTW * kDownBN, NTH>(
+        ssc,
+        [&](int r) {
+          const int n = min(r / kDownBN, dnt - 1 - nt0);
+          const int ch = min((nt0 + n) * kDownBN + r % kDownBN, d - 1);
+          return S.e2 + ((size_t)g * d + ch) * (F / 32);
+        },
+        tid);
 #pragma unroll
   for (int i = 0; i < HPT; ++i) {
     const int e = tid + i * NTH;
@@ -889,16 +974,23 @@ __global__ __launch_bounds__(8 * kWave) void down_fp8_lds_kernel(
     uint8_t* bs = (st % 3 == 0) ? b0 : (st % 3 == 1) ? b1 : b2;
     if (st + 1 < NSTEP) load_a(st + 1, (st % 2 == 0) ? a1 : a0);
     if (st + 2 < NSTEP) load_b(st + 2, (st % 3 == 0) ? b2 : (st % 3 == 1) ? b0 : b1);
-    v8i bf[NB];
+    BFrag<W4> bf[NB];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) bf[j] = lds_afrag(bs + (wn * 64 + j * 16) * kBK, 0, lane);
+    for (int j = 0; j < NB; ++j) {
+      if constexpr (W4) {
+        const int r = wn * 64 + j * 16 + (lane & 15);
+        bf[j].w = *reinterpret_cast<const v4i*>(bs + r * KB + (((lane >> 4) ^ ((r >> 2) & 3)) << 4));
+        bf[j].s = scale_from_tile<KTC>(ssc, n * kDownBN + r, kt, lane);
+      } else {
+        bf[j] = lds_afrag(bs + (wn * 64 + j * 16) * kBK, 0, lane);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < MS; ++i) {
       const v8i af = lds_afrag(as + rbase * kBK, i, lane);
       v4f part[NB];
 #pragma unroll
-      for (int j = 0; j < NB; ++j)
-        part[j] = mfma_fp8_16x16x128(af, bf[j], v4f{0.f, 0.f, 0.f, 0.f});
+      for (int j = 0; j < NB; ++j) part[j] = mfma_w(af, bf[j], v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float hs = hsl[kt][rbase + i * 16 + 4 * (lane >> 4) + q];
@@ -1171,19 +1263,17 @@ __global__ __launch_bounds__(256) void down_f32_kernel(FfnCall c, int sid) {
 template <int BM>
 constexpr int waves_m() { return BM >= 64 ? 2 : 1; }
 
-// W4: MXFP4 weights, which take the register-streaming kernels only (the
-// tall-tile LDS kernels stage FP8 weight rows).
+// W4: MXFP4 weights (every kernel has an MXFP4 variant).
 template <int BM, int KTU, int BMD, int KTD, bool W4>
 hipError_t launch_gemms_bm(const FfnCall& c, TileHeader* hdr, TileEntry* up, TileEntry* dn,
                            size_t cap_u, size_t cap_d, hipStream_t s, const StepEvents& ev) {
   const size_t cu = align_up(cap_u * up_ntiles_max(c), kXcds);
   const size_t cd = align_up(cap_d * down_ntiles(c.d), kXcds);
   constexpr int WU = waves_m<BM>(), WD = waves_m<BMD>();
-  static_assert(!W4 || BMD <= 128, "MXFP4 down tiles are at most 128 rows");
   ev.mark(true, MOE_STEP_GATE_UP, s);
   if (cu > 0) {
-    if constexpr (!W4 && KTU > 0 && BM >= 128)  // tall tiles: both operands through LDS
-      hipLaunchKernelGGL((gateup_fp8_lds_kernel<BM, KTU>), dim3((unsigned)cu), dim3(8 * kWave),
+    if constexpr (KTU > 0 && BM >= 128)  // tall tiles: both operands through LDS
+      hipLaunchKernelGGL((gateup_fp8_lds_kernel<BM, KTU, W4>), dim3((unsigned)cu), dim3(8 * kWave),
                          0, s, c, hdr, up);
     else  // (a fully unrolled K loop of tall tiles would spill: looped there)
       hipLaunchKernelGGL((gateup_fp8_kernel<BM, WU, (BM >= 128 ? 0 : KTU), W4>),
@@ -1192,11 +1282,11 @@ hipError_t launch_gemms_bm(const FfnCall& c, TileHeader* hdr, TileEntry* up, Til
   ev.mark(false, MOE_STEP_GATE_UP, s);
   ev.mark(true, MOE_STEP_DOWN, s);
   if (cap_d > 0) {
-    if constexpr (!W4 && KTD > 0 && BMD >= 128) {
+    if constexpr (KTD > 0 && BMD >= 128) {
       // tall tiles: both operands through LDS, 16 steps per workgroup
       constexpr int NTW = KTD >= 16 ? 1 : 16 / KTD;
       const size_t cdl = align_up(cap_d * ceil_div(down_ntiles(c.d), NTW), kXcds);
-      hipLaunchKernelGGL((down_fp8_lds_kernel<BMD, KTD, NTW>), dim3((unsigned)cdl),
+      hipLaunchKernelGGL((down_fp8_lds_kernel<BMD, KTD, NTW, W4>), dim3((unsigned)cdl),
                          dim3(8 * kWave), 0, s, c, hdr, dn);
     } else if constexpr (KTD > 0 && BMD * KTD * kBK <= 65536) {
       // resident h slab; 64-row tiles: 8 waves, 4 N tiles per workgroup
@@ -1221,11 +1311,11 @@ template <int BM, int BMD, int KTU, bool W4>
 hipError_t launch_gemms_kd(const FfnCall& c, TileHeader* hdr, TileEntry* up, TileEntry* dn,
                            size_t cap_u, size_t cap_d, hipStream_t s, const StepEvents& ev) {
   const int kdn = down_ksteps(c);
-  if constexpr (BMD <= 64 || (!W4 && BMD >= 128)) {
+  if constexpr (BMD <= 64 || BMD >= 128) {
     if (kdn == 8)
       return launch_gemms_bm<BM, KTU, BMD, 8, W4>(c, hdr, up, dn, cap_u, cap_d, s, ev);
   }
-  if constexpr (!W4 && BMD >= 128) {
+  if constexpr (BMD >= 128) {
     if (kdn == 16)
       return launch_gemms_bm<BM, KTU, BMD, 16, W4>(c, hdr, up, dn, cap_u, cap_d, s, ev);
   }
@@ -1251,11 +1341,8 @@ hipError_t launch_gemms_w(const FfnCall& c, int bm, TileHeader* hdr, TileEntry* 
     case 64: return launch_gemms_k<64, 64, W4>(c, hdr, up, dn, cu, cd, s, ev);
     case 128: return launch_gemms_k<128, 128, W4>(c, hdr, up, dn, cu, cd, s, ev);
     default:
-      if constexpr (!W4) {
-        if (down_bm(c, bm) == 192)
-          return launch_gemms_k<192, 192, W4>(c, hdr, up, dn, cu, cd, s, ev);
-      }
-      return launch_gemms_k<192, 128, W4>(c, hdr, up, dn, cu, cd, s, ev);
+      return down_bm(c, bm) == 192 ? launch_gemms_k<192, 192, W4>(c, hdr, up, dn, cu, cd, s, ev)
+                                   : launch_gemms_k<192, 128, W4>(c, hdr, up, dn, cu, cd, s, ev);
   }
 }
 

@@ -66,10 +66,10 @@ __host__ __device__ inline int down_ksteps(const FfnCall& c) {
 // Tile height of the down GEMM for a gate/up tile height: the same up to 32
 // rows; 64 rows stay 64 (h slab resident in LDS when F = 1024); taller tiles
 // keep their height where the tall-tile kernel's K is fixed (F = 1024 or
-// 2048, FP8 weights), else at most 128 (the looped kernel's register tile).
+// 2048), else at most 128 (the looped kernel's register tile).
 __host__ __device__ inline int down_bm(const FfnCall& c, int bm_up) {
   if (bm_up <= 64) return bm_up;
-  if (down_ksteps(c) > 0 && !c.set[0].w4) return bm_up;
+  if (down_ksteps(c) > 0) return bm_up;
   return bm_up < 128 ? bm_up : 128;
 }
 

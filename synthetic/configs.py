@@ -52,8 +52,9 @@ CONFIGS = {
     "skew": LayerConfig("skew", 2048, 4096, 128, 6, 1024, 1024, "fp8", seed=5, skew=True),
     # a mixed batch: a 256-token prefill chunk and 32 decode tokens in one call
     "mixed": LayerConfig("mixed", 288, 4096, 128, 6, 1024, 1024, "fp8", seed=6),
-    # the decode step with MXFP4 expert weights
+    # the decode step and the prefill with MXFP4 expert weights
     "decode_mxfp4": LayerConfig("decode_mxfp4", 64, 4096, 128, 6, 1024, 1024, "mxfp4", seed=2),
+    "prefill_mxfp4": LayerConfig("prefill_mxfp4", 3584, 4096, 128, 6, 1024, 1024, "mxfp4", seed=3),
 }
 
 # Small parity shapes (several tiles, ragged tails).

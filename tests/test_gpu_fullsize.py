@@ -14,7 +14,8 @@ from tests import gpu_helpers as H
 
 pytestmark = pytest.mark.gpu
 
-SAMPLES = {"decode": 64, "prefill": 16, "b100": 10, "skew": 16, "mixed": 24, "decode_mxfp4": 64}
+SAMPLES = {"decode": 64, "prefill": 16, "b100": 10, "skew": 16, "mixed": 24, "decode_mxfp4": 64,
+           "prefill_mxfp4": 16}
 
 
 @pytest.fixture(autouse=True)
@@ -31,7 +32,8 @@ def _sample(T, n, seed, extra=()):
     return np.array(sorted(base | set(rest.tolist())))[: max(n, len(base))]
 
 
-@pytest.mark.parametrize("name", ["decode", "prefill", "b100", "skew", "mixed", "decode_mxfp4"])
+@pytest.mark.parametrize("name", ["decode", "prefill", "b100", "skew", "mixed", "decode_mxfp4",
+                                  "prefill_mxfp4"])
 def test_fullsize_sampled(name):
     cfg = CONFIGS[name]
     lt = H.gen(cfg)
