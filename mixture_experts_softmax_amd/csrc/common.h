@@ -97,6 +97,15 @@ __device__ inline v4f mfma_bf16_16x16x32(const v8bf& a, const v8bf& b, const v4f
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Raw buffer store resource over [base, base + bytes): a lane whose byte
+// offset falls outside that range is dropped by the hardware's range check,
+// so a masked store is still one issued instruction (which keeps hand-counted
+// vmcnt waits exact). Word 3 is the gfx9 value (32-bit data format, required
+// for untyped access).
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, 0x00020000);
+}
+
 __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 }  // namespace moe

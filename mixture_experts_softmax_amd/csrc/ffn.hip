@@ -209,6 +209,15 @@ __device__ inline v4f mfma_w(const v8i& a, const Fp4Frag& b, const v4f& c) {
   const v8i bw = v8i{b.w[0], b.w[1], b.w[2], b.w[3], 0, 0, 0, 0};
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bw, c, 0, 4, 0, 127, 0, b.s);
 }
+// The same products with the weights as the A operand: lane l then holds the
+// four consecutive output channels 4 (l / 16) + q of activation row l % 16.
+__device__ inline v4f mfma_wt(const v8i& w, const v8i& x, const v4f& c) {
+  return mfma_fp8_16x16x128(w, x, c);
+}
+__device__ inline v4f mfma_wt(const Fp4Frag& w, const v8i& x, const v4f& c) {
+  const v8i ww = v8i{w.w[0], w.w[1], w.w[2], w.w[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ww, x, c, 4, 0, 0, w.s, 0, 127);
+}
 
 // The fields of set `sid` (0 or 1), read field by field from the kernel
 // arguments so the compiler keeps them in scalar registers.
@@ -255,7 +264,15 @@ constexpr int prefetch_depth() { return ROWS <= LIMIT ? 3 : 2; }
 // second time from the L2.
 constexpr int kNWaves = 4;
 
-// Gate/up epilogue, shared by the gate/up kernels: x and weight scales,
+// h / s from s's reciprocal and one FMA correction of the quotient: the
+// correctly rounded quotient unless the reciprocal's last-bit error decides
+// it, and then one ulp from it.
+__device__ inline float div_by(float h, float s, float rs) {
+  const float q = h * rs;
+  return fmaf(fmaf(-q, s, h), rs, q);
+}
+
+// Gate/up epilogue, of the register-fed gate/up kernels: x and weight scales,
 // SwiGLU, per-(row, 128-column) amax across the kNWaves N waves (through LDS
 // `red`), then FP8 h codes and their block scale. acc[i][jj] holds gate
 // columns, acc[i][NS + jj] the matching up columns; the wave owns rows
@@ -278,7 +295,7 @@ __device__ inline void gateup_epilogue(v4f (&acc)[MS][2 * NS], const float* sxl,
       for (int jj = 0; jj < NS; ++jj) {
         const float gv = acc[i][jj][q] * sx * sg[jj];
         const float uv = acc[i][NS + jj][q] * sx * su[jj];
-        const float h = gv / (1.0f + __expf(-gv)) * uv;
+        const float h = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
         acc[i][jj][q] = h;
         m = fmaxf(m, fabsf(h));
       }
@@ -298,12 +315,14 @@ __device__ inline void gateup_epilogue(v4f (&acc)[MS][2 * NS], const float* sxl,
 #pragma unroll
       for (int ww = 1; ww < kNWaves; ++ww) am = fmaxf(am, red[ww][r]);
       const float s = (am > 0.f) ? __fdiv_rn(am, kE4M3Max) : 1.0f;
+      const float rs = __builtin_amdgcn_rcpf(s);
       const size_t grow = (size_t)(te.row0 + r);
       uint8_t* hrow = S.h + grow * F;
 #pragma unroll
       for (int jj = 0; jj < NS; ++jj) {
         const int hc = ntile * kHN + wn * WN + jj * 16 + (lane & 15);
-        hrow[hc] = e4m3_encode(__fdiv_rn(acc[i][jj][q], s));
+        hrow[hc] = (uint8_t)__builtin_amdgcn_cvt_pk_fp8_f32(div_by(acc[i][jj][q], s, rs), 0.f, 0,
+                                                            false);
       }
       if (wn == 0 && (lane & 15) == 0) S.h_scale[grow * hblocks + ntile] = s;
     }
@@ -487,6 +506,73 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void gateup_fp8_kernel(
   gateup_epilogue<BM, MS, NS>(acc, sxl, red, sg, su, rbase, wn, lane, te, S, ntile);
 }
 
+// Gate/up epilogue for the transposed product (weights as the MFMA A operand):
+// lane l holds, for tile row rbase + 16 i + l % 16, the four consecutive h
+// columns 16 jj + 4 (l / 16) + q of the wave's 16 NS (gate in acc[i][jj], up in
+// acc[i][NS + jj]). SwiGLU, the row's block amax over the 128 h columns of the
+// tile (the four lanes of a row, then the waves through LDS), its scale
+// amax / 448, and the four E4M3 codes packed into one 32-bit store. The codes
+// come from the packed float32 -> FP8 conversion, which rounds to nearest even
+// and saturates exactly as e4m3_encode does for quotients of magnitude <= 448.
+// `s13` holds the tile's channel scales, gate rows then up rows (FP8 weights).
+template <int BM, int MS, int NS, bool W4>
+__device__ inline void gateup_epilogue_t(v4f (&acc)[MS][2 * NS], const float* sxl,
+                                         float (&red)[kNWaves][BM], const float* s13,
+                                         int rbase, int wn, int lane, const Tile& te,
+                                         const SetView& S, int ntile) {
+  constexpr int WN = NS * 16;
+  const int F = S.F;
+  const int c0 = wn * WN + 4 * (lane >> 4);  // tile h column of (jj, q) = (0, 0)
+#pragma unroll
+  for (int i = 0; i < MS; ++i) {
+    const int r = rbase + i * 16 + (lane & 15);
+    const float sx = sxl[r];
+    float m = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < NS; ++jj) {
+      v4f sg = v4f{1.f, 1.f, 1.f, 1.f}, su = sg;
+      if constexpr (!W4) {
+        sg = *reinterpret_cast<const v4f*>(&s13[c0 + 16 * jj]);
+        su = *reinterpret_cast<const v4f*>(&s13[kHN + c0 + 16 * jj]);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float gv = acc[i][jj][q] * sx * sg[q];
+        const float uv = acc[i][NS + jj][q] * sx * su[q];
+        const float h = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+        acc[i][jj][q] = h;
+        m = fmaxf(m, fabsf(h));
+      }
+    }
+    m = fmaxf(m, __shfl_xor(m, 16, kWave));
+    m = fmaxf(m, __shfl_xor(m, 32, kWave));
+    if (lane < 16) red[wn][r] = m;
+  }
+  __syncthreads();
+  const int hblocks = F / kHN;
+#pragma unroll
+  for (int i = 0; i < MS; ++i) {
+    const int r = rbase + i * 16 + (lane & 15);
+    if (r >= te.nrows) continue;
+    float am = red[0][r];
+#pragma unroll
+    for (int ww = 1; ww < kNWaves; ++ww) am = fmaxf(am, red[ww][r]);
+    const float s = (am > 0.f) ? __fdiv_rn(am, kE4M3Max) : 1.0f;
+    const float rs = __builtin_amdgcn_rcpf(s);
+    const size_t grow = (size_t)(te.row0 + r);
+    uint8_t* hrow = S.h + grow * F + ntile * kHN + c0;
+#pragma unroll
+    for (int jj = 0; jj < NS; ++jj) {
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(div_by(acc[i][jj][0], s, rs),
+                                              div_by(acc[i][jj][1], s, rs), 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(div_by(acc[i][jj][2], s, rs),
+                                          div_by(acc[i][jj][3], s, rs), w, true);
+      *reinterpret_cast<int*>(hrow + 16 * jj) = w;
+    }
+    if (wn == 0 && lane < 16) S.h_scale[grow * hblocks + ntile] = s;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Gate/up GEMM for tall tiles (prefill): both operands staged through LDS, so
 // each weight byte is fetched once per workgroup (the two M halves share it).
@@ -535,6 +621,7 @@ __global__ __launch_bounds__(8 * kWave) void gateup_fp8_lds_kernel(
   __shared__ int ssc[W4 ? BROWS * (KTC + 1) : 1];  // MXFP4 scale tile
   __shared__ float sxl[BM];
   __shared__ float red[kNWaves][BM];
+  __shared__ __attribute__((aligned(16))) float s13l[W4 ? 1 : BROWS];  // channel scales
 
   Tile te;
   if (!pick_tile<BM>(list, hdr->n_up, up_ntiles_max(c), te)) return;
@@ -590,17 +677,8 @@ __global__ __launch_bounds__(8 * kWave) void gateup_fp8_lds_kernel(
     const int src = min(max(S.row_src ? S.row_src[grow] / S.src_div : grow, 0), c.a_rows - 1);
     sxl[tid] = c.a_scale[src];
   }
-  float sg[NS], su[NS];
-#pragma unroll
-  for (int jj = 0; jj < NS; ++jj) {
-    const int hc = ntile * kHN + wn * 32 + jj * 16 + (lane & 15);
-    if constexpr (W4) {
-      sg[jj] = 1.f;
-      su[jj] = 1.f;
-    } else {
-      sg[jj] = S.s13[(size_t)g * 2 * F + hc];
-      su[jj] = S.s13[(size_t)g * 2 * F + F + hc];
-    }
+  if constexpr (!W4) {
+    if (tid < BROWS) s13l[tid] = S.s13[(size_t)g * 2 * F + wrow_of(tid)];
   }
 
   v4i ra[2][NAD], rb[2][NBD];  // K steps in flight, two deep
@@ -653,7 +731,7 @@ __global__ __launch_bounds__(8 * kWave) void gateup_fp8_lds_kernel(
     for (int i = 0; i < MS; ++i) {
       const v8i af = lds_afrag(as + rbase * kBK, i, lane);
 #pragma unroll
-      for (int j = 0; j < NB; ++j) acc[i][j] = mfma_w(af, bf[j], acc[i][j]);
+      for (int j = 0; j < NB; ++j) acc[i][j] = mfma_wt(bf[j], af, acc[i][j]);
     }
     if constexpr (W4) {
       // keep the step's block-scaled MFMAs in the step (left free, the
@@ -671,7 +749,7 @@ __global__ __launch_bounds__(8 * kWave) void gateup_fp8_lds_kernel(
     __builtin_amdgcn_sched_barrier(0);
   }
   __syncthreads();
-  gateup_epilogue<BM, MS, NS>(acc, sxl, red, sg, su, rbase, wn, lane, te, S, ntile);
+  gateup_epilogue_t<BM, MS, NS, W4>(acc, sxl, red, s13l, rbase, wn, lane, te, S, ntile);
 }
 
 // ---------------------------------------------------------------------------
@@ -863,6 +941,7 @@ __global__ __launch_bounds__(8 * kWave) void down_fp8_lds_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t b2[kDownBN * KB];
   __shared__ int ssc[W4 ? NTW * kDownBN * (KTC + 1) : 1];  // MXFP4 scale tile
   __shared__ float hsl[KTC][BM];
+  __shared__ __attribute__((aligned(16))) float s2l[W4 ? 1 : NTW * kDownBN];  // channel scales
 
   const int d = c.d, dnt = down_ntiles(d);
   Tile te;
@@ -923,15 +1002,15 @@ __global__ __launch_bounds__(8 * kWave) void down_fp8_lds_kernel(
     const int r = e / KTC, kt = e % KTC;
     hv[i] = S.h_scale[(size_t)(te.row0 + min(r, te.nrows - 1)) * KTC + kt];
   }
+  // the MFMAs take the weights as A, so lane l accumulates channels
+  // 16 j + 4 (l / 16) + q of the wave's 64 for tile row 16 i + l % 16
   auto mcol = [&](int n, int j) {
-    return (nt0 + n) * kDownBN + wn * (NB * 16) + j * 16 + (lane & 15);
+    return (nt0 + n) * kDownBN + wn * (NB * 16) + j * 16 + 4 * (lane >> 4);
   };
-  float s2v[NTW][NB];
-#pragma unroll
-  for (int n = 0; n < NTW; ++n)
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-      s2v[n][j] = W4 ? 1.f : S.s2[(size_t)g * d + min(mcol(n, j), d - 1)];
+  if constexpr (!W4) {
+    for (int e = tid; e < NTW * kDownBN; e += NTH)
+      s2l[e] = S.s2[(size_t)g * d + min((nt0 + e / kDownBN) * kDownBN + e % kDownBN, d - 1)];
+  }
   // MXFP4: every N tile's channel rows' E8M0 scales into LDS (published by
   // the first barrier); tile row n 256 + r is channel (nt0 + n) 256 + r
   if constexpr (W4)
@@ -954,7 +1033,11 @@ __global__ __launch_bounds__(8 * kWave) void down_fp8_lds_kernel(
   load_a(0, a0);
   if (NSTEP > 1) load_b(1, b1);
 
-  uint16_t* out = static_cast<uint16_t*>(S.out);
+  // output rows of this tile, written with buffer stores (masked lanes are
+  // dropped by the range check, so each store is one instruction for vmcnt)
+  constexpr int NSTV = MS * NB;  // stores per wave per N tile
+  const __amdgpu_buffer_rsrc_t orsrc = buffer_rsrc(
+      static_cast<uint16_t*>(S.out) + (size_t)te.row0 * d, te.nrows * d * 2);
   v4f acc[MS][NB];
 #pragma unroll (NSTEP)
   for (int st = 0; st < NSTEP; ++st) {
@@ -965,10 +1048,14 @@ __global__ __launch_bounds__(8 * kWave) void down_fp8_lds_kernel(
 #pragma unroll
         for (int j = 0; j < NB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
     }
-    if (st + 1 < NSTEP)
-      wait_vmcnt<NBD>();
-    else
+    // the previous N tile's stores, issued after this step's loads, may
+    // stay in flight
+    if (st + 1 == NSTEP)
       wait_vmcnt<0>();
+    else if (kt == 0 && st > 0)
+      wait_vmcnt<NBD + NSTV>();
+    else
+      wait_vmcnt<NBD>();
     __builtin_amdgcn_s_barrier();  // also publishes hsl on the first step
     uint8_t* as = (st % 2 == 0) ? a0 : a1;
     uint8_t* bs = (st % 3 == 0) ? b0 : (st % 3 == 1) ? b1 : b2;
@@ -990,13 +1077,12 @@ __global__ __launch_bounds__(8 * kWave) void down_fp8_lds_kernel(
       const v8i af = lds_afrag(as + rbase * kBK, i, lane);
       v4f part[NB];
 #pragma unroll
-      for (int j = 0; j < NB; ++j) part[j] = mfma_w(af, bf[j], v4f{0.f, 0.f, 0.f, 0.f});
+      for (int j = 0; j < NB; ++j) part[j] = mfma_wt(bf[j], af, v4f{0.f, 0.f, 0.f, 0.f});
+      const float hs = hsl[kt][rbase + i * 16 + (lane & 15)];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float hs = hsl[kt][rbase + i * 16 + 4 * (lane >> 4) + q];
+      for (int j = 0; j < NB; ++j)
 #pragma unroll
-        for (int j = 0; j < NB; ++j) acc[i][j][q] = fmaf(part[j][q], hs, acc[i][j][q]);
-      }
+        for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(part[j][q], hs, acc[i][j][q]);
     }
 #pragma unroll
     for (int i = 0; i < MS; ++i)
@@ -1005,16 +1091,21 @@ __global__ __launch_bounds__(8 * kWave) void down_fp8_lds_kernel(
     if (kt == KTC - 1 && nt0 + n < dnt) {  // this N tile is done: channel scale, bf16
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        const int m = mcol(n, j);
-        if (m >= d) continue;
+        const int m = mcol(n, j);  // d is a multiple of 4: all four or none
+        v4f sc = v4f{1.f, 1.f, 1.f, 1.f};
+        if constexpr (!W4)
+          sc = *reinterpret_cast<const v4f*>(&s2l[n * kDownBN + wn * (NB * 16) + j * 16 +
+                                                  4 * (lane >> 4)]);
 #pragma unroll
         for (int i = 0; i < MS; ++i) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int r = rbase + i * 16 + 4 * (lane >> 4) + q;
-            if (r < te.nrows)
-              out[(size_t)(te.row0 + r) * d + m] = f32_to_bf16(acc[i][j][q] * s2v[n][j]);
-          }
+          const int r = rbase + i * 16 + (lane & 15);
+          const uint32_t lo = f32_to_bf16(acc[i][j][0] * sc[0]) |
+                              ((uint32_t)f32_to_bf16(acc[i][j][1] * sc[1]) << 16);
+          const uint32_t hi = f32_to_bf16(acc[i][j][2] * sc[2]) |
+                              ((uint32_t)f32_to_bf16(acc[i][j][3] * sc[3]) << 16);
+          const int off = (r < te.nrows && m < d) ? (r * d + m) * 2 : -1;
+          __builtin_amdgcn_raw_buffer_store_b64(
+              (__attribute__((ext_vector_type(2))) uint32_t){lo, hi}, orsrc, off, 0, 0);
         }
       }
     }
