@@ -80,6 +80,9 @@ PARITY = {
     "fp8_model_m192": LayerConfig("fp8_model_m192", 380, 4096, 8, 4, 1024, 1024, "fp8", seed=23),
     # the 100B-shaped expert width F = 2048 (16 down K steps) with 128-row tiles
     "fp8_model_f2048": LayerConfig("fp8_model_f2048", 400, 4096, 8, 2, 2048, 2048, "fp8", seed=24),
+    # ~150 rows per expert at F = 1024 select 192-row tiles and the tall down
+    # GEMM; d = 640 leaves its last 256-channel N tile half outside d
+    "fp8_tall_dpart": LayerConfig("fp8_tall_dpart", 600, 640, 8, 2, 1024, 1024, "fp8", seed=26),
     # MXFP4 expert weights (FP8 activations): small and model-shaped
     "mx_small": LayerConfig("mx_small", 45, 512, 16, 4, 256, 256, "mxfp4", seed=31),
     "mx_ragged": LayerConfig("mx_ragged", 203, 1024, 32, 6, 384, 256, "mxfp4", seed=32),
@@ -88,6 +91,7 @@ PARITY = {
     "mx_model_m192": LayerConfig("mx_model_m192", 380, 4096, 8, 4, 1024, 1024, "mxfp4", seed=35),
     "mx_model_m32": LayerConfig("mx_model_m32", 96, 4096, 16, 4, 1024, 1024, "mxfp4", seed=36),
     "mx_model_f2048": LayerConfig("mx_model_f2048", 400, 4096, 8, 2, 2048, 2048, "mxfp4", seed=37),
+    "mx_tall_dpart": LayerConfig("mx_tall_dpart", 600, 640, 8, 2, 1024, 1024, "mxfp4", seed=38),
 }
 
 
