@@ -32,6 +32,7 @@ constexpr int kLogitMinSlice = 256;               // smallest K slice
 constexpr int kLogitTargetWgs = 256;              // aim: at least one workgroup per CU
 constexpr int kTallTokens = 64;                   // tokens per tall-batch logits workgroup
 constexpr int kTallMin = 64;                      // batches above this use the tall kernel
+constexpr int kTallMaxChunks = 8;                 // K chunks per slice of the unrolled tall kernel
 constexpr int kTopkWaves = 16;  // one 64-token tile per top-k workgroup
 constexpr int kTokPerWave = kPermTile / kTopkWaves;
 constexpr int kXcds = 8;
@@ -126,8 +127,16 @@ LogitGrid logit_grid(int T, int d, int E, bool quant) {
   g.n_et = ceil_div(E, kLogitExperts);
   const int nch = d / kLogitChunk;
   const int tiles = max(1, g.n_tt * g.n_et);  // T = 0 still sizes one tile
-  int ks = max(1, min(ceil_div(kLogitTargetWgs, tiles), d / kLogitMinSlice));
+  const int ks_want = ceil_div(kLogitTargetWgs, tiles);
+  int ks = max(1, min(ks_want, d / kLogitMinSlice));
   g.cps = ceil_div(nch, ks);
+  if (T > kTallMin) {
+    // the unrolled tall kernel: the largest of 8, 4, 2 chunks per slice that
+    // still gives at least ks_want slices, when it divides the K chunks
+    int cps = kTallMaxChunks;
+    while (cps > 2 && nch / cps < ks_want) cps /= 2;
+    if (nch % cps == 0) g.cps = cps;
+  }
   g.ks = ceil_div(nch, g.cps);  // no empty slice
   g.n_logit = tiles * g.ks;
   g.n_lblocks = (int)align_up(g.n_logit, kXcds);
@@ -226,6 +235,13 @@ __device__ inline int tall_swz(int r, int q) {  // element offset of 16-byte chu
   return r * kLogitChunk + ((q ^ (r & 15)) << 3);
 }
 
+//
+// CPS > 0: every slice is exactly CPS chunks and the K loop is unrolled, so
+// the wait for each chunk's operands counts exactly the loads issued after
+// them (a loop with a run-time trip count and a conditional second half
+// makes the compiler drain every load in flight once per chunk, prefetches
+// included). CPS = 0: any slice length.
+template <int CPS>
 __global__ __launch_bounds__(kLogitWaves * kWave) void route_logits_tall_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int d, int E,
     LogitGrid g, float* __restrict__ part, uint8_t* __restrict__ xq, float* __restrict__ xs) {
@@ -293,6 +309,36 @@ __global__ __launch_bounds__(kLogitWaves * kWave) void route_logits_tall_kernel(
   store_w(wst, wl[0]);
   load_w(min(c0 + 1, c1 - 1), wst);
   __syncthreads();
+  if constexpr (CPS > 0) {
+    // chunk i: its 8 weight fragments of each MFMA step are read before the
+    // step's MFMAs; the next chunk's weights go to the other LDS stage, and
+    // chunk i + 2's weights and x are loaded (none past the slice)
+#pragma unroll
+    for (int i = 0; i < CPS; ++i) {
+      const int h = i & 1;
+      const uint16_t* wb = wl[h];
+#pragma unroll
+      for (int s2 = 0; s2 < NS; ++s2) {
+        v8bf bf[NB];
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+          const int r = n * 16 + (lane & 15);
+          bf[n] = *reinterpret_cast<const v8bf*>(wb + tall_swz(r, 4 * s2 + (lane >> 4)));
+        }
+#pragma unroll
+        for (int n = 0; n < NB; ++n) acc[n] = mfma_bf16_16x16x32(xa[h][s2], bf[n], acc[n]);
+      }
+      if (i + 1 < CPS) {
+        // the other stage's readers finished at the barrier ending chunk i-1
+        store_w(wst, wl[h ^ 1]);
+        if (i + 2 < CPS) {
+          load_w(c0 + i + 2, wst);
+          load_x(c0 + i + 2, xa[h]);
+        }
+        __syncthreads();
+      }
+    }
+  } else {
   for (int c = c0; c < c1; c += 2) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -315,6 +361,7 @@ __global__ __launch_bounds__(kLogitWaves * kWave) void route_logits_tall_kernel(
         __syncthreads();
       }
     }
+  }
   }
   float* out = part + (size_t)kz * T * E;
 #pragma unroll
@@ -614,7 +661,11 @@ size_t route_partial_rows(int T, int d, int E) {
   const size_t n_et = ceil_div(E, kLogitExperts);
   const size_t a = (size_t)T * max(1, d / kLogitMinSlice);
   const size_t b = (size_t)T + ceil_div(kLogitTargetWgs * kTallTokens, (int)n_et);
-  return a < b ? a : b;
+  // the tall kernel's power-of-two chunk counts give fewer than twice the
+  // wanted slices, or d / (8 x 128) slices where the 8-chunk cap binds
+  const size_t c = (size_t)T * max(1, d / (kLogitChunk * kTallMaxChunks));
+  const size_t bc = 2 * b > c ? 2 * b : c;
+  return a < bc ? a : bc;
 }
 
 size_t route_ws_bytes(int T, int d, int E) {
@@ -631,11 +682,22 @@ hipError_t launch_route(bool bf16, const void* x, const void* w_router, const fl
     const LogitGrid g = logit_grid(T, d, E, xq != nullptr);
     ks = g.ks;
     if ((size_t)ks * T > route_partial_rows(T, d, E)) return hipErrorInvalidValue;
-    if (T > kTallMin)
-      hipLaunchKernelGGL(route_logits_tall_kernel, dim3(g.n_lblocks + g.n_quant),
-                         dim3(kLogitWaves * kWave), 0, s, static_cast<const uint16_t*>(x),
-                         static_cast<const uint16_t*>(w_router), T, d, E, g, part, xq, x_scale);
-    else
+    if (T > kTallMin) {
+      const bool exact = g.cps * g.ks == d / kLogitChunk;
+#define MOE_TALL(C)                                                                      \
+  hipLaunchKernelGGL(route_logits_tall_kernel<C>, dim3(g.n_lblocks + g.n_quant),         \
+                     dim3(kLogitWaves * kWave), 0, s, static_cast<const uint16_t*>(x), \
+                     static_cast<const uint16_t*>(w_router), T, d, E, g, part, xq, x_scale)
+      if (exact && g.cps == 8)
+        MOE_TALL(8);
+      else if (exact && g.cps == 4)
+        MOE_TALL(4);
+      else if (exact && g.cps == 2)
+        MOE_TALL(2);
+      else
+        MOE_TALL(0);
+#undef MOE_TALL
+    } else
       hipLaunchKernelGGL(route_logits_bf16_kernel, dim3(g.n_lblocks + g.n_quant),
                          dim3(kLogitWaves * kWave), 0, s, static_cast<const uint16_t*>(x),
                          static_cast<const uint16_t*>(w_router), T, d, E, g, part, xq, x_scale);
