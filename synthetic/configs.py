@@ -71,6 +71,8 @@ PARITY = {
                                   seed=19, skew=True),
     # the largest expert count: two 128-expert router tiles, a ragged token tail
     "fp8_e256": LayerConfig("fp8_e256", 130, 512, 256, 8, 128, 128, "fp8", seed=25),
+    # two expert tiles in the tall-batch router at d = 1024, a ragged token tail
+    "fp8_e256_rows": LayerConfig("fp8_e256_rows", 150, 1024, 256, 8, 128, 128, "fp8", seed=27),
     # the model's d = 4096 and F = 1024 (the shapes with fully unrolled K
     # loops) at few tokens, one per GEMM tile height: ~12, 24, 100 and 190
     # rows per expert select 16-, 32-, 128- and 192-row tiles
