@@ -443,9 +443,12 @@ def cpu_baseline(cfg, lt, n_tokens):
     ids = omoe.topk_ids(omoe.router_logits(x64, omoe.router_weight(inp), inp.router_bias), cfg.k)
     for e in np.unique(ids):
         inp.expert(int(e))
-    t = time.perf_counter()
-    omoe.layer_forward_tokens(inp, tok)
-    dt = time.perf_counter() - t
+    runs = []
+    for _ in range(3):  # the median of three runs
+        t = time.perf_counter()
+        omoe.layer_forward_tokens(inp, tok)
+        runs.append(time.perf_counter() - t)
+    dt = sorted(runs)[1]
     try:
         import threadpoolctl
         cores = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] + [1])
@@ -453,7 +456,8 @@ def cpu_baseline(cfg, lt, n_tokens):
         cores = os.cpu_count() or 1
     return dict(value=round(n_tokens / dt, 3), unit="tokens/s", cores=int(cores), kind="oracle",
                 sample=f"first {n_tokens} tokens of the {cfg.name} workload (T={cfg.T}), "
-                       f"{len(np.unique(ids))} touched experts, {dt:.1f}s of float64 numpy")
+                       f"{len(np.unique(ids))} touched experts, {dt:.1f}s of float64 numpy per "
+                       f"run, median of 3 runs ({sum(runs):.1f}s in all)")
 
 
 def main():
