@@ -76,6 +76,9 @@ QK_PARITY = {
     "qk_idle_lanes": QkConfig("qk_idle_lanes", 7, 2, 1, 128, "bf16", "halves", "random", seed=51),
     "qk_idle_lanes_f32": QkConfig("qk_idle_lanes_f32", 7, 1, 0, 256, "f32", "interleaved",
                                   "random", seed=52, pad=4),
+    # over a thousand tokens of float32 heads, an odd count
+    "qk_many_tail_f32": QkConfig("qk_many_tail_f32", 1030, 4, 2, 128, "f32", "interleaved",
+                                 "prefill", seed=54),
     # 2048 chunks per token: two passes of 1024 threads
     "qk_two_passes": QkConfig("qk_two_passes", 3, 120, 8, 128, "bf16", "interleaved", "decode",
                               seed=53),
