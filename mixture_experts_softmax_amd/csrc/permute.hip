@@ -2,8 +2,8 @@
 // token order inside each expert's group (the scatter the InferX page, section
 // 3.3, places after its top-k router). Deterministic, no global atomics:
 //   1. count:   per 64-token tile, a 64-bit token mask per expert (ds_or in
-//               LDS) and its popcount. The layer path gets both from the
-//               top-k kernel instead.
+//               LDS). The layer path gets the masks from the top-k kernel
+//               instead (each of its workgroups writes a 16-token slice).
 //   2. scan:    one workgroup; per expert an exclusive prefix over tiles (tile
 //               counts staged through LDS in chunks), then an exclusive prefix
 //               over experts gives offsets[E+1]. In the layer path the same
@@ -44,11 +44,13 @@ __global__ __launch_bounds__(kPermTile) void perm_count_kernel(const int32_t* __
   }
 }
 
-// One workgroup. counts [ntiles][E] is replaced by the per-tile bases. With
+// One workgroup. Tile counts are the popcounts of the tile masks; counts
+// [ntiles][E] receives the per-tile bases. With
 // hdr != nullptr also emits the tile lists of `c` (set 0 = the E routed
 // groups with these offsets, set 1 = the shared expert if present).
 __global__ __launch_bounds__(kScanThreads) void perm_scan_kernel(
-    int32_t* __restrict__ counts, int ntiles, int E, int32_t* __restrict__ offsets, FfnCall c,
+    const uint64_t* __restrict__ masks, int32_t* __restrict__ counts, int ntiles, int E,
+    int32_t* __restrict__ offsets, FfnCall c,
     int bm, TileHeader* hdr, TileEntry* up, TileEntry* down, int cap_up, int cap_dn) {
   __shared__ int stage[kScanStage];
   __shared__ int tot[MOE_MAX_E];
@@ -58,7 +60,7 @@ __global__ __launch_bounds__(kScanThreads) void perm_scan_kernel(
   const int ct = kScanStage / E;  // tiles per chunk
   for (int t0 = 0; t0 < ntiles; t0 += ct) {
     const int nt = min(ct, ntiles - t0);
-    for (int i = tid; i < nt * E; i += kScanThreads) stage[i] = counts[(size_t)t0 * E + i];
+    for (int i = tid; i < nt * E; i += kScanThreads) stage[i] = __popcll(masks[(size_t)t0 * E + i]);
     __syncthreads();
     if (tid < E) {
       for (int t = 0; t < nt; ++t) {
@@ -160,8 +162,8 @@ hipError_t launch_perm_scan_scatter(const int32_t* ids, int T, int E, int k, uin
     cc = *c;
     tile_lists(cc, bm, tiles_ws, &hdr, &up, &dn, &cap_up, &cap_dn);
   }
-  hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, counts, ntiles, E,
-                     offsets, cc, bm, hdr, up, dn, cap_up, cap_dn);
+  hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, masks, counts, ntiles,
+                     E, offsets, cc, bm, hdr, up, dn, cap_up, cap_dn);
   hipLaunchKernelGGL(perm_scatter_kernel, dim3(ntiles), dim3(kPermTile), 0, s, ids, T, E, k, masks,
                      counts, offsets, sorted_pair, pair_to_row);
   return hipGetLastError();

@@ -33,8 +33,9 @@ constexpr int kLogitTargetWgs = 256;              // aim: at least one workgroup
 constexpr int kTallTokens = 64;                   // tokens per tall-batch logits workgroup
 constexpr int kTallMin = 64;                      // batches above this use the tall kernel
 constexpr int kTallMaxChunks = 8;                 // K chunks per slice of the unrolled tall kernel
-constexpr int kTopkWaves = 16;  // one 64-token tile per top-k workgroup
-constexpr int kTokPerWave = kPermTile / kTopkWaves;
+constexpr int kTopkWaves = 16;      // fused permutation: one 64-token tile per workgroup
+constexpr int kTopkWavesTall = 4;   // otherwise 16 tokens per workgroup
+constexpr int kTokPerWave = 4;      // 16 lanes per token
 constexpr int kXcds = 8;
 
 constexpr int kQuantGroup = 8;  // 16-byte loads per lane in flight per group
@@ -393,14 +394,17 @@ __global__ __launch_bounds__(kLogitWaves * kWave) void route_logits_f32_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Top-k over the logits of one 64-token tile. Each wave serves 4 tokens at
-// once: the 16 lanes [16q, 16q + 16) take token 4w + q, lane s holding the
+// Top-k over the logits of 64 tokens (NW = 16 waves, the fused permutation)
+// or 16 (NW = 4 waves, a quarter of a permutation tile: more workgroups for
+// the VALU-bound selection). Each wave serves 4 tokens at once: the 16 lanes
+// [16q, 16q + 16) take token 4w + q, lane s holding the
 // PL = ceil(E/16) experts [s PL, s PL + PL). A logit is the sum of its K
 // slices in slice order, plus the bias. k rounds of a 16-lane (value desc,
-// index asc) argmax butterfly. Records, per expert, the 64-bit mask of the
-// tile's tokens routed to it; then either writes masks and popcounts (the
-// permutation's per-tile histogram) or, with FUSED (the batch is this one
-// tile), performs the permutation itself.
+// index asc) argmax butterfly. Records, per expert, the mask of its tokens
+// routed to it; then either writes them into the 64-bit tile masks (the
+// permutation's per-tile histogram: its own bits, the scan counts by
+// popcount) or, with FUSED (the batch is this one tile), performs the
+// permutation itself.
 // ---------------------------------------------------------------------------
 constexpr int kPerLane16 = MOE_MAX_E / 16;  // logits held per lane, at most
 
@@ -472,8 +476,8 @@ __device__ inline uint64_t max16_u64(uint64_t v) {
 // PL4 > 0: E = 64 PL4, lane logits read as PL4 16-byte vectors per K slice;
 // PL4 = 0: any E, scalar reads. Either way every read of a batch of K slices
 // is issued before the first is used, and the slices are added in order.
-template <bool FUSED, int PL4>
-__global__ __launch_bounds__(kTopkWaves * kWave) void route_topk_kernel(
+template <bool FUSED, int PL4, int NW>
+__global__ __launch_bounds__(NW * kWave) void route_topk_kernel(
     const float* __restrict__ part, int ks, const float* __restrict__ bias, int T, int E, int k,
     int32_t* __restrict__ ids, float* __restrict__ wts, uint64_t* __restrict__ masks,
     int32_t* __restrict__ counts, TopkPermute po, FfnCall c) {
@@ -481,11 +485,13 @@ __global__ __launch_bounds__(kTopkWaves * kWave) void route_topk_kernel(
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int sub = lane & 15;
-  const int tl = wave * kTokPerWave + (lane >> 4);  // token within the tile
-  const int t = blockIdx.x * kPermTile + tl;
+  constexpr int TPW = NW * kTokPerWave;             // tokens per workgroup
+  static_assert(TPW == kPermTile || TPW == 16, "a workgroup takes a tile or a 16-bit slice");
+  const int tl = wave * kTokPerWave + (lane >> 4);  // token within the workgroup
+  const int t = blockIdx.x * TPW + tl;
   const bool track = FUSED || masks != nullptr;
   if (track) {
-    for (int e = threadIdx.x; e < E; e += kTopkWaves * kWave) mask[e] = 0ull;
+    for (int e = threadIdx.x; e < E; e += NW * kWave) mask[e] = 0ull;
     __syncthreads();
   }
   const bool live = t < T;
@@ -590,9 +596,18 @@ __global__ __launch_bounds__(kTopkWaves * kWave) void route_topk_kernel(
   if (!track) return;
   __syncthreads();
   if constexpr (!FUSED) {
-    for (int e = threadIdx.x; e < E; e += kTopkWaves * kWave) {
-      masks[(size_t)blockIdx.x * E + e] = mask[e];
-      counts[(size_t)blockIdx.x * E + e] = __popcll(mask[e]);
+    if constexpr (TPW == kPermTile) {
+      for (int e = threadIdx.x; e < E; e += NW * kWave) {
+        masks[(size_t)blockIdx.x * E + e] = mask[e];
+        counts[(size_t)blockIdx.x * E + e] = __popcll(mask[e]);
+      }
+    } else {
+      // this workgroup's 16 tokens are bits [16 part, 16 part + 16) of the
+      // tile's masks: bytes 2 part, 2 part + 1 of each (the four workgroups
+      // of a tile write disjoint bytes; the scan counts by popcount)
+      const int tile = blockIdx.x / (kPermTile / TPW), part = blockIdx.x % (kPermTile / TPW);
+      for (int e = threadIdx.x; e < E; e += NW * kWave)
+        reinterpret_cast<uint16_t*>(masks + (size_t)tile * E + e)[part] = (uint16_t)mask[e];
     }
   } else {
     // the permutation of this one tile: group sizes are the mask popcounts,
@@ -706,7 +721,11 @@ hipError_t launch_route(bool bf16, const void* x, const void* w_router, const fl
                        dim3(kLogitWaves * kWave), 0, s, static_cast<const float*>(x),
                        static_cast<const float*>(w_router), T, d, E, part);
   }
-  const dim3 grid(ceil_div(T, kPermTile)), block(kTopkWaves * kWave);
+  // fused: one workgroup of 16 waves; otherwise 16-token workgroups, four
+  // per 64-token tile (past T too, so every byte of the masks is written)
+  const dim3 grid_f(ceil_div(T, kPermTile)), block_f(kTopkWaves * kWave);
+  const dim3 grid_t(ceil_div(T, kPermTile) * (kPermTile / (kTopkWavesTall * kTokPerWave))),
+      block_t(kTopkWavesTall * kWave);
   TopkPermute po{};
   FfnCall c{};
   if (fuse != nullptr && T <= kPermTile) {
@@ -721,9 +740,13 @@ hipError_t launch_route(bool bf16, const void* x, const void* w_router, const fl
   }
   const bool fused = po.offsets != nullptr;
   const int pl4 = (E % 64 == 0) ? E / 64 : 0;
-#define MOE_TOPK(F, P)                                                                          \
-  hipLaunchKernelGGL((route_topk_kernel<F, P>), grid, block, 0, s, part, ks, bias, T, E, k, ids, \
-                     w, masks, counts, po, c)
+#define MOE_TOPK(F, P)                                                                       \
+  if constexpr (F)                                                                            \
+    hipLaunchKernelGGL((route_topk_kernel<F, P, kTopkWaves>), grid_f, block_f, 0, s, part, ks, \
+                       bias, T, E, k, ids, w, masks, counts, po, c);                          \
+  else                                                                                        \
+    hipLaunchKernelGGL((route_topk_kernel<F, P, kTopkWavesTall>), grid_t, block_t, 0, s, part, \
+                       ks, bias, T, E, k, ids, w, masks, counts, po, c)
 #define MOE_TOPK_F(F)        \
   switch (pl4) {             \
     case 1: MOE_TOPK(F, 1); break; \
