@@ -562,21 +562,30 @@ __global__ __launch_bounds__(NW * kWave) void route_topk_kernel(
   // lowest index first among equal logits. Branch-free: per round the lane's
   // largest remaining key, the row's largest by DPP butterfly, and the owner
   // clears it.
-  uint64_t key[kPerLane16];
+  // KL key slots can be live: 4 PL4 when E = 64 PL4, else all kPerLane16
+  constexpr int KL = PL4 > 0 ? 4 * PL4 : kPerLane16;
+  uint64_t key[KL];
 #pragma unroll
-  for (int cc = 0; cc < kPerLane16; ++cc) {
+  for (int cc = 0; cc < KL; ++cc) {
     const int e = ebase + cc;
     key[cc] = (cc < PL && e < E) ? logit_key(v[cc], e) : 0ull;
   }
   int my_e = 0;
   float my_v = -FLT_MAX, top = 0.f;
   for (int j = 0; j < k; ++j) {
-    uint64_t best = key[0];
+    // the lane's largest key by a pairwise tree (depth log2 KLP, not KL - 1;
+    // slots past KL hold key 0, below every real key)
+    constexpr int KLP = KL <= 4 ? 4 : KL <= 8 ? 8 : 16;
+    uint64_t m[KLP];
 #pragma unroll
-    for (int cc = 1; cc < kPerLane16; ++cc) best = key[cc] > best ? key[cc] : best;
-    best = max16_u64(best);
+    for (int cc = 0; cc < KLP; ++cc) m[cc] = cc < KL ? key[cc] : 0ull;
 #pragma unroll
-    for (int cc = 0; cc < kPerLane16; ++cc) key[cc] = key[cc] == best ? 0ull : key[cc];
+    for (int w = KLP / 2; w >= 1; w /= 2)
+#pragma unroll
+      for (int cc = 0; cc < w; ++cc) m[cc] = m[cc + w] > m[cc] ? m[cc + w] : m[cc];
+    const uint64_t best = max16_u64(m[0]);
+#pragma unroll
+    for (int cc = 0; cc < KL; ++cc) key[cc] = key[cc] == best ? 0ull : key[cc];
     const int bi = key_expert(best);
     const float bv = key_logit(best);
     if (j == 0) top = bv;
