@@ -117,6 +117,8 @@ __device__ inline void quantize_row(const uint16_t* __restrict__ xr, int d, int 
 // ---------------------------------------------------------------------------
 struct LogitGrid {
   int n_tt, n_et, ks, cps;  // token tiles, expert tiles, K slices, chunks per slice
+  int ksplit;               // decode kernel: waves of a workgroup on 4 K slices (1) or on 4
+                            // expert groups (0); with 1 it writes ks / 4 partial slices
   int n_logit;              // logits work items
   int n_lblocks;            // logits blocks: n_logit rounded up to a multiple of the XCDs
   int n_quant;              // quantisation workgroups
@@ -139,7 +141,9 @@ LogitGrid logit_grid(int T, int d, int E, bool quant) {
     if (nch % cps == 0) g.cps = cps;
   }
   g.ks = ceil_div(nch, g.cps);  // no empty slice
-  g.n_logit = tiles * g.ks;
+  g.ksplit = (T <= kTallMin && g.ks % kLogitWaves == 0) ? 1 : 0;
+  // with ksplit a workgroup takes one 32-expert group over kLogitWaves slices
+  g.n_logit = g.ksplit ? g.n_tt * ceil_div(E, 32) * (g.ks / kLogitWaves) : tiles * g.ks;
   g.n_lblocks = (int)align_up(g.n_logit, kXcds);
   g.n_quant = quant ? ceil_div(T, kLogitWaves) : 0;
   return g;
@@ -155,6 +159,11 @@ __device__ inline void load_chunk(const uint16_t* xr, const uint16_t* w0, const 
   }
 }
 
+// KSPLIT: the four waves take four consecutive K slices of one 32-expert
+// group and add their sums through LDS in wave order, so the workgroup
+// writes one partial of ks / 4 (the top-k kernel then reads a quarter of the
+// partial logits).
+template <bool KSPLIT>
 __global__ __launch_bounds__(kLogitWaves * kWave) void route_logits_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int d, int E,
     LogitGrid g, float* __restrict__ part, uint8_t* __restrict__ xq, float* __restrict__ xs) {
@@ -173,12 +182,22 @@ __global__ __launch_bounds__(kLogitWaves * kWave) void route_logits_bf16_kernel(
   const int wi = (b % kXcds) * per_xcd + b / kXcds;
   if (wi >= g.n_logit) return;
   const int tt = wi % g.n_tt;
-  const int et = (wi / g.n_tt) % g.n_et;
-  const int kz = wi / (g.n_tt * g.n_et);
+  int kz, eb, kzo;  // the wave's K slice, its first expert, the output slice
+  if constexpr (KSPLIT) {
+    const int n_eg = ceil_div(E, 32);
+    const int eg = (wi / g.n_tt) % n_eg;
+    kzo = wi / (g.n_tt * n_eg);
+    kz = kzo * kLogitWaves + wave;
+    eb = eg * 32;
+  } else {
+    const int et = (wi / g.n_tt) % g.n_et;
+    kz = wi / (g.n_tt * g.n_et);
+    kzo = kz;
+    eb = et * kLogitExperts + wave * 32;
+  }
 
   const int tok = min(tt * kRouteTokens + (lane & 15), T - 1);
   const int kq = (lane >> 4) * 8;  // the lane's 8 K elements of each 32-deep MFMA step
-  const int eb = et * kLogitExperts + wave * 32;
   const uint16_t* xr = x + (size_t)tok * d + kq;
   const uint16_t* w0 = wr + (size_t)min(eb + (lane & 15), E - 1) * d + kq;
   const uint16_t* w1 = wr + (size_t)min(eb + 16 + (lane & 15), E - 1) * d + kq;
@@ -208,7 +227,19 @@ __global__ __launch_bounds__(kLogitWaves * kWave) void route_logits_bf16_kernel(
     }
     load_chunk(xr, w0, w1, min(c + 3, c1 - 1) * kLogitChunk, xa[1], b0[1], b1[1]);
   }
-  float* out = part + (size_t)kz * T * E;
+  if constexpr (KSPLIT) {
+    __shared__ v4f red[kLogitWaves][2][kWave];
+    red[wave][0][lane] = a0;
+    red[wave][1][lane] = a1;
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int w = 1; w < kLogitWaves; ++w) {
+      a0 += red[w][0][lane];
+      a1 += red[w][1][lane];
+    }
+  }
+  float* out = part + (size_t)kzo * T * E;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int t = tt * kRouteTokens + 4 * (lane >> 4) + q;
@@ -704,7 +735,7 @@ hipError_t launch_route(bool bf16, const void* x, const void* w_router, const fl
   int ks = 1;
   if (bf16) {
     const LogitGrid g = logit_grid(T, d, E, xq != nullptr);
-    ks = g.ks;
+    ks = g.ksplit ? g.ks / kLogitWaves : g.ks;  // partial slices the top-k sums
     if ((size_t)ks * T > route_partial_rows(T, d, E)) return hipErrorInvalidValue;
     if (T > kTallMin) {
       const bool exact = g.cps * g.ks == d / kLogitChunk;
@@ -721,10 +752,15 @@ hipError_t launch_route(bool bf16, const void* x, const void* w_router, const fl
       else
         MOE_TALL(0);
 #undef MOE_TALL
-    } else
-      hipLaunchKernelGGL(route_logits_bf16_kernel, dim3(g.n_lblocks + g.n_quant),
+    } else if (g.ksplit) {
+      hipLaunchKernelGGL(route_logits_bf16_kernel<true>, dim3(g.n_lblocks + g.n_quant),
                          dim3(kLogitWaves * kWave), 0, s, static_cast<const uint16_t*>(x),
                          static_cast<const uint16_t*>(w_router), T, d, E, g, part, xq, x_scale);
+    } else {
+      hipLaunchKernelGGL(route_logits_bf16_kernel<false>, dim3(g.n_lblocks + g.n_quant),
+                         dim3(kLogitWaves * kWave), 0, s, static_cast<const uint16_t*>(x),
+                         static_cast<const uint16_t*>(w_router), T, d, E, g, part, xq, x_scale);
+    }
   } else {
     hipLaunchKernelGGL(route_logits_f32_kernel, dim3(ceil_div(T, kLogitWaves)),
                        dim3(kLogitWaves * kWave), 0, s, static_cast<const float*>(x),
