@@ -70,12 +70,36 @@ __device__ inline uint2 encode8(const v4i& c, float s) {
 
 // One wave quantises one bf16 row of length d (a multiple of 8) to FP8 E4M3
 // with scale amax/448: an amax pass and an encode pass, each issuing its
-// 16-byte loads in groups of 8 per lane. Loads are unconditional (chunk index
+// 16-byte loads in groups of 8 per lane (one pass over registers when the
+// row is a single group). Loads are unconditional (chunk index
 // clamped: a repeated chunk changes no maximum and is never stored) and the
 // codes are computed before the guarded stores, so no store waits on a load.
 __device__ inline void quantize_row(const uint16_t* __restrict__ xr, int d, int lane,
                                     uint8_t* __restrict__ qr, float* __restrict__ s_out) {
   const int nch = d / 8;  // 8-element chunks in the row
+  if (nch <= kWave * kQuantGroup) {
+    // the row fits one load group (d <= 4096): it stays in registers between
+    // the maximum and the encode, so it is read once
+    v4i v[kQuantGroup];
+#pragma unroll
+    for (int i = 0; i < kQuantGroup; ++i)
+      v[i] = *reinterpret_cast<const v4i*>(xr + (size_t)min(i * kWave + lane, nch - 1) * 8);
+    float am = 0.f;
+#pragma unroll
+    for (int i = 0; i < kQuantGroup; ++i) am = absmax8(v[i], am);
+    am = wave_max(am);
+    const float sc = (am > 0.f) ? __fdiv_rn(am, kE4M3Max) : 1.0f;
+    uint2 q[kQuantGroup];
+#pragma unroll
+    for (int i = 0; i < kQuantGroup; ++i) q[i] = encode8(v[i], sc);
+#pragma unroll
+    for (int i = 0; i < kQuantGroup; ++i) {
+      const int c = i * kWave + lane;
+      if (c < nch) *reinterpret_cast<uint2*>(qr + (size_t)c * 8) = q[i];
+    }
+    if (lane == 0) *s_out = sc;
+    return;
+  }
   float amax = 0.f;
   for (int c0 = 0; c0 < nch; c0 += kWave * kQuantGroup) {
     v4i v[kQuantGroup];
