@@ -676,9 +676,11 @@ __global__ __launch_bounds__(NW * kWave) void route_topk_kernel(
   } else {
     // the permutation of this one tile: group sizes are the mask popcounts,
     // offsets their exclusive scan (wave 0, 4 experts per lane), a pair's row
-    // its group offset plus the number of earlier tokens in the group
+    // its group offset plus the number of earlier tokens in the group. The
+    // same wave writes the FFN work lists: the groups' M-tile counts scanned
+    // alongside, each lane writing the entries of its own groups (the order
+    // and `first` indices of emit_tiles: routed groups, then the shared one)
     __shared__ int offs[MOE_MAX_E + 1];
-    __shared__ TileLds L;
     if (wave == 0) {
       constexpr int per = MOE_MAX_E / kWave;
       int cnt[per], sum = 0;
@@ -689,17 +691,13 @@ __global__ __launch_bounds__(NW * kWave) void route_topk_kernel(
         sum += cnt[i];
       }
       int acc = wave_incl_scan(sum, lane) - sum;
+      const int row_start = acc;
 #pragma unroll
       for (int i = 0; i < per; ++i) {
         const int e = lane * per + i;
         if (e < E) {
           offs[e] = acc;
           po.offsets[e] = acc;
-          if (po.hdr != nullptr) {
-            L.g_row0[e] = acc;
-            L.g_rows[e] = cnt[i];
-            L.g_set[e] = 0;
-          }
         }
         acc += cnt[i];
       }
@@ -707,10 +705,44 @@ __global__ __launch_bounds__(NW * kWave) void route_topk_kernel(
         offs[E] = acc;
         po.offsets[E] = acc;
       }
-      if (lane == 0 && po.hdr != nullptr && c.nsets > 1) {
-        L.g_row0[E] = 0;
-        L.g_rows[E] = min(c.set[1].rows_fixed, c.set[1].max_rows);
-        L.g_set[E] = 1;
+      if (po.hdr != nullptr) {
+        const int bm = po.bm, bmd = down_bm(c, bm);
+        int su = 0, sd = 0;
+#pragma unroll
+        for (int i = 0; i < per; ++i) {
+          su += ceil_div(cnt[i], bm);
+          sd += ceil_div(cnt[i], bmd);
+        }
+        int pu = wave_incl_scan(su, lane) - su, pd = wave_incl_scan(sd, lane) - sd;
+        int r0 = row_start;
+        auto put = [&](TileEntry* list, int cap, int first, int n, const TileEntry& te) {
+          for (int m = 0; m < n; ++m)
+            if (first + m < cap) list[first + m] = te;
+        };
+#pragma unroll
+        for (int i = 0; i < per; ++i) {
+          const int e = lane * per + i;
+          if (e < E && cnt[i] > 0) {
+            const int mu = ceil_div(cnt[i], bm), md = ceil_div(cnt[i], bmd);
+            put(po.up, po.cap_up, pu, mu, TileEntry{r0, cnt[i], e, pu});
+            put(po.dn, po.cap_dn, pd, md, TileEntry{r0, cnt[i], e, pd});
+            pu += mu;
+            pd += md;
+          }
+          r0 += cnt[i];
+        }
+        if (lane == kWave - 1) {  // holds the routed totals: the shared group last
+          const int nsh = c.nsets > 1 ? min(c.set[1].rows_fixed, c.set[1].max_rows) : 0;
+          if (nsh > 0) {
+            const int mu = ceil_div(nsh, bm), md = ceil_div(nsh, bmd);
+            put(po.up, po.cap_up, pu, mu, TileEntry{0, nsh, 1 << 16, pu});
+            put(po.dn, po.cap_dn, pd, md, TileEntry{0, nsh, 1 << 16, pd});
+            pu += mu;
+            pd += md;
+          }
+          po.hdr->n_up = min(pu, po.cap_up);
+          po.hdr->n_down = min(pd, po.cap_dn);
+        }
       }
     }
     __syncthreads();
@@ -721,9 +753,6 @@ __global__ __launch_bounds__(NW * kWave) void route_topk_kernel(
       po.sorted_pair[row] = p;
       po.pair_to_row[p] = row;
     }
-    if (po.hdr != nullptr)
-      emit_tiles(c, po.bm, E + (c.nsets > 1 ? 1 : 0), E, L, po.hdr, po.up, po.dn, po.cap_up,
-                 po.cap_dn);
   }
 }
 
