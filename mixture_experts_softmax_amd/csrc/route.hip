@@ -705,45 +705,9 @@ __global__ __launch_bounds__(NW * kWave) void route_topk_kernel(
         offs[E] = acc;
         po.offsets[E] = acc;
       }
-      if (po.hdr != nullptr) {
-        const int bm = po.bm, bmd = down_bm(c, bm);
-        int su = 0, sd = 0;
-#pragma unroll
-        for (int i = 0; i < per; ++i) {
-          su += ceil_div(cnt[i], bm);
-          sd += ceil_div(cnt[i], bmd);
-        }
-        int pu = wave_incl_scan(su, lane) - su, pd = wave_incl_scan(sd, lane) - sd;
-        int r0 = row_start;
-        auto put = [&](TileEntry* list, int cap, int first, int n, const TileEntry& te) {
-          for (int m = 0; m < n; ++m)
-            if (first + m < cap) list[first + m] = te;
-        };
-#pragma unroll
-        for (int i = 0; i < per; ++i) {
-          const int e = lane * per + i;
-          if (e < E && cnt[i] > 0) {
-            const int mu = ceil_div(cnt[i], bm), md = ceil_div(cnt[i], bmd);
-            put(po.up, po.cap_up, pu, mu, TileEntry{r0, cnt[i], e, pu});
-            put(po.dn, po.cap_dn, pd, md, TileEntry{r0, cnt[i], e, pd});
-            pu += mu;
-            pd += md;
-          }
-          r0 += cnt[i];
-        }
-        if (lane == kWave - 1) {  // holds the routed totals: the shared group last
-          const int nsh = c.nsets > 1 ? min(c.set[1].rows_fixed, c.set[1].max_rows) : 0;
-          if (nsh > 0) {
-            const int mu = ceil_div(nsh, bm), md = ceil_div(nsh, bmd);
-            put(po.up, po.cap_up, pu, mu, TileEntry{0, nsh, 1 << 16, pu});
-            put(po.dn, po.cap_dn, pd, md, TileEntry{0, nsh, 1 << 16, pd});
-            pu += mu;
-            pd += md;
-          }
-          po.hdr->n_up = min(pu, po.cap_up);
-          po.hdr->n_down = min(pd, po.cap_dn);
-        }
-      }
+      if (po.hdr != nullptr)
+        emit_tiles_wave<per>(c, po.bm, E, cnt, row_start, lane, po.hdr, po.up, po.dn, po.cap_up,
+                             po.cap_dn);
     }
     __syncthreads();
     if (mine) {

@@ -151,4 +151,56 @@ __device__ inline void emit_tiles(const FfnCall& c, int bm, int NG, int G0, Tile
   }
 }
 
+// The same lists written by one wave that holds the routed groups' sizes
+// (the fused decode permutation, a few rows per group; with many M tiles per
+// group the block-wide emit_tiles is faster):
+// lane l holds groups [l PER, (l + 1) PER) of the E routed ones (sizes cnt[],
+// the first starting at grouped row row0); the shared expert's group (set 1,
+// if present) follows them. The wave scans the groups' M-tile counts and each
+// lane writes its own groups' entries, the last lane also the shared group's
+// and the header: the entries and positions emit_tiles writes, without its
+// block-wide scan or per-entry search.
+template <int PER>
+__device__ inline void emit_tiles_wave(const FfnCall& c, int bm, int E, const int (&cnt)[PER],
+                                       int row0, int lane, TileHeader* hdr, TileEntry* up,
+                                       TileEntry* down, int cap_up, int cap_dn) {
+  const int bmd = down_bm(c, bm);
+  int su = 0, sd = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    su += ceil_div(cnt[i], bm);
+    sd += ceil_div(cnt[i], bmd);
+  }
+  int pu = wave_incl_scan(su, lane) - su, pd = wave_incl_scan(sd, lane) - sd;
+  auto put = [](TileEntry* list, int cap, int first, int n, const TileEntry& te) {
+    for (int m = 0; m < n; ++m)
+      if (first + m < cap) list[first + m] = te;
+  };
+  int r0 = row0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = lane * PER + i;
+    if (e < E && cnt[i] > 0) {
+      const int mu = ceil_div(cnt[i], bm), md = ceil_div(cnt[i], bmd);
+      put(up, cap_up, pu, mu, TileEntry{r0, cnt[i], e, pu});
+      put(down, cap_dn, pd, md, TileEntry{r0, cnt[i], e, pd});
+      pu += mu;
+      pd += md;
+    }
+    r0 += cnt[i];
+  }
+  if (lane == kWave - 1) {  // holds the routed totals
+    const int nsh = c.nsets > 1 ? min(c.set[1].rows_fixed, c.set[1].max_rows) : 0;
+    if (nsh > 0) {
+      const int mu = ceil_div(nsh, bm), md = ceil_div(nsh, bmd);
+      put(up, cap_up, pu, mu, TileEntry{0, nsh, 1 << 16, pu});
+      put(down, cap_dn, pd, md, TileEntry{0, nsh, 1 << 16, pd});
+      pu += mu;
+      pd += md;
+    }
+    hdr->n_up = min(pu, cap_up);
+    hdr->n_down = min(pd, cap_dn);
+  }
+}
+
 }  // namespace moe
