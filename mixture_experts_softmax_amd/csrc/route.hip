@@ -450,8 +450,8 @@ __global__ __launch_bounds__(kLogitWaves * kWave) void route_logits_f32_kernel(
 
 // ---------------------------------------------------------------------------
 // Top-k over the logits of 64 tokens (NW = 16 waves, the fused permutation)
-// or 16 (NW = 4 waves, a quarter of a permutation tile: more workgroups for
-// the VALU-bound selection). Each wave serves 4 tokens at once: the 16 lanes
+// or 16 (NW = 4 waves, a quarter of a permutation tile: four times the
+// workgroups, so a large batch's selection spreads over more CUs). Each wave serves 4 tokens at once: the 16 lanes
 // [16q, 16q + 16) take token 4w + q, lane s holding the
 // PL = ceil(E/16) experts [s PL, s PL + PL). A logit is the sum of its K
 // slices in slice order, plus the bias. k rounds of a 16-lane (value desc,
