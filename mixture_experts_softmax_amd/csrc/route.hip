@@ -690,7 +690,7 @@ __global__ __launch_bounds__(NW * kWave) void route_topk_kernel(
         cnt[i] = (e < E) ? __popcll(mask[e]) : 0;
         sum += cnt[i];
       }
-      int acc = wave_incl_scan(sum, lane) - sum;
+      int acc = wave_incl_scan_dpp(sum) - sum;
       const int row_start = acc;
 #pragma unroll
       for (int i = 0; i < per; ++i) {

@@ -160,18 +160,39 @@ __device__ inline void emit_tiles(const FfnCall& c, int bm, int NG, int G0, Tile
 // lane writes its own groups' entries, the last lane also the shared group's
 // and the header: the entries and positions emit_tiles writes, without its
 // block-wide scan or per-entry search.
+// Inclusive scan over the 64 lanes by DPP: row shifts by 1, 2, 4 and 8 (zero
+// past the row start) scan each row of 16, then the last lane of row 0 is
+// added to rows 1 and 3 (row_bcast:15) and that of row 1 to rows 2 and 3
+// (row_bcast:31). No LDS round trips, unlike the shuffle scan.
+__device__ inline int wave_incl_scan_dpp(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+
+// ceil(x / b) for b > 0, by a shift when b is a power of two
+__device__ inline int ceil_div_p2(int x, int b) {
+  return (b & (b - 1)) == 0 ? (x + b - 1) >> __builtin_ctz(b) : ceil_div(x, b);
+}
+
 template <int PER>
 __device__ inline void emit_tiles_wave(const FfnCall& c, int bm, int E, const int (&cnt)[PER],
                                        int row0, int lane, TileHeader* hdr, TileEntry* up,
                                        TileEntry* down, int cap_up, int cap_dn) {
   const int bmd = down_bm(c, bm);
-  int su = 0, sd = 0;
+  int mu_[PER], md_[PER], su = 0, sd = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    su += ceil_div(cnt[i], bm);
-    sd += ceil_div(cnt[i], bmd);
+    mu_[i] = ceil_div_p2(cnt[i], bm);
+    md_[i] = ceil_div_p2(cnt[i], bmd);
+    su += mu_[i];
+    sd += md_[i];
   }
-  int pu = wave_incl_scan(su, lane) - su, pd = wave_incl_scan(sd, lane) - sd;
+  int pu = wave_incl_scan_dpp(su) - su, pd = wave_incl_scan_dpp(sd) - sd;
   auto put = [](TileEntry* list, int cap, int first, int n, const TileEntry& te) {
     for (int m = 0; m < n; ++m)
       if (first + m < cap) list[first + m] = te;
@@ -181,7 +202,7 @@ __device__ inline void emit_tiles_wave(const FfnCall& c, int bm, int E, const in
   for (int i = 0; i < PER; ++i) {
     const int e = lane * PER + i;
     if (e < E && cnt[i] > 0) {
-      const int mu = ceil_div(cnt[i], bm), md = ceil_div(cnt[i], bmd);
+      const int mu = mu_[i], md = md_[i];
       put(up, cap_up, pu, mu, TileEntry{r0, cnt[i], e, pu});
       put(down, cap_dn, pd, md, TileEntry{r0, cnt[i], e, pd});
       pu += mu;
@@ -192,7 +213,7 @@ __device__ inline void emit_tiles_wave(const FfnCall& c, int bm, int E, const in
   if (lane == kWave - 1) {  // holds the routed totals
     const int nsh = c.nsets > 1 ? min(c.set[1].rows_fixed, c.set[1].max_rows) : 0;
     if (nsh > 0) {
-      const int mu = ceil_div(nsh, bm), md = ceil_div(nsh, bmd);
+      const int mu = ceil_div_p2(nsh, bm), md = ceil_div_p2(nsh, bmd);
       put(up, cap_up, pu, mu, TileEntry{0, nsh, 1 << 16, pu});
       put(down, cap_dn, pd, md, TileEntry{0, nsh, 1 << 16, pd});
       pu += mu;
