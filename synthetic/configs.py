@@ -73,6 +73,12 @@ PARITY = {
     "fp8_e256": LayerConfig("fp8_e256", 130, 512, 256, 8, 128, 128, "fp8", seed=25),
     # two expert tiles in the tall-batch router at d = 1024, a ragged token tail
     "fp8_e256_rows": LayerConfig("fp8_e256_rows", 150, 1024, 256, 8, 128, 128, "fp8", seed=27),
+    # one-tile batches (routing and permutation in one launch) with 4 and 3
+    # experts per lane of the work-list wave, the 192-expert one ragged in T
+    "fp8_e256_one_tile": LayerConfig("fp8_e256_one_tile", 64, 512, 256, 8, 128, 128, "fp8",
+                                     seed=28),
+    "fp8_e192_one_tile": LayerConfig("fp8_e192_one_tile", 41, 512, 192, 6, 256, 128, "fp8",
+                                     seed=29),
     # the model's d = 4096 and F = 1024 (the shapes with fully unrolled K
     # loops) at few tokens, one per GEMM tile height: ~12, 24, 100 and 190
     # rows per expert select 16-, 32-, 128- and 192-row tiles

@@ -14,7 +14,8 @@ from tests import gpu_helpers as H
 pytestmark = pytest.mark.gpu
 
 SMALL = ["tiny", "f32_ragged", "f32_noshared", "fp8_small", "fp8_ragged", "fp8_noshared",
-         "fp8_k1", "fp8_kE", "fp8_wide", "fp8_skew_small", "fp8_e256", "fp8_e256_rows"]
+         "fp8_k1", "fp8_kE", "fp8_wide", "fp8_skew_small", "fp8_e256", "fp8_e256_rows",
+         "fp8_e256_one_tile", "fp8_e192_one_tile"]
 MODEL = ["fp8_model_m16", "fp8_model_m32", "fp8_model_m128", "fp8_model_m192", "fp8_model_f2048",
          "fp8_tall_dpart"]
 # MXFP4 expert weights: every kernel variant (tile heights 16 to 192, looped
