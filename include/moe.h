@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 /* Limits checked by every entry point. */
 #define MOE_MAX_E 256      /* routed experts */
@@ -165,30 +165,46 @@ moe_status_t moe_grouped_ffn_workspace_size(const moe_ffn_t* ffn, size_t* bytes)
  * paths (bf16 activations) the
  * logits launch also writes xq [T][d] (FP8 E4M3 codes of x / x_scale[t]) and
  * x_scale [T] (amax of row t over 448, 1.0 for a zero row); both are required
- * there and ignored on the float32 path. Two launches (logits, selection).
+ * there and ignored on the float32 path.
+ * tile_counts (optional, NULL to skip): int32 [ceil(T/64)][E], the number of
+ * tokens of each 64-token tile routed to each expert (the permutation's
+ * histogram, taken from the selection kernel's per-tile expert masks; one more
+ * small launch when requested). Two launches otherwise (logits, selection).
  * Needs a workspace of moe_route_workspace_size() bytes (the float32 partial
- * logits of the K slices).
+ * logits of the K slices and the tile masks).
  */
 moe_status_t moe_route_topk(const moe_shape_t* shape, const void* x, const void* w_router,
                             const float* router_bias, int32_t* topk_ids, float* topk_w,
-                            uint8_t* xq, float* x_scale, void* workspace, size_t workspace_bytes,
-                            void* stream);
+                            uint8_t* xq, float* x_scale, int32_t* tile_counts, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /*
  * Permutation of the T*k (token, slot) pairs into expert-contiguous order (the
- * scatter that the InferX page, section 3.3, fuses after its top-k router).
+ * scatter that the InferX page, section 3.3, fuses after its top-k router:
+ * moe_scatter moves each token's row to the rows of its chosen experts).
  * Pair p = t*k + j. Rows of expert e are offsets[e] .. offsets[e+1]-1, pairs
  * of one expert in ascending token order:
- *   offsets     [E+1]  offsets[0] = 0, offsets[E] = T*k
+ *   offsets     [E+1]  offsets[0] = 0, offsets[E] = number of valid pairs
  *   sorted_pair [T*k]  row -> pair
  *   pair_to_row [T*k]  pair -> row
+ *   tile_counts [ceil(T/64)][E] int32 (optional, NULL to skip): tokens of each
+ *               64-token tile routed to each expert (the histogram)
+ * Gather (optional; on the quantised paths, all four pointers or none):
+ *   x_perm       [T*k][d] bytes: x_perm[row] = xq[sorted_pair[row] / k]
+ *   x_perm_scale [T*k] float32:  x_scale[sorted_pair[row] / k]
+ * from xq [T][d] FP8 codes and x_scale [T] (as moe_route_topk writes them);
+ * only rows below offsets[E] are written. The result is moe_grouped_ffn's
+ * activation input with row_src = NULL. moe_layer_forward does not materialise
+ * it: its GEMMs read the rows of xq through sorted_pair while staging them.
  * topk_ids must hold values in [0, E), distinct within a token; a pair with an
  * id outside [0, E) gets no row and pair_to_row = -1. Needs a workspace of
  * moe_permute_workspace_size() bytes.
  */
-moe_status_t moe_permute(const moe_shape_t* shape, const int32_t* topk_ids, int32_t* offsets,
-                         int32_t* sorted_pair, int32_t* pair_to_row, void* workspace,
-                         size_t workspace_bytes, void* stream);
+moe_status_t moe_permute(const moe_shape_t* shape, const int32_t* topk_ids, const uint8_t* xq,
+                         const float* x_scale, int32_t* offsets, int32_t* sorted_pair,
+                         int32_t* pair_to_row, uint8_t* x_perm, float* x_perm_scale,
+                         int32_t* tile_counts, void* workspace, size_t workspace_bytes,
+                         void* stream);
 
 /*
  * Grouped SwiGLU expert FFN (NVIDIA blog, section "Performance challenges":
@@ -212,9 +228,11 @@ moe_status_t moe_grouped_ffn(const moe_ffn_t* ffn, void* workspace, size_t works
                              void* stream);
 
 /*
- * Gate-weighted combine, in this order with float32 accumulation and no
- * atomics:  y[t] = sum_{j=0}^{k-1} topk_w[t, j] * expert_out[pair_to_row[t*k + j]]
- *                  + shared_out[t]
+ * Gate-weighted combine (ijyty.com "InferX" page, section 3.3: the experts'
+ * rows of a token are brought back and added with the router's weights; the
+ * NVIDIA blog's layer adds the shared expert's output to the routed sum), in
+ * this order with float32 accumulation and no atomics:
+ *   y[t] = sum_{j=0}^{k-1} topk_w[t, j] * expert_out[pair_to_row[t*k + j]] + shared_out[t]
  * expert_out [T*k][d] and shared_out [T][d] (NULL: no shared term) are bf16 on
  * the FP8 and MXFP4 paths and float32 on the float32 path, as is y [T][d]. Pairs whose
  * pair_to_row is outside [0, T*k) contribute nothing.
@@ -232,6 +250,31 @@ moe_status_t moe_combine(const moe_shape_t* shape, const void* expert_out,
 moe_status_t moe_layer_forward(const moe_shape_t* shape, const moe_weights_t* weights,
                                const void* x, void* y, int32_t* topk_ids, float* topk_w,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Where moe_layer_forward leaves its intermediate results inside its workspace:
+ * byte offsets from the workspace start (MOE_NO_REGION where the shape has no
+ * such result). They hold the results of the last call that used the
+ * workspace once the stream has reached its end, until the next call:
+ *   xq, x_scale        FP8 codes [T][d] and float32 scales [T] of x (quantised paths)
+ *   offsets            int32 [E+1], sorted_pair and pair_to_row int32 [T*k]: the
+ *                      permutation, as moe_permute defines it
+ *   h, h_scale         the routed experts' SwiGLU output by grouped row: FP8 codes
+ *                      [T*k][F] and float32 block scales [T*k][F/128] (float32
+ *                      [T*k][F] and no scales on the float32 path)
+ *   h_shared, h_shared_scale   the shared expert's, [T][F_shared] and [T][F_shared/128]
+ *   expert_out         [T*k][d] by grouped row, shared_out [T][d] (bf16, or float32)
+ * Host-only; nothing is enqueued.
+ */
+#define MOE_NO_REGION ((size_t)-1)
+typedef struct moe_layer_regions {
+  size_t xq, x_scale;
+  size_t offsets, sorted_pair, pair_to_row;
+  size_t h, h_scale, h_shared, h_shared_scale;
+  size_t expert_out, shared_out;
+} moe_layer_regions_t;
+
+moe_status_t moe_layer_workspace_regions(const moe_shape_t* shape, moe_layer_regions_t* regions);
 
 /* Steps of moe_layer_forward, in launch order (for moe_layer_forward_events). */
 typedef enum moe_step {

@@ -17,7 +17,8 @@ import torch
 from . import _lib
 from ._lib import (MoeError, moe_abi_version, moe_check_shape, moe_combine,  # noqa: F401
                    moe_grouped_ffn, moe_grouped_ffn_workspace_size, moe_layer_forward,
-                   moe_layer_workspace_size, moe_permute, moe_permute_workspace_size,
+                   moe_layer_workspace_regions, moe_layer_workspace_size, moe_permute,
+                   moe_permute_workspace_size,
                    moe_route_topk, moe_host_e4m3_encode, moe_qk_norm_rope, qk_shape)
 
 __all__ = ["MoELayer", "MoeError", "moe_route_topk", "moe_permute", "moe_grouped_ffn",
@@ -71,5 +72,37 @@ class MoELayer:
         w = _lib.make_weights(s, **self.tensors)
         moe_layer_forward(s, w, x, y, topk_ids, topk_w, ws, stream)
         return y
+
+    def intermediates(self, T: int) -> dict:
+        """Views into the workspace of the intermediate results that the last
+        forward over T tokens left there (offsets from
+        moe_layer_workspace_regions): valid once the stream has reached the end
+        of that call, until the next call. Keys: xq, x_scale, offsets,
+        sorted_pair, pair_to_row, h, h_scale, h_shared, h_shared_scale,
+        expert_out, shared_out (absent where the shape has no such result)."""
+        if self._ws is None:
+            raise RuntimeError("no forward has run yet")
+        s = self.shape(T)
+        q = self.precision != "f32"
+        E, k, d, F, Fs = self.E, self.k, self.d, self.F, self.F_shared
+        f32, i32, u8 = torch.float32, torch.int32, torch.uint8
+        act = torch.bfloat16 if q else f32
+        hdt = u8 if q else f32
+        layout = {"xq": (u8, (T, d)), "x_scale": (f32, (T,)), "offsets": (i32, (E + 1,)),
+                  "sorted_pair": (i32, (T * k,)), "pair_to_row": (i32, (T * k,)),
+                  "h": (hdt, (T * k, F)), "h_scale": (f32, (T * k, F // 128)),
+                  "h_shared": (hdt, (T, Fs)), "h_shared_scale": (f32, (T, Fs // 128)),
+                  "expert_out": (act, (T * k, d)), "shared_out": (act, (T, d))}
+        out = {}
+        for name, off in moe_layer_workspace_regions(s).items():
+            if off is None:
+                continue
+            dt, shp = layout[name]
+            n = 1
+            for v in shp:
+                n *= v
+            nbytes = n * torch.tensor([], dtype=dt).element_size()
+            out[name] = self._ws[off:off + nbytes].view(dt).view(shp)
+        return out
 
     __call__ = forward

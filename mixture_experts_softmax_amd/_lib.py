@@ -22,7 +22,7 @@ MOE_DTYPE_F32, MOE_DTYPE_BF16, MOE_DTYPE_FP8_E4M3, MOE_DTYPE_MXFP4 = 0, 1, 2, 3
 EXPORTS = [
     "moe_abi_version", "moe_status_string", "moe_check_shape",
     "moe_layer_workspace_size", "moe_route_workspace_size", "moe_permute_workspace_size",
-    "moe_grouped_ffn_workspace_size",
+    "moe_grouped_ffn_workspace_size", "moe_layer_workspace_regions",
     "moe_route_topk", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_forward",
     "moe_layer_forward_events", "moe_host_e4m3_encode", "moe_qk_norm_rope",
 ]
@@ -60,6 +60,15 @@ class MoeQkShape(C.Structure):
                 ("style", C.c_int32), ("dtype", C.c_int32)]
 
 
+MOE_NO_REGION = (1 << 64) - 1
+REGIONS = ["xq", "x_scale", "offsets", "sorted_pair", "pair_to_row", "h", "h_scale", "h_shared",
+           "h_shared_scale", "expert_out", "shared_out"]
+
+
+class MoeLayerRegions(C.Structure):
+    _fields_ = [(n, C.c_size_t) for n in REGIONS]
+
+
 class MoeError(RuntimeError):
     def __init__(self, status: int, what: str):
         super().__init__(f"{what}: {status_string(status)} ({status})")
@@ -87,10 +96,12 @@ def lib() -> C.CDLL:
                   "moe_permute_workspace_size", "moe_grouped_ffn_workspace_size"):
             getattr(L, n).restype = I32
             getattr(L, n).argtypes = [P, C.POINTER(SZ)]
+        L.moe_layer_workspace_regions.restype = I32
+        L.moe_layer_workspace_regions.argtypes = [P, P]
         L.moe_route_topk.restype = I32
-        L.moe_route_topk.argtypes = [P] * 9 + [SZ, P]
+        L.moe_route_topk.argtypes = [P] * 10 + [SZ, P]
         L.moe_permute.restype = I32
-        L.moe_permute.argtypes = [P, P, P, P, P, P, SZ, P]
+        L.moe_permute.argtypes = [P] * 11 + [SZ, P]
         L.moe_grouped_ffn.restype = I32
         L.moe_grouped_ffn.argtypes = [P, P, SZ, P]
         L.moe_combine.restype = I32
@@ -211,26 +222,45 @@ def moe_grouped_ffn_workspace_size(f: MoeFfn) -> int:
     return n.value
 
 
+def moe_layer_workspace_regions(s: MoeShape) -> dict:
+    """Byte offsets of moe_layer_forward's intermediate results in its
+    workspace ({name: offset}; None where the shape has no such result)."""
+    r = MoeLayerRegions()
+    _check(lib().moe_layer_workspace_regions(C.byref(s), C.byref(r)), "moe_layer_workspace_regions")
+    return {n: (None if getattr(r, n) == MOE_NO_REGION else getattr(r, n)) for n in REGIONS}
+
+
 def moe_route_topk(s: MoeShape, x, w_router, router_bias, topk_ids, topk_w, xq, x_scale,
-                   workspace, stream=None):
+                   workspace, stream=None, tile_counts=None):
     T, d, E, k = s.T, s.d, s.E, s.k
     fp8 = _is_fp8(s)
+    ntiles = (T + 63) // 64
     args = (C.byref(s), _ptr(x, "x", _act_dtype(s), T * d), _ptr(w_router, "w_router", _act_dtype(s), E * d),
             _ptr(router_bias, "router_bias", torch.float32, E),
             _ptr(topk_ids, "topk_ids", torch.int32, T * k), _ptr(topk_w, "topk_w", torch.float32, T * k),
             _ptr(xq, "xq", torch.uint8, T * d) if fp8 else None,
             _ptr(x_scale, "x_scale", torch.float32, T) if fp8 else None,
+            _ptr(tile_counts, "tile_counts", torch.int32, ntiles * E),
             _ptr(workspace, "workspace", torch.uint8),
             workspace.numel() if workspace is not None else 0, _stream(stream))
     _check(lib().moe_route_topk(*args), "moe_route_topk")
 
 
-def moe_permute(s: MoeShape, topk_ids, offsets, sorted_pair, pair_to_row, workspace, stream=None):
+def moe_permute(s: MoeShape, topk_ids, offsets, sorted_pair, pair_to_row, workspace, stream=None,
+                xq=None, x_scale=None, x_perm=None, x_perm_scale=None, tile_counts=None):
+    """Permutation; optionally the gather of xq / x_scale into x_perm /
+    x_perm_scale (all four or none) and the per-64-token-tile expert counts."""
     n = s.T * s.k
+    ntiles = (s.T + 63) // 64
     _check(lib().moe_permute(C.byref(s), _ptr(topk_ids, "topk_ids", torch.int32, n),
+                             _ptr(xq, "xq", torch.uint8, s.T * s.d),
+                             _ptr(x_scale, "x_scale", torch.float32, s.T),
                              _ptr(offsets, "offsets", torch.int32, s.E + 1),
                              _ptr(sorted_pair, "sorted_pair", torch.int32, n),
                              _ptr(pair_to_row, "pair_to_row", torch.int32, n),
+                             _ptr(x_perm, "x_perm", torch.uint8, n * s.d),
+                             _ptr(x_perm_scale, "x_perm_scale", torch.float32, n),
+                             _ptr(tile_counts, "tile_counts", torch.int32, ntiles * s.E),
                              _ptr(workspace, "workspace", torch.uint8),
                              workspace.numel() if workspace is not None else 0, _stream(stream)),
            "moe_permute")

@@ -162,6 +162,23 @@ LayerWs layer_ws(const moe_shape_t* s, void* base, FfnCall* call) {
   return L;
 }
 
+// Pointers and alignment of a layer call (shape already checked, T > 0).
+moe_status_t check_layer_args(const moe_shape_t* s, const moe_weights_t* wt, const void* x,
+                              const void* y) {
+  if (!wt || !x || !y || !wt->w_router || !wt->w13 || !wt->w2) return MOE_ERR_INVALID_ARG;
+  if (!al16(x) || !al16(y) || !al16(wt->w_router) || !al16(wt->w13) || !al16(wt->w2))
+    return MOE_ERR_INVALID_ARG;
+  if (s->F_shared > 0 && (!al16(wt->ws13) || !al16(wt->ws2))) return MOE_ERR_INVALID_ARG;
+  const bool fp8 = is_fp8(s);
+  if (fp8 && (!wt->w13_scale || !wt->w2_scale)) return MOE_ERR_INVALID_ARG;
+  if (s->F_shared > 0 && (!wt->ws13 || !wt->ws2 || (fp8 && (!wt->ws13_scale || !wt->ws2_scale))))
+    return MOE_ERR_INVALID_ARG;
+  if (is_w4(s->w_dtype) && (!al16(wt->w13_scale) || !al16(wt->w2_scale) ||
+                            (s->F_shared > 0 && (!al16(wt->ws13_scale) || !al16(wt->ws2_scale)))))
+    return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
 moe_status_t check_qk(const moe_qk_shape_t* s) {
   if (s == nullptr) return MOE_ERR_INVALID_ARG;
   if (s->dtype != MOE_DTYPE_BF16 && s->dtype != MOE_DTYPE_F32) return MOE_ERR_UNSUPPORTED;
@@ -221,11 +238,44 @@ moe_status_t moe_layer_workspace_size(const moe_shape_t* shape, size_t* bytes) {
   return MOE_OK;
 }
 
+moe_status_t moe_layer_workspace_regions(const moe_shape_t* shape, moe_layer_regions_t* r) {
+  const moe_status_t st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (r == nullptr) return MOE_ERR_INVALID_ARG;
+  // laid out against a base far from zero, so that a region at offset 0
+  // cannot be mistaken for a missing one
+  uint8_t* const base = reinterpret_cast<uint8_t*>(uintptr_t(1) << 40);
+  FfnCall c;
+  const LayerWs L = layer_ws(shape, base, &c);
+  auto off = [&](const void* p) {
+    return p == nullptr ? MOE_NO_REGION : (size_t)(static_cast<const uint8_t*>(p) - base);
+  };
+  const bool fp8 = is_fp8(shape);
+  r->xq = off(L.xq);
+  r->x_scale = off(L.xs);
+  r->offsets = off(L.offsets);
+  r->sorted_pair = off(L.sorted_pair);
+  r->pair_to_row = off(L.pair_to_row);
+  r->h = off(c.set[0].h);
+  r->h_scale = fp8 ? off(c.set[0].h_scale) : MOE_NO_REGION;
+  r->h_shared = c.nsets > 1 ? off(c.set[1].h) : MOE_NO_REGION;
+  r->h_shared_scale = (c.nsets > 1 && fp8) ? off(c.set[1].h_scale) : MOE_NO_REGION;
+  r->expert_out = off(L.expert_out);
+  r->shared_out = off(L.shared_out);
+  return MOE_OK;
+}
+
+// The router's workspace: the K-split partial logits, then the tile masks
+// (written when tile counts are requested).
+static size_t route_call_ws_bytes(const moe_shape_t* s) {
+  return route_ws_bytes(s->T, s->d, s->E) + perm_masks_bytes(s->T, s->E);
+}
+
 moe_status_t moe_route_workspace_size(const moe_shape_t* shape, size_t* bytes) {
   const moe_status_t st = check_shape(shape);
   if (st != MOE_OK) return st;
   if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
-  *bytes = route_ws_bytes(shape->T, shape->d, shape->E);
+  *bytes = route_call_ws_bytes(shape);
   return MOE_OK;
 }
 
@@ -263,8 +313,8 @@ moe_status_t moe_grouped_ffn_workspace_size(const moe_ffn_t* ffn, size_t* bytes)
 
 moe_status_t moe_route_topk(const moe_shape_t* s, const void* x, const void* w_router,
                             const float* router_bias, int32_t* topk_ids, float* topk_w,
-                            uint8_t* xq, float* x_scale, void* workspace, size_t workspace_bytes,
-                            void* stream) {
+                            uint8_t* xq, float* x_scale, int32_t* tile_counts, void* workspace,
+                            size_t workspace_bytes, void* stream) {
   moe_status_t st = check_shape(s);
   if (st != MOE_OK) return st;
   if (s->T == 0) return MOE_OK;
@@ -272,25 +322,44 @@ moe_status_t moe_route_topk(const moe_shape_t* s, const void* x, const void* w_r
   if (!al16(x) || !al16(w_router)) return MOE_ERR_INVALID_ARG;
   const bool fp8 = is_fp8(s);
   if (fp8 && (!xq || !x_scale || !al16(xq))) return MOE_ERR_INVALID_ARG;
-  if (!workspace || workspace_bytes < route_ws_bytes(s->T, s->d, s->E) || !al256(workspace))
+  if (!workspace || workspace_bytes < route_call_ws_bytes(s) || !al256(workspace))
     return MOE_ERR_WORKSPACE;
-  return from_hip(launch_route(fp8, x, w_router, router_bias, s->T, s->d, s->E, s->k, topk_ids,
-                               topk_w, fp8 ? xq : nullptr, fp8 ? x_scale : nullptr,
-                               workspace, nullptr, nullptr, nullptr,
-                               static_cast<hipStream_t>(stream)));
+  uint64_t* masks = tile_counts == nullptr
+                        ? nullptr
+                        : reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(workspace) +
+                                                      route_ws_bytes(s->T, s->d, s->E));
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_route(fp8, x, w_router, router_bias, s->T, s->d, s->E, s->k, topk_ids,
+                              topk_w, fp8 ? xq : nullptr, fp8 ? x_scale : nullptr, workspace,
+                              masks, nullptr, nullptr, hs);
+  if (e == hipSuccess && tile_counts != nullptr)
+    e = launch_tile_counts(masks, s->T, s->E, tile_counts, hs);
+  return from_hip(e);
 }
 
-moe_status_t moe_permute(const moe_shape_t* s, const int32_t* topk_ids, int32_t* offsets,
-                         int32_t* sorted_pair, int32_t* pair_to_row, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+moe_status_t moe_permute(const moe_shape_t* s, const int32_t* topk_ids, const uint8_t* xq,
+                         const float* x_scale, int32_t* offsets, int32_t* sorted_pair,
+                         int32_t* pair_to_row, uint8_t* x_perm, float* x_perm_scale,
+                         int32_t* tile_counts, void* workspace, size_t workspace_bytes,
+                         void* stream) {
   moe_status_t st = check_shape(s);
   if (st != MOE_OK) return st;
   if (s->T == 0) return MOE_OK;
   if (!topk_ids || !offsets || !sorted_pair || !pair_to_row) return MOE_ERR_INVALID_ARG;
+  // the gather: all four pointers (quantised paths only) or none
+  const int ng = (xq != nullptr) + (x_scale != nullptr) + (x_perm != nullptr) +
+                 (x_perm_scale != nullptr);
+  if (ng != 0 && (ng != 4 || !is_fp8(s) || !al16(xq) || !al16(x_perm)))
+    return MOE_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < permute_ws_bytes(s->T, s->E) || !al256(workspace))
     return MOE_ERR_WORKSPACE;
-  return from_hip(launch_permute(topk_ids, s->T, s->E, s->k, offsets, sorted_pair, pair_to_row,
-                                 workspace, static_cast<hipStream_t>(stream)));
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_permute(topk_ids, s->T, s->E, s->k, offsets, sorted_pair, pair_to_row,
+                                tile_counts, workspace, hs);
+  if (e == hipSuccess && ng == 4)
+    e = launch_perm_gather(xq, x_scale, sorted_pair, offsets, s->T, s->E, s->k, s->d, x_perm,
+                           x_perm_scale, hs);
+  return from_hip(e);
 }
 
 moe_status_t moe_grouped_ffn(const moe_ffn_t* f, void* workspace, size_t workspace_bytes,
@@ -354,18 +423,10 @@ moe_status_t moe_layer_forward_events(const moe_shape_t* s, const moe_weights_t*
   moe_status_t st = check_shape(s);
   if (st != MOE_OK) return st;
   if (s->T == 0) return MOE_OK;
-  if (!wt || !x || !y || !wt->w_router || !wt->w13 || !wt->w2) return MOE_ERR_INVALID_ARG;
-  if (!al16(x) || !al16(y) || !al16(wt->w_router) || !al16(wt->w13) || !al16(wt->w2))
-    return MOE_ERR_INVALID_ARG;
-  if (s->F_shared > 0 && (!al16(wt->ws13) || !al16(wt->ws2))) return MOE_ERR_INVALID_ARG;
+  st = check_layer_args(s, wt, x, y);
+  if (st != MOE_OK) return st;
   const bool fp8 = is_fp8(s);
   const bool w4 = is_w4(s->w_dtype);
-  if (fp8 && (!wt->w13_scale || !wt->w2_scale)) return MOE_ERR_INVALID_ARG;
-  if (s->F_shared > 0 && (!wt->ws13 || !wt->ws2 || (fp8 && (!wt->ws13_scale || !wt->ws2_scale))))
-    return MOE_ERR_INVALID_ARG;
-  if (w4 && (!al16(wt->w13_scale) || !al16(wt->w2_scale) ||
-             (s->F_shared > 0 && (!al16(wt->ws13_scale) || !al16(wt->ws2_scale)))))
-    return MOE_ERR_INVALID_ARG;
   const size_t need = layer_ws(s, nullptr, nullptr).bytes;
   if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255))
     return MOE_ERR_WORKSPACE;

@@ -40,8 +40,18 @@ hipError_t launch_route(bool bf16, const void* x, const void* w_router, const fl
 size_t perm_masks_bytes(int T, int E);
 size_t perm_counts_bytes(int T, int E);
 size_t permute_ws_bytes(int T, int E);
+// tile_counts (optional): [ceil(T/64)][E] per-tile expert counts.
 hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* offsets,
-                          int32_t* sorted_pair, int32_t* pair_to_row, void* ws, hipStream_t s);
+                          int32_t* sorted_pair, int32_t* pair_to_row, int32_t* tile_counts,
+                          void* ws, hipStream_t s);
+// tile_counts[i] = popcount(masks[i]) over the [ceil(T/64)][E] tile masks.
+hipError_t launch_tile_counts(const uint64_t* masks, int T, int E, int32_t* tile_counts,
+                              hipStream_t s);
+// x_perm[r] = xq[sorted_pair[r] / k] (d bytes) and x_perm_scale[r] = x_scale[...]
+// for every row r below offsets[E].
+hipError_t launch_perm_gather(const uint8_t* xq, const float* x_scale, const int32_t* sorted_pair,
+                              const int32_t* offsets, int T, int E, int k, int d, uint8_t* x_perm,
+                              float* x_perm_scale, hipStream_t s);
 // scan + scatter from masks/counts already computed (counts become the tile
 // bases); with c != nullptr also writes the grouped-FFN tile lists of c.
 hipError_t launch_perm_scan_scatter(const int32_t* ids, int T, int E, int k, uint64_t* masks,

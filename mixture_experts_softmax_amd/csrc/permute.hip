@@ -11,6 +11,9 @@
 //               the first to know every group's size.
 //   3. scatter: row = offsets[e] + tile base[e] + popcount(mask[e] below the
 //               token's lane).
+//   4. gather (optional, moe_permute only): the FP8 rows of x and their
+//               scales copied into grouped-row order. The layer path skips it:
+//               its GEMMs read x's rows through sorted_pair while staging them.
 #include "common.h"
 #include "internal.h"
 #include "tiles.h"
@@ -25,7 +28,8 @@ constexpr int kScanStage = 8192;  // tile counts staged per chunk (32 KiB of LDS
 __global__ __launch_bounds__(kPermTile) void perm_count_kernel(const int32_t* __restrict__ ids,
                                                                int T, int E, int k,
                                                                uint64_t* __restrict__ masks,
-                                                               int32_t* __restrict__ counts) {
+                                                               int32_t* __restrict__ counts,
+                                                               int32_t* __restrict__ tile_counts) {
   __shared__ unsigned long long mask[MOE_MAX_E];
   const int lane = threadIdx.x;
   for (int e = lane; e < E; e += kPermTile) mask[e] = 0ull;
@@ -39,9 +43,45 @@ __global__ __launch_bounds__(kPermTile) void perm_count_kernel(const int32_t* __
   }
   __syncthreads();
   for (int e = lane; e < E; e += kPermTile) {
+    const int n = __popcll(mask[e]);
     masks[(size_t)blockIdx.x * E + e] = mask[e];
-    counts[(size_t)blockIdx.x * E + e] = __popcll(mask[e]);
+    counts[(size_t)blockIdx.x * E + e] = n;
+    if (tile_counts != nullptr) tile_counts[(size_t)blockIdx.x * E + e] = n;
   }
+}
+
+// Tile counts from tile masks: out[i] = popcount(masks[i]) for i < n.
+__global__ __launch_bounds__(256) void perm_popcount_kernel(const uint64_t* __restrict__ masks,
+                                                            int n, int32_t* __restrict__ out) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) out[i] = __popcll(masks[i]);
+}
+
+// Gather of the FP8 activation rows into grouped-row order: row r < offsets[E]
+// gets xq[sorted_pair[r] / k] and its scale. One wave per row, 16-byte pieces,
+// every load of a lane issued before its first store.
+constexpr int kGatherRows = 4;  // rows (waves) per workgroup
+constexpr int kGatherMaxPieces = MOE_MAX_D / 16 / kWave;
+
+__global__ __launch_bounds__(kGatherRows * kWave) void perm_gather_kernel(
+    const uint8_t* __restrict__ xq, const float* __restrict__ x_scale,
+    const int32_t* __restrict__ sorted_pair, const int32_t* __restrict__ offsets, int E, int k,
+    int d, int max_rows, uint8_t* __restrict__ x_perm, float* __restrict__ x_perm_scale) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int r = blockIdx.x * kGatherRows + threadIdx.x / kWave;
+  if (r >= min(offsets[E], max_rows)) return;
+  const int t = sorted_pair[r] / k;
+  const int pieces = d / 16;  // d is a multiple of 128: whole pieces
+  const v4i* src = reinterpret_cast<const v4i*>(xq + (size_t)t * d);
+  v4i* dst = reinterpret_cast<v4i*>(x_perm + (size_t)r * d);
+  v4i v[kGatherMaxPieces];
+#pragma unroll
+  for (int i = 0; i < kGatherMaxPieces; ++i)
+    if (lane + i * kWave < pieces) v[i] = src[lane + i * kWave];
+#pragma unroll
+  for (int i = 0; i < kGatherMaxPieces; ++i)
+    if (lane + i * kWave < pieces) dst[lane + i * kWave] = v[i];
+  if (lane == 0) x_perm_scale[r] = x_scale[t];
 }
 
 // One workgroup. Tile counts are the popcounts of the tile masks; counts
@@ -170,14 +210,33 @@ hipError_t launch_perm_scan_scatter(const int32_t* ids, int T, int E, int k, uin
 }
 
 hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* offsets,
-                          int32_t* sorted_pair, int32_t* pair_to_row, void* ws, hipStream_t s) {
+                          int32_t* sorted_pair, int32_t* pair_to_row, int32_t* tile_counts,
+                          void* ws, hipStream_t s) {
   uint64_t* masks = static_cast<uint64_t*>(ws);
   int32_t* counts =
       reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + perm_masks_bytes(T, E));
   hipLaunchKernelGGL(perm_count_kernel, dim3(ceil_div(T, kPermTile)), dim3(kPermTile), 0, s, ids,
-                     T, E, k, masks, counts);
+                     T, E, k, masks, counts, tile_counts);
   return launch_perm_scan_scatter(ids, T, E, k, masks, counts, offsets, sorted_pair, pair_to_row,
                                   nullptr, 0, nullptr, s);
+}
+
+hipError_t launch_tile_counts(const uint64_t* masks, int T, int E, int32_t* tile_counts,
+                              hipStream_t s) {
+  const int n = ceil_div(T, kPermTile) * E;
+  hipLaunchKernelGGL(perm_popcount_kernel, dim3(ceil_div(n, 256)), dim3(256), 0, s, masks, n,
+                     tile_counts);
+  return hipGetLastError();
+}
+
+hipError_t launch_perm_gather(const uint8_t* xq, const float* x_scale, const int32_t* sorted_pair,
+                              const int32_t* offsets, int T, int E, int k, int d, uint8_t* x_perm,
+                              float* x_perm_scale, hipStream_t s) {
+  const int rows = T * k;
+  hipLaunchKernelGGL(perm_gather_kernel, dim3(ceil_div(rows, kGatherRows)),
+                     dim3(kGatherRows * kWave), 0, s, xq, x_scale, sorted_pair, offsets, E, k, d,
+                     rows, x_perm, x_perm_scale);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -140,6 +140,28 @@ def permute(ids: np.ndarray, E: int) -> Permutation:
     return Permutation(counts, offsets, sorted_pair, pair_to_row)
 
 
+def tile_histogram(ids: np.ndarray, E: int, tile: int = 64) -> np.ndarray:
+    """counts[i][e] = number of tokens among rows [tile i, tile (i + 1)) of ids
+    that chose expert e (the per-tile histogram a counting permutation starts
+    from); ids outside [0, E) are not counted."""
+    T = ids.shape[0]
+    n = -(-T // tile)
+    out = np.zeros((n, E), dtype=np.int32)
+    for i in range(n):
+        block = ids[i * tile:(i + 1) * tile].reshape(-1)
+        valid = block[(block >= 0) & (block < E)].astype(np.int64)
+        out[i] = np.bincount(valid, minlength=E)
+    return out
+
+
+def gather_rows(xq: np.ndarray, s_x: np.ndarray, perm: Permutation, k: int):
+    """The row copy of the scatter (InferX page, section 3.3): grouped row r
+    holds the activation row of the token of pair sorted_pair[r], with its
+    scale. Returns (x_perm [T*k][d], x_perm_scale [T*k])."""
+    tok = perm.sorted_pair.astype(np.int64) // k
+    return xq[tok], s_x[tok]
+
+
 # ---------------------------------------------------------------------------
 # FP8 activation quantisation (reading R7): decisions taken in float32.
 # ---------------------------------------------------------------------------
@@ -163,11 +185,6 @@ def quantize_blocks_e4m3(h: np.ndarray, block: int = H_BLOCK):
     hb = np.asarray(h, np.float32).reshape(R, C // block, block)
     q, s = quantize_rows_e4m3(hb)
     return q.reshape(R, C), s
-
-
-def dequant(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
-    """FP8 codes times a per-row float32 scale, as float64."""
-    return codecs.e4m3_decode(codes) * np.asarray(scale, np.float64)[..., None]
 
 
 def silu(z: np.ndarray) -> np.ndarray:

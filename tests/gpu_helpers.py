@@ -39,16 +39,41 @@ def layer(lt: LayerTensors) -> moe_lib.MoELayer:
                             ws13_scale=lt.ws13_scale, ws2=lt.ws2, ws2_scale=lt.ws2_scale)
 
 
-def run_layer(lt: LayerTensors, x=None):
-    """Whole layer through moe_layer_forward; returns host (ids, w, y as float64)."""
+def run_layer(lt: LayerTensors, x=None, inter: bool = False):
+    """Whole layer through moe_layer_forward; returns host (ids, w, y as
+    float64), and with inter=True also a dict of the layer's own intermediate
+    results read back from its workspace (the keys run_stepwise uses)."""
     c = lt.cfg
     x = lt.x if x is None else x
     T = x.shape[0]
     ids = torch.full((T, c.k), -1, dtype=torch.int32, device=DEV)
     w = torch.full((T, c.k), -1.0, dtype=torch.float32, device=DEV)
-    y = layer(lt).forward(x, topk_ids=ids, topk_w=w)
+    L = layer(lt)
+    y = L.forward(x, topk_ids=ids, topk_w=w)
     torch.cuda.synchronize()
-    return ids.cpu().numpy(), w.cpu().numpy(), y.to(torch.float64).cpu().numpy()
+    out = (ids.cpu().numpy(), w.cpu().numpy(), y.to(torch.float64).cpu().numpy())
+    if not inter:
+        return out
+    mid = {n: t.cpu() for n, t in L.intermediates(T).items()}
+    st = dict(ids=out[0], w=out[1], y=out[2],
+              xq=mid["xq"].numpy() if "xq" in mid else None,
+              xs=mid["x_scale"].numpy() if "x_scale" in mid else None,
+              offsets=mid["offsets"].numpy(), sorted_pair=mid["sorted_pair"].numpy(),
+              pair_to_row=mid["pair_to_row"].numpy(), h=mid["h"].numpy(),
+              hs=mid["h_scale"].numpy() if "h_scale" in mid else None,
+              h_sh=mid["h_shared"].numpy() if "h_shared" in mid else None,
+              hs_sh=mid["h_shared_scale"].numpy() if "h_shared_scale" in mid else None,
+              eo=mid["expert_out"].to(torch.float64).numpy())
+    return out + (st,)
+
+
+def check_permutation(st: dict, ids_ref: np.ndarray, E: int, what: str = "layer"):
+    """offsets, sorted_pair and pair_to_row bit-exact against the oracle's
+    permutation of the oracle's expert ids."""
+    P = omoe.permute(ids_ref, E)
+    assert np.array_equal(st["offsets"], P.offsets), f"{what}: offsets differ"
+    assert np.array_equal(st["sorted_pair"], P.sorted_pair), f"{what}: sorted_pair differs"
+    assert np.array_equal(st["pair_to_row"], P.pair_to_row), f"{what}: pair_to_row differs"
 
 
 def shape_of(c, T=None):

@@ -123,6 +123,43 @@ def pin_permutation_invariants():
             assert np.all(np.diff(toks) > 0)  # ascending, no token twice
 
 
+def pin_tile_histogram_by_loop():
+    """Per-64-token-tile counts against an explicit loop over tokens and
+    slots; summed over tiles they are the permutation's group sizes."""
+    rng = _rng(112)
+    for T, E, k in [(1, 4, 2), (64, 8, 3), (65, 8, 8), (200, 32, 6), (130, 5, 1)]:
+        ids = np.array([rng.permutation(E)[:k] for _ in range(T)], dtype=np.int32).reshape(T, k)
+        H = moe.tile_histogram(ids, E)
+        assert H.shape == ((T + 63) // 64, E)
+        want = [[0] * E for _ in range((T + 63) // 64)]
+        for t in range(T):
+            for j in range(k):
+                want[t // 64][ids[t, j]] += 1
+        assert H.tolist() == want
+        assert np.array_equal(H.sum(axis=0), moe.permute(ids, E).counts)
+    # out-of-range ids are not counted
+    ids = np.array([[0, 9], [-1, 1]], dtype=np.int32)
+    assert moe.tile_histogram(ids, 4).tolist() == [[1, 1, 0, 0]]
+
+
+def pin_gather_rows_by_loop():
+    """Grouped rows hold, group by group in ascending token order, the rows of
+    the tokens routed to that group (explicit loop over experts and tokens)."""
+    rng = _rng(113)
+    T, E, k, d = 23, 6, 3, 8
+    ids = np.array([rng.permutation(E)[:k] for _ in range(T)], dtype=np.int32)
+    xq = rng.integers(0, 256, (T, d), dtype=np.uint8)
+    sx = rng.uniform(0.1, 2.0, T).astype(np.float32)
+    xp, sp = moe.gather_rows(xq, sx, moe.permute(ids, E), k)
+    r = 0
+    for e in range(E):
+        for t in range(T):
+            if e in ids[t]:
+                assert np.array_equal(xp[r], xq[t]) and sp[r] == sx[t]
+                r += 1
+    assert r == T * k
+
+
 # --------------------------------------------------------------- codecs ---
 
 def pin_quant_rows_exact_and_bounded():

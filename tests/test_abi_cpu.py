@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
     L = _lib.lib()
     for n in header_functions():
         assert hasattr(L, n), n
-    assert _lib.moe_abi_version() == 4
+    assert _lib.moe_abi_version() == 5
 
 
 def fp8_shape(**kw):
@@ -110,14 +110,15 @@ def test_mxfp4_shapes_and_workspace():
 def test_null_pointers_rejected_before_launch():
     L = _lib.lib()
     s = fp8_shape()
-    assert L.moe_route_topk(C.byref(s), None, None, None, None, None, None, None, None, 0, None) == _lib.MOE_ERR_INVALID_ARG
+    assert L.moe_route_topk(C.byref(s), None, None, None, None, None, None, None, None, None, 0, None) == _lib.MOE_ERR_INVALID_ARG
     assert L.moe_combine(C.byref(s), None, None, None, None, None, None) == _lib.MOE_ERR_INVALID_ARG
-    assert L.moe_permute(C.byref(s), None, None, None, None, None, 0, None) == _lib.MOE_ERR_INVALID_ARG
+    assert L.moe_permute(C.byref(s), *([None] * 10), 0, None) == _lib.MOE_ERR_INVALID_ARG
     assert L.moe_layer_forward(C.byref(s), None, None, None, None, None, None, 0, None) == _lib.MOE_ERR_INVALID_ARG
     assert L.moe_layer_forward(None, None, None, None, None, None, None, 0, None) == _lib.MOE_ERR_INVALID_ARG
     # T == 0 is a valid no-op even with null pointers
     s0 = fp8_shape(T=0)
-    assert L.moe_route_topk(C.byref(s0), None, None, None, None, None, None, None, None, 0, None) == _lib.MOE_OK
+    assert L.moe_route_topk(C.byref(s0), None, None, None, None, None, None, None, None, None, 0, None) == _lib.MOE_OK
+    assert L.moe_permute(C.byref(s0), *([None] * 10), 0, None) == _lib.MOE_OK
     assert L.moe_layer_forward(C.byref(s0), None, None, None, None, None, None, 0, None) == _lib.MOE_OK
 
 
@@ -135,12 +136,68 @@ def test_workspace_checks():
     assert L.moe_layer_forward(C.byref(s), C.byref(w), fake, fake, None, None, C.c_void_p((1 << 40) + 16), need, None) == _lib.MOE_ERR_WORKSPACE
     rw = _lib.moe_route_workspace_size(s)
     assert rw >= 64 * 128 * 4
-    assert L.moe_route_topk(C.byref(s), fake, fake, None, fake, fake, fake, fake, fake, rw - 1, None) == _lib.MOE_ERR_WORKSPACE
+    assert L.moe_route_topk(C.byref(s), fake, fake, None, fake, fake, fake, fake, None, fake, rw - 1, None) == _lib.MOE_ERR_WORKSPACE
     pw = _lib.moe_permute_workspace_size(s)
-    assert L.moe_permute(C.byref(s), fake, fake, fake, fake, fake, pw - 1, None) == _lib.MOE_ERR_WORKSPACE
+    assert L.moe_permute(C.byref(s), fake, None, None, fake, fake, fake, None, None, None, fake, pw - 1, None) == _lib.MOE_ERR_WORKSPACE
     # shared expert requested but its weights missing
     w2 = _lib.MoeWeights(A, None, A, A, A, A, None, None, None, None)
     assert L.moe_layer_forward(C.byref(s), C.byref(w2), fake, fake, None, None, fake, need, None) == _lib.MOE_ERR_INVALID_ARG
+
+
+def test_permute_gather_needs_all_four_pointers():
+    """The gather of x into grouped-row order takes xq, x_scale, x_perm and
+    x_perm_scale together, on the quantised paths only."""
+    L = _lib.lib()
+    s = fp8_shape()
+    fake = C.c_void_p(1 << 40)
+    pw = _lib.moe_permute_workspace_size(s)
+    ok = L.moe_permute(C.byref(s), fake, None, None, fake, fake, fake, None, None, None, fake, pw - 1, None)
+    assert ok == _lib.MOE_ERR_WORKSPACE  # reaches the workspace check: the pointer set is valid
+    for present in ([1, 0, 0, 0], [1, 1, 1, 0], [0, 1, 1, 1], [0, 0, 1, 0]):
+        g = [fake if p else None for p in present]
+        st = L.moe_permute(C.byref(s), fake, g[0], g[1], fake, fake, fake, g[2], g[3], None, fake, pw, None)
+        assert st == _lib.MOE_ERR_INVALID_ARG, present
+    s32 = _lib.shape(64, 4096, 128, 6, 1024, 1024, "f32")
+    st = L.moe_permute(C.byref(s32), fake, fake, fake, fake, fake, fake, fake, fake, None, fake, 1 << 30, None)
+    assert st == _lib.MOE_ERR_INVALID_ARG
+    odd = C.c_void_p((1 << 40) + 8)
+    st = L.moe_permute(C.byref(s), fake, odd, fake, fake, fake, fake, fake, fake, None, fake, pw, None)
+    assert st == _lib.MOE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("prec,Fs", [("fp8", 1024), ("mxfp4", 1024), ("fp8", 0), ("f32", 128)])
+@pytest.mark.parametrize("T", [1, 64, 65, 3584])
+def test_layer_workspace_regions(prec, Fs, T):
+    """The regions of moe_layer_forward's intermediates lie inside its
+    workspace, 256-byte aligned, without overlapping, sized as documented."""
+    d, E, k, F = (4096, 128, 6, 1024) if prec != "f32" else (256, 8, 2, 128)
+    s = _lib.shape(T, d, E, k, F, Fs, prec)
+    need = _lib.moe_layer_workspace_size(s)
+    r = _lib.moe_layer_workspace_regions(s)
+    q = prec != "f32"
+    eb = 2 if q else 4
+    size = {"xq": T * d, "x_scale": 4 * T, "offsets": 4 * (E + 1), "sorted_pair": 4 * T * k,
+            "pair_to_row": 4 * T * k, "h": T * k * F * (1 if q else 4), "h_scale": 4 * T * k * (F // 128),
+            "h_shared": T * Fs * (1 if q else 4), "h_shared_scale": 4 * T * (Fs // 128),
+            "expert_out": eb * T * k * d, "shared_out": eb * T * d}
+    absent = set()
+    if not q:
+        absent |= {"xq", "x_scale", "h_scale", "h_shared_scale"}
+    if not Fs:
+        absent |= {"h_shared", "h_shared_scale", "shared_out"}
+    spans = []
+    for n, off in r.items():
+        if n in absent:
+            assert off is None, n
+            continue
+        assert off is not None and off % 256 == 0, n
+        assert off + size[n] <= need, n
+        spans.append((off, off + size[n], n))
+    spans.sort()
+    for (a0, a1, na), (b0, b1, nb) in zip(spans, spans[1:]):
+        assert a1 <= b0, (na, nb)
+    with pytest.raises(_lib.MoeError):
+        _lib.moe_layer_workspace_regions(fp8_shape(k=0))
 
 
 def test_grouped_ffn_checks():

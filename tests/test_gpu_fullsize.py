@@ -38,8 +38,12 @@ def test_fullsize_sampled(name):
     cfg = CONFIGS[name]
     lt = H.gen(cfg)
     H.say(f"  cfg={cfg} redraws={lt.redraws} beta={lt.beta}")
-    ids, w, y = H.run_layer(lt)
+    ids, w, y, mid = H.run_layer(lt, inter=True)
     H.check_routing_invariants(ids, w, cfg.E)
+    # the permutation the layer computed, bit-exact against the oracle's
+    # stable sort of the layer's ids (every id is checked against the oracle
+    # on the sampled tokens below and by the router parity test on all)
+    H.check_permutation(mid, ids, cfg.E)
     counts = np.bincount(ids.reshape(-1), minlength=cfg.E)
     H.say(f"  touched experts={int((counts > 0).sum())} rows/group max={counts.max()} min={counts.min()}")
     extra = ()
@@ -59,7 +63,8 @@ def test_fullsize_sampled(name):
     assert np.array_equal(ids[tok], r_ids)
     assert np.abs(w[tok] - r_w).max() <= H.W_MAX_ABS
     assert np.array_equal(st["xq"][tok], r_xq) and np.array_equal(st["xs"][tok], r_sx)
-    bound, _, _, flips = H.fp8_bounds(inp, st, tokens=tok)
+    assert np.array_equal(mid["xq"][tok], r_xq) and np.array_equal(mid["xs"][tok], r_sx)
+    bound, _, _, flips = H.fp8_bounds(inp, mid, tokens=tok)
     H.say(f"  h: {flips} validated neighbouring-code decisions on the sampled tokens")
     H.compare_y(y[tok], r_y64, cfg.precision, f"y[{len(tok)} sampled tokens]", bound)
     assert np.all(np.isfinite(y))

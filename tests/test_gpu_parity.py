@@ -50,14 +50,16 @@ def test_route_topk(name):
     fp8 = cfg.precision != "f32"
     xq = torch.empty((T, d), dtype=torch.uint8, device=H.DEV) if fp8 else None
     xs = torch.empty((T,), dtype=torch.float32, device=H.DEV) if fp8 else None
+    tc = torch.full(((T + 63) // 64, cfg.E), -1, dtype=torch.int32, device=H.DEV)
     _lib.moe_route_topk(s, lt.x, lt.w_router, lt.router_bias, ids, w, xq, xs,
-                        alloc_workspace(_lib.moe_route_workspace_size(s), H.DEV))
+                        alloc_workspace(_lib.moe_route_workspace_size(s), H.DEV), tile_counts=tc)
     torch.cuda.synchronize()
     inp = oinputs.layer_inputs(lt)
     x64 = omoe.activations(inp)
     _, _, ids_ref, w_ref = omoe.route(x64, omoe.router_weight(inp), inp.router_bias, k)
     assert np.array_equal(ids.cpu().numpy(), ids_ref)
     assert np.abs(w.cpu().numpy() - w_ref).max() <= H.W_MAX_ABS
+    assert np.array_equal(tc.cpu().numpy(), omoe.tile_histogram(ids_ref, cfg.E))
     if fp8:
         # FP8 codes of x on every row, or (full-size batches, where the
         # oracle's encoder takes seconds per thousand rows) on 256 sampled
@@ -81,7 +83,8 @@ def test_permute(T, E, k):
         ids = np.where(ids == 3, (ids + 1) % E, ids)
         ids = np.stack([row if len(set(row)) == k else rng.permutation([e for e in range(E) if e != 3])[:k]
                         for row in ids]).astype(np.int32)
-    s = _lib.shape(T, 128, E, k, 128, 0, "fp8")
+    d = 256 if T * k <= 50_000 else 128
+    s = _lib.shape(T, d, E, k, 128, 0, "fp8")
     d_ids = torch.from_numpy(ids).to(H.DEV)
     off = torch.empty(E + 1, dtype=torch.int32, device=H.DEV)
     sp = torch.empty(T * k, dtype=torch.int32, device=H.DEV)
@@ -93,6 +96,20 @@ def test_permute(T, E, k):
     assert np.array_equal(off.cpu().numpy(), P.offsets)
     assert np.array_equal(sp.cpu().numpy(), P.sorted_pair)
     assert np.array_equal(p2r.cpu().numpy(), P.pair_to_row)
+    # again with the histogram and the gather of (random) x codes and scales
+    xq = torch.from_numpy(rng.integers(0, 256, (T, d), dtype=np.uint8)).to(H.DEV)
+    xs = torch.from_numpy(rng.uniform(0.01, 3.0, T).astype(np.float32)).to(H.DEV)
+    xp = torch.zeros((T * k, d), dtype=torch.uint8, device=H.DEV)
+    xps = torch.zeros((T * k,), dtype=torch.float32, device=H.DEV)
+    tc = torch.full(((T + 63) // 64, E), -1, dtype=torch.int32, device=H.DEV)
+    _lib.moe_permute(s, d_ids, off, sp, p2r, ws, xq=xq, x_scale=xs, x_perm=xp, x_perm_scale=xps,
+                     tile_counts=tc)
+    torch.cuda.synchronize()
+    assert np.array_equal(sp.cpu().numpy(), P.sorted_pair)
+    g, gs = omoe.gather_rows(xq.cpu().numpy(), xs.cpu().numpy(), P, k)
+    assert np.array_equal(xp.cpu().numpy(), g)
+    assert np.array_equal(xps.cpu().numpy(), gs)
+    assert np.array_equal(tc.cpu().numpy(), omoe.tile_histogram(ids, E))
 
 
 def test_permute_out_of_range_ids_get_no_row():
@@ -110,6 +127,33 @@ def test_permute_out_of_range_ids_get_no_row():
     p2r = p2r.cpu().numpy()
     assert p2r[3 * 2 + 1] == -1 and p2r[7 * 2 + 0] == -1
     assert off.cpu().numpy()[-1] == T * k - 2
+
+
+@pytest.mark.parametrize("name", ["fp8_ragged", "fp8_model_m128", "mx_ragged"])
+def test_gathered_rows_feed_grouped_ffn(name):
+    """The grouped FFN over rows gathered by moe_permute (row_src = NULL)
+    equals, bit for bit, the same call reading x's rows through sorted_pair."""
+    cfg = get(name)
+    lt = H.gen(cfg)
+    H.say(f"  cfg={cfg}")
+    st = H.run_stepwise(lt)
+    T, d, E, k, F = cfg.T, cfg.d, cfg.E, cfg.k, cfg.F
+    s = H.shape_of(cfg)
+    dev = lambda a: torch.from_numpy(a).to(H.DEV)
+    ids, xq, xs = dev(st["ids"]), dev(st["xq"]), dev(st["xs"])
+    off = torch.empty(E + 1, dtype=torch.int32, device=H.DEV)
+    sp = torch.empty(T * k, dtype=torch.int32, device=H.DEV)
+    p2r = torch.empty(T * k, dtype=torch.int32, device=H.DEV)
+    xp = torch.empty((T * k, d), dtype=torch.uint8, device=H.DEV)
+    xps = torch.empty((T * k,), dtype=torch.float32, device=H.DEV)
+    _lib.moe_permute(s, ids, off, sp, p2r, alloc_workspace(_lib.moe_permute_workspace_size(s), H.DEV),
+                     xq=xq, x_scale=xs, x_perm=xp, x_perm_scale=xps)
+    out = torch.empty((T * k, d), dtype=torch.bfloat16, device=H.DEV)
+    f = _lib.make_ffn(d, F, E, T * k, cfg.precision, off, None, 1, xp, xps, lt.w13, lt.w13_scale,
+                      lt.w2, lt.w2_scale, out)
+    _lib.moe_grouped_ffn(f, alloc_workspace(_lib.moe_grouped_ffn_workspace_size(f), H.DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(out.to(torch.float64).cpu().numpy(), st["eo"])
 
 
 @pytest.mark.parametrize("name", ["fp8_small", "fp8_ragged", "fp8_wide", "fp8_skew_small", "tiny",
@@ -208,23 +252,30 @@ def test_combine(precision):
 
 @pytest.mark.parametrize("name", SMALL + MODEL + MX)
 def test_layer_forward(name):
-    """moe_layer_forward against the oracle; the separate entry points give
-    bit-identical results, and their h decisions are validated."""
+    """moe_layer_forward against the oracle: ids, gate weights, x codes and the
+    permutation the layer itself computed (read back from its workspace)
+    bit-exact, its own h decisions validated, y within bound; the separate
+    entry points give bit-identical results."""
     cfg = get(name)
     lt = H.gen(cfg)
     H.say(f"  cfg={cfg} redraws={lt.redraws}")
-    ids, w, y = H.run_layer(lt)
-    st = H.run_stepwise(lt)
-    assert np.array_equal(st["ids"], ids) and np.array_equal(st["w"], w)
-    assert np.array_equal(st["y"], y), "moe_layer_forward differs from the separate entry points"
+    ids, w, y, mid = H.run_layer(lt, inter=True)
     inp = oinputs.layer_inputs(lt)
     ref = omoe.layer_forward(inp)
     assert np.array_equal(ids, ref.ids)
     assert np.abs(w - ref.w).max() <= H.W_MAX_ABS
+    H.check_permutation(mid, ref.ids, cfg.E)
+    if cfg.precision != "f32":
+        assert np.array_equal(mid["xq"], ref.xq) and np.array_equal(mid["xs"], ref.s_x)
+    st = H.run_stepwise(lt)
+    assert np.array_equal(st["ids"], ids) and np.array_equal(st["w"], w)
+    assert np.array_equal(st["y"], y), "moe_layer_forward differs from the separate entry points"
     extra = 0.0
     if cfg.precision != "f32":
-        extra, _, _, flips = H.fp8_bounds(inp, st)
+        extra, _, _, flips = H.fp8_bounds(inp, mid)
         H.say(f"  h: {flips} validated neighbouring-code decisions")
+    else:
+        assert np.array_equal(mid["eo"], st["eo"])
     H.compare_y(y, ref.y64, cfg.precision, "y", extra)
 
 

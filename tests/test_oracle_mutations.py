@@ -82,8 +82,17 @@ def _e8m0_bias_126(e):
     return np.ldexp(1.0, np.asarray(e, np.int64) - 126)
 
 
+def _histogram_tile_63(ids, E, tile=64):
+    return ORIG["tile_histogram"](ids, E, 63)
+
+
+def _gather_slot_not_token(xq, s_x, perm, k):
+    tok = perm.sorted_pair.astype(np.int64) % k
+    return xq[tok], s_x[tok]
+
+
 ORIG = {n: getattr(moe, n) for n in
-        ["ffn_fp32", "ffn_fp8", "router_logits", "permute", "combine"]}
+        ["ffn_fp32", "ffn_fp8", "router_logits", "permute", "combine", "tile_histogram"]}
 
 MUTANTS = {
     "swap_gate_up": ("ffn_fp32", _swap_gate_up),
@@ -97,6 +106,8 @@ MUTANTS = {
     "shared_expert_dropped": ("combine", _shared_dropped),
     "fp4_high_nibble_first": ("codecs.unpack_fp4", _fp4_high_nibble_first),
     "e8m0_bias_126": ("codecs.e8m0_decode", _e8m0_bias_126),
+    "histogram_tile_63": ("tile_histogram", _histogram_tile_63),
+    "gather_slot_not_token": ("gather_rows", _gather_slot_not_token),
 }
 
 
