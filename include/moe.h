@@ -15,6 +15,8 @@
  *    the device can access) owned by the caller; the library never allocates,
  *    frees or synchronises inside these calls and keeps no global state, so
  *    calls on different streams do not interfere unless their buffers alias.
+ *    The one exception is moe_layer_forward_noalloc, whose workspace is a
+ *    static buffer of the library (one per GPU), declared last below.
  *  - `stream` is a hipStream_t (NULL = the null stream). Calls only enqueue
  *    work and return; results are ready when the stream reaches them.
  *  - Arguments are checked on the host before anything is enqueued; a
@@ -71,7 +73,9 @@ typedef enum moe_status {
   MOE_ERR_INVALID_ARG = -1, /* null pointer, bad size or shape */
   MOE_ERR_UNSUPPORTED = -2, /* unsupported (act_dtype, w_dtype) pair */
   MOE_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
-  MOE_ERR_HIP = -4          /* the HIP runtime reported an error */
+  MOE_ERR_HIP = -4,         /* the HIP runtime reported an error */
+  MOE_ERR_SCRATCH = -5      /* the shape needs more than moe_layer_forward_noalloc's
+                               static scratch (MOE_NOALLOC_SCRATCH_BYTES) */
 } moe_status_t;
 
 typedef enum moe_dtype {
@@ -359,6 +363,32 @@ typedef struct moe_qk_shape {
 
 moe_status_t moe_qk_norm_rope(const moe_qk_shape_t* shape, void* qkv, const int32_t* positions,
                               const void* q_weight, const void* k_weight, void* stream);
+
+/* ---- the layer without a caller workspace -------------------------------------
+ * For callers that cannot allocate device memory: code that a HIP graph
+ * captures, tight serving loops, harnesses that forbid allocation. The same
+ * computation and kernels as moe_layer_forward, bit-identical results, with
+ * the workspace in a static device array of the library of
+ * MOE_NOALLOC_SCRATCH_BYTES bytes: 32 MiB holds the workspace of the 30B-shaped
+ * layer (d = 4096, E = 128, top-6, F = F_shared = 1024) up to T = 434 tokens
+ * (a decode step, or a 256-token prefill chunk with 32 decode tokens), and of
+ * the 100B-shaped layer (top-8, F = 2048) up to T = 318. Each GPU the library runs on holds
+ * its own copy from the first call on that GPU until the process ends; that
+ * first call looks up the array's device address (make it before any graph
+ * capture). The call allocates nothing, frees nothing and enqueues only
+ * kernels. Every call on one GPU shares that GPU's array: calls that may
+ * overlap on one GPU (different streams, or graphs replayed concurrently) race
+ * and must be serialised by the caller. Nothing in the array needs to start at
+ * zero; it keeps the last call's intermediate results (at the offsets
+ * moe_layer_workspace_regions gives). Arguments as moe_layer_forward; a shape
+ * whose workspace exceeds the array returns MOE_ERR_SCRATCH before anything is
+ * enqueued.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+moe_status_t moe_layer_forward_noalloc(const moe_shape_t* shape, const moe_weights_t* weights,
+                                       const void* x, void* y, int32_t* topk_ids, float* topk_w,
+                                       void* stream);
 
 #ifdef __cplusplus
 }

@@ -16,6 +16,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_ERR_SCRATCH = -5
+MOE_NOALLOC_SCRATCH_BYTES = 32 << 20
 MOE_DTYPE_F32, MOE_DTYPE_BF16, MOE_DTYPE_FP8_E4M3, MOE_DTYPE_MXFP4 = 0, 1, 2, 3
 
 # Names declared in include/moe.h, in order.
@@ -25,6 +27,7 @@ EXPORTS = [
     "moe_grouped_ffn_workspace_size", "moe_layer_workspace_regions",
     "moe_route_topk", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_forward",
     "moe_layer_forward_events", "moe_host_e4m3_encode", "moe_qk_norm_rope",
+    "moe_layer_forward_noalloc",
 ]
 MOE_ROPE_INTERLEAVED, MOE_ROPE_HALVES = 0, 1
 
@@ -108,6 +111,8 @@ def lib() -> C.CDLL:
         L.moe_combine.argtypes = [P] * 7
         L.moe_layer_forward.restype = I32
         L.moe_layer_forward.argtypes = [P, P, P, P, P, P, P, SZ, P]
+        L.moe_layer_forward_noalloc.restype = I32
+        L.moe_layer_forward_noalloc.argtypes = [P] * 7
         L.moe_layer_forward_events.restype = I32
         L.moe_layer_forward_events.argtypes = [P, P, P, P, P, P, P, SZ, P, P, P]
         L.moe_host_e4m3_encode.restype = None
@@ -339,6 +344,18 @@ def moe_layer_forward(s: MoeShape, weights: MoeWeights, x, y, topk_ids, topk_w, 
                                    _ptr(workspace, "workspace", torch.uint8),
                                    workspace.numel() if workspace is not None else 0,
                                    _stream(stream)), "moe_layer_forward")
+
+
+def moe_layer_forward_noalloc(s: MoeShape, weights: MoeWeights, x, y, topk_ids, topk_w,
+                              stream=None):
+    """moe_layer_forward with the library's static per-GPU scratch as workspace."""
+    T, d, k = s.T, s.d, s.k
+    ad = _act_dtype(s)
+    _check(lib().moe_layer_forward_noalloc(C.byref(s), C.byref(weights), _ptr(x, "x", ad, T * d),
+                                           _ptr(y, "y", ad, T * d),
+                                           _ptr(topk_ids, "topk_ids", torch.int32, T * k),
+                                           _ptr(topk_w, "topk_w", torch.float32, T * k),
+                                           _stream(stream)), "moe_layer_forward_noalloc")
 
 
 MOE_STEPS = ["route", "permute", "tiles", "gate_up", "down", "combine"]

@@ -2,7 +2,9 @@
 // Nothing here allocates, frees or synchronises.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
+#include <mutex>
 
 #include "common.h"
 #include "internal.h"
@@ -10,7 +12,39 @@
 
 using namespace moe;
 
+// Workspace of moe_layer_forward_noalloc: one copy per GPU, held from the
+// library's load until the process ends. Host code never uses this name as an
+// address (on the host it is only a stand-in for the symbol); the device
+// address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device, looked up on the first
+// call per device and kept.
+hipError_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (p == nullptr) return hipErrorInvalidSymbol;
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
 
 bool is_dim(int v, int max) { return v >= MOE_DIM_ALIGN && v <= max && v % MOE_DIM_ALIGN == 0; }
 
@@ -224,6 +258,8 @@ const char* moe_status_string(int32_t status) {
     case MOE_ERR_UNSUPPORTED: return "unsupported dtype combination";
     case MOE_ERR_WORKSPACE: return "workspace missing or too small";
     case MOE_ERR_HIP: return "HIP runtime error";
+    case MOE_ERR_SCRATCH:
+      return "shape needs more workspace than the no-allocation entry point's static scratch";
     default: return "unknown status";
   }
 }
@@ -501,6 +537,21 @@ moe_status_t moe_layer_forward_events(const moe_shape_t* s, const moe_weights_t*
                            s->d, s->k, hs);
   ev.mark(false, MOE_STEP_COMBINE, hs);
   return from_hip(e);
+}
+
+moe_status_t moe_layer_forward_noalloc(const moe_shape_t* s, const moe_weights_t* wt,
+                                       const void* x, void* y, int32_t* topk_ids, float* topk_w,
+                                       void* stream) {
+  moe_status_t st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (s->T == 0) return MOE_OK;
+  st = check_layer_args(s, wt, x, y);
+  if (st != MOE_OK) return st;
+  if (layer_ws(s, nullptr, nullptr).bytes > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (scratch_address(&ws) != hipSuccess) return MOE_ERR_HIP;
+  return moe_layer_forward_events(s, wt, x, y, topk_ids, topk_w, ws, MOE_NOALLOC_SCRATCH_BYTES,
+                                  stream, nullptr, nullptr);
 }
 
 void moe_host_e4m3_encode(const float* in, uint8_t* out, int64_t n) {

@@ -222,6 +222,31 @@ def test_grouped_ffn_checks():
     assert L.moe_grouped_ffn(C.byref(ub), None, 0, None) == _lib.MOE_ERR_UNSUPPORTED
 
 
+def test_noalloc_rejects_before_touching_the_device():
+    """The no-allocation layer call validates everything on the host: bad
+    pointers, and shapes whose workspace exceeds the static scratch, are
+    rejected before any HIP call (this container has no GPU)."""
+    L = _lib.lib()
+    A = 1 << 40  # a well-aligned stand-in address; never dereferenced
+    fake = C.c_void_p(A)
+    w = _lib.MoeWeights(A, None, A, A, A, A, A, A, A, A)
+    s = fp8_shape()
+    assert L.moe_layer_forward_noalloc(C.byref(s), None, fake, fake, None, None, None) == _lib.MOE_ERR_INVALID_ARG
+    assert L.moe_layer_forward_noalloc(C.byref(s), C.byref(w), None, fake, None, None, None) == _lib.MOE_ERR_INVALID_ARG
+    assert L.moe_layer_forward_noalloc(C.byref(s), C.byref(w), C.c_void_p(A + 2), fake, None, None, None) == _lib.MOE_ERR_INVALID_ARG
+    assert L.moe_layer_forward_noalloc(C.byref(fp8_shape(k=0)), C.byref(w), fake, fake, None, None, None) == _lib.MOE_ERR_INVALID_ARG
+    assert L.moe_layer_forward_noalloc(C.byref(fp8_shape(T=0)), None, None, None, None, None, None) == _lib.MOE_OK
+    # the largest batch whose workspace fits, and the first that does not
+    fits = [T for T in range(1, 700) if _lib.moe_layer_workspace_size(fp8_shape(T=T)) <= _lib.MOE_NOALLOC_SCRATCH_BYTES]
+    assert 288 <= fits[-1] < 699 and fits == list(range(1, fits[-1] + 1))
+    big = fp8_shape(T=fits[-1] + 1)
+    assert L.moe_layer_forward_noalloc(C.byref(big), C.byref(w), fake, fake, None, None, None) == _lib.MOE_ERR_SCRATCH
+    assert L.moe_layer_forward_noalloc(C.byref(fp8_shape(T=3584)), C.byref(w), fake, fake, None, None, None) == _lib.MOE_ERR_SCRATCH
+    s100 = _lib.shape(288, 4096, 128, 8, 2048, 2048, "fp8")
+    assert _lib.moe_layer_workspace_size(s100) <= _lib.MOE_NOALLOC_SCRATCH_BYTES
+    assert "scratch" in _lib.status_string(_lib.MOE_ERR_SCRATCH)
+
+
 def test_status_strings():
     assert _lib.status_string(0) == "ok"
     assert "workspace" in _lib.status_string(-3)
