@@ -16,6 +16,7 @@
 // so a weight tile read by several M tiles, and a group's activation rows, are
 // served from that XCD's L2.
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 #include "internal.h"
@@ -752,6 +753,315 @@ __global__ __launch_bounds__(8 * kWave) void gateup_fp8_lds_kernel(
   gateup_epilogue_t<BM, MS, NS, W4>(acc, sxl, red, s13l, rbase, wn, lane, te, S, ntile);
 }
 
+// Workgroup barrier for LDS written by ordinary stores: waits for this wave's
+// LDS operations (lgkmcnt) only, so global loads -- direct-to-LDS ones
+// included, whose completion the caller waits for by vmcnt -- stay in flight
+// (a release fence would wait for those too). The empty asm statements keep
+// the compiler from moving memory accesses across the barrier.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt: no wait
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Calls f(std::integral_constant<int, K>) for K = 0 .. N - 1 in order, so the
+// body sees each K as a compile-time constant (a fully unrolled loop whose
+// wait counts are template arguments).
+template <class Fn, int... Ks>
+__device__ inline void static_for_impl(Fn&& f, std::integer_sequence<int, Ks...>) {
+  (f(std::integral_constant<int, Ks>{}), ...);
+}
+template <int N, class Fn>
+__device__ inline void static_for(Fn&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Global loads of the ping-pong gate/up kernel, in issue order: the prologue
+// issues A(0), B(0) .. B(D - 2), A(1), B(D - 1); LOAD(j) issues A(j + 2) then
+// B(j + D), each only if that K step exists. A(s) is NA loads per thread, B(s)
+// NB. These count the loads issued after A(kt + 1) (at the start of LOAD(kt),
+// before its own loads), and after B(kt + 1) up to the end of LOAD(kt): the
+// vmcnt that waits for exactly that step's loads.
+__host__ __device__ constexpr int pp_count_below(int a, int b, int c) {
+  // #{j in [a, b] : j < c}
+  return (b < c - 1 ? b : c - 1) - a + 1 > 0 ? (b < c - 1 ? b : c - 1) - a + 1 : 0;
+}
+__host__ __device__ constexpr int pp_after_a(int kt, int D, int KT, int NB) {
+  return (kt - 1 + D < KT) ? NB : 0;  // only B(kt - 1 + D) follows A(kt + 1)
+}
+__host__ __device__ constexpr int pp_after_b(int kt, int D, int KT, int NA, int NB) {
+  const int s = kt + 1;
+  // loads of the prologue after B(s), when the prologue issued it
+  const int pro = (s >= D) ? 0 : (s <= D - 2) ? (D - 2 - s) * NB + NA + NB : 0;
+  // LOAD(j) for j in [j0, kt] follow B(s) entirely: A(j + 2) if j + 2 < KT,
+  // B(j + D) if j + D < KT
+  const int j0 = (s >= D) ? s - D + 1 : 0;
+  return pro + NA * pp_count_below(j0, kt, KT - 2) + NB * pp_count_below(j0, kt, KT - D);
+}
+
+// Gate/up epilogue of the ping-pong kernel: gateup_epilogue_t with the scales
+// read through accessors: sx(i) the x scale of row rbase + 16 i + lane % 16,
+// sg(jj) / su(jj) the channel scales of gate / up columns c0 + 16 jj .. + 3.
+template <int BM, int MS, int NS, class SX, class SG, class SU>
+__device__ inline void gateup_epilogue_pp(v4f (&acc)[MS][2 * NS], SX sx, SG sg, SU su,
+                                          float (*red)[BM], int rbase, int wn, int lane,
+                                          const Tile& te, const SetView& S, int ntile) {
+  constexpr int WN = NS * 16;
+  const int F = S.F;
+  const int c0 = wn * WN + 4 * (lane >> 4);
+#pragma unroll
+  for (int i = 0; i < MS; ++i) {
+    const int r = rbase + i * 16 + (lane & 15);
+    const float sxi = sx(i);
+    float m = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < NS; ++jj) {
+      const v4f sgj = sg(jj), suj = su(jj);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float gv = acc[i][jj][q] * sxi * sgj[q];
+        const float uv = acc[i][NS + jj][q] * sxi * suj[q];
+        const float h = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+        acc[i][jj][q] = h;
+        m = fmaxf(m, fabsf(h));
+      }
+    }
+    m = fmaxf(m, __shfl_xor(m, 16, kWave));
+    m = fmaxf(m, __shfl_xor(m, 32, kWave));
+    if (lane < 16) red[wn][r] = m;
+  }
+  __syncthreads();
+  const int hblocks = F / kHN;
+#pragma unroll
+  for (int i = 0; i < MS; ++i) {
+    const int r = rbase + i * 16 + (lane & 15);
+    if (r >= te.nrows) continue;
+    float am = red[0][r];
+#pragma unroll
+    for (int ww = 1; ww < kNWaves; ++ww) am = fmaxf(am, red[ww][r]);
+    const float s = (am > 0.f) ? __fdiv_rn(am, kE4M3Max) : 1.0f;
+    const float rs = __builtin_amdgcn_rcpf(s);
+    const size_t grow = (size_t)(te.row0 + r);
+    uint8_t* hrow = S.h + grow * F + ntile * kHN + c0;
+#pragma unroll
+    for (int jj = 0; jj < NS; ++jj) {
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(div_by(acc[i][jj][0], s, rs),
+                                              div_by(acc[i][jj][1], s, rs), 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(div_by(acc[i][jj][2], s, rs),
+                                          div_by(acc[i][jj][3], s, rs), w, true);
+      *reinterpret_cast<int*>(hrow + 16 * jj) = w;
+    }
+    if (wn == 0 && lane < 16) S.h_scale[grow * hblocks + ntile] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Gate/up GEMM for tall tiles (prefill), FP8 weights, ping-pong schedule.
+// Tile BM rows x 128 h columns (256 weight rows: 128 gate, 128 up), 8 waves in
+// two groups of four: group g owns rows [g BM/2, (g + 1) BM/2), wave wn of a
+// group h columns [32 wn, 32 wn + 32). Each SIMD runs one wave of each group.
+// Every K step is two phases per wave, LOAD (read the step's MFMA fragments
+// from LDS into registers, write the next step's activation rows into LDS,
+// issue later steps' global loads) and COMPUTE (the step's MFMAs, no memory
+// access), separated by workgroup barriers; group 1 runs one phase behind
+// group 0, so on every SIMD one wave loads while the other computes and the
+// matrix core is fed from registers without waiting on LDS.
+//
+// Operand staging: activation rows (gathered through the permutation) are
+// loaded into registers two steps ahead and written into one of two LDS
+// stages a step ahead; weight rows go straight from global memory into one of
+// NBS LDS stages D = NBS - 1 steps ahead (direct-to-LDS loads). Phase by phase
+// the two groups' reads of a stage finish before either overwrites it:
+//   phase 2 kt:     group 0 LOAD(kt)    group 1 COMPUTE(kt - 1)
+//   phase 2 kt + 1: group 0 COMPUTE(kt) group 1 LOAD(kt)
+// LOAD(kt) reads A stage kt % 2 and B stage kt % NBS, writes A stage
+// (kt + 1) % 2 and loads B stage (kt + D) % NBS, both last read in phase
+// 2 kt - 1; each wave waits for its own part of B step kt + 1 before the
+// barrier that ends phase 2 kt + 1, the last one before that step is first
+// read. The K loop is fully unrolled, so every wait count is exact. After the
+// loop the A stages hold the epilogue's row maxima.
+// ---------------------------------------------------------------------------
+template <int BM, int KTC, int NBS>
+__global__ __launch_bounds__(8 * kWave) void gateup_fp8_pp_kernel(
+    FfnCall c, const TileHeader* __restrict__ hdr, const TileEntry* __restrict__ list) {
+  constexpr int NW = 8;
+  constexpr int BMW = BM / 2, MS = BMW / 16;
+  constexpr int NS = 2, NB = 2 * NS;
+  constexpr int BROWS = 2 * kHN;                 // weight rows per tile
+  constexpr int NAD = BM * kBK / 1024 / NW;      // A pieces (16 B) per thread per step
+  constexpr int NBD = BROWS * kBK / 1024 / NW;   // B pieces per thread per step
+  constexpr int D = NBS - 1;                     // weight steps loaded ahead
+  static_assert(BM * kBK % (1024 * NW) == 0, "A tile must split into whole wave loads");
+  static_assert(KTC >= NBS, "the pipeline holds NBS K steps");
+  static_assert(NBS >= 3 && NBS <= 4, "three or four weight stages");
+  static_assert(kNWaves * BM * 4 <= BM * kBK, "row maxima fit in an A stage");
+  // the x and channel scales stay in LDS when it has room beside the stages,
+  // else in registers
+  constexpr bool SCL = (2 * BM + NBS * BROWS) * kBK + (BM + BROWS) * 4 <= 163840;
+
+  __shared__ __attribute__((aligned(1024))) uint8_t a0[BM * kBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t a1[BM * kBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t b0[BROWS * kBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t b1[BROWS * kBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t b2[BROWS * kBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t b3[NBS > 3 ? BROWS * kBK : 16];
+  __shared__ float sxl[SCL ? BM : 1];
+  __shared__ __attribute__((aligned(16))) float s13l[SCL ? BROWS : 1];
+
+  Tile te;
+  if (!pick_tile<BM>(list, hdr->n_up, up_ntiles_max(c), te)) return;
+  const int ntile = te.ntile;
+  const int sid = te.gid >> 16, g = te.gid & 0xffff;
+  const SetView S = set_view(c, sid);
+  const int d = c.d, F = S.F;
+  if (ntile >= F / kHN) return;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int grp = wave / kNWaves, wn = wave % kNWaves;
+  const int rbase = grp * BMW;
+  const uint8_t* a = static_cast<const uint8_t*>(c.a);
+  auto src_row = [&](int r) {  // activation row of tile row r
+    const int grow = te.row0 + min(r, te.nrows - 1);
+    return min(max(S.row_src ? S.row_src[grow] / S.src_div : grow, 0), c.a_rows - 1);
+  };
+
+  // A piece i of this thread: tile row 8 (NAD wave + i) + lane / 8, stored at
+  // (its 1 KiB block) + 16 lane, the swizzle applied by the source chunk
+  const uint8_t* asrc[NAD];
+#pragma unroll
+  for (int i = 0; i < NAD; ++i) {
+    const int r = 8 * (NAD * wave + i) + (lane >> 3);
+    const int cch = (lane & 7) ^ (r & 7);
+    asrc[i] = a + (size_t)src_row(r) * d + cch * 16;
+  }
+  // B piece i: weight-tile row 8 (NBD wave + i) + lane / 8 (rows 0..127 gate,
+  // 128..255 up), the same layout
+  const uint8_t* w13 = S.w13 + (size_t)g * 2 * F * d;
+  auto wrow_of = [&](int rr) { return (rr < kHN) ? ntile * kHN + rr : F + ntile * kHN + (rr - kHN); };
+  const uint8_t* bsrc[NBD];
+#pragma unroll
+  for (int i = 0; i < NBD; ++i) {
+    const int rr = 8 * (NBD * wave + i) + (lane >> 3);
+    const int cch = (lane & 7) ^ (rr & 7);
+    bsrc[i] = w13 + (size_t)wrow_of(rr) * d + cch * 16;
+  }
+  // the epilogue's x scales and channel scales, loaded now
+  const float* s13 = S.s13 + (size_t)g * 2 * F;
+  float sxr[SCL ? 1 : MS];
+  v4f sgr[SCL ? 1 : NS], sur[SCL ? 1 : NS];
+  if constexpr (SCL) {
+    if (tid < BM) sxl[tid] = c.a_scale[src_row(tid)];
+    if (tid < BROWS) s13l[tid] = s13[wrow_of(tid)];
+  } else {
+#pragma unroll
+    for (int i = 0; i < MS; ++i) sxr[i] = c.a_scale[src_row(rbase + i * 16 + (lane & 15))];
+    const float* sc = s13 + ntile * kHN + wn * 32 + 4 * (lane >> 4);
+#pragma unroll
+    for (int jj = 0; jj < NS; ++jj) {
+      sgr[jj] = *reinterpret_cast<const v4f*>(sc + 16 * jj);
+      sur[jj] = *reinterpret_cast<const v4f*>(sc + F + 16 * jj);
+    }
+  }
+
+  v4i ra[2][NAD];  // activation rows of two K steps in flight
+  auto lda = [&](int kt, int slot) {
+#pragma unroll
+    for (int i = 0; i < NAD; ++i) ra[slot][i] = *reinterpret_cast<const v4i*>(asrc[i] + kt * kBK);
+  };
+  auto sta = [&](int slot, uint8_t* ad) {
+#pragma unroll
+    for (int i = 0; i < NAD; ++i)
+      *reinterpret_cast<v4i*>(ad + (NAD * wave + i) * 1024 + lane * 16) = ra[slot][i];
+  };
+  auto ldb = [&](int kt, uint8_t* bd) {
+#pragma unroll
+    for (int i = 0; i < NBD; ++i) dma16(bsrc[i] + kt * kBK, bd + (NBD * wave + i) * 1024);
+  };
+  auto astage = [&](int kt) { return (kt & 1) ? a1 : a0; };
+  auto bstage = [&](int kt) {
+    const int m = kt % NBS;
+    return m == 0 ? b0 : m == 1 ? b1 : m == 2 ? b2 : b3;
+  };
+
+  // prologue: A(0), B(0) .. B(D - 2), A(1), B(D - 1); A(0) into its stage,
+  // B(0) landed (pp_after_a / pp_after_b count this order)
+  lda(0, 0);
+#pragma unroll
+  for (int s = 0; s + 1 < D; ++s) ldb(s, bstage(s));
+  lda(1, 1);
+  ldb(D - 1, bstage(D - 1));
+  wait_vmcnt<(D - 1) * NBD + NAD + NBD>();
+  sta(0, a0);
+  wait_vmcnt<(D - 2) * NBD + NAD + NBD>();
+  lds_barrier();  // publishes A(0) and B(0)
+  if (grp == 1) __builtin_amdgcn_s_barrier();  // group 1 one phase behind
+  __builtin_amdgcn_sched_barrier(0);
+
+  v4f acc[MS][NB];
+#pragma unroll
+  for (int i = 0; i < MS; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  static_for<KTC>([&](auto ktc) {
+    constexpr int kt = decltype(ktc)::value;
+    // ---- LOAD(kt) ----
+    if constexpr (kt + 1 < KTC) {
+      wait_vmcnt<pp_after_a(kt, D, KTC, NBD)>();  // A(kt + 1) in registers
+      sta((kt + 1) & 1, astage(kt + 1));
+    }
+    v8i bf[NB], af[MS];
+    {
+      const uint8_t* bs = bstage(kt);
+      const uint8_t* as = astage(kt);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int row0 = (j < NS) ? wn * 32 + j * 16 : kHN + wn * 32 + (j - NS) * 16;
+        bf[j] = lds_afrag(bs + row0 * kBK, 0, lane);
+      }
+#pragma unroll
+      for (int i = 0; i < MS; ++i) af[i] = lds_afrag(as + rbase * kBK, i, lane);
+    }
+    if constexpr (kt + 2 < KTC) lda(kt + 2, kt & 1);
+    if constexpr (kt + D < KTC) ldb(kt + D, bstage(kt + D));
+    // this wave's part of B(kt + 1) lands before the barrier ending phase
+    // 2 kt + 1: group 1 waits here, group 0 after its COMPUTE(kt)
+    constexpr int wb = (kt + 1 < KTC) ? pp_after_b(kt, D, KTC, NAD, NBD) : 0;
+    if (grp == 1) wait_vmcnt<wb>();
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- COMPUTE(kt) ----
+#pragma unroll
+    for (int i = 0; i < MS; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) acc[i][j] = mfma_wt(bf[j], af[i], acc[i][j]);
+    if (grp == 0) wait_vmcnt<wb>();
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  if (grp == 0) __builtin_amdgcn_s_barrier();  // both groups aligned again
+  wait_vmcnt<0>();
+  float(*red)[BM] = reinterpret_cast<float(*)[BM]>(a0);
+  if constexpr (SCL) {
+    const int c0 = wn * 32 + 4 * (lane >> 4);
+    gateup_epilogue_pp<BM, MS, NS>(
+        acc, [&](int i) { return sxl[rbase + i * 16 + (lane & 15)]; },
+        [&](int jj) { return *reinterpret_cast<const v4f*>(&s13l[c0 + 16 * jj]); },
+        [&](int jj) { return *reinterpret_cast<const v4f*>(&s13l[kHN + c0 + 16 * jj]); }, red,
+        rbase, wn, lane, te, S, ntile);
+  } else {
+    gateup_epilogue_pp<BM, MS, NS>(
+        acc, [&](int i) { return sxr[i]; }, [&](int jj) { return sgr[jj]; },
+        [&](int jj) { return sur[jj]; }, red, rbase, wn, lane, te, S, ntile);
+  }
+}
+
+// Weight stages of the ping-pong gate/up kernel for a tile height: four at
+// 128 rows (the LDS holds them), three at 192.
+template <int BM>
+constexpr int pp_weight_stages() { return BM <= 128 ? 4 : 3; }
+
 // ---------------------------------------------------------------------------
 // Down GEMM with per-(row, 128-K block) h scales. Tile: BM rows x 256 output
 // channels; wave (wm, wn) owns channels [64 wn, 64 wn + 64) of rows
@@ -1363,7 +1673,10 @@ hipError_t launch_gemms_bm(const FfnCall& c, TileHeader* hdr, TileEntry* up, Til
   constexpr int WU = waves_m<BM>(), WD = waves_m<BMD>();
   ev.mark(true, MOE_STEP_GATE_UP, s);
   if (cu > 0) {
-    if constexpr (KTU > 0 && BM >= 128)  // tall tiles: both operands through LDS
+    if constexpr (KTU > 0 && BM >= 128 && !W4)  // tall tiles, FP8: ping-pong schedule
+      hipLaunchKernelGGL((gateup_fp8_pp_kernel<BM, KTU, pp_weight_stages<BM>()>), dim3((unsigned)cu), dim3(8 * kWave), 0,
+                         s, c, hdr, up);
+    else if constexpr (KTU > 0 && BM >= 128)  // tall tiles: both operands through LDS
       hipLaunchKernelGGL((gateup_fp8_lds_kernel<BM, KTU, W4>), dim3((unsigned)cu), dim3(8 * kWave),
                          0, s, c, hdr, up);
     else  // (a fully unrolled K loop of tall tiles would spill: looped there)
