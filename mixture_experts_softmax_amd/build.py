@@ -21,6 +21,9 @@ LIB = os.path.join(PKG, "libmoe.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.hip", "route.hip", "permute.hip", "ffn.hip", "combine.hip", "qk_rope.hip"]
+# test-only device probes (tests/probes/<name>.hip -> tests/probes/lib<name>.so)
+PROBES = ["mfma_fp8_probe"]
+PROBE_DIR = os.path.join(ROOT, "tests", "probes")
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -66,7 +69,20 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
+    build_probes(verbose)
     return LIB
+
+
+def build_probes(verbose: bool = False):
+    """Compiles the test suite's device probes (not part of libmoe)."""
+    cc = hipcc()
+    for name in PROBES:
+        src = os.path.join(PROBE_DIR, name + ".hip")
+        if not os.path.exists(src):
+            continue
+        out = os.path.join(PROBE_DIR, "lib" + name + ".so")
+        _run([cc, *FLAGS, "-shared", src, "-o", out + ".tmp"], verbose)
+        os.replace(out + ".tmp", out)
 
 
 if __name__ == "__main__":
