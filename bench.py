@@ -87,8 +87,26 @@ def accounting(cfg, counts):
     layer_bytes = touched * (wb(2 * F, d) + wb(d, F)) \
         + ((wb(2 * Fs, d) + wb(d, Fs)) if Fs else 0) + E * d * 2 + 2 * T * d * 2
     layer_flops = 6.0 * d * (T * k * F + (T * Fs if Fs else 0))
+    # down launch: each touched group's W2 codes + scales once; per row the h
+    # codes + block scales in and the bf16 output row out
+    down_bytes = touched * wb(d, F) + (wb(d, Fs) if Fs else 0) \
+        + T * k * (F + F // 32 + 2 * d) + (T * (Fs + Fs // 32 + 2 * d) if Fs else 0)
+    down_flops = 2.0 * d * (T * k * F + (T * Fs if Fs else 0))
     return dict(touched=touched, groups=groups, rows=rows, up_bytes=up_bytes, up_flops=up_flops,
+                down_bytes=down_bytes, down_flops=down_flops,
                 layer_bytes=layer_bytes, layer_flops=layer_flops)
+
+
+def kernel_roofline(name, alg_bytes, flops, us):
+    """HBM and FP8 matrix-core fractions of one launch from its algorithmic
+    bytes and FLOPs and its average duration (us)."""
+    gbs = alg_bytes / (us / 1e6) / 1e9
+    tfl = flops / (us / 1e6) / 1e12
+    hbm, mfma = gbs / HBM_PEAK_GBS, tfl / FP8_PEAK_TFLOPS
+    return {"kernel": name, "bound": "hbm" if hbm >= mfma else "mfma", "avg_launch_us": round(us, 2),
+            "alg_bytes_per_launch": int(alg_bytes), "achieved_GBs": round(gbs, 1),
+            "hbm_frac": round(hbm, 4), "fp8_flops_per_launch": flops,
+            "achieved_TFLOPs": round(tfl, 1), "fp8_mfma_frac": round(mfma, 4)}
 
 
 def kernel_source_digest() -> str:
@@ -427,7 +445,13 @@ def hbm_copy_probe():
 def summarize(cfg, r):
     a = r["acc"]
     t = r["ms_step"] / 1e3
+    # the layer's two GEMM launches against both peaks: gate/up timed by events
+    # inside the timed loop, down by the per-step breakdown loop
+    roof = {"gate_up": kernel_roofline("gate_up", a["up_bytes"], a["up_flops"], r["up_ms"] * 1e3)}
+    if r["breakdown_us"].get("down"):
+        roof["down"] = kernel_roofline("down", a["down_bytes"], a["down_flops"], r["breakdown_us"]["down"])
     return {"workload": f"{cfg.name}: T={cfg.T} k={cfg.k} F={cfg.F}", "value": round(cfg.T / t, 1),
+            "roofline": roof,
             "unit": "tokens/s", "ms_per_step": round(r["ms_step"], 4),
             "hbm_frac": round(a["layer_bytes"] / t / 1e9 / HBM_PEAK_GBS, 4),
             "fp8_mfma_frac": round(a["layer_flops"] / t / 1e12 / FP8_PEAK_TFLOPS, 4),
@@ -468,6 +492,35 @@ def cpu_baseline(cfg, lt, n_tokens):
                 sample=f"first {n_tokens} tokens of the {cfg.name} workload (T={cfg.T}), "
                        f"{len(np.unique(ids))} touched experts, {dt:.1f}s of float64 numpy per "
                        f"run, median of 3 runs ({sum(runs):.1f}s in all)")
+
+
+def cpu_single_core(cfg, lt, n_tokens, reps):
+    """The oracle on one host thread (BLAS limited to one thread): median of
+    `reps` runs of the first n_tokens tokens of the workload."""
+    import numpy as np
+    import threadpoolctl
+
+    from oracle import inputs as oinputs
+    from oracle import moe as omoe
+
+    inp = oinputs.layer_inputs(lt, cache_all=True)
+    tok = np.arange(n_tokens)
+    x64 = omoe.activations(inp)[:n_tokens]
+    ids = omoe.topk_ids(omoe.router_logits(x64, omoe.router_weight(inp), inp.router_bias), cfg.k)
+    for e in np.unique(ids):
+        inp.expert(int(e))
+    runs = []
+    with threadpoolctl.threadpool_limits(1):
+        for _ in range(reps):
+            t = time.perf_counter()
+            omoe.layer_forward_tokens(inp, tok)
+            runs.append(time.perf_counter() - t)
+    dt = sorted(runs)[len(runs) // 2]
+    return dict(value=round(n_tokens / dt, 3), unit="tokens/s", cores=1, kind="oracle",
+                us_per_layer=round(dt * 1e6, 1) if n_tokens == cfg.T else None,
+                sample=f"first {n_tokens} of the {cfg.T} tokens of the {cfg.name} workload, "
+                       f"{len(np.unique(ids))} touched experts, one thread, median of {reps} runs "
+                       f"({sum(runs):.1f}s in all)")
 
 
 def main():
@@ -554,6 +607,7 @@ def main():
                   "touched_experts": acc["touched"], "step_breakdown_us": r["breakdown_us"]},
     }
     out["layer"]["call_us"] = r["call_us"]
+    out["layer"]["kernels"] = summarize(cfg, r)["roofline"]
     if not args.no_secondary:
         # the other workloads, reported beside the headline (not part of `value`)
         sec_steps, sec_warm = max(5, args.steps // 2), max(2, args.warmup // 2)
@@ -608,6 +662,16 @@ def main():
         log("[bench] timing the CPU oracle")
         n = args.cpu_tokens if args.cpu_tokens > 0 else min(cfg.T, 64)
         out["cpu_baseline"] = cpu_baseline(cfg, lt, n)
+        # the same oracle on one host thread: the whole tiny workload, and a
+        # sample of the decode step
+        from synthetic import make_layer
+        log("[bench] timing the CPU oracle on one thread")
+        tiny = CONFIGS["tiny"]
+        lt_tiny = make_layer(tiny, device="cuda")
+        single = {"tiny": cpu_single_core(tiny, lt_tiny, tiny.T, 21)}
+        if cfg.name == "decode":
+            single["decode"] = cpu_single_core(cfg, lt, 8, 3)
+        out["cpu_baseline"]["single_core"] = single
     print(json.dumps(out), flush=True)
 
 

@@ -1260,7 +1260,11 @@ __global__ __launch_bounds__(8 * kWave) void down_fp8_lds_kernel(
   const int sid = te.gid >> 16, g = te.gid & 0xffff;
   const SetView S = set_view(c, sid);
   const int F = S.F;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  // the wave index in a scalar register frees vector registers on the FP8
+  // path (spill-free at 192 rows x 2 N tiles); the MXFP4 path allocates best
+  // with it in a vector register
+  const int wave = W4 ? tid / kWave : __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave / kNWaves, wn = wave % kNWaves;
   const int rbase = wm * BMW;
 
@@ -1278,19 +1282,12 @@ __global__ __launch_bounds__(8 * kWave) void down_fp8_lds_kernel(
   // (never used)
   const size_t wrb = W4 ? F / 2 : F;
   const uint8_t* w2 = S.w2 + (size_t)g * d * wrb;
-  int brow[NBD], bcc[NBD];
-#pragma unroll
-  for (int i = 0; i < NBD; ++i) {
-    if constexpr (W4) {
-      const int rr = 16 * (NBD * wave + i) + (lane >> 2);
-      brow[i] = rr;
-      bcc[i] = ((lane & 3) ^ ((rr >> 2) & 3)) * 16;
-    } else {
-      const int rr = 8 * (NBD * wave + i) + (lane >> 3);
-      brow[i] = rr;
-      bcc[i] = ((lane & 7) ^ (rr & 7)) * 16;
-    }
-  }
+  // B piece i of this thread: row brow0 + RPB i of the N tile; its chunk
+  // (the swizzle) is the same for every i, since RPB is a multiple of the
+  // swizzle period
+  constexpr int RPB = W4 ? 16 : 8;  // rows per 1 KiB block
+  const int brow0 = RPB * NBD * wave + (W4 ? (lane >> 2) : (lane >> 3));
+  const int bcc = W4 ? ((lane & 3) ^ ((brow0 >> 2) & 3)) * 16 : ((lane & 7) ^ (brow0 & 7)) * 16;
   auto load_a = [&](int st, uint8_t* dst) {
     const int kt = st % KTC;
 #pragma unroll
@@ -1300,8 +1297,8 @@ __global__ __launch_bounds__(8 * kWave) void down_fp8_lds_kernel(
     const int n = min(st / KTC, dnt - 1 - nt0), kt = st % KTC;
 #pragma unroll
     for (int i = 0; i < NBD; ++i) {
-      const int ch = min((nt0 + n) * kDownBN + brow[i], d - 1);
-      dma16(w2 + (size_t)ch * wrb + kt * KB + bcc[i], dst + (NBD * wave + i) * 1024);
+      const int ch = min((nt0 + n) * kDownBN + brow0 + RPB * i, d - 1);
+      dma16(w2 + (size_t)ch * wrb + kt * KB + bcc, dst + (NBD * wave + i) * 1024);
     }
   };
   // h block scales of the tile's rows, and every N tile's channel scales
