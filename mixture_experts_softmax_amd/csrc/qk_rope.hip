@@ -4,19 +4,25 @@
 // RMS-normalised with its learned weight, rotated by its token's position
 // and written back.
 //
-// One workgroup per token, one lane per 16 bytes of its query and key heads
-// (LPH lanes per head, all in one wave). Each lane issues its loads first;
-// while they are in flight the first HD/2 lanes evaluate the token's rotation
-// table into LDS, one pair each (angle p * theta^(-2i/HD) in float64). After
-// the barrier the head's sum of squares is reduced across its lanes by xor
-// shuffles, and each lane normalises, rotates (the partner half comes from
-// lane ^ LPH/2 for the halves pairing; interleaved pairs lie within the lane)
-// and stores. One table per token: a table per wave costs more in fp64
-// arithmetic than the barrier it saves.
+// Lane layout: a lane holds NCH 16-byte chunks of a head that together
+// contain whole rotation pairs -- one chunk for the interleaved pairing
+// (pairs (2i, 2i+1) inside the chunk), chunk c and chunk c + HD/2 for the
+// halves pairing (pairs (i, i + HD/2) across them) -- so the rotation needs
+// no lane exchange; LPH = HD / (VEC NCH) lanes per head, 64 / LPH heads side
+// by side per round. Wave tasks: a wave takes RPW consecutive rounds of one
+// token (all of them for long batches, one for short ones, so that a batch of
+// any size has enough waves in flight). A lane's weight chunks (query and
+// key) are loaded once; all of the task's head loads are issued before the
+// first is used, and while they are in flight the wave evaluates its token's
+// rotation table (angle p * theta^(-2i/HD) in float64) into its own LDS
+// slice -- no workgroup barrier, a wave's LDS accesses stay in order. The
+// head's sum of squares is reduced over its lanes by DPP row moves; each lane
+// normalises, rotates and stores.
 // HBM-bound: every byte of the q and k heads is read once and written once.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "internal.h"
@@ -53,113 +59,168 @@ __device__ inline float2 rope_cs(int i, int pos, double log2_theta) {
   return make_float2(cn, sn);
 }
 
-template <typename E, int HD, int STYLE>
-__global__ __launch_bounds__(1024) void qk_norm_rope_kernel(E* __restrict__ qkv,
-                                                            const int32_t* __restrict__ positions,
-                                                            const E* __restrict__ qw,
-                                                            const E* __restrict__ kw, int n_q,
-                                                            int n_kv, int64_t row_stride,
-                                                            int64_t q_off, int64_t k_off,
-                                                            float eps, float theta) {
-  constexpr int VEC = Elem<E>::kVec;  // elements per 16-byte lane chunk
-  constexpr int LPH = HD / VEC;       // lanes per head (divides the wave)
-  static_assert(LPH <= kWave && kWave % LPH == 0, "a head must sit in one wave");
-  __shared__ float2 cs[HD / 2];       // (cos, sin) of pair i
+constexpr int kQkWavesPerBlock = 4;  // wave tasks per workgroup
+// rounds per wave task, at most: 9 chunk loads in flight per lane
+__host__ __device__ constexpr int qk_batch(int nch) { return nch == 2 ? 5 : 9; }
 
-  const int t = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int nch = (n_q + n_kv) * LPH;
-  E* row = qkv + (size_t)t * row_stride;
-  auto chunk_ptr = [&](int ch, const E*& w) {
-    const int h = ch / LPH, l = ch % LPH;
-    const bool is_q = h < n_q;
-    w = (is_q ? qw : kw) + l * VEC;
-    return row + (is_q ? q_off + (int64_t)h * HD : k_off + (int64_t)(h - n_q) * HD) + l * VEC;
+// Sum over aligned groups of N lanes (N a power of two): DPP within rows of
+// 16 (quad swaps, then the half-row and row mirrors, each pairing lanes of
+// the two halves combined so far), shuffles across rows.
+template <int N>
+__device__ inline float group_sum(float v) {
+  auto dpp = [](float x, auto ctrl) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                 decltype(ctrl)::value, 0xF, 0xF,
+                                                                 false));
   };
-  // each thread's first chunk is loaded before the table is computed, so
-  // the loads' latency overlaps that work
-  v4i xr, wr;
-  if (tid < nch) {
-    const E* w;
-    const E* p = chunk_ptr(tid, w);
-    xr = *reinterpret_cast<const v4i*>(p);
-    wr = *reinterpret_cast<const v4i*>(w);
+  if constexpr (N >= 2) v += dpp(v, std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]
+  if constexpr (N >= 4) v += dpp(v, std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]
+  if constexpr (N >= 8) v += dpp(v, std::integral_constant<int, 0x141>{});  // row_half_mirror
+  if constexpr (N >= 16) v += dpp(v, std::integral_constant<int, 0x140>{}); // row_mirror
+  if constexpr (N >= 32) v += __shfl_xor(v, 16, kWave);
+  if constexpr (N >= 64) v += __shfl_xor(v, 32, kWave);
+  return v;
+}
+
+template <typename E, int HD, int STYLE>
+__global__ __launch_bounds__(kQkWavesPerBlock * kWave) void qk_norm_rope_kernel(
+    E* __restrict__ qkv, const int32_t* __restrict__ positions, const E* __restrict__ qw,
+    const E* __restrict__ kw, int T, int n_q, int n_kv, int64_t row_stride, int64_t q_off,
+    int64_t k_off, float eps, float theta, int rpw) {
+  constexpr int VEC = Elem<E>::kVec;                      // elements per 16-byte chunk
+  constexpr int NCH = STYLE == MOE_ROPE_HALVES ? 2 : 1;   // chunks per lane and head
+  constexpr int LPH = HD / (VEC * NCH);                   // lanes per head
+  constexpr int HPR = kWave / LPH;                        // heads per round
+  constexpr int RB = qk_batch(NCH);
+  static_assert(LPH <= kWave && kWave % LPH == 0, "a head must sit in one wave");
+  __shared__ float2 cs_all[kQkWavesPerBlock][HD / 2];  // (cos, sin) of pair i, per wave
+
+  const int wv = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int nh = n_q + n_kv;
+  const int rounds_all = (nh + HPR - 1) / HPR;
+  const int wpt = (rounds_all + rpw - 1) / rpw;  // wave tasks per token
+  const int task = blockIdx.x * kQkWavesPerBlock + wv;
+  const int t = task / wpt;
+  if (t >= T) return;  // whole waves: nothing below synchronises across waves
+  const int rbeg = (task % wpt) * rpw;
+  const int rounds = min(rbeg + rpw, rounds_all);  // this task: rounds [rbeg, rounds)
+  float2* cs = cs_all[wv];
+  const int l = lane % LPH, hs = lane / LPH;  // lane of the head, head slot of the round
+  // element offset of chunk n of this lane within a head
+  auto coff = [&](int n) { return (n == 0 ? l : l + HD / (2 * VEC)) * VEC; };
+  E* row = qkv + (size_t)t * row_stride;
+  auto head_ptr = [&](int h) {  // head h (h < nh)
+    return row + (h < n_q ? q_off + (int64_t)h * HD : k_off + (int64_t)(h - n_q) * HD);
+  };
+  // the lane's weight chunks and the task's head chunks, then the rotation
+  // table while they are in flight
+  v4i wq[NCH], wk[NCH];
+#pragma unroll
+  for (int n = 0; n < NCH; ++n) {
+    wq[n] = n_q > 0 ? *reinterpret_cast<const v4i*>(qw + coff(n)) : v4i{0, 0, 0, 0};
+    wk[n] = n_kv > 0 ? *reinterpret_cast<const v4i*>(kw + coff(n)) : v4i{0, 0, 0, 0};
   }
-  if (tid < HD / 2) cs[tid] = rope_cs<HD>(tid, positions[t], log2((double)theta));
-  __syncthreads();
+  v4i xr[RB][NCH];
+#pragma unroll
+  for (int j = 0; j < RB; ++j) {
+    const int h = (rbeg + j) * HPR + hs;
+    if (rbeg + j < rounds && h < nh) {
+#pragma unroll
+      for (int n = 0; n < NCH; ++n) xr[j][n] = *reinterpret_cast<const v4i*>(head_ptr(h) + coff(n));
+    }
+  }
+  {
+    const int pos = positions[t];
+    const double l2t = log2((double)theta);
+#pragma unroll
+    for (int i = lane; i < HD / 2; i += kWave) cs[i] = rope_cs<HD>(i, pos, l2t);
+  }
+  __builtin_amdgcn_wave_barrier();
 
   const float inv_hd = 1.0f / HD;
-  // blockDim is a multiple of LPH, so a head's lanes run every iteration together
-  for (int ch = tid; ch < nch; ch += blockDim.x) {
-    const int l = ch % LPH;
-    const E* w;
-    E* p = chunk_ptr(ch, w);
-    E xv[VEC], wv[VEC];
-    if (ch == tid) {
-      *reinterpret_cast<v4i*>(xv) = xr;
-      *reinterpret_cast<v4i*>(wv) = wr;
-    } else {
-      *reinterpret_cast<v4i*>(xv) = *reinterpret_cast<const v4i*>(p);
-      *reinterpret_cast<v4i*>(wv) = *reinterpret_cast<const v4i*>(w);
-    }
-    float v[VEC];
+#pragma unroll
+  for (int j = 0; j < RB; ++j) {
+    const int rr = rbeg + j;
+    if (rr >= rounds) break;  // uniform across the wave
+    const int h = rr * HPR + hs;
+    const bool live = h < nh;  // a head slot of the last round may be empty
+    float v[NCH][VEC];
     float ss = 0.f;
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      v[e] = Elem<E>::load(xv[e]);
-      ss = fmaf(v[e], v[e], ss);
+    for (int n = 0; n < NCH; ++n) {
+      E xv[VEC];
+      *reinterpret_cast<v4i*>(xv) = xr[j][n];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        v[n][e] = live ? Elem<E>::load(xv[e]) : 0.f;
+        ss = fmaf(v[n][e], v[n][e], ss);
+      }
     }
+    ss = group_sum<LPH>(ss);
+    const float rn = 1.0f / sqrtf(ss * inv_hd + eps);
 #pragma unroll
-    for (int m = LPH / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
-    const float r = 1.0f / sqrtf(ss * inv_hd + eps);
+    for (int n = 0; n < NCH; ++n) {  // normalised, times the learned weight
+      E wv_[VEC];
+      *reinterpret_cast<v4i*>(wv_) = (h < n_q) ? wq[n] : wk[n];
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) v[e] = v[e] * r * Elem<E>::load(wv[e]);
+      for (int e = 0; e < VEC; ++e) v[n][e] = v[n][e] * rn * Elem<E>::load(wv_[e]);
+    }
 
-    float o[VEC];
+    float o[NCH][VEC];
     if constexpr (STYLE == MOE_ROPE_INTERLEAVED) {
 #pragma unroll
       for (int m = 0; m < VEC / 2; ++m) {
         const float2 f = cs[(l * VEC) / 2 + m];
-        const float a = v[2 * m], b = v[2 * m + 1];
-        o[2 * m] = a * f.x - b * f.y;
-        o[2 * m + 1] = a * f.y + b * f.x;
+        const float a = v[0][2 * m], b = v[0][2 * m + 1];
+        o[0][2 * m] = a * f.x - b * f.y;
+        o[0][2 * m + 1] = a * f.y + b * f.x;
       }
-    } else {
-      const bool first = l < LPH / 2;
-      const int i0 = (first ? l : l - LPH / 2) * VEC;
+    } else {  // pair i = l VEC + e: a in chunk 0, b in chunk 1
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
-        const float q = __shfl_xor(v[e], LPH / 2);
-        const float2 f = cs[i0 + e];
-        // first half: a = own, b = partner; second half: a = partner, b = own
-        o[e] = first ? v[e] * f.x - q * f.y : q * f.y + v[e] * f.x;
+        const float2 f = cs[l * VEC + e];
+        const float a = v[0][e], b = v[1][e];
+        o[0][e] = a * f.x - b * f.y;
+        o[1][e] = a * f.y + b * f.x;
       }
     }
+    if (live) {
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) xv[e] = Elem<E>::store(o[e]);
-    *reinterpret_cast<v4i*>(p) = *reinterpret_cast<const v4i*>(xv);
+      for (int n = 0; n < NCH; ++n) {
+        E xv[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) xv[e] = Elem<E>::store(o[n][e]);
+        *reinterpret_cast<v4i*>(head_ptr(h) + coff(n)) = *reinterpret_cast<const v4i*>(xv);
+      }
+    }
   }
 }
 
 template <typename E, int HD>
 hipError_t launch_hd(const moe_qk_shape_t& s, void* qkv, const int32_t* pos, const void* qw,
                      const void* kw, hipStream_t st) {
-  constexpr int LPH = HD / Elem<E>::kVec;
-  const int nch = (s.n_q + s.n_kv) * LPH;
   const auto* q = static_cast<const E*>(qw);
   const auto* k = static_cast<const E*>(kw);
-  // one thread per 16-byte chunk of the token's heads (looping beyond 1024
-  // threads), and at least one per rotation pair for the table, in whole waves
-  const int need = std::max(std::min(nch, 1024), HD / 2);
-  const int nth = ((need + kWave - 1) / kWave) * kWave;
+  // rounds per wave task: enough tasks to keep the chip's waves busy (a
+  // short batch splits each token over several waves), at most qk_batch
+  const int nch = s.style == MOE_ROPE_HALVES ? 2 : 1;
+  const int hpr = kWave / (HD / (Elem<E>::kVec * nch));
+  const int rounds = (s.n_q + s.n_kv + hpr - 1) / hpr;
+  const long long target = 2048;  // wave tasks
+  const int rpw = (int)std::max(1LL, std::min<long long>(
+                                         std::min(rounds, qk_batch(nch)),
+                                         (long long)s.T * rounds / target));
+  const long long tasks = (long long)s.T * ((rounds + rpw - 1) / rpw);
+  const dim3 grid((unsigned)((tasks + kQkWavesPerBlock - 1) / kQkWavesPerBlock));
+  const dim3 block(kQkWavesPerBlock * kWave);
   if (s.style == MOE_ROPE_INTERLEAVED)
-    hipLaunchKernelGGL((qk_norm_rope_kernel<E, HD, MOE_ROPE_INTERLEAVED>), dim3(s.T), dim3(nth), 0,
-                       st, static_cast<E*>(qkv), pos, q, k, s.n_q, s.n_kv, s.row_stride,
-                       s.q_offset, s.k_offset, s.eps, s.theta);
+    hipLaunchKernelGGL((qk_norm_rope_kernel<E, HD, MOE_ROPE_INTERLEAVED>), grid, block, 0, st,
+                       static_cast<E*>(qkv), pos, q, k, s.T, s.n_q, s.n_kv, s.row_stride,
+                       s.q_offset, s.k_offset, s.eps, s.theta, rpw);
   else
-    hipLaunchKernelGGL((qk_norm_rope_kernel<E, HD, MOE_ROPE_HALVES>), dim3(s.T), dim3(nth), 0, st,
-                       static_cast<E*>(qkv), pos, q, k, s.n_q, s.n_kv, s.row_stride, s.q_offset,
-                       s.k_offset, s.eps, s.theta);
+    hipLaunchKernelGGL((qk_norm_rope_kernel<E, HD, MOE_ROPE_HALVES>), grid, block, 0, st,
+                       static_cast<E*>(qkv), pos, q, k, s.T, s.n_q, s.n_kv, s.row_stride,
+                       s.q_offset, s.k_offset, s.eps, s.theta, rpw);
   return hipGetLastError();
 }
 
