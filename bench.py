@@ -228,6 +228,61 @@ def time_layer(cfg, steps, warmup, hip):
                 call_us=pct)
 
 
+def time_overlap(cfg, steps, warmup, hip):
+    """Back-to-back layer calls, one stream against moe_layer_forward_overlap
+    (the shared expert on a second stream, forked after the router's logits):
+    ms per call of each, from events on the main stream around `steps` calls."""
+    import torch
+
+    import mixture_experts_softmax_amd as M
+    from mixture_experts_softmax_amd import _lib
+    from synthetic import make_layer
+
+    lt = make_layer(cfg, device="cuda")
+    L = M.MoELayer(d=cfg.d, E=cfg.E, k=cfg.k, F=cfg.F, F_shared=cfg.F_shared,
+                   precision=cfg.precision, w_router=lt.w_router, router_bias=lt.router_bias,
+                   w13=lt.w13, w13_scale=lt.w13_scale, w2=lt.w2, w2_scale=lt.w2_scale, ws13=lt.ws13,
+                   ws13_scale=lt.ws13_scale, ws2=lt.ws2, ws2_scale=lt.ws2_scale)
+    T = cfg.T
+    s = L.shape(T)
+    ws = L.workspace(T, "cuda")
+    W = _lib.make_weights(s, **L.tensors)
+    x, y = lt.x, torch.empty_like(lt.x)
+    ids = torch.empty((T, cfg.k), dtype=torch.int32, device="cuda")
+    gw = torch.empty((T, cfg.k), dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    hip.L.hipEventCreateWithFlags.argtypes = [C.POINTER(C.c_void_p), C.c_uint]
+    hip.L.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
+    evs = []
+    for _ in range(2):
+        e = C.c_void_p()
+        hip.L.hipEventCreateWithFlags(C.byref(e), 2)  # no timing
+        evs.append(e.value)
+    stream = torch.cuda.current_stream().cuda_stream
+    calls = {"single": lambda: _lib.moe_layer_forward(s, W, x, y, ids, gw, ws),
+             "overlap": lambda: _lib.moe_layer_forward_overlap(s, W, x, y, ids, gw, ws, side,
+                                                               evs[0], evs[1])}
+    out = {}
+    for name, fn in calls.items():
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = hip.event(), hip.event()
+        hip.L.hipEventRecord(C.c_void_p(a), C.c_void_p(stream))
+        for _ in range(steps):
+            fn()
+        hip.L.hipEventRecord(C.c_void_p(b), C.c_void_p(stream))
+        out[name + "_ms_per_call"] = round(hip.ms(a, b) / steps, 4)
+        hip.destroy(a)
+        hip.destroy(b)
+    for e in evs:
+        hip.destroy(e)
+    out["speedup"] = round(out["single_ms_per_call"] / out["overlap_ms_per_call"], 3)
+    del L, ws, W, x, y, lt
+    torch.cuda.empty_cache()
+    return out
+
+
 def time_graph(cfg, steps, warmup, hip):
     """moe_layer_forward captured once into a HIP graph (torch.cuda.CUDAGraph
     on the capturing stream) and replayed: per-replay GPU time from events on
@@ -648,6 +703,11 @@ def main():
         out["mixed"]["split_256_32_ms"] = round(rs["ms"], 4)
         out["mixed"]["speedup_vs_split"] = round(rs["ms"] / rm["ms_step"], 3)
         torch.cuda.empty_cache()
+        # the shared expert overlapped with the routing on a second stream
+        for name in ("decode", "prefill"):
+            log(f"[bench] {name}: shared expert on a second stream")
+            out.setdefault(name if name != cfg.name else "layer", {})["shared_overlap"] = \
+                time_overlap(CONFIGS[name], sec_steps, sec_warm, hip)
         # the decode step captured into a HIP graph and replayed
         log("[bench] decode replayed from a HIP graph")
         out["decode_graph"] = time_graph(cfg if cfg.T <= 64 else CONFIGS["decode"],

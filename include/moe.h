@@ -256,6 +256,29 @@ moe_status_t moe_layer_forward(const moe_shape_t* shape, const moe_weights_t* we
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * moe_layer_forward with the shared expert overlapped with the routing, as the
+ * NVIDIA blog runs it (section "Cutting transformer-layer time by 34%": the
+ * shared expert's computation on a second stream, hidden behind the router
+ * logits and top-k; Table 1 row "Shared expert compute"). The shared expert's
+ * GEMMs go on side_stream, which waits for fork_event -- recorded on `stream`
+ * right after the router's logits launch, which writes the FP8 x codes the
+ * shared expert reads -- while `stream` runs the selection, the permutation
+ * and the routed GEMMs; `stream` waits for join_event, recorded on side_stream
+ * after the shared expert's down GEMM, before the combine. side_stream and
+ * both events (hipStream_t, hipEvent_t; events created by the caller,
+ * preferably without timing) belong to the caller and must be distinct; the
+ * call enqueues work on both streams and returns. Results are bit-identical
+ * to moe_layer_forward. Shapes without a shared expert, and the float32 path,
+ * run entirely on `stream` (nothing is enqueued on side_stream). Workspace as
+ * moe_layer_forward; a call must not overlap another call on the same
+ * workspace or events.
+ */
+moe_status_t moe_layer_forward_overlap(const moe_shape_t* shape, const moe_weights_t* weights,
+                                       const void* x, void* y, int32_t* topk_ids, float* topk_w,
+                                       void* workspace, size_t workspace_bytes, void* stream,
+                                       void* side_stream, void* fork_event, void* join_event);
+
+/*
  * Where moe_layer_forward leaves its intermediate results inside its workspace:
  * byte offsets from the workspace start (MOE_NO_REGION where the shape has no
  * such result). They hold the results of the last call that used the

@@ -27,7 +27,7 @@ EXPORTS = [
     "moe_grouped_ffn_workspace_size", "moe_layer_workspace_regions",
     "moe_route_topk", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_forward",
     "moe_layer_forward_events", "moe_host_e4m3_encode", "moe_qk_norm_rope",
-    "moe_layer_forward_noalloc",
+    "moe_layer_forward_noalloc", "moe_layer_forward_overlap",
 ]
 MOE_ROPE_INTERLEAVED, MOE_ROPE_HALVES = 0, 1
 
@@ -111,6 +111,8 @@ def lib() -> C.CDLL:
         L.moe_combine.argtypes = [P] * 7
         L.moe_layer_forward.restype = I32
         L.moe_layer_forward.argtypes = [P, P, P, P, P, P, P, SZ, P]
+        L.moe_layer_forward_overlap.restype = I32
+        L.moe_layer_forward_overlap.argtypes = [P, P, P, P, P, P, P, SZ, P, P, P, P]
         L.moe_layer_forward_noalloc.restype = I32
         L.moe_layer_forward_noalloc.argtypes = [P] * 7
         L.moe_layer_forward_events.restype = I32
@@ -344,6 +346,20 @@ def moe_layer_forward(s: MoeShape, weights: MoeWeights, x, y, topk_ids, topk_w, 
                                    _ptr(workspace, "workspace", torch.uint8),
                                    workspace.numel() if workspace is not None else 0,
                                    _stream(stream)), "moe_layer_forward")
+
+
+def moe_layer_forward_overlap(s: MoeShape, weights: MoeWeights, x, y, topk_ids, topk_w, workspace,
+                              side_stream, fork_event: int, join_event: int, stream=None):
+    """moe_layer_forward with the shared expert on side_stream (a torch stream),
+    forked and joined through two caller-created hipEvent_t handles (int)."""
+    T, d, k = s.T, s.d, s.k
+    ad = _act_dtype(s)
+    _check(lib().moe_layer_forward_overlap(
+        C.byref(s), C.byref(weights), _ptr(x, "x", ad, T * d), _ptr(y, "y", ad, T * d),
+        _ptr(topk_ids, "topk_ids", torch.int32, T * k), _ptr(topk_w, "topk_w", torch.float32, T * k),
+        _ptr(workspace, "workspace", torch.uint8), workspace.numel() if workspace is not None else 0,
+        _stream(stream), _stream(side_stream), C.c_void_p(fork_event), C.c_void_p(join_event)),
+        "moe_layer_forward_overlap")
 
 
 def moe_layer_forward_noalloc(s: MoeShape, weights: MoeWeights, x, y, topk_ids, topk_w,

@@ -145,6 +145,20 @@ size_t carve_ffn(FfnCall& c, bool fp8, Carve& cv, void** tiles) {
   return cv.off;
 }
 
+// The routed experts alone (set 0) and the shared expert alone (set 1 as the
+// only set) of a layer's grouped-FFN call.
+FfnCall routed_call(const FfnCall& c) {
+  FfnCall r = c;
+  r.nsets = 1;
+  return r;
+}
+FfnCall shared_call(const FfnCall& c) {
+  FfnCall r = c;
+  r.nsets = 1;
+  r.set[0] = c.set[1];
+  return r;
+}
+
 // The layer's workspace; with base == nullptr only the size is computed.
 struct LayerWs {
   int32_t* ids;
@@ -160,6 +174,7 @@ struct LayerWs {
   void* expert_out;
   void* shared_out;
   void* tiles;
+  void* tiles_shared;  // the shared expert's own tile lists (second-stream schedule)
   size_t bytes;
 };
 
@@ -191,6 +206,11 @@ LayerWs layer_ws(const moe_shape_t* s, void* base, FfnCall* call) {
     c.set[1] = make_set(nullptr, nullptr, nullptr, nullptr, w4, nullptr, nullptr, 1, 1,
                         s->F_shared, s->T, s->T, L.shared_out);
   carve_ffn(c, fp8, cv, &L.tiles);
+  L.tiles_shared = nullptr;
+  if (fp8 && c.nsets > 1) {
+    FfnCall cs = shared_call(c);
+    L.tiles_shared = cv.take<uint8_t>(ffn_tiles_ws_bytes(cs));
+  }
   L.bytes = cv.off;
   if (call) *call = c;
   return L;
@@ -449,13 +469,13 @@ moe_status_t moe_layer_forward(const moe_shape_t* s, const moe_weights_t* wt, co
                                   stream, nullptr, nullptr);
 }
 
-moe_status_t moe_layer_forward_events(const moe_shape_t* s, const moe_weights_t* wt,
-                                      const void* x, void* y, int32_t* topk_ids, float* topk_w,
-                                      void* workspace, size_t workspace_bytes, void* stream,
-                                      void* const* start_events, void* const* stop_events) {
-  StepEvents ev;
-  ev.start = start_events;
-  ev.stop = stop_events;
+// The layer on `stream`; with side != nullptr (quantised paths with a shared
+// expert) the shared expert's GEMMs run on `side`, forked by `fork` right after
+// the router's logits launch and joined by `join` before the combine.
+static moe_status_t layer_forward(const moe_shape_t* s, const moe_weights_t* wt, const void* x,
+                                  void* y, int32_t* topk_ids, float* topk_w, void* workspace,
+                                  size_t workspace_bytes, hipStream_t hs, const StepEvents& ev,
+                                  hipStream_t side, hipEvent_t fork, hipEvent_t join) {
   moe_status_t st = check_shape(s);
   if (st != MOE_OK) return st;
   if (s->T == 0) return MOE_OK;
@@ -471,7 +491,6 @@ moe_status_t moe_layer_forward_events(const moe_shape_t* s, const moe_weights_t*
   LayerWs L = layer_ws(s, workspace, &c);
   int32_t* ids = topk_ids ? topk_ids : L.ids;
   float* w = topk_w ? topk_w : L.w;
-  const hipStream_t hs = static_cast<hipStream_t>(stream);
 
   c.a_rows = s->T;
   c.a = fp8 ? static_cast<const void*>(L.xq) : x;
@@ -484,47 +503,61 @@ moe_status_t moe_layer_forward_events(const moe_shape_t* s, const moe_weights_t*
   {
     FfnSet& R = c.set[0];
     uint8_t* h = R.h;
-    float* hs = R.h_scale;
+    float* hsc = R.h_scale;
     set_weights(R, wt->w13, wt->w13_scale, wt->w2, wt->w2_scale);
     R.h = h;
-    R.h_scale = hs;
+    R.h_scale = hsc;
   }
   if (c.nsets > 1) {
     FfnSet& Sh = c.set[1];
     uint8_t* h = Sh.h;
-    float* hs = Sh.h_scale;
+    float* hsc = Sh.h_scale;
     set_weights(Sh, wt->ws13, wt->ws13_scale, wt->ws2, wt->ws2_scale);
     Sh.h = h;
-    Sh.h_scale = hs;
+    Sh.h_scale = hsc;
   }
   const int bm = choose_bm(ceil_div(s->T * s->k, s->E));
+  // second-stream schedule: the routed launches carry set 0 only, the shared
+  // expert (same tile height, so the same kernels and tiles) runs on `side`
+  const bool split = side != nullptr && fp8 && c.nsets > 1;
+  const FfnCall cr = split ? routed_call(c) : c;
 
   // Up to one permutation tile of tokens, the top-k workgroup also does the
   // permutation (and, FP8 path, writes the FFN tile lists); the permute step
   // then has no kernels of its own.
   const bool fused = s->T <= kPermTile;
-  RoutePermute rp{L.offsets, L.sorted_pair, L.pair_to_row, fp8 ? &c : nullptr, bm,
+  RoutePermute rp{L.offsets, L.sorted_pair, L.pair_to_row, fp8 ? &cr : nullptr, bm,
                   fp8 ? L.tiles : nullptr};
   hipError_t e;
   ev.mark(true, MOE_STEP_ROUTE, hs);
   e = launch_route(fp8, x, wt->w_router, wt->router_bias, s->T, s->d, s->E, s->k, ids, w, L.xq,
-                   L.xs, L.logits, L.masks, L.counts, fused ? &rp : nullptr, hs);
+                   L.xs, L.logits, L.masks, L.counts, fused ? &rp : nullptr, hs,
+                   split ? fork : nullptr);
   ev.mark(false, MOE_STEP_ROUTE, hs);
   if (e != hipSuccess) return MOE_ERR_HIP;
+  if (split) {  // the shared expert needs only the x codes
+    const FfnCall csh = shared_call(c);
+    e = hipStreamWaitEvent(side, fork, 0);
+    if (e == hipSuccess) e = launch_ffn_tiles(csh, bm, L.tiles_shared, side);
+    if (e == hipSuccess) e = launch_ffn_gemms(csh, bm, L.tiles_shared, side);
+    if (e == hipSuccess) e = hipEventRecord(join, side);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
   // scan + scatter; on the FP8 path the scan also writes the FFN tile lists
   ev.mark(true, MOE_STEP_PERMUTE, hs);
   if (!fused)
     e = launch_perm_scan_scatter(ids, s->T, s->E, s->k, L.masks, L.counts, L.offsets,
-                                 L.sorted_pair, L.pair_to_row, fp8 ? &c : nullptr, bm,
+                                 L.sorted_pair, L.pair_to_row, fp8 ? &cr : nullptr, bm,
                                  fp8 ? L.tiles : nullptr, hs);
   ev.mark(false, MOE_STEP_PERMUTE, hs);
   if (e != hipSuccess) return MOE_ERR_HIP;
 
   if (fp8)
-    e = launch_ffn_gemms(c, bm, L.tiles, hs, ev);
+    e = launch_ffn_gemms(cr, bm, L.tiles, hs, ev);
   else
     e = launch_grouped_ffn_f32(c, hs, ev);
   if (e != hipSuccess) return MOE_ERR_HIP;
+  if (split && hipStreamWaitEvent(hs, join, 0) != hipSuccess) return MOE_ERR_HIP;
 
   ev.mark(true, MOE_STEP_COMBINE, hs);
   if (fp8)
@@ -537,6 +570,30 @@ moe_status_t moe_layer_forward_events(const moe_shape_t* s, const moe_weights_t*
                            s->d, s->k, hs);
   ev.mark(false, MOE_STEP_COMBINE, hs);
   return from_hip(e);
+}
+
+moe_status_t moe_layer_forward_events(const moe_shape_t* s, const moe_weights_t* wt,
+                                      const void* x, void* y, int32_t* topk_ids, float* topk_w,
+                                      void* workspace, size_t workspace_bytes, void* stream,
+                                      void* const* start_events, void* const* stop_events) {
+  StepEvents ev;
+  ev.start = start_events;
+  ev.stop = stop_events;
+  return layer_forward(s, wt, x, y, topk_ids, topk_w, workspace, workspace_bytes,
+                       static_cast<hipStream_t>(stream), ev, nullptr, nullptr, nullptr);
+}
+
+moe_status_t moe_layer_forward_overlap(const moe_shape_t* s, const moe_weights_t* wt,
+                                       const void* x, void* y, int32_t* topk_ids, float* topk_w,
+                                       void* workspace, size_t workspace_bytes, void* stream,
+                                       void* side_stream, void* fork_event, void* join_event) {
+  if (side_stream == nullptr || side_stream == stream || fork_event == nullptr ||
+      join_event == nullptr || fork_event == join_event)
+    return MOE_ERR_INVALID_ARG;
+  return layer_forward(s, wt, x, y, topk_ids, topk_w, workspace, workspace_bytes,
+                       static_cast<hipStream_t>(stream), StepEvents(),
+                       static_cast<hipStream_t>(side_stream), static_cast<hipEvent_t>(fork_event),
+                       static_cast<hipEvent_t>(join_event));
 }
 
 moe_status_t moe_layer_forward_noalloc(const moe_shape_t* s, const moe_weights_t* wt,

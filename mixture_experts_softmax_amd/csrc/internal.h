@@ -31,10 +31,12 @@ struct RoutePermute {
 // [ceil(T/64)][E]) get the permutation's per-tile expert masks and counts;
 // ignored when the permutation is fused (T <= kPermTile and fuse != nullptr).
 size_t route_ws_bytes(int T, int d, int E);
+// after_logits (optional): recorded on s between the logits launch (which
+// writes xq and x_scale) and the selection launch.
 hipError_t launch_route(bool bf16, const void* x, const void* w_router, const float* bias, int T,
                         int d, int E, int k, int32_t* ids, float* w, uint8_t* xq, float* x_scale,
                         void* ws, uint64_t* masks, int32_t* counts, const RoutePermute* fuse,
-                        hipStream_t s);
+                        hipStream_t s, hipEvent_t after_logits = nullptr);
 
 // ----- permutation ----------------------------------------------------------
 size_t perm_masks_bytes(int T, int E);

@@ -747,7 +747,7 @@ size_t route_ws_bytes(int T, int d, int E) {
 hipError_t launch_route(bool bf16, const void* x, const void* w_router, const float* bias, int T,
                         int d, int E, int k, int32_t* ids, float* w, uint8_t* xq, float* x_scale,
                         void* ws, uint64_t* masks, int32_t* counts, const RoutePermute* fuse,
-                        hipStream_t s) {
+                        hipStream_t s, hipEvent_t after_logits) {
   float* part = static_cast<float*>(ws);
   int ks = 1;
   if (bf16) {
@@ -782,6 +782,10 @@ hipError_t launch_route(bool bf16, const void* x, const void* w_router, const fl
     hipLaunchKernelGGL(route_logits_f32_kernel, dim3(ceil_div(T, kLogitWaves)),
                        dim3(kLogitWaves * kWave), 0, s, static_cast<const float*>(x),
                        static_cast<const float*>(w_router), T, d, E, part);
+  }
+  if (after_logits != nullptr) {  // x codes and scales are written: the caller may fork
+    const hipError_t e = hipEventRecord(after_logits, s);
+    if (e != hipSuccess) return e;
   }
   // fused: one workgroup of 16 waves; otherwise 16-token workgroups, four
   // per 64-token tile (past T too, so every byte of the masks is written)

@@ -247,6 +247,25 @@ def test_noalloc_rejects_before_touching_the_device():
     assert "scratch" in _lib.status_string(_lib.MOE_ERR_SCRATCH)
 
 
+def test_overlap_argument_checks():
+    """The second-stream layer call needs its own side stream and two distinct
+    events; all checks happen before anything is enqueued."""
+    L = _lib.lib()
+    A = 1 << 40  # a well-aligned stand-in address; never dereferenced
+    fake = C.c_void_p(A)
+    w = _lib.MoeWeights(A, None, A, A, A, A, A, A, A, A)
+    s = fp8_shape()
+    need = _lib.moe_layer_workspace_size(s)
+    st, side, e1, e2 = C.c_void_p(A + 256), C.c_void_p(A + 512), C.c_void_p(A + 768), C.c_void_p(A + 1024)
+    f = L.moe_layer_forward_overlap
+    assert f(C.byref(s), C.byref(w), fake, fake, None, None, fake, need, st, None, e1, e2) == _lib.MOE_ERR_INVALID_ARG
+    assert f(C.byref(s), C.byref(w), fake, fake, None, None, fake, need, st, st, e1, e2) == _lib.MOE_ERR_INVALID_ARG
+    assert f(C.byref(s), C.byref(w), fake, fake, None, None, fake, need, st, side, None, e2) == _lib.MOE_ERR_INVALID_ARG
+    assert f(C.byref(s), C.byref(w), fake, fake, None, None, fake, need, st, side, e1, e1) == _lib.MOE_ERR_INVALID_ARG
+    assert f(C.byref(s), C.byref(w), fake, fake, None, None, fake, need - 1, st, side, e1, e2) == _lib.MOE_ERR_WORKSPACE
+    assert f(C.byref(s), None, fake, fake, None, None, fake, need, st, side, e1, e2) == _lib.MOE_ERR_INVALID_ARG
+
+
 def test_status_strings():
     assert _lib.status_string(0) == "ok"
     assert "workspace" in _lib.status_string(-3)
