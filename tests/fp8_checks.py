@@ -12,8 +12,9 @@ and h = silu(g) u can sit on the other side of an E4M3 rounding midpoint from
 the exact h; both codes are then valid quantisations of h.
 
 The kernel's h codes and block scales are checked against an error bound
-propagated from MFMA_EPS * sum_i |x_i w_i| (MFMA_EPS = 2^-15, ~3.7x the
-largest measured per-instruction error) through the scales and SwiGLU:
+propagated from MFMA_EPS * sum_i |x_i w_i| (MFMA_EPS = 2^-15, 2.7x the
+largest per-instruction error measured on layer-like operands by
+tests/test_gpu_mfma_accuracy.py) through the scales and SwiGLU:
 
   * every block scale lies within the bound of the oracle's amax/448;
   * every code's value lies between the codes of v - 2 dv and v + 2 dv, where
