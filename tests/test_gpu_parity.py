@@ -75,7 +75,8 @@ def test_route_topk(name):
 
 @pytest.mark.parametrize("T,E,k", [(1, 4, 2), (64, 16, 4), (65, 8, 8), (130, 128, 6),
                                    (1000, 32, 1), (4096, 128, 8), (333, 256, 16),
-                                   (8200, 128, 6), (2000, 12, 3)])
+                                   (8200, 128, 6), (2000, 12, 3), (5000, 32, 16),
+                                   (256, 64, 16), (257, 64, 16)])
 def test_permute(T, E, k):
     rng = np.random.default_rng(T * 1000 + E)
     ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
