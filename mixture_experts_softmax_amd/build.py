@@ -22,7 +22,7 @@ ARCH = "gfx950"
 
 SOURCES = ["api.hip", "route.hip", "permute.hip", "ffn.hip", "combine.hip", "qk_rope.hip"]
 # test-only device probes (tests/probes/<name>.hip -> tests/probes/lib<name>.so)
-PROBES = ["mfma_fp8_probe"]
+PROBES = ["mfma_fp8_probe", "stream_probe"]
 PROBE_DIR = os.path.join(ROOT, "tests", "probes")
 
 FLAGS = [
