@@ -463,7 +463,26 @@ def time_qk(cfg, steps, warmup, hip, copies=8):
     el = 2 if cfg.precision == "bf16" else 4
     alg = 2 * cfg.T * (cfg.n_q + cfg.n_kv) * cfg.head_dim * el + 4 * cfg.T + 2 * cfg.head_dim * el
     mean_us = float(us.mean())
-    del bufs, qt
+    del bufs
+    # reference: torch's elementwise in-place multiply over contiguous buffers
+    # of the query and key heads' size, timed the same way (copies in turn,
+    # an event between calls) -- a plain read-modify-write pass over the same
+    # bytes, the practical floor for this traffic at this size
+    nel = cfg.T * (cfg.n_q + cfg.n_kv) * cfg.head_dim
+    refs = [torch.ones(nel, dtype=qt.qkv.dtype, device="cuda") for _ in range(copies)]
+    for i in range(warmup):
+        refs[i % copies].mul_(1.0)
+    torch.cuda.synchronize()
+    ev = [hip.event() for _ in range(steps + 1)]
+    for i in range(steps):
+        hip.L.hipEventRecord(C.c_void_p(ev[i]), sp)
+        refs[i % copies].mul_(1.0)
+    hip.L.hipEventRecord(C.c_void_p(ev[steps]), sp)
+    torch.cuda.synchronize()
+    ref_us = float(np.mean([hip.ms(ev[i], ev[i + 1]) * 1e3 for i in range(steps)]))
+    for e in ev:
+        hip.destroy(e)
+    del refs, qt
     torch.cuda.empty_cache()
     return {"workload": f"{cfg.name}: T={cfg.T} heads {cfg.n_q}+{cfg.n_kv} x {cfg.head_dim} "
                         f"{cfg.precision} {cfg.style}, in place",
@@ -473,7 +492,8 @@ def time_qk(cfg, steps, warmup, hip, copies=8):
                         "p90": round(float(np.percentile(us, 90)), 2), "calls": steps},
             "alg_bytes": alg, "GBs": round(alg / (mean_us / 1e6) / 1e9, 1),
             "hbm_frac": round(alg / (mean_us / 1e6) / 1e9 / HBM_PEAK_GBS, 4),
-            "tokens_per_s": round(cfg.T / (mean_us / 1e6), 1)}
+            "tokens_per_s": round(cfg.T / (mean_us / 1e6), 1),
+            "inplace_reference_us": round(ref_us, 2)}
 
 
 def hbm_copy_probe():
