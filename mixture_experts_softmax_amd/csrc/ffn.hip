@@ -575,14 +575,16 @@ __device__ inline void gateup_epilogue_t(v4f (&acc)[MS][2 * NS], const float* sx
 }
 
 // ---------------------------------------------------------------------------
-// Gate/up GEMM for tall tiles (prefill): both operands staged through LDS, so
-// each weight byte is fetched once per workgroup (the two M halves share it).
+// Gate/up GEMM for tall tiles (prefill) with MXFP4 weights (FP8 tall tiles
+// take the ping-pong kernel below): both operands staged through LDS, so each
+// weight byte is fetched once per workgroup (the two M halves share it).
 // Tile BM x 128 h columns (256 weight rows), 8 waves, wave (wm, wn) owns rows
 // [wm BM/2, (wm + 1) BM/2) and h columns [32 wn, 32 wn + 32). Each K step's
 // operands are loaded into registers two steps ahead and written into one of
-// two LDS stages a step ahead (staging through registers measured 5% faster
-// than direct global->LDS loads with a 3-stage weight ring, in less LDS).
-// The K loop is fully unrolled, so the compiler's wait counts are exact.
+// two LDS stages a step ahead (with all eight waves in one phase this
+// measured 5% faster than direct global->LDS loads with a 3-stage weight
+// ring, in less LDS). The K loop is fully unrolled, so the compiler's wait
+// counts are exact.
 //
 // A thread's 16-byte pieces land at (the piece's 1 KiB block) + 16 lane, 8
 // rows of 128 bytes per block; the swizzle is applied by choosing which
