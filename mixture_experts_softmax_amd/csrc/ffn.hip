@@ -507,89 +507,12 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void gateup_fp8_kernel(
   gateup_epilogue<BM, MS, NS>(acc, sxl, red, sg, su, rbase, wn, lane, te, S, ntile);
 }
 
-// Gate/up epilogue for the transposed product (weights as the MFMA A operand):
-// lane l holds, for tile row rbase + 16 i + l % 16, the four consecutive h
-// columns 16 jj + 4 (l / 16) + q of the wave's 16 NS (gate in acc[i][jj], up in
-// acc[i][NS + jj]). SwiGLU, the row's block amax over the 128 h columns of the
-// tile (the four lanes of a row, then the waves through LDS), its scale
-// amax / 448, and the four E4M3 codes packed into one 32-bit store. The codes
-// come from the packed float32 -> FP8 conversion, which rounds to nearest even
-// and saturates exactly as e4m3_encode does for quotients of magnitude <= 448.
-// `s13` holds the tile's channel scales, gate rows then up rows (FP8 weights).
-template <int BM, int MS, int NS, bool W4>
-__device__ inline void gateup_epilogue_t(v4f (&acc)[MS][2 * NS], const float* sxl,
-                                         float (&red)[kNWaves][BM], const float* s13,
-                                         int rbase, int wn, int lane, const Tile& te,
-                                         const SetView& S, int ntile) {
-  constexpr int WN = NS * 16;
-  const int F = S.F;
-  const int c0 = wn * WN + 4 * (lane >> 4);  // tile h column of (jj, q) = (0, 0)
-#pragma unroll
-  for (int i = 0; i < MS; ++i) {
-    const int r = rbase + i * 16 + (lane & 15);
-    const float sx = sxl[r];
-    float m = 0.f;
-#pragma unroll
-    for (int jj = 0; jj < NS; ++jj) {
-      v4f sg = v4f{1.f, 1.f, 1.f, 1.f}, su = sg;
-      if constexpr (!W4) {
-        sg = *reinterpret_cast<const v4f*>(&s13[c0 + 16 * jj]);
-        su = *reinterpret_cast<const v4f*>(&s13[kHN + c0 + 16 * jj]);
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float gv = acc[i][jj][q] * sx * sg[q];
-        const float uv = acc[i][NS + jj][q] * sx * su[q];
-        const float h = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
-        acc[i][jj][q] = h;
-        m = fmaxf(m, fabsf(h));
-      }
-    }
-    m = fmaxf(m, __shfl_xor(m, 16, kWave));
-    m = fmaxf(m, __shfl_xor(m, 32, kWave));
-    if (lane < 16) red[wn][r] = m;
-  }
-  __syncthreads();
-  const int hblocks = F / kHN;
-#pragma unroll
-  for (int i = 0; i < MS; ++i) {
-    const int r = rbase + i * 16 + (lane & 15);
-    if (r >= te.nrows) continue;
-    float am = red[0][r];
-#pragma unroll
-    for (int ww = 1; ww < kNWaves; ++ww) am = fmaxf(am, red[ww][r]);
-    const float s = (am > 0.f) ? __fdiv_rn(am, kE4M3Max) : 1.0f;
-    const float rs = __builtin_amdgcn_rcpf(s);
-    const size_t grow = (size_t)(te.row0 + r);
-    uint8_t* hrow = S.h + grow * F + ntile * kHN + c0;
-#pragma unroll
-    for (int jj = 0; jj < NS; ++jj) {
-      int w = __builtin_amdgcn_cvt_pk_fp8_f32(div_by(acc[i][jj][0], s, rs),
-                                              div_by(acc[i][jj][1], s, rs), 0, false);
-      w = __builtin_amdgcn_cvt_pk_fp8_f32(div_by(acc[i][jj][2], s, rs),
-                                          div_by(acc[i][jj][3], s, rs), w, true);
-      *reinterpret_cast<int*>(hrow + 16 * jj) = w;
-    }
-    if (wn == 0 && lane < 16) S.h_scale[grow * hblocks + ntile] = s;
-  }
-}
 
-// ---------------------------------------------------------------------------
-// Gate/up GEMM for tall tiles (prefill) with MXFP4 weights (FP8 tall tiles
-// take the ping-pong kernel below): both operands staged through LDS, so each
-// weight byte is fetched once per workgroup (the two M halves share it).
-// Tile BM x 128 h columns (256 weight rows), 8 waves, wave (wm, wn) owns rows
-// [wm BM/2, (wm + 1) BM/2) and h columns [32 wn, 32 wn + 32). Each K step's
-// operands are loaded into registers two steps ahead and written into one of
-// two LDS stages a step ahead (with all eight waves in one phase this
-// measured 5% faster than direct global->LDS loads with a 3-stage weight
-// ring, in less LDS). The K loop is fully unrolled, so the compiler's wait
-// counts are exact.
-//
-// A thread's 16-byte pieces land at (the piece's 1 KiB block) + 16 lane, 8
-// rows of 128 bytes per block; the swizzle is applied by choosing which
-// global chunk each lane fetches.
-// ---------------------------------------------------------------------------
+
+// Direct-to-LDS load of 16 bytes per lane (global_load_lds_dwordx4): a wave's
+// 64 pieces land at lds_base + 16 lane. The tall-tile kernels stage tiles
+// this way: a thread's piece lands at (the piece's 1 KiB block) + 16 lane, and
+// a swizzle is applied by choosing which global chunk each lane fetches.
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 __device__ inline void dma16(const uint8_t* src, uint8_t* lds_base) {
@@ -602,157 +525,6 @@ template <int N>
 __device__ inline void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt out of range");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-template <int BM, int KTC, bool W4>
-__global__ __launch_bounds__(8 * kWave) void gateup_fp8_lds_kernel(
-    FfnCall c, const TileHeader* __restrict__ hdr, const TileEntry* __restrict__ list) {
-  constexpr int NW = 8, NTH = NW * kWave;
-  constexpr int BMW = BM / 2, MS = BMW / 16;
-  constexpr int NS = 2, NB = 2 * NS;
-  constexpr int BROWS = 2 * kHN;                     // weight rows per tile
-  constexpr int KB = kstep_bytes<W4>();              // weight bytes per row and K step
-  constexpr int NAD = BM * kBK / 1024 / NW;          // A loads per thread per step
-  constexpr int NBD = BROWS * KB / 1024 / NW;        // B loads per thread per step
-  static_assert(BM * kBK % (1024 * NW) == 0, "A tile must split into whole wave loads");
-  static_assert(!W4 || KTC % 4 == 0, "MXFP4 scales are held per row in K-step quads");
-
-  __shared__ __attribute__((aligned(1024))) uint8_t a0[BM * kBK];
-  __shared__ __attribute__((aligned(1024))) uint8_t a1[BM * kBK];
-  __shared__ __attribute__((aligned(1024))) uint8_t b0[BROWS * KB];
-  __shared__ __attribute__((aligned(1024))) uint8_t b1[BROWS * KB];
-  __shared__ int ssc[W4 ? BROWS * (KTC + 1) : 1];  // MXFP4 scale tile
-  __shared__ float sxl[BM];
-  __shared__ float red[kNWaves][BM];
-  __shared__ __attribute__((aligned(16))) float s13l[W4 ? 1 : BROWS];  // channel scales
-
-  Tile te;
-  if (!pick_tile<BM>(list, hdr->n_up, up_ntiles_max(c), te)) return;
-  const int ntile = te.ntile;
-  const int sid = te.gid >> 16, g = te.gid & 0xffff;
-  const SetView S = set_view(c, sid);
-  const int d = c.d, F = S.F;
-  if (ntile >= F / kHN) return;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int wm = wave / kNWaves, wn = wave % kNWaves;
-  const int rbase = wm * BMW;
-  const uint8_t* a = static_cast<const uint8_t*>(c.a);
-
-  // this thread's pieces of a K step: A piece i covers tile rows
-  // 8 (NAD wave + i) + lane / 8, B piece i weight-tile rows 8 (NBD wave + i) + lane / 8;
-  // a piece is 16 bytes, stored at (piece's 1 KiB block) + 16 lane, the swizzle
-  // applied by the choice of source chunk
-  const uint8_t* asrc[NAD];
-#pragma unroll
-  for (int i = 0; i < NAD; ++i) {
-    const int r = 8 * (NAD * wave + i) + (lane >> 3);
-    const int cch = (lane & 7) ^ (r & 7);
-    const int grow = te.row0 + min(r, te.nrows - 1);
-    const int src = min(max(S.row_src ? S.row_src[grow] / S.src_div : grow, 0), c.a_rows - 1);
-    asrc[i] = a + (size_t)src * d + cch * 16;
-  }
-  // weight rows: FP8 as the A tile (8 rows of 128 bytes per 1 KiB block);
-  // MXFP4 16 rows of 64 bytes per block, 16-byte chunk q of row r stored at
-  // chunk q ^ ((r / 4) % 4), so the 16 rows a fragment read touches cover all
-  // 16 chunk slots of 256 bytes
-  const size_t wrb = W4 ? d / 2 : d;
-  const uint8_t* w13 = S.w13 + (size_t)g * 2 * F * wrb;
-  auto wrow_of = [&](int rr) { return (rr < kHN) ? ntile * kHN + rr : F + ntile * kHN + (rr - kHN); };
-  const uint8_t* bsrc[NBD];
-#pragma unroll
-  for (int i = 0; i < NBD; ++i) {
-    if constexpr (W4) {
-      const int rr = 16 * (NBD * wave + i) + (lane >> 2);
-      const int cch = (lane & 3) ^ ((rr >> 2) & 3);
-      bsrc[i] = w13 + (size_t)wrow_of(rr) * wrb + cch * 16;
-    } else {
-      const int rr = 8 * (NBD * wave + i) + (lane >> 3);
-      const int cch = (lane & 7) ^ (rr & 7);
-      bsrc[i] = w13 + (size_t)wrow_of(rr) * wrb + cch * 16;
-    }
-  }
-  // MXFP4: the tile's E8M0 scales into LDS (published by the first barrier)
-  if constexpr (W4)
-    fill_scale_tile<KTC, BROWS, NTH>(
-        ssc, [&](int r) { return S.e13 + ((size_t)g * 2 * F + wrow_of(r)) * (d / 32); }, tid);
-  if (tid < BM) {
-    const int grow = te.row0 + min(tid, te.nrows - 1);
-    const int src = min(max(S.row_src ? S.row_src[grow] / S.src_div : grow, 0), c.a_rows - 1);
-    sxl[tid] = c.a_scale[src];
-  }
-  if constexpr (!W4) {
-    if (tid < BROWS) s13l[tid] = S.s13[(size_t)g * 2 * F + wrow_of(tid)];
-  }
-
-  v4i ra[2][NAD], rb[2][NBD];  // K steps in flight, two deep
-  auto ld = [&](int kt, int slot) {
-#pragma unroll
-    for (int i = 0; i < NAD; ++i) ra[slot][i] = *reinterpret_cast<const v4i*>(asrc[i] + kt * kBK);
-#pragma unroll
-    for (int i = 0; i < NBD; ++i) rb[slot][i] = *reinterpret_cast<const v4i*>(bsrc[i] + kt * KB);
-  };
-  auto st = [&](int slot, uint8_t* ad, uint8_t* bd) {
-#pragma unroll
-    for (int i = 0; i < NAD; ++i)
-      *reinterpret_cast<v4i*>(ad + (NAD * wave + i) * 1024 + lane * 16) = ra[slot][i];
-#pragma unroll
-    for (int i = 0; i < NBD; ++i)
-      *reinterpret_cast<v4i*>(bd + (NBD * wave + i) * 1024 + lane * 16) = rb[slot][i];
-  };
-
-  v4f acc[MS][NB];
-#pragma unroll
-  for (int i = 0; i < MS; ++i)
-#pragma unroll
-    for (int j = 0; j < NB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  // step kt's operands are loaded into registers at the end of step kt-3 and
-  // stored into LDS stage kt % 2 at the end of step kt-1 (that stage's
-  // readers finished at the barrier ending step kt-2)
-  ld(0, 0);
-  ld(min(1, KTC - 1), 1);
-  st(0, a0, b0);
-  ld(min(2, KTC - 1), 0);
-  __syncthreads();
-#pragma unroll
-  for (int kt = 0; kt < KTC; ++kt) {
-    uint8_t* as = (kt % 2 == 0) ? a0 : a1;
-    uint8_t* bs = (kt % 2 == 0) ? b0 : b1;
-    BFrag<W4> bf[NB];
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int row0 = (j < NS) ? wn * 32 + j * 16 : kHN + wn * 32 + (j - NS) * 16;
-      if constexpr (W4) {
-        const int r = row0 + (lane & 15);
-        bf[j].w = *reinterpret_cast<const v4i*>(bs + r * KB + (((lane >> 4) ^ ((r >> 2) & 3)) << 4));
-        bf[j].s = scale_from_tile<KTC>(ssc, r, kt, lane);
-      } else {
-        bf[j] = lds_afrag(bs + row0 * kBK, 0, lane);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < MS; ++i) {
-      const v8i af = lds_afrag(as + rbase * kBK, i, lane);
-#pragma unroll
-      for (int j = 0; j < NB; ++j) acc[i][j] = mfma_wt(bf[j], af, acc[i][j]);
-    }
-    if constexpr (W4) {
-      // keep the step's block-scaled MFMAs in the step (left free, the
-      // scheduler defers them and runs out of registers)
-#pragma unroll
-      for (int i = 0; i < MS; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j) asm volatile("" : "+v"(acc[i][j]));
-    }
-    if (kt + 1 < KTC) {
-      st((kt + 1) % 2, (kt % 2 == 0) ? a1 : a0, (kt % 2 == 0) ? b1 : b0);
-      ld(min(kt + 3, KTC - 1), (kt + 1) % 2);
-    }
-    __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  __syncthreads();
-  gateup_epilogue_t<BM, MS, NS, W4>(acc, sxl, red, s13l, rbase, wn, lane, te, S, ntile);
 }
 
 // Workgroup barrier for LDS written by ordinary stores: waits for this wave's
@@ -802,9 +574,17 @@ __host__ __device__ constexpr int pp_after_b(int kt, int D, int KT, int NA, int 
   return pro + NA * pp_count_below(j0, kt, KT - 2) + NB * pp_count_below(j0, kt, KT - D);
 }
 
-// Gate/up epilogue of the ping-pong kernel: gateup_epilogue_t with the scales
-// read through accessors: sx(i) the x scale of row rbase + 16 i + lane % 16,
-// sg(jj) / su(jj) the channel scales of gate / up columns c0 + 16 jj .. + 3.
+// Gate/up epilogue for the transposed product (weights as the MFMA A operand):
+// lane l holds, for tile row rbase + 16 i + l % 16, the four consecutive h
+// columns 16 jj + 4 (l / 16) + q of the wave's 16 NS (gate in acc[i][jj], up in
+// acc[i][NS + jj]). SwiGLU, the row's block amax over the 128 h columns of the
+// tile (the four lanes of a row, then the waves through LDS), its scale
+// amax / 448, and the four E4M3 codes packed into one 32-bit store. The codes
+// come from the packed float32 -> FP8 conversion, which rounds to nearest even
+// and saturates exactly as e4m3_encode does for quotients of magnitude <= 448.
+// The scales are read through accessors: sx(i) the x scale of row rbase +
+// 16 i + lane % 16, sg(jj) / su(jj) the channel scales of gate / up columns
+// c0 + 16 jj .. + 3 (ones for MXFP4 weights, which have none).
 template <int BM, int MS, int NS, class SX, class SG, class SU>
 __device__ inline void gateup_epilogue_pp(v4f (&acc)[MS][2 * NS], SX sx, SG sg, SU su,
                                           float (*red)[BM], int rbase, int wn, int lane,
@@ -859,7 +639,8 @@ __device__ inline void gateup_epilogue_pp(v4f (&acc)[MS][2 * NS], SX sx, SG sg, 
 }
 
 // ---------------------------------------------------------------------------
-// Gate/up GEMM for tall tiles (prefill), FP8 weights, ping-pong schedule.
+// Gate/up GEMM for tall tiles (prefill), FP8 or MXFP4 weights (W4), ping-pong
+// schedule.
 // Tile BM rows x 128 h columns (256 weight rows: 128 gate, 128 up), 8 waves in
 // two groups of four: group g owns rows [g BM/2, (g + 1) BM/2), wave wn of a
 // group h columns [32 wn, 32 wn + 32). Each SIMD runs one wave of each group.
@@ -873,7 +654,9 @@ __device__ inline void gateup_epilogue_pp(v4f (&acc)[MS][2 * NS], SX sx, SG sg, 
 // Operand staging: activation rows (gathered through the permutation) are
 // loaded into registers two steps ahead and written into one of two LDS
 // stages a step ahead; weight rows go straight from global memory into one of
-// NBS LDS stages D = NBS - 1 steps ahead (direct-to-LDS loads). Phase by phase
+// NBS LDS stages D = NBS - 1 steps ahead (direct-to-LDS loads; MXFP4 rows of
+// 64 bytes per K step, 16 to a 1 KiB block, their E8M0 scales in an LDS tile
+// filled once per workgroup, one dword of padding per row). Phase by phase
 // the two groups' reads of a stage finish before either overwrites it:
 //   phase 2 kt:     group 0 LOAD(kt)    group 1 COMPUTE(kt - 1)
 //   phase 2 kt + 1: group 0 COMPUTE(kt) group 1 LOAD(kt)
@@ -884,32 +667,37 @@ __device__ inline void gateup_epilogue_pp(v4f (&acc)[MS][2 * NS], SX sx, SG sg, 
 // read. The K loop is fully unrolled, so every wait count is exact. After the
 // loop the A stages hold the epilogue's row maxima.
 // ---------------------------------------------------------------------------
-template <int BM, int KTC, int NBS>
+template <int BM, int KTC, int NBS, bool W4>
 __global__ __launch_bounds__(8 * kWave) void gateup_fp8_pp_kernel(
     FfnCall c, const TileHeader* __restrict__ hdr, const TileEntry* __restrict__ list) {
   constexpr int NW = 8;
   constexpr int BMW = BM / 2, MS = BMW / 16;
   constexpr int NS = 2, NB = 2 * NS;
   constexpr int BROWS = 2 * kHN;                 // weight rows per tile
+  constexpr int KB = kstep_bytes<W4>();          // weight bytes per row and K step
   constexpr int NAD = BM * kBK / 1024 / NW;      // A pieces (16 B) per thread per step
-  constexpr int NBD = BROWS * kBK / 1024 / NW;   // B pieces per thread per step
+  constexpr int NBD = BROWS * KB / 1024 / NW;    // B pieces per thread per step
   constexpr int D = NBS - 1;                     // weight steps loaded ahead
+  constexpr int SSC = W4 ? BROWS * (KTC + 1) : 1;  // MXFP4 scale tile (dwords)
   static_assert(BM * kBK % (1024 * NW) == 0, "A tile must split into whole wave loads");
   static_assert(KTC >= NBS, "the pipeline holds NBS K steps");
   static_assert(NBS >= 3 && NBS <= 4, "three or four weight stages");
   static_assert(kNWaves * BM * 4 <= BM * kBK, "row maxima fit in an A stage");
+  static_assert(!W4 || KTC % 4 == 0, "MXFP4 scales are held per row in K-step quads");
   // the x and channel scales stay in LDS when it has room beside the stages,
   // else in registers
-  constexpr bool SCL = (2 * BM + NBS * BROWS) * kBK + (BM + BROWS) * 4 <= 163840;
+  constexpr bool SCL =
+      2 * BM * kBK + NBS * BROWS * KB + (W4 ? 4 * SSC : 0) + (BM + BROWS) * 4 <= 163840;
 
   __shared__ __attribute__((aligned(1024))) uint8_t a0[BM * kBK];
   __shared__ __attribute__((aligned(1024))) uint8_t a1[BM * kBK];
-  __shared__ __attribute__((aligned(1024))) uint8_t b0[BROWS * kBK];
-  __shared__ __attribute__((aligned(1024))) uint8_t b1[BROWS * kBK];
-  __shared__ __attribute__((aligned(1024))) uint8_t b2[BROWS * kBK];
-  __shared__ __attribute__((aligned(1024))) uint8_t b3[NBS > 3 ? BROWS * kBK : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t b0[BROWS * KB];
+  __shared__ __attribute__((aligned(1024))) uint8_t b1[BROWS * KB];
+  __shared__ __attribute__((aligned(1024))) uint8_t b2[BROWS * KB];
+  __shared__ __attribute__((aligned(1024))) uint8_t b3[NBS > 3 ? BROWS * KB : 16];
+  __shared__ int ssc[SSC];
   __shared__ float sxl[SCL ? BM : 1];
-  __shared__ __attribute__((aligned(16))) float s13l[SCL ? BROWS : 1];
+  __shared__ __attribute__((aligned(16))) float s13l[(SCL && !W4) ? BROWS : 1];
 
   Tile te;
   if (!pick_tile<BM>(list, hdr->n_up, up_ntiles_max(c), te)) return;
@@ -937,32 +725,50 @@ __global__ __launch_bounds__(8 * kWave) void gateup_fp8_pp_kernel(
     const int cch = (lane & 7) ^ (r & 7);
     asrc[i] = a + (size_t)src_row(r) * d + cch * 16;
   }
-  // B piece i: weight-tile row 8 (NBD wave + i) + lane / 8 (rows 0..127 gate,
-  // 128..255 up), the same layout
-  const uint8_t* w13 = S.w13 + (size_t)g * 2 * F * d;
+  // B piece i (rows 0..127 gate, 128..255 up): FP8 weight-tile row
+  // 8 (NBD wave + i) + lane / 8, the same layout; MXFP4 16 rows of 64 bytes
+  // per 1 KiB block, row 16 (NBD wave + i) + lane / 4, its 16-byte chunk q
+  // stored at chunk q ^ ((row / 4) % 4), so the 16 rows a fragment read
+  // touches cover all 16 chunk slots of 256 bytes
+  const size_t wrb = W4 ? d / 2 : d;  // weight bytes per row
+  const uint8_t* w13 = S.w13 + (size_t)g * 2 * F * wrb;
   auto wrow_of = [&](int rr) { return (rr < kHN) ? ntile * kHN + rr : F + ntile * kHN + (rr - kHN); };
   const uint8_t* bsrc[NBD];
 #pragma unroll
   for (int i = 0; i < NBD; ++i) {
-    const int rr = 8 * (NBD * wave + i) + (lane >> 3);
-    const int cch = (lane & 7) ^ (rr & 7);
-    bsrc[i] = w13 + (size_t)wrow_of(rr) * d + cch * 16;
+    if constexpr (W4) {
+      const int rr = 16 * (NBD * wave + i) + (lane >> 2);
+      const int cch = (lane & 3) ^ ((rr >> 2) & 3);
+      bsrc[i] = w13 + (size_t)wrow_of(rr) * wrb + cch * 16;
+    } else {
+      const int rr = 8 * (NBD * wave + i) + (lane >> 3);
+      const int cch = (lane & 7) ^ (rr & 7);
+      bsrc[i] = w13 + (size_t)wrow_of(rr) * wrb + cch * 16;
+    }
   }
-  // the epilogue's x scales and channel scales, loaded now
-  const float* s13 = S.s13 + (size_t)g * 2 * F;
+  // MXFP4: the tile's E8M0 scales into LDS (published by the prologue's barrier)
+  if constexpr (W4)
+    fill_scale_tile<KTC, BROWS, 8 * kWave>(
+        ssc, [&](int r) { return S.e13 + ((size_t)g * 2 * F + wrow_of(r)) * (d / 32); }, tid);
+  // the epilogue's x scales and channel scales (FP8), loaded now
+  const float* s13 = W4 ? nullptr : S.s13 + (size_t)g * 2 * F;
   float sxr[SCL ? 1 : MS];
-  v4f sgr[SCL ? 1 : NS], sur[SCL ? 1 : NS];
+  v4f sgr[(SCL || W4) ? 1 : NS], sur[(SCL || W4) ? 1 : NS];
   if constexpr (SCL) {
     if (tid < BM) sxl[tid] = c.a_scale[src_row(tid)];
-    if (tid < BROWS) s13l[tid] = s13[wrow_of(tid)];
+    if constexpr (!W4) {
+      if (tid < BROWS) s13l[tid] = s13[wrow_of(tid)];
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < MS; ++i) sxr[i] = c.a_scale[src_row(rbase + i * 16 + (lane & 15))];
-    const float* sc = s13 + ntile * kHN + wn * 32 + 4 * (lane >> 4);
+    if constexpr (!W4) {
+      const float* sc = s13 + ntile * kHN + wn * 32 + 4 * (lane >> 4);
 #pragma unroll
-    for (int jj = 0; jj < NS; ++jj) {
-      sgr[jj] = *reinterpret_cast<const v4f*>(sc + 16 * jj);
-      sur[jj] = *reinterpret_cast<const v4f*>(sc + F + 16 * jj);
+      for (int jj = 0; jj < NS; ++jj) {
+        sgr[jj] = *reinterpret_cast<const v4f*>(sc + 16 * jj);
+        sur[jj] = *reinterpret_cast<const v4f*>(sc + F + 16 * jj);
+      }
     }
   }
 
@@ -978,7 +784,7 @@ __global__ __launch_bounds__(8 * kWave) void gateup_fp8_pp_kernel(
   };
   auto ldb = [&](int kt, uint8_t* bd) {
 #pragma unroll
-    for (int i = 0; i < NBD; ++i) dma16(bsrc[i] + kt * kBK, bd + (NBD * wave + i) * 1024);
+    for (int i = 0; i < NBD; ++i) dma16(bsrc[i] + kt * KB, bd + (NBD * wave + i) * 1024);
   };
   auto astage = [&](int kt) { return (kt & 1) ? a1 : a0; };
   auto bstage = [&](int kt) {
@@ -1013,14 +819,21 @@ __global__ __launch_bounds__(8 * kWave) void gateup_fp8_pp_kernel(
       wait_vmcnt<pp_after_a(kt, D, KTC, NBD)>();  // A(kt + 1) in registers
       sta((kt + 1) & 1, astage(kt + 1));
     }
-    v8i bf[NB], af[MS];
+    BFrag<W4> bf[NB];
+    v8i af[MS];
     {
       const uint8_t* bs = bstage(kt);
       const uint8_t* as = astage(kt);
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         const int row0 = (j < NS) ? wn * 32 + j * 16 : kHN + wn * 32 + (j - NS) * 16;
-        bf[j] = lds_afrag(bs + row0 * kBK, 0, lane);
+        if constexpr (W4) {
+          const int r = row0 + (lane & 15);
+          bf[j].w = *reinterpret_cast<const v4i*>(bs + r * KB + (((lane >> 4) ^ ((r >> 2) & 3)) << 4));
+          bf[j].s = scale_from_tile<KTC>(ssc, r, kt, lane);
+        } else {
+          bf[j] = lds_afrag(bs + row0 * kBK, 0, lane);
+        }
       }
 #pragma unroll
       for (int i = 0; i < MS; ++i) af[i] = lds_afrag(as + rbase * kBK, i, lane);
@@ -1038,6 +851,14 @@ __global__ __launch_bounds__(8 * kWave) void gateup_fp8_pp_kernel(
     for (int i = 0; i < MS; ++i)
 #pragma unroll
       for (int j = 0; j < NB; ++j) acc[i][j] = mfma_wt(bf[j], af[i], acc[i][j]);
+    if constexpr (W4) {
+      // the block-scaled MFMAs stay in their phase (left free, the scheduler
+      // defers them and runs out of registers)
+#pragma unroll
+      for (int i = 0; i < MS; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) asm volatile("" : "+v"(acc[i][j]));
+    }
     if (grp == 0) wait_vmcnt<wb>();
     lds_barrier();
     __builtin_amdgcn_sched_barrier(0);
@@ -1045,24 +866,25 @@ __global__ __launch_bounds__(8 * kWave) void gateup_fp8_pp_kernel(
   if (grp == 0) __builtin_amdgcn_s_barrier();  // both groups aligned again
   wait_vmcnt<0>();
   float(*red)[BM] = reinterpret_cast<float(*)[BM]>(a0);
+  const v4f one = v4f{1.f, 1.f, 1.f, 1.f};  // MXFP4: no channel scales
   if constexpr (SCL) {
     const int c0 = wn * 32 + 4 * (lane >> 4);
     gateup_epilogue_pp<BM, MS, NS>(
         acc, [&](int i) { return sxl[rbase + i * 16 + (lane & 15)]; },
-        [&](int jj) { return *reinterpret_cast<const v4f*>(&s13l[c0 + 16 * jj]); },
-        [&](int jj) { return *reinterpret_cast<const v4f*>(&s13l[kHN + c0 + 16 * jj]); }, red,
-        rbase, wn, lane, te, S, ntile);
+        [&](int jj) { return W4 ? one : *reinterpret_cast<const v4f*>(&s13l[c0 + 16 * jj]); },
+        [&](int jj) { return W4 ? one : *reinterpret_cast<const v4f*>(&s13l[kHN + c0 + 16 * jj]); },
+        red, rbase, wn, lane, te, S, ntile);
   } else {
     gateup_epilogue_pp<BM, MS, NS>(
-        acc, [&](int i) { return sxr[i]; }, [&](int jj) { return sgr[jj]; },
-        [&](int jj) { return sur[jj]; }, red, rbase, wn, lane, te, S, ntile);
+        acc, [&](int i) { return sxr[i]; }, [&](int jj) { return W4 ? one : sgr[jj]; },
+        [&](int jj) { return W4 ? one : sur[jj]; }, red, rbase, wn, lane, te, S, ntile);
   }
 }
 
-// Weight stages of the ping-pong gate/up kernel for a tile height: four at
-// 128 rows (the LDS holds them), three at 192.
-template <int BM>
-constexpr int pp_weight_stages() { return BM <= 128 ? 4 : 3; }
+// Weight stages of the ping-pong gate/up kernel: four where the LDS holds them
+// (128 rows; MXFP4, whose stages are half the bytes), three at 192 rows of FP8.
+template <int BM, bool W4>
+constexpr int pp_weight_stages() { return (W4 || BM <= 128) ? 4 : 3; }
 
 // ---------------------------------------------------------------------------
 // Down GEMM with per-(row, 128-K block) h scales. Tile: BM rows x 256 output
@@ -1224,8 +1046,8 @@ __global__ __launch_bounds__(kNWaves * WM * kWave) void down_fp8_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Down GEMM for tall tiles (prefill): the LDS-staged structure of the gate/up
-// kernel above. Tile BM rows x 256 output channels, 8 waves, wave (wm, wn)
+// Down GEMM for tall tiles (prefill): LDS-staged like the gate/up kernel
+// above, with all eight waves in one phase. Tile BM rows x 256 output channels, 8 waves, wave (wm, wn)
 // owns rows [wm BM/2, (wm + 1) BM/2) and channels [64 wn, 64 wn + 64). h rows
 // (2 stages) and W2 rows (3 stages) arrive by direct loads; a workgroup runs
 // NTW consecutive N tiles as one continuous sequence of NTW x KT steps, so
@@ -1672,12 +1494,9 @@ hipError_t launch_gemms_bm(const FfnCall& c, TileHeader* hdr, TileEntry* up, Til
   constexpr int WU = waves_m<BM>(), WD = waves_m<BMD>();
   ev.mark(true, MOE_STEP_GATE_UP, s);
   if (cu > 0) {
-    if constexpr (KTU > 0 && BM >= 128 && !W4)  // tall tiles, FP8: ping-pong schedule
-      hipLaunchKernelGGL((gateup_fp8_pp_kernel<BM, KTU, pp_weight_stages<BM>()>), dim3((unsigned)cu), dim3(8 * kWave), 0,
-                         s, c, hdr, up);
-    else if constexpr (KTU > 0 && BM >= 128)  // tall tiles: both operands through LDS
-      hipLaunchKernelGGL((gateup_fp8_lds_kernel<BM, KTU, W4>), dim3((unsigned)cu), dim3(8 * kWave),
-                         0, s, c, hdr, up);
+    if constexpr (KTU > 0 && BM >= 128)  // tall tiles: ping-pong schedule
+      hipLaunchKernelGGL((gateup_fp8_pp_kernel<BM, KTU, pp_weight_stages<BM, W4>(), W4>),
+                         dim3((unsigned)cu), dim3(8 * kWave), 0, s, c, hdr, up);
     else  // (a fully unrolled K loop of tall tiles would spill: looped there)
       hipLaunchKernelGGL((gateup_fp8_kernel<BM, WU, (BM >= 128 ? 0 : KTU), W4>),
                          dim3((unsigned)cu), dim3(kNWaves * WU * kWave), 0, s, c, hdr, up);

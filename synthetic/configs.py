@@ -97,6 +97,7 @@ PARITY = {
     "mx_model_m16": LayerConfig("mx_model_m16", 48, 4096, 16, 4, 1024, 1024, "mxfp4", seed=33),
     "mx_model_m64": LayerConfig("mx_model_m64", 200, 4096, 8, 2, 1024, 1024, "mxfp4", seed=34),
     "mx_model_m192": LayerConfig("mx_model_m192", 380, 4096, 8, 4, 1024, 1024, "mxfp4", seed=35),
+    "mx_model_m128": LayerConfig("mx_model_m128", 400, 4096, 8, 2, 1024, 1024, "mxfp4", seed=39),
     "mx_model_m32": LayerConfig("mx_model_m32", 96, 4096, 16, 4, 1024, 1024, "mxfp4", seed=36),
     "mx_model_f2048": LayerConfig("mx_model_f2048", 400, 4096, 8, 2, 2048, 2048, "mxfp4", seed=37),
     "mx_tall_dpart": LayerConfig("mx_tall_dpart", 600, 640, 8, 2, 1024, 1024, "mxfp4", seed=38),

@@ -20,7 +20,8 @@ MODEL = ["fp8_model_m16", "fp8_model_m32", "fp8_model_m128", "fp8_model_m192", "
          "fp8_tall_dpart"]
 # MXFP4 expert weights: every kernel variant (tile heights 16 to 192, looped
 # and unrolled K loops, resident and looped down GEMMs)
-MX = ["mx_small", "mx_ragged", "mx_model_m16", "mx_model_m32", "mx_model_m64", "mx_model_m192",
+MX = ["mx_small", "mx_ragged", "mx_model_m16", "mx_model_m32", "mx_model_m64", "mx_model_m128",
+      "mx_model_m192",
       "mx_model_f2048", "mx_tall_dpart"]
 
 
