@@ -201,6 +201,7 @@ __device__ inline int scale_from_tile(const int* tile, int r, int kt, int lane) 
   return reinterpret_cast<const uint8_t*>(tile)[4 * (r * (KT + 1) + kt) + (lane >> 4)];
 }
 
+
 // E4M3 activations x E4M3 weights, or x MXFP4 weights (A scale 2^0, B scale
 // per lane from the fragment; the FP4 operand occupies the low 4 registers).
 __device__ inline v4f mfma_w(const v8i& a, const v8i& b, const v4f& c) {
@@ -728,8 +729,10 @@ __global__ __launch_bounds__(8 * kWave) void gateup_fp8_pp_kernel(
   // B piece i (rows 0..127 gate, 128..255 up): FP8 weight-tile row
   // 8 (NBD wave + i) + lane / 8, the same layout; MXFP4 16 rows of 64 bytes
   // per 1 KiB block, row 16 (NBD wave + i) + lane / 4, its 16-byte chunk q
-  // stored at chunk q ^ ((row / 4) % 4), so the 16 rows a fragment read
-  // touches cover all 16 chunk slots of 256 bytes
+  // stored at chunk q ^ ((row / 2) % 4): a 16-byte-per-lane LDS read is served
+  // 8 lanes at a time from a 128-byte bank window, and any 8 consecutive rows
+  // of a fragment read then fall in 8 different 16-byte slots of it (with
+  // q ^ ((row / 4) % 4) rows r and r + 2 shared a slot: 2-way bank conflicts)
   const size_t wrb = W4 ? d / 2 : d;  // weight bytes per row
   const uint8_t* w13 = S.w13 + (size_t)g * 2 * F * wrb;
   auto wrow_of = [&](int rr) { return (rr < kHN) ? ntile * kHN + rr : F + ntile * kHN + (rr - kHN); };
@@ -738,7 +741,7 @@ __global__ __launch_bounds__(8 * kWave) void gateup_fp8_pp_kernel(
   for (int i = 0; i < NBD; ++i) {
     if constexpr (W4) {
       const int rr = 16 * (NBD * wave + i) + (lane >> 2);
-      const int cch = (lane & 3) ^ ((rr >> 2) & 3);
+      const int cch = (lane & 3) ^ ((rr >> 1) & 3);
       bsrc[i] = w13 + (size_t)wrow_of(rr) * wrb + cch * 16;
     } else {
       const int rr = 8 * (NBD * wave + i) + (lane >> 3);
@@ -829,7 +832,7 @@ __global__ __launch_bounds__(8 * kWave) void gateup_fp8_pp_kernel(
         const int row0 = (j < NS) ? wn * 32 + j * 16 : kHN + wn * 32 + (j - NS) * 16;
         if constexpr (W4) {
           const int r = row0 + (lane & 15);
-          bf[j].w = *reinterpret_cast<const v4i*>(bs + r * KB + (((lane >> 4) ^ ((r >> 2) & 3)) << 4));
+          bf[j].w = *reinterpret_cast<const v4i*>(bs + r * KB + (((lane >> 4) ^ ((r >> 1) & 3)) << 4));
           bf[j].s = scale_from_tile<KTC>(ssc, r, kt, lane);
         } else {
           bf[j] = lds_afrag(bs + row0 * kBK, 0, lane);
@@ -1101,7 +1104,7 @@ __global__ __launch_bounds__(8 * kWave) void down_fp8_lds_kernel(
     asrc[i] = S.h + (size_t)(te.row0 + min(r, te.nrows - 1)) * F + cch * 16;
   }
   // B load i covers channel rows 8 (NBD wave + i) + lane / 8 of an N tile
-  // (MXFP4: 16 rows of 64 bytes, chunk q of row r stored at q ^ ((r / 4) % 4),
+  // (MXFP4: 16 rows of 64 bytes, chunk q of row r stored at q ^ ((r / 2) % 4),
   // as in the gate/up kernel); steps past the last N tile re-read its rows
   // (never used)
   const size_t wrb = W4 ? F / 2 : F;
@@ -1111,7 +1114,7 @@ __global__ __launch_bounds__(8 * kWave) void down_fp8_lds_kernel(
   // swizzle period
   constexpr int RPB = W4 ? 16 : 8;  // rows per 1 KiB block
   const int brow0 = RPB * NBD * wave + (W4 ? (lane >> 2) : (lane >> 3));
-  const int bcc = W4 ? ((lane & 3) ^ ((brow0 >> 2) & 3)) * 16 : ((lane & 7) ^ (brow0 & 7)) * 16;
+  const int bcc = W4 ? ((lane & 3) ^ ((brow0 >> 1) & 3)) * 16 : ((lane & 7) ^ (brow0 & 7)) * 16;
   auto load_a = [&](int st, uint8_t* dst) {
     const int kt = st % KTC;
 #pragma unroll
@@ -1197,7 +1200,7 @@ __global__ __launch_bounds__(8 * kWave) void down_fp8_lds_kernel(
     for (int j = 0; j < NB; ++j) {
       if constexpr (W4) {
         const int r = wn * 64 + j * 16 + (lane & 15);
-        bf[j].w = *reinterpret_cast<const v4i*>(bs + r * KB + (((lane >> 4) ^ ((r >> 2) & 3)) << 4));
+        bf[j].w = *reinterpret_cast<const v4i*>(bs + r * KB + (((lane >> 4) ^ ((r >> 1) & 3)) << 4));
         bf[j].s = scale_from_tile<KTC>(ssc, n * kDownBN + r, kt, lane);
       } else {
         bf[j] = lds_afrag(bs + (wn * 64 + j * 16) * kBK, 0, lane);
