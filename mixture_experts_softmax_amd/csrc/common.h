@@ -51,6 +51,15 @@ __device__ inline uint16_t f32_to_bf16(float f) {
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
+// Two float32 -> two bf16 in one dword (a low, b high) by gfx950's packed
+// conversion (v_cvt_pk_bf16_f32), which rounds to nearest even: the same
+// bits as f32_to_bf16 for finite inputs, in one instruction.
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // ---------------------------------------------------------------------------
 // Wave-level reductions (64 lanes).
 // ---------------------------------------------------------------------------

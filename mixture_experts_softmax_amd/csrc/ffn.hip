@@ -1096,12 +1096,14 @@ __global__ __launch_bounds__(8 * kWave) void down_fp8_lds_kernel(
   const int rbase = wm * BMW;
 
   // direct-load sources: A load i covers tile rows 8 (NAD wave + i) + lane / 8
-  const uint8_t* asrc[NAD];
+  // (a uniform tile base and 32-bit per-lane offsets: fewer vector registers)
+  const uint8_t* hbase = S.h + (size_t)te.row0 * F;
+  uint32_t aoff[NAD];
 #pragma unroll
   for (int i = 0; i < NAD; ++i) {
     const int r = 8 * (NAD * wave + i) + (lane >> 3);
     const int cch = (lane & 7) ^ (r & 7);
-    asrc[i] = S.h + (size_t)(te.row0 + min(r, te.nrows - 1)) * F + cch * 16;
+    aoff[i] = (uint32_t)min(r, te.nrows - 1) * (uint32_t)F + cch * 16;
   }
   // B load i covers channel rows 8 (NBD wave + i) + lane / 8 of an N tile
   // (MXFP4: 16 rows of 64 bytes, chunk q of row r stored at q ^ ((r / 2) % 4),
@@ -1118,7 +1120,7 @@ __global__ __launch_bounds__(8 * kWave) void down_fp8_lds_kernel(
   auto load_a = [&](int st, uint8_t* dst) {
     const int kt = st % KTC;
 #pragma unroll
-    for (int i = 0; i < NAD; ++i) dma16(asrc[i] + kt * kBK, dst + (NAD * wave + i) * 1024);
+    for (int i = 0; i < NAD; ++i) dma16(hbase + aoff[i] + kt * kBK, dst + (NAD * wave + i) * 1024);
   };
   auto load_b = [&](int st, uint8_t* dst) {
     const int n = min(st / KTC, dnt - 1 - nt0), kt = st % KTC;
@@ -1138,9 +1140,6 @@ __global__ __launch_bounds__(8 * kWave) void down_fp8_lds_kernel(
   }
   // the MFMAs take the weights as A, so lane l accumulates channels
   // 16 j + 4 (l / 16) + q of the wave's 64 for tile row 16 i + l % 16
-  auto mcol = [&](int n, int j) {
-    return (nt0 + n) * kDownBN + wn * (NB * 16) + j * 16 + 4 * (lane >> 4);
-  };
   if constexpr (!W4) {
     for (int e = tid; e < NTW * kDownBN; e += NTH)
       s2l[e] = S.s2[(size_t)g * d + min((nt0 + e / kDownBN) * kDownBN + e % kDownBN, d - 1)];
@@ -1169,7 +1168,7 @@ __global__ __launch_bounds__(8 * kWave) void down_fp8_lds_kernel(
 
   // output rows of this tile, written with buffer stores (masked lanes are
   // dropped by the range check, so each store is one instruction for vmcnt)
-  constexpr int NSTV = MS * NB;  // stores per wave per N tile
+  constexpr int NSTV = MS * NB / 2;  // stores per wave per N tile
   const __amdgpu_buffer_rsrc_t orsrc = buffer_rsrc(
       static_cast<uint16_t*>(S.out) + (size_t)te.row0 * d, te.nrows * d * 2);
   v4f acc[MS][NB];
@@ -1223,23 +1222,43 @@ __global__ __launch_bounds__(8 * kWave) void down_fp8_lds_kernel(
 #pragma unroll
       for (int j = 0; j < NB; ++j) asm volatile("" : "+v"(acc[i][j]));
     if (kt == KTC - 1 && nt0 + n < dnt) {  // this N tile is done: channel scale, bf16
+      // Lane l holds 4 channels of subtile j for its row; lanes l and l ^ 16
+      // (the same row, neighbouring channel quads) swap one subtile's quad of
+      // a pair (j0, j0 + 1), so each lane stores 8 consecutive channels: even
+      // lane groups those of j0, odd ones those of j0 + 1. A store then
+      // writes 16 rows x 64 contiguous bytes (instead of 32).
+      const bool ev = ((lane >> 4) & 1) == 0;
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int m = mcol(n, j);  // d is a multiple of 4: all four or none
-        v4f sc = v4f{1.f, 1.f, 1.f, 1.f};
-        if constexpr (!W4)
-          sc = *reinterpret_cast<const v4f*>(&s2l[n * kDownBN + wn * (NB * 16) + j * 16 +
-                                                  4 * (lane >> 4)]);
+      for (int j0 = 0; j0 < NB; j0 += 2) {
+        v4f sc0 = v4f{1.f, 1.f, 1.f, 1.f}, sc1 = sc0;
+        if constexpr (!W4) {
+          const float* sp = &s2l[n * kDownBN + wn * (NB * 16) + j0 * 16 + 4 * (lane >> 4)];
+          sc0 = *reinterpret_cast<const v4f*>(sp);
+          sc1 = *reinterpret_cast<const v4f*>(sp + 16);
+        }
+        // channel of the lane's first stored element: 16 (j0 or j0 + 1) +
+        // 8 (lane group / 2) of the wave's 64 in N tile n
+        const int m = (nt0 + n) * kDownBN + wn * (NB * 16) + (j0 + (ev ? 0 : 1)) * 16 +
+                      8 * (lane >> 5);  // d is a multiple of 128: all eight or none
 #pragma unroll
         for (int i = 0; i < MS; ++i) {
+          const v4f a0v = acc[i][j0], a1v = acc[i][j0 + 1];
+          const uint32_t p00 = pack_bf16x2(a0v[0] * sc0[0], a0v[1] * sc0[1]);
+          const uint32_t p01 = pack_bf16x2(a0v[2] * sc0[2], a0v[3] * sc0[3]);
+          const uint32_t p10 = pack_bf16x2(a1v[0] * sc1[0], a1v[1] * sc1[1]);
+          const uint32_t p11 = pack_bf16x2(a1v[2] * sc1[2], a1v[3] * sc1[3]);
+          // the quad the partner lane stores goes to it, the partner's quad
+          // this lane stores comes back: lane l ^ 16 by ds_swizzle in bitmask
+          // mode (and 0x1f, or 0, xor 0x10 within each 32 lanes; no address
+          // register, unlike a bpermute)
+          const uint32_t g0 = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(ev ? p10 : p00), 0x401F);
+          const uint32_t g1 = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(ev ? p11 : p01), 0x401F);
+          const __attribute__((ext_vector_type(4))) uint32_t v =
+              ev ? (__attribute__((ext_vector_type(4))) uint32_t){p00, p01, g0, g1}
+                 : (__attribute__((ext_vector_type(4))) uint32_t){g0, g1, p10, p11};
           const int r = rbase + i * 16 + (lane & 15);
-          const uint32_t lo = f32_to_bf16(acc[i][j][0] * sc[0]) |
-                              ((uint32_t)f32_to_bf16(acc[i][j][1] * sc[1]) << 16);
-          const uint32_t hi = f32_to_bf16(acc[i][j][2] * sc[2]) |
-                              ((uint32_t)f32_to_bf16(acc[i][j][3] * sc[3]) << 16);
           const int off = (r < te.nrows && m < d) ? (r * d + m) * 2 : -1;
-          __builtin_amdgcn_raw_buffer_store_b64(
-              (__attribute__((ext_vector_type(2))) uint32_t){lo, hi}, orsrc, off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, off, 0, 0);
         }
       }
     }
