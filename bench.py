@@ -685,7 +685,10 @@ def main():
     out["layer"]["kernels"] = summarize(cfg, r)["roofline"]
     if not args.no_secondary:
         # the other workloads, reported beside the headline (not part of `value`)
-        sec_steps, sec_warm = max(5, args.steps // 2), max(2, args.warmup // 2)
+        # at least 50 warm-up steps: after the seconds of input generation the
+        # first few hundred microseconds of GPU work run slower (prefill: 598 us
+        # per timed step after 5 warm-up steps, 546 after 50, 542 per call)
+        sec_steps, sec_warm = max(5, args.steps // 2), max(50, args.warmup)
         for name in ("prefill", "b100", "skew", "decode_mxfp4", "prefill_mxfp4"):
             if name == args.workload:
                 continue
