@@ -20,6 +20,7 @@
 
 #include "common.h"
 #include "internal.h"
+#include "pipeline.h"
 #include "tiles.h"
 
 namespace moe {
@@ -552,41 +553,18 @@ __device__ inline void static_for(Fn&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// Global loads of the ping-pong gate/up kernel, in issue order: the prologue
-// issues A(0), B(0) .. B(D - 2), A(1), B(D - 1); LOAD(j) issues A(j + 2) then
-// B(j + D), each only if that K step exists. A(s) is NA loads per thread, B(s)
-// NB. These count the loads issued after A(kt + 1) (at the start of LOAD(kt),
-// before its own loads), and after B(kt + 1) up to the end of LOAD(kt): the
-// vmcnt that waits for exactly that step's loads.
-__host__ __device__ constexpr int pp_count_below(int a, int b, int c) {
-  // #{j in [a, b] : j < c}
-  return (b < c - 1 ? b : c - 1) - a + 1 > 0 ? (b < c - 1 ? b : c - 1) - a + 1 : 0;
-}
-__host__ __device__ constexpr int pp_after_a(int kt, int D, int KT, int NB) {
-  return (kt - 1 + D < KT) ? NB : 0;  // only B(kt - 1 + D) follows A(kt + 1)
-}
-__host__ __device__ constexpr int pp_after_b(int kt, int D, int KT, int NA, int NB) {
-  const int s = kt + 1;
-  // loads of the prologue after B(s), when the prologue issued it
-  const int pro = (s >= D) ? 0 : (s <= D - 2) ? (D - 2 - s) * NB + NA + NB : 0;
-  // LOAD(j) for j in [j0, kt] follow B(s) entirely: A(j + 2) if j + 2 < KT,
-  // B(j + D) if j + D < KT
-  const int j0 = (s >= D) ? s - D + 1 : 0;
-  return pro + NA * pp_count_below(j0, kt, KT - 2) + NB * pp_count_below(j0, kt, KT - D);
-}
-
 // Gate/up epilogue for the transposed product (weights as the MFMA A operand):
 // lane l holds, for tile row rbase + 16 i + l % 16, the four consecutive h
 // columns 16 jj + 4 (l / 16) + q of the wave's 16 NS (gate in acc[i][jj], up in
 // acc[i][NS + jj]). SwiGLU, the row's block amax over the 128 h columns of the
-// tile (the four lanes of a row, then the waves through LDS), its scale
-// amax / 448, and the four E4M3 codes packed into one 32-bit store. The codes
+// tile (the four lanes of a row, then the NWN waves of the row through LDS),
+// its scale amax / 448, and the four E4M3 codes packed into one 32-bit store. The codes
 // come from the packed float32 -> FP8 conversion, which rounds to nearest even
 // and saturates exactly as e4m3_encode does for quotients of magnitude <= 448.
 // The scales are read through accessors: sx(i) the x scale of row rbase +
 // 16 i + lane % 16, sg(jj) / su(jj) the channel scales of gate / up columns
 // c0 + 16 jj .. + 3 (ones for MXFP4 weights, which have none).
-template <int BM, int MS, int NS, class SX, class SG, class SU>
+template <int BM, int MS, int NS, int NWN, class SX, class SG, class SU>
 __device__ inline void gateup_epilogue_pp(v4f (&acc)[MS][2 * NS], SX sx, SG sg, SU su,
                                           float (*red)[BM], int rbase, int wn, int lane,
                                           const Tile& te, const SetView& S, int ntile) {
@@ -622,7 +600,7 @@ __device__ inline void gateup_epilogue_pp(v4f (&acc)[MS][2 * NS], SX sx, SG sg, 
     if (r >= te.nrows) continue;
     float am = red[0][r];
 #pragma unroll
-    for (int ww = 1; ww < kNWaves; ++ww) am = fmaxf(am, red[ww][r]);
+    for (int ww = 1; ww < NWN; ++ww) am = fmaxf(am, red[ww][r]);
     const float s = (am > 0.f) ? __fdiv_rn(am, kE4M3Max) : 1.0f;
     const float rs = __builtin_amdgcn_rcpf(s);
     const size_t grow = (size_t)(te.row0 + r);
@@ -690,6 +668,10 @@ __global__ __launch_bounds__(8 * kWave) void gateup_fp8_pp_kernel(
   constexpr bool SCL =
       2 * BM * kBK + NBS * BROWS * KB + (W4 ? 4 * SSC : 0) + (BM + BROWS) * 4 <= 163840;
 
+  // one LDS variable per stage: the compiler tells distinct variables apart,
+  // so a read of one stage does not wait for the direct-to-LDS loads still in
+  // flight into the others (slices of one array it cannot separate, and it
+  // would drain every weight load before each LOAD phase)
   __shared__ __attribute__((aligned(1024))) uint8_t a0[BM * kBK];
   __shared__ __attribute__((aligned(1024))) uint8_t a1[BM * kBK];
   __shared__ __attribute__((aligned(1024))) uint8_t b0[BROWS * KB];
@@ -795,13 +777,18 @@ __global__ __launch_bounds__(8 * kWave) void gateup_fp8_pp_kernel(
     return m == 0 ? b0 : m == 1 ? b1 : m == 2 ? b2 : b3;
   };
 
-  // prologue: A(0), B(0) .. B(D - 2), A(1), B(D - 1); A(0) into its stage,
-  // B(0) landed (pp_after_a / pp_after_b count this order)
+  // prologue: A(0), B(0) .. B(D - 2), A(1), B(D - 1) (the order the wait
+  // counts of pipeline.h assume; scheduling barriers keep the compiler from
+  // reordering the groups); A(0) into its stage, B(0) landed
   lda(0, 0);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int s = 0; s + 1 < D; ++s) ldb(s, bstage(s));
+  __builtin_amdgcn_sched_barrier(0);
   lda(1, 1);
+  __builtin_amdgcn_sched_barrier(0);
   ldb(D - 1, bstage(D - 1));
+  __builtin_amdgcn_sched_barrier(0);
   wait_vmcnt<(D - 1) * NBD + NAD + NBD>();
   sta(0, a0);
   wait_vmcnt<(D - 2) * NBD + NAD + NBD>();
@@ -819,7 +806,7 @@ __global__ __launch_bounds__(8 * kWave) void gateup_fp8_pp_kernel(
     constexpr int kt = decltype(ktc)::value;
     // ---- LOAD(kt) ----
     if constexpr (kt + 1 < KTC) {
-      wait_vmcnt<pp_after_a(kt, D, KTC, NBD)>();  // A(kt + 1) in registers
+      wait_vmcnt<pp_after_a(kt, D, KTC, NAD, NBD)>();  // A(kt + 1) in registers
       sta((kt + 1) & 1, astage(kt + 1));
     }
     BFrag<W4> bf[NB];
@@ -842,6 +829,7 @@ __global__ __launch_bounds__(8 * kWave) void gateup_fp8_pp_kernel(
       for (int i = 0; i < MS; ++i) af[i] = lds_afrag(as + rbase * kBK, i, lane);
     }
     if constexpr (kt + 2 < KTC) lda(kt + 2, kt & 1);
+    __builtin_amdgcn_sched_barrier(0);  // A before B: the order the counts assume
     if constexpr (kt + D < KTC) ldb(kt + D, bstage(kt + D));
     // this wave's part of B(kt + 1) lands before the barrier ending phase
     // 2 kt + 1: group 1 waits here, group 0 after its COMPUTE(kt)
@@ -872,13 +860,13 @@ __global__ __launch_bounds__(8 * kWave) void gateup_fp8_pp_kernel(
   const v4f one = v4f{1.f, 1.f, 1.f, 1.f};  // MXFP4: no channel scales
   if constexpr (SCL) {
     const int c0 = wn * 32 + 4 * (lane >> 4);
-    gateup_epilogue_pp<BM, MS, NS>(
+    gateup_epilogue_pp<BM, MS, NS, kNWaves>(
         acc, [&](int i) { return sxl[rbase + i * 16 + (lane & 15)]; },
         [&](int jj) { return W4 ? one : *reinterpret_cast<const v4f*>(&s13l[c0 + 16 * jj]); },
         [&](int jj) { return W4 ? one : *reinterpret_cast<const v4f*>(&s13l[kHN + c0 + 16 * jj]); },
         red, rbase, wn, lane, te, S, ntile);
   } else {
-    gateup_epilogue_pp<BM, MS, NS>(
+    gateup_epilogue_pp<BM, MS, NS, kNWaves>(
         acc, [&](int i) { return sxr[i]; }, [&](int jj) { return W4 ? one : sgr[jj]; },
         [&](int jj) { return W4 ? one : sur[jj]; }, red, rbase, wn, lane, te, S, ntile);
   }
@@ -888,6 +876,305 @@ __global__ __launch_bounds__(8 * kWave) void gateup_fp8_pp_kernel(
 // (128 rows; MXFP4, whose stages are half the bytes), three at 192 rows of FP8.
 template <int BM, bool W4>
 constexpr int pp_weight_stages() { return (W4 || BM <= 128) ? 4 : 3; }
+
+// Side work of one K step of the four-wave gate/up kernel, one item per MFMA
+// slot (m = 0 .. NSLOT - 1). Global loads sit in every third slot -- A piece
+// p's LDS write in slot 3 p, its next load in 3 p + 1, then weight piece q in
+// 3 (NA + q) + 1 -- because the four waves reach the same slot together, and
+// bunched loads back up the CU's address queue, which stalls the loading
+// wave's MFMAs behind them. LDS fragment reads fill the other slots: B
+// fragment j (two reads) only after slot MS j + MS - 1, its last MFMA (except
+// the last fragment, whose registers alternate), A fragment halves anywhere.
+enum IwOp { kIwNone, kIwStA, kIwLdA, kIwLdB, kIwRdA, kIwRdB };
+template <int NSLOT>
+struct IwSlots {
+  int op[NSLOT];
+  int arg[NSLOT];
+};
+template <int NSLOT, int NA, int NB_LD, int MS, int NBF>
+constexpr IwSlots<NSLOT> iw_slots() {
+  IwSlots<NSLOT> t{};
+  for (int m = 0; m < NSLOT; ++m) t.op[m] = kIwNone, t.arg[m] = 0;
+  for (int p = 0; p < NA; ++p) {
+    t.op[3 * p] = kIwStA, t.arg[3 * p] = p;
+    t.op[3 * p + 1] = kIwLdA, t.arg[3 * p + 1] = p;
+  }
+  for (int q = 0; q < NB_LD; ++q) t.op[3 * (NA + q) + 1] = kIwLdB, t.arg[3 * (NA + q) + 1] = q;
+  // B fragment halves in order, each in the earliest free slot after its
+  // fragment's last MFMA (the last fragment: any free slot)
+  for (int f = 0; f < 2 * NBF; ++f) {
+    const int j = f / 2, lo = (j + 1 < NBF) ? MS * j + MS : 0;
+    for (int m = lo; m < NSLOT; ++m)
+      if (t.op[m] == kIwNone) {
+        t.op[m] = kIwRdB, t.arg[m] = f;
+        break;
+      }
+  }
+  for (int f = 0; f < 2 * MS; ++f)
+    for (int m = 0; m < NSLOT; ++m)
+      if (t.op[m] == kIwNone) {
+        t.op[m] = kIwRdA, t.arg[m] = f;
+        break;
+      }
+  return t;
+}
+template <int NSLOT, int NA, int NB_LD, int MS, int NBF>
+constexpr bool iw_slots_complete() {
+  constexpr IwSlots<NSLOT> t = iw_slots<NSLOT, NA, NB_LD, MS, NBF>();
+  int n[6] = {0, 0, 0, 0, 0, 0};
+  for (int m = 0; m < NSLOT; ++m) ++n[t.op[m]];
+  return 3 * (NA + NB_LD) <= NSLOT && n[kIwStA] == NA && n[kIwLdA] == NA && n[kIwLdB] == NB_LD &&
+         n[kIwRdA] == 2 * MS && n[kIwRdB] == 2 * NBF;
+}
+
+// ---------------------------------------------------------------------------
+// Gate/up GEMM for tall tiles, one wave per SIMD. Tile BM rows x 128 h
+// columns (256 weight rows), 4 waves: wave (wm, wn) owns rows
+// [wm BM/2, (wm + 1) BM/2) and h columns [64 wn, 64 wn + 64) (weight rows
+// [64 wn, +64) gate and 128 + [64 wn, +64) up). A wave's 96 x 128
+// accumulator tile (192 registers per lane) needs more registers than two
+// waves per SIMD leave each, and reads 7/10 of the LDS bytes per MFMA of the
+// ping-pong kernel's 96 x 64 tiles; the ping-pong kernel's K steps are bound
+// by their LDS reads, this one's by its MFMAs.
+//
+// Each wave overlaps its own LDS traffic with its MFMAs: while the MFMAs of
+// step kt run (B fragment by B fragment), it reads step kt + 1's fragments
+// (each B fragment's registers right after the last MFMA that uses them; the
+// A fragments into a second set), writes step kt + 2's activation rows into
+// the A stage step kt's rows left, and issues later steps' global loads.
+// One workgroup barrier per step, at its end: by then every wave has read
+// step kt + 1's fragments (so the stages of step kt + 1 may be overwritten
+// from step kt + 1 on), written A(kt + 2) and received its part of B(kt + 2)
+// (both read during step kt + 1).
+//
+// Operand staging: activation rows (gathered through the permutation) go
+// through registers, loaded two steps before they are written and written
+// two steps before their fragments are computed with (two A stages); weight
+// rows go straight into one of NBS LDS stages, NBS steps ahead (the stage of
+// step kt is free once its fragments are read, during step kt - 1). MXFP4:
+// the weights' E8M0 scales in an LDS tile filled once per workgroup.
+// ---------------------------------------------------------------------------
+template <int BM, int KTC, int NBS, bool W4>
+__global__ __launch_bounds__(4 * kWave) void gateup_fp8_iw_kernel(
+    FfnCall c, const TileHeader* __restrict__ hdr, const TileEntry* __restrict__ list) {
+  constexpr int NW = 4;
+  constexpr int BMW = BM / 2, MS = BMW / 16;
+  constexpr int NS = 4, NB = 2 * NS;             // gate and up fragments per wave
+  constexpr int BROWS = 2 * kHN;                 // weight rows per tile
+  constexpr int KB = kstep_bytes<W4>();          // weight bytes per row and K step
+  constexpr int NAD = BM * kBK / 1024 / NW;      // A pieces (16 B) per thread per step
+  constexpr int NBD = BROWS * KB / 1024 / NW;    // B pieces per thread per step
+  constexpr int D = NBS;                         // weight steps loaded ahead
+  constexpr int SSC = W4 ? BROWS * (KTC + 1) : 1;  // MXFP4 scale tile (dwords)
+  static_assert(BM * kBK % (1024 * NW) == 0, "A tile must split into whole wave loads");
+  static_assert(KTC >= D + 4, "the prologue loads four activation and D weight steps");
+  static_assert(NBS >= 3 && NBS <= 4, "three or four weight stages");
+  static_assert(2 * BM * 4 <= BM * kBK, "row maxima fit in an A stage");
+  static_assert(!W4 || KTC % 4 == 0, "MXFP4 scales are held per row in K-step quads");
+  static_assert(2 * BM * kBK + NBS * BROWS * KB + (W4 ? 4 * SSC : 0) + (BM + BROWS) * 4 <= 163840,
+                "stages and scales fit the LDS");
+
+  // one LDS variable per stage (the compiler then tells the stages apart and
+  // does not drain the direct-to-LDS loads before reading another stage)
+  __shared__ __attribute__((aligned(1024))) uint8_t a0[BM * kBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t a1[BM * kBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t b0[BROWS * KB];
+  __shared__ __attribute__((aligned(1024))) uint8_t b1[BROWS * KB];
+  __shared__ __attribute__((aligned(1024))) uint8_t b2[BROWS * KB];
+  __shared__ __attribute__((aligned(1024))) uint8_t b3[NBS > 3 ? BROWS * KB : 16];
+  __shared__ int ssc[SSC];
+  __shared__ float sxl[BM];
+  __shared__ __attribute__((aligned(16))) float s13l[W4 ? 1 : BROWS];
+
+  Tile te;
+  if (!pick_tile<BM>(list, hdr->n_up, up_ntiles_max(c), te)) return;
+  const int ntile = te.ntile;
+  const int sid = te.gid >> 16, g = te.gid & 0xffff;
+  const SetView S = set_view(c, sid);
+  const int d = c.d, F = S.F;
+  if (ntile >= F / kHN) return;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int rbase = wm * BMW;
+  auto src_row = [&](int r) {  // activation row of tile row r
+    const int grow = te.row0 + min(r, te.nrows - 1);
+    return min(max(S.row_src ? S.row_src[grow] / S.src_div : grow, 0), c.a_rows - 1);
+  };
+
+  // A piece i of this thread: tile row 8 (NAD wave + i) + lane / 8, stored at
+  // (its 1 KiB block) + 16 lane, the swizzle applied by the source chunk
+  // (32-bit offsets from the activation base)
+  const uint8_t* a = static_cast<const uint8_t*>(c.a);
+  uint32_t aoff[NAD];
+#pragma unroll
+  for (int i = 0; i < NAD; ++i) {
+    const int r = 8 * (NAD * wave + i) + (lane >> 3);
+    aoff[i] = (uint32_t)src_row(r) * (uint32_t)d + (((lane & 7) ^ (r & 7)) << 4);
+  }
+  // B piece i: FP8 weight-tile row 8 (NBD wave + i) + lane / 8 (rows 0..127
+  // gate, 128..255 up), chunks swizzled as the A tile's; MXFP4 rows of 64
+  // bytes, 16 to a block, row 16 (NBD wave + i) + lane / 4, its chunk q
+  // stored at q ^ ((row / 2) % 4) (conflict-free 16-byte fragment reads)
+  const size_t wrb = W4 ? d / 2 : d;  // weight bytes per row
+  const uint8_t* w13 = S.w13 + (size_t)g * 2 * F * wrb;
+  auto wrow_of = [&](int rr) { return (rr < kHN) ? ntile * kHN + rr : F + ntile * kHN + (rr - kHN); };
+  uint32_t boff[NBD];
+#pragma unroll
+  for (int i = 0; i < NBD; ++i) {
+    if constexpr (W4) {
+      const int rr = 16 * (NBD * wave + i) + (lane >> 2);
+      boff[i] = (uint32_t)wrow_of(rr) * (uint32_t)wrb + ((((lane & 3) ^ ((rr >> 1) & 3))) << 4);
+    } else {
+      const int rr = 8 * (NBD * wave + i) + (lane >> 3);
+      boff[i] = (uint32_t)wrow_of(rr) * (uint32_t)wrb + (((lane & 7) ^ (rr & 7)) << 4);
+    }
+  }
+  if constexpr (W4)
+    fill_scale_tile<KTC, BROWS, NW * kWave>(
+        ssc, [&](int r) { return S.e13 + ((size_t)g * 2 * F + wrow_of(r)) * (d / 32); }, tid);
+  if (tid < BM) sxl[tid] = c.a_scale[src_row(tid)];
+  if constexpr (!W4) {
+    const float* s13 = S.s13 + (size_t)g * 2 * F;
+    s13l[tid] = s13[wrow_of(tid)];  // 256 threads, 256 weight rows
+  }
+
+  v4i ra[2][NAD];  // activation rows, loaded two steps before they are written
+  auto lda = [&](int kt, int slot) {
+#pragma unroll
+    for (int i = 0; i < NAD; ++i) ra[slot][i] = *reinterpret_cast<const v4i*>(a + aoff[i] + kt * kBK);
+  };
+  auto sta = [&](int slot, uint8_t* ad) {
+#pragma unroll
+    for (int i = 0; i < NAD; ++i)
+      *reinterpret_cast<v4i*>(ad + (NAD * wave + i) * 1024 + lane * 16) = ra[slot][i];
+  };
+  auto ldb = [&](int kt, uint8_t* bd) {
+#pragma unroll
+    for (int i = 0; i < NBD; ++i) dma16(w13 + boff[i] + kt * KB, bd + (NBD * wave + i) * 1024);
+  };
+  auto astage = [&](int kt) { return (kt & 1) ? a1 : a0; };
+  auto bstage = [&](int kt) {
+    const int m = kt % NBS;
+    return m == 0 ? b0 : m == 1 ? b1 : m == 2 ? b2 : b3;
+  };
+  // Fragments are read in halves, one LDS instruction each: A fragment i of
+  // a stage is two 16-byte reads at rows rbase + 16 i + lane % 16; B fragment
+  // j (rows 0..63 of the wave's 128: gate, 64..127: up) two reads (FP8) or
+  // the codes and the scale byte (MXFP4).
+  auto brow0 = [&](int j) { return (j < NS) ? wn * 64 + j * 16 : kHN + wn * 64 + (j - NS) * 16; };
+  auto rda_half = [&](v8i& f, const uint8_t* as, int i, int h) {
+    const int r = rbase + i * 16 + (lane & 15);
+    const v4i v = *reinterpret_cast<const v4i*>(as + swz(r, 4 * h + (lane >> 4)));
+    if (h == 0) f.lo = v; else f.hi = v;
+  };
+  auto rdb_half = [&](BFrag<W4>& f, const uint8_t* bs, int j, int h, int kt) {
+    const int r = brow0(j) + (lane & 15);
+    if constexpr (W4) {
+      if (h == 0)
+        f.w = *reinterpret_cast<const v4i*>(bs + r * KB + (((lane >> 4) ^ ((r >> 1) & 3)) << 4));
+      else
+        f.s = scale_from_tile<KTC>(ssc, r, kt, lane);
+    } else {
+      const v4i v = *reinterpret_cast<const v4i*>(bs + swz(r, 4 * h + (lane >> 4)));
+      if (h == 0) f.lo = v; else f.hi = v;
+    }
+  };
+
+  // prologue: A(0), A(1), B(0) .. B(D - 1); A(0), A(1) into their stages;
+  // A(2), A(3); B(0) and B(1) landed (the order iw_after counts; scheduling
+  // barriers keep the compiler from reordering the groups)
+  lda(0, 0);
+  lda(1, 1);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int s = 0; s < D; ++s) ldb(s, bstage(s));
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vmcnt<D * NBD>();
+  sta(0, a0);
+  sta(1, a1);
+  __builtin_amdgcn_sched_barrier(0);
+  lda(2, 0);
+  lda(3, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vmcnt<iw_after(KTC, D, NAD, NBD, false, 1, 0)>();
+  lds_barrier();  // publishes A(0), A(1), B(0), B(1) and the scales
+
+  // B fragment NB - 1 is used by a step's last MFMA, so it alternates
+  // between two register sets; the others are re-read into their own
+  // registers after their step's last MFMA with them
+  BFrag<W4> bf[NB + 1];
+  v8i af[2][MS];
+  auto bslot = [&](int j, int kt) { return (j == NB - 1 && (kt & 1)) ? NB : j; };
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    rdb_half(bf[j], b0, j, 0, 0);
+    rdb_half(bf[j], b0, j, 1, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < MS; ++i) {
+    rda_half(af[0][i], a0, i, 0);
+    rda_half(af[0][i], a0, i, 1);
+  }
+  lds_barrier();  // every wave has read stage 0, which step 0 overwrites
+
+  v4f acc[MS][NB];
+#pragma unroll
+  for (int i = 0; i < MS; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  __builtin_amdgcn_sched_barrier(0);
+
+  constexpr int NSLOT = NB * MS;  // MFMAs per step
+  static_assert(iw_slots_complete<NSLOT, NAD, NBD, MS, NB>(), "a step's side work fits its slots");
+  constexpr IwSlots<NSLOT> slots = iw_slots<NSLOT, NAD, NBD, MS, NB>();
+
+  static_for<KTC>([&](auto ktc) {
+    constexpr int kt = decltype(ktc)::value;
+    constexpr int cur = kt & 1, nxt = cur ^ 1;
+    // A(kt + 2) in registers (waited for here, MFMAs before its LDS writes:
+    // waited for just before them, the compiler merges the wait with its own
+    // for those registers and drains every load while direct-to-LDS loads
+    // are outstanding)
+    if constexpr (kt + 2 < KTC) wait_vmcnt<iw_after(KTC, D, NAD, NBD, true, kt + 2, kt)>();
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<NB * MS>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      constexpr int j = m / MS, i = m % MS;
+      acc[i][j] = mfma_wt(bf[bslot(j, kt)], af[cur][i], acc[i][j]);
+      constexpr int op = slots.op[m], q = slots.arg[m];
+      if constexpr (op == kIwStA) {
+        if constexpr (kt + 2 < KTC)  // over A(kt), whose fragments were read in step kt - 1
+          *reinterpret_cast<v4i*>(astage(kt + 2) + (NAD * wave + q) * 1024 + lane * 16) = ra[cur][q];
+      } else if constexpr (op == kIwLdA) {
+        if constexpr (kt + 4 < KTC)
+          ra[cur][q] = *reinterpret_cast<const v4i*>(a + aoff[q] + (kt + 4) * kBK);
+      } else if constexpr (op == kIwLdB) {
+        if constexpr (kt + D < KTC)  // over B(kt)
+          dma16(w13 + boff[q] + (kt + D) * KB, bstage(kt + D) + (NBD * wave + q) * 1024);
+      } else if constexpr (op == kIwRdA) {
+        if constexpr (kt + 1 < KTC) rda_half(af[nxt][q / 2], astage(kt + 1), q / 2, q % 2);
+      } else if constexpr (op == kIwRdB) {
+        if constexpr (kt + 1 < KTC) rdb_half(bf[bslot(q / 2, kt + 1)], bstage(kt + 1), q / 2, q % 2, kt + 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    // this wave's part of B(kt + 2) landed; with the barrier's LDS wait, A(kt +
+    // 2) is written and step kt + 1's fragments are in registers
+    if constexpr (kt + 2 < KTC) wait_vmcnt<iw_after(KTC, D, NAD, NBD, false, kt + 2, kt + 1)>();
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  wait_vmcnt<0>();
+  float(*red)[BM] = reinterpret_cast<float(*)[BM]>(a0);
+  const v4f one = v4f{1.f, 1.f, 1.f, 1.f};  // MXFP4: no channel scales
+  const int c0 = wn * 64 + 4 * (lane >> 4);
+  gateup_epilogue_pp<BM, MS, NS, 2>(
+      acc, [&](int i) { return sxl[rbase + i * 16 + (lane & 15)]; },
+      [&](int jj) { return W4 ? one : *reinterpret_cast<const v4f*>(&s13l[c0 + 16 * jj]); },
+      [&](int jj) { return W4 ? one : *reinterpret_cast<const v4f*>(&s13l[kHN + c0 + 16 * jj]); },
+      red, rbase, wn, lane, te, S, ntile);
+}
 
 // ---------------------------------------------------------------------------
 // Down GEMM with per-(row, 128-K block) h scales. Tile: BM rows x 256 output
@@ -1516,7 +1803,10 @@ hipError_t launch_gemms_bm(const FfnCall& c, TileHeader* hdr, TileEntry* up, Til
   constexpr int WU = waves_m<BM>(), WD = waves_m<BMD>();
   ev.mark(true, MOE_STEP_GATE_UP, s);
   if (cu > 0) {
-    if constexpr (KTU > 0 && BM >= 128)  // tall tiles: ping-pong schedule
+    if constexpr (KTU > 0 && BM == 192)  // tallest tiles: one wave per SIMD
+      hipLaunchKernelGGL((gateup_fp8_iw_kernel<BM, KTU, W4 ? 4 : 3, W4>),
+                         dim3((unsigned)cu), dim3(4 * kWave), 0, s, c, hdr, up);
+    else if constexpr (KTU > 0 && BM >= 128)  // tall tiles: ping-pong schedule
       hipLaunchKernelGGL((gateup_fp8_pp_kernel<BM, KTU, pp_weight_stages<BM, W4>(), W4>),
                          dim3((unsigned)cu), dim3(8 * kWave), 0, s, c, hdr, up);
     else  // (a fully unrolled K loop of tall tiles would spill: looped there)
