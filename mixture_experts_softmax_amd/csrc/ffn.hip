@@ -255,6 +255,29 @@ __device__ inline SetView set_view(const FfnCall& c, int sid) {
   return v;
 }
 
+// Activation rows of tile rows r[0..N) (rows past the tile repeat its last
+// row; the permutation's entries divided by the set's src_div). The entries
+// are loaded under one uniform branch, so the N loads issue back to back: a
+// branch per row makes each wait for the one before.
+template <int N>
+__device__ inline void gather_rows(const Tile& te, const SetView& S, int a_rows, const int (&r)[N],
+                                   int (&src)[N]) {
+  int grow[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) grow[i] = te.row0 + min(r[i], te.nrows - 1);
+  if (S.row_src != nullptr) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) src[i] = S.row_src[grow[i]];
+#pragma unroll
+    for (int i = 0; i < N; ++i) src[i] /= S.src_div;
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) src[i] = grow[i];
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) src[i] = min(max(src[i], 0), a_rows - 1);
+}
+
 // B operand prefetch depth (K steps of weights in flight per wave), by the
 // rows a wave holds (more rows: a bigger accumulator, fewer registers left).
 template <int ROWS, int LIMIT>
@@ -877,54 +900,62 @@ __global__ __launch_bounds__(8 * kWave) void gateup_fp8_pp_kernel(
 template <int BM, bool W4>
 constexpr int pp_weight_stages() { return (W4 || BM <= 128) ? 4 : 3; }
 
-// Side work of one K step of the four-wave gate/up kernel, one item per MFMA
-// slot (m = 0 .. NSLOT - 1). Global loads sit in every third slot -- A piece
-// p's LDS write in slot 3 p, its next load in 3 p + 1, then weight piece q in
-// 3 (NA + q) + 1 -- because the four waves reach the same slot together, and
+// Side work of one K step of the four-wave gate/up kernel, at most two items
+// per MFMA slot (m = 0 .. NSLOT - 1). Global loads sit in every third slot,
+// each right after the LDS write that frees its registers (activation piece
+// p: write in slot 3 p, reload in 3 p + 1; then weight piece q likewise at
+// 3 (NA + q)), because the four waves reach the same slot together and
 // bunched loads back up the CU's address queue, which stalls the loading
-// wave's MFMAs behind them. LDS fragment reads fill the other slots: B
-// fragment j (two reads) only after slot MS j + MS - 1, its last MFMA (except
-// the last fragment, whose registers alternate), A fragment halves anywhere.
-enum IwOp { kIwNone, kIwStA, kIwLdA, kIwLdB, kIwRdA, kIwRdB };
+// wave's MFMAs behind them. LDS fragment reads fill the rest, two to a slot
+// where needed: B fragment j (two reads) only after slot MS j + MS - 1, its
+// last MFMA (except the last fragment, whose registers alternate), A
+// fragment halves anywhere.
+enum IwOp { kIwNone, kIwStA, kIwLdA, kIwStB, kIwLdB, kIwRdA, kIwRdB };
 template <int NSLOT>
 struct IwSlots {
-  int op[NSLOT];
-  int arg[NSLOT];
+  int op[2][NSLOT];
+  int arg[2][NSLOT];
 };
-template <int NSLOT, int NA, int NB_LD, int MS, int NBF>
+template <int NSLOT, int NA, int NBL, int MS, int NBF>
 constexpr IwSlots<NSLOT> iw_slots() {
   IwSlots<NSLOT> t{};
-  for (int m = 0; m < NSLOT; ++m) t.op[m] = kIwNone, t.arg[m] = 0;
-  for (int p = 0; p < NA; ++p) {
-    t.op[3 * p] = kIwStA, t.arg[3 * p] = p;
-    t.op[3 * p + 1] = kIwLdA, t.arg[3 * p + 1] = p;
+  for (int h = 0; h < 2; ++h)
+    for (int m = 0; m < NSLOT; ++m) t.op[h][m] = kIwNone, t.arg[h][m] = 0;
+  for (int p = 0; p < NA + NBL; ++p) {
+    const bool a = p < NA;
+    t.op[0][3 * p] = a ? kIwStA : kIwStB, t.arg[0][3 * p] = a ? p : p - NA;
+    t.op[0][3 * p + 1] = a ? kIwLdA : kIwLdB, t.arg[0][3 * p + 1] = a ? p : p - NA;
   }
-  for (int q = 0; q < NB_LD; ++q) t.op[3 * (NA + q) + 1] = kIwLdB, t.arg[3 * (NA + q) + 1] = q;
-  // B fragment halves in order, each in the earliest free slot after its
-  // fragment's last MFMA (the last fragment: any free slot)
+  // a read goes to the earliest slot at or after lo with room: an empty
+  // slot, else the second place of a slot that holds no global load
+  auto place = [&](int lo, int op, int arg) {
+    for (int pass = 0; pass < 2; ++pass)
+      for (int m = lo; m < NSLOT; ++m) {
+        if (pass == 0 && t.op[0][m] == kIwNone) {
+          t.op[0][m] = op, t.arg[0][m] = arg;
+          return;
+        }
+        if (pass == 1 && t.op[1][m] == kIwNone && t.op[0][m] != kIwLdA && t.op[0][m] != kIwLdB) {
+          t.op[1][m] = op, t.arg[1][m] = arg;
+          return;
+        }
+      }
+  };
   for (int f = 0; f < 2 * NBF; ++f) {
-    const int j = f / 2, lo = (j + 1 < NBF) ? MS * j + MS : 0;
-    for (int m = lo; m < NSLOT; ++m)
-      if (t.op[m] == kIwNone) {
-        t.op[m] = kIwRdB, t.arg[m] = f;
-        break;
-      }
+    const int j = f / 2;
+    place((j + 1 < NBF) ? MS * j + MS : 0, kIwRdB, f);
   }
-  for (int f = 0; f < 2 * MS; ++f)
-    for (int m = 0; m < NSLOT; ++m)
-      if (t.op[m] == kIwNone) {
-        t.op[m] = kIwRdA, t.arg[m] = f;
-        break;
-      }
+  for (int f = 0; f < 2 * MS; ++f) place(0, kIwRdA, f);
   return t;
 }
-template <int NSLOT, int NA, int NB_LD, int MS, int NBF>
+template <int NSLOT, int NA, int NBL, int MS, int NBF>
 constexpr bool iw_slots_complete() {
-  constexpr IwSlots<NSLOT> t = iw_slots<NSLOT, NA, NB_LD, MS, NBF>();
-  int n[6] = {0, 0, 0, 0, 0, 0};
-  for (int m = 0; m < NSLOT; ++m) ++n[t.op[m]];
-  return 3 * (NA + NB_LD) <= NSLOT && n[kIwStA] == NA && n[kIwLdA] == NA && n[kIwLdB] == NB_LD &&
-         n[kIwRdA] == 2 * MS && n[kIwRdB] == 2 * NBF;
+  constexpr IwSlots<NSLOT> t = iw_slots<NSLOT, NA, NBL, MS, NBF>();
+  int n[7] = {0, 0, 0, 0, 0, 0, 0};
+  for (int h = 0; h < 2; ++h)
+    for (int m = 0; m < NSLOT; ++m) ++n[t.op[h][m]];
+  return 3 * (NA + NBL) <= NSLOT && n[kIwStA] == NA && n[kIwLdA] == NA && n[kIwStB] == NBL &&
+         n[kIwLdB] == NBL && n[kIwRdA] == 2 * MS && n[kIwRdB] == 2 * NBF;
 }
 
 // ---------------------------------------------------------------------------
@@ -940,21 +971,24 @@ constexpr bool iw_slots_complete() {
 // Each wave overlaps its own LDS traffic with its MFMAs: while the MFMAs of
 // step kt run (B fragment by B fragment), it reads step kt + 1's fragments
 // (each B fragment's registers right after the last MFMA that uses them; the
-// A fragments into a second set), writes step kt + 2's activation rows into
-// the A stage step kt's rows left, and issues later steps' global loads.
+// A fragments into a second set), writes step kt + 2's operand rows into the
+// stages step kt's rows left, and issues later steps' global loads.
 // One workgroup barrier per step, at its end: by then every wave has read
 // step kt + 1's fragments (so the stages of step kt + 1 may be overwritten
-// from step kt + 1 on), written A(kt + 2) and received its part of B(kt + 2)
-// (both read during step kt + 1).
+// from step kt + 1 on) and written its part of step kt + 2 (read during step
+// kt + 1).
 //
-// Operand staging: activation rows (gathered through the permutation) go
-// through registers, loaded two steps before they are written and written
-// two steps before their fragments are computed with (two A stages); weight
-// rows go straight into one of NBS LDS stages, NBS steps ahead (the stage of
-// step kt is free once its fragments are read, during step kt - 1). MXFP4:
-// the weights' E8M0 scales in an LDS tile filled once per workgroup.
+// Operand staging: both operands go through registers -- weight rows loaded
+// two steps before they are written into LDS (two register sets), activation
+// rows one step (one set; mostly L2 hits) -- and are written two steps before
+// their fragments are computed with (two LDS stages each).
+// Direct-to-LDS loads would save the registers and the LDS writes, but each
+// stalls its (only) wave's instruction issue for tens of cycles, and here
+// that wave also issues the MFMAs. Activation rows are gathered through the
+// permutation; MXFP4 weights' E8M0 scales sit in an LDS tile filled once per
+// workgroup.
 // ---------------------------------------------------------------------------
-template <int BM, int KTC, int NBS, bool W4>
+template <int BM, int KTC, bool W4>
 __global__ __launch_bounds__(4 * kWave) void gateup_fp8_iw_kernel(
     FfnCall c, const TileHeader* __restrict__ hdr, const TileEntry* __restrict__ list) {
   constexpr int NW = 4;
@@ -964,24 +998,18 @@ __global__ __launch_bounds__(4 * kWave) void gateup_fp8_iw_kernel(
   constexpr int KB = kstep_bytes<W4>();          // weight bytes per row and K step
   constexpr int NAD = BM * kBK / 1024 / NW;      // A pieces (16 B) per thread per step
   constexpr int NBD = BROWS * KB / 1024 / NW;    // B pieces per thread per step
-  constexpr int D = NBS;                         // weight steps loaded ahead
   constexpr int SSC = W4 ? BROWS * (KTC + 1) : 1;  // MXFP4 scale tile (dwords)
   static_assert(BM * kBK % (1024 * NW) == 0, "A tile must split into whole wave loads");
-  static_assert(KTC >= D + 4, "the prologue loads four activation and D weight steps");
-  static_assert(NBS >= 3 && NBS <= 4, "three or four weight stages");
+  static_assert(KTC >= 4, "the prologue loads four steps");
   static_assert(2 * BM * 4 <= BM * kBK, "row maxima fit in an A stage");
   static_assert(!W4 || KTC % 4 == 0, "MXFP4 scales are held per row in K-step quads");
-  static_assert(2 * BM * kBK + NBS * BROWS * KB + (W4 ? 4 * SSC : 0) + (BM + BROWS) * 4 <= 163840,
+  static_assert(2 * BM * kBK + 2 * BROWS * KB + (W4 ? 4 * SSC : 0) + (BM + BROWS) * 4 <= 163840,
                 "stages and scales fit the LDS");
 
-  // one LDS variable per stage (the compiler then tells the stages apart and
-  // does not drain the direct-to-LDS loads before reading another stage)
   __shared__ __attribute__((aligned(1024))) uint8_t a0[BM * kBK];
   __shared__ __attribute__((aligned(1024))) uint8_t a1[BM * kBK];
   __shared__ __attribute__((aligned(1024))) uint8_t b0[BROWS * KB];
   __shared__ __attribute__((aligned(1024))) uint8_t b1[BROWS * KB];
-  __shared__ __attribute__((aligned(1024))) uint8_t b2[BROWS * KB];
-  __shared__ __attribute__((aligned(1024))) uint8_t b3[NBS > 3 ? BROWS * KB : 16];
   __shared__ int ssc[SSC];
   __shared__ float sxl[BM];
   __shared__ __attribute__((aligned(16))) float s13l[W4 ? 1 : BROWS];
@@ -997,67 +1025,71 @@ __global__ __launch_bounds__(4 * kWave) void gateup_fp8_iw_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave >> 1, wn = wave & 1;
   const int rbase = wm * BMW;
-  auto src_row = [&](int r) {  // activation row of tile row r
-    const int grow = te.row0 + min(r, te.nrows - 1);
-    return min(max(S.row_src ? S.row_src[grow] / S.src_div : grow, 0), c.a_rows - 1);
+  // B piece i: FP8 weight-tile row RPB (NBD wave + i) + lane / 8 (rows
+  // 0..127 gate, 128..255 up), chunks swizzled as the A tile's; MXFP4 rows of
+  // 64 bytes, RPB = 16 to a block, row 16 (NBD wave + i) + lane / 4, its chunk
+  // q stored at q ^ ((row / 2) % 4) (conflict-free 16-byte fragment reads). A
+  // wave's pieces lie in one half (64 rows) and share the chunk, so piece i
+  // is piece 0 plus i RPB rows: one per-lane offset, the rest uniform.
+  constexpr int RPB = W4 ? 16 : 8;  // weight rows per 1 KiB block
+  static_assert(NBD * RPB * NW == BROWS && NBD * RPB <= kHN / 2, "a wave's pieces in one half");
+  const size_t wrb = W4 ? d / 2 : d;  // weight bytes per row
+  const uint8_t* w13 = S.w13 + (size_t)g * 2 * F * wrb;
+  auto wrow_of = [&](int rr) { return (rr < kHN) ? ntile * kHN + rr : F + ntile * kHN + (rr - kHN); };
+  uint32_t boff;
+  {
+    const int rr = RPB * NBD * wave + (W4 ? (lane >> 2) : (lane >> 3));
+    const int cch = W4 ? ((lane & 3) ^ ((rr >> 1) & 3)) : ((lane & 7) ^ (rr & 7));
+    boff = (uint32_t)wrow_of(rr) * (uint32_t)wrb + (cch << 4);
+  }
+  auto bsrc = [&](int kt, int i) { return w13 + (size_t)i * RPB * wrb + kt * KB + boff; };
+
+  // operand rows in registers from their load to their LDS write: weight
+  // rows two steps ahead (set kt & 1 holds step kt's), activation rows one
+  // (one set; they mostly come from the L2)
+  v4i ra[NAD], rb[2][NBD];
+  auto ldb = [&](int kt, int slot) {
+#pragma unroll
+    for (int i = 0; i < NBD; ++i) rb[slot][i] = *reinterpret_cast<const v4i*>(bsrc(kt, i));
   };
 
   // A piece i of this thread: tile row 8 (NAD wave + i) + lane / 8, stored at
   // (its 1 KiB block) + 16 lane, the swizzle applied by the source chunk
-  // (32-bit offsets from the activation base)
+  // (32-bit offsets from the activation base); row NAD of the lookup is the
+  // x-scale row of thread tid
   const uint8_t* a = static_cast<const uint8_t*>(c.a);
   uint32_t aoff[NAD];
+  float sxv;
+  {
+    // the permutation's entries in one batch (the activation loads wait for
+    // them; the weights' loads are issued with the activations', after this
+    // wait, since an earlier issue would make the wait for the entries wait
+    // for them as well: loads complete in issue order)
+    int r[NAD + 1], src[NAD + 1];
 #pragma unroll
-  for (int i = 0; i < NAD; ++i) {
-    const int r = 8 * (NAD * wave + i) + (lane >> 3);
-    aoff[i] = (uint32_t)src_row(r) * (uint32_t)d + (((lane & 7) ^ (r & 7)) << 4);
-  }
-  // B piece i: FP8 weight-tile row 8 (NBD wave + i) + lane / 8 (rows 0..127
-  // gate, 128..255 up), chunks swizzled as the A tile's; MXFP4 rows of 64
-  // bytes, 16 to a block, row 16 (NBD wave + i) + lane / 4, its chunk q
-  // stored at q ^ ((row / 2) % 4) (conflict-free 16-byte fragment reads)
-  const size_t wrb = W4 ? d / 2 : d;  // weight bytes per row
-  const uint8_t* w13 = S.w13 + (size_t)g * 2 * F * wrb;
-  auto wrow_of = [&](int rr) { return (rr < kHN) ? ntile * kHN + rr : F + ntile * kHN + (rr - kHN); };
-  uint32_t boff[NBD];
-#pragma unroll
-  for (int i = 0; i < NBD; ++i) {
-    if constexpr (W4) {
-      const int rr = 16 * (NBD * wave + i) + (lane >> 2);
-      boff[i] = (uint32_t)wrow_of(rr) * (uint32_t)wrb + ((((lane & 3) ^ ((rr >> 1) & 3))) << 4);
-    } else {
-      const int rr = 8 * (NBD * wave + i) + (lane >> 3);
-      boff[i] = (uint32_t)wrow_of(rr) * (uint32_t)wrb + (((lane & 7) ^ (rr & 7)) << 4);
-    }
-  }
-  if constexpr (W4)
-    fill_scale_tile<KTC, BROWS, NW * kWave>(
-        ssc, [&](int r) { return S.e13 + ((size_t)g * 2 * F + wrow_of(r)) * (d / 32); }, tid);
-  if (tid < BM) sxl[tid] = c.a_scale[src_row(tid)];
-  if constexpr (!W4) {
-    const float* s13 = S.s13 + (size_t)g * 2 * F;
-    s13l[tid] = s13[wrow_of(tid)];  // 256 threads, 256 weight rows
-  }
-
-  v4i ra[2][NAD];  // activation rows, loaded two steps before they are written
-  auto lda = [&](int kt, int slot) {
-#pragma unroll
-    for (int i = 0; i < NAD; ++i) ra[slot][i] = *reinterpret_cast<const v4i*>(a + aoff[i] + kt * kBK);
-  };
-  auto sta = [&](int slot, uint8_t* ad) {
+    for (int i = 0; i < NAD; ++i) r[i] = 8 * (NAD * wave + i) + (lane >> 3);
+    r[NAD] = min(tid, BM - 1);
+    gather_rows(te, S, c.a_rows, r, src);
 #pragma unroll
     for (int i = 0; i < NAD; ++i)
-      *reinterpret_cast<v4i*>(ad + (NAD * wave + i) * 1024 + lane * 16) = ra[slot][i];
-  };
-  auto ldb = [&](int kt, uint8_t* bd) {
+      aoff[i] = (uint32_t)src[i] * (uint32_t)d + (((lane & 7) ^ (r[i] & 7)) << 4);
+    sxv = c.a_scale[src[NAD]];
+  }
+  auto lda = [&](v4i (&r)[NAD], int kt) {
 #pragma unroll
-    for (int i = 0; i < NBD; ++i) dma16(w13 + boff[i] + kt * KB, bd + (NBD * wave + i) * 1024);
+    for (int i = 0; i < NAD; ++i) r[i] = *reinterpret_cast<const v4i*>(a + aoff[i] + kt * kBK);
+  };
+  auto sta = [&](const v4i (&r)[NAD], uint8_t* ad) {
+#pragma unroll
+    for (int i = 0; i < NAD; ++i) *reinterpret_cast<v4i*>(ad + (NAD * wave + i) * 1024 + lane * 16) = r[i];
+  };
+  auto stb = [&](int slot, uint8_t* bd) {
+#pragma unroll
+    for (int i = 0; i < NBD; ++i)
+      *reinterpret_cast<v4i*>(bd + (NBD * wave + i) * 1024 + lane * 16) = rb[slot][i];
   };
   auto astage = [&](int kt) { return (kt & 1) ? a1 : a0; };
-  auto bstage = [&](int kt) {
-    const int m = kt % NBS;
-    return m == 0 ? b0 : m == 1 ? b1 : m == 2 ? b2 : b3;
-  };
+  auto bstage = [&](int kt) { return (kt & 1) ? b1 : b0; };
   // Fragments are read in halves, one LDS instruction each: A fragment i of
   // a stage is two 16-byte reads at rows rbase + 16 i + lane % 16; B fragment
   // j (rows 0..63 of the wave's 128: gate, 64..127: up) two reads (FP8) or
@@ -1081,24 +1113,35 @@ __global__ __launch_bounds__(4 * kWave) void gateup_fp8_iw_kernel(
     }
   };
 
-  // prologue: A(0), A(1), B(0) .. B(D - 1); A(0), A(1) into their stages;
-  // A(2), A(3); B(0) and B(1) landed (the order iw_after counts; scheduling
-  // barriers keep the compiler from reordering the groups)
-  lda(0, 0);
-  lda(1, 1);
+  // prologue: steps 0 and 1 written (the activation rows through registers
+  // that the K loop's fragments take later; the tile's scales are loaded
+  // while they are in flight), weights of steps 2 and 3 and activations of
+  // step 2 loaded
+  {
+    v4i t0[NAD], t1[NAD];
+    lda(t0, 0);
+    ldb(0, 0);
+    lda(t1, 1);
+    ldb(1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (W4)
+      fill_scale_tile<KTC, BROWS, NW * kWave>(
+          ssc, [&](int r) { return S.e13 + ((size_t)g * 2 * F + wrow_of(r)) * (d / 32); }, tid);
+    if (tid < BM) sxl[tid] = sxv;
+    if constexpr (!W4) {
+      const float* s13 = S.s13 + (size_t)g * 2 * F;
+      s13l[tid] = s13[wrow_of(tid)];  // 256 threads, 256 weight rows
+    }
+    sta(t0, a0);
+    stb(0, b0);
+    sta(t1, a1);
+    stb(1, b1);
+  }
   __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int s = 0; s < D; ++s) ldb(s, bstage(s));
-  __builtin_amdgcn_sched_barrier(0);
-  wait_vmcnt<D * NBD>();
-  sta(0, a0);
-  sta(1, a1);
-  __builtin_amdgcn_sched_barrier(0);
-  lda(2, 0);
-  lda(3, 1);
-  __builtin_amdgcn_sched_barrier(0);
-  wait_vmcnt<iw_after(KTC, D, NAD, NBD, false, 1, 0)>();
-  lds_barrier();  // publishes A(0), A(1), B(0), B(1) and the scales
+  lda(ra, 2);
+  ldb(2, 0);
+  ldb(3, 1);
+  lds_barrier();  // publishes steps 0 and 1 and the scales
 
   // B fragment NB - 1 is used by a step's last MFMA, so it alternates
   // between two register sets; the others are re-read into their own
@@ -1132,40 +1175,39 @@ __global__ __launch_bounds__(4 * kWave) void gateup_fp8_iw_kernel(
   static_for<KTC>([&](auto ktc) {
     constexpr int kt = decltype(ktc)::value;
     constexpr int cur = kt & 1, nxt = cur ^ 1;
-    // A(kt + 2) in registers (waited for here, MFMAs before its LDS writes:
-    // waited for just before them, the compiler merges the wait with its own
-    // for those registers and drains every load while direct-to-LDS loads
-    // are outstanding)
-    if constexpr (kt + 2 < KTC) wait_vmcnt<iw_after(KTC, D, NAD, NBD, true, kt + 2, kt)>();
-    __builtin_amdgcn_sched_barrier(0);
-    static_for<NB * MS>([&](auto mc) {
+    static_for<NSLOT>([&](auto mc) {
       constexpr int m = decltype(mc)::value;
       constexpr int j = m / MS, i = m % MS;
       acc[i][j] = mfma_wt(bf[bslot(j, kt)], af[cur][i], acc[i][j]);
-      constexpr int op = slots.op[m], q = slots.arg[m];
-      if constexpr (op == kIwStA) {
-        if constexpr (kt + 2 < KTC)  // over A(kt), whose fragments were read in step kt - 1
-          *reinterpret_cast<v4i*>(astage(kt + 2) + (NAD * wave + q) * 1024 + lane * 16) = ra[cur][q];
-      } else if constexpr (op == kIwLdA) {
-        if constexpr (kt + 4 < KTC)
-          ra[cur][q] = *reinterpret_cast<const v4i*>(a + aoff[q] + (kt + 4) * kBK);
-      } else if constexpr (op == kIwLdB) {
-        if constexpr (kt + D < KTC)  // over B(kt)
-          dma16(w13 + boff[q] + (kt + D) * KB, bstage(kt + D) + (NBD * wave + q) * 1024);
-      } else if constexpr (op == kIwRdA) {
-        if constexpr (kt + 1 < KTC) rda_half(af[nxt][q / 2], astage(kt + 1), q / 2, q % 2);
-      } else if constexpr (op == kIwRdB) {
-        if constexpr (kt + 1 < KTC) rdb_half(bf[bslot(q / 2, kt + 1)], bstage(kt + 1), q / 2, q % 2, kt + 1);
-      }
+      static_for<2>([&](auto hc) {
+        constexpr int op = slots.op[decltype(hc)::value][m], q = slots.arg[decltype(hc)::value][m];
+        if constexpr (op == kIwStA) {  // over step kt's rows, read in step kt - 1
+          if constexpr (kt + 2 < KTC)
+            *reinterpret_cast<v4i*>(astage(kt) + (NAD * wave + q) * 1024 + lane * 16) = ra[q];
+        } else if constexpr (op == kIwStB) {
+          if constexpr (kt + 2 < KTC)
+            *reinterpret_cast<v4i*>(bstage(kt) + (NBD * wave + q) * 1024 + lane * 16) = rb[cur][q];
+        } else if constexpr (op == kIwLdA) {
+          if constexpr (kt + 3 < KTC)
+            ra[q] = *reinterpret_cast<const v4i*>(a + aoff[q] + (kt + 3) * kBK);
+        } else if constexpr (op == kIwLdB) {
+          if constexpr (kt + 4 < KTC)
+            rb[cur][q] = *reinterpret_cast<const v4i*>(bsrc(kt + 4, q));
+        } else if constexpr (op == kIwRdA) {
+          if constexpr (kt + 1 < KTC) rda_half(af[nxt][q / 2], astage(kt + 1), q / 2, q % 2);
+        } else if constexpr (op == kIwRdB) {
+          if constexpr (kt + 1 < KTC)
+            rdb_half(bf[bslot(q / 2, kt + 1)], bstage(kt + 1), q / 2, q % 2, kt + 1);
+        }
+      });
       __builtin_amdgcn_sched_barrier(0);
     });
-    // this wave's part of B(kt + 2) landed; with the barrier's LDS wait, A(kt +
-    // 2) is written and step kt + 1's fragments are in registers
-    if constexpr (kt + 2 < KTC) wait_vmcnt<iw_after(KTC, D, NAD, NBD, false, kt + 2, kt + 1)>();
+    // with the barrier's LDS wait: step kt + 2 is written and step kt + 1's
+    // fragments are in registers (the compiler waits for each register load
+    // before the LDS write that uses it)
     lds_barrier();
     __builtin_amdgcn_sched_barrier(0);
   });
-  wait_vmcnt<0>();
   float(*red)[BM] = reinterpret_cast<float(*)[BM]>(a0);
   const v4f one = v4f{1.f, 1.f, 1.f, 1.f};  // MXFP4: no channel scales
   const int c0 = wn * 64 + 4 * (lane >> 4);
@@ -1804,7 +1846,7 @@ hipError_t launch_gemms_bm(const FfnCall& c, TileHeader* hdr, TileEntry* up, Til
   ev.mark(true, MOE_STEP_GATE_UP, s);
   if (cu > 0) {
     if constexpr (KTU > 0 && BM == 192)  // tallest tiles: one wave per SIMD
-      hipLaunchKernelGGL((gateup_fp8_iw_kernel<BM, KTU, W4 ? 4 : 3, W4>),
+      hipLaunchKernelGGL((gateup_fp8_iw_kernel<BM, KTU, W4>),
                          dim3((unsigned)cu), dim3(4 * kWave), 0, s, c, hdr, up);
     else if constexpr (KTU > 0 && BM >= 128)  // tall tiles: ping-pong schedule
       hipLaunchKernelGGL((gateup_fp8_pp_kernel<BM, KTU, pp_weight_stages<BM, W4>(), W4>),

@@ -1,7 +1,6 @@
-// Load counting of the tall gate/up kernels' fully unrolled K loops.
+// Load counting of the ping-pong gate/up kernel's fully unrolled K loop.
 //
-// Ping-pong kernel. A thread's global loads, in issue order: the prologue
-// issues A(0), B(0) ..
+// A thread's global loads, in issue order: the prologue issues A(0), B(0) ..
 // B(D - 2), A(1), B(D - 1); LOAD(j) issues A(j + 2) then B(j + D), each only
 // if that K step exists (KT steps in all). A(s) is the NA activation loads of
 // step s, B(s) the NB weight loads of step s, D the weight steps loaded ahead.
@@ -46,40 +45,6 @@ MOE_PP_HD constexpr int pp_after_b(int kt, int D, int KT, int NA, int NB) {
   // B(j + D) if j + D < KT
   const int j0 = (s >= D) ? s - D + 1 : 0;
   return pro + NA * pp_count_below(j0, kt, KT - 2) + NB * pp_count_below(j0, kt, KT - D);
-}
-
-// Four-wave kernel. A thread's loads, in issue order: the prologue issues
-// A(0), A(1), B(0) .. B(D - 1), then (once A(0) and A(1) are in LDS) A(2) and
-// A(3); step j issues A(j + 4), then B(j + D); steps at or past KT are never
-// loaded. Returns the loads issued after group (A if a, else B; step s) and
-// before step `cut` (cut = kt: the start of step kt; kt + 1: its end).
-MOE_PP_HD constexpr int iw_after(int KT, int D, int NA, int NB, bool a, int s, int cut) {
-  int n = 0;
-  bool seen = false;
-  for (int g = 0; g < D + 4; ++g) {  // the prologue's groups
-    const bool ga = g < 2 || g >= D + 2;
-    const int gs = g < 2 ? g : (g < D + 2 ? g - 2 : g - D);
-    if (gs >= KT) continue;
-    if (seen)
-      n += ga ? NA : NB;
-    else if (ga == a && gs == s)
-      seen = true;
-  }
-  for (int j = 0; j < cut && j < KT; ++j) {
-    if (j + 4 < KT) {
-      if (seen)
-        n += NA;
-      else if (a && s == j + 4)
-        seen = true;
-    }
-    if (j + D < KT) {
-      if (seen)
-        n += NB;
-      else if (!a && s == j + D)
-        seen = true;
-    }
-  }
-  return n;
 }
 
 }  // namespace moe
