@@ -15,6 +15,8 @@
 // same group -- run on the same XCD (blocks are dealt to the 8 XCDs in turn),
 // so a weight tile read by several M tiles, and a group's activation rows, are
 // served from that XCD's L2.
+#include <algorithm>
+#include <atomic>
 #include <type_traits>
 #include <utility>
 
@@ -85,11 +87,10 @@ struct Tile {
 };
 
 template <int BM>
-__device__ inline bool pick_tile(const TileEntry* __restrict__ list, int n_entries, int NT,
-                                 Tile& t) {
+__device__ inline bool pick_tile_at(const TileEntry* __restrict__ list, int n_entries, int NT,
+                                    int xcd, int slot, Tile& t) {
   const int total = n_entries * NT;
   const int per = ceil_div(total, kXcds);
-  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
   const int w = xcd * per + slot;
   if (slot >= per || w >= total) return false;
   const TileEntry te = list[w / NT];
@@ -101,6 +102,12 @@ __device__ inline bool pick_tile(const TileEntry* __restrict__ list, int n_entri
   t.nrows = min(BM, te.rows - m * BM);
   t.gid = te.gid;
   return true;
+}
+
+template <int BM>
+__device__ inline bool pick_tile(const TileEntry* __restrict__ list, int n_entries, int NT,
+                                 Tile& t) {
+  return pick_tile_at<BM>(list, n_entries, NT, blockIdx.x % kXcds, blockIdx.x / kXcds, t);
 }
 
 __device__ inline v8i pack8(const v4i& lo, const v4i& hi) {
@@ -194,6 +201,35 @@ __device__ inline void fill_scale_tile(int* tile, RowPtr rowp, int tid) {
       const v4i v = *reinterpret_cast<const v4i*>(rowp(r) + 16 * q);
 #pragma unroll
       for (int t = 0; t < 4; ++t) tile[r * (KT + 1) + 4 * q + t] = v[t];
+    }
+  }
+}
+
+// The same fill in two halves, so a kernel can issue the loads early and
+// write the tile later: a thread's pieces in registers, then into the tile.
+template <int KT, int ROWS, int NTH>
+constexpr int scale_pieces() { return (ROWS * (KT / 4) + NTH - 1) / NTH; }
+template <int KT, int ROWS, int NTH, int NP, typename RowPtr>
+__device__ inline void load_scale_pieces(v4i (&v)[NP], RowPtr rowp, int tid) {
+  static_assert(NP == scale_pieces<KT, ROWS, NTH>(), "one register per piece");
+  constexpr int PPR = KT / 4;
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int p = min(tid + i * NTH, ROWS * PPR - 1);
+    v[i] = *reinterpret_cast<const v4i*>(rowp(p / PPR) + 16 * (p % PPR));
+  }
+}
+template <int KT, int ROWS, int NTH, int NP>
+__device__ inline void store_scale_pieces(int* tile, const v4i (&v)[NP], int tid) {
+  static_assert(NP == scale_pieces<KT, ROWS, NTH>(), "one register per piece");
+  constexpr int PPR = KT / 4;
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int p = tid + i * NTH;
+    if (ROWS * PPR % NTH == 0 || p < ROWS * PPR) {
+      const int r = p / PPR, q = p % PPR;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) tile[r * (KT + 1) + 4 * q + t] = v[i][t];
     }
   }
 }
@@ -999,11 +1035,13 @@ __global__ __launch_bounds__(4 * kWave) void gateup_fp8_iw_kernel(
   constexpr int NAD = BM * kBK / 1024 / NW;      // A pieces (16 B) per thread per step
   constexpr int NBD = BROWS * KB / 1024 / NW;    // B pieces per thread per step
   constexpr int SSC = W4 ? BROWS * (KTC + 1) : 1;  // MXFP4 scale tile (dwords)
+  constexpr int NSP = W4 ? scale_pieces<KTC, BROWS, NW * kWave>() : 1;
+  constexpr int RPB = W4 ? 16 : 8;  // weight rows per 1 KiB block
   static_assert(BM * kBK % (1024 * NW) == 0, "A tile must split into whole wave loads");
   static_assert(KTC >= 4, "the prologue loads four steps");
-  static_assert(2 * BM * 4 <= BM * kBK, "row maxima fit in an A stage");
   static_assert(!W4 || KTC % 4 == 0, "MXFP4 scales are held per row in K-step quads");
-  static_assert(2 * BM * kBK + 2 * BROWS * KB + (W4 ? 4 * SSC : 0) + (BM + BROWS) * 4 <= 163840,
+  static_assert(NBD * RPB * NW == BROWS && NBD * RPB <= kHN / 2, "a wave's pieces in one half");
+  static_assert(2 * BM * kBK + 2 * BROWS * KB + (W4 ? 4 * SSC : 0) + (3 * BM + BROWS) * 4 <= 163840,
                 "stages and scales fit the LDS");
 
   __shared__ __attribute__((aligned(1024))) uint8_t a0[BM * kBK];
@@ -1013,58 +1051,67 @@ __global__ __launch_bounds__(4 * kWave) void gateup_fp8_iw_kernel(
   __shared__ int ssc[SSC];
   __shared__ float sxl[BM];
   __shared__ __attribute__((aligned(16))) float s13l[W4 ? 1 : BROWS];
+  __shared__ float red[2][BM];  // the epilogue's row maxima
 
-  Tile te;
-  if (!pick_tile<BM>(list, hdr->n_up, up_ntiles_max(c), te)) return;
-  const int ntile = te.ntile;
-  const int sid = te.gid >> 16, g = te.gid & 0xffff;
-  const SetView S = set_view(c, sid);
-  const int d = c.d, F = S.F;
-  if (ntile >= F / kHN) return;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  // (tid and lane are re-declared unknown to the compiler at each tile, so
+  // addresses derived from them are computed per tile: hoisted out of the
+  // tile loop they would stay live across the K loop, which needs every
+  // register)
+  int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave >> 1, wn = wave & 1;
   const int rbase = wm * BMW;
-  // B piece i: FP8 weight-tile row RPB (NBD wave + i) + lane / 8 (rows
-  // 0..127 gate, 128..255 up), chunks swizzled as the A tile's; MXFP4 rows of
-  // 64 bytes, RPB = 16 to a block, row 16 (NBD wave + i) + lane / 4, its chunk
-  // q stored at q ^ ((row / 2) % 4) (conflict-free 16-byte fragment reads). A
-  // wave's pieces lie in one half (64 rows) and share the chunk, so piece i
-  // is piece 0 plus i RPB rows: one per-lane offset, the rest uniform.
-  constexpr int RPB = W4 ? 16 : 8;  // weight rows per 1 KiB block
-  static_assert(NBD * RPB * NW == BROWS && NBD * RPB <= kHN / 2, "a wave's pieces in one half");
-  const size_t wrb = W4 ? d / 2 : d;  // weight bytes per row
-  const uint8_t* w13 = S.w13 + (size_t)g * 2 * F * wrb;
-  auto wrow_of = [&](int rr) { return (rr < kHN) ? ntile * kHN + rr : F + ntile * kHN + (rr - kHN); };
-  uint32_t boff;
-  {
+  const int d = c.d;
+  const uint8_t* a = static_cast<const uint8_t*>(c.a);
+
+  // The workgroup's tiles: slots slot, slot + sstep, ... of its XCD's items
+  // (pick_tile's order), skipping N tiles past a set's width.
+  const int NT = up_ntiles_max(c), n_ent = hdr->n_up;
+  const int xcd = blockIdx.x % kXcds, sstep = gridDim.x / kXcds;
+  auto next_tile = [&](int& sl, Tile& t) {
+    for (; pick_tile_at<BM>(list, n_ent, NT, xcd, sl, t); sl += sstep)
+      if (t.ntile < ((t.gid >> 16) ? c.set[1].F : c.set[0].F) / kHN) return true;
+    return false;
+  };
+
+  // Per-tile state. B piece i: FP8 weight-tile row RPB (NBD wave + i) +
+  // lane / 8 (rows 0..127 gate, 128..255 up), chunks swizzled as the A
+  // tile's; MXFP4 rows of 64 bytes, RPB = 16 to a block, row 16 (NBD wave + i)
+  // + lane / 4, its chunk q stored at q ^ ((row / 2) % 4) (conflict-free
+  // 16-byte fragment reads). A wave's pieces lie in one half (64 rows) and
+  // share the chunk, so piece i is piece 0 plus i RPB rows: one per-lane
+  // offset, the rest uniform. A piece i: tile row 8 (NAD wave + i) + lane / 8,
+  // stored at (its 1 KiB block) + 16 lane, the swizzle applied by the source
+  // chunk (32-bit offsets from the activation base).
+  // (only derived values live across the K loop: the tile, its weights,
+  // scale rows and output pointers -- not the whole set view)
+  Tile te;
+  int F = 0, sxrow = 0;
+  size_t wrb = 0;
+  const uint8_t* w13 = nullptr;   // the group's gate/up weight rows
+  const uint8_t* e13g = nullptr;  // MXFP4: their scale rows
+  const float* s13g = nullptr;    // FP8: their channel scales
+  uint8_t* h_out = nullptr;
+  float* hs_out = nullptr;
+  uint32_t boff = 0, aoff[NAD];
+  auto wrow_of = [&](int rr) { return (rr < kHN) ? te.ntile * kHN + rr : F + te.ntile * kHN + (rr - kHN); };
+  auto setup = [&]() {
+    const SetView S = set_view(c, te.gid >> 16);
+    const int g = te.gid & 0xffff;
+    F = S.F;
+    wrb = W4 ? d / 2 : d;
+    w13 = S.w13 + (size_t)g * 2 * F * wrb;
+    if constexpr (W4)
+      e13g = S.e13 + (size_t)g * 2 * F * (d / 32);
+    else
+      s13g = S.s13 + (size_t)g * 2 * F;
+    h_out = S.h;
+    hs_out = S.h_scale;
     const int rr = RPB * NBD * wave + (W4 ? (lane >> 2) : (lane >> 3));
     const int cch = W4 ? ((lane & 3) ^ ((rr >> 1) & 3)) : ((lane & 7) ^ (rr & 7));
     boff = (uint32_t)wrow_of(rr) * (uint32_t)wrb + (cch << 4);
-  }
-  auto bsrc = [&](int kt, int i) { return w13 + (size_t)i * RPB * wrb + kt * KB + boff; };
-
-  // operand rows in registers from their load to their LDS write: weight
-  // rows two steps ahead (set kt & 1 holds step kt's), activation rows one
-  // (one set; they mostly come from the L2)
-  v4i ra[NAD], rb[2][NBD];
-  auto ldb = [&](int kt, int slot) {
-#pragma unroll
-    for (int i = 0; i < NBD; ++i) rb[slot][i] = *reinterpret_cast<const v4i*>(bsrc(kt, i));
-  };
-
-  // A piece i of this thread: tile row 8 (NAD wave + i) + lane / 8, stored at
-  // (its 1 KiB block) + 16 lane, the swizzle applied by the source chunk
-  // (32-bit offsets from the activation base); row NAD of the lookup is the
-  // x-scale row of thread tid
-  const uint8_t* a = static_cast<const uint8_t*>(c.a);
-  uint32_t aoff[NAD];
-  float sxv;
-  {
-    // the permutation's entries in one batch (the activation loads wait for
-    // them; the weights' loads are issued with the activations', after this
-    // wait, since an earlier issue would make the wait for the entries wait
-    // for them as well: loads complete in issue order)
+    // the permutation's entries in one batch (row NAD: the x-scale row of
+    // thread tid)
     int r[NAD + 1], src[NAD + 1];
 #pragma unroll
     for (int i = 0; i < NAD; ++i) r[i] = 8 * (NAD * wave + i) + (lane >> 3);
@@ -1073,20 +1120,21 @@ __global__ __launch_bounds__(4 * kWave) void gateup_fp8_iw_kernel(
 #pragma unroll
     for (int i = 0; i < NAD; ++i)
       aoff[i] = (uint32_t)src[i] * (uint32_t)d + (((lane & 7) ^ (r[i] & 7)) << 4);
-    sxv = c.a_scale[src[NAD]];
-  }
+    sxrow = src[NAD];
+  };
+  auto bsrc = [&](int kt, int i) { return w13 + (size_t)i * RPB * wrb + kt * KB + boff; };
+
+  // operand rows in registers from their load to their LDS write: weight
+  // rows two steps ahead (set kt & 1 holds step kt's), activation rows one
+  // (one set; they mostly come from the L2)
+  v4i ra[NAD], rb[2][NBD];
   auto lda = [&](v4i (&r)[NAD], int kt) {
 #pragma unroll
     for (int i = 0; i < NAD; ++i) r[i] = *reinterpret_cast<const v4i*>(a + aoff[i] + kt * kBK);
   };
-  auto sta = [&](const v4i (&r)[NAD], uint8_t* ad) {
+  auto ldb = [&](int kt, int slot) {
 #pragma unroll
-    for (int i = 0; i < NAD; ++i) *reinterpret_cast<v4i*>(ad + (NAD * wave + i) * 1024 + lane * 16) = r[i];
-  };
-  auto stb = [&](int slot, uint8_t* bd) {
-#pragma unroll
-    for (int i = 0; i < NBD; ++i)
-      *reinterpret_cast<v4i*>(bd + (NBD * wave + i) * 1024 + lane * 16) = rb[slot][i];
+    for (int i = 0; i < NBD; ++i) rb[slot][i] = *reinterpret_cast<const v4i*>(bsrc(kt, i));
   };
   auto astage = [&](int kt) { return (kt & 1) ? a1 : a0; };
   auto bstage = [&](int kt) { return (kt & 1) ? b1 : b0; };
@@ -1113,109 +1161,154 @@ __global__ __launch_bounds__(4 * kWave) void gateup_fp8_iw_kernel(
     }
   };
 
-  // prologue: steps 0 and 1 written (the activation rows through registers
-  // that the K loop's fragments take later; the tile's scales are loaded
-  // while they are in flight), weights of steps 2 and 3 and activations of
-  // step 2 loaded
-  {
-    v4i t0[NAD], t1[NAD];
-    lda(t0, 0);
-    ldb(0, 0);
-    lda(t1, 1);
-    ldb(1, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (W4)
-      fill_scale_tile<KTC, BROWS, NW * kWave>(
-          ssc, [&](int r) { return S.e13 + ((size_t)g * 2 * F + wrow_of(r)) * (d / 32); }, tid);
-    if (tid < BM) sxl[tid] = sxv;
-    if constexpr (!W4) {
-      const float* s13 = S.s13 + (size_t)g * 2 * F;
-      s13l[tid] = s13[wrow_of(tid)];  // 256 threads, 256 weight rows
+  // A tile's first loads: activations and weights of steps 0 and 1 straight
+  // into their LDS stages (the same layout the register path writes; outside
+  // the K loop a direct-to-LDS load's issue stall costs nothing), its x and
+  // channel scales (MXFP4: its scale tile's pieces) into registers. Issued
+  // for the next tile before the current one's epilogue, which uses none of
+  // the stages, so they land meanwhile.
+  v4i scp[NSP];
+  float sxv = 0.f, s13v = 0.f;
+  auto issue_first = [&]() {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int i = 0; i < NAD; ++i)
+        dma16(a + aoff[i] + s * kBK, astage(s) + (NAD * wave + i) * 1024);
+#pragma unroll
+      for (int i = 0; i < NBD; ++i) dma16(bsrc(s, i), bstage(s) + (NBD * wave + i) * 1024);
     }
-    sta(t0, a0);
-    stb(0, b0);
-    sta(t1, a1);
-    stb(1, b1);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  lda(ra, 2);
-  ldb(2, 0);
-  ldb(3, 1);
-  lds_barrier();  // publishes steps 0 and 1 and the scales
+    sxv = c.a_scale[sxrow];
+    if constexpr (W4)
+      load_scale_pieces<KTC, BROWS, NW * kWave>(
+          scp, [&](int r) { return e13g + (size_t)wrow_of(r) * (d / 32); }, tid);
+    else
+      s13v = s13g[wrow_of(tid)];  // 256 threads, 256 weight rows
+  };
 
-  // B fragment NB - 1 is used by a step's last MFMA, so it alternates
-  // between two register sets; the others are re-read into their own
-  // registers after their step's last MFMA with them
-  BFrag<W4> bf[NB + 1];
-  v8i af[2][MS];
-  auto bslot = [&](int j, int kt) { return (j == NB - 1 && (kt & 1)) ? NB : j; };
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    rdb_half(bf[j], b0, j, 0, 0);
-    rdb_half(bf[j], b0, j, 1, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < MS; ++i) {
-    rda_half(af[0][i], a0, i, 0);
-    rda_half(af[0][i], a0, i, 1);
-  }
-  lds_barrier();  // every wave has read stage 0, which step 0 overwrites
+  int slot = blockIdx.x / kXcds;
+  if (!next_tile(slot, te)) return;
+  setup();
+  issue_first();
+  for (;;) {
+    asm volatile("" : "+v"(tid), "+v"(lane));
+    // prologue: steps 0 and 1 landed in LDS (this wave's part: every load
+    // it issued, the previous tile's epilogue stores included), the scales
+    // into LDS, weights of steps 2 and 3 and activations of step 2 loaded,
+    // step 0's fragments read
+    wait_vmcnt<0>();
+    if (tid < BM) sxl[tid] = sxv;
+    if constexpr (W4)
+      store_scale_pieces<KTC, BROWS, NW * kWave>(ssc, scp, tid);
+    else
+      s13l[tid] = s13v;
+    __builtin_amdgcn_sched_barrier(0);
+    lda(ra, 2);
+    ldb(2, 0);
+    ldb(3, 1);
+    lds_barrier();  // publishes steps 0 and 1 and the scales
 
-  v4f acc[MS][NB];
+    // B fragment NB - 1 is used by a step's last MFMA, so it alternates
+    // between two register sets; the others are re-read into their own
+    // registers after their step's last MFMA with them
+    BFrag<W4> bf[NB + 1];
+    v8i af[2][MS];
+    auto bslot = [&](int j, int kt) { return (j == NB - 1 && (kt & 1)) ? NB : j; };
 #pragma unroll
-  for (int i = 0; i < MS; ++i)
+    for (int j = 0; j < NB; ++j) {
+      rdb_half(bf[j], b0, j, 0, 0);
+      rdb_half(bf[j], b0, j, 1, 0);
+    }
 #pragma unroll
-    for (int j = 0; j < NB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-  __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < MS; ++i) {
+      rda_half(af[0][i], a0, i, 0);
+      rda_half(af[0][i], a0, i, 1);
+    }
+    lds_barrier();  // every wave has read stage 0, which step 0 overwrites
 
-  constexpr int NSLOT = NB * MS;  // MFMAs per step
-  static_assert(iw_slots_complete<NSLOT, NAD, NBD, MS, NB>(), "a step's side work fits its slots");
-  constexpr IwSlots<NSLOT> slots = iw_slots<NSLOT, NAD, NBD, MS, NB>();
+    v4f acc[MS][NB];
+#pragma unroll
+    for (int i = 0; i < MS; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    __builtin_amdgcn_sched_barrier(0);
 
-  static_for<KTC>([&](auto ktc) {
-    constexpr int kt = decltype(ktc)::value;
-    constexpr int cur = kt & 1, nxt = cur ^ 1;
-    static_for<NSLOT>([&](auto mc) {
-      constexpr int m = decltype(mc)::value;
-      constexpr int j = m / MS, i = m % MS;
-      acc[i][j] = mfma_wt(bf[bslot(j, kt)], af[cur][i], acc[i][j]);
-      static_for<2>([&](auto hc) {
-        constexpr int op = slots.op[decltype(hc)::value][m], q = slots.arg[decltype(hc)::value][m];
-        if constexpr (op == kIwStA) {  // over step kt's rows, read in step kt - 1
-          if constexpr (kt + 2 < KTC)
-            *reinterpret_cast<v4i*>(astage(kt) + (NAD * wave + q) * 1024 + lane * 16) = ra[q];
-        } else if constexpr (op == kIwStB) {
-          if constexpr (kt + 2 < KTC)
-            *reinterpret_cast<v4i*>(bstage(kt) + (NBD * wave + q) * 1024 + lane * 16) = rb[cur][q];
-        } else if constexpr (op == kIwLdA) {
-          if constexpr (kt + 3 < KTC)
-            ra[q] = *reinterpret_cast<const v4i*>(a + aoff[q] + (kt + 3) * kBK);
-        } else if constexpr (op == kIwLdB) {
-          if constexpr (kt + 4 < KTC)
-            rb[cur][q] = *reinterpret_cast<const v4i*>(bsrc(kt + 4, q));
-        } else if constexpr (op == kIwRdA) {
-          if constexpr (kt + 1 < KTC) rda_half(af[nxt][q / 2], astage(kt + 1), q / 2, q % 2);
-        } else if constexpr (op == kIwRdB) {
-          if constexpr (kt + 1 < KTC)
-            rdb_half(bf[bslot(q / 2, kt + 1)], bstage(kt + 1), q / 2, q % 2, kt + 1);
-        }
+    constexpr int NSLOT = NB * MS;  // MFMAs per step
+    static_assert(iw_slots_complete<NSLOT, NAD, NBD, MS, NB>(), "a step's side work fits its slots");
+    constexpr IwSlots<NSLOT> slots = iw_slots<NSLOT, NAD, NBD, MS, NB>();
+
+    static_for<KTC>([&](auto ktc) {
+      constexpr int kt = decltype(ktc)::value;
+      constexpr int cur = kt & 1, nxt = cur ^ 1;
+      static_for<NSLOT>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        constexpr int j = m / MS, i = m % MS;
+        acc[i][j] = mfma_wt(bf[bslot(j, kt)], af[cur][i], acc[i][j]);
+        static_for<2>([&](auto hc) {
+          constexpr int op = slots.op[decltype(hc)::value][m], q = slots.arg[decltype(hc)::value][m];
+          if constexpr (op == kIwStA) {  // over step kt's rows, read in step kt - 1
+            if constexpr (kt + 2 < KTC)
+              *reinterpret_cast<v4i*>(astage(kt) + (NAD * wave + q) * 1024 + lane * 16) = ra[q];
+          } else if constexpr (op == kIwStB) {
+            if constexpr (kt + 2 < KTC)
+              *reinterpret_cast<v4i*>(bstage(kt) + (NBD * wave + q) * 1024 + lane * 16) = rb[cur][q];
+          } else if constexpr (op == kIwLdA) {
+            if constexpr (kt + 3 < KTC)
+              ra[q] = *reinterpret_cast<const v4i*>(a + aoff[q] + (kt + 3) * kBK);
+          } else if constexpr (op == kIwLdB) {
+            if constexpr (kt + 4 < KTC)
+              rb[cur][q] = *reinterpret_cast<const v4i*>(bsrc(kt + 4, q));
+          } else if constexpr (op == kIwRdA) {
+            if constexpr (kt + 1 < KTC) rda_half(af[nxt][q / 2], astage(kt + 1), q / 2, q % 2);
+          } else if constexpr (op == kIwRdB) {
+            if constexpr (kt + 1 < KTC)
+              rdb_half(bf[bslot(q / 2, kt + 1)], bstage(kt + 1), q / 2, q % 2, kt + 1);
+          }
+        });
+        __builtin_amdgcn_sched_barrier(0);
       });
+      // with the barrier's LDS wait: step kt + 2 is written and step kt + 1's
+      // fragments are in registers (the compiler waits for each register load
+      // before the LDS write that uses it)
+      lds_barrier();
       __builtin_amdgcn_sched_barrier(0);
     });
-    // with the barrier's LDS wait: step kt + 2 is written and step kt + 1's
-    // fragments are in registers (the compiler waits for each register load
-    // before the LDS write that uses it)
-    lds_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-  });
-  float(*red)[BM] = reinterpret_cast<float(*)[BM]>(a0);
-  const v4f one = v4f{1.f, 1.f, 1.f, 1.f};  // MXFP4: no channel scales
-  const int c0 = wn * 64 + 4 * (lane >> 4);
-  gateup_epilogue_pp<BM, MS, NS, 2>(
-      acc, [&](int i) { return sxl[rbase + i * 16 + (lane & 15)]; },
-      [&](int jj) { return W4 ? one : *reinterpret_cast<const v4f*>(&s13l[c0 + 16 * jj]); },
-      [&](int jj) { return W4 ? one : *reinterpret_cast<const v4f*>(&s13l[kHN + c0 + 16 * jj]); },
-      red, rbase, wn, lane, te, S, ntile);
+
+    // the accumulators as of the last step (an empty use here keeps the
+    // MFMAs, whose results only the epilogue reads, from being moved past
+    // the branch below into the epilogue, with every step's fragments kept
+    // alive until then)
+#pragma unroll
+    for (int i = 0; i < MS; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) asm volatile("" : "+a"(acc[i][j]));
+    // the next tile's first loads, then this tile's epilogue (its scales
+    // stay in LDS until the next prologue's first barrier; the stages are
+    // free since the last step's barrier)
+    const Tile tc = te;
+    SetView Sc;  // what the epilogue reads of the set
+    Sc.h = h_out;
+    Sc.h_scale = hs_out;
+    Sc.F = F;
+    int sn = slot + sstep;
+    Tile tn;
+    const bool more = next_tile(sn, tn);
+    if (more) {
+      te = tn;
+      slot = sn;
+      setup();
+      issue_first();
+    }
+    const v4f one = v4f{1.f, 1.f, 1.f, 1.f};  // MXFP4: no channel scales
+    const int c0 = wn * 64 + 4 * (lane >> 4);
+    gateup_epilogue_pp<BM, MS, NS, 2>(
+        acc, [&](int i) { return sxl[rbase + i * 16 + (lane & 15)]; },
+        [&](int jj) { return W4 ? one : *reinterpret_cast<const v4f*>(&s13l[c0 + 16 * jj]); },
+        [&](int jj) { return W4 ? one : *reinterpret_cast<const v4f*>(&s13l[kHN + c0 + 16 * jj]); },
+        red, rbase, wn, lane, tc, Sc, tc.ntile);
+    if (!more) break;
+    // the epilogue read sxl and s13l before its barrier; every wave is past it
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1832,6 +1925,25 @@ __global__ __launch_bounds__(256) void down_f32_kernel(FfnCall c, int sid) {
   static_cast<float*>(S.out)[(size_t)r * d + m] = acc;
 }
 
+// Compute units of the current device, looked up once per device (the
+// persistent gate/up kernel runs one workgroup per compute unit).
+hipError_t device_cus(int* out) {
+  static std::atomic<int> cus[64];
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (n <= 0) return hipErrorInvalidDevice;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  *out = n;
+  return hipSuccess;
+}
+
 // Waves along M for a tile height: one for decode-sized tiles, two from 64 rows.
 template <int BM>
 constexpr int waves_m() { return BM >= 64 ? 2 : 1; }
@@ -1845,9 +1957,17 @@ hipError_t launch_gemms_bm(const FfnCall& c, TileHeader* hdr, TileEntry* up, Til
   constexpr int WU = waves_m<BM>(), WD = waves_m<BMD>();
   ev.mark(true, MOE_STEP_GATE_UP, s);
   if (cu > 0) {
-    if constexpr (KTU > 0 && BM == 192)  // tallest tiles: one wave per SIMD
-      hipLaunchKernelGGL((gateup_fp8_iw_kernel<BM, KTU, W4>),
-                         dim3((unsigned)cu), dim3(4 * kWave), 0, s, c, hdr, up);
+    if constexpr (KTU > 0 && BM == 192) {
+      // tallest tiles: one wave per SIMD, one workgroup per compute unit
+      // (a multiple of the XCD count, as the tile order assumes), each
+      // working through its XCD's tiles
+      int ncu = 0;
+      const hipError_t e = device_cus(&ncu);
+      if (e != hipSuccess) return e;
+      const size_t grid = std::min(cu, (size_t)std::max(kXcds, ncu / kXcds * kXcds));
+      hipLaunchKernelGGL((gateup_fp8_iw_kernel<BM, KTU, W4>), dim3((unsigned)grid),
+                         dim3(4 * kWave), 0, s, c, hdr, up);
+    }
     else if constexpr (KTU > 0 && BM >= 128)  // tall tiles: ping-pong schedule
       hipLaunchKernelGGL((gateup_fp8_pp_kernel<BM, KTU, pp_weight_stages<BM, W4>(), W4>),
                          dim3((unsigned)cu), dim3(8 * kWave), 0, s, c, hdr, up);
