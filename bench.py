@@ -111,7 +111,7 @@ def kernel_roofline(name, alg_bytes, flops, us):
 
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
-    for f in ("ffn.hip", "common.h"):
+    for f in ("ffn.hip", "common.h", "pipeline.h"):
         h.update(open(os.path.join(ROOT, "mixture_experts_softmax_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
