@@ -528,11 +528,16 @@ static moe_status_t layer_forward(const moe_shape_t* s, const moe_weights_t* wt,
   const bool fused = s->T <= kPermTile;
   RoutePermute rp{L.offsets, L.sorted_pair, L.pair_to_row, fp8 ? &cr : nullptr, bm,
                   fp8 ? L.tiles : nullptr};
+  // Above one permutation tile (single stream) x is quantised by the scan
+  // launch, whose one scanning workgroup leaves the other CUs idle; with
+  // the second stream the shared expert needs the codes right after the
+  // logits, so the logits launch writes them.
+  const bool quant_in_scan = fp8 && !fused && !split;
   hipError_t e;
   ev.mark(true, MOE_STEP_ROUTE, hs);
-  e = launch_route(fp8, x, wt->w_router, wt->router_bias, s->T, s->d, s->E, s->k, ids, w, L.xq,
-                   L.xs, L.logits, L.masks, L.counts, fused ? &rp : nullptr, hs,
-                   split ? fork : nullptr);
+  e = launch_route(fp8, x, wt->w_router, wt->router_bias, s->T, s->d, s->E, s->k, ids, w,
+                   quant_in_scan ? nullptr : L.xq, L.xs, L.logits, L.masks, L.counts,
+                   fused ? &rp : nullptr, hs, split ? fork : nullptr);
   ev.mark(false, MOE_STEP_ROUTE, hs);
   if (e != hipSuccess) return MOE_ERR_HIP;
   if (split) {  // the shared expert needs only the x codes
@@ -545,10 +550,11 @@ static moe_status_t layer_forward(const moe_shape_t* s, const moe_weights_t* wt,
   }
   // scan + scatter; on the FP8 path the scan also writes the FFN tile lists
   ev.mark(true, MOE_STEP_PERMUTE, hs);
+  const QuantRows qr{static_cast<const uint16_t*>(x), s->T, s->d, L.xq, L.xs};
   if (!fused)
     e = launch_perm_scan_scatter(ids, s->T, s->E, s->k, L.masks, L.counts, L.offsets,
                                  L.sorted_pair, L.pair_to_row, fp8 ? &cr : nullptr, bm,
-                                 fp8 ? L.tiles : nullptr, hs);
+                                 fp8 ? L.tiles : nullptr, hs, quant_in_scan ? &qr : nullptr);
   ev.mark(false, MOE_STEP_PERMUTE, hs);
   if (e != hipSuccess) return MOE_ERR_HIP;
 

@@ -326,12 +326,18 @@ constexpr int prefetch_depth() { return ROWS <= LIMIT ? 3 : 2; }
 // second time from the L2.
 constexpr int kNWaves = 4;
 
-// h / s from s's reciprocal and one FMA correction of the quotient: the
-// correctly rounded quotient unless the reciprocal's last-bit error decides
-// it, and then one ulp from it.
-__device__ inline float div_by(float h, float s, float rs) {
-  const float q = h * rs;
-  return fmaf(fmaf(-q, s, h), rs, q);
+// The gate/up epilogues' arithmetic, shared so that every gate/up kernel
+// writes the same h codes and scales. h = silu(g) u with g, u the scaled
+// gate and up values; the row's x scale sx is left out of u (silu(g) u / sx
+// is what the epilogues keep) and put back in the block's amax and in the
+// code factor: codes = (h / sx) (sx / s), with s = amax |h| / 448.
+__device__ inline float silu_times(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+// s from the block's largest |h / sx| (1 for an all-zero block)
+__device__ inline float h_block_scale(float am_over_sx, float sx) {
+  const float am = am_over_sx * sx;
+  return (am > 0.f) ? __fdiv_rn(am, kE4M3Max) : 1.0f;
 }
 
 // Gate/up epilogue, of the register-fed gate/up kernels: x and weight scales,
@@ -356,10 +362,9 @@ __device__ inline void gateup_epilogue(v4f (&acc)[MS][2 * NS], const float* sxl,
 #pragma unroll
       for (int jj = 0; jj < NS; ++jj) {
         const float gv = acc[i][jj][q] * sx * sg[jj];
-        const float uv = acc[i][NS + jj][q] * sx * su[jj];
-        const float h = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
-        acc[i][jj][q] = h;
-        m = fmaxf(m, fabsf(h));
+        const float hx = silu_times(gv, acc[i][NS + jj][q] * su[jj]);  // h / sx
+        acc[i][jj][q] = hx;
+        m = fmaxf(m, fabsf(hx));
       }
       m = max16(m);
       if ((lane & 15) == 0) red[wn][r] = m;
@@ -376,15 +381,15 @@ __device__ inline void gateup_epilogue(v4f (&acc)[MS][2 * NS], const float* sxl,
       float am = red[0][r];
 #pragma unroll
       for (int ww = 1; ww < kNWaves; ++ww) am = fmaxf(am, red[ww][r]);
-      const float s = (am > 0.f) ? __fdiv_rn(am, kE4M3Max) : 1.0f;
-      const float rs = __builtin_amdgcn_rcpf(s);
+      const float sx = sxl[r];
+      const float s = h_block_scale(am, sx);
+      const float f = sx * __builtin_amdgcn_rcpf(s);
       const size_t grow = (size_t)(te.row0 + r);
       uint8_t* hrow = S.h + grow * F;
 #pragma unroll
       for (int jj = 0; jj < NS; ++jj) {
         const int hc = ntile * kHN + wn * WN + jj * 16 + (lane & 15);
-        hrow[hc] = (uint8_t)__builtin_amdgcn_cvt_pk_fp8_f32(div_by(acc[i][jj][q], s, rs), 0.f, 0,
-                                                            false);
+        hrow[hc] = (uint8_t)__builtin_amdgcn_cvt_pk_fp8_f32(acc[i][jj][q] * f, 0.f, 0, false);
       }
       if (wn == 0 && (lane & 15) == 0) S.h_scale[grow * hblocks + ntile] = s;
     }
@@ -618,8 +623,9 @@ __device__ inline void static_for(Fn&& f) {
 // acc[i][NS + jj]). SwiGLU, the row's block amax over the 128 h columns of the
 // tile (the four lanes of a row, then the NWN waves of the row through LDS),
 // its scale amax / 448, and the four E4M3 codes packed into one 32-bit store. The codes
-// come from the packed float32 -> FP8 conversion, which rounds to nearest even
-// and saturates exactly as e4m3_encode does for quotients of magnitude <= 448.
+// are h (1/s) by one multiply (silu_times, h_block_scale) and come from the
+// packed float32 -> FP8 conversion, which rounds to nearest even and
+// saturates exactly as e4m3_encode does for quotients of magnitude <= 448.
 // The scales are read through accessors: sx(i) the x scale of row rbase +
 // 16 i + lane % 16, sg(jj) / su(jj) the channel scales of gate / up columns
 // c0 + 16 jj .. + 3 (ones for MXFP4 weights, which have none).
@@ -630,10 +636,14 @@ __device__ inline void gateup_epilogue_pp(v4f (&acc)[MS][2 * NS], SX sx, SG sg, 
   constexpr int WN = NS * 16;
   const int F = S.F;
   const int c0 = wn * WN + 4 * (lane >> 4);
+  // the rows' x scales, read once before the barrier below: a persistent
+  // caller's next tile may overwrite them once every wave is past it
+  float sxv[MS];
 #pragma unroll
   for (int i = 0; i < MS; ++i) {
     const int r = rbase + i * 16 + (lane & 15);
     const float sxi = sx(i);
+    sxv[i] = sxi;
     float m = 0.f;
 #pragma unroll
     for (int jj = 0; jj < NS; ++jj) {
@@ -641,10 +651,9 @@ __device__ inline void gateup_epilogue_pp(v4f (&acc)[MS][2 * NS], SX sx, SG sg, 
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float gv = acc[i][jj][q] * sxi * sgj[q];
-        const float uv = acc[i][NS + jj][q] * sxi * suj[q];
-        const float h = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
-        acc[i][jj][q] = h;
-        m = fmaxf(m, fabsf(h));
+        const float hx = silu_times(gv, acc[i][NS + jj][q] * suj[q]);  // h / sx
+        acc[i][jj][q] = hx;
+        m = fmaxf(m, fabsf(hx));
       }
     }
     m = fmaxf(m, __shfl_xor(m, 16, kWave));
@@ -660,16 +669,14 @@ __device__ inline void gateup_epilogue_pp(v4f (&acc)[MS][2 * NS], SX sx, SG sg, 
     float am = red[0][r];
 #pragma unroll
     for (int ww = 1; ww < NWN; ++ww) am = fmaxf(am, red[ww][r]);
-    const float s = (am > 0.f) ? __fdiv_rn(am, kE4M3Max) : 1.0f;
-    const float rs = __builtin_amdgcn_rcpf(s);
+    const float s = h_block_scale(am, sxv[i]);
+    const float f = sxv[i] * __builtin_amdgcn_rcpf(s);
     const size_t grow = (size_t)(te.row0 + r);
     uint8_t* hrow = S.h + grow * F + ntile * kHN + c0;
 #pragma unroll
     for (int jj = 0; jj < NS; ++jj) {
-      int w = __builtin_amdgcn_cvt_pk_fp8_f32(div_by(acc[i][jj][0], s, rs),
-                                              div_by(acc[i][jj][1], s, rs), 0, false);
-      w = __builtin_amdgcn_cvt_pk_fp8_f32(div_by(acc[i][jj][2], s, rs),
-                                          div_by(acc[i][jj][3], s, rs), w, true);
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(acc[i][jj][0] * f, acc[i][jj][1] * f, 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(acc[i][jj][2] * f, acc[i][jj][3] * f, w, true);
       *reinterpret_cast<int*>(hrow + 16 * jj) = w;
     }
     if (wn == 0 && lane < 16) S.h_scale[grow * hblocks + ntile] = s;

@@ -54,12 +54,21 @@ hipError_t launch_tile_counts(const uint64_t* masks, int T, int E, int32_t* tile
 hipError_t launch_perm_gather(const uint8_t* xq, const float* x_scale, const int32_t* sorted_pair,
                               const int32_t* offsets, int T, int E, int k, int d, uint8_t* x_perm,
                               float* x_perm_scale, hipStream_t s);
+// x rows to quantise to FP8 (quant.h): T rows of d bf16 values at x, their
+// codes to xq [T][d] and scales to xs [T]; T = 0: none.
+struct QuantRows {
+  const uint16_t* x;
+  int T, d;
+  uint8_t* xq;
+  float* xs;
+};
 // scan + scatter from masks/counts already computed (counts become the tile
-// bases); with c != nullptr also writes the grouped-FFN tile lists of c.
+// bases); with c != nullptr also writes the grouped-FFN tile lists of c; with
+// quant != nullptr the scan launch also quantises those rows.
 hipError_t launch_perm_scan_scatter(const int32_t* ids, int T, int E, int k, uint64_t* masks,
                                     int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
                                     int32_t* pair_to_row, const FfnCall* c, int bm, void* tiles_ws,
-                                    hipStream_t s);
+                                    hipStream_t s, const QuantRows* quant = nullptr);
 
 // ----- QK-Norm + RoPE (shape already validated) --------------------------------
 hipError_t launch_qk_norm_rope(const moe_qk_shape_t& s, void* qkv, const int32_t* positions,

@@ -16,6 +16,7 @@
 //               its GEMMs read x's rows through sorted_pair while staging them.
 #include "common.h"
 #include "internal.h"
+#include "quant.h"
 #include "tiles.h"
 
 namespace moe {
@@ -84,18 +85,28 @@ __global__ __launch_bounds__(kGatherRows * kWave) void perm_gather_kernel(
   if (lane == 0) x_perm_scale[r] = x_scale[t];
 }
 
-// One workgroup. Tile counts are the popcounts of the tile masks; counts
+// Workgroup 0 scans. Tile counts are the popcounts of the tile masks; counts
 // [ntiles][E] receives the per-tile bases. With
 // hdr != nullptr also emits the tile lists of `c` (set 0 = the E routed
 // groups with these offsets, set 1 = the shared expert if present).
+// Workgroups 1, 2, ... (q.T > 0) quantise x to FP8, one token row per wave:
+// the scan occupies one CU, so the rows are quantised on the others.
 __global__ __launch_bounds__(kScanThreads) void perm_scan_kernel(
     const uint64_t* __restrict__ masks, int32_t* __restrict__ counts, int ntiles, int E,
     int32_t* __restrict__ offsets, FfnCall c,
-    int bm, TileHeader* hdr, TileEntry* up, TileEntry* down, int cap_up, int cap_dn) {
+    int bm, TileHeader* hdr, TileEntry* up, TileEntry* down, int cap_up, int cap_dn,
+    QuantRows q) {
   __shared__ int stage[kScanStage];
   __shared__ int tot[MOE_MAX_E];
   __shared__ TileLds L;
   const int tid = threadIdx.x;
+  if (blockIdx.x > 0) {
+    const int t = (blockIdx.x - 1) * (kScanThreads / kWave) + tid / kWave;
+    if (t < q.T)
+      quantize_row(q.x + (size_t)t * q.d, q.d, tid & (kWave - 1), q.xq + (size_t)t * q.d,
+                   q.xs + t);
+    return;
+  }
   int run = 0;
   const int ct = kScanStage / E;  // tiles per chunk
   for (int t0 = 0; t0 < ntiles; t0 += ct) {
@@ -192,7 +203,7 @@ size_t permute_ws_bytes(int T, int E) { return perm_masks_bytes(T, E) + perm_cou
 hipError_t launch_perm_scan_scatter(const int32_t* ids, int T, int E, int k, uint64_t* masks,
                                     int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
                                     int32_t* pair_to_row, const FfnCall* c, int bm, void* tiles_ws,
-                                    hipStream_t s) {
+                                    hipStream_t s, const QuantRows* quant) {
   const int ntiles = ceil_div(T, kPermTile);
   TileHeader* hdr = nullptr;
   TileEntry *up = nullptr, *dn = nullptr;
@@ -202,8 +213,11 @@ hipError_t launch_perm_scan_scatter(const int32_t* ids, int T, int E, int k, uin
     cc = *c;
     tile_lists(cc, bm, tiles_ws, &hdr, &up, &dn, &cap_up, &cap_dn);
   }
-  hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, masks, counts, ntiles,
-                     E, offsets, cc, bm, hdr, up, dn, cap_up, cap_dn);
+  QuantRows q{};
+  if (quant != nullptr) q = *quant;
+  const int nq = ceil_div(q.T, kScanThreads / kWave);
+  hipLaunchKernelGGL(perm_scan_kernel, dim3(1 + nq), dim3(kScanThreads), 0, s, masks, counts,
+                     ntiles, E, offsets, cc, bm, hdr, up, dn, cap_up, cap_dn, q);
   hipLaunchKernelGGL(perm_scatter_kernel, dim3(ntiles), dim3(kPermTile), 0, s, ids, T, E, k, masks,
                      counts, offsets, sorted_pair, pair_to_row);
   return hipGetLastError();
@@ -218,7 +232,7 @@ hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* offs
   hipLaunchKernelGGL(perm_count_kernel, dim3(ceil_div(T, kPermTile)), dim3(kPermTile), 0, s, ids,
                      T, E, k, masks, counts, tile_counts);
   return launch_perm_scan_scatter(ids, T, E, k, masks, counts, offsets, sorted_pair, pair_to_row,
-                                  nullptr, 0, nullptr, s);
+                                  nullptr, 0, nullptr, s, nullptr);
 }
 
 hipError_t launch_tile_counts(const uint64_t* masks, int T, int E, int32_t* tile_counts,
