@@ -584,6 +584,12 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 __device__ inline void dma16(const uint8_t* src, uint8_t* lds_base) {
   __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (lds_void_t*)lds_base, 16, 0, 0);
 }
+// The same with 4 bytes per lane (lane l's dword lands at lds_base + 4 l).
+template <typename T>
+__device__ inline void dma4(const T* src, T* lds_base) {
+  static_assert(sizeof(T) == 4, "one dword per lane");
+  __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (lds_void_t*)lds_base, 4, 0, 0);
+}
 
 // s_waitcnt vmcnt(n) alone (expcnt and lgkmcnt left at their "no wait"
 // maxima; gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
@@ -1496,16 +1502,20 @@ __global__ __launch_bounds__(8 * kWave) void down_fp8_lds_kernel(
   constexpr int NAD = BM * kBK / 1024 / NW;           // A loads per thread per step
   constexpr int NBD = kDownBN * KB / 1024 / NW;       // B loads per thread per step
   constexpr int NSTEP = NTW * KTC;
-  constexpr int HPT = (BM * KTC + NTH - 1) / NTH;
+  constexpr int HCH = BM * KTC / kWave;  // 64-value chunks of the h block scales
+  // ... of the channel scales (FP8) or of the MXFP4 scale tile
+  constexpr int SCH = W4 ? (NTW * kDownBN * (KTC + 1) + kWave - 1) / kWave : NTW * kDownBN / kWave;
   static_assert(BM * kBK % (1024 * NW) == 0, "A tile must split into whole wave loads");
-  static_assert(!W4 || KTC % 4 == 0, "MXFP4 scales are held per row in K-step quads");
+  static_assert(HCH % NW == 0, "h scale chunks split evenly over the waves");
+  static_assert(W4 || SCH <= NW, "one channel-scale chunk per wave at most");
 
   __shared__ __attribute__((aligned(1024))) uint8_t a0[BM * kBK];
   __shared__ __attribute__((aligned(1024))) uint8_t a1[BM * kBK];
   __shared__ __attribute__((aligned(1024))) uint8_t b0[kDownBN * KB];
   __shared__ __attribute__((aligned(1024))) uint8_t b1[kDownBN * KB];
   __shared__ __attribute__((aligned(1024))) uint8_t b2[kDownBN * KB];
-  __shared__ int ssc[W4 ? NTW * kDownBN * (KTC + 1) : 1];  // MXFP4 scale tile
+  // MXFP4 scale tile (whole 64-dword chunks: it is filled by them)
+  __shared__ int ssc[W4 ? SCH * kWave : 1];
   __shared__ float hsl[KTC][BM];
   __shared__ __attribute__((aligned(16))) float s2l[W4 ? 1 : NTW * kDownBN];  // channel scales
 
@@ -1559,40 +1569,45 @@ __global__ __launch_bounds__(8 * kWave) void down_fp8_lds_kernel(
       dma16(w2 + (size_t)ch * wrb + kt * KB + bcc, dst + (NBD * wave + i) * 1024);
     }
   };
-  // h block scales of the tile's rows, and every N tile's channel scales
-  float hv[HPT];
-#pragma unroll
-  for (int i = 0; i < HPT; ++i) {
-    const int e = min(tid + i * NTH, BM * KTC - 1);
-    const int r = e / KTC, kt = e % KTC;
-    hv[i] = S.h_scale[(size_t)(te.row0 + min(r, te.nrows - 1)) * KTC + kt];
-  }
-  // the MFMAs take the weights as A, so lane l accumulates channels
-  // 16 j + 4 (l / 16) + q of the wave's 64 for tile row 16 i + l % 16
-  if constexpr (!W4) {
-    for (int e = tid; e < NTW * kDownBN; e += NTH)
-      s2l[e] = S.s2[(size_t)g * d + min((nt0 + e / kDownBN) * kDownBN + e % kDownBN, d - 1)];
-  }
-  // MXFP4: every N tile's channel rows' E8M0 scales into LDS (published by
-  // the first barrier); tile row n 256 + r is channel (nt0 + n) 256 + r
-  if constexpr (W4)
-    fill_scale_tile<KTC, NTW * kDownBN, NTH>(
-        ssc,
-        [&](int r) {
-          const int n = min(r / kDownBN, dnt - 1 - nt0);
-          const int ch = min((nt0 + n) * kDownBN + r % kDownBN, d - 1);
-          return S.e2 + ((size_t)g * d + ch) * (F / 32);
-        },
-        tid);
-#pragma unroll
-  for (int i = 0; i < HPT; ++i) {
-    const int e = tid + i * NTH;
-    if ((BM * KTC) % NTH == 0 || e < BM * KTC) hsl[e % KTC][e / KTC] = hv[i];
-  }
-
-  // prologue: B(0), A(0), B(1)
+  // Prologue: the operands of the first step, every scale the tile needs (h
+  // block scales of its rows, every N tile's channel scales or MXFP4 scale
+  // rows), then the weights of the second step, all by direct-to-LDS loads
+  // issued at once (the first step's wait leaves only the last in flight), so they
+  // arrive together (through registers, the scales' LDS writes would wait
+  // for their loads before the operands' loads could issue). Scales go in
+  // 64-value chunks, one value per lane. (The MFMAs take the weights as A,
+  // so lane l accumulates channels 16 j + 4 (l / 16) + q of the wave's 64
+  // for tile row 16 i + l % 16.)
   load_b(0, b0);
   load_a(0, a0);
+#pragma unroll
+  for (int q = 0; q < HCH / NW; ++q) {  // hsl[kt][r] = h_scale[row r][kt]
+    const int ci = wave + q * NW, f = ci * kWave + lane;
+    const int kt = f / BM, r = f % BM;
+    dma4(S.h_scale + (size_t)(te.row0 + min(r, te.nrows - 1)) * KTC + kt, &hsl[0][0] + ci * kWave);
+  }
+  if constexpr (!W4) {
+    if (wave < SCH) {  // s2l[e]: channel (nt0 + e / 256) 256 + e % 256
+      const int e = wave * kWave + lane;
+      dma4(S.s2 + (size_t)g * d + min((nt0 + e / kDownBN) * kDownBN + e % kDownBN, d - 1),
+           s2l + wave * kWave);
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < (SCH + NW - 1) / NW; ++q) {
+      // MXFP4 tile dword r (KTC + 1) + kt: K step kt's four E8M0 scales of
+      // tile row r = channel (nt0 + r / 256) 256 + r % 256 (kt = KTC: the
+      // row's padding, loaded with a repeated dword)
+      const int ci = wave + q * NW, f = ci * kWave + lane;
+      if (SCH % NW == 0 || ci < SCH) {
+        const int r = min(f / (KTC + 1), NTW * kDownBN - 1), kt = min(f % (KTC + 1), KTC - 1);
+        const int n = min(r / kDownBN, dnt - 1 - nt0);
+        const int ch = min((nt0 + n) * kDownBN + r % kDownBN, d - 1);
+        dma4(reinterpret_cast<const int*>(S.e2 + ((size_t)g * d + ch) * (F / 32) + 4 * kt),
+             ssc + ci * kWave);
+      }
+    }
+  }
   if (NSTEP > 1) load_b(1, b1);
 
   // output rows of this tile, written with buffer stores (masked lanes are
