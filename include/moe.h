@@ -247,7 +247,10 @@ moe_status_t moe_combine(const moe_shape_t* shape, const void* expert_out,
 
 /*
  * The whole layer: router, permutation, grouped FFN over the routed experts
- * and the shared expert, combine. x [T][d] and y [T][d] in act_dtype.
+ * and the shared expert, combine. x [T][d] and y [T][d] in act_dtype. The FP8
+ * codes of x (quantised paths) are the ones moe_route_topk writes; above 64
+ * tokens the layer computes them in its scan launch instead of the logits
+ * launch (moe_layer_forward_overlap keeps them in the logits launch).
  * topk_ids [T][k] and topk_w [T][k] receive the routing when non-NULL. Needs a
  * workspace of moe_layer_workspace_size() bytes, aligned to 256 bytes.
  */
@@ -305,9 +308,11 @@ moe_status_t moe_layer_workspace_regions(const moe_shape_t* shape, moe_layer_reg
 
 /* Steps of moe_layer_forward, in launch order (for moe_layer_forward_events). */
 typedef enum moe_step {
-  MOE_STEP_ROUTE = 0,    /* router: logits and top-k kernels (T <= 64: the top-k kernel also
-                            does the permutation and writes the FFN tile lists) */
-  MOE_STEP_PERMUTE = 1,  /* permutation: scan (which also writes the FFN tile lists) and
+  MOE_STEP_ROUTE = 0,    /* router: logits and top-k kernels (T <= 64: the logits launch
+                            also quantises x, and the top-k kernel does the permutation and
+                            writes the FFN tile lists) */
+  MOE_STEP_PERMUTE = 1,  /* permutation: scan (which also writes the FFN tile lists and,
+                            T > 64, quantises x beside its one scanning workgroup) and
                             scatter; no kernels when T <= 64 */
   MOE_STEP_TILES = 2,    /* separate FFN tile-list kernel (moe_grouped_ffn only; none in the layer) */
   MOE_STEP_GATE_UP = 3,  /* gate/up GEMM + SwiGLU + h quantisation */
