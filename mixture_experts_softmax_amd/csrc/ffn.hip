@@ -642,18 +642,23 @@ __device__ inline void gateup_epilogue_pp(v4f (&acc)[MS][2 * NS], SX sx, SG sg, 
   constexpr int WN = NS * 16;
   const int F = S.F;
   const int c0 = wn * WN + 4 * (lane >> 4);
-  // the rows' x scales, read once before the barrier below: a persistent
-  // caller's next tile may overwrite them once every wave is past it
+  // the rows' x scales and the columns' channel scales, read once before
+  // the barrier below (a persistent caller's next tile may overwrite them
+  // once every wave is past it) and up front (one wait for all of them)
   float sxv[MS];
+  v4f sgv[NS], suv[NS];
+#pragma unroll
+  for (int jj = 0; jj < NS; ++jj) sgv[jj] = sg(jj), suv[jj] = su(jj);
+#pragma unroll
+  for (int i = 0; i < MS; ++i) sxv[i] = sx(i);
 #pragma unroll
   for (int i = 0; i < MS; ++i) {
     const int r = rbase + i * 16 + (lane & 15);
-    const float sxi = sx(i);
-    sxv[i] = sxi;
+    const float sxi = sxv[i];
     float m = 0.f;
 #pragma unroll
     for (int jj = 0; jj < NS; ++jj) {
-      const v4f sgj = sg(jj), suj = su(jj);
+      const v4f sgj = sgv[jj], suj = suv[jj];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float gv = acc[i][jj][q] * sxi * sgj[q];
@@ -678,12 +683,36 @@ __device__ inline void gateup_epilogue_pp(v4f (&acc)[MS][2 * NS], SX sx, SG sg, 
     const float s = h_block_scale(am, sxv[i]);
     const float f = sxv[i] * __builtin_amdgcn_rcpf(s);
     const size_t grow = (size_t)(te.row0 + r);
-    uint8_t* hrow = S.h + grow * F + ntile * kHN + c0;
+    int w[NS];
 #pragma unroll
     for (int jj = 0; jj < NS; ++jj) {
-      int w = __builtin_amdgcn_cvt_pk_fp8_f32(acc[i][jj][0] * f, acc[i][jj][1] * f, 0, false);
-      w = __builtin_amdgcn_cvt_pk_fp8_f32(acc[i][jj][2] * f, acc[i][jj][3] * f, w, true);
-      *reinterpret_cast<int*>(hrow + 16 * jj) = w;
+      w[jj] = __builtin_amdgcn_cvt_pk_fp8_f32(acc[i][jj][0] * f, acc[i][jj][1] * f, 0, false);
+      w[jj] = __builtin_amdgcn_cvt_pk_fp8_f32(acc[i][jj][2] * f, acc[i][jj][3] * f, w[jj], true);
+    }
+    if constexpr (NS == 4) {
+      // The row's 64 bytes of this wave sit in its four lanes l % 16 + 16 q
+      // as dwords 4 jj + q; a 4 x 4 transpose among them (two rounds of
+      // pairwise exchanges, lanes l ^ 16 then l ^ 32) gives lane q dwords
+      // 4 q .. 4 q + 3, stored as one 16-byte piece: an instruction writes
+      // 16 rows x 64 contiguous bytes instead of 16 rows x 16.
+      const int q = lane >> 4;
+      {
+        const int sa = (q & 1) ? w[0] : w[1], sb = (q & 1) ? w[2] : w[3];
+        const int ra = __builtin_amdgcn_ds_swizzle(sa, 0x401F);  // lane ^ 16
+        const int rb = __builtin_amdgcn_ds_swizzle(sb, 0x401F);
+        if (q & 1) w[0] = ra, w[2] = rb; else w[1] = ra, w[3] = rb;
+      }
+      {
+        const int sa = (q & 2) ? w[0] : w[2], sb = (q & 2) ? w[1] : w[3];
+        const int ra = __shfl_xor(sa, 32, kWave), rb = __shfl_xor(sb, 32, kWave);
+        if (q & 2) w[0] = ra, w[1] = rb; else w[2] = ra, w[3] = rb;
+      }
+      *reinterpret_cast<v4i*>(S.h + grow * F + ntile * kHN + wn * WN + 16 * q) =
+          v4i{w[0], w[1], w[2], w[3]};
+    } else {
+      uint8_t* hrow = S.h + grow * F + ntile * kHN + c0;
+#pragma unroll
+      for (int jj = 0; jj < NS; ++jj) *reinterpret_cast<int*>(hrow + 16 * jj) = w[jj];
     }
     if (wn == 0 && lane < 16) S.h_scale[grow * hblocks + ntile] = s;
   }
