@@ -709,6 +709,17 @@ __device__ inline void gateup_epilogue_pp(v4f (&acc)[MS][2 * NS], SX sx, SG sg, 
       }
       *reinterpret_cast<v4i*>(S.h + grow * F + ntile * kHN + wn * WN + 16 * q) =
           v4i{w[0], w[1], w[2], w[3]};
+    } else if constexpr (NS == 2) {
+      // The same with 32 bytes per row and wave (dwords 4 jj + q, jj < 2):
+      // lane q ends with dwords 2 q and 2 q + 1, one 8-byte store.
+      const int q = lane >> 4;
+      const int keep = (q & 2) ? w[1] : w[0];
+      const int got = __shfl_xor((q & 2) ? w[0] : w[1], 32, kWave);
+      const int recv = __builtin_amdgcn_ds_swizzle(((q & 1) == ((q >> 1) & 1)) ? got : keep, 0x401F);
+      const int lo = (q & 1) ? recv : ((q & 2) ? got : keep);
+      const int hi = (q & 1) ? ((q & 2) ? keep : got) : recv;
+      *reinterpret_cast<uint2*>(S.h + grow * F + ntile * kHN + wn * WN + 8 * q) =
+          make_uint2((uint32_t)lo, (uint32_t)hi);
     } else {
       uint8_t* hrow = S.h + grow * F + ntile * kHN + c0;
 #pragma unroll
